@@ -1,0 +1,192 @@
+"""ctypes wrapper around the fp64 C oracle (``coda_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, the bench's CPU-baseline leg).
+
+The C file is compiled with gcc on first use (or by ``build()``) into
+``oracle/liborcl.so``; no part of the HIP library is involved.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "coda_oracle.c")
+_LIB = os.path.join(_HERE, "liborcl.so")
+
+BF16 = 0
+E4M3 = 1
+ACT_NONE = 0
+ACT_SWIGLU = 1
+
+__all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
+           "e4m3_encode", "fold_bf16", "quant_e4m3", "chain", "prepare", "BF16", "E4M3",
+           "ACT_NONE", "ACT_SWIGLU"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle (plain C, fp64, OpenMP, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                               "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        i64 = C.c_int64
+        L.orc_max_threads.restype = C.c_int
+        L.orc_bf16_decode.restype = C.c_double
+        L.orc_bf16_decode.argtypes = [C.c_uint16]
+        L.orc_bf16_encode_rne.restype = C.c_uint16
+        L.orc_bf16_encode_rne.argtypes = [C.c_double]
+        L.orc_e4m3_decode.restype = C.c_double
+        L.orc_e4m3_decode.argtypes = [C.c_uint8]
+        L.orc_e4m3_encode_sat_rne.restype = C.c_uint8
+        L.orc_e4m3_encode_sat_rne.argtypes = [C.c_double]
+        for f in ("orc_bf16_decode_n", "orc_bf16_encode_n", "orc_e4m3_decode_n", "orc_e4m3_encode_n"):
+            getattr(L, f).restype = None
+            getattr(L, f).argtypes = [i64, P, P]
+        L.orc_fold_bf16.restype = None
+        L.orc_fold_bf16.argtypes = [i64, i64, P, P, P]
+        L.orc_quant_e4m3.restype = None
+        L.orc_quant_e4m3.argtypes = [i64, i64, P, P, P, P, P]
+        L.orc_chain.restype = C.c_int
+        L.orc_chain.argtypes = [i64, P, i64, i64, i64, C.c_int,
+                                P, C.c_int, C.c_double,
+                                P, C.c_int, C.c_double,
+                                P, P, P, C.c_int, C.c_double, C.c_double,
+                                P, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
+def bf16_decode(c) -> np.ndarray:
+    c = np.ascontiguousarray(c, dtype=np.uint16)
+    out = np.empty(c.shape, np.float64)
+    lib().orc_bf16_decode_n(c.size, _p(c), _p(out))
+    return out
+
+
+def bf16_encode(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_bf16_encode_n(x.size, _p(x), _p(out))
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().orc_e4m3_decode_n(c.size, _p(c), _p(out))
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_e4m3_encode_n(x.size, _p(x), _p(out))
+    return out
+
+
+def fold_bf16(W_t: np.ndarray, gamma: np.ndarray | None) -> np.ndarray:
+    """W'[n,k] = bf16_rne(fl32(gamma[k] * W[n,k])), W_t [N, K] bf16 bits."""
+    W_t = np.ascontiguousarray(W_t, dtype=np.uint16)
+    N, K = W_t.shape
+    g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float32)
+    out = np.empty((N, K), np.uint16)
+    lib().orc_fold_bf16(N, K, _p(W_t), _p(g), _p(out))
+    return out
+
+
+def quant_e4m3(W_t: np.ndarray, gamma: np.ndarray | None):
+    """Per-tensor e4m3 quantisation of fl32(gamma*W) (gamma None: of W itself).
+
+    Returns (codes uint8 [N, K], amax float32, scale float32)."""
+    W_t = np.ascontiguousarray(W_t, dtype=np.uint16)
+    N, K = W_t.shape
+    g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float32)
+    out = np.empty((N, K), np.uint8)
+    amax = np.zeros(1, np.float32)
+    scale = np.zeros(1, np.float32)
+    lib().orc_quant_e4m3(N, K, _p(W_t), _p(g), _p(out), _p(amax), _p(scale))
+    return out, np.float32(amax[0]), np.float32(scale[0])
+
+
+def prepare(inputs: dict, dtype: str) -> dict:
+    """The oracle's own weight/activation preparation for a workload.
+
+    bf16: Wp = fold_bf16(W_t, gamma); scales 1.
+    e4m3: A, Wo_t quantised per tensor; Wp = quant_e4m3(W_t, gamma) (fold first).
+    Returns dict(A, a_dt, a_scale, Wo, wo_dt, wo_scale, Wp, wp_dt, wp_scale)."""
+    if dtype == "bf16":
+        return dict(A=inputs["A"], a_dt=BF16, a_scale=1.0, Wo=inputs["Wo_t"], wo_dt=BF16,
+                    wo_scale=1.0, Wp=fold_bf16(inputs["W_t"], inputs["gamma"]), wp_dt=BF16,
+                    wp_scale=1.0)
+    if dtype == "e4m3":
+        qa, _, sa = quant_e4m3(inputs["A"], None)
+        qo, _, so = quant_e4m3(inputs["Wo_t"], None)
+        qw, _, sw = quant_e4m3(inputs["W_t"], inputs["gamma"])
+        return dict(A=qa, a_dt=E4M3, a_scale=float(sa), Wo=qo, wo_dt=E4M3, wo_scale=float(so),
+                    Wp=qw, wp_dt=E4M3, wp_scale=float(sw))
+    raise ValueError(dtype)
+
+
+def chain(prep: dict, x_res, gamma, act: int, eps: float, rows=None, M: int | None = None):
+    """Run the unfused fp64 chain on the listed rows (default: all M rows).
+
+    ``prep`` is the output of :func:`prepare`.  Returns dict(h, hb, S, r, y) with one
+    entry per computed row: h fp64 [R, d] (unrounded), hb uint16 [R, d] (bf16 bits),
+    S fp64 [R] = sum hb^2, r fp64 [R], y fp64 [R, n_out]."""
+    A = np.ascontiguousarray(prep["A"])
+    Wo = np.ascontiguousarray(prep["Wo"])
+    Wp = np.ascontiguousarray(prep["Wp"])
+    M = A.shape[0] if M is None else M
+    K1 = A.shape[1]
+    d = Wo.shape[0]
+    N2w = Wp.shape[0]
+    if Wo.shape[1] != K1 or Wp.shape[1] != d:
+        raise ValueError("shape mismatch")
+    if rows is None:
+        rows_a = None
+        R = M
+    else:
+        rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+        R = rows_a.size
+    n_out = N2w // 2 if act == ACT_SWIGLU else N2w
+    xr = None if x_res is None else np.ascontiguousarray(x_res, dtype=np.uint16)
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    h = np.empty((R, d), np.float64)
+    hb = np.empty((R, d), np.uint16)
+    S = np.empty(R, np.float64)
+    r = np.empty(R, np.float64)
+    y = np.empty((R, n_out), np.float64)
+    rc = lib().orc_chain(R, _p(rows_a), K1, d, N2w, act,
+                         _p(A), prep["a_dt"], prep["a_scale"],
+                         _p(Wo), prep["wo_dt"], prep["wo_scale"],
+                         _p(xr), _p(g), _p(Wp), prep["wp_dt"], prep["wp_scale"], eps,
+                         _p(h), _p(hb), _p(S), _p(r), _p(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle chain failed ({rc})")
+    return dict(h=h, hb=hb, S=S, r=r, y=y)

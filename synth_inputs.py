@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs for the GEMM -> residual -> RMSNorm -> GEMM(+SwiGLU) chain.
+
+This module is the ONLY code shared by the fp64 oracle (``oracle/``) and the HIP path
+(``gemm_epilogue_transformer_amd/``).  It draws random numbers and stores them in the
+chain's input dtypes; it holds none of the chain's arithmetic (no GEMM, no residual,
+no RMSNorm, no gamma fold, no quantisation, no activation).
+
+Workloads.  The pages evaluate LLaMA-style Transformer blocks at 16K-token batches
+(ecosistemastartup "CODA: Nuevo kernel GPU..." section "Que mejoras de rendimiento
+reporta el paper?"; kucoin "CODA: new research..." section "Resultados del
+experimento", hidden dims of 1B/7B/70B models).  No dataset or trained weights are
+involved: every tensor here is synthetic with the shapes of those blocks.
+
+Distributions (the same for every workload):
+  activations A ~ N(0, 1), residual x_res ~ N(0, 1),
+  weights W ~ N(0, 1/K) (variance 1/K, K = that weight's reduction dim),
+  gamma = 1 + 0.1 * N(0, 1) (fp32).
+All samples are drawn in fp32 from numpy's PCG64 ``default_rng(seed)`` in the fixed
+order A, Wo, x_res, gamma, W, then rounded to bf16 (round-to-nearest-even, done by
+torch's CPU dtype cast, a library routine).
+
+Weights are stored K-contiguous, i.e. in the [out_features, in_features] layout of
+``torch.nn.Linear``: the mathematical Wo[K1, d] is held as Wo_t[d, K1] and the
+mathematical Wgu[d, 2F] as W_t[2F, d] (gate rows first, then up rows).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+ACT_NONE = 0
+ACT_SWIGLU = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int          # tokens (rows)
+    K1: int         # reduction dim of the first GEMM
+    d: int          # hidden dim = N of the first GEMM = reduction dim of the second GEMM
+    N2w: int        # rows of the second weight (2F for SwiGLU, N2 otherwise)
+    act: int        # ACT_NONE or ACT_SWIGLU
+    dtype: str      # "bf16" or "e4m3" (fp8 variant: A, Wo and the second weight in e4m3)
+    eps: float
+    seed: int
+
+    @property
+    def n_out(self) -> int:
+        return self.N2w // 2 if self.act == ACT_SWIGLU else self.N2w
+
+    @property
+    def gemm_flops(self) -> int:
+        """2*M*K*N for each of the two GEMMs (epilogue arithmetic not counted)."""
+        return 2 * self.M * self.K1 * self.d + 2 * self.M * self.d * self.N2w
+
+
+# The five workloads.  1: tiny correctness case; 2: LLaMA-3-1B attention-out ->
+# SwiGLU MLP-in; 3: LLaMA-3-1B MLP-out -> next layer QKV (32x64 query + 2x8x64 KV
+# heads = 3072); 4: LLaMA-3-8B-shaped attention-out -> SwiGLU MLP-in; 5: workload 2
+# with A, Wo and the second weight quantised to e4m3 (same draws as workload 2).
+WORKLOADS = {
+    1: Workload("tiny_m128_d256_n512_none", 128, 256, 256, 512, ACT_NONE, "bf16", 1e-5, 1001),
+    2: Workload("llama1b_attnout_mlpin_m16384", 16384, 2048, 2048, 16384, ACT_SWIGLU, "bf16", 1e-5, 1002),
+    3: Workload("llama1b_mlpout_qkv_m16384", 16384, 8192, 2048, 3072, ACT_NONE, "bf16", 1e-5, 1003),
+    4: Workload("llama8b_attnout_mlpin_m16384", 16384, 4096, 4096, 28672, ACT_SWIGLU, "bf16", 1e-5, 1004),
+    5: Workload("llama1b_attnout_mlpin_m16384_fp8", 16384, 2048, 2048, 16384, ACT_SWIGLU, "e4m3", 1e-5, 1002),
+}
+
+
+def custom(M: int, K1: int, d: int, N2w: int, act: int, seed: int, dtype: str = "bf16",
+           eps: float = 1e-5) -> Workload:
+    """A workload of arbitrary shape (ragged and edge-case tests)."""
+    if act == ACT_SWIGLU and N2w % 2:
+        raise ValueError("SwiGLU needs an even number of second-weight rows")
+    return Workload(f"custom_m{M}_k{K1}_d{d}_n{N2w}_a{act}", M, K1, d, N2w, act, dtype, eps, seed)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 array -> bf16 bit patterns (uint16), round-to-nearest-even via torch."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact widening)."""
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def generate(w: Workload, rows: int | None = None) -> dict:
+    """Draw the inputs of workload ``w``.
+
+    Returns a dict of numpy arrays:
+      A      uint16 [M, K1]   bf16 bits
+      Wo_t   uint16 [d, K1]   bf16 bits (first weight, nn.Linear layout)
+      x_res  uint16 [M, d]    bf16 bits
+      gamma  float32 [d]
+      W_t    uint16 [N2w, d]  bf16 bits (second weight before the gamma fold)
+    For an e4m3 workload these are the pre-quantisation tensors (quantisation is a
+    step of the chain's weight/activation preparation, not of input generation).
+    ``rows`` (optional) truncates M, keeping the draws of the first rows identical.
+    """
+    rng = np.random.default_rng(w.seed)
+    f32 = np.float32
+    A = rng.standard_normal((w.M, w.K1), dtype=f32)
+    Wo = rng.standard_normal((w.d, w.K1), dtype=f32) * f32(1.0 / np.sqrt(w.K1))
+    x = rng.standard_normal((w.M, w.d), dtype=f32)
+    gamma = (f32(1.0) + f32(0.1) * rng.standard_normal(w.d, dtype=f32)).astype(f32)
+    W = rng.standard_normal((w.N2w, w.d), dtype=f32) * f32(1.0 / np.sqrt(w.d))
+    if rows is not None:
+        A, x = A[:rows], x[:rows]
+    return {
+        "A": to_bf16_bits(A),
+        "Wo_t": to_bf16_bits(Wo),
+        "x_res": to_bf16_bits(x),
+        "gamma": gamma,
+        "W_t": to_bf16_bits(W),
+    }
