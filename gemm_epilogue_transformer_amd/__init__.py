@@ -1,0 +1,139 @@
+"""MI355X (gfx950) GEMM-epilogue chain: GEMM -> residual -> RMSNorm -> GEMM(+SwiGLU).
+
+Thin Python binding over the C ABI of ``libcoda.so`` (declared in ``include/coda.h``).
+Every step of the chain runs in the library's HIP kernels; this module only marshals
+torch device tensors (memory) and the current HIP stream into the C calls.  If the
+library is missing, importing the binding's functions raises: there is no CPU path.
+
+    h, P = gemm_resid_partialrms(A, Wo_t, x_res)          # first GEMM + epilogue
+    r    = rowscale_reduce(P, N=d, eps=1e-5)               # light reduction
+    y    = gemm_rowscale_swiglu(h, Wp_t, r, act=SWIGLU)   # second GEMM + epilogue
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import CODA_ACT_NONE, CODA_ACT_SWIGLU, CODA_BF16, CODA_E4M3, CodaError  # noqa: F401
+
+NONE = CODA_ACT_NONE
+SWIGLU = CODA_ACT_SWIGLU
+
+__all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3",
+           "partials_per_row", "gemm_resid_partialrms", "rowscale_reduce",
+           "gemm_rowscale_swiglu", "chain", "version"]
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _esize(t, n):
+    if t.element_size() != n:
+        raise ValueError(f"expected {n}-byte elements, got {t.dtype}")
+
+
+def version() -> str:
+    return _lib.load().coda_version().decode()
+
+
+def partials_per_row(N: int) -> int:
+    return int(_lib.load().coda_partials_per_row(N))
+
+
+def prepare_weight_bf16(W_t, gamma=None, out=None, stream=None):
+    """Wp[n,k] = bf16(gamma[k] * W[n,k]);  W_t [N, K] bf16, gamma [K] fp32."""
+    _esize(W_t, 2)
+    N, K = W_t.shape
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=W_t.device) if out is None else out
+    _lib.check("coda_prepare_weight_bf16", _lib.load().coda_prepare_weight_bf16(
+        N, K, _ptr(W_t), _ptr(gamma), _ptr(out), _stream(stream)))
+    return out
+
+
+def quantize_e4m3(X, gamma=None, out=None, amax_scale=None, stream=None):
+    """Per-tensor e4m3 quantisation (gamma folded first if given).
+
+    Returns (Q uint8 [N, K], amax_scale fp32 [2] = {amax, scale})."""
+    _esize(X, 2)
+    N, K = X.shape
+    out = torch.empty((N, K), dtype=torch.uint8, device=X.device) if out is None else out
+    if amax_scale is None:
+        amax_scale = torch.empty(2, dtype=torch.float32, device=X.device)
+    _lib.check("coda_quantize_e4m3", _lib.load().coda_quantize_e4m3(
+        N, K, _ptr(X), _ptr(gamma), _ptr(out), _ptr(amax_scale), _stream(stream)))
+    return out, amax_scale
+
+
+def gemm_resid_partialrms(A, W, x_res=None, a_scale=None, w_scale=None, h=None,
+                          partials=None, stream=None):
+    """h = bf16(sa*sw*A.W^T + x_res);  P[m,t] = sum of h^2 over N-tile t.
+
+    A [M, K] and W [N, K] both bf16 (2-byte) or both e4m3 (1-byte, scales required)."""
+    fp8 = A.element_size() == 1
+    _esize(W, A.element_size())
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("A and W disagree on K")
+    dev = A.device
+    if h is None:
+        h = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if partials is None:
+        partials = torch.empty((M, partials_per_row(N)), dtype=torch.float32, device=dev)
+    _lib.check("coda_gemm_resid_partialrms", _lib.load().coda_gemm_resid_partialrms(
+        M, N, K, _ptr(A), CODA_E4M3 if fp8 else CODA_BF16, _ptr(a_scale), _ptr(W), _ptr(w_scale),
+        _ptr(x_res), _ptr(h), _ptr(partials), _stream(stream)))
+    return h, partials
+
+
+def rowscale_reduce(partials, N: int, eps: float, r=None, stream=None):
+    """r[m] = 1/sqrt(sum_t P[m,t]/N + eps)."""
+    M = partials.shape[0]
+    r = torch.empty(M, dtype=torch.float32, device=partials.device) if r is None else r
+    _lib.check("coda_rowscale_reduce", _lib.load().coda_rowscale_reduce(
+        M, N, _ptr(partials), float(eps), _ptr(r), _stream(stream)))
+    return r
+
+
+def gemm_rowscale_swiglu(h, W, r, act=SWIGLU, w_scale=None, y=None, stream=None):
+    """y = act(r * sw * h.W^T); W [2F, K] (SwiGLU: gate rows then up rows) or [N, K]."""
+    M, K = h.shape
+    fp8 = W.element_size() == 1
+    n_w = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("h and W disagree on K")
+    if act == SWIGLU and n_w % 2:
+        raise ValueError("SwiGLU weight needs an even number of rows")
+    n_out = n_w // 2 if act == SWIGLU else n_w
+    y = torch.empty((M, n_out), dtype=torch.bfloat16, device=h.device) if y is None else y
+    _lib.check("coda_gemm_rowscale_swiglu", _lib.load().coda_gemm_rowscale_swiglu(
+        M, n_out, K, act, _ptr(h), _ptr(W), CODA_E4M3 if fp8 else CODA_BF16, _ptr(w_scale),
+        _ptr(r), _ptr(y), _stream(stream)))
+    return y
+
+
+def chain(A, Wo_t, x_res, Wp_t, eps, act=SWIGLU, a_scale=None, wo_scale=None, wp_scale=None,
+          out=None, stream=None):
+    """The three calls in order on one stream.  Returns (h, P, r, y).
+
+    ``out`` may hold preallocated h, partials, r, y tensors (dict)."""
+    out = out or {}
+    h, P = gemm_resid_partialrms(A, Wo_t, x_res, a_scale, wo_scale, out.get("h"),
+                                 out.get("partials"), stream)
+    r = rowscale_reduce(P, Wo_t.shape[0], eps, out.get("r"), stream)
+    y = gemm_rowscale_swiglu(h, Wp_t, r, act, wp_scale, out.get("y"), stream)
+    return h, P, r, y

@@ -1,0 +1,171 @@
+// C ABI of the chain (declared in include/coda.h): host-side validation, then one
+// launcher per call.  Nothing here allocates device memory or synchronises; every
+// check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/coda.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = INT32_MAX;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b) {
+    return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dim_ok(int64_t v, int64_t lo) { return v >= lo && v <= kMaxDim; }
+
+bool prod_ok(int64_t a, int64_t b) {  // a*b elements addressable and below 2^62
+    return a == 0 || b <= (int64_t(1) << 62) / a;
+}
+
+coda_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return CODA_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return CODA_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* coda_version(void) { return "coda-mi355x 0.1 (gfx950)"; }
+
+const char* coda_status_string(coda_status s) {
+    switch (s) {
+        case CODA_OK: return "ok";
+        case CODA_ERR_NULL: return "a required pointer is NULL";
+        case CODA_ERR_SHAPE: return "invalid shape (sign, zero, size limit or granule)";
+        case CODA_ERR_DTYPE: return "unsupported dtype or activation";
+        case CODA_ERR_VALUE: return "invalid value (eps must be finite and >= 0)";
+        case CODA_ERR_ALIAS: return "an output overlaps an input or another output";
+        case CODA_ERR_HIP: return "HIP launch failed (see coda_last_hip_error)";
+        case CODA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+int coda_last_hip_error(void) { return g_last_hip_error; }
+
+int64_t coda_partials_per_row(int64_t N) { return coda::partials_per_row(N); }
+
+coda_status coda_prepare_weight_bf16(int64_t N, int64_t K, const void* W, const float* gamma,
+                                     void* Wp, void* stream) {
+    if (!W || !Wp) return CODA_ERR_NULL;
+    if (!dim_ok(N, 1) || !dim_ok(K, 1) || K % 8 != 0 || !prod_ok(N, K)) return CODA_ERR_SHAPE;
+    if (!aligned16(W) || !aligned16(Wp) || (gamma && !aligned16(gamma))) return CODA_ERR_ALIGN;
+    const Range out = span(Wp, N * K * 2);
+    if (overlap(out, span(W, N * K * 2)) || (gamma && overlap(out, span(gamma, K * 4))))
+        return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_fold_bf16(N, K, W, gamma, Wp, as_stream(stream)));
+}
+
+coda_status coda_quantize_e4m3(int64_t N, int64_t K, const void* X, const float* gamma, void* Q,
+                               float* amax_scale, void* stream) {
+    if (!X || !Q || !amax_scale) return CODA_ERR_NULL;
+    if (!dim_ok(N, 1) || !dim_ok(K, 1) || K % 16 != 0 || !prod_ok(N, K)) return CODA_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(Q) || (gamma && !aligned16(gamma)) || !aligned16(amax_scale))
+        return CODA_ERR_ALIGN;
+    const Range q = span(Q, N * K), sc = span(amax_scale, 8);
+    const Range x = span(X, N * K * 2);
+    if (overlap(q, x) || overlap(sc, x) || overlap(q, sc)) return CODA_ERR_ALIAS;
+    if (gamma) {
+        const Range g = span(gamma, K * 4);
+        if (overlap(q, g) || overlap(sc, g)) return CODA_ERR_ALIAS;
+    }
+    return hip_status(coda::launch_quantize_e4m3(N, K, X, gamma, Q, amax_scale, as_stream(stream)));
+}
+
+coda_status coda_gemm_resid_partialrms(int64_t M, int64_t N, int64_t K, const void* A,
+                                       coda_dtype ab_dtype, const float* a_scale, const void* W,
+                                       const float* w_scale, const void* x_res, void* h,
+                                       float* partials, void* stream) {
+    if (ab_dtype != CODA_BF16 && ab_dtype != CODA_E4M3) return CODA_ERR_DTYPE;
+    const bool fp8 = ab_dtype == CODA_E4M3;
+    if (!dim_ok(M, 0) || !dim_ok(N, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (N % 8 != 0 || K % (fp8 ? 16 : 8) != 0) return CODA_ERR_SHAPE;
+    if (!prod_ok(M, K) || !prod_ok(N, K) || !prod_ok(M, N)) return CODA_ERR_SHAPE;
+    const int64_t T = coda::partials_per_row(N);
+    if (coda::gemm1_tiles(M, N) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;  // empty problem: nothing to enqueue, empty tensors may be NULL
+    if (!A || !W || !h || !partials) return CODA_ERR_NULL;
+    if (fp8 && (!a_scale || !w_scale)) return CODA_ERR_NULL;
+    if (!aligned16(A) || !aligned16(W) || !aligned16(h) || !aligned16(partials) ||
+        (x_res && !aligned16(x_res)))
+        return CODA_ERR_ALIGN;
+    const int64_t eb = fp8 ? 1 : 2;
+    const Range rh = span(h, M * N * 2), rp = span(partials, M * T * 4);
+    const Range ra = span(A, M * K * eb), rw = span(W, N * K * eb);
+    if (overlap(rh, rp) || overlap(rh, ra) || overlap(rh, rw) || overlap(rp, ra) || overlap(rp, rw))
+        return CODA_ERR_ALIAS;
+    if (x_res) {
+        const Range rx = span(x_res, M * N * 2);
+        if (overlap(rp, rx) || (x_res != h && overlap(rh, rx))) return CODA_ERR_ALIAS;
+    }
+    for (const float* s : {a_scale, w_scale})
+        if (s && (overlap(rh, span(s, 4)) || overlap(rp, span(s, 4)))) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_resid_partialrms(int(M), int(N), int(K), A, fp8, a_scale, W,
+                                                         w_scale, x_res, h, partials,
+                                                         as_stream(stream)));
+}
+
+coda_status coda_rowscale_reduce(int64_t M, int64_t N, const float* partials, float eps, float* r,
+                                 void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(N, 1)) return CODA_ERR_SHAPE;
+    const int64_t T = coda::partials_per_row(N);
+    if (!prod_ok(M, T)) return CODA_ERR_SHAPE;
+    if (!std::isfinite(eps) || eps < 0.0f) return CODA_ERR_VALUE;
+    if (M == 0) return CODA_OK;
+    if (!partials || !r) return CODA_ERR_NULL;
+    if (!aligned16(partials) || !aligned16(r)) return CODA_ERR_ALIGN;
+    if (overlap(span(partials, M * T * 4), span(r, M * 4))) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_rowscale_reduce(int(M), int(N), int(T), partials, eps, r,
+                                                   as_stream(stream)));
+}
+
+coda_status coda_gemm_rowscale_swiglu(int64_t M, int64_t N_out, int64_t K, coda_act act,
+                                      const void* h, const void* W, coda_dtype w_dtype,
+                                      const float* w_scale, const float* r, void* y,
+                                      void* stream) {
+    if (act != CODA_ACT_NONE && act != CODA_ACT_SWIGLU) return CODA_ERR_DTYPE;
+    if (w_dtype != CODA_BF16 && w_dtype != CODA_E4M3) return CODA_ERR_DTYPE;
+    const bool fp8 = w_dtype == CODA_E4M3;
+    const bool swiglu = act == CODA_ACT_SWIGLU;
+    if (!dim_ok(M, 0) || !dim_ok(N_out, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (N_out % 8 != 0 || K % (fp8 ? 16 : 8) != 0) return CODA_ERR_SHAPE;
+    const int64_t n_w = swiglu ? 2 * N_out : N_out;
+    if (n_w > kMaxDim || !prod_ok(M, K) || !prod_ok(n_w, K) || !prod_ok(M, N_out))
+        return CODA_ERR_SHAPE;
+    if (coda::gemm3_tiles(M, N_out, swiglu) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;  // empty problem: nothing to enqueue, empty tensors may be NULL
+    if (!h || !W || !r || !y) return CODA_ERR_NULL;
+    if (fp8 && !w_scale) return CODA_ERR_NULL;
+    if (!aligned16(h) || !aligned16(W) || !aligned16(r) || !aligned16(y)) return CODA_ERR_ALIGN;
+    const Range ry = span(y, M * N_out * 2);
+    if (overlap(ry, span(h, M * K * 2)) || overlap(ry, span(W, n_w * K * (fp8 ? 1 : 2))) ||
+        overlap(ry, span(r, M * 4)) || (w_scale && overlap(ry, span(w_scale, 4))))
+        return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_rowscale_swiglu(int(M), int(N_out), int(K), swiglu, h, W, fp8,
+                                                        w_scale, r, y, as_stream(stream)));
+}
+
+}  // extern "C"

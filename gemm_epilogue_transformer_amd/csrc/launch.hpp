@@ -1,0 +1,36 @@
+// Host-side launchers of the chain's kernels (internal to the library).  Arguments are
+// validated by the C ABI layer before any of these is called; each launcher only
+// configures the grid and enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coda {
+
+int64_t partials_per_row(int64_t N);
+
+// Number of workgroups (tiles) each GEMM launches; the ABI checks them against the grid
+// limit before launching.
+int64_t gemm1_tiles(int64_t M, int64_t N);
+int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu);
+
+hipError_t launch_gemm_resid_partialrms(int M, int N, int K, const void* A, bool fp8,
+                                        const float* a_scale, const void* W,
+                                        const float* w_scale, const void* x_res, void* h,
+                                        float* P, hipStream_t stream);
+
+hipError_t launch_rowscale_reduce(int M, int N, int T, const float* P, float eps, float* r,
+                                  hipStream_t stream);
+
+hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, const void* h,
+                                       const void* W, bool w_fp8, const float* w_scale,
+                                       const float* r, void* y, hipStream_t stream);
+
+hipError_t launch_fold_bf16(int64_t N, int64_t K, const void* W, const float* gamma, void* Wp,
+                            hipStream_t stream);
+
+hipError_t launch_quantize_e4m3(int64_t N, int64_t K, const void* X, const float* gamma,
+                                void* Q, float* amax_scale, hipStream_t stream);
+
+}  // namespace coda

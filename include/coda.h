@@ -1,0 +1,153 @@
+/*
+ * coda.h -- C ABI of the MI355X (gfx950) GEMM-epilogue chain
+ *
+ *     h = x_res + A . Wo^T                 (first GEMM, residual add in its epilogue)
+ *     r = 1 / sqrt(mean_n(h^2) + eps)      (RMSNorm row scale, from per-tile partials)
+ *     y = act( r * (h . W'^T) )            (second GEMM, row scale + SwiGLU epilogue)
+ *
+ * with W'[n,k] = gamma[k] * W[n,k] (RMSNorm weight folded into the second weight).
+ *
+ * The chain is the GEMM -> residual -> RMSNorm -> GEMM pattern of the kucoin page
+ * "CODA: new research optimizes Transformer training with GEMM-epilogue programming",
+ * section "CODA: El epilogo esconde un tesoro": the per-row RMSNorm scale r commutes
+ * with the second matrix product, so it is applied at the END of the second GEMM; the
+ * first GEMM's end only produces partial sums of squares, combined by a very light
+ * reduction kernel.  SwiGLU is applied as a pairwise transform in the second GEMM's
+ * epilogue (same section, last paragraph; q2bstudio page: "pairwise transformations").
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or keeps them.  Row-major storage.  Weights are K-contiguous,
+ *    i.e. [out_features, in_features] (the torch.nn.Linear layout).
+ *  - Every tensor pointer must be 16-byte aligned (CODA_ERR_ALIGN otherwise).
+ *  - bf16 = IEEE binary32 truncated to its upper 16 bits (8-bit exponent); e4m3 =
+ *    OCP 8-bit "E4M3FN" (bias 7, max 448, no infinities, NaN = S.1111.111).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only ENQUEUES
+ *    work on that stream and returns; ordering between calls comes from the stream.
+ *    The library never synchronises.
+ *  - Arguments are validated on the host BEFORE anything is enqueued; on any error the
+ *    call returns a non-zero status and enqueues nothing.  A failed launch returns
+ *    CODA_ERR_HIP (the hipError_t is kept per thread, see coda_last_hip_error).  Device
+ *    faults surface at the caller's next synchronisation.  No C++ exception crosses
+ *    this interface.
+ *  - Calls are stateless and may be issued from several host threads.
+ *  - Size limits: every dimension <= 2^31 - 1; M = 0 is a valid empty problem
+ *    (nothing is enqueued, and the M-sized tensors may then be NULL), every other
+ *    dimension must be >= 1.
+ *  - Checks run in the order: dtype/activation codes, shapes, values, (M == 0 ->
+ *    CODA_OK), NULL pointers, alignment, overlap.
+ */
+#ifndef CODA_H_
+#define CODA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CODA_OK = 0,
+    CODA_ERR_NULL = 1,   /* a required pointer is NULL                                   */
+    CODA_ERR_SHAPE = 2,  /* a dimension is negative, zero where >= 1 is needed, too large,
+                            or not a multiple of the granule the call states             */
+    CODA_ERR_DTYPE = 3,  /* unsupported dtype / activation code or combination           */
+    CODA_ERR_VALUE = 4,  /* eps < 0 or not finite                                         */
+    CODA_ERR_ALIAS = 5,  /* an output overlaps an input or another output (other than an
+                            alias the call explicitly allows)                             */
+    CODA_ERR_HIP = 6,    /* the HIP runtime rejected a launch                             */
+    CODA_ERR_ALIGN = 7   /* a tensor pointer is not 16-byte aligned                       */
+} coda_status;
+
+typedef enum { CODA_BF16 = 0, CODA_E4M3 = 1 } coda_dtype;
+typedef enum { CODA_ACT_NONE = 0, CODA_ACT_SWIGLU = 1 } coda_act;
+
+/* ------------------------------------------------------------ weight preparation ----
+ * The RMSNorm weight gamma multiplies the second GEMM's reduction dimension, so it is
+ * a diagonal that folds into the second weight once per weight update (kucoin page,
+ * section "Cinco bloques y un lenguaje LEGO": RMSNorm weights are a broadcast vector
+ * operand).  These calls are the preparation step; they are not part of the chain.
+ */
+
+/* Wp[n,k] = bf16_rne( fl32(gamma[k] * W[n,k]) )   (gamma == NULL: Wp = W)
+ *   W     [N, K] bf16, device, read
+ *   gamma [K] fp32, device, read, or NULL
+ *   Wp    [N, K] bf16, device, written; must not overlap W or gamma
+ * Granule: K % 8 == 0.                                                               */
+coda_status coda_prepare_weight_bf16(int64_t N, int64_t K, const void* W, const float* gamma,
+                                     void* Wp, void* stream);
+
+/* Per-tensor e4m3 quantisation with an fp32 scale (the 8-bit variant of the chain):
+ *   x[n,k]  = fl32(gamma[k] * X[n,k])        (gamma == NULL: x = X)
+ *   amax    = max |x|;   scale = fl32(amax / 448)   (amax == 0: scale = 1)
+ *   Q[n,k]  = e4m3_saturate_rne( fl32(x[n,k] / scale) )
+ *   X          [N, K] bf16, device, read
+ *   gamma      [K] fp32, device, or NULL (used to fold gamma into the second weight
+ *              BEFORE quantising it)
+ *   Q          [N, K] e4m3 (one byte each), device, written
+ *   amax_scale [2] fp32, device, written: {amax, scale}.  Pass &amax_scale[1] as the
+ *              scale argument of the GEMM calls.
+ * Granule: K % 16 == 0.  Enqueues three kernels (clear, max-reduce, quantise).        */
+coda_status coda_quantize_e4m3(int64_t N, int64_t K, const void* X, const float* gamma,
+                               void* Q, float* amax_scale, void* stream);
+
+/* -------------------------------------------------------------------- the chain ---- */
+
+/* Number of per-row partial sums the first GEMM writes for a hidden size N; the caller
+ * sizes `partials` as M * coda_partials_per_row(N) floats.  Returns -1 if N < 1.      */
+int64_t coda_partials_per_row(int64_t N);
+
+/* First GEMM with residual + partial-RMS epilogue (kucoin page, section "CODA: El
+ * epilogo esconde un tesoro": residual add, then only a PARTIAL root-mean-square at the
+ * end of the first GEMM; the combinable partial is the sum of squares over the tile).
+ *   v[m,n]  = sa * sw * sum_k A[m,k] * W[n,k]  +  x_res[m,n]      (fp32 accumulation)
+ *   h[m,n]  = bf16_rne(v[m,n])
+ *   P[m,t]  = sum over the columns n of tile t of h[m,n]^2       (fp32, fixed order)
+ *   A       [M, K]  bf16 or e4m3 (ab_dtype), device
+ *   a_scale device fp32 scalar sa, or NULL (= 1; required for e4m3)
+ *   W       [N, K]  same dtype as A, device
+ *   w_scale device fp32 scalar sw, or NULL (= 1; required for e4m3)
+ *   x_res   [M, N]  bf16, device, or NULL (= 0).  May be EXACTLY equal to h (in place).
+ *   h       [M, N]  bf16, device, written
+ *   partials[M, coda_partials_per_row(N)] fp32, device, written
+ * Granules: N % 8 == 0; K % 8 == 0 (bf16) or K % 16 == 0 (e4m3).                      */
+coda_status coda_gemm_resid_partialrms(int64_t M, int64_t N, int64_t K,
+                                       const void* A, coda_dtype ab_dtype, const float* a_scale,
+                                       const void* W, const float* w_scale,
+                                       const void* x_res, void* h, float* partials,
+                                       void* stream);
+
+/* The light reduction that turns the partials into the row scale:
+ *   r[m] = fl32( 1 / sqrt( (sum_t P[m,t]) / N + eps ) )   (sum and sqrt in fp64)
+ *   partials [M, coda_partials_per_row(N)] fp32, device;  r [M] fp32, device, written.
+ * eps must be finite and >= 0.  A row whose sum and eps are both 0 yields +inf.       */
+coda_status coda_rowscale_reduce(int64_t M, int64_t N, const float* partials, float eps,
+                                 float* r, void* stream);
+
+/* Second GEMM with row-scale (+SwiGLU) epilogue.  z = sw * (h . W^T), with gamma
+ * already folded into W:
+ *   CODA_ACT_NONE:   W [N_out, K];   y[m,n] = bf16_rne( r[m] * z[m,n] )
+ *   CODA_ACT_SWIGLU: W [2*N_out, K], rows [0, N_out) = gate, [N_out, 2*N_out) = up;
+ *                    g = r[m]*z[m,j], u = r[m]*z[m,N_out+j],
+ *                    y[m,j] = bf16_rne( g / (1 + exp(-g)) * u )
+ *   (r multiplies both halves BEFORE the SiLU: it commutes with the GEMM, not with SiLU.)
+ *   h       [M, K] bf16, device (the first call's output)
+ *   W       bf16 or e4m3 (w_dtype; e4m3 = weight-only 8-bit, decoded exactly to bf16)
+ *   w_scale device fp32 scalar sw, or NULL (= 1; required for e4m3)
+ *   r       [M] fp32, device
+ *   y       [M, N_out] bf16, device, written; must not overlap any input
+ * Granules: K % 8 == 0 (bf16 W) or K % 16 == 0 (e4m3 W); N_out % 8 == 0.              */
+coda_status coda_gemm_rowscale_swiglu(int64_t M, int64_t N_out, int64_t K, coda_act act,
+                                      const void* h, const void* W, coda_dtype w_dtype,
+                                      const float* w_scale, const float* r, void* y,
+                                      void* stream);
+
+/* ------------------------------------------------------------------- utilities ---- */
+const char* coda_status_string(coda_status s);
+int coda_last_hip_error(void);      /* hipError_t of this thread's last CODA_ERR_HIP      */
+const char* coda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CODA_H_ */

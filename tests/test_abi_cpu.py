@@ -1,0 +1,132 @@
+"""The C ABI library loads, exports every symbol include/coda.h declares, and rejects
+invalid arguments with the documented status codes before enqueuing anything.
+
+No compute call is made here.  The validation cases pass fake (but aligned) addresses;
+they only run on hosts WITHOUT a GPU so that a validation mistake could never turn into
+a launch on fake pointers.
+"""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+from gemm_epilogue_transformer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coda.h")
+
+OK, NULL, SHAPE, DTYPE, VALUE, ALIAS, HIP, ALIGN = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(coda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_chain_calls():
+    names = declared_functions()
+    for n in ("coda_gemm_resid_partialrms", "coda_rowscale_reduce", "coda_gemm_rowscale_swiglu"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_utilities():
+    L = _lib.load()
+    assert b"gfx950" in L.coda_version()
+    for s in range(8):
+        assert L.coda_status_string(s)
+    assert L.coda_partials_per_row(0) == -1
+    assert L.coda_partials_per_row(1) == 1
+    T = L.coda_partials_per_row(2048)
+    assert T >= 1 and 2048 % T == 0
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="fake-pointer validation cases run on GPU-less hosts only")
+
+# fake, 16-byte aligned, far apart device addresses
+P1, P2, P3, P4, P5, P6 = (0x10000000 * (i + 1) for i in range(6))
+
+
+@no_gpu
+def test_gemm1_validation():
+    f = _lib.load().coda_gemm_resid_partialrms
+    # M, N, K, A, dt, sa, W, sw, x, h, P, stream
+    assert f(16, 64, 64, None, 0, None, P2, None, P3, P4, P5, None) == NULL
+    assert f(16, 64, 64, P1, 0, None, P2, None, P3, None, P5, None) == NULL
+    assert f(16, 64, 64, P1, 1, None, P2, P6, P3, P4, P5, None) == NULL     # e4m3 needs scales
+    assert f(16, 64, 64, P1, 7, None, P2, None, P3, P4, P5, None) == DTYPE
+    assert f(-1, 64, 64, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE
+    assert f(16, 0, 64, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE
+    assert f(16, 64, 0, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE
+    assert f(16, 60, 64, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE  # N % 8
+    assert f(16, 64, 60, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE  # K % 8
+    assert f(16, 64, 24, P1, 1, P6, P2, P6, P3, P4, P5, None) == SHAPE      # e4m3 K % 16
+    assert f(1 << 31, 64, 64, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE
+    assert f(16, 64, 64, P1 + 8, 0, None, P2, None, P3, P4, P5, None) == ALIGN
+    assert f(16, 64, 64, P1, 0, None, P2, None, P3, P4, P5 + 4, None) == ALIGN
+    assert f(16, 64, 64, P1, 0, None, P2, None, P3, P1, P5, None) == ALIAS   # h over A
+    assert f(16, 64, 64, P1, 0, None, P2, None, P3, P4, P4 + 16, None) == ALIAS  # P over h
+    assert f(16, 64, 64, P1, 0, None, P2, None, P4 + 16, P4, P5, None) == ALIAS  # partial alias
+    # the exact alias h == x_res is allowed; M == 0 enqueues nothing and succeeds
+    assert f(0, 64, 64, P1, 0, None, P2, None, P4, P4, P5, None) == OK
+
+
+@no_gpu
+def test_rowscale_validation():
+    f = _lib.load().coda_rowscale_reduce
+    assert f(16, 64, None, 1e-5, P2, None) == NULL
+    assert f(16, 0, P1, 1e-5, P2, None) == SHAPE
+    assert f(16, 64, P1, -1.0, P2, None) == VALUE
+    assert f(16, 64, P1, float("nan"), P2, None) == VALUE
+    assert f(16, 64, P1, float("inf"), P2, None) == VALUE
+    assert f(16, 64, P1, 1e-5, P1, None) == ALIAS
+    assert f(16, 64, P1 + 4, 1e-5, P2, None) == ALIGN
+    assert f(0, 64, P1, 1e-5, P2, None) == OK
+
+
+@no_gpu
+def test_gemm2_validation():
+    f = _lib.load().coda_gemm_rowscale_swiglu
+    # M, N_out, K, act, h, W, wdt, sw, r, y, stream
+    assert f(16, 64, 64, 1, None, P2, 0, None, P3, P4, None) == NULL
+    assert f(16, 64, 64, 1, P1, P2, 1, None, P3, P4, None) == NULL           # e4m3 needs scale
+    assert f(16, 64, 64, 2, P1, P2, 0, None, P3, P4, None) == DTYPE
+    assert f(16, 64, 64, 1, P1, P2, 3, None, P3, P4, None) == DTYPE
+    assert f(16, 60, 64, 1, P1, P2, 0, None, P3, P4, None) == SHAPE
+    assert f(16, 64, 8, 1, P1, P2, 1, P5, P3, P4, None) == SHAPE             # e4m3 K % 16
+    assert f(16, 1 << 30, 64, 1, P1, P2, 0, None, P3, P4, None) == SHAPE     # 2F too large
+    assert f(16, 64, 64, 1, P1, P2, 0, None, P3, P1, None) == ALIAS          # y over h
+    assert f(16, 64, 64, 1, P1, P2, 0, None, P3, P3, None) == ALIAS          # y over r
+    assert f(16, 64, 64, 1, P1, P2, 0, None, P3 + 8, P4, None) == ALIGN
+    assert f(0, 64, 64, 1, P1, P2, 0, None, P3, P4, None) == OK
+
+
+@no_gpu
+def test_prepare_validation():
+    L = _lib.load()
+    assert L.coda_prepare_weight_bf16(8, 64, None, None, P2, None) == NULL
+    assert L.coda_prepare_weight_bf16(8, 60, P1, None, P2, None) == SHAPE
+    assert L.coda_prepare_weight_bf16(8, 64, P1, None, P1, None) == ALIAS
+    assert L.coda_prepare_weight_bf16(8, 64, P1, P3 + 4, P2, None) == ALIGN
+    assert L.coda_quantize_e4m3(8, 64, P1, None, P2, None, None) == NULL
+    assert L.coda_quantize_e4m3(8, 40, P1, None, P2, P3, None) == SHAPE
+    assert L.coda_quantize_e4m3(8, 64, P1, None, P2, P2, None) == ALIAS
+    assert L.coda_quantize_e4m3(8, 64, P1, None, P2, P1 + 16, None) == ALIAS
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

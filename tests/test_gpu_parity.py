@@ -1,0 +1,234 @@
+"""GPU parity of the HIP chain against the fp64 oracle (through the C ABI).
+
+Small shapes are compared on every row; the full-size workloads on sampled rows (the
+oracle computes those rows one by one) plus properties checked on every row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_epilogue_transformer_amd as coda
+import oracle
+import synth_inputs as si
+from harness import (check_chain, dev_bf16, gpu_chain, gpu_prepare, host_bits, sample_rows,
+                     upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------- weight preparation ----
+
+@pytest.mark.parametrize("N,K", [(8, 8), (3, 64), (200, 136), (1024, 2048)])
+def test_fold_bf16_bit_exact(N, K):
+    w = si.custom(4, 16, K, N, si.ACT_NONE, seed=N + K)
+    inp = si.generate(w)
+    d = upload(inp)
+    Wp = coda.prepare_weight_bf16(d["W_t"], d["gamma"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(Wp), oracle.fold_bf16(inp["W_t"], inp["gamma"]))
+    Wc = coda.prepare_weight_bf16(d["W_t"], None)
+    assert np.array_equal(host_bits(Wc), inp["W_t"])
+
+
+@pytest.mark.parametrize("N,K,fold", [(1, 16, False), (37, 48, True), (256, 1024, True),
+                                      (16384, 2048, True), (2048, 2048, False)])
+def test_quantize_e4m3_bit_exact(N, K, fold):
+    w = si.custom(4, 16, K, N, si.ACT_NONE, seed=3 * N + K)
+    inp = si.generate(w)
+    d = upload(inp)
+    q, sc = coda.quantize_e4m3(d["W_t"], d["gamma"] if fold else None)
+    torch.cuda.synchronize()
+    qo, amax, scale = oracle.quant_e4m3(inp["W_t"], inp["gamma"] if fold else None)
+    sc = sc.cpu().numpy()
+    assert sc[0] == amax and sc[1] == scale
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_quantize_e4m3_every_code_and_tie():
+    # amax = 448 makes the scale exactly 1, so every e4m3 value, every midpoint between
+    # neighbours and the bf16 values one ulp either side of it reach the GPU encoder
+    # unchanged; its codes must equal the oracle's.
+    codes = np.arange(0x7F, dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    mids = oracle.bf16_encode((vals[:-1] + vals[1:]) / 2)
+    near = np.concatenate([mids[mids > 0] + np.uint16(1), mids[mids > 0] - np.uint16(1)])
+    pos = np.concatenate([oracle.bf16_encode(vals), mids, near])
+    bits = np.concatenate([pos, pos | np.uint16(0x8000)])
+    K = ((bits.size + 15) // 16) * 16
+    row = np.zeros(K, np.uint16)
+    row[: bits.size] = bits
+    X = np.stack([row, row[::-1].copy()])
+    q, sc = coda.quantize_e4m3(dev_bf16(X))
+    torch.cuda.synchronize()
+    qo, amax, scale = oracle.quant_e4m3(X, None)
+    assert amax == 448.0 and scale == 1.0
+    assert sc.cpu().numpy()[1] == scale
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+# ---------------------------------------------------------------------- the chain ----
+
+SMALL = [
+    # M, K1, d, N2w, act, dtype: several tiles and ragged tails in every dimension
+    (128, 256, 256, 512, si.ACT_NONE, "bf16"),
+    (300, 136, 200, 2 * 104, si.ACT_SWIGLU, "bf16"),
+    (257, 72, 264, 392, si.ACT_NONE, "bf16"),
+    (1, 8, 8, 16, si.ACT_SWIGLU, "bf16"),
+    (130, 64, 144, 2 * 72, si.ACT_SWIGLU, "e4m3"),
+    (333, 272, 528, 2 * 200, si.ACT_SWIGLU, "e4m3"),
+    (64, 48, 128, 136, si.ACT_NONE, "e4m3"),
+]
+
+
+@pytest.mark.parametrize("M,K1,d,N2w,act,dtype", SMALL)
+def test_chain_small_all_rows(M, K1, d, N2w, act, dtype):
+    w = si.custom(M, K1, d, N2w, act, seed=M * 7 + d, dtype=dtype)
+    _log(f"chain small {w.name} {dtype}")
+    inp = si.generate(w)
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    h, P, r, y = gpu_chain(w, dd, prep)
+    torch.cuda.synchronize()
+    assert P.shape == (M, coda.partials_per_row(d))
+    check_chain(w, inp, h, P, r, y)
+
+
+def test_tiny_workload_all_rows():
+    w = si.WORKLOADS[1]
+    inp = si.generate(w)
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    h, P, r, y = gpu_chain(w, dd, prep)
+    torch.cuda.synchronize()
+    stats = check_chain(w, inp, h, P, r, y)
+    _log(f"tiny workload: {stats}")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_workload_sampled_rows(cfg):
+    w = si.WORKLOADS[cfg]
+    _log(f"full workload {cfg} {w.name}: generating")
+    inp = si.generate(w)
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    h, P, r, y = gpu_chain(w, dd, prep)
+    torch.cuda.synchronize()
+    _log(f"full workload {cfg}: gpu done; oracle on sampled rows")
+    rows = sample_rows(w.M, 40, seed=cfg)
+    stats = check_chain(w, inp, h, P, r, y, rows=rows)
+    _log(f"full workload {cfg}: {stats}")
+    # properties on every row: finite outputs, partials consistent with h, r from partials
+    hf = h.float()
+    s = (hf.double() ** 2).sum(1)
+    Ps = P.double().sum(1)
+    assert torch.allclose(Ps, s, rtol=w.d * 2.0 ** -24, atol=0)
+    r64 = 1.0 / torch.sqrt(Ps / w.d + float(np.float32(w.eps)))
+    assert torch.allclose(r.double(), r64, rtol=2.5e-7, atol=0)
+    assert torch.isfinite(y.float()).all()
+
+
+# ------------------------------------------------------------- metamorphic / edges ----
+
+def _small(act=si.ACT_SWIGLU, dtype="bf16", M=200, seed=1):
+    return si.custom(M, 96, 136, 2 * 88 if act == si.ACT_SWIGLU else 176, act, seed=seed, dtype=dtype)
+
+
+def test_deterministic_bitwise():
+    w = _small()
+    inp = si.generate(w)
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    o1 = [t.clone() for t in gpu_chain(w, dd, prep)]
+    o2 = gpu_chain(w, dd, prep)
+    torch.cuda.synchronize()
+    for a, b in zip(o1, o2):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_zero_first_weight_gives_residual_exactly():
+    w = _small()
+    inp = si.generate(w)
+    inp["Wo_t"][:] = 0
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    h, P, r, y = gpu_chain(w, dd, prep)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(h), inp["x_res"])
+    check_chain(w, inp, h, P, r, y)
+
+
+def test_zero_gate_gives_zero_output():
+    w = _small()
+    inp = si.generate(w)
+    inp["W_t"][: w.n_out] = 0
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    h, P, r, y = gpu_chain(w, dd, prep)
+    torch.cuda.synchronize()
+    assert torch.all(y.float() == 0)
+
+
+def test_no_residual_and_in_place_residual():
+    w = _small(act=si.ACT_NONE)
+    inp = si.generate(w)
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    # x_res = NULL: h = A.W^T
+    h, P, r, y = gpu_chain(w, dd, prep, x_res=None)
+    torch.cuda.synchronize()
+    inp0 = dict(inp, x_res=np.zeros_like(inp["x_res"]))
+    check_chain(w, inp0, h, P, r, y)
+    # h written over x_res (the one alias the ABI allows)
+    buf = dd["x_res"].clone()
+    h2, P2, r2, y2 = gpu_chain(w, dd, prep, x_res=buf, h_out=buf)
+    torch.cuda.synchronize()
+    assert h2.data_ptr() == buf.data_ptr()
+    check_chain(w, inp, h2, P2, r2, y2)
+
+
+def test_scale_invariance_at_zero_eps():
+    # inputs x2 (exact in bf16) and eps = 0: hb doubles exactly, r halves, y is unchanged
+    w = si.custom(160, 64, 128, 2 * 64, si.ACT_SWIGLU, seed=5, eps=0.0)
+    inp = si.generate(w)
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    h1, P1, r1, y1 = [t.clone() for t in gpu_chain(w, dd, prep)]
+    inp2 = dict(inp, A=inp["A"] + np.uint16(0x80), x_res=inp["x_res"] + np.uint16(0x80))
+    dd2 = upload(inp2)
+    prep2 = gpu_prepare(w, dd2)
+    h2, P2, r2, y2 = gpu_chain(w, dd2, prep2)
+    torch.cuda.synchronize()
+    assert torch.equal(h2.float(), 2 * h1.float())
+    assert torch.equal(P2, 4 * P1)
+    assert torch.equal(r2, r1 / 2)
+    assert torch.equal(y2.view(torch.int16), y1.view(torch.int16))
+
+
+def test_empty_m_is_a_no_op():
+    w = _small(M=1)
+    inp = si.generate(w)
+    dd = upload(inp)
+    prep = gpu_prepare(w, dd)
+    A0 = prep["A"][:0]
+    h, P = coda.gemm_resid_partialrms(A0, prep["Wo"], dd["x_res"][:0])
+    r = coda.rowscale_reduce(P, w.d, w.eps)
+    y = coda.gemm_rowscale_swiglu(h, prep["Wp"], r, act=w.act)
+    torch.cuda.synchronize()
+    assert h.shape[0] == 0 and y.shape[0] == 0
+
+
+def test_binding_rejects_bad_arguments_on_device():
+    w = _small()
+    inp = si.generate(w)
+    dd = upload(inp)
+    with pytest.raises(coda.CodaError) as e:
+        coda.gemm_resid_partialrms(dd["A"], dd["Wo_t"], dd["x_res"], h=dd["A"])
+    assert e.value.status == 5
+    with pytest.raises(coda.CodaError) as e:
+        coda.rowscale_reduce(torch.zeros((4, coda.partials_per_row(w.d)), device="cuda"), w.d, -1.0)
+    assert e.value.status == 4
