@@ -80,16 +80,24 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
 
     prep = oracle.prepare(inp, w.dtype)
     per_row = 2 * (w.K1 * w.d + w.d * w.N2w)
-    rows = np.arange(2)
-    t0 = time.perf_counter()
-    oracle.chain(prep, inp["x_res"], inp["gamma"], w.act, w.eps, rows=rows)
-    t_probe = time.perf_counter() - t0
-    n = int(max(4, min(w.M, 2 * target_s / max(t_probe, 1e-3))))
     rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(w.M, size=n, replace=False))
-    t0 = time.perf_counter()
-    oracle.chain(prep, inp["x_res"], inp["gamma"], w.act, w.eps, rows=rows)
-    dt = time.perf_counter() - t0
+    # grow the sample until one call takes >= 1/4 of the target, then size it to the target
+    n, dt = 8, 0.0
+    while True:
+        rows = np.sort(rng.choice(w.M, size=min(n, w.M), replace=False))
+        t0 = time.perf_counter()
+        oracle.chain(prep, inp["x_res"], inp["gamma"], w.act, w.eps, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or n >= w.M:
+            break
+        n *= 4
+    if dt < target_s / 2 and n < w.M:
+        n = int(min(w.M, n * target_s / dt))
+        rows = np.sort(rng.choice(w.M, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.chain(prep, inp["x_res"], inp["gamma"], w.act, w.eps, rows=rows)
+        dt = time.perf_counter() - t0
+    n = rows.size
     return {"value": round(n * per_row / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{n} random rows of the {w.M}-row workload in one oracle call "

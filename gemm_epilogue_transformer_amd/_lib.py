@@ -8,7 +8,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcoda.so")
+LIB_PATH = os.environ.get("CODA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcoda.so")
 
 CODA_OK = 0
 STATUS_NAMES = {0: "CODA_OK", 1: "CODA_ERR_NULL", 2: "CODA_ERR_SHAPE", 3: "CODA_ERR_DTYPE",

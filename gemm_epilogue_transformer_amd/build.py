@@ -40,15 +40,16 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def build(verbose: bool = False, save_temps: bool = False) -> str:
+def build(verbose: bool = False, save_temps: bool = False, defines=(), out: str = LIB,
+          build_dir: str = BUILD) -> str:
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     objs = []
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc, *HIPCC_FLAGS, *(f"-D{d}" for d in defines), "-c", src, "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         if save_temps:
@@ -66,13 +67,13 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
 
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -14,6 +14,9 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxDim = INT32_MAX;
+// The kernels address one block tile (up to 256 rows) of any operand through a 32-bit
+// buffer offset range below 2^31, so row lengths are capped at 2^22 elements.
+constexpr int64_t kMaxRow = int64_t(1) << 22;
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -102,7 +105,7 @@ coda_status coda_gemm_resid_partialrms(int64_t M, int64_t N, int64_t K, const vo
     if (ab_dtype != CODA_BF16 && ab_dtype != CODA_E4M3) return CODA_ERR_DTYPE;
     const bool fp8 = ab_dtype == CODA_E4M3;
     if (!dim_ok(M, 0) || !dim_ok(N, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
-    if (N % 8 != 0 || K % (fp8 ? 16 : 8) != 0) return CODA_ERR_SHAPE;
+    if (N % 8 != 0 || K % (fp8 ? 16 : 8) != 0 || N > kMaxRow || K > kMaxRow) return CODA_ERR_SHAPE;
     if (!prod_ok(M, K) || !prod_ok(N, K) || !prod_ok(M, N)) return CODA_ERR_SHAPE;
     const int64_t T = coda::partials_per_row(N);
     if (coda::gemm1_tiles(M, N) > kMaxDim) return CODA_ERR_SHAPE;
@@ -151,7 +154,8 @@ coda_status coda_gemm_rowscale_swiglu(int64_t M, int64_t N_out, int64_t K, coda_
     const bool fp8 = w_dtype == CODA_E4M3;
     const bool swiglu = act == CODA_ACT_SWIGLU;
     if (!dim_ok(M, 0) || !dim_ok(N_out, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
-    if (N_out % 8 != 0 || K % (fp8 ? 16 : 8) != 0) return CODA_ERR_SHAPE;
+    if (N_out % 8 != 0 || K % (fp8 ? 16 : 8) != 0 || N_out > kMaxRow || K > kMaxRow)
+        return CODA_ERR_SHAPE;
     const int64_t n_w = swiglu ? 2 * N_out : N_out;
     if (n_w > kMaxDim || !prod_ok(M, K) || !prod_ok(n_w, K) || !prod_ok(M, N_out))
         return CODA_ERR_SHAPE;

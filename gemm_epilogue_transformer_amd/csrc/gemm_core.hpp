@@ -7,9 +7,8 @@
 // Block tile BM x BN, 256 threads = 4 waves arranged WAVES_M x WAVES_N; each wave owns
 // a (BM/WAVES_M) x (BN/WAVES_N) sub-tile made of 32x32 MFMA blocks.  One k-tile is 128
 // BYTES of every row (64 bf16 or 128 e4m3 values).  LDS holds two k-tiles (double
-// buffer).  Inside a row the eight 16-byte chunks are XOR-swizzled with (row & 7), so
-// the 32 lanes that read 32 consecutive rows at the same chunk hit 8 distinct chunk
-// slots of every 8-row group (no bank conflicts for ds_read_b128).
+// buffer).  Inside a row the eight 16-byte chunks are XOR-swizzled with ((row >> 1) & 7)
+// (see lds_off), so fragment reads are free of bank conflicts.
 //
 // MFMA output layout (32x32 blocks): lane l, accumulator i holds
 //   row (A side) = 8*(i/4) + 4*(l/32) + (i%4),   column (B side) = l % 32.
@@ -22,8 +21,11 @@ namespace coda {
 constexpr int kRowBytes = 128;   // bytes of one row per k-tile
 constexpr int kThreads = 256;
 
+// 16-byte chunk c of a 128-byte row r sits in slot c ^ ((r >> 1) & 7): the 16 lanes the
+// 64-bank LDS serves together read 16 consecutive rows at one chunk and hit 16 distinct
+// 16-byte bank groups.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+    return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 // Operand kinds -------------------------------------------------------------------

@@ -2,30 +2,34 @@
 //
 //   v[m,n] = sa*sw * sum_k A[m,k] W[n,k] + x_res[m,n];   h = bf16_rne(v)
 //   P[m,t] = sum over the tile's columns n of h[m,n]^2   (one fp32 partial per row and
-//            N-tile, reduced in a fixed order: in lane, across the 32 lanes of a row,
-//            then across the waves that share the row)
+//            N-tile, reduced in a fixed order: 8 columns in lane, a butterfly over the
+//            lanes that hold one row of a wave's slab, then the waves sharing the row)
 //
 // The output tile never leaves the chip between the accumulate and the epilogue (kucoin
 // page, section "CODA: El epilogo esconde un tesoro": the matrix product's result still
 // lives in registers when the epilogue runs; RMSNorm only needs a PARTIAL root mean
 // square at the end of the first GEMM, here the combinable sum of squares).
-#include "gemm_core.hpp"
+#include "epilogue.hpp"
+#include "gemm_pipeline.hpp"
 #include "launch.hpp"
 
 namespace coda {
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, Elt E>
-__global__ void __launch_bounds__(kThreads, 2)
+template <int BM, int BN, int OCC, Elt E>
+__global__ void __launch_bounds__(kThreads, OCC)
 k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
                         const float* __restrict__ a_scale, const float* __restrict__ w_scale,
                         const uint16_t* x_res, uint16_t* h, float* __restrict__ P,
                         int M, int N, int K, int tiles_m, int tiles_n) {
+    constexpr int WAVES_M = 2, WAVES_N = 2;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int EB = EltInfo<E>::kBytes;
-    static_assert(WAVES_M * WAVES_N * kWave == kThreads, "4 waves");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BM + BN) * kRowBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[(BM + BN) * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[(BM + BN) * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[(BM + BN) * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[(BM + BN) * kTileBytes];
     __shared__ float red[WAVES_N][BM];
 
     int tile_m, tile_n;
@@ -34,16 +38,13 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    const size_t kbytes_row = static_cast<size_t>(K) * EB;
     const int kbytes = K * EB;
-    auto a_ptr = [&](int r) -> const uint8_t* {
-        const int m = m0 + r;
-        return m < M ? A + static_cast<size_t>(m) * kbytes_row : nullptr;
-    };
-    auto b_ptr = [&](int r) -> const uint8_t* {
-        const int n = n0 + r;
-        return n < N ? W + static_cast<size_t>(n) * kbytes_row : nullptr;
-    };
+    DmaPanel<BM, BM> pa;
+    DmaPanel<BN, BN> pb;
+    const uint8_t* a0 = A + static_cast<size_t>(m0) * kbytes;
+    const uint8_t* b0 = W + static_cast<size_t>(n0) * kbytes;
+    pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
+    pb.init(b0, min(BN, N - n0), b0, 0, kbytes);
     auto a_row = [&](int tm) { return wm * WM + tm * 32; };
     auto b_row = [&](int tn) { return wn * WN + tn * 32; };
 
@@ -55,77 +56,64 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    PanelStage<BM> sa;
-    PanelStage<BN> sb;
-    const int nk = (kbytes + kRowBytes - 1) / kRowBytes;
-    if (nk > 0) {
-        sa.load(a_ptr, 0, kbytes);
-        sb.load(b_ptr, 0, kbytes);
-        sa.store(smem[0]);
-        sb.store(smem[0] + BM * kRowBytes);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            sa.load(a_ptr, (kt + 1) * kRowBytes, kbytes);
-            sb.load(b_ptr, (kt + 1) * kRowBytes, kbytes);
-        }
-        WaveMma<E, TM, TN>::run(acc, smem[cur], smem[cur] + BM * kRowBytes, a_row, b_row);
-        if (kt + 1 < nk) {
-            sa.store(smem[cur ^ 1]);
-            sb.store(smem[cur ^ 1] + BM * kRowBytes);
-        }
-        __syncthreads();
-    }
+    mainloop_dma<E, BM, BN, BN>(acc, pa, pb, kbytes, st0, st1, st2, st3, a_row, b_row);
 
     // ---------------------------------------------------------------- epilogue ----
+    // Per 32-row slab of this wave: stage scale*acc row-major in the wave's own (now
+    // free) LDS stage, then each lane takes runs of 8 columns: 16-byte residual load,
+    // fp32 add, one bf16 rounding, 16-byte store of h, and the sum of the 8 squares.
+    // Row sums: 16 lanes hold one slab row -> butterfly over them -> per-wave partial in
+    // `red`, then the WAVES_N waves sharing a row are added in a fixed order.
     const float scale = (a_scale ? *a_scale : 1.0f) * (w_scale ? *w_scale : 1.0f);
-    const int lr = lane & 31, lh = lane >> 5;
-    float rs[TM][16];
+    using S = Slab<TN>;
+    static_assert(S::kBytes <= (BM + BN) * kTileBytes, "slab fits one stage");
+    uint8_t* slab = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    const int valid_rows = min(BM, M - m0);
+    const uint32_t row_bytes = static_cast<uint32_t>(N) * 2;
+    const size_t tile_off = static_cast<size_t>(m0) * N;
+    const __amdgpu_buffer_rsrc_t xr_rsrc =
+        make_buffer_rsrc(x_res ? x_res + tile_off : h + tile_off, x_res ? valid_rows * row_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t h_rsrc = make_buffer_rsrc(h + tile_off, valid_rows * row_bytes);
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+    for (int tm = 0; tm < TM; ++tm) {
+        float v[TN][16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) rs[tm][i] = 0.0f;
-
+        for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+            for (int i = 0; i < 16; ++i) v[tn][i] = acc[tm][tn][i] * scale;
+        S::put(slab, v);
+        uint32_t voff[S::kSegPerLane];
+        i32x4_t xr[S::kSegPerLane];
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const int n = n0 + wn * WN + tn * 32 + lr;
+        for (int j = 0; j < S::kSegPerLane; ++j) {
+            const int tr = wm * WM + tm * 32 + S::seg_row(j);
+            const int n = n0 + wn * WN + S::seg_col(j);
+            voff[j] = n < N ? static_cast<uint32_t>(tr) * row_bytes + static_cast<uint32_t>(n) * 2 : kOobOffset;
+            xr[j] = __builtin_amdgcn_raw_buffer_load_b128(xr_rsrc, voff[j], 0, 0);
+        }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = m0 + wm * WM + tm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                if (m < M && n < N) {
-                    const size_t off = static_cast<size_t>(m) * N + n;
-                    float v = acc[tm][tn][i] * scale;
-                    if (x_res) v += bf16_bits_to_f32(x_res[off]);
-                    const uint16_t hb = f32_to_bf16_bits(v);
-                    h[off] = hb;
-                    const float q = bf16_bits_to_f32(hb);
-                    rs[tm][i] += q * q;
-                }
+        for (int j = 0; j < S::kSegPerLane; ++j) {
+            float t[8];
+            S::get(slab, j, t);
+            float sq = 0.0f;
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = static_cast<uint32_t>(xr[j][e]);
+                const uint16_t h0 = f32_to_bf16_bits(t[2 * e] + bf16_bits_to_f32(static_cast<uint16_t>(x & 0xFFFFu)));
+                const uint16_t h1 = f32_to_bf16_bits(t[2 * e + 1] + bf16_bits_to_f32(static_cast<uint16_t>(x >> 16)));
+                const float q0 = bf16_bits_to_f32(h0), q1 = bf16_bits_to_f32(h1);
+                sq += q0 * q0;
+                sq += q1 * q1;
+                o[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
             }
+            __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])},
+                                                   h_rsrc, voff[j], 0, 0);
+            // columns past N contribute nothing (their residual reads and sums are zero)
+#pragma unroll
+            for (int off = S::kSegPerRow / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, S::kSegPerRow);
+            if ((lane & (S::kSegPerRow - 1)) == 0) red[wn][wm * WM + tm * 32 + S::seg_row(j)] = sq;
         }
-    // sum over the 32 lanes that hold one row's columns
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float v = rs[tm][i];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 8, 64);
-            v += __shfl_xor(v, 4, 64);
-            v += __shfl_xor(v, 2, 64);
-            v += __shfl_xor(v, 1, 64);
-            rs[tm][i] = v;
-        }
-    if (lr == 0) {
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                red[wn][wm * WM + tm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3)] = rs[tm][i];
     }
     __syncthreads();
     const int T = tiles_n;
@@ -140,9 +128,14 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     }
 }
 
-// Tile configuration of the first GEMM.  The partial count per row is the number of
-// N-tiles, so it is fixed by BN1.
-constexpr int BM1 = 128, BN1 = 128;
+// Tile configuration of the first GEMM (compile-time).  The partial count per row is the
+// number of N-tiles, so it is fixed by BN1.
+#ifndef CODA_G1_BM
+#define CODA_G1_BM 256
+#define CODA_G1_BN 256
+#define CODA_G1_OCC 1
+#endif
+constexpr int BM1 = CODA_G1_BM, BN1 = CODA_G1_BN, OCC1 = CODA_G1_OCC;
 
 int64_t partials_per_row(int64_t N) { return N < 1 ? -1 : (N + BN1 - 1) / BN1; }
 
@@ -155,12 +148,12 @@ hipError_t launch_gemm_resid_partialrms(int M, int N, int K, const void* A, bool
     const int tiles_m = (M + BM1 - 1) / BM1, tiles_n = (N + BN1 - 1) / BN1;
     const dim3 grid(tiles_m * tiles_n), block(kThreads);
     if (fp8) {
-        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, 2, 2, Elt::E4M3>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, OCC1, Elt::E4M3>), grid, block, 0,
                            stream, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W),
                            a_scale, w_scale, static_cast<const uint16_t*>(x_res),
                            static_cast<uint16_t*>(h), P, M, N, K, tiles_m, tiles_n);
     } else {
-        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, 2, 2, Elt::BF16>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, OCC1, Elt::BF16>), grid, block, 0,
                            stream, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W),
                            a_scale, w_scale, static_cast<const uint16_t*>(x_res),
                            static_cast<uint16_t*>(h), P, M, N, K, tiles_m, tiles_n);

@@ -15,52 +15,113 @@
 //
 // 8-bit weights (weight-only): W is e4m3 in HBM and decoded exactly to bf16 while it is
 // staged into LDS; the MFMA is the bf16 one and sw is applied in the epilogue.
-#include "gemm_core.hpp"
+#include "epilogue.hpp"
+#include "gemm_pipeline.hpp"
 #include "launch.hpp"
 
 namespace coda {
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, bool WFP8>
-__global__ void __launch_bounds__(kThreads, 2)
+// Epilogue shared by both variants.  Wave (wm, wn) holds TM x TN 32x32 accumulator blocks;
+// with SwiGLU, blocks [0, TN/2) are gate columns and [TN/2, TN) the matching up columns.
+// Per 32-row slab: r (times sw) is applied lane-locally to both accumulators before the
+// SiLU; the finished fp32 outputs are staged row-major in the wave's LDS region `slab`
+// and written as 16-byte runs of 8 bf16.  Rows / columns outside y are masked by the
+// buffer range check.
+template <int BM, int BN, int TM, int TN, bool SWIGLU>
+__device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
+                                                  const float* __restrict__ R, float sw,
+                                                  uint16_t* __restrict__ Y, int M, int N_out,
+                                                  int m0, int j0, int wm, int wn, uint8_t* slab) {
+    constexpr int WM = BM / 2;
+    constexpr int NB = SWIGLU ? TN / 2 : TN;          // output blocks per wave
+    using S = Slab<NB>;
+    const int lane = threadIdx.x & 63;
+    const int lh = lane >> 5;
+    const int valid_rows = min(BM, M - m0);
+    const uint32_t row_bytes = static_cast<uint32_t>(N_out) * 2;
+    const __amdgpu_buffer_rsrc_t r_rsrc = make_buffer_rsrc(R + m0, static_cast<uint32_t>(valid_rows) * 4);
+    const __amdgpu_buffer_rsrc_t y_rsrc =
+        make_buffer_rsrc(Y + static_cast<size_t>(m0) * N_out, static_cast<uint32_t>(valid_rows) * row_bytes);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        // r of the 16 rows this lane holds: rows 8g + 4*lh + (0..3), g = 0..3
+        float rr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t row = static_cast<uint32_t>(wm * WM + tm * 32 + 8 * g + 4 * lh);
+            const i32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(r_rsrc, row * 4, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rr[4 * g + e] = __int_as_float(q[e]) * sw;
+        }
+        float v[NB][16];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if constexpr (SWIGLU) {
+                    const float gv = acc[tm][b][i] * rr[i];
+                    const float uv = acc[tm][b + NB][i] * rr[i];
+                    v[b][i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+                } else {
+                    v[b][i] = acc[tm][b][i] * rr[i];
+                }
+            }
+        S::put(slab, v);
+#pragma unroll
+        for (int j = 0; j < S::kSegPerLane; ++j) {
+            const int tr = wm * WM + tm * 32 + S::seg_row(j);
+            const int n = j0 + wn * NB * 32 + S::seg_col(j);
+            const uint32_t voff =
+                n < N_out ? static_cast<uint32_t>(tr) * row_bytes + static_cast<uint32_t>(n) * 2 : kOobOffset;
+            float t[8];
+            S::get(slab, j, t);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                i32x4_t{int(pack_bf16x2(t[0], t[1])), int(pack_bf16x2(t[2], t[3])),
+                        int(pack_bf16x2(t[4], t[5])), int(pack_bf16x2(t[6], t[7]))},
+                y_rsrc, voff, 0, 0);
+        }
+    }
+}
+
+// bf16 weights: direct-to-LDS mainloop.
+template <int BM, int BN, int OCC, bool SWIGLU>
+__global__ void __launch_bounds__(kThreads, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
                        uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
                        int tiles_n) {
-    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int TM = WM / 32, TN = WN / 32;
     static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs gate and up blocks");
-    // output columns covered by one block tile / one wave
-    constexpr int BNO = SWIGLU ? BN / 2 : BN;
+    constexpr int BNO = SWIGLU ? BN / 2 : BN;       // output columns of one block tile
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BM + BN) * kRowBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[(BM + BN) * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[(BM + BN) * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[(BM + BN) * kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[(BM + BN) * kTileBytes];
 
     int tile_m, tile_n;
     tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, j0 = tile_n * BNO;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
 
-    const int kbytes = K * 2;                                    // bf16 bytes of a row
-    const size_t h_row = static_cast<size_t>(K) * 2;
-    const size_t w_row = static_cast<size_t>(K) * (WFP8 ? 1 : 2);
-    auto a_ptr = [&](int r) -> const uint8_t* {
-        const int m = m0 + r;
-        return m < M ? H + static_cast<size_t>(m) * h_row : nullptr;
-    };
-    auto b_ptr = [&](int r) -> const uint8_t* {
-        if (SWIGLU) {
-            const int j = j0 + (r < BN / 2 ? r : r - BN / 2);
-            if (j >= N_out) return nullptr;
-            const int n = r < BN / 2 ? j : N_out + j;
-            return W + static_cast<size_t>(n) * w_row;
-        }
-        const int n = j0 + r;
-        return n < N_out ? W + static_cast<size_t>(n) * w_row : nullptr;
-    };
+    const int kbytes = K * 2;
+    DmaPanel<BM, BM> pa;
+    DmaPanel<BN, SWIGLU ? BN / 2 : BN> pb;
+    const uint8_t* a0 = H + static_cast<size_t>(m0) * kbytes;
+    pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
+    const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes;
+    if constexpr (SWIGLU) {
+        const uint8_t* u0 = W + static_cast<size_t>(N_out + j0) * kbytes;
+        pb.init(g0, min(BN / 2, N_out - j0), u0, min(BN / 2, N_out - j0), kbytes);
+    } else {
+        pb.init(g0, min(BN, N_out - j0), g0, 0, kbytes);
+    }
     auto a_row = [&](int tm) { return wm * WM + tm * 32; };
-    // SWIGLU: blocks [0, TN/2) = gate rows of this wave, [TN/2, TN) = the matching up rows
+    // SWIGLU: blocks [0, TN/2) = this wave's gate rows, [TN/2, TN) = the matching up rows
     auto b_row = [&](int tn) {
-        if (SWIGLU) {
+        if constexpr (SWIGLU) {
             constexpr int TH = TN / 2;
             return (tn < TH ? 0 : BN / 2) + wn * TH * 32 + (tn % TH) * 32;
         }
@@ -75,9 +136,70 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    using BStage = typename std::conditional<WFP8, PanelStageE4m3ToBf16<BN>, PanelStage<BN>>::type;
+    mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN)>(acc, pa, pb, kbytes, st0, st1, st2, st3, a_row, b_row);
+
+    const float sw = w_scale ? *w_scale : 1.0f;
+    uint8_t* slab = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    rowscale_epilogue<BM, BN, TM, TN, SWIGLU>(acc, R, sw, Y, M, N_out, m0, j0, wm, wn, slab);
+}
+
+// 8-bit weights (weight-only): e4m3 decoded exactly to bf16 while staged into LDS
+// through registers.
+template <int BM, int BN, int OCC, bool SWIGLU>
+__global__ void __launch_bounds__(kThreads, OCC)
+k_gemm_rowscale_swiglu_w8(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
+                          const float* __restrict__ w_scale, const float* __restrict__ R,
+                          uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
+                          int tiles_n) {
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs gate and up blocks");
+    constexpr int BNO = SWIGLU ? BN / 2 : BN;
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BM + BN) * kRowBytes];
+
+    int tile_m, tile_n;
+    tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+    const int m0 = tile_m * BM, j0 = tile_n * BNO;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int kbytes = K * 2;                                    // bf16 bytes of a row
+    const size_t h_row = static_cast<size_t>(K) * 2;
+    const size_t w_row = static_cast<size_t>(K);
+    auto a_ptr = [&](int r) -> const uint8_t* {
+        const int m = m0 + r;
+        return m < M ? H + static_cast<size_t>(m) * h_row : nullptr;
+    };
+    auto b_ptr = [&](int r) -> const uint8_t* {
+        if constexpr (SWIGLU) {
+            const int j = j0 + (r < BN / 2 ? r : r - BN / 2);
+            if (j >= N_out) return nullptr;
+            const int n = r < BN / 2 ? j : N_out + j;
+            return W + static_cast<size_t>(n) * w_row;
+        }
+        const int n = j0 + r;
+        return n < N_out ? W + static_cast<size_t>(n) * w_row : nullptr;
+    };
+    auto a_row = [&](int tm) { return wm * WM + tm * 32; };
+    auto b_row = [&](int tn) {
+        if constexpr (SWIGLU) {
+            constexpr int TH = TN / 2;
+            return (tn < TH ? 0 : BN / 2) + wn * TH * 32 + (tn % TH) * 32;
+        }
+        return wn * WN + tn * 32;
+    };
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
     PanelStage<BM> sa;
-    BStage sb;
+    PanelStageE4m3ToBf16<BN> sb;
     const int nk = (kbytes + kRowBytes - 1) / kRowBytes;
     if (nk > 0) {
         sa.load(a_ptr, 0, kbytes);
@@ -100,64 +222,44 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
         __syncthreads();
     }
 
-    // ---------------------------------------------------------------- epilogue ----
     const float sw = w_scale ? *w_scale : 1.0f;
-    const int lr = lane & 31, lh = lane >> 5;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        float rr[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = m0 + wm * WM + tm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-            rr[i] = m < M ? R[m] * sw : 0.0f;
-        }
-        if (SWIGLU) {
-            constexpr int TH = TN / 2;
-#pragma unroll
-            for (int g = 0; g < TH; ++g) {
-                const int j = j0 + wn * TH * 32 + g * 32 + lr;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int m = m0 + wm * WM + tm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                    if (m < M && j < N_out) {
-                        const float gv = acc[tm][g][i] * rr[i];
-                        const float uv = acc[tm][g + TH][i] * rr[i];
-                        const float silu = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
-                        Y[static_cast<size_t>(m) * N_out + j] = f32_to_bf16_bits(silu * uv);
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const int n = j0 + wn * WN + tn * 32 + lr;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int m = m0 + wm * WM + tm * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-                    if (m < M && n < N_out)
-                        Y[static_cast<size_t>(m) * N_out + n] = f32_to_bf16_bits(acc[tm][tn][i] * rr[i]);
-                }
-            }
-        }
-    }
+    static_assert(4 * Slab<SWIGLU ? TN / 2 : TN>::kBytes <= 2 * (BM + BN) * kRowBytes, "slabs fit");
+    uint8_t* slab = &smem[0][0] + wave * Slab<SWIGLU ? TN / 2 : TN>::kBytes;
+    rowscale_epilogue<BM, BN, TM, TN, SWIGLU>(acc, R, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
-constexpr int BM3 = 128, BN3 = 128;
+// Tile configurations of the second GEMM (compile-time).
+#ifndef CODA_G3_BM
+#define CODA_G3_BM 256
+#define CODA_G3_BN 256
+#define CODA_G3_OCC 1
+#endif
+constexpr int BM3 = CODA_G3_BM, BN3 = CODA_G3_BN, OCC3 = CODA_G3_OCC;
+constexpr int BM3W8 = 128, BN3W8 = 128;   // 8-bit weights: register-staged, 2 blocks per CU
 
 int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
-    const int64_t bno = swiglu ? BN3 / 2 : BN3;
-    return ((M + BM3 - 1) / BM3) * ((N_out + bno - 1) / bno);
+    const int64_t bno = swiglu ? BN3 / 2 : BN3, bno8 = swiglu ? BN3W8 / 2 : BN3W8;
+    const int64_t a = ((M + BM3 - 1) / BM3) * ((N_out + bno - 1) / bno);
+    const int64_t b = ((M + BM3W8 - 1) / BM3W8) * ((N_out + bno8 - 1) / bno8);
+    return a > b ? a : b;
 }
 
 template <bool SWIGLU, bool WFP8>
 static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                           const float* w_scale, const float* r, void* y, hipStream_t stream) {
-    constexpr int BNO = SWIGLU ? BN3 / 2 : BN3;
-    const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BNO - 1) / BNO;
+    constexpr int BM = WFP8 ? BM3W8 : BM3, BN = WFP8 ? BN3W8 : BN3;
+    constexpr int BNO = SWIGLU ? BN / 2 : BN;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N_out + BNO - 1) / BNO;
     const dim3 grid(tiles_m * tiles_n), block(kThreads);
-    hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, 2, 2, SWIGLU, WFP8>), grid, block, 0,
-                       stream, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W),
-                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
+    if constexpr (WFP8) {
+        hipLaunchKernelGGL((k_gemm_rowscale_swiglu_w8<BM, BN, 2, SWIGLU>), grid, block, 0, stream,
+                           static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale,
+                           r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
+    } else {
+        hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM, BN, OCC3, SWIGLU>), grid, block, 0, stream,
+                           static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale,
+                           r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
+    }
     return hipGetLastError();
 }
 

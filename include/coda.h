@@ -31,7 +31,8 @@
  *    faults surface at the caller's next synchronisation.  No C++ exception crosses
  *    this interface.
  *  - Calls are stateless and may be issued from several host threads.
- *  - Size limits: every dimension <= 2^31 - 1; M = 0 is a valid empty problem
+ *  - Size limits: M <= 2^31 - 1; the row lengths N, N_out and K of the GEMM calls are
+ *    at most 2^22 (4194304) elements; M = 0 is a valid empty problem
  *    (nothing is enqueued, and the M-sized tensors may then be NULL), every other
  *    dimension must be >= 1.
  *  - Checks run in the order: dtype/activation codes, shapes, values, (M == 0 ->

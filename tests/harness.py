@@ -3,9 +3,10 @@ calls the C ABI) and the fp64 oracle on the same seeded inputs, and compare.
 
 Tolerances (elementwise): |gpu - ref| <= tol * (1 + |ref|) with tol = 2e-2 for the bf16
 chain and 6e-2 for the 8-bit chain, for h and y.  Tighter diagnostics on the
-intermediates: h is within one bf16 ulp of the oracle's rounded hb; the partials sum to
-sum_n h_gpu^2 within the fp32 summation bound; r follows the GPU's own partials within
-2 fp32 ulp, and the oracle's r within 1e-4 relative.
+intermediates: h is within the fp32 summation bound of the oracle's rounded hb (bf16
+path); the partials sum to sum_n h_gpu^2 within the fp32 summation bound; r follows the
+GPU's own partials within 2 fp32 ulp, and the oracle's r within 1e-4 (bf16) / 2e-3
+(8-bit) relative.
 """
 
 from __future__ import annotations
@@ -88,14 +89,38 @@ def check_chain(w: si.Workload, inp: dict, h, P, r, y, rows=None, ref=None, prep
     assert ey.max() <= tol, f"y error {ey.max():.3e} > {tol} at {np.unravel_index(ey.argmax(), ey.shape)}"
 
     # diagnostics on the intermediates
+    #  h: the GPU sums exact products in fp32 (any order), adds x_res in fp32 and rounds
+    #  once to bf16, so |h_gpu - hb_ref| <= gamma_K * sum_k |a_k w_k| + 2^-24 |v|
+    #  + half a bf16 ulp of each side (gamma_K = K u / (1 - K u), u = 2^-24).  The 8-bit
+    #  MFMA sums its 64 products per instruction at a precision the ISA does not pin to
+    #  IEEE fp32, so for e4m3 the bound is reported (ratio) and only checked loosely.
     hb_ref = oracle.bf16_decode(ref["hb"])
-    ulp = np.abs(hb_ref) * 2.0 ** -7 + 2.0 ** -133
-    assert np.all(np.abs(hg - hb_ref) <= ulp * 1.0000001), "h more than one bf16 ulp from the oracle"
+    K = prep_ref["A"].shape[1]
+    dec = oracle.bf16_decode if prep_ref["a_dt"] == oracle.BF16 else oracle.e4m3_decode
+    rows_sel = slice(None) if rows is None else rows
+    a_abs = np.abs(dec(prep_ref["A"][rows_sel]) * prep_ref["a_scale"])
+    w_abs = np.abs((oracle.bf16_decode if prep_ref["wo_dt"] == oracle.BF16 else oracle.e4m3_decode)(
+        prep_ref["Wo"]) * prep_ref["wo_scale"])
+    s_abs = a_abs @ w_abs.T
+    u = 2.0 ** -24
+    gamma_k = K * u / (1 - K * u)
+    bound = gamma_k * s_abs + u * np.abs(ref["h"]) + 2.0 ** -8 * (np.abs(hg) + np.abs(hb_ref)) + 2.0 ** -133
+    dev = np.abs(hg - hb_ref)
+    ratio = dev / bound
+    print(f"h vs oracle hb: max {ratio.max():.3f} of the fp32-summation bound; "
+          f"max |h-hb_ref|/sum|a w| {np.max(dev / (s_abs + 1e-30)):.3e}", flush=True)
+    if w.dtype == "bf16":
+        assert np.all(ratio <= 1.0), "h outside the fp32 summation bound"
+    else:
+        assert np.all(dev <= 2.0 ** -10 * s_abs + 2.0 ** -8 * (np.abs(hg) + np.abs(hb_ref)) + 1e-30), \
+            "8-bit h deviates by more than 2^-10 of sum|a w|"
     d = hg.shape[1]
     s_gpu = (hg * hg).sum(1)
     assert np.allclose(Pg.sum(1), s_gpu, rtol=d * 2.0 ** -24, atol=0), "partials disagree with h"
     r64 = 1.0 / np.sqrt(Pg.sum(1) / d + np.float64(np.float32(w.eps)))
     assert np.all(np.abs(rg - r64) <= 2 * np.spacing(np.float32(r64)).astype(np.float64)), "r not fp32-rounded"
-    assert np.allclose(rg, ref["r"], rtol=1e-4, atol=0), "r disagrees with the oracle"
+    r_rel = float(np.max(np.abs(rg - ref["r"]) / ref["r"]))
+    print(f"r vs oracle: max rel {r_rel:.3e}", flush=True)
+    assert r_rel <= (1e-4 if w.dtype == "bf16" else 2e-3), "r disagrees with the oracle"
     return dict(h_err=float(eh.max()), y_err=float(ey.max()),
                 y_err_rms=float(np.sqrt(np.mean((yg - ref["y"]) ** 2))))

@@ -73,6 +73,8 @@ def test_gemm1_validation():
     assert f(16, 64, 60, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE  # K % 8
     assert f(16, 64, 24, P1, 1, P6, P2, P6, P3, P4, P5, None) == SHAPE      # e4m3 K % 16
     assert f(1 << 31, 64, 64, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE
+    assert f(16, 64, (1 << 22) + 8, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE  # row cap
+    assert f(16, (1 << 22) + 8, 64, P1, 0, None, P2, None, P3, P4, P5, None) == SHAPE
     assert f(16, 64, 64, P1 + 8, 0, None, P2, None, P3, P4, P5, None) == ALIGN
     assert f(16, 64, 64, P1, 0, None, P2, None, P3, P4, P5 + 4, None) == ALIGN
     assert f(16, 64, 64, P1, 0, None, P2, None, P3, P1, P5, None) == ALIAS   # h over A
@@ -106,6 +108,7 @@ def test_gemm2_validation():
     assert f(16, 60, 64, 1, P1, P2, 0, None, P3, P4, None) == SHAPE
     assert f(16, 64, 8, 1, P1, P2, 1, P5, P3, P4, None) == SHAPE             # e4m3 K % 16
     assert f(16, 1 << 30, 64, 1, P1, P2, 0, None, P3, P4, None) == SHAPE     # 2F too large
+    assert f(16, 64, (1 << 22) + 8, 1, P1, P2, 0, None, P3, P4, None) == SHAPE  # row cap
     assert f(16, 64, 64, 1, P1, P2, 0, None, P3, P1, None) == ALIAS          # y over h
     assert f(16, 64, 64, 1, P1, P2, 0, None, P3, P3, None) == ALIAS          # y over r
     assert f(16, 64, 64, 1, P1, P2, 0, None, P3 + 8, P4, None) == ALIGN
