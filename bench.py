@@ -73,6 +73,61 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _counter_means(directory: str, counter: str) -> dict:
+    """Mean value per dispatch of a derived counter, per kernel name (rocprofv3 CSV)."""
+    acc = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"]
+        acc.setdefault(name, {}).setdefault(r["Dispatch_Id"], 0.0)
+        acc[name][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+
+
+def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, then of the
+    plain copy) into profiles/traffic_<kernel>_<workload>.json: HBM-side bytes per launch,
+    each counter divided by what it reads per byte of the plain copy."""
+    f_run, w_run, f_cal, w_cal = (_counter_means(d, c) for d, c in
+                                  zip(dirs, ("FETCH_SIZE", "WRITE_SIZE", "FETCH_SIZE", "WRITE_SIZE")))
+    pick = lambda d: next(v for k, v in d.items() if "copy" in k.lower())  # noqa: E731
+    kib = copy_bytes / 1024.0
+    ff, fw = pick(f_cal) / kib, pick(w_cal) / kib
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    lines = [f"# HBM traffic per launch, workload {workload}",
+             f"# commands: {command}",
+             f"# copy calibration: {copy_bytes} bytes copied; FETCH_SIZE reads {ff:.4f} KiB per KiB, "
+             f"WRITE_SIZE {fw:.4f} KiB per KiB",
+             "kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, traffic bytes (scaled)"]
+    for kname in ("k_gemm_resid_partialrms", "k_rowscale_reduce", "k_gemm_rowscale_swiglu"):
+        fk = [v for k, v in f_run.items() if kname in k and "swiglu_w8" not in k]
+        wk = [v for k, v in w_run.items() if kname in k and "swiglu_w8" not in k]
+        if not fk or not wk:
+            continue
+        traffic = fk[0] * 1024 / ff + wk[0] * 1024 / fw
+        rec = {"kernel": kname, "workload": workload, "source_hash": kernel_source_hash(),
+               "fetch_kib": fk[0], "write_kib": wk[0], "copy_factor_fetch": ff,
+               "copy_factor_write": fw, "hbm_bytes_per_launch": round(traffic), "command": command}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{workload}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        lines.append(f"{kname}, {fk[0]:.1f}, {wk[0]:.1f}, {traffic:.0f}")
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(w, inp, target_s: float) -> dict:
     import numpy as np
 
@@ -113,7 +168,20 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="also time the unfused torch chain")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times): the "
+                         "reference for scaling HBM byte counters, then exit")
+    ap.add_argument("--ingest-traffic", nargs=4, metavar="DIR",
+                    help="write profiles/traffic_*.json from rocprofv3 --pmc output dirs: "
+                         "FETCH_SIZE run, WRITE_SIZE run, FETCH_SIZE copy run, WRITE_SIZE copy run")
+    ap.add_argument("--ingest-command", default="", help="command line recorded with --ingest-traffic")
     args = ap.parse_args()
+    if args.ingest_traffic:
+        import synth_inputs as si
+
+        ingest_traffic(args.ingest_traffic, si.WORKLOADS[args.workload].name,
+                       (args.copy_calibration or 1024) << 20, args.ingest_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on ONE GPU; --gpus {args.gpus} is not supported "
               "(the chain shards along tokens with no exchange; see the design notes)",
@@ -122,6 +190,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
 
     import gemm_epilogue_transformer_amd as coda
     import synth_inputs as si
@@ -193,7 +271,7 @@ def main():
     peak = PEAK_TFLOPS[k2_dtype]
     byt = algorithmic_bytes(w)
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name, "gemm_rowscale_swiglu"),
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name, "k_gemm_rowscale_swiglu"),
             "kernel": "k_gemm_rowscale_swiglu", "kernel_ms": round(k3_ms, 4),
             "algorithmic_bytes": byt["gemm2"]}
 
