@@ -1,42 +1,45 @@
 // Direct-to-LDS MFMA mainloop (gfx950) shared by both GEMM kernels of the chain.
 //
-// Block tile BM x BN, 4 waves in a 2 x 2 grid, each wave owning (BM/2) x (BN/2) made of
-// 32x32 MFMA blocks.  A k-tile is 64 bytes of every row (32 bf16 or 64 e4m3 values).
+// Block tile BM x BN, NW waves in a WAVES_M x WAVES_N grid, each wave owning a sub-tile
+// made of 32x32 MFMA blocks.  A k-tile is RB bytes of every row (RB = 64: 32 bf16 / 64
+// e4m3 values; RB = 128: 64 bf16 / 128 e4m3).
 //
 // Global -> LDS: `buffer_load_dwordx4 ... lds` moves 16 bytes per lane straight into
-// LDS (no VGPR staging).  One instruction fills 1 KB = 16 consecutive panel rows of 64
-// bytes: lane i lands at LDS byte 16*i of that 1 KB, i.e. row i/4, slot i%4.
+// LDS (no VGPR staging).  One instruction fills 1 KB = 1024/RB consecutive panel rows:
+// lane i lands at LDS byte 16*i of that 1 KB, i.e. row i / (RB/16), slot i % (RB/16).
 //
-// LDS layout: 16-byte chunk c of row r sits in slot c ^ ((r >> 2) & 3).  The LDS has 64
-// banks (256 bytes) and serves a ds_read_b128 16 lanes at a time; the 16 lanes of a
+// LDS layout: 16-byte chunk c of row r sits in a swizzled slot (swz below).  The LDS has
+// 64 banks (256 bytes) and serves a ds_read_b128 16 lanes at a time; the 16 lanes of a
 // fragment read touch 16 consecutive rows at one chunk, and the swizzle spreads them over
-// all 16 distinct 16-byte bank groups.  On the DMA side lane i therefore FETCHES chunk
-// (i%4) ^ ((i/16) & 3) of its row.
+// all 16 distinct 16-byte bank groups:  RB = 64: slot = c ^ ((r >> 2) & 3);  RB = 128:
+// slot = c ^ ((r >> 1) & 7).  On the DMA side each lane therefore FETCHES the chunk that
+// belongs in the slot it lands in.
 //
 // Rows past the matrix and chunks past K read as zero through the buffer descriptor's
 // range check (each descriptor spans exactly the valid rows of one row segment; K-tail
 // chunks get an offset beyond every range).
 //
-// Pipeline: 4 LDS stages in 4 distinct __shared__ arrays (so the compiler can tell the
-// DMA into one stage from the fragment reads of another), DMA running 3 k-tiles ahead.
-// Per k-tile: wait until this tile's DMA has landed (the 2 younger tiles may still be in
-// flight), barrier, issue the DMA of tile kt+3 into the stage freed by tile kt-1, MFMAs.
+// Pipeline: NS LDS stages; the DMA of tile kt+NS is issued once tile kt has been read
+// (details at mainloop_dma).
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "gemm_core.hpp"
 
 namespace coda {
 
-constexpr int kTileBytes = 64;          // bytes of one row per k-tile
-constexpr int kStages = 4;
 constexpr uint32_t kOob = 0x80000000u;  // offset that no descriptor range reaches
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// LDS byte offset of 16-byte chunk `chunk` of panel row `row` (RB bytes per row).
+template <int RB>
 __device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kTileBytes + ((chunk ^ ((row >> 2) & 3)) << 4);
+    static_assert(RB == 64 || RB == 128, "row depth");
+    if constexpr (RB == 64) return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+    return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -69,17 +72,23 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 
 // One operand panel of R rows, made of up to two row segments (the SwiGLU weight panel
 // takes its first SPLIT rows from the gate rows and the rest from the up rows; SPLIT == R
-// for a single segment).  Instruction j of wave w covers panel rows [(4j + w) * 16, +16),
-// so with SPLIT % 64 == 0 every instruction stays inside one segment and the segment of
-// instruction j is j < SPLIT/64.
-template <int R, int SPLIT>
+// for a single segment), loaded by NW waves.  Instruction j of wave w covers panel rows
+// [(NW*j + w) * RPI, +RPI) with RPI = 1024/RB rows per instruction, so with
+// SPLIT % (RPI*NW) == 0 every instruction stays inside one segment and the segment of
+// instruction j is j < SPLIT/(RPI*NW).
+template <int R, int SPLIT, int NW, int RB>
 struct DmaPanel {
-    static_assert(R % 64 == 0 && SPLIT % 64 == 0 && SPLIT <= R, "panel geometry");
-    static constexpr int kInst = R / 64;           // DMA instructions per wave per k-tile
+    static constexpr int kCpr = RB / 16;            // 16-byte chunks per row
+    static constexpr int kRpi = 1024 / RB;          // rows per instruction (one wave)
+    static constexpr int kRowsPerInst = kRpi * NW;  // rows per instruction index, all waves
+    static_assert(R % kRowsPerInst == 0 && SPLIT % kRowsPerInst == 0 && SPLIT <= R, "panel geometry");
+    static_assert(RB == 64 || NW % 2 == 0, "RB = 128 swizzle phase needs an even wave count");
+    static constexpr int kInst = R / kRowsPerInst;  // DMA instructions per wave per k-tile
+    static constexpr int kSplitInst = SPLIT / kRowsPerInst;
     u32x4_t rsrc[2];
     uint32_t off0;            // byte offset of this lane's chunk in instruction 0 at k-tile 0
     uint32_t chunk_byte;      // 16 * the chunk this lane fetches
-    uint32_t stride;          // bytes between instruction j and j+1 (64 rows), wave-uniform
+    uint32_t stride;          // bytes between instruction j and j+1, wave-uniform
 
     // seg_base[s]: address of the segment's first row; seg_rows[s]: rows of the segment that
     // exist in the matrix (the descriptor range); kbytes: bytes of one matrix row.
@@ -89,98 +98,119 @@ struct DmaPanel {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         rsrc[0] = make_rsrc(seg_base0, static_cast<uint32_t>(max(seg_rows0, 0)) * kbytes);
         rsrc[1] = make_rsrc(seg_base1, static_cast<uint32_t>(max(seg_rows1, 0)) * kbytes);
-        chunk_byte = static_cast<uint32_t>((lane & 3) ^ ((lane >> 4) & 3)) << 4;
-        off0 = static_cast<uint32_t>(wave * 16 + (lane >> 2)) * kbytes + chunk_byte;
-        stride = __builtin_amdgcn_readfirstlane(64u * static_cast<uint32_t>(kbytes));
+        // lane lands in row r = row0 + lane/kCpr, slot lane%kCpr; it fetches the chunk that
+        // swz<RB> places in that slot.  The swizzle phase of r does not depend on the
+        // instruction index j (row0 = (NW*j + wave) * kRpi).
+        const int r = wave * kRpi + lane / kCpr;
+        const int slot = lane % kCpr;
+        const int chunk = (RB == 64) ? (slot ^ ((r >> 2) & 3)) : (slot ^ ((r >> 1) & 7));
+        chunk_byte = static_cast<uint32_t>(chunk) << 4;
+        off0 = static_cast<uint32_t>(r) * kbytes + chunk_byte;
+        stride = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kRowsPerInst) * static_cast<uint32_t>(kbytes));
     }
 
-    // Issue the DMA of k-tile kt into `stage` (R rows x 64 bytes).  Row of instruction j,
-    // lane l: (4j + wave) * 16 + l/4; segment-1 rows are rebased by SPLIT.
-    __device__ __forceinline__ void issue(uint8_t* stage, int kt, int kbytes) const {
-        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const uint32_t kb = static_cast<uint32_t>(kt) * kTileBytes;
-        // a chunk past K starts from kOob: kOob + jj*stride stays beyond every range
-        // (each descriptor spans < 2^31 bytes), so the whole lane reads zeros
+    // Offset of this lane's chunk for k-tile kt (kOob past K): a chunk past K starts from
+    // kOob, and kOob + jj*stride stays beyond every range (each descriptor spans < 2^31
+    // bytes), so the whole lane reads zeros.
+    __device__ __forceinline__ uint32_t base_offset(int kt, int kbytes) const {
+        const uint32_t kb = static_cast<uint32_t>(kt) * RB;
         const bool kin = kb + chunk_byte < static_cast<uint32_t>(kbytes);
         uint32_t base = kin ? off0 + kb : kOob;
-        // keep the per-instruction offsets derived here (not hoisted as kInst live registers)
+        // keep the per-instruction offsets derived at their use (not kInst live registers)
         asm volatile("" : "+v"(base));
+        return base;
+    }
+    // DMA instruction j of k-tile (base from base_offset) into `stage` (R rows x RB bytes).
+    // Row of instruction j, lane l: (NW*j + wave) * kRpi + l/kCpr; segment-1 rows are
+    // rebased by SPLIT.
+    __device__ __forceinline__ void issue_one(int j, uint8_t* stage, uint32_t base) const {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int row0 = (NW * j + wave) * kRpi;
+        const int jj = (j < kSplitInst) ? j : j - kSplitInst;
+        dma16(rsrc[(j < kSplitInst) ? 0 : 1], base + static_cast<uint32_t>(jj) * stride,
+              lds_addr(stage + row0 * RB));
+    }
+    // All kInst instructions of k-tile kt.
+    __device__ __forceinline__ void issue(uint8_t* stage, int kt, int kbytes) const {
+        const uint32_t base = base_offset(kt, kbytes);
 #pragma unroll
-        for (int j = 0; j < kInst; ++j) {
-            const int row0 = (4 * j + wave) * 16;
-            const int jj = (j < SPLIT / 64) ? j : j - SPLIT / 64;
-            const uint32_t voff = base + static_cast<uint32_t>(jj) * stride;
-            dma16(rsrc[(j < SPLIT / 64) ? 0 : 1], voff, lds_addr(stage + row0 * kTileBytes));
-        }
+        for (int j = 0; j < kInst; ++j) issue_one(j, stage, base);
     }
 };
 
 // Fragments of one MFMA k-step for a wave's TM x TN 32x32 blocks.  bf16: a k-step is
-// k16 (2 per k-tile), one 16-byte ds_read per fragment.  e4m3: a k-step is k64 (1 per
-// k-tile), two 16-byte ds_reads per fragment.
-template <Elt E, int TM, int TN>
+// k16 (RB/32 per k-tile), one 16-byte ds_read per fragment.  e4m3: a k-step is k64
+// (RB/64 per k-tile), two 16-byte ds_reads per fragment.
+template <Elt E, int TM, int TN, int RB>
 struct Frags;
 
-template <int TM, int TN>
-struct Frags<Elt::BF16, TM, TN> {
-    static constexpr int kSteps = 2;
+template <int TM, int TN, int RB>
+struct Frags<Elt::BF16, TM, TN, RB> {
+    static constexpr int kSteps = RB / 32;
     static constexpr int kReads = TM + TN;         // ds_read_b128 per k-step
     bf16x8_t a[TM], b[TN];
+    // fragment read i of k-step s: i < TM -> a[i], else b[i - TM]
+    template <class ARow, class BRow>
+    __device__ __forceinline__ void load_one(int i, const uint8_t* sA, const uint8_t* sB, int s,
+                                             const ARow& a_row, const BRow& b_row) {
+        const int lane = threadIdx.x & 63;
+        const int lr = lane & 31, lh = lane >> 5;
+        if (i < TM)
+            a[i] = *reinterpret_cast<const bf16x8_t*>(sA + swz<RB>(a_row(i) + lr, 2 * s + lh));
+        else
+            b[i - TM] = *reinterpret_cast<const bf16x8_t*>(sB + swz<RB>(b_row(i - TM) + lr, 2 * s + lh));
+    }
     template <class ARow, class BRow>
     __device__ __forceinline__ void load(const uint8_t* sA, const uint8_t* sB, int s,
                                          const ARow& a_row, const BRow& b_row) {
-        const int lane = threadIdx.x & 63;
-        const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-            a[tm] = *reinterpret_cast<const bf16x8_t*>(sA + swz(a_row(tm) + lr, 2 * s + lh));
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-            b[tn] = *reinterpret_cast<const bf16x8_t*>(sB + swz(b_row(tn) + lr, 2 * s + lh));
+        for (int i = 0; i < kReads; ++i) load_one(i, sA, sB, s, a_row, b_row);
+    }
+    // MFMA i of the k-step: block (i / TN, i % TN)
+    __device__ __forceinline__ void mma_one(int i, f32x16_t (&acc)[TM][TN]) const {
+        const int tm = i / TN, tn = i % TN;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
     }
     __device__ __forceinline__ void mma(f32x16_t (&acc)[TM][TN]) const {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-                acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+        for (int i = 0; i < TM * TN; ++i) mma_one(i, acc);
     }
 };
 
-template <int TM, int TN>
-struct Frags<Elt::E4M3, TM, TN> {
-    static constexpr int kSteps = 1;
-    static constexpr int kReads = 2 * (TM + TN);
+template <int TM, int TN, int RB>
+struct Frags<Elt::E4M3, TM, TN, RB> {
+    static constexpr int kSteps = RB / 64;
+    static constexpr int kReads = TM + TN;         // fragments (two ds_read_b128 each)
     i32x8_t a[TM], b[TN];
+    // fragment i of k-step s: lane holds 32 bytes of its row = chunks 4s + 2*lh, +1
     template <class ARow, class BRow>
-    __device__ __forceinline__ void load(const uint8_t* sA, const uint8_t* sB, int,
-                                         const ARow& a_row, const BRow& b_row) {
+    __device__ __forceinline__ void load_one(int i, const uint8_t* sA, const uint8_t* sB, int s,
+                                             const ARow& a_row, const BRow& b_row) {
         const int lane = threadIdx.x & 63;
         const int lr = lane & 31, lh = lane >> 5;
-        // lane holds 32 bytes of its row = chunks 2*lh, 2*lh+1
+        const bool isa = i < TM;
+        const int row = (isa ? a_row(i) : b_row(i - TM)) + lr;
+        const uint8_t* base = isa ? sA : sB;
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + swz<RB>(row, 4 * s + 2 * lh));
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + swz<RB>(row, 4 * s + 2 * lh + 1));
+        const i32x8_t v = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (isa) a[i] = v; else b[i - TM] = v;
+    }
+    template <class ARow, class BRow>
+    __device__ __forceinline__ void load(const uint8_t* sA, const uint8_t* sB, int s,
+                                         const ARow& a_row, const BRow& b_row) {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            const int row = a_row(tm) + lr;
-            const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(sA + swz(row, 2 * lh));
-            const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(sA + swz(row, 2 * lh + 1));
-            a[tm] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const int row = b_row(tn) + lr;
-            const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(sB + swz(row, 2 * lh));
-            const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(sB + swz(row, 2 * lh + 1));
-            b[tn] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
+        for (int i = 0; i < kReads; ++i) load_one(i, sA, sB, s, a_row, b_row);
+    }
+    __device__ __forceinline__ void mma_one(int i, f32x16_t (&acc)[TM][TN]) const {
+        const int tm = i / TN, tn = i % TN;
+        // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
+        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[tm], b[tn], acc[tm][tn], 0, 0, 0,
+                                                                      127, 0, 127);
     }
     __device__ __forceinline__ void mma(f32x16_t (&acc)[TM][TN]) const {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-                // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
-                acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    a[tm], b[tn], acc[tm][tn], 0, 0, 0, 127, 0, 127);
+        for (int i = 0; i < TM * TN; ++i) mma_one(i, acc);
     }
 };
 
@@ -188,97 +218,109 @@ struct Frags<Elt::E4M3, TM, TN> {
 // vmcnt_hi[15:14]); expcnt / lgkmcnt are left at their maxima.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Instruction classes for the scheduler hints (llvm.amdgcn.sched.group.barrier masks).
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
-
-// Interleave `n_mfma` MFMAs with `n_ds` LDS reads and `n_vm` global->LDS loads: one MFMA,
-// then one of each memory op, while they last; the remaining MFMAs follow.
-template <int N_MFMA, int N_DS, int N_VM>
-__device__ __forceinline__ void sched_interleave() {
-    constexpr int kMem = N_DS > N_VM ? N_DS : N_VM;
-#pragma unroll
-    for (int i = 0; i < kMem; ++i) {
-        if (i < N_MFMA) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (i < N_VM) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-        if (i < N_DS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    if (N_MFMA > kMem) __builtin_amdgcn_sched_group_barrier(kSchedMfma, N_MFMA - kMem, 0);
+// Compile-time loop: f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // The whole mainloop: acc += A_panel . B_panel^T over the k-tiles of one row.
-// st0..st3 are the four stage buffers, each (BM + BN) * 64 bytes.
+// st[0..NS-1] are the NS stage buffers, each (BM + BN) * RB bytes.
 //
 // Software pipeline (per wave).  Fragments are double-buffered by MFMA k-step: the
 // fragments of step j+1 are read from LDS while the MFMAs of step j run.  The last
-// k-step of tile kt is where the next tile's first fragments are needed, so that is
-// where the wave waits for tile kt+1's DMA, passes the barrier (after which every wave
-// has also finished reading tile kt-1, whose stage receives the DMA of tile kt+3), issues
-// that DMA and reads tile kt+1's first fragments, all interleaved with the MFMAs.
-template <Elt E, int BM, int BN, int SPLIT, int TM, int TN, class ARow, class BRow>
-__device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM>& pa,
-                                             const DmaPanel<BN, SPLIT>& pb, int kbytes,
-                                             uint8_t* st0, uint8_t* st1, uint8_t* st2,
-                                             uint8_t* st3, const ARow& a_row, const BRow& b_row) {
-    using F = Frags<E, TM, TN>;
+// k-step of tile kt is where tile kt+1's first fragments are needed; its MFMAs only use
+// fragments already in registers, so every LDS read of tile kt has been issued before it.
+// There the wave waits for tile kt+1's DMA and passes the barrier; after it every wave
+// has finished reading tile kt, so tile kt's stage receives the DMA of tile kt+NS, issued
+// (one instruction per MFMA) together with the reads of tile kt+1's first fragments.
+// The DMA thus runs NS tiles ahead of the reads, and tiles kt+2 .. kt+NS-1 may still be
+// in flight at the barrier of tile kt.
+template <Elt E, int BM, int BN, int SPLIT, int NS, int NW, int RB, int TM, int TN, class ARow, class BRow>
+__device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
+                                             const DmaPanel<BN, SPLIT, NW, RB>& pb, int kbytes,
+                                             uint8_t* const (&st)[NS], const ARow& a_row,
+                                             const BRow& b_row) {
+    static_assert(NS >= 2, "at least two stages");
+    using F = Frags<E, TM, TN, RB>;
     constexpr int KS = F::kSteps;
+    static_assert((NS * KS) % 2 == 0, "fragment double-buffer parity must repeat every stage group");
     constexpr int kMfma = TM * TN;
-    // DMA instructions per wave per k-tile; when tile kt+1 must have landed, only tile
-    // kt+2 is younger, so kPerTile DMA instructions may stay in flight
-    constexpr int kPerTile = DmaPanel<BM, BM>::kInst + DmaPanel<BN, SPLIT>::kInst;
-    static_assert(2 * kPerTile < 64, "vmcnt range");
-    const int nk = (kbytes + kTileBytes - 1) / kTileBytes;
-    // k-tiles run in groups of 4 (one per stage); the count is padded to a multiple of 4
-    // with k-tiles past K, which the DMA fills with zeros.  The DMA always runs 3 tiles
+    constexpr int nA = DmaPanel<BM, BM, NW, RB>::kInst;
+    constexpr int kPerTile = nA + DmaPanel<BN, SPLIT, NW, RB>::kInst;   // DMA per wave per tile
+    static_assert((NS - 1) * kPerTile < 64, "vmcnt range");
+    static_assert(kPerTile <= kMfma, "one MFMA ahead of every DMA instruction");
+    const int nk = (kbytes + RB - 1) / RB;
+    // k-tiles run in groups of NS (one per stage); the count is padded to a multiple of NS
+    // with k-tiles past K, which the DMA fills with zeros.  The DMA always runs NS tiles
     // ahead, past the padded end too (zeros into stages that are not read again), so the
     // wait counts are exact on every tile.
-    const int nq = (nk + 3) >> 2;
-    auto issue = [&](uint8_t* st, int kt) {
-        pa.issue(st, kt, kbytes);
-        pb.issue(st + BM * kTileBytes, kt, kbytes);
-    };
+    const int ng = (nk + NS - 1) / NS;
     F f[2];
-    issue(st0, 0);
-    issue(st1, 1);
-    issue(st2, 2);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPerTile));   // tile 0 landed
+    static_for<NS>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        pa.issue(st[i], i, kbytes);
+        pb.issue(st[i] + BM * RB, i, kbytes);
+    });
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 1) * kPerTile));   // tile 0 landed
     __syncthreads();
-    f[0].load(st0, st0 + BM * kTileBytes, 0, a_row, b_row);
+    f[0].load(st[0], st[0] + BM * RB, 0, a_row, b_row);
 
-    // one k-tile in stage `cur`; `nxt` holds tile kt+1, `dst` receives the DMA of kt+3.
-    // G = global k-step index parity base (k-steps of this tile use f[(G + s) & 1]).
-    auto tile = [&](auto G, uint8_t* cur, uint8_t* nxt, uint8_t* dst, int kt) {
-        constexpr int g = decltype(G)::value;
+    for (int g = 0; g < ng; ++g) {
+        static_for<NS>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            constexpr int par = (i * KS) & 1;     // k-step s of this tile uses f[(par + s) & 1]
+            uint8_t* cur = st[i];
+            uint8_t* nxt = st[(i + 1) % NS];
+            const int kt = g * NS + i;
 #pragma unroll
-        for (int s = 0; s < KS - 1; ++s) {
-            f[(g + s + 1) & 1].load(cur, cur + BM * kTileBytes, s + 1, a_row, b_row);
-            f[(g + s) & 1].mma(acc);
-            sched_interleave<kMfma, F::kReads, 0>();
+            for (int s = 0; s < KS - 1; ++s) {
+                // k-step s: MFMA j, then fragment read j of k-step s+1
+                static_for<kMfma>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    f[(par + s) & 1].mma_one(j, acc);
+                    if (j < F::kReads) f[(par + s + 1) & 1].load_one(j, cur, cur + BM * RB, s + 1, a_row, b_row);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
+            // last k-step of the tile: cross into tile kt+1
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile));  // tile kt+1 landed
+            __syncthreads();                                             // ... for every wave
             __builtin_amdgcn_sched_barrier(0);
-        }
-        // last k-step of the tile: cross into tile kt+1
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPerTile));   // tile kt+1 landed (this wave)
-        __syncthreads();                                    // ... for every wave
-        __builtin_amdgcn_sched_barrier(0);
-        issue(dst, kt + 3);
-        f[(g + KS) & 1].load(nxt, nxt + BM * kTileBytes, 0, a_row, b_row);
-        f[(g + KS - 1) & 1].mma(acc);
-        sched_interleave<kMfma, F::kReads, 0>();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    using G0 = std::integral_constant<int, 0>;
-    using G1 = std::integral_constant<int, KS & 1>;
-    using G2 = std::integral_constant<int, 0>;
-    using G3 = std::integral_constant<int, KS & 1>;
-    for (int q = 0; q < nq; ++q) {
-        const int kt = 4 * q;
-        tile(G0{}, st0, st1, st3, kt);
-        tile(G1{}, st1, st2, st0, kt + 1);
-        tile(G2{}, st2, st3, st1, kt + 2);
-        tile(G3{}, st3, st0, st2, kt + 3);
+            const uint32_t base_a = pa.base_offset(kt + NS, kbytes);
+            const uint32_t base_b = pb.base_offset(kt + NS, kbytes);
+            // MFMA j, then DMA instruction j of tile kt+NS into this tile's stage, then
+            // fragment read j of tile kt+1's first k-step
+            static_for<kMfma>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                f[(par + KS - 1) & 1].mma_one(j, acc);
+                if (j < nA) pa.issue_one(j, cur, base_a);
+                else if (j < kPerTile) pb.issue_one(j - nA, cur + BM * RB, base_b);
+                if (j < F::kReads) f[(par + KS) & 1].load_one(j, nxt, nxt + BM * RB, 0, a_row, b_row);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
     }
     // drain the DMA that ran past the end before the LDS is reused or released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+}
+
+// Per-wave epilogue slab region: NW slabs of SLAB_BYTES packed into the stage buffers
+// (as many per stage as fit).
+template <int NS, int NW, int STAGE_BYTES, int SLAB_BYTES>
+__device__ __forceinline__ uint8_t* slab_region(uint8_t* const (&st)[NS], int wave) {
+    constexpr int kPer = STAGE_BYTES / SLAB_BYTES;
+    static_assert(kPer >= 1 && (NW + kPer - 1) / kPer <= NS, "epilogue slabs fit the stages");
+    uint8_t* p = st[0];
+    static_for<NS>([&](auto I) {
+        if (wave / kPer == decltype(I)::value) p = st[decltype(I)::value];
+    });
+    return p + (wave % kPer) * SLAB_BYTES;
 }
 
 }  // namespace coda

@@ -15,22 +15,23 @@
 
 namespace coda {
 
-template <int BM, int BN, int OCC, Elt E>
-__global__ void __launch_bounds__(kThreads, OCC)
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int OCC, Elt E>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
                         const float* __restrict__ a_scale, const float* __restrict__ w_scale,
                         const uint16_t* x_res, uint16_t* h, float* __restrict__ P,
                         int M, int N, int K, int tiles_m, int tiles_n) {
-    constexpr int WAVES_M = 2, WAVES_N = 2;
+    constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int EB = EltInfo<E>::kBytes;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[(BM + BN) * kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[(BM + BN) * kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[(BM + BN) * kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st3[(BM + BN) * kTileBytes];
+    constexpr int kStage = (BM + BN) * RB;
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
     __shared__ float red[WAVES_N][BM];
+    uint8_t* st[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) st[i] = stages[i];
 
     int tile_m, tile_n;
     tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
@@ -39,8 +40,8 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     const int kbytes = K * EB;
-    DmaPanel<BM, BM> pa;
-    DmaPanel<BN, BN> pb;
+    DmaPanel<BM, BM, NW, RB> pa;
+    DmaPanel<BN, BN, NW, RB> pb;
     const uint8_t* a0 = A + static_cast<size_t>(m0) * kbytes;
     const uint8_t* b0 = W + static_cast<size_t>(n0) * kbytes;
     pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
@@ -56,7 +57,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    mainloop_dma<E, BM, BN, BN>(acc, pa, pb, kbytes, st0, st1, st2, st3, a_row, b_row);
+    mainloop_dma<E, BM, BN, BN, NS, NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row);
 
     // ---------------------------------------------------------------- epilogue ----
     // Per 32-row slab of this wave: stage scale*acc row-major in the wave's own (now
@@ -66,31 +67,36 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     // `red`, then the WAVES_N waves sharing a row are added in a fixed order.
     const float scale = (a_scale ? *a_scale : 1.0f) * (w_scale ? *w_scale : 1.0f);
     using S = Slab<TN>;
-    static_assert(S::kBytes <= (BM + BN) * kTileBytes, "slab fits one stage");
-    uint8_t* slab = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+    uint8_t* slab = slab_region<NS, NW, kStage, S::kBytes>(st, wave);
     const int valid_rows = min(BM, M - m0);
     const uint32_t row_bytes = static_cast<uint32_t>(N) * 2;
     const size_t tile_off = static_cast<size_t>(m0) * N;
     const __amdgpu_buffer_rsrc_t xr_rsrc =
         make_buffer_rsrc(x_res ? x_res + tile_off : h + tile_off, x_res ? valid_rows * row_bytes : 0u);
     const __amdgpu_buffer_rsrc_t h_rsrc = make_buffer_rsrc(h + tile_off, valid_rows * row_bytes);
+    // residual loads of slab tm+1 are in flight while slab tm is processed
+    auto seg_voff = [&](int tm, int j) -> uint32_t {
+        const int tr = wm * WM + tm * 32 + S::seg_row(j);
+        const int n = n0 + wn * WN + S::seg_col(j);
+        return n < N ? static_cast<uint32_t>(tr) * row_bytes + static_cast<uint32_t>(n) * 2 : kOobOffset;
+    };
+    i32x4_t xr[2][S::kSegPerLane];
+#pragma unroll
+    for (int j = 0; j < S::kSegPerLane; ++j)
+        xr[0][j] = __builtin_amdgcn_raw_buffer_load_b128(xr_rsrc, seg_voff(0, j), 0, 0);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
+        if (tm + 1 < TM) {
+#pragma unroll
+            for (int j = 0; j < S::kSegPerLane; ++j)
+                xr[(tm + 1) & 1][j] = __builtin_amdgcn_raw_buffer_load_b128(xr_rsrc, seg_voff(tm + 1, j), 0, 0);
+        }
         float v[TN][16];
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[tn][i] = acc[tm][tn][i] * scale;
         S::put(slab, v);
-        uint32_t voff[S::kSegPerLane];
-        i32x4_t xr[S::kSegPerLane];
-#pragma unroll
-        for (int j = 0; j < S::kSegPerLane; ++j) {
-            const int tr = wm * WM + tm * 32 + S::seg_row(j);
-            const int n = n0 + wn * WN + S::seg_col(j);
-            voff[j] = n < N ? static_cast<uint32_t>(tr) * row_bytes + static_cast<uint32_t>(n) * 2 : kOobOffset;
-            xr[j] = __builtin_amdgcn_raw_buffer_load_b128(xr_rsrc, voff[j], 0, 0);
-        }
 #pragma unroll
         for (int j = 0; j < S::kSegPerLane; ++j) {
             float t[8];
@@ -99,7 +105,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
             uint32_t o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t x = static_cast<uint32_t>(xr[j][e]);
+                const uint32_t x = static_cast<uint32_t>(xr[tm & 1][j][e]);
                 const uint16_t h0 = f32_to_bf16_bits(t[2 * e] + bf16_bits_to_f32(static_cast<uint16_t>(x & 0xFFFFu)));
                 const uint16_t h1 = f32_to_bf16_bits(t[2 * e + 1] + bf16_bits_to_f32(static_cast<uint16_t>(x >> 16)));
                 const float q0 = bf16_bits_to_f32(h0), q1 = bf16_bits_to_f32(h1);
@@ -108,7 +114,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
                 o[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
             }
             __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])},
-                                                   h_rsrc, voff[j], 0, 0);
+                                                   h_rsrc, seg_voff(tm, j), 0, 0);
             // columns past N contribute nothing (their residual reads and sums are zero)
 #pragma unroll
             for (int off = S::kSegPerRow / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, S::kSegPerRow);
@@ -117,7 +123,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     }
     __syncthreads();
     const int T = tiles_n;
-    for (int r = threadIdx.x; r < BM; r += kThreads) {
+    for (int r = threadIdx.x; r < BM; r += NT) {
         const int m = m0 + r;
         if (m < M) {
             float s = 0.0f;
@@ -133,9 +139,17 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #ifndef CODA_G1_BM
 #define CODA_G1_BM 256
 #define CODA_G1_BN 256
+#define CODA_G1_WM 2
+#define CODA_G1_WN 4
+#define CODA_G1_NS 2
+#define CODA_G1_RB 128
 #define CODA_G1_OCC 1
 #endif
-constexpr int BM1 = CODA_G1_BM, BN1 = CODA_G1_BN, OCC1 = CODA_G1_OCC;
+constexpr int BM1 = CODA_G1_BM, BN1 = CODA_G1_BN, NS1 = CODA_G1_NS, OCC1 = CODA_G1_OCC;
+constexpr int RB1 = CODA_G1_RB;
+// the 8-bit mainloop has one MFMA k-step per 64-byte k-tile: it needs an even stage count
+constexpr int NS1_8 = (RB1 == 64 && NS1 % 2) ? NS1 + 1 : NS1;
+constexpr int WM1 = CODA_G1_WM, WN1 = CODA_G1_WN;
 
 int64_t partials_per_row(int64_t N) { return N < 1 ? -1 : (N + BN1 - 1) / BN1; }
 
@@ -146,14 +160,14 @@ hipError_t launch_gemm_resid_partialrms(int M, int N, int K, const void* A, bool
                                         const float* w_scale, const void* x_res, void* h,
                                         float* P, hipStream_t stream) {
     const int tiles_m = (M + BM1 - 1) / BM1, tiles_n = (N + BN1 - 1) / BN1;
-    const dim3 grid(tiles_m * tiles_n), block(kThreads);
+    const dim3 grid(tiles_m * tiles_n), block(64 * WM1 * WN1);
     if (fp8) {
-        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, OCC1, Elt::E4M3>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1_8, RB1, OCC1, Elt::E4M3>), grid, block, 0,
                            stream, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W),
                            a_scale, w_scale, static_cast<const uint16_t*>(x_res),
                            static_cast<uint16_t*>(h), P, M, N, K, tiles_m, tiles_n);
     } else {
-        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, OCC1, Elt::BF16>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1, RB1, OCC1, Elt::BF16>), grid, block, 0,
                            stream, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W),
                            a_scale, w_scale, static_cast<const uint16_t*>(x_res),
                            static_cast<uint16_t*>(h), P, M, N, K, tiles_m, tiles_n);

@@ -23,23 +23,22 @@ namespace coda {
 
 // Epilogue shared by both variants.  Wave (wm, wn) holds TM x TN 32x32 accumulator blocks;
 // with SwiGLU, blocks [0, TN/2) are gate columns and [TN/2, TN) the matching up columns.
-// Per 32-row slab: r (times sw) is applied lane-locally to both accumulators before the
-// SiLU; the finished fp32 outputs are staged row-major in the wave's LDS region `slab`
+// Per 32-row slab: r (times sw; the tile's r values were brought into LDS by the
+// prologue) is applied lane-locally to both accumulators before the SiLU; the finished fp32 outputs are staged row-major in the wave's LDS region `slab`
 // and written as 16-byte runs of 8 bf16.  Rows / columns outside y are masked by the
 // buffer range check.
-template <int BM, int BN, int TM, int TN, bool SWIGLU>
+template <int BM, int BN, int WAVES_M, int TM, int TN, bool SWIGLU>
 __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
-                                                  const float* __restrict__ R, float sw,
+                                                  const float* r_tile, float sw,
                                                   uint16_t* __restrict__ Y, int M, int N_out,
                                                   int m0, int j0, int wm, int wn, uint8_t* slab) {
-    constexpr int WM = BM / 2;
+    constexpr int WM = BM / WAVES_M;
     constexpr int NB = SWIGLU ? TN / 2 : TN;          // output blocks per wave
     using S = Slab<NB>;
     const int lane = threadIdx.x & 63;
     const int lh = lane >> 5;
     const int valid_rows = min(BM, M - m0);
     const uint32_t row_bytes = static_cast<uint32_t>(N_out) * 2;
-    const __amdgpu_buffer_rsrc_t r_rsrc = make_buffer_rsrc(R + m0, static_cast<uint32_t>(valid_rows) * 4);
     const __amdgpu_buffer_rsrc_t y_rsrc =
         make_buffer_rsrc(Y + static_cast<size_t>(m0) * N_out, static_cast<uint32_t>(valid_rows) * row_bytes);
 #pragma unroll
@@ -48,10 +47,9 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
         float rr[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const uint32_t row = static_cast<uint32_t>(wm * WM + tm * 32 + 8 * g + 4 * lh);
-            const i32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(r_rsrc, row * 4, 0, 0);
+            const f32x4_t q = *reinterpret_cast<const f32x4_t*>(r_tile + wm * WM + tm * 32 + 8 * g + 4 * lh);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rr[4 * g + e] = __int_as_float(q[e]) * sw;
+            for (int e = 0; e < 4; ++e) rr[4 * g + e] = q[e] * sw;
         }
         float v[NB][16];
 #pragma unroll
@@ -84,31 +82,43 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
 }
 
 // bf16 weights: direct-to-LDS mainloop.
-template <int BM, int BN, int OCC, bool SWIGLU>
-__global__ void __launch_bounds__(kThreads, OCC)
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int OCC, bool SWIGLU>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
                        uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
                        int tiles_n) {
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
     static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs gate and up blocks");
     constexpr int BNO = SWIGLU ? BN / 2 : BN;       // output columns of one block tile
 
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[(BM + BN) * kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[(BM + BN) * kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[(BM + BN) * kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st3[(BM + BN) * kTileBytes];
+    constexpr int kStage = (BM + BN) * RB;
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+    // one 1 KB DMA instruction fills r_tile: it holds 256 floats whatever BM is
+    __shared__ __attribute__((aligned(16))) float r_tile[256];
+    uint8_t* st[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) st[i] = stages[i];
 
     int tile_m, tile_n;
     tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, j0 = tile_n * BNO;
     const int wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    // the tile's row scales (BM floats) go straight to LDS ahead of the mainloop; rows
+    // past M read zero.  They are the oldest DMA of wave 0, so the mainloop's waits and
+    // its final drain cover them.
+    static_assert(BM <= 256, "one 1 KB DMA instruction carries the tile's r values");
+    if (wave == 0)
+        dma16(make_rsrc(R + m0, static_cast<uint32_t>(min(BM, M - m0)) * 4),
+              static_cast<uint32_t>(threadIdx.x & 63) * 16, lds_addr(reinterpret_cast<uint8_t*>(r_tile)));
 
     const int kbytes = K * 2;
-    DmaPanel<BM, BM> pa;
-    DmaPanel<BN, SWIGLU ? BN / 2 : BN> pb;
+    DmaPanel<BM, BM, NW, RB> pa;
+    DmaPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB> pb;
     const uint8_t* a0 = H + static_cast<size_t>(m0) * kbytes;
     pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
     const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes;
@@ -136,11 +146,11 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN)>(acc, pa, pb, kbytes, st0, st1, st2, st3, a_row, b_row);
+    mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NS, NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row);
 
     const float sw = w_scale ? *w_scale : 1.0f;
-    uint8_t* slab = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
-    rowscale_epilogue<BM, BN, TM, TN, SWIGLU>(acc, R, sw, Y, M, N_out, m0, j0, wm, wn, slab);
+    uint8_t* slab = slab_region<NS, NW, kStage, Slab<SWIGLU ? TN / 2 : TN>::kBytes>(st, wave);
+    rowscale_epilogue<BM, BN, WAVES_M, TM, TN, SWIGLU>(acc, r_tile, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
 // 8-bit weights (weight-only): e4m3 decoded exactly to bf16 while staged into LDS
@@ -223,18 +233,26 @@ k_gemm_rowscale_swiglu_w8(const uint8_t* __restrict__ H, const uint8_t* __restri
     }
 
     const float sw = w_scale ? *w_scale : 1.0f;
+    __shared__ __attribute__((aligned(16))) float r_tile[BM];
+    for (int i = threadIdx.x; i < BM; i += kThreads) r_tile[i] = m0 + i < M ? R[m0 + i] : 0.0f;
+    __syncthreads();
     static_assert(4 * Slab<SWIGLU ? TN / 2 : TN>::kBytes <= 2 * (BM + BN) * kRowBytes, "slabs fit");
     uint8_t* slab = &smem[0][0] + wave * Slab<SWIGLU ? TN / 2 : TN>::kBytes;
-    rowscale_epilogue<BM, BN, TM, TN, SWIGLU>(acc, R, sw, Y, M, N_out, m0, j0, wm, wn, slab);
+    rowscale_epilogue<BM, BN, 2, TM, TN, SWIGLU>(acc, r_tile, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
 // Tile configurations of the second GEMM (compile-time).
 #ifndef CODA_G3_BM
 #define CODA_G3_BM 256
 #define CODA_G3_BN 256
+#define CODA_G3_WM 2
+#define CODA_G3_WN 4
+#define CODA_G3_NS 2
+#define CODA_G3_RB 128
 #define CODA_G3_OCC 1
 #endif
-constexpr int BM3 = CODA_G3_BM, BN3 = CODA_G3_BN, OCC3 = CODA_G3_OCC;
+constexpr int BM3 = CODA_G3_BM, BN3 = CODA_G3_BN, NS3 = CODA_G3_NS, OCC3 = CODA_G3_OCC;
+constexpr int WM3 = CODA_G3_WM, WN3 = CODA_G3_WN, RB3 = CODA_G3_RB;
 constexpr int BM3W8 = 128, BN3W8 = 128;   // 8-bit weights: register-staged, 2 blocks per CU
 
 int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
@@ -250,13 +268,13 @@ static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
     constexpr int BM = WFP8 ? BM3W8 : BM3, BN = WFP8 ? BN3W8 : BN3;
     constexpr int BNO = SWIGLU ? BN / 2 : BN;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N_out + BNO - 1) / BNO;
-    const dim3 grid(tiles_m * tiles_n), block(kThreads);
+    const dim3 grid(tiles_m * tiles_n), block(WFP8 ? kThreads : 64 * WM3 * WN3);
     if constexpr (WFP8) {
         hipLaunchKernelGGL((k_gemm_rowscale_swiglu_w8<BM, BN, 2, SWIGLU>), grid, block, 0, stream,
                            static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale,
                            r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
     } else {
-        hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM, BN, OCC3, SWIGLU>), grid, block, 0, stream,
+        hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM, BN, WM3, WN3, NS3, RB3, OCC3, SWIGLU>), grid, block, 0, stream,
                            static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale,
                            r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
     }
