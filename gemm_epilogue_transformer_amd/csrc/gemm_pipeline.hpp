@@ -149,16 +149,19 @@ struct Frags<Elt::BF16, TM, TN, RB> {
     static constexpr int kSteps = RB / 32;
     static constexpr int kReads = TM + TN;         // ds_read_b128 per k-step
     bf16x8_t a[TM], b[TN];
-    // fragment read i of k-step s: i < TM -> a[i], else b[i - TM]
+    // fragment read i of k-step s, in the order the k-step's MFMAs first use them
+    // (MFMA j uses a[j / TN] and b[j % TN]): a[0], b[0..TN-1], a[1..TM-1]
     template <class ARow, class BRow>
     __device__ __forceinline__ void load_one(int i, const uint8_t* sA, const uint8_t* sB, int s,
                                              const ARow& a_row, const BRow& b_row) {
         const int lane = threadIdx.x & 63;
         const int lr = lane & 31, lh = lane >> 5;
-        if (i < TM)
-            a[i] = *reinterpret_cast<const bf16x8_t*>(sA + swz<RB>(a_row(i) + lr, 2 * s + lh));
+        if (i == 0)
+            a[0] = *reinterpret_cast<const bf16x8_t*>(sA + swz<RB>(a_row(0) + lr, 2 * s + lh));
+        else if (i <= TN)
+            b[i - 1] = *reinterpret_cast<const bf16x8_t*>(sB + swz<RB>(b_row(i - 1) + lr, 2 * s + lh));
         else
-            b[i - TM] = *reinterpret_cast<const bf16x8_t*>(sB + swz<RB>(b_row(i - TM) + lr, 2 * s + lh));
+            a[i - TN] = *reinterpret_cast<const bf16x8_t*>(sA + swz<RB>(a_row(i - TN) + lr, 2 * s + lh));
     }
     template <class ARow, class BRow>
     __device__ __forceinline__ void load(const uint8_t* sA, const uint8_t* sB, int s,
@@ -182,19 +185,21 @@ struct Frags<Elt::E4M3, TM, TN, RB> {
     static constexpr int kSteps = RB / 64;
     static constexpr int kReads = TM + TN;         // fragments (two ds_read_b128 each)
     i32x8_t a[TM], b[TN];
-    // fragment i of k-step s: lane holds 32 bytes of its row = chunks 4s + 2*lh, +1
+    // fragment i of k-step s (lane holds 32 bytes of its row = chunks 4s + 2*lh, +1), in
+    // the order the k-step's MFMAs first use them: a[0], b[0..TN-1], a[1..TM-1]
     template <class ARow, class BRow>
     __device__ __forceinline__ void load_one(int i, const uint8_t* sA, const uint8_t* sB, int s,
                                              const ARow& a_row, const BRow& b_row) {
         const int lane = threadIdx.x & 63;
         const int lr = lane & 31, lh = lane >> 5;
-        const bool isa = i < TM;
-        const int row = (isa ? a_row(i) : b_row(i - TM)) + lr;
+        const bool isa = i == 0 || i > TN;
+        const int idx = i == 0 ? 0 : (i <= TN ? i - 1 : i - TN);
+        const int row = (isa ? a_row(idx) : b_row(idx)) + lr;
         const uint8_t* base = isa ? sA : sB;
         const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + swz<RB>(row, 4 * s + 2 * lh));
         const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + swz<RB>(row, 4 * s + 2 * lh + 1));
         const i32x8_t v = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if (isa) a[i] = v; else b[i - TM] = v;
+        if (isa) a[idx] = v; else b[idx] = v;
     }
     template <class ARow, class BRow>
     __device__ __forceinline__ void load(const uint8_t* sA, const uint8_t* sB, int s,
