@@ -245,7 +245,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 // (one instruction per MFMA) together with the reads of tile kt+1's first fragments.
 // The DMA thus runs NS tiles ahead of the reads, and tiles kt+2 .. kt+NS-1 may still be
 // in flight at the barrier of tile kt.
-template <Elt E, int BM, int BN, int SPLIT, int NS, int NW, int RB, int TM, int TN, class ARow, class BRow>
+//
+// SPREAD (1 .. k-steps per tile) spreads the DMA of tile kt+NS over SPREAD k-steps: the
+// last k-step of tile kt and the first SPREAD-1 k-steps of tile kt+1, at most
+// ceil(kPerTile / SPREAD) instructions per k-step.  A wave whose DMA instructions back up
+// in the memory pipeline stops issuing MFMAs too, so a burst of them in one k-step
+// stalls the wave and skews it against the others at the next barrier.  Every
+// instruction of tile kt+NS is still issued before the last k-step of tile kt+1, so the
+// wait counts above hold unchanged.  The prologue issues tile NS-1 the same way (its
+// first share up front, the rest during tile 0).
+template <Elt E, int BM, int BN, int SPLIT, int NS, int NW, int RB, int SPREAD, int TM, int TN, class ARow,
+          class BRow>
 __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
                                              const DmaPanel<BN, SPLIT, NW, RB>& pb, int kbytes,
                                              uint8_t* const (&st)[NS], const ARow& a_row,
@@ -258,7 +268,9 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
     constexpr int nA = DmaPanel<BM, BM, NW, RB>::kInst;
     constexpr int kPerTile = nA + DmaPanel<BN, SPLIT, NW, RB>::kInst;   // DMA per wave per tile
     static_assert((NS - 1) * kPerTile < 64, "vmcnt range");
-    static_assert(kPerTile <= kMfma, "one MFMA ahead of every DMA instruction");
+    static_assert(SPREAD >= 1 && SPREAD <= KS, "the DMA of a tile ends before the next tile's last k-step");
+    constexpr int kPer = (kPerTile + SPREAD - 1) / SPREAD;            // DMA per k-step
+    static_assert(kPer <= kMfma, "one MFMA ahead of every DMA instruction");
     const int nk = (kbytes + RB - 1) / RB;
     // k-tiles run in groups of NS (one per stage); the count is padded to a multiple of NS
     // with k-tiles past K, which the DMA fills with zeros.  The DMA always runs NS tiles
@@ -266,12 +278,21 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
     // wait counts are exact on every tile.
     const int ng = (nk + NS - 1) / NS;
     F f[2];
-    static_for<NS>([&](auto I) {
+    // DMA instruction q (0 .. kPerTile-1) of the tile with base offsets (ba, bb)
+    auto issue_q = [&](int q, uint8_t* stage, uint32_t ba, uint32_t bb) {
+        if (q < nA) pa.issue_one(q, stage, ba);
+        else pb.issue_one(q - nA, stage + BM * RB, bb);
+    };
+    static_for<NS - 1>([&](auto I) {
         constexpr int i = decltype(I)::value;
         pa.issue(st[i], i, kbytes);
         pb.issue(st[i] + BM * RB, i, kbytes);
     });
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 1) * kPerTile));   // tile 0 landed
+    // tile NS-1: its first share now, the rest as pending DMA during tile 0
+    uint32_t pend_a = pa.base_offset(NS - 1, kbytes);
+    uint32_t pend_b = pb.base_offset(NS - 1, kbytes);
+    static_for<kPer>([&](auto Q) { issue_q(decltype(Q)::value, st[NS - 1], pend_a, pend_b); });
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile + kPer));   // tile 0 landed
     __syncthreads();
     f[0].load(st[0], st[0] + BM * RB, 0, a_row, b_row);
 
@@ -281,13 +302,17 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
             constexpr int par = (i * KS) & 1;     // k-step s of this tile uses f[(par + s) & 1]
             uint8_t* cur = st[i];
             uint8_t* nxt = st[(i + 1) % NS];
+            uint8_t* prv = st[(i + NS - 1) % NS];    // stage receiving the pending DMA
             const int kt = g * NS + i;
 #pragma unroll
             for (int s = 0; s < KS - 1; ++s) {
-                // k-step s: MFMA j, then fragment read j of k-step s+1
+                // k-step s: MFMA j, then pending DMA instruction (s+1)*kPer + j, then
+                // fragment read j of k-step s+1
                 static_for<kMfma>([&](auto J) {
                     constexpr int j = decltype(J)::value;
                     f[(par + s) & 1].mma_one(j, acc);
+                    if (s + 1 < SPREAD && j < kPer && (s + 1) * kPer + j < kPerTile)
+                        issue_q((s + 1) * kPer + j, prv, pend_a, pend_b);
                     if (j < F::kReads) f[(par + s + 1) & 1].load_one(j, cur, cur + BM * RB, s + 1, a_row, b_row);
                     __builtin_amdgcn_sched_barrier(0);
                 });
@@ -296,15 +321,15 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
             __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile));  // tile kt+1 landed
             __syncthreads();                                             // ... for every wave
             __builtin_amdgcn_sched_barrier(0);
-            const uint32_t base_a = pa.base_offset(kt + NS, kbytes);
-            const uint32_t base_b = pb.base_offset(kt + NS, kbytes);
-            // MFMA j, then DMA instruction j of tile kt+NS into this tile's stage, then
-            // fragment read j of tile kt+1's first k-step
+            pend_a = pa.base_offset(kt + NS, kbytes);
+            pend_b = pb.base_offset(kt + NS, kbytes);
+            // MFMA j, then DMA instruction j of tile kt+NS into this tile's stage (the
+            // first kPer; the rest follow in tile kt+1), then fragment read j of tile
+            // kt+1's first k-step
             static_for<kMfma>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 f[(par + KS - 1) & 1].mma_one(j, acc);
-                if (j < nA) pa.issue_one(j, cur, base_a);
-                else if (j < kPerTile) pb.issue_one(j - nA, cur + BM * RB, base_b);
+                if (j < kPer) issue_q(j, cur, pend_a, pend_b);
                 if (j < F::kReads) f[(par + KS) & 1].load_one(j, nxt, nxt + BM * RB, 0, a_row, b_row);
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -312,6 +337,149 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
     }
     // drain the DMA that ran past the end before the LDS is reused or released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------
+// Register-staged variant: global -> VGPR -> LDS.
+//
+// The same panels, stage layout (swz) and fragments as above, but every lane loads its
+// 16-byte chunks into registers (buffer_load_dwordx4, range-checked like the DMA) and
+// writes them to LDS with ds_write_b128.  The registers form a third stage ahead of the
+// two LDS stages, so a tile's global loads are issued one full tile before they are
+// written to LDS, and each load is waited for individually, right before its write,
+// instead of all of them at the barrier.
+template <int R, int SPLIT, int NW, int RB>
+struct RegPanel {
+    static constexpr int kCpr = RB / 16;
+    static constexpr int kRpi = 1024 / RB;
+    static constexpr int kRowsPerInst = kRpi * NW;
+    static_assert(R % kRowsPerInst == 0 && SPLIT % kRowsPerInst == 0 && SPLIT <= R, "panel geometry");
+    static constexpr int kInst = R / kRowsPerInst;  // loads per wave per k-tile
+    static constexpr int kSplitInst = SPLIT / kRowsPerInst;
+    __amdgpu_buffer_rsrc_t rsrc[2];
+    uint32_t off0;        // byte offset of this lane's chunk in load 0 at k-tile 0
+    uint32_t chunk_byte;
+    uint32_t stride;      // bytes between load j and j+1 (same segment)
+    int lds0;             // LDS offset (in a stage panel) of this lane's chunk in load 0
+
+    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
+        const uint64_t p = reinterpret_cast<uint64_t>(base);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+        const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+        void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+        return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, static_cast<int>(n), 0x00020000);
+    }
+    __device__ __forceinline__ void init(const uint8_t* seg_base0, int seg_rows0,
+                                         const uint8_t* seg_base1, int seg_rows1, int kbytes) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        rsrc[0] = rsrc_of(seg_base0, static_cast<uint32_t>(max(seg_rows0, 0)) * kbytes);
+        rsrc[1] = rsrc_of(seg_base1, static_cast<uint32_t>(max(seg_rows1, 0)) * kbytes);
+        // load j of this lane: row (NW*j + wave) * kRpi + lane / kCpr, chunk lane % kCpr;
+        // the swizzle phase of the row does not depend on j (NW*kRpi rows apart)
+        const int r = wave * kRpi + lane / kCpr;
+        const int chunk = lane % kCpr;
+        chunk_byte = static_cast<uint32_t>(chunk) << 4;
+        off0 = static_cast<uint32_t>(r) * kbytes + chunk_byte;
+        stride = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kRowsPerInst) * static_cast<uint32_t>(kbytes));
+        lds0 = swz<RB>(r, chunk);
+    }
+    __device__ __forceinline__ uint32_t base_offset(int kt, int kbytes) const {
+        const uint32_t kb = static_cast<uint32_t>(kt) * RB;
+        const bool kin = kb + chunk_byte < static_cast<uint32_t>(kbytes);
+        uint32_t base = kin ? off0 + kb : kOob;
+        asm volatile("" : "+v"(base));
+        return base;
+    }
+    __device__ __forceinline__ i32x4_t load_one(int j, uint32_t base) const {
+        const int jj = (j < kSplitInst) ? j : j - kSplitInst;
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc[(j < kSplitInst) ? 0 : 1],
+                                                     base + static_cast<uint32_t>(jj) * stride, 0, 0);
+    }
+    __device__ __forceinline__ void store_one(int j, uint8_t* panel, const i32x4_t& v) const {
+        *reinterpret_cast<i32x4_t*>(panel + lds0 + j * kRowsPerInst * RB) = v;
+    }
+};
+
+// Two LDS stages + one register stage.  Per k-tile kt (reading stage kt%2):
+//   k-steps 0 .. KS-2: the registers holding tile kt+1 are written to stage (kt+1)%2
+//     (free since the barrier of tile kt-1), and each register is reloaded right after
+//     its write with the same chunk of tile kt+2;
+//   last k-step: wait for the own LDS writes, barrier (tile kt+1 complete in LDS, stage
+//     kt%2 read by every wave), then MFMAs with the reads of tile kt+1's first fragments.
+template <Elt E, int BM, int BN, int SPLIT, int NW, int RB, int TM, int TN, class ARow, class BRow>
+__device__ __forceinline__ void mainloop_reg(f32x16_t (&acc)[TM][TN], const RegPanel<BM, BM, NW, RB>& pa,
+                                             const RegPanel<BN, SPLIT, NW, RB>& pb, int kbytes,
+                                             uint8_t* const (&st)[2], const ARow& a_row,
+                                             const BRow& b_row) {
+    using F = Frags<E, TM, TN, RB>;
+    constexpr int KS = F::kSteps;
+    static_assert(KS >= 2, "writes go in the k-steps before the last");
+    constexpr int kMfma = TM * TN;
+    constexpr int nA = RegPanel<BM, BM, NW, RB>::kInst;
+    constexpr int kPerTile = nA + RegPanel<BN, SPLIT, NW, RB>::kInst;
+    constexpr int kPer = (kPerTile + KS - 2) / (KS - 1);      // writes per k-step
+    static_assert(2 * kPer <= kMfma + 1, "one write + load per odd MFMA slot");
+    const int nk = (kbytes + RB - 1) / RB;
+    const int ng = (nk + 1) / 2;
+    i32x4_t g[kPerTile];
+    auto load_q = [&](int q, uint32_t ba, uint32_t bb) {
+        g[q] = q < nA ? pa.load_one(q, ba) : pb.load_one(q - nA, bb);
+    };
+    auto store_q = [&](int q, uint8_t* stage) {
+        if (q < nA) pa.store_one(q, stage, g[q]);
+        else pb.store_one(q - nA, stage + BM * RB, g[q]);
+    };
+    F f[2];
+    {
+        uint32_t ba = pa.base_offset(0, kbytes), bb = pb.base_offset(0, kbytes);
+        static_for<kPerTile>([&](auto Q) { load_q(decltype(Q)::value, ba, bb); });
+        static_for<kPerTile>([&](auto Q) { store_q(decltype(Q)::value, st[0]); });
+        ba = pa.base_offset(1, kbytes); bb = pb.base_offset(1, kbytes);
+        static_for<kPerTile>([&](auto Q) { load_q(decltype(Q)::value, ba, bb); });
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    f[0].load(st[0], st[0] + BM * RB, 0, a_row, b_row);
+
+    for (int gi = 0; gi < ng; ++gi) {
+        static_for<2>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            constexpr int par = (i * KS) & 1;
+            uint8_t* cur = st[i];
+            uint8_t* nxt = st[i ^ 1];
+            const int kt = gi * 2 + i;
+            const uint32_t ba = pa.base_offset(kt + 2, kbytes);
+            const uint32_t bb = pb.base_offset(kt + 2, kbytes);
+#pragma unroll
+            for (int s = 0; s < KS - 1; ++s) {
+                // MFMA j; fragment read j of k-step s+1; on odd slots, register chunk q of
+                // tile kt+1 to LDS, then its reload with tile kt+2
+                static_for<kMfma>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    f[(par + s) & 1].mma_one(j, acc);
+                    if (j < F::kReads) f[(par + s + 1) & 1].load_one(j, cur, cur + BM * RB, s + 1, a_row, b_row);
+                    if (j % 2 == 1) {
+                        const int q = s * kPer + j / 2;
+                        if (j / 2 < kPer && q < kPerTile) {
+                            store_q(q, nxt);
+                            load_q(q, ba, bb);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<kMfma>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                f[(par + KS - 1) & 1].mma_one(j, acc);
+                if (j < F::kReads) f[(par + KS) & 1].load_one(j, nxt, nxt + BM * RB, 0, a_row, b_row);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    }
     __syncthreads();
 }
 

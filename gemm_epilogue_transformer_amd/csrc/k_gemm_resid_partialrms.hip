@@ -15,7 +15,7 @@
 
 namespace coda {
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int OCC, Elt E>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC, Elt E>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
                         const float* __restrict__ a_scale, const float* __restrict__ w_scale,
@@ -57,7 +57,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    mainloop_dma<E, BM, BN, BN, NS, NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row);
+    mainloop_dma<E, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
 
     // ---------------------------------------------------------------- epilogue ----
     // Per 32-row slab of this wave: stage scale*acc row-major in the wave's own (now
@@ -140,16 +140,22 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #define CODA_G1_BM 256
 #define CODA_G1_BN 256
 #define CODA_G1_WM 2
-#define CODA_G1_WN 4
+#define CODA_G1_WN 2
 #define CODA_G1_NS 2
 #define CODA_G1_RB 128
 #define CODA_G1_OCC 1
+#endif
+#ifndef CODA_G1_SPREAD
+#define CODA_G1_SPREAD 2
 #endif
 constexpr int BM1 = CODA_G1_BM, BN1 = CODA_G1_BN, NS1 = CODA_G1_NS, OCC1 = CODA_G1_OCC;
 constexpr int RB1 = CODA_G1_RB;
 // the 8-bit mainloop has one MFMA k-step per 64-byte k-tile: it needs an even stage count
 constexpr int NS1_8 = (RB1 == 64 && NS1 % 2) ? NS1 + 1 : NS1;
 constexpr int WM1 = CODA_G1_WM, WN1 = CODA_G1_WN;
+// k-steps the DMA of a k-tile is spread over (at most the k-steps of a k-tile: RB/32 for
+// bf16, RB/64 for e4m3)
+constexpr int SP1 = CODA_G1_SPREAD, SP1_8 = SP1 < RB1 / 64 ? SP1 : RB1 / 64;
 
 int64_t partials_per_row(int64_t N) { return N < 1 ? -1 : (N + BN1 - 1) / BN1; }
 
@@ -162,12 +168,12 @@ hipError_t launch_gemm_resid_partialrms(int M, int N, int K, const void* A, bool
     const int tiles_m = (M + BM1 - 1) / BM1, tiles_n = (N + BN1 - 1) / BN1;
     const dim3 grid(tiles_m * tiles_n), block(64 * WM1 * WN1);
     if (fp8) {
-        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1_8, RB1, OCC1, Elt::E4M3>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1_8, RB1, SP1_8, OCC1, Elt::E4M3>), grid, block, 0,
                            stream, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W),
                            a_scale, w_scale, static_cast<const uint16_t*>(x_res),
                            static_cast<uint16_t*>(h), P, M, N, K, tiles_m, tiles_n);
     } else {
-        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1, RB1, OCC1, Elt::BF16>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1, RB1, SP1, OCC1, Elt::BF16>), grid, block, 0,
                            stream, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W),
                            a_scale, w_scale, static_cast<const uint16_t*>(x_res),
                            static_cast<uint16_t*>(h), P, M, N, K, tiles_m, tiles_n);

@@ -23,13 +23,17 @@ namespace coda {
 
 // Epilogue shared by both variants.  Wave (wm, wn) holds TM x TN 32x32 accumulator blocks;
 // with SwiGLU, blocks [0, TN/2) are gate columns and [TN/2, TN) the matching up columns.
-// Per 32-row slab: r (times sw; the tile's r values were brought into LDS by the
-// prologue) is applied lane-locally to both accumulators before the SiLU; the finished fp32 outputs are staged row-major in the wave's LDS region `slab`
+// Per 32-row slab: r (times sw) is applied lane-locally to both accumulators before the
+// SiLU; the finished fp32 outputs are staged row-major in the wave's LDS region `slab`
 // and written as 16-byte runs of 8 bf16.  Rows / columns outside y are masked by the
 // buffer range check.
+//
+// r of the wave's WM rows lives in registers: lane l holds rows l, 64 + l, ... of the
+// wave (rv[WM / 64]), loaded before the mainloop; the epilogue fetches the rows it needs
+// with cross-lane permutes, so r takes no LDS (the stages may fill all of it).
 template <int BM, int BN, int WAVES_M, int TM, int TN, bool SWIGLU>
 __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
-                                                  const float* r_tile, float sw,
+                                                  const float (&rv)[BM / WAVES_M / 64], float sw,
                                                   uint16_t* __restrict__ Y, int M, int N_out,
                                                   int m0, int j0, int wm, int wn, uint8_t* slab) {
     constexpr int WM = BM / WAVES_M;
@@ -46,11 +50,10 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
         // r of the 16 rows this lane holds: rows 8g + 4*lh + (0..3), g = 0..3
         float rr[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4_t q = *reinterpret_cast<const f32x4_t*>(r_tile + wm * WM + tm * 32 + 8 * g + 4 * lh);
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rr[4 * g + e] = q[e] * sw;
-        }
+            for (int e = 0; e < 4; ++e)
+                rr[4 * g + e] = __shfl(rv[tm / 2], (tm % 2) * 32 + 8 * g + 4 * lh + e) * sw;
         float v[NB][16];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -82,7 +85,7 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
 }
 
 // bf16 weights: direct-to-LDS mainloop.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int OCC, bool SWIGLU>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int PIPE, int OCC, bool SWIGLU>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
@@ -96,8 +99,6 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 
     constexpr int kStage = (BM + BN) * RB;
     __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
-    // one 1 KB DMA instruction fills r_tile: it holds 256 floats whatever BM is
-    __shared__ __attribute__((aligned(16))) float r_tile[256];
     uint8_t* st[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) st[i] = stages[i];
@@ -108,17 +109,22 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    // the tile's row scales (BM floats) go straight to LDS ahead of the mainloop; rows
-    // past M read zero.  They are the oldest DMA of wave 0, so the mainloop's waits and
-    // its final drain cover them.
-    static_assert(BM <= 256, "one 1 KB DMA instruction carries the tile's r values");
-    if (wave == 0)
-        dma16(make_rsrc(R + m0, static_cast<uint32_t>(min(BM, M - m0)) * 4),
-              static_cast<uint32_t>(threadIdx.x & 63) * 16, lds_addr(reinterpret_cast<uint8_t*>(r_tile)));
+    // r of this wave's rows (lane l: rows l, 64 + l, ...), loaded now so that its latency
+    // hides behind the mainloop; rows past M hold 0
+    static_assert(WM % 64 == 0, "each lane holds WM / 64 row scales");
+    float rv[WM / 64];
+#pragma unroll
+    for (int i = 0; i < WM / 64; ++i) {
+        const int m = m0 + wm * WM + 64 * i + (threadIdx.x & 63);
+        rv[i] = m < M ? R[m] : 0.0f;
+    }
 
     const int kbytes = K * 2;
-    DmaPanel<BM, BM, NW, RB> pa;
-    DmaPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB> pb;
+    using PanelA = std::conditional_t<PIPE == 1, RegPanel<BM, BM, NW, RB>, DmaPanel<BM, BM, NW, RB>>;
+    using PanelB = std::conditional_t<PIPE == 1, RegPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB>,
+                                      DmaPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB>>;
+    PanelA pa;
+    PanelB pb;
     const uint8_t* a0 = H + static_cast<size_t>(m0) * kbytes;
     pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
     const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes;
@@ -146,11 +152,16 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NS, NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row);
+    if constexpr (PIPE == 1) {
+        static_assert(NS == 2, "the register-staged mainloop has two LDS stages");
+        mainloop_reg<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row);
+    } else {
+        mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
+    }
 
     const float sw = w_scale ? *w_scale : 1.0f;
     uint8_t* slab = slab_region<NS, NW, kStage, Slab<SWIGLU ? TN / 2 : TN>::kBytes>(st, wave);
-    rowscale_epilogue<BM, BN, WAVES_M, TM, TN, SWIGLU>(acc, r_tile, sw, Y, M, N_out, m0, j0, wm, wn, slab);
+    rowscale_epilogue<BM, BN, WAVES_M, TM, TN, SWIGLU>(acc, rv, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
 // 8-bit weights (weight-only): e4m3 decoded exactly to bf16 while staged into LDS
@@ -233,12 +244,17 @@ k_gemm_rowscale_swiglu_w8(const uint8_t* __restrict__ H, const uint8_t* __restri
     }
 
     const float sw = w_scale ? *w_scale : 1.0f;
-    __shared__ __attribute__((aligned(16))) float r_tile[BM];
-    for (int i = threadIdx.x; i < BM; i += kThreads) r_tile[i] = m0 + i < M ? R[m0 + i] : 0.0f;
-    __syncthreads();
+    // r of this wave's rows (lane l: rows l, 64 + l, ...); rows past M hold 0.  The
+    // mainloop's last barrier already frees smem for the slabs.
+    float rv[WM / 64];
+#pragma unroll
+    for (int i = 0; i < WM / 64; ++i) {
+        const int m = m0 + wm * WM + 64 * i + (threadIdx.x & 63);
+        rv[i] = m < M ? R[m] : 0.0f;
+    }
     static_assert(4 * Slab<SWIGLU ? TN / 2 : TN>::kBytes <= 2 * (BM + BN) * kRowBytes, "slabs fit");
     uint8_t* slab = &smem[0][0] + wave * Slab<SWIGLU ? TN / 2 : TN>::kBytes;
-    rowscale_epilogue<BM, BN, 2, TM, TN, SWIGLU>(acc, r_tile, sw, Y, M, N_out, m0, j0, wm, wn, slab);
+    rowscale_epilogue<BM, BN, 2, TM, TN, SWIGLU>(acc, rv, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
 // Tile configurations of the second GEMM (compile-time).
@@ -246,13 +262,19 @@ k_gemm_rowscale_swiglu_w8(const uint8_t* __restrict__ H, const uint8_t* __restri
 #define CODA_G3_BM 256
 #define CODA_G3_BN 256
 #define CODA_G3_WM 2
-#define CODA_G3_WN 4
+#define CODA_G3_WN 2
 #define CODA_G3_NS 2
 #define CODA_G3_RB 128
 #define CODA_G3_OCC 1
 #endif
+#ifndef CODA_G3_SPREAD
+#define CODA_G3_SPREAD 2
+#endif
+#ifndef CODA_G3_PIPE
+#define CODA_G3_PIPE 0
+#endif
 constexpr int BM3 = CODA_G3_BM, BN3 = CODA_G3_BN, NS3 = CODA_G3_NS, OCC3 = CODA_G3_OCC;
-constexpr int WM3 = CODA_G3_WM, WN3 = CODA_G3_WN, RB3 = CODA_G3_RB;
+constexpr int WM3 = CODA_G3_WM, WN3 = CODA_G3_WN, RB3 = CODA_G3_RB, SP3 = CODA_G3_SPREAD, PIPE3 = CODA_G3_PIPE;
 constexpr int BM3W8 = 128, BN3W8 = 128;   // 8-bit weights: register-staged, 2 blocks per CU
 
 int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
@@ -274,7 +296,7 @@ static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                            static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale,
                            r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
     } else {
-        hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM, BN, WM3, WN3, NS3, RB3, OCC3, SWIGLU>), grid, block, 0, stream,
+        hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM, BN, WM3, WN3, NS3, RB3, SP3, PIPE3, OCC3, SWIGLU>), grid, block, 0, stream,
                            static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale,
                            r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
     }
