@@ -26,9 +26,15 @@
 #include <type_traits>
 #include <utility>
 
-#include "gemm_core.hpp"
+#include "device_common.hpp"
 
 namespace coda {
+
+// Operand element kinds and their sizes.
+enum class Elt { BF16, E4M3 };
+template <Elt E> struct EltInfo;
+template <> struct EltInfo<Elt::BF16> { static constexpr int kBytes = 2; };
+template <> struct EltInfo<Elt::E4M3> { static constexpr int kBytes = 1; };
 
 constexpr uint32_t kOob = 0x80000000u;  // offset that no descriptor range reaches
 
@@ -219,10 +225,6 @@ struct Frags<Elt::E4M3, TM, TN, RB> {
     }
 };
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
-// vmcnt_hi[15:14]); expcnt / lgkmcnt are left at their maxima.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 // Compile-time loop: f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>).
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -232,6 +234,92 @@ template <int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
+
+// The fragments of two consecutive k-steps (parity p = k-step & 1), as the mainloop
+// drives them: mma_one(p, j) is MFMA j of a k-step, slot<J>(p, ...) the LDS work of slot
+// J that prepares the next k-step (here: fragment read J).
+template <class F>
+struct FragPair {
+    static constexpr int kSteps = F::kSteps;
+    F f[2];
+    template <int J, class ARow, class BRow>
+    __device__ __forceinline__ void slot(int p, const uint8_t* sA, const uint8_t* sB, int s,
+                                         const ARow& a_row, const BRow& b_row) {
+        if constexpr (J < F::kReads) f[p].load_one(J, sA, sB, s, a_row, b_row);
+    }
+    template <class ARow, class BRow>
+    __device__ __forceinline__ void load(int p, const uint8_t* sA, const uint8_t* sB, int s,
+                                         const ARow& a_row, const BRow& b_row) {
+        f[p].load(sA, sB, s, a_row, b_row);
+    }
+    template <int TM, int TN>
+    __device__ __forceinline__ void mma_one(int p, int j, f32x16_t (&acc)[TM][TN]) const {
+        f[p].mma_one(j, acc);
+    }
+};
+
+// bf16 activations x e4m3 weights (weight-only 8-bit), bf16 MFMA.  A panel: 128-byte
+// rows (64 bf16 per k-tile); B panel: 64-byte rows (64 e4m3 per k-tile), kept as e4m3 in
+// LDS and converted exactly to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8, scale 1).
+//
+// k order inside a 64-k tile: k-step s = 2t + h gives lane half lh the k values
+// 32t + 16lh + 8h + (0..7) of BOTH operands, i.e. A chunk 4t + 2lh + h of its row and
+// bytes 8h .. 8h+7 of B chunk 2t + lh.  Each k-step still sums over 16 distinct k, so the
+// tile computes the plain product; one 16-byte B read per lane serves two k-steps.
+//
+// Slots of the k-step before step s (parity p = s & 1): A reads in slots 0 .. TM-1; for
+// an even s the raw B reads in slots TM .. TM+TN-1 and the conversion of their low halves
+// in the last TN slots (the reads have had the slots in between to land); for an odd s
+// the conversion of the high halves of the same raw chunks.
+template <int TM, int TN>
+struct FragsW8 {
+    static constexpr int kSteps = 4;
+    static constexpr int kRbA = 128, kRbB = 64;
+    static constexpr int kMfma = TM * TN;
+    static_assert(TM + 2 * TN <= kMfma, "reads and conversions fit the MFMA slots");
+    bf16x8_t a[2][TM], b[2][TN];
+    i32x4_t raw[TN];
+
+    __device__ __forceinline__ static bf16x8_t cvt8(int w0, int w1) {
+        typedef int i32x4v __attribute__((ext_vector_type(4)));
+        const i32x4v q = {__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                          __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                          __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                          __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+        return __builtin_bit_cast(bf16x8_t, q);
+    }
+    template <int J, class ARow, class BRow>
+    __device__ __forceinline__ void slot(int p, const uint8_t* sA, const uint8_t* sB, int s,
+                                         const ARow& a_row, const BRow& b_row) {
+        const int lane = threadIdx.x & 63;
+        const int lr = lane & 31, lh = lane >> 5;
+        const int t = s >> 1, h = s & 1;
+        if constexpr (J < TM) {
+            a[p][J] = *reinterpret_cast<const bf16x8_t*>(sA + swz<kRbA>(a_row(J) + lr, 4 * t + 2 * lh + h));
+        } else if constexpr (J < TM + TN) {
+            if (h == 0)
+                raw[J - TM] = *reinterpret_cast<const i32x4_t*>(sB + swz<kRbB>(b_row(J - TM) + lr, 2 * t + lh));
+        }
+        if constexpr (J >= kMfma - TN) {
+            constexpr int tn = J - (kMfma - TN);
+            b[p][tn] = h == 0 ? cvt8(raw[tn][0], raw[tn][1]) : cvt8(raw[tn][2], raw[tn][3]);
+        }
+    }
+    template <class ARow, class BRow>
+    __device__ __forceinline__ void load(int p, const uint8_t* sA, const uint8_t* sB, int s,
+                                         const ARow& a_row, const BRow& b_row) {
+        static_for<kMfma>([&](auto J) { slot<decltype(J)::value>(p, sA, sB, s, a_row, b_row); });
+    }
+    __device__ __forceinline__ void mma_one(int p, int i, f32x16_t (&acc)[TM][TN]) const {
+        const int tm = i / TN, tn = i % TN;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p][tm], b[p][tn], acc[tm][tn], 0, 0, 0);
+    }
+};
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt_hi[15:14]); expcnt / lgkmcnt are left at their maxima.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 
 // The whole mainloop: acc += A_panel . B_panel^T over the k-tiles of one row.
 // st[0..NS-1] are the NS stage buffers, each (BM + BN) * RB bytes.
@@ -254,47 +342,52 @@ __device__ __forceinline__ void static_for(F&& f) {
 // instruction of tile kt+NS is still issued before the last k-step of tile kt+1, so the
 // wait counts above hold unchanged.  The prologue issues tile NS-1 the same way (its
 // first share up front, the rest during tile 0).
-template <Elt E, int BM, int BN, int SPLIT, int NS, int NW, int RB, int SPREAD, int TM, int TN, class ARow,
-          class BRow>
-__device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
-                                             const DmaPanel<BN, SPLIT, NW, RB>& pb, int kbytes,
-                                             uint8_t* const (&st)[NS], const ARow& a_row,
-                                             const BRow& b_row) {
+//
+// FP provides the fragments (FragPair<Frags<...>> or FragsW8); RBA / RBB are the row
+// bytes of one k-tile in the A and B panels (a stage holds BM*RBA + BN*RBB bytes, B
+// after A).  kbytes is the byte length of an A row (k-tile count = ceil(kbytes / RBA));
+// the B panel's descriptor and K-tail checks use its own row length, set at init.
+template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
+          class ARow, class BRow>
+__device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RBA>& pa,
+                                                const DmaPanel<BN, SPLIT, NW, RBB>& pb, int kbytes,
+                                                int kbytes_b, uint8_t* const (&st)[NS],
+                                                const ARow& a_row, const BRow& b_row) {
     static_assert(NS >= 2, "at least two stages");
-    using F = Frags<E, TM, TN, RB>;
-    constexpr int KS = F::kSteps;
+    constexpr int KS = FP::kSteps;
     static_assert((NS * KS) % 2 == 0, "fragment double-buffer parity must repeat every stage group");
     constexpr int kMfma = TM * TN;
-    constexpr int nA = DmaPanel<BM, BM, NW, RB>::kInst;
-    constexpr int kPerTile = nA + DmaPanel<BN, SPLIT, NW, RB>::kInst;   // DMA per wave per tile
+    constexpr int nA = DmaPanel<BM, BM, NW, RBA>::kInst;
+    constexpr int kPerTile = nA + DmaPanel<BN, SPLIT, NW, RBB>::kInst;   // DMA per wave per tile
     static_assert((NS - 1) * kPerTile < 64, "vmcnt range");
     static_assert(SPREAD >= 1 && SPREAD <= KS, "the DMA of a tile ends before the next tile's last k-step");
     constexpr int kPer = (kPerTile + SPREAD - 1) / SPREAD;            // DMA per k-step
     static_assert(kPer <= kMfma, "one MFMA ahead of every DMA instruction");
-    const int nk = (kbytes + RB - 1) / RB;
+    const int nk = (kbytes + RBA - 1) / RBA;
     // k-tiles run in groups of NS (one per stage); the count is padded to a multiple of NS
     // with k-tiles past K, which the DMA fills with zeros.  The DMA always runs NS tiles
     // ahead, past the padded end too (zeros into stages that are not read again), so the
     // wait counts are exact on every tile.
     const int ng = (nk + NS - 1) / NS;
-    F f[2];
+    constexpr int kOffB = BM * RBA;          // B panel offset inside a stage
+    FP f;
     // DMA instruction q (0 .. kPerTile-1) of the tile with base offsets (ba, bb)
     auto issue_q = [&](int q, uint8_t* stage, uint32_t ba, uint32_t bb) {
         if (q < nA) pa.issue_one(q, stage, ba);
-        else pb.issue_one(q - nA, stage + BM * RB, bb);
+        else pb.issue_one(q - nA, stage + kOffB, bb);
     };
     static_for<NS - 1>([&](auto I) {
         constexpr int i = decltype(I)::value;
         pa.issue(st[i], i, kbytes);
-        pb.issue(st[i] + BM * RB, i, kbytes);
+        pb.issue(st[i] + kOffB, i, kbytes_b);
     });
     // tile NS-1: its first share now, the rest as pending DMA during tile 0
     uint32_t pend_a = pa.base_offset(NS - 1, kbytes);
-    uint32_t pend_b = pb.base_offset(NS - 1, kbytes);
+    uint32_t pend_b = pb.base_offset(NS - 1, kbytes_b);
     static_for<kPer>([&](auto Q) { issue_q(decltype(Q)::value, st[NS - 1], pend_a, pend_b); });
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile + kPer));   // tile 0 landed
     __syncthreads();
-    f[0].load(st[0], st[0] + BM * RB, 0, a_row, b_row);
+    f.load(0, st[0], st[0] + kOffB, 0, a_row, b_row);
 
     for (int g = 0; g < ng; ++g) {
         static_for<NS>([&](auto I) {
@@ -310,10 +403,10 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
                 // fragment read j of k-step s+1
                 static_for<kMfma>([&](auto J) {
                     constexpr int j = decltype(J)::value;
-                    f[(par + s) & 1].mma_one(j, acc);
+                    f.mma_one((par + s) & 1, j, acc);
                     if (s + 1 < SPREAD && j < kPer && (s + 1) * kPer + j < kPerTile)
                         issue_q((s + 1) * kPer + j, prv, pend_a, pend_b);
-                    if (j < F::kReads) f[(par + s + 1) & 1].load_one(j, cur, cur + BM * RB, s + 1, a_row, b_row);
+                    f.template slot<j>((par + s + 1) & 1, cur, cur + kOffB, s + 1, a_row, b_row);
                     __builtin_amdgcn_sched_barrier(0);
                 });
             }
@@ -322,15 +415,15 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
             __syncthreads();                                             // ... for every wave
             __builtin_amdgcn_sched_barrier(0);
             pend_a = pa.base_offset(kt + NS, kbytes);
-            pend_b = pb.base_offset(kt + NS, kbytes);
+            pend_b = pb.base_offset(kt + NS, kbytes_b);
             // MFMA j, then DMA instruction j of tile kt+NS into this tile's stage (the
             // first kPer; the rest follow in tile kt+1), then fragment read j of tile
             // kt+1's first k-step
             static_for<kMfma>([&](auto J) {
                 constexpr int j = decltype(J)::value;
-                f[(par + KS - 1) & 1].mma_one(j, acc);
+                f.mma_one((par + KS - 1) & 1, j, acc);
                 if (j < kPer) issue_q(j, cur, pend_a, pend_b);
-                if (j < F::kReads) f[(par + KS) & 1].load_one(j, nxt, nxt + BM * RB, 0, a_row, b_row);
+                f.template slot<j>((par + KS) & 1, nxt, nxt + kOffB, 0, a_row, b_row);
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
@@ -338,6 +431,17 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
     // drain the DMA that ran past the end before the LDS is reused or released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+}
+
+// Both operands of one element type E with RB-byte k-tile rows.
+template <Elt E, int BM, int BN, int SPLIT, int NS, int NW, int RB, int SPREAD, int TM, int TN, class ARow,
+          class BRow>
+__device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
+                                             const DmaPanel<BN, SPLIT, NW, RB>& pb, int kbytes,
+                                             uint8_t* const (&st)[NS], const ARow& a_row,
+                                             const BRow& b_row) {
+    mainloop_dma_fp<FragPair<Frags<E, TM, TN, RB>>, BM, BN, SPLIT, NS, NW, RB, RB, SPREAD>(
+        acc, pa, pb, kbytes, kbytes, st, a_row, b_row);
 }
 
 // ---------------------------------------------------------------------------------

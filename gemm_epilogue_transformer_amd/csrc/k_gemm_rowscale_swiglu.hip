@@ -13,15 +13,16 @@
 // r multiplies both accumulators BEFORE the SiLU (it commutes with the GEMM, not with
 // the nonlinearity).
 //
-// 8-bit weights (weight-only): W is e4m3 in HBM and decoded exactly to bf16 while it is
-// staged into LDS; the MFMA is the bf16 one and sw is applied in the epilogue.
+// 8-bit weights (weight-only): W is e4m3 in HBM and in LDS (half the bytes of a bf16
+// panel) and is converted exactly to bf16 in registers after the LDS read; the MFMA is
+// the bf16 one and sw is applied in the epilogue.
 #include "epilogue.hpp"
 #include "gemm_pipeline.hpp"
 #include "launch.hpp"
 
 namespace coda {
 
-// Epilogue shared by both variants.  Wave (wm, wn) holds TM x TN 32x32 accumulator blocks;
+// Epilogue shared by the bf16 and 8-bit weight instantiations.  Wave (wm, wn) holds TM x TN 32x32 accumulator blocks;
 // with SwiGLU, blocks [0, TN/2) are gate columns and [TN/2, TN) the matching up columns.
 // Per 32-row slab: r (times sw) is applied lane-locally to both accumulators before the
 // SiLU; the finished fp32 outputs are staged row-major in the wave's LDS region `slab`
@@ -84,8 +85,10 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
     }
 }
 
-// bf16 weights: direct-to-LDS mainloop.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int PIPE, int OCC, bool SWIGLU>
+// Direct-to-LDS mainloop (PIPE 1: the register-staged one, bf16 weights only).  W8: the
+// weights are e4m3, RB is the k-tile depth of a bf16 h row and a W row holds RB/2 bytes.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int PIPE, int OCC, bool SWIGLU,
+          bool W8>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
@@ -97,7 +100,9 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs gate and up blocks");
     constexpr int BNO = SWIGLU ? BN / 2 : BN;       // output columns of one block tile
 
-    constexpr int kStage = (BM + BN) * RB;
+    constexpr int RBB = W8 ? RB / 2 : RB;            // bytes of a W row per k-tile
+    constexpr int kStage = BM * RB + BN * RBB;
+    static_assert(!W8 || (RB == 128 && PIPE == 0), "8-bit weights: DMA mainloop, 64-k tiles");
     __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
     uint8_t* st[NS];
 #pragma unroll
@@ -119,20 +124,21 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
         rv[i] = m < M ? R[m] : 0.0f;
     }
 
-    const int kbytes = K * 2;
+    const int kbytes = K * 2;                       // bytes of an h row
+    const int kbytes_b = W8 ? K : K * 2;            // bytes of a W row
     using PanelA = std::conditional_t<PIPE == 1, RegPanel<BM, BM, NW, RB>, DmaPanel<BM, BM, NW, RB>>;
     using PanelB = std::conditional_t<PIPE == 1, RegPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB>,
-                                      DmaPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB>>;
+                                      DmaPanel<BN, SWIGLU ? BN / 2 : BN, NW, RBB>>;
     PanelA pa;
     PanelB pb;
     const uint8_t* a0 = H + static_cast<size_t>(m0) * kbytes;
     pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
-    const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes;
+    const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes_b;
     if constexpr (SWIGLU) {
-        const uint8_t* u0 = W + static_cast<size_t>(N_out + j0) * kbytes;
-        pb.init(g0, min(BN / 2, N_out - j0), u0, min(BN / 2, N_out - j0), kbytes);
+        const uint8_t* u0 = W + static_cast<size_t>(N_out + j0) * kbytes_b;
+        pb.init(g0, min(BN / 2, N_out - j0), u0, min(BN / 2, N_out - j0), kbytes_b);
     } else {
-        pb.init(g0, min(BN, N_out - j0), g0, 0, kbytes);
+        pb.init(g0, min(BN, N_out - j0), g0, 0, kbytes_b);
     }
     auto a_row = [&](int tm) { return wm * WM + tm * 32; };
     // SWIGLU: blocks [0, TN/2) = this wave's gate rows, [TN/2, TN) = the matching up rows
@@ -152,7 +158,10 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    if constexpr (PIPE == 1) {
+    if constexpr (W8) {
+        mainloop_dma_fp<FragsW8<TM, TN>, BM, BN, (SWIGLU ? BN / 2 : BN), NS, NW, RB, RBB, SPREAD>(
+            acc, pa, pb, kbytes, kbytes_b, st, a_row, b_row);
+    } else if constexpr (PIPE == 1) {
         static_assert(NS == 2, "the register-staged mainloop has two LDS stages");
         mainloop_reg<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row);
     } else {
@@ -162,99 +171,6 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     const float sw = w_scale ? *w_scale : 1.0f;
     uint8_t* slab = slab_region<NS, NW, kStage, Slab<SWIGLU ? TN / 2 : TN>::kBytes>(st, wave);
     rowscale_epilogue<BM, BN, WAVES_M, TM, TN, SWIGLU>(acc, rv, sw, Y, M, N_out, m0, j0, wm, wn, slab);
-}
-
-// 8-bit weights (weight-only): e4m3 decoded exactly to bf16 while staged into LDS
-// through registers.
-template <int BM, int BN, int OCC, bool SWIGLU>
-__global__ void __launch_bounds__(kThreads, OCC)
-k_gemm_rowscale_swiglu_w8(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
-                          const float* __restrict__ w_scale, const float* __restrict__ R,
-                          uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
-                          int tiles_n) {
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int TM = WM / 32, TN = WN / 32;
-    static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs gate and up blocks");
-    constexpr int BNO = SWIGLU ? BN / 2 : BN;
-
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BM + BN) * kRowBytes];
-
-    int tile_m, tile_n;
-    tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
-    const int m0 = tile_m * BM, j0 = tile_n * BNO;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    const int kbytes = K * 2;                                    // bf16 bytes of a row
-    const size_t h_row = static_cast<size_t>(K) * 2;
-    const size_t w_row = static_cast<size_t>(K);
-    auto a_ptr = [&](int r) -> const uint8_t* {
-        const int m = m0 + r;
-        return m < M ? H + static_cast<size_t>(m) * h_row : nullptr;
-    };
-    auto b_ptr = [&](int r) -> const uint8_t* {
-        if constexpr (SWIGLU) {
-            const int j = j0 + (r < BN / 2 ? r : r - BN / 2);
-            if (j >= N_out) return nullptr;
-            const int n = r < BN / 2 ? j : N_out + j;
-            return W + static_cast<size_t>(n) * w_row;
-        }
-        const int n = j0 + r;
-        return n < N_out ? W + static_cast<size_t>(n) * w_row : nullptr;
-    };
-    auto a_row = [&](int tm) { return wm * WM + tm * 32; };
-    auto b_row = [&](int tn) {
-        if constexpr (SWIGLU) {
-            constexpr int TH = TN / 2;
-            return (tn < TH ? 0 : BN / 2) + wn * TH * 32 + (tn % TH) * 32;
-        }
-        return wn * WN + tn * 32;
-    };
-
-    f32x16_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    PanelStage<BM> sa;
-    PanelStageE4m3ToBf16<BN> sb;
-    const int nk = (kbytes + kRowBytes - 1) / kRowBytes;
-    if (nk > 0) {
-        sa.load(a_ptr, 0, kbytes);
-        sb.load(b_ptr, 0, kbytes);
-        sa.store(smem[0]);
-        sb.store(smem[0] + BM * kRowBytes);
-        __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            sa.load(a_ptr, (kt + 1) * kRowBytes, kbytes);
-            sb.load(b_ptr, (kt + 1) * kRowBytes, kbytes);
-        }
-        WaveMma<Elt::BF16, TM, TN>::run(acc, smem[cur], smem[cur] + BM * kRowBytes, a_row, b_row);
-        if (kt + 1 < nk) {
-            sa.store(smem[cur ^ 1]);
-            sb.store(smem[cur ^ 1] + BM * kRowBytes);
-        }
-        __syncthreads();
-    }
-
-    const float sw = w_scale ? *w_scale : 1.0f;
-    // r of this wave's rows (lane l: rows l, 64 + l, ...); rows past M hold 0.  The
-    // mainloop's last barrier already frees smem for the slabs.
-    float rv[WM / 64];
-#pragma unroll
-    for (int i = 0; i < WM / 64; ++i) {
-        const int m = m0 + wm * WM + 64 * i + (threadIdx.x & 63);
-        rv[i] = m < M ? R[m] : 0.0f;
-    }
-    static_assert(4 * Slab<SWIGLU ? TN / 2 : TN>::kBytes <= 2 * (BM + BN) * kRowBytes, "slabs fit");
-    uint8_t* slab = &smem[0][0] + wave * Slab<SWIGLU ? TN / 2 : TN>::kBytes;
-    rowscale_epilogue<BM, BN, 2, TM, TN, SWIGLU>(acc, rv, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
 // Tile configurations of the second GEMM (compile-time).
@@ -273,33 +189,29 @@ k_gemm_rowscale_swiglu_w8(const uint8_t* __restrict__ H, const uint8_t* __restri
 #ifndef CODA_G3_PIPE
 #define CODA_G3_PIPE 0
 #endif
+#ifndef CODA_G3_NS8
+#define CODA_G3_NS8 2
+#endif
 constexpr int BM3 = CODA_G3_BM, BN3 = CODA_G3_BN, NS3 = CODA_G3_NS, OCC3 = CODA_G3_OCC;
 constexpr int WM3 = CODA_G3_WM, WN3 = CODA_G3_WN, RB3 = CODA_G3_RB, SP3 = CODA_G3_SPREAD, PIPE3 = CODA_G3_PIPE;
-constexpr int BM3W8 = 128, BN3W8 = 128;   // 8-bit weights: register-staged, 2 blocks per CU
+// 8-bit weights: a stage is 3/4 of a bf16 one, so a third stage fits where two do
+constexpr int NS3_8 = CODA_G3_NS8;
 
 int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
-    const int64_t bno = swiglu ? BN3 / 2 : BN3, bno8 = swiglu ? BN3W8 / 2 : BN3W8;
-    const int64_t a = ((M + BM3 - 1) / BM3) * ((N_out + bno - 1) / bno);
-    const int64_t b = ((M + BM3W8 - 1) / BM3W8) * ((N_out + bno8 - 1) / bno8);
-    return a > b ? a : b;
+    const int64_t bno = swiglu ? BN3 / 2 : BN3;
+    return ((M + BM3 - 1) / BM3) * ((N_out + bno - 1) / bno);
 }
 
 template <bool SWIGLU, bool WFP8>
 static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                           const float* w_scale, const float* r, void* y, hipStream_t stream) {
-    constexpr int BM = WFP8 ? BM3W8 : BM3, BN = WFP8 ? BN3W8 : BN3;
-    constexpr int BNO = SWIGLU ? BN / 2 : BN;
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N_out + BNO - 1) / BNO;
-    const dim3 grid(tiles_m * tiles_n), block(WFP8 ? kThreads : 64 * WM3 * WN3);
-    if constexpr (WFP8) {
-        hipLaunchKernelGGL((k_gemm_rowscale_swiglu_w8<BM, BN, 2, SWIGLU>), grid, block, 0, stream,
-                           static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale,
-                           r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
-    } else {
-        hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM, BN, WM3, WN3, NS3, RB3, SP3, PIPE3, OCC3, SWIGLU>), grid, block, 0, stream,
-                           static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale,
-                           r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
-    }
+    constexpr int BNO = SWIGLU ? BN3 / 2 : BN3;
+    const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BNO - 1) / BNO;
+    const dim3 grid(tiles_m * tiles_n), block(64 * WM3 * WN3);
+    hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, WFP8 ? 0 : PIPE3,
+                                               OCC3, SWIGLU, WFP8>),
+                       grid, block, 0, stream, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W),
+                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
     return hipGetLastError();
 }
 

@@ -71,6 +71,35 @@ def test_quantize_e4m3_every_code_and_tie():
     assert np.array_equal(q.cpu().numpy(), qo)
 
 
+@pytest.mark.parametrize("act", [coda.NONE, coda.SWIGLU])
+def test_weight_only_e4m3_gemm_reproduces_every_code(act):
+    # One-hot rows of h pick single weights: with r = sw = 1 the NONE output y[m, n] is the
+    # one exact product 1 * decode(W[n, m]), so every finite e4m3 code must come back as
+    # its exact bf16 value (the oracle's decoder).  -0 comes back as +0 (the zero products
+    # of the other k are +0).  With SwiGLU the up rows are all 0x38 (= 1.0), so y is
+    # SiLU(decode(gate)), compared at the bf16 tolerance.
+    K = 256
+    N = K if act == coda.NONE else 2 * K
+    codes = ((np.arange(N)[:, None] + 7 * np.arange(K)[None, :]) % 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0                       # the two NaN codes
+    if act == coda.SWIGLU:
+        codes[K:] = 0x38                                    # up rows: 1.0
+    h = np.zeros((K, K), np.uint16)
+    h[np.arange(K), np.arange(K)] = 0x3F80                 # bf16 1.0
+    y = coda.gemm_rowscale_swiglu(dev_bf16(h), torch.from_numpy(codes).cuda(),
+                                  torch.ones(K, device="cuda"), act,
+                                  w_scale=torch.ones(1, device="cuda"))
+    torch.cuda.synchronize()
+    if act == coda.NONE:
+        expect = oracle.bf16_encode(oracle.e4m3_decode(codes.T) + 0.0)
+        assert np.array_equal(host_bits(y), expect)
+    else:
+        g = oracle.e4m3_decode(codes[:K].T)
+        ref = g / (1.0 + np.exp(-g))
+        got = oracle.bf16_decode(host_bits(y))
+        assert np.all(np.abs(got - ref) <= 2e-2 * (1.0 + np.abs(ref)))
+
+
 # ---------------------------------------------------------------------- the chain ----
 
 SMALL = [
