@@ -6,7 +6,8 @@
  * What it computes, in the order the pages state it (kucoin "CODA: new research
  * optimizes Transformer training..." section "CODA: El epilogo esconde un tesoro"):
  * a matrix product, a residual add, RMS normalisation, a second matrix product, and
- * (same section, last paragraph; section "Resultados del experimento") SwiGLU.
+ * (same section, last paragraph; section "Resultados del experimento") SwiGLU, or
+ * (same paragraph) RoPE on the QKV product (orc_rope, applied to the act-NONE output).
  * It is the UNFUSED definition: no tiling, no partial sums, no deferred row scale.
  *
  * Readings where the pages are silent (all listed in the design notes):
@@ -254,6 +255,43 @@ int orc_chain(int64_t R, const int64_t* rows,
     free(wo);
     free(wor);
     return fail ? 2 : 0;
+}
+
+/* ----------------------------------------------------------------- RoPE ---- */
+
+/*
+ * Rotary position embedding as a pairwise epilogue of the QKV product (kucoin page,
+ * section "CODA: El epilogo esconde un tesoro", last paragraph: the same
+ * reparameterisation holds for RoPE; section "Cinco bloques y un lenguaje LEGO": RoPE
+ * is an element-wise transform).  The pages do not define it; the reading used is the
+ * LLaMA one (listed in the design notes):
+ *   columns [0, rot_cols) are heads of head_dim values (Q heads, then K heads); in each
+ *   head, value i pairs with value i + head_dim/2 (i < head_dim/2) and the pair is
+ *   rotated by the angle pos * theta_i, theta_i = base^(-2 i / head_dim):
+ *     x1' = x1 cos - x2 sin,   x2' = x2 cos + x1 sin;
+ *   columns [rot_cols, ncols) (V heads) pass through.
+ * In place on y [R, ncols] (fp64, the unrounded chain output); pos[i] is row i's
+ * position.  fp64 throughout, cos/sin from the C library.
+ */
+int orc_rope(int64_t R, int64_t ncols, double* y, const int32_t* pos, double base,
+             int64_t head_dim, int64_t rot_cols) {
+    if (head_dim < 2 || head_dim % 2 || rot_cols % head_dim || rot_cols > ncols) return 1;
+    int64_t half = head_dim / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < R; ++i) {
+        double p = (double)pos[i];
+        for (int64_t h0 = 0; h0 < rot_cols; h0 += head_dim) {
+            for (int64_t j = 0; j < half; ++j) {
+                double theta = pow(base, -2.0 * (double)j / (double)head_dim);
+                double ang = p * theta;
+                double c = cos(ang), sn = sin(ang);
+                double x1 = y[i * ncols + h0 + j], x2 = y[i * ncols + h0 + half + j];
+                y[i * ncols + h0 + j] = x1 * c - x2 * sn;
+                y[i * ncols + h0 + half + j] = x2 * c + x1 * sn;
+            }
+        }
+    }
+    return 0;
 }
 
 /* ------------------------------------------------- array helpers (tests) ---- */

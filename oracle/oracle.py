@@ -24,7 +24,7 @@ ACT_NONE = 0
 ACT_SWIGLU = 1
 
 __all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
-           "e4m3_encode", "fold_bf16", "quant_e4m3", "chain", "prepare", "BF16", "E4M3",
+           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "chain", "prepare", "BF16", "E4M3",
            "ACT_NONE", "ACT_SWIGLU"]
 
 
@@ -64,6 +64,8 @@ def lib():
         L.orc_fold_bf16.argtypes = [i64, i64, P, P, P]
         L.orc_quant_e4m3.restype = None
         L.orc_quant_e4m3.argtypes = [i64, i64, P, P, P, P, P]
+        L.orc_rope.restype = C.c_int
+        L.orc_rope.argtypes = [i64, i64, P, P, C.c_double, i64, i64]
         L.orc_chain.restype = C.c_int
         L.orc_chain.argtypes = [i64, P, i64, i64, i64, C.c_int,
                                 P, C.c_int, C.c_double,
@@ -190,3 +192,17 @@ def chain(prep: dict, x_res, gamma, act: int, eps: float, rows=None, M: int | No
     if rc != 0:
         raise RuntimeError(f"oracle chain failed ({rc})")
     return dict(h=h, hb=hb, S=S, r=r, y=y)
+
+
+def rope(y: np.ndarray, pos, base: float, head_dim: int, rot_cols: int) -> np.ndarray:
+    """RoPE of the chain output: a rotated copy of ``y`` (fp64 [R, ncols]), row i at
+    position ``pos[i]``; columns [0, rot_cols) are heads of ``head_dim`` values (pair
+    i, i + head_dim/2 rotated by pos * base^(-2i/head_dim)), the rest pass through."""
+    out = np.array(y, dtype=np.float64, order="C", copy=True)
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    if out.ndim != 2 or p.shape != (out.shape[0],):
+        raise ValueError("y must be [R, ncols] and pos [R]")
+    rc = lib().orc_rope(out.shape[0], out.shape[1], _p(out), _p(p), float(base), int(head_dim), int(rot_cols))
+    if rc != 0:
+        raise ValueError("bad RoPE layout")
+    return out

@@ -32,6 +32,7 @@ import numpy as np
 
 ACT_NONE = 0
 ACT_SWIGLU = 1
+ACT_ROPE = 2      # rotary position embedding on the QKV product (no activation)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -41,10 +42,16 @@ class Workload:
     K1: int         # reduction dim of the first GEMM
     d: int          # hidden dim = N of the first GEMM = reduction dim of the second GEMM
     N2w: int        # rows of the second weight (2F for SwiGLU, N2 otherwise)
-    act: int        # ACT_NONE or ACT_SWIGLU
+    act: int        # ACT_NONE, ACT_SWIGLU or ACT_ROPE
     dtype: str      # "bf16" or "e4m3" (fp8 variant: A, Wo and the second weight in e4m3)
     eps: float
     seed: int
+    # RoPE only: the first rot_cols output columns are Q and K heads of head_dim values,
+    # the tokens are M / seq_len sequences of seq_len positions, base of the angles
+    rot_cols: int = 0
+    head_dim: int = 64
+    seq_len: int = 0
+    rope_base: float = 500000.0
 
     @property
     def n_out(self) -> int:
@@ -59,22 +66,29 @@ class Workload:
 # The five workloads.  1: tiny correctness case; 2: LLaMA-3-1B attention-out ->
 # SwiGLU MLP-in; 3: LLaMA-3-1B MLP-out -> next layer QKV (32x64 query + 2x8x64 KV
 # heads = 3072); 4: LLaMA-3-8B-shaped attention-out -> SwiGLU MLP-in; 5: workload 2
-# with A, Wo and the second weight quantised to e4m3 (same draws as workload 2).
+# with A, Wo and the second weight quantised to e4m3 (same draws as workload 2);
+# 6: workload 3 with RoPE on its Q and K columns (32 + 8 heads of 64 = 2560 of the 3072
+# columns; V passes), 16384 tokens = 4 sequences of 4096 (same draws as workload 3).
 WORKLOADS = {
     1: Workload("tiny_m128_d256_n512_none", 128, 256, 256, 512, ACT_NONE, "bf16", 1e-5, 1001),
     2: Workload("llama1b_attnout_mlpin_m16384", 16384, 2048, 2048, 16384, ACT_SWIGLU, "bf16", 1e-5, 1002),
     3: Workload("llama1b_mlpout_qkv_m16384", 16384, 8192, 2048, 3072, ACT_NONE, "bf16", 1e-5, 1003),
     4: Workload("llama8b_attnout_mlpin_m16384", 16384, 4096, 4096, 28672, ACT_SWIGLU, "bf16", 1e-5, 1004),
     5: Workload("llama1b_attnout_mlpin_m16384_fp8", 16384, 2048, 2048, 16384, ACT_SWIGLU, "e4m3", 1e-5, 1002),
+    6: Workload("llama1b_mlpout_qkv_rope_m16384", 16384, 8192, 2048, 3072, ACT_ROPE, "bf16", 1e-5, 1003,
+                rot_cols=2560, seq_len=4096),
 }
 
 
 def custom(M: int, K1: int, d: int, N2w: int, act: int, seed: int, dtype: str = "bf16",
-           eps: float = 1e-5) -> Workload:
+           eps: float = 1e-5, rot_cols: int = 0, seq_len: int = 0) -> Workload:
     """A workload of arbitrary shape (ragged and edge-case tests)."""
     if act == ACT_SWIGLU and N2w % 2:
         raise ValueError("SwiGLU needs an even number of second-weight rows")
-    return Workload(f"custom_m{M}_k{K1}_d{d}_n{N2w}_a{act}", M, K1, d, N2w, act, dtype, eps, seed)
+    if act == ACT_ROPE and (rot_cols % 64 or rot_cols > N2w or seq_len < 1):
+        raise ValueError("RoPE needs whole 64-value heads within the columns and a sequence length")
+    return Workload(f"custom_m{M}_k{K1}_d{d}_n{N2w}_a{act}", M, K1, d, N2w, act, dtype, eps, seed,
+                    rot_cols=rot_cols, seq_len=seq_len)
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -99,6 +113,7 @@ def generate(w: Workload, rows: int | None = None) -> dict:
       x_res  uint16 [M, d]    bf16 bits
       gamma  float32 [d]
       W_t    uint16 [N2w, d]  bf16 bits (second weight before the gamma fold)
+      pos    int32 [M]        RoPE workloads only: token m's position, m mod seq_len
     For an e4m3 workload these are the pre-quantisation tensors (quantisation is a
     step of the chain's weight/activation preparation, not of input generation).
     ``rows`` (optional) truncates M, keeping the draws of the first rows identical.
@@ -112,10 +127,13 @@ def generate(w: Workload, rows: int | None = None) -> dict:
     W = rng.standard_normal((w.N2w, w.d), dtype=f32) * f32(1.0 / np.sqrt(w.d))
     if rows is not None:
         A, x = A[:rows], x[:rows]
-    return {
+    out = {
         "A": to_bf16_bits(A),
         "Wo_t": to_bf16_bits(Wo),
         "x_res": to_bf16_bits(x),
         "gamma": gamma,
         "W_t": to_bf16_bits(W),
     }
+    if w.act == ACT_ROPE:
+        out["pos"] = (np.arange(A.shape[0]) % w.seq_len).astype(np.int32)
+    return out
