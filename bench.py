@@ -47,15 +47,23 @@ def kernel_source_hash() -> str:
 def algorithmic_bytes(w, fused=True) -> dict:
     """Each tensor moved once (bytes).  fused: the three-kernel chain; unfused: GEMM,
     add, RMSNorm, GEMM, SwiGLU as separate kernels with bf16 intermediates."""
+    import synth_inputs as si
+
     eb = 1 if w.dtype == "e4m3" else 2
     M, K1, d, N2w, n_out = w.M, w.K1, w.d, w.N2w, w.n_out
-    T = -(-d // 128)
+    T = -(-d // 256)                      # one partial per 256-column tile of GEMM 1
+    rope = w.act == si.ACT_ROPE
     k1 = M * K1 * eb + d * K1 * eb + M * d * 2 + M * d * 2 + M * T * 4
     k2 = M * T * 4 + M * 4
     k3 = M * d * 2 + N2w * d * eb + M * 4 + M * n_out * 2
+    if rope:                              # positions, cos / sin table
+        k3 += M * 4 + 2 * w.seq_len * 32 * 4
     if fused:
         return {"gemm1": k1, "reduce": k2, "gemm2": k3, "total": k1 + k2 + k3}
-    act = M * N2w * 2 + M * n_out * 2 if n_out != N2w else 0
+    # unfused: the activation / rotation is a kernel of its own (reads z, writes y)
+    act = M * N2w * 2 + M * n_out * 2 if (n_out != N2w or rope) else 0
+    if rope:
+        act += M * 4 + 2 * w.seq_len * 32 * 4
     tot = (M * K1 * eb + d * K1 * eb + M * d * 2) + 3 * M * d * 2 + 2 * M * d * 2 + d * 4 \
         + (M * d * 2 + N2w * d * eb + M * N2w * 2) + act
     return {"total": tot}
@@ -224,6 +232,12 @@ def main():
     torch.cuda.synchronize()
     prep_ms = (time.perf_counter() - t0) * 1e3
 
+    rope_in = None
+    if w.act == si.ACT_ROPE:              # angle table and positions: once, like the weights
+        cos_t, sin_t = coda.rope_table(w.seq_len, w.rope_base)
+        rope_in = (torch.from_numpy(inp["pos"]).cuda(), cos_t, sin_t)
+        torch.cuda.synchronize()
+
     M, d = w.M, w.d
     out = {"h": torch.empty((M, d), dtype=torch.bfloat16, device="cuda"),
            "partials": torch.empty((M, coda.partials_per_row(d)), dtype=torch.float32, device="cuda"),
@@ -240,7 +254,10 @@ def main():
         r = coda.rowscale_reduce(P, d, w.eps, out["r"])
         if ev is not None:
             ev[2].record(stream)
-        coda.gemm_rowscale_swiglu(h, Wp, r, w.act, sw, out["y"])
+        if rope_in is None:
+            coda.gemm_rowscale_swiglu(h, Wp, r, w.act, sw, out["y"])
+        else:
+            coda.gemm_rowscale_rope(h, Wp, r, *rope_in, w.rot_cols, sw, out["y"])
         if ev is not None:
             ev[3].record(stream)
 
@@ -281,8 +298,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "e4m3/bf16", "data": "synthetic",
         "config": {"workload": w.name, "M": M, "K1": w.K1, "d": d, "N2w": w.N2w,
-                   "act": "swiglu" if w.act == si.ACT_SWIGLU else "none", "eps": w.eps,
-                   "seed": w.seed},
+                   "act": {si.ACT_SWIGLU: "swiglu", si.ACT_ROPE: "rope"}.get(w.act, "none"), "eps": w.eps,
+                   "seed": w.seed, **({"rot_cols": w.rot_cols, "seq_len": w.seq_len, "rope_base": w.rope_base}
+                                      if w.act == si.ACT_ROPE else {})},
         "frac_of_peak_chain": round(value / PEAK_TFLOPS["bf16"], 4),
         "kernels_ms": {"gemm_resid_partialrms": round(k1_ms, 4), "rowscale_reduce": round(k2_ms, 4),
                        "gemm_rowscale_swiglu": round(k3_ms, 4)},
@@ -304,6 +322,13 @@ def main():
             if w.act == si.ACT_SWIGLU:
                 F_ = w.n_out
                 return torch.nn.functional.silu(z[:, :F_]) * z[:, F_:]
+            if w.act == si.ACT_ROPE:
+                pos_t, cos_t, sin_t = rope_in
+                q = z[:, : w.rot_cols].view(M, -1, 64)
+                c, s_ = cos_t[pos_t].unsqueeze(1), sin_t[pos_t].unsqueeze(1)
+                x1, x2 = q[..., :32], q[..., 32:]
+                rq = torch.cat([x1 * c - x2 * s_, x2 * c + x1 * s_], -1).to(torch.bfloat16)
+                return torch.cat([rq.view(M, -1), z[:, w.rot_cols:]], 1)
             return z
 
         for _ in range(3):

@@ -22,7 +22,7 @@ SWIGLU = CODA_ACT_SWIGLU
 
 __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3",
            "partials_per_row", "gemm_resid_partialrms", "rowscale_reduce",
-           "gemm_rowscale_swiglu", "chain", "version"]
+           "gemm_rowscale_swiglu", "rope_table", "gemm_rowscale_rope", "chain", "version"]
 
 
 def _stream(stream):
@@ -123,6 +123,35 @@ def gemm_rowscale_swiglu(h, W, r, act=SWIGLU, w_scale=None, y=None, stream=None)
     _lib.check("coda_gemm_rowscale_swiglu", _lib.load().coda_gemm_rowscale_swiglu(
         M, n_out, K, act, _ptr(h), _ptr(W), CODA_E4M3 if fp8 else CODA_BF16, _ptr(w_scale),
         _ptr(r), _ptr(y), _stream(stream)))
+    return y
+
+
+def rope_table(rows, base=500000.0, cos=None, sin=None, stream=None):
+    """cos / sin [rows, 32] fp32 of the angles p * base^(-2i/64) (RoPE, heads of 64)."""
+    dev = torch.device("cuda")
+    cos = torch.empty((rows, 32), dtype=torch.float32, device=dev) if cos is None else cos
+    sin = torch.empty((rows, 32), dtype=torch.float32, device=dev) if sin is None else sin
+    _lib.check("coda_rope_table", _lib.load().coda_rope_table(rows, float(base), _ptr(cos), _ptr(sin),
+                                                               _stream(stream)))
+    return cos, sin
+
+
+def gemm_rowscale_rope(h, W, r, pos, cos, sin, rot_cols, w_scale=None, y=None, stream=None):
+    """y = RoPE(r * sw * h.W^T): W [N_out, K]; the first rot_cols columns (Q and K heads
+    of 64) turn by the angles of their row's position pos [M] (int32) from the cos / sin
+    table [rows, 32]; the rest (V) pass."""
+    M, K = h.shape
+    fp8 = W.element_size() == 1
+    if W.shape[1] != K:
+        raise ValueError("h and W disagree on K")
+    n_out = W.shape[0]
+    if pos is not None and pos.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    rows = 0 if cos is None else cos.shape[0]
+    y = torch.empty((M, n_out), dtype=torch.bfloat16, device=h.device) if y is None else y
+    _lib.check("coda_gemm_rowscale_rope", _lib.load().coda_gemm_rowscale_rope(
+        M, n_out, K, _ptr(h), _ptr(W), CODA_E4M3 if fp8 else CODA_BF16, _ptr(w_scale), _ptr(r),
+        _ptr(pos), _ptr(cos), _ptr(sin), rows, rot_cols, _ptr(y), _stream(stream)))
     return y
 
 

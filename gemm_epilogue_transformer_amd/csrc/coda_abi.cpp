@@ -172,4 +172,46 @@ coda_status coda_gemm_rowscale_swiglu(int64_t M, int64_t N_out, int64_t K, coda_
                                                         w_scale, r, y, as_stream(stream)));
 }
 
+coda_status coda_rope_table(int64_t rows, double base, float* cos, float* sin, void* stream) {
+    if (rows < 1 || rows >= (int64_t(1) << 24)) return CODA_ERR_SHAPE;
+    if (!std::isfinite(base) || !(base > 1.0)) return CODA_ERR_VALUE;
+    if (!cos || !sin) return CODA_ERR_NULL;
+    if (!aligned16(cos) || !aligned16(sin)) return CODA_ERR_ALIGN;
+    if (overlap(span(cos, rows * 32 * 4), span(sin, rows * 32 * 4))) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_rope_table(int(rows), base, cos, sin, as_stream(stream)));
+}
+
+coda_status coda_gemm_rowscale_rope(int64_t M, int64_t N_out, int64_t K, const void* h,
+                                    const void* W, coda_dtype w_dtype, const float* w_scale,
+                                    const float* r, const int32_t* pos, const float* cos,
+                                    const float* sin, int64_t table_rows, int64_t rot_cols,
+                                    void* y, void* stream) {
+    if (w_dtype != CODA_BF16 && w_dtype != CODA_E4M3) return CODA_ERR_DTYPE;
+    const bool fp8 = w_dtype == CODA_E4M3;
+    if (!dim_ok(M, 0) || !dim_ok(N_out, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (N_out % 8 != 0 || K % (fp8 ? 16 : 8) != 0 || N_out > kMaxRow || K > kMaxRow)
+        return CODA_ERR_SHAPE;
+    if (rot_cols < 0 || rot_cols > N_out || rot_cols % 64 != 0) return CODA_ERR_SHAPE;
+    const bool rot = rot_cols > 0;
+    if (rot && (table_rows < 1 || table_rows >= (int64_t(1) << 24))) return CODA_ERR_SHAPE;
+    if (!prod_ok(M, K) || !prod_ok(N_out, K) || !prod_ok(M, N_out)) return CODA_ERR_SHAPE;
+    if (coda::gemm3_tiles(M, N_out, false) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!h || !W || !r || !y) return CODA_ERR_NULL;
+    if (fp8 && !w_scale) return CODA_ERR_NULL;
+    if (rot && (!pos || !cos || !sin)) return CODA_ERR_NULL;
+    if (!aligned16(h) || !aligned16(W) || !aligned16(r) || !aligned16(y)) return CODA_ERR_ALIGN;
+    if (rot && (!aligned16(pos) || !aligned16(cos) || !aligned16(sin))) return CODA_ERR_ALIGN;
+    const Range ry = span(y, M * N_out * 2);
+    if (overlap(ry, span(h, M * K * 2)) || overlap(ry, span(W, N_out * K * (fp8 ? 1 : 2))) ||
+        overlap(ry, span(r, M * 4)) || (w_scale && overlap(ry, span(w_scale, 4))))
+        return CODA_ERR_ALIAS;
+    if (rot && (overlap(ry, span(pos, M * 4)) || overlap(ry, span(cos, table_rows * 128)) ||
+                overlap(ry, span(sin, table_rows * 128))))
+        return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_rowscale_rope(int(M), int(N_out), int(K), h, W, fp8, w_scale, r,
+                                                      rot ? pos : nullptr, cos, sin, int(rot ? table_rows : 0),
+                                                      int(rot_cols), y, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -13,6 +13,12 @@
 // r multiplies both accumulators BEFORE the SiLU (it commutes with the GEMM, not with
 // the nonlinearity).
 //
+// RoPE (kucoin page, same section, last paragraph: the reparameterisation covers RoPE
+// too): act NONE's product, then in every Q/K head of 64 columns value i and value i+32
+// turn by pos[m] * theta_i (cos / sin from a table).  A head's two halves are the wave's
+// blocks b and b+1 (b even) in the same lane and rows, so the rotation is lane-local,
+// like the gate/up pairing of SwiGLU.
+//
 // 8-bit weights (weight-only): W is e4m3 in HBM and in LDS (half the bytes of a bf16
 // panel) and is converted exactly to bf16 in registers after the LDS read; the MFMA is
 // the bf16 one and sw is applied in the epilogue.
@@ -21,6 +27,17 @@
 #include "launch.hpp"
 
 namespace coda {
+
+enum { kActNone = 0, kActSwiglu = 1, kActRope = 2 };
+
+// RoPE operands (unused by the other activations).
+struct RopeArgs {
+    const int32_t* pos;       // [M] positions
+    const float* cos;         // [table_rows, 32]
+    const float* sin;         // [table_rows, 32]
+    int table_rows;
+    int rot_cols;             // leading rotated columns (whole 64-column heads)
+};
 
 // Epilogue shared by the bf16 and 8-bit weight instantiations.  Wave (wm, wn) holds TM x TN 32x32 accumulator blocks;
 // with SwiGLU, blocks [0, TN/2) are gate columns and [TN/2, TN) the matching up columns.
@@ -32,13 +49,20 @@ namespace coda {
 // r of the wave's WM rows lives in registers: lane l holds rows l, 64 + l, ... of the
 // wave (rv[WM / 64]), loaded before the mainloop; the epilogue fetches the rows it needs
 // with cross-lane permutes, so r takes no LDS (the stages may fill all of it).
-template <int BM, int BN, int WAVES_M, int TM, int TN, bool SWIGLU>
+//
+// RoPE: pv holds the positions of the wave's rows like rv holds r; per slab each lane
+// loads cos / sin of its 16 rows at frequency lane % 32 (range-checked: a position
+// outside the table reads 0).
+template <int BM, int BN, int WAVES_M, int TM, int TN, int ACT>
 __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
-                                                  const float (&rv)[BM / WAVES_M / 64], float sw,
-                                                  uint16_t* __restrict__ Y, int M, int N_out,
+                                                  const float (&rv)[BM / WAVES_M / 64],
+                                                  const int (&pv)[BM / WAVES_M / 64], const RopeArgs& rope,
+                                                  float sw, uint16_t* __restrict__ Y, int M, int N_out,
                                                   int m0, int j0, int wm, int wn, uint8_t* slab) {
+    constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int WM = BM / WAVES_M;
     constexpr int NB = SWIGLU ? TN / 2 : TN;          // output blocks per wave
+    static_assert(ACT != kActRope || NB % 2 == 0, "a head's halves are blocks b and b+1 of one wave");
     using S = Slab<NB>;
     const int lane = threadIdx.x & 63;
     const int lh = lane >> 5;
@@ -46,6 +70,12 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
     const uint32_t row_bytes = static_cast<uint32_t>(N_out) * 2;
     const __amdgpu_buffer_rsrc_t y_rsrc =
         make_buffer_rsrc(Y + static_cast<size_t>(m0) * N_out, static_cast<uint32_t>(valid_rows) * row_bytes);
+    // RoPE: first column of the wave; heads whose first column is below rot_cols turn
+    const int n_wave = j0 + wn * NB * 32;
+    const bool any_rot = ACT == kActRope && n_wave < rope.rot_cols;
+    const uint32_t tbytes = ACT == kActRope ? static_cast<uint32_t>(rope.table_rows) * 128u : 0u;
+    const __amdgpu_buffer_rsrc_t cos_rsrc = make_buffer_rsrc(rope.cos, tbytes);
+    const __amdgpu_buffer_rsrc_t sin_rsrc = make_buffer_rsrc(rope.sin, tbytes);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         // r of the 16 rows this lane holds: rows 8g + 4*lh + (0..3), g = 0..3
@@ -56,18 +86,52 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
             for (int e = 0; e < 4; ++e)
                 rr[4 * g + e] = __shfl(rv[tm / 2], (tm % 2) * 32 + 8 * g + 4 * lh + e) * sw;
         float v[NB][16];
+        if constexpr (ACT == kActRope) {
+            float cs[16] = {}, sn[16] = {};
+            if (any_rot) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+                for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if constexpr (SWIGLU) {
-                    const float gv = acc[tm][b][i] * rr[i];
-                    const float uv = acc[tm][b + NB][i] * rr[i];
-                    v[b][i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+                    for (int e = 0; e < 4; ++e) {
+                        const int p = __shfl(pv[tm / 2], (tm % 2) * 32 + 8 * g + 4 * lh + e);
+                        const uint32_t off = (p >= 0 && p < rope.table_rows)
+                                                 ? static_cast<uint32_t>(p) * 128u + static_cast<uint32_t>(lane & 31) * 4u
+                                                 : kOobOffset;
+                        cs[4 * g + e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cos_rsrc, off, 0, 0));
+                        sn[4 * g + e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sin_rsrc, off, 0, 0));
+                    }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; b += 2) {
+                if (n_wave + b * 32 < rope.rot_cols) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float x1 = acc[tm][b][i] * rr[i], x2 = acc[tm][b + 1][i] * rr[i];
+                        v[b][i] = x1 * cs[i] - x2 * sn[i];
+                        v[b + 1][i] = x2 * cs[i] + x1 * sn[i];
+                    }
                 } else {
-                    v[b][i] = acc[tm][b][i] * rr[i];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        v[b][i] = acc[tm][b][i] * rr[i];
+                        v[b + 1][i] = acc[tm][b + 1][i] * rr[i];
+                    }
                 }
             }
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if constexpr (SWIGLU) {
+                        const float gv = acc[tm][b][i] * rr[i];
+                        const float uv = acc[tm][b + NB][i] * rr[i];
+                        v[b][i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+                    } else {
+                        v[b][i] = acc[tm][b][i] * rr[i];
+                    }
+                }
+        }
         S::put(slab, v);
 #pragma unroll
         for (int j = 0; j < S::kSegPerLane; ++j) {
@@ -87,13 +151,14 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
 
 // Direct-to-LDS mainloop (PIPE 1: the register-staged one, bf16 weights only).  W8: the
 // weights are e4m3, RB is the k-tile depth of a bf16 h row and a W row holds RB/2 bytes.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int PIPE, int OCC, bool SWIGLU,
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int PIPE, int OCC, int ACT,
           bool W8>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
                        uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
-                       int tiles_n) {
+                       int tiles_n, RopeArgs rope) {
+    constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -118,10 +183,13 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     // hides behind the mainloop; rows past M hold 0
     static_assert(WM % 64 == 0, "each lane holds WM / 64 row scales");
     float rv[WM / 64];
+    int pv[WM / 64];                                // RoPE: positions of the same rows
 #pragma unroll
     for (int i = 0; i < WM / 64; ++i) {
         const int m = m0 + wm * WM + 64 * i + (threadIdx.x & 63);
         rv[i] = m < M ? R[m] : 0.0f;
+        pv[i] = 0;
+        if constexpr (ACT == kActRope) pv[i] = (m < M && rope.rot_cols > 0) ? rope.pos[m] : 0;
     }
 
     const int kbytes = K * 2;                       // bytes of an h row
@@ -170,7 +238,7 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 
     const float sw = w_scale ? *w_scale : 1.0f;
     uint8_t* slab = slab_region<NS, NW, kStage, Slab<SWIGLU ? TN / 2 : TN>::kBytes>(st, wave);
-    rowscale_epilogue<BM, BN, WAVES_M, TM, TN, SWIGLU>(acc, rv, sw, Y, M, N_out, m0, j0, wm, wn, slab);
+    rowscale_epilogue<BM, BN, WAVES_M, TM, TN, ACT>(acc, rv, pv, rope, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
 // Tile configurations of the second GEMM (compile-time).
@@ -202,27 +270,38 @@ int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
     return ((M + BM3 - 1) / BM3) * ((N_out + bno - 1) / bno);
 }
 
-template <bool SWIGLU, bool WFP8>
+template <int ACT, bool WFP8>
 static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
-                          const float* w_scale, const float* r, void* y, hipStream_t stream) {
-    constexpr int BNO = SWIGLU ? BN3 / 2 : BN3;
+                          const float* w_scale, const float* r, void* y, const RopeArgs& rope,
+                          hipStream_t stream) {
+    constexpr int BNO = ACT == kActSwiglu ? BN3 / 2 : BN3;
     const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BNO - 1) / BNO;
     const dim3 grid(tiles_m * tiles_n), block(64 * WM3 * WN3);
     hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, WFP8 ? 0 : PIPE3,
-                                               OCC3, SWIGLU, WFP8>),
+                                               OCC3, ACT, WFP8>),
                        grid, block, 0, stream, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W),
-                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n);
+                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n, rope);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, const void* h,
                                        const void* W, bool w_fp8, const float* w_scale,
                                        const float* r, void* y, hipStream_t stream) {
+    const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
     if (swiglu)
-        return w_fp8 ? launch3<true, true>(M, N_out, K, h, W, w_scale, r, y, stream)
-                     : launch3<true, false>(M, N_out, K, h, W, w_scale, r, y, stream);
-    return w_fp8 ? launch3<false, true>(M, N_out, K, h, W, w_scale, r, y, stream)
-                 : launch3<false, false>(M, N_out, K, h, W, w_scale, r, y, stream);
+        return w_fp8 ? launch3<kActSwiglu, true>(M, N_out, K, h, W, w_scale, r, y, none, stream)
+                     : launch3<kActSwiglu, false>(M, N_out, K, h, W, w_scale, r, y, none, stream);
+    return w_fp8 ? launch3<kActNone, true>(M, N_out, K, h, W, w_scale, r, y, none, stream)
+                 : launch3<kActNone, false>(M, N_out, K, h, W, w_scale, r, y, none, stream);
+}
+
+hipError_t launch_gemm_rowscale_rope(int M, int N_out, int K, const void* h, const void* W,
+                                     bool w_fp8, const float* w_scale, const float* r,
+                                     const int32_t* pos, const float* cos, const float* sin,
+                                     int table_rows, int rot_cols, void* y, hipStream_t stream) {
+    const RopeArgs rope{pos, cos, sin, table_rows, rot_cols};
+    return w_fp8 ? launch3<kActRope, true>(M, N_out, K, h, W, w_scale, r, y, rope, stream)
+                 : launch3<kActRope, false>(M, N_out, K, h, W, w_scale, r, y, rope, stream);
 }
 
 }  // namespace coda

@@ -107,6 +107,26 @@ static unsigned grid_for(int64_t n_vec) {
     return static_cast<unsigned>(blocks < 8192 ? (blocks < 1 ? 1 : blocks) : 8192);
 }
 
+// RoPE angle table: cos / sin of p * base^(-2i/64) for p < rows, i < 32, in fp64, one
+// rounding to fp32.  One thread per (p, i).
+__global__ void __launch_bounds__(256)
+k_rope_table(int rows, double base, float* __restrict__ cos_t, float* __restrict__ sin_t) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= static_cast<int64_t>(rows) * 32) return;
+    const int p = static_cast<int>(idx >> 5), i = static_cast<int>(idx & 31);
+    const double theta = pow(base, -2.0 * static_cast<double>(i) / 64.0);
+    const double ang = static_cast<double>(p) * theta;
+    cos_t[idx] = static_cast<float>(cos(ang));
+    sin_t[idx] = static_cast<float>(sin(ang));
+}
+
+hipError_t launch_rope_table(int rows, double base, float* cos_t, float* sin_t, hipStream_t stream) {
+    const int64_t n = static_cast<int64_t>(rows) * 32;
+    hipLaunchKernelGGL(k_rope_table, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, rows,
+                       base, cos_t, sin_t);
+    return hipGetLastError();
+}
+
 hipError_t launch_fold_bf16(int64_t N, int64_t K, const void* W, const float* gamma, void* Wp,
                             hipStream_t stream) {
     const int64_t k_vec = K / 8, n_vec = N * k_vec;

@@ -27,6 +27,15 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
                                        const void* W, bool w_fp8, const float* w_scale,
                                        const float* r, void* y, hipStream_t stream);
 
+// Row scale + RoPE epilogue (no activation); pos / cos / sin may be NULL when
+// rot_cols == 0.
+hipError_t launch_gemm_rowscale_rope(int M, int N_out, int K, const void* h, const void* W,
+                                     bool w_fp8, const float* w_scale, const float* r,
+                                     const int32_t* pos, const float* cos, const float* sin,
+                                     int table_rows, int rot_cols, void* y, hipStream_t stream);
+
+hipError_t launch_rope_table(int rows, double base, float* cos, float* sin, hipStream_t stream);
+
 hipError_t launch_fold_bf16(int64_t N, int64_t K, const void* W, const float* gamma, void* Wp,
                             hipStream_t stream);
 

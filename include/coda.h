@@ -143,6 +143,46 @@ coda_status coda_gemm_rowscale_swiglu(int64_t M, int64_t N_out, int64_t K, coda_
                                       const float* w_scale, const float* r, void* y,
                                       void* stream);
 
+/* ------------------------------------------------------------------------ RoPE ----
+ * Rotary position embedding as the pairwise epilogue of the QKV GEMM (kucoin page,
+ * section "CODA: El epilogo esconde un tesoro", last paragraph: the reparameterisation
+ * also covers RoPE; section "Cinco bloques y un lenguaje LEGO": an element-wise
+ * transform).  LLaMA layout: the output columns are heads of 64 values, Q heads then K
+ * heads then V heads; in a rotated head value i pairs with value i + 32 (i < 32) and
+ * the pair turns by the angle pos * theta_i, theta_i = base^(-2i/64).
+ */
+
+/* cos / sin table of the angles:  cos[p*32 + i] = fl32( cos(p * base^(-2i/64)) ),
+ * sin likewise, for positions p in [0, rows), i in [0, 32) (angles and cosines in
+ * fp64, one rounding to fp32).
+ *   cos, sin [rows, 32] fp32, device, written; must not overlap.
+ * rows in [1, 2^24); base finite and > 1 (CODA_ERR_VALUE otherwise).                   */
+coda_status coda_rope_table(int64_t rows, double base, float* cos, float* sin, void* stream);
+
+/* Second GEMM with row-scale + RoPE epilogue (no activation).  z = sw * (h . W^T):
+ *   x[m,n] = r[m] * z[m,n];
+ *   for a column n < rot_cols in head c = n / 64 at offset i = n % 64 < 32, with
+ *   p = pos[m], C = cos[p*32 + i], S = sin[p*32 + i]:
+ *     y[m, 64c + i]      = bf16_rne( x[m, 64c + i] * C - x[m, 64c + i + 32] * S )
+ *     y[m, 64c + i + 32] = bf16_rne( x[m, 64c + i + 32] * C + x[m, 64c + i] * S )
+ *   columns n >= rot_cols (V):  y[m,n] = bf16_rne( x[m,n] ).
+ *   h, W, w_dtype, w_scale, r as for coda_gemm_rowscale_swiglu with CODA_ACT_NONE
+ *             (W [N_out, K])
+ *   pos       [M] int32, device: the row's position.  A position outside
+ *             [0, table_rows) reads cos = sin = 0 (the table lookups are range-checked),
+ *             i.e. zeros in that row's rotated columns -- not an error.
+ *   cos, sin  [table_rows, 32] fp32, device (coda_rope_table)
+ *   rot_cols  number of leading rotated columns (Q and K heads): a multiple of 64,
+ *             0 <= rot_cols <= N_out.  With rot_cols == 0 pos / cos / sin may be NULL.
+ *   y         [M, N_out] bf16, device, written; must not overlap any input
+ * Granules: as coda_gemm_rowscale_swiglu with CODA_ACT_NONE; table_rows in [1, 2^24)
+ * when rot_cols > 0.                                                                  */
+coda_status coda_gemm_rowscale_rope(int64_t M, int64_t N_out, int64_t K, const void* h,
+                                    const void* W, coda_dtype w_dtype, const float* w_scale,
+                                    const float* r, const int32_t* pos, const float* cos,
+                                    const float* sin, int64_t table_rows, int64_t rot_cols,
+                                    void* y, void* stream);
+
 /* ------------------------------------------------------------------- utilities ---- */
 const char* coda_status_string(coda_status s);
 int coda_last_hip_error(void);      /* hipError_t of this thread's last CODA_ERR_HIP      */

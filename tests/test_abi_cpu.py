@@ -133,3 +133,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+@no_gpu
+def test_rope_validation():
+    L = _lib.load()
+    t = L.coda_rope_table
+    assert t(0, 500000.0, P1, P2, None) == SHAPE
+    assert t(1 << 24, 500000.0, P1, P2, None) == SHAPE
+    assert t(16, 1.0, P1, P2, None) == VALUE
+    assert t(16, float("inf"), P1, P2, None) == VALUE
+    assert t(16, 500000.0, None, P2, None) == NULL
+    assert t(16, 500000.0, P1 + 4, P2, None) == ALIGN
+    assert t(16, 500000.0, P1, P1 + 16, None) == ALIAS
+    f = L.coda_gemm_rowscale_rope
+    # M, N_out, K, h, W, wdt, sw, r, pos, cos, sin, rows, rot_cols, y, stream
+    assert f(16, 128, 64, P1, P2, 2, None, P3, P4, P5, P6, 8, 64, P6 + 4096, None) == DTYPE
+    assert f(16, 128, 64, P1, P2, 0, None, P3, P4, P5, P6, 8, 32, P6 + 4096, None) == SHAPE   # not whole heads
+    assert f(16, 128, 64, P1, P2, 0, None, P3, P4, P5, P6, 8, 192, P6 + 4096, None) == SHAPE  # > N_out
+    assert f(16, 128, 64, P1, P2, 0, None, P3, P4, P5, P6, 0, 64, P6 + 4096, None) == SHAPE   # no table
+    assert f(16, 124, 64, P1, P2, 0, None, P3, P4, P5, P6, 8, 64, P6 + 4096, None) == SHAPE   # N_out % 8
+    assert f(16, 128, 64, P1, P2, 0, None, P3, None, P5, P6, 8, 64, P6 + 4096, None) == NULL
+    assert f(16, 128, 64, P1, P2, 1, None, P3, P4, P5, P6, 8, 64, P6 + 4096, None) == NULL    # e4m3 scale
+    assert f(16, 128, 64, P1, P2, 0, None, P3, P4 + 4, P5, P6, 8, 64, P6 + 4096, None) == ALIGN
+    assert f(16, 128, 64, P1, P2, 0, None, P3, P4, P5, P6, 8, 64, P4, None) == ALIAS          # y over pos
+    assert f(16, 128, 64, P1, P2, 0, None, P3, P4, P5, P6, 8, 64, P5, None) == ALIAS          # y over cos
+    # rot_cols == 0: no table, positions or angles needed; M == 0 enqueues nothing
+    assert f(0, 128, 64, P1, P2, 0, None, P3, None, None, None, 0, 0, P6 + 4096, None) == OK
+    assert f(0, 128, 64, P1, P2, 0, None, P3, P4, P5, P6, 8, 64, P6 + 4096, None) == OK
