@@ -7,7 +7,8 @@
  * optimizes Transformer training..." section "CODA: El epilogo esconde un tesoro"):
  * a matrix product, a residual add, RMS normalisation, a second matrix product, and
  * (same section, last paragraph; section "Resultados del experimento") SwiGLU, or
- * (same paragraph) RoPE on the QKV product (orc_rope, applied to the act-NONE output).
+ * (same paragraph) RoPE on the QKV product (orc_rope) or the cross-entropy loss of the
+ * LM-head product (orc_cross_entropy), both applied to the act-NONE output.
  * It is the UNFUSED definition: no tiling, no partial sums, no deferred row scale.
  *
  * Readings where the pages are silent (all listed in the design notes):
@@ -290,6 +291,36 @@ int orc_rope(int64_t R, int64_t ncols, double* y, const int32_t* pos, double bas
                 y[i * ncols + h0 + half + j] = x2 * c + x1 * sn;
             }
         }
+    }
+    return 0;
+}
+
+/* -------------------------------------------------------- cross-entropy ---- */
+
+/*
+ * Cross-entropy of the LM-head product's logits (kucoin page, section "CODA: El
+ * epilogo esconde un tesoro", last paragraph: the reparameterisation covers the
+ * cross-entropy loss; section "Cinco bloques y un lenguaje LEGO": block log-sum-exp
+ * and the max / sum-exp statistics of online normalisation).  Per row of z [R, V]
+ * (fp64, the unrounded chain output, i.e. r * (h . W'^T)):
+ *   lse  = log( sum_v exp(z[v]) )          (evaluated as m + log(sum exp(z - m)),
+ *                                            m = max z: the same number, no overflow)
+ *   loss = lse - z[t]  for a target t in [0, V);  0 for any other t (an ignored row).
+ */
+int orc_cross_entropy(int64_t R, int64_t V, const double* z, const int32_t* targets,
+                      double* lse_out, double* loss_out) {
+    if (V < 1) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < R; ++i) {
+        const double* zi = z + i * V;
+        double m = zi[0];
+        for (int64_t v = 1; v < V; ++v) m = zi[v] > m ? zi[v] : m;
+        double s = 0.0;
+        for (int64_t v = 0; v < V; ++v) s += exp(zi[v] - m);
+        double lse = m + log(s);
+        int64_t t = targets[i];
+        lse_out[i] = lse;
+        loss_out[i] = (t >= 0 && t < V) ? lse - zi[t] : 0.0;
     }
     return 0;
 }

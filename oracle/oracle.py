@@ -24,7 +24,7 @@ ACT_NONE = 0
 ACT_SWIGLU = 1
 
 __all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
-           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "chain", "prepare", "BF16", "E4M3",
+           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "cross_entropy", "chain", "prepare", "BF16", "E4M3",
            "ACT_NONE", "ACT_SWIGLU"]
 
 
@@ -64,6 +64,8 @@ def lib():
         L.orc_fold_bf16.argtypes = [i64, i64, P, P, P]
         L.orc_quant_e4m3.restype = None
         L.orc_quant_e4m3.argtypes = [i64, i64, P, P, P, P, P]
+        L.orc_cross_entropy.restype = C.c_int
+        L.orc_cross_entropy.argtypes = [i64, i64, P, P, P, P]
         L.orc_rope.restype = C.c_int
         L.orc_rope.argtypes = [i64, i64, P, P, C.c_double, i64, i64]
         L.orc_chain.restype = C.c_int
@@ -206,3 +208,17 @@ def rope(y: np.ndarray, pos, base: float, head_dim: int, rot_cols: int) -> np.nd
     if rc != 0:
         raise ValueError("bad RoPE layout")
     return out
+
+
+def cross_entropy(z: np.ndarray, targets):
+    """(lse, loss) per row of the logits ``z`` (fp64 [R, V]): lse = log sum exp z,
+    loss = lse - z[target] (0 for a target outside [0, V), an ignored row)."""
+    zz = np.ascontiguousarray(z, dtype=np.float64)
+    t = np.ascontiguousarray(targets, dtype=np.int32)
+    if zz.ndim != 2 or t.shape != (zz.shape[0],):
+        raise ValueError("z must be [R, V] and targets [R]")
+    lse = np.empty(zz.shape[0], np.float64)
+    loss = np.empty(zz.shape[0], np.float64)
+    if lib().orc_cross_entropy(zz.shape[0], zz.shape[1], _p(zz), _p(t), _p(lse), _p(loss)) != 0:
+        raise ValueError("empty vocabulary")
+    return lse, loss

@@ -33,6 +33,7 @@ import numpy as np
 ACT_NONE = 0
 ACT_SWIGLU = 1
 ACT_ROPE = 2      # rotary position embedding on the QKV product (no activation)
+ACT_CE = 3        # cross-entropy of the LM-head product against per-row targets
 
 
 @dataclasses.dataclass(frozen=True)
@@ -42,7 +43,7 @@ class Workload:
     K1: int         # reduction dim of the first GEMM
     d: int          # hidden dim = N of the first GEMM = reduction dim of the second GEMM
     N2w: int        # rows of the second weight (2F for SwiGLU, N2 otherwise)
-    act: int        # ACT_NONE, ACT_SWIGLU or ACT_ROPE
+    act: int        # ACT_NONE, ACT_SWIGLU, ACT_ROPE or ACT_CE (then N2w = vocabulary size)
     dtype: str      # "bf16" or "e4m3" (fp8 variant: A, Wo and the second weight in e4m3)
     eps: float
     seed: int
@@ -68,7 +69,9 @@ class Workload:
 # heads = 3072); 4: LLaMA-3-8B-shaped attention-out -> SwiGLU MLP-in; 5: workload 2
 # with A, Wo and the second weight quantised to e4m3 (same draws as workload 2);
 # 6: workload 3 with RoPE on its Q and K columns (32 + 8 heads of 64 = 2560 of the 3072
-# columns; V passes), 16384 tokens = 4 sequences of 4096 (same draws as workload 3).
+# columns; V passes), 16384 tokens = 4 sequences of 4096 (same draws as workload 3);
+# 7: the last block of LLaMA-3-1B -- MLP-out + residual, final RMSNorm, LM head over the
+# 128256-token vocabulary -- ending in the cross-entropy loss against uniform targets.
 WORKLOADS = {
     1: Workload("tiny_m128_d256_n512_none", 128, 256, 256, 512, ACT_NONE, "bf16", 1e-5, 1001),
     2: Workload("llama1b_attnout_mlpin_m16384", 16384, 2048, 2048, 16384, ACT_SWIGLU, "bf16", 1e-5, 1002),
@@ -77,6 +80,7 @@ WORKLOADS = {
     5: Workload("llama1b_attnout_mlpin_m16384_fp8", 16384, 2048, 2048, 16384, ACT_SWIGLU, "e4m3", 1e-5, 1002),
     6: Workload("llama1b_mlpout_qkv_rope_m16384", 16384, 8192, 2048, 3072, ACT_ROPE, "bf16", 1e-5, 1003,
                 rot_cols=2560, seq_len=4096),
+    7: Workload("llama1b_mlpout_lmhead_ce_m16384", 16384, 8192, 2048, 128256, ACT_CE, "bf16", 1e-5, 1007),
 }
 
 
@@ -114,6 +118,8 @@ def generate(w: Workload, rows: int | None = None) -> dict:
       gamma  float32 [d]
       W_t    uint16 [N2w, d]  bf16 bits (second weight before the gamma fold)
       pos    int32 [M]        RoPE workloads only: token m's position, m mod seq_len
+      targets int32 [M]       cross-entropy workloads only: uniform in [0, N2w), drawn
+                              after W
     For an e4m3 workload these are the pre-quantisation tensors (quantisation is a
     step of the chain's weight/activation preparation, not of input generation).
     ``rows`` (optional) truncates M, keeping the draws of the first rows identical.
@@ -125,8 +131,10 @@ def generate(w: Workload, rows: int | None = None) -> dict:
     x = rng.standard_normal((w.M, w.d), dtype=f32)
     gamma = (f32(1.0) + f32(0.1) * rng.standard_normal(w.d, dtype=f32)).astype(f32)
     W = rng.standard_normal((w.N2w, w.d), dtype=f32) * f32(1.0 / np.sqrt(w.d))
+    tgt = rng.integers(0, w.N2w, size=w.M, dtype=np.int32) if w.act == ACT_CE else None
     if rows is not None:
         A, x = A[:rows], x[:rows]
+        tgt = None if tgt is None else tgt[:rows]
     out = {
         "A": to_bf16_bits(A),
         "Wo_t": to_bf16_bits(Wo),
@@ -136,4 +144,6 @@ def generate(w: Workload, rows: int | None = None) -> dict:
     }
     if w.act == ACT_ROPE:
         out["pos"] = (np.arange(A.shape[0]) % w.seq_len).astype(np.int32)
+    if tgt is not None:
+        out["targets"] = tgt
     return out
