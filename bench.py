@@ -53,11 +53,24 @@ def algorithmic_bytes(w, fused=True) -> dict:
     M, K1, d, N2w, n_out = w.M, w.K1, w.d, w.N2w, w.n_out
     T = -(-d // 256)                      # one partial per 256-column tile of GEMM 1
     rope = w.act == si.ACT_ROPE
+    ce = w.act == si.ACT_CE
     k1 = M * K1 * eb + d * K1 * eb + M * d * 2 + M * d * 2 + M * T * 4
     k2 = M * T * 4 + M * 4
     k3 = M * d * 2 + N2w * d * eb + M * 4 + M * n_out * 2
     if rope:                              # positions, cos / sin table
         k3 += M * 4 + 2 * w.seq_len * 32 * 4
+    if ce:
+        # no logits: targets in, one (max, sum-exp) pair per row and 256-column tile and
+        # the target's logit out; the loss reduction reads those and writes lse and loss
+        Tv = -(-N2w // 256)
+        k3 = M * d * 2 + N2w * d * eb + M * 4 + M * 4 + M * Tv * 8 + M * 4
+        k4 = M * Tv * 8 + M * 4 + M * 4 + 2 * M * 4
+        if fused:
+            return {"gemm1": k1, "reduce": k2, "gemm2": k3, "ce_reduce": k4, "total": k1 + k2 + k3 + k4}
+        # unfused: GEMM 2 writes the bf16 logits, the loss kernel reads them
+        tot = (M * K1 * eb + d * K1 * eb + M * d * 2) + 3 * M * d * 2 + 2 * M * d * 2 + d * 4 \
+            + (M * d * 2 + N2w * d * eb + M * N2w * 2) + M * N2w * 2 + M * 4 + M * 4
+        return {"total": tot}
     if fused:
         return {"gemm1": k1, "reduce": k2, "gemm2": k3, "total": k1 + k2 + k3}
     # unfused: the activation / rotation is a kernel of its own (reads z, writes y)
@@ -136,6 +149,19 @@ def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
     print("\n".join(lines))
 
 
+def _oracle_path(oracle, prep, inp, w, rows):
+    """The oracle's whole path for the rows: the chain, then RoPE or the loss."""
+    import synth_inputs as si
+
+    act = w.act if w.act in (si.ACT_NONE, si.ACT_SWIGLU) else si.ACT_NONE
+    ref = oracle.chain(prep, inp["x_res"], inp["gamma"], act, w.eps, rows=rows)
+    if w.act == si.ACT_ROPE:
+        oracle.rope(ref["y"], inp["pos"][rows], w.rope_base, w.head_dim, w.rot_cols)
+    elif w.act == si.ACT_CE:
+        oracle.cross_entropy(ref["y"], inp["targets"][rows])
+    return ref
+
+
 def cpu_baseline(w, inp, target_s: float) -> dict:
     import numpy as np
 
@@ -149,7 +175,7 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
     while True:
         rows = np.sort(rng.choice(w.M, size=min(n, w.M), replace=False))
         t0 = time.perf_counter()
-        oracle.chain(prep, inp["x_res"], inp["gamma"], w.act, w.eps, rows=rows)
+        _oracle_path(oracle, prep, inp, w, rows)
         dt = time.perf_counter() - t0
         if dt >= target_s / 4 or n >= w.M:
             break
@@ -158,7 +184,7 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
         n = int(min(w.M, n * target_s / dt))
         rows = np.sort(rng.choice(w.M, size=n, replace=False))
         t0 = time.perf_counter()
-        oracle.chain(prep, inp["x_res"], inp["gamma"], w.act, w.eps, rows=rows)
+        _oracle_path(oracle, prep, inp, w, rows)
         dt = time.perf_counter() - t0
     n = rows.size
     return {"value": round(n * per_row / dt / 1e12, 6), "unit": "TFLOP/s",
@@ -232,6 +258,14 @@ def main():
     torch.cuda.synchronize()
     prep_ms = (time.perf_counter() - t0) * 1e3
 
+    ce_in = None
+    if w.act == si.ACT_CE:
+        T_ce = coda.ce_partials_per_row(w.N2w)
+        ce_in = {"targets": torch.from_numpy(inp["targets"]).cuda(),
+                 "partials": torch.empty((w.M, T_ce, 2), dtype=torch.float32, device="cuda"),
+                 "tgt": torch.empty(w.M, dtype=torch.float32, device="cuda"),
+                 "lse": torch.empty(w.M, dtype=torch.float32, device="cuda"),
+                 "loss": torch.empty(w.M, dtype=torch.float32, device="cuda")}
     rope_in = None
     if w.act == si.ACT_ROPE:              # angle table and positions: once, like the weights
         cos_t, sin_t = coda.rope_table(w.seq_len, w.rope_base)
@@ -242,7 +276,7 @@ def main():
     out = {"h": torch.empty((M, d), dtype=torch.bfloat16, device="cuda"),
            "partials": torch.empty((M, coda.partials_per_row(d)), dtype=torch.float32, device="cuda"),
            "r": torch.empty(M, dtype=torch.float32, device="cuda"),
-           "y": torch.empty((M, w.n_out), dtype=torch.bfloat16, device="cuda")}
+           "y": None if ce_in else torch.empty((M, w.n_out), dtype=torch.bfloat16, device="cuda")}
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -254,19 +288,25 @@ def main():
         r = coda.rowscale_reduce(P, d, w.eps, out["r"])
         if ev is not None:
             ev[2].record(stream)
-        if rope_in is None:
+        if ce_in is not None:
+            coda.gemm_rowscale_ce(h, Wp, r, ce_in["targets"], sw, ce_in["partials"], ce_in["tgt"])
+        elif rope_in is None:
             coda.gemm_rowscale_swiglu(h, Wp, r, w.act, sw, out["y"])
         else:
             coda.gemm_rowscale_rope(h, Wp, r, *rope_in, w.rot_cols, sw, out["y"])
         if ev is not None:
             ev[3].record(stream)
+        if ce_in is not None:
+            coda.ce_reduce(ce_in["partials"], ce_in["targets"], ce_in["tgt"], w.N2w, ce_in["lse"], ce_in["loss"])
+            if ev is not None:
+                ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # timed region: K chains, per-kernel HIP events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -278,6 +318,7 @@ def main():
     k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     k3_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    k4_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if ce_in is not None else None
 
     flops = w.gemm_flops
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -298,12 +339,14 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "e4m3/bf16", "data": "synthetic",
         "config": {"workload": w.name, "M": M, "K1": w.K1, "d": d, "N2w": w.N2w,
-                   "act": {si.ACT_SWIGLU: "swiglu", si.ACT_ROPE: "rope"}.get(w.act, "none"), "eps": w.eps,
+                   "act": {si.ACT_SWIGLU: "swiglu", si.ACT_ROPE: "rope", si.ACT_CE: "cross_entropy"}.get(
+                       w.act, "none"), "eps": w.eps,
                    "seed": w.seed, **({"rot_cols": w.rot_cols, "seq_len": w.seq_len, "rope_base": w.rope_base}
                                       if w.act == si.ACT_ROPE else {})},
         "frac_of_peak_chain": round(value / PEAK_TFLOPS["bf16"], 4),
         "kernels_ms": {"gemm_resid_partialrms": round(k1_ms, 4), "rowscale_reduce": round(k2_ms, 4),
-                       "gemm_rowscale_swiglu": round(k3_ms, 4)},
+                       "gemm_rowscale_swiglu": round(k3_ms, 4),
+                       **({"ce_reduce": round(k4_ms, 4)} if k4_ms is not None else {})},
         "gemm1_tflops": round(g1_flops / (k1_ms * 1e-3) / 1e12, 2),
         "hbm_bytes_algorithmic": {"fused": byt["total"], "unfused": algorithmic_bytes(w, False)["total"]},
         "prep_ms": round(prep_ms, 3),
@@ -322,6 +365,8 @@ def main():
             if w.act == si.ACT_SWIGLU:
                 F_ = w.n_out
                 return torch.nn.functional.silu(z[:, :F_]) * z[:, F_:]
+            if w.act == si.ACT_CE:
+                return torch.nn.functional.cross_entropy(z.float(), ce_in["targets"].long(), reduction="none")
             if w.act == si.ACT_ROPE:
                 pos_t, cos_t, sin_t = rope_in
                 q = z[:, : w.rot_cols].view(M, -1, 64)

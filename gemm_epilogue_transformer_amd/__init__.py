@@ -22,7 +22,8 @@ SWIGLU = CODA_ACT_SWIGLU
 
 __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3",
            "partials_per_row", "gemm_resid_partialrms", "rowscale_reduce",
-           "gemm_rowscale_swiglu", "rope_table", "gemm_rowscale_rope", "chain", "version"]
+           "gemm_rowscale_swiglu", "rope_table", "gemm_rowscale_rope", "ce_partials_per_row",
+           "gemm_rowscale_ce", "ce_reduce", "chain", "version"]
 
 
 def _stream(stream):
@@ -153,6 +154,40 @@ def gemm_rowscale_rope(h, W, r, pos, cos, sin, rot_cols, w_scale=None, y=None, s
         M, n_out, K, _ptr(h), _ptr(W), CODA_E4M3 if fp8 else CODA_BF16, _ptr(w_scale), _ptr(r),
         _ptr(pos), _ptr(cos), _ptr(sin), rows, rot_cols, _ptr(y), _stream(stream)))
     return y
+
+
+def ce_partials_per_row(V: int) -> int:
+    return int(_lib.load().coda_ce_partials_per_row(V))
+
+
+def gemm_rowscale_ce(h, W, r, targets, w_scale=None, partials=None, tgt_logit=None, stream=None):
+    """LM-head GEMM with the block log-sum-exp epilogue: W [V, K]; returns (partials
+    [M, T, 2] = per-tile (max, sum exp(z - max)), tgt_logit [M] = z[m, targets[m]])."""
+    M, K = h.shape
+    V = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("h and W disagree on K")
+    if targets.dtype != torch.int32:
+        raise ValueError("targets must be int32")
+    T = ce_partials_per_row(V)
+    dev = h.device
+    partials = torch.empty((M, T, 2), dtype=torch.float32, device=dev) if partials is None else partials
+    tgt_logit = torch.empty(M, dtype=torch.float32, device=dev) if tgt_logit is None else tgt_logit
+    fp8 = W.element_size() == 1
+    _lib.check("coda_gemm_rowscale_ce", _lib.load().coda_gemm_rowscale_ce(
+        M, V, K, _ptr(h), _ptr(W), CODA_E4M3 if fp8 else CODA_BF16, _ptr(w_scale), _ptr(r), _ptr(targets),
+        _ptr(partials), _ptr(tgt_logit), _stream(stream)))
+    return partials, tgt_logit
+
+
+def ce_reduce(partials, targets, tgt_logit, V, lse=None, loss=None, stream=None):
+    """(lse [M], loss [M]) from the LM-head GEMM's partials (loss 0 for ignored rows)."""
+    M = partials.shape[0]
+    lse = torch.empty(M, dtype=torch.float32, device=partials.device) if lse is None else lse
+    loss = torch.empty(M, dtype=torch.float32, device=partials.device) if loss is None else loss
+    _lib.check("coda_ce_reduce", _lib.load().coda_ce_reduce(
+        M, V, _ptr(partials), _ptr(targets), _ptr(tgt_logit), _ptr(lse), _ptr(loss), _stream(stream)))
+    return lse, loss
 
 
 def chain(A, Wo_t, x_res, Wp_t, eps, act=SWIGLU, a_scale=None, wo_scale=None, wp_scale=None,

@@ -27,6 +27,9 @@ SIGNATURES = {
     "coda_gemm_rowscale_swiglu": (_I, [_I64, _I64, _I64, _I, _P, _P, _I, _P, _P, _P, _P]),
     "coda_rope_table": (_I, [_I64, C.c_double, _P, _P, _P]),
     "coda_gemm_rowscale_rope": (_I, [_I64, _I64, _I64, _P, _P, _I, _P, _P, _P, _P, _P, _I64, _I64, _P, _P]),
+    "coda_ce_partials_per_row": (_I64, [_I64]),
+    "coda_gemm_rowscale_ce": (_I, [_I64, _I64, _I64, _P, _P, _I, _P, _P, _P, _P, _P, _P]),
+    "coda_ce_reduce": (_I, [_I64, _I64, _P, _P, _P, _P, _P, _P]),
     "coda_status_string": (C.c_char_p, [_I]),
     "coda_last_hip_error": (_I, []),
     "coda_version": (C.c_char_p, []),

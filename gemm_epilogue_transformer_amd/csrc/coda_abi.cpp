@@ -214,4 +214,51 @@ coda_status coda_gemm_rowscale_rope(int64_t M, int64_t N_out, int64_t K, const v
                                                       int(rot_cols), y, as_stream(stream)));
 }
 
+int64_t coda_ce_partials_per_row(int64_t V) { return V < 1 || V > kMaxRow ? -1 : coda::ce_partials_per_row(V); }
+
+coda_status coda_gemm_rowscale_ce(int64_t M, int64_t V, int64_t K, const void* h, const void* W,
+                                  coda_dtype w_dtype, const float* w_scale, const float* r,
+                                  const int32_t* targets, float* partials, float* tgt_logit,
+                                  void* stream) {
+    if (w_dtype != CODA_BF16 && w_dtype != CODA_E4M3) return CODA_ERR_DTYPE;
+    const bool fp8 = w_dtype == CODA_E4M3;
+    if (!dim_ok(M, 0) || !dim_ok(V, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (K % (fp8 ? 16 : 8) != 0 || V > kMaxRow || K > kMaxRow) return CODA_ERR_SHAPE;
+    const int64_t T = coda::ce_partials_per_row(V);
+    if (!prod_ok(M, K) || !prod_ok(V, K) || !prod_ok(M, 2 * T)) return CODA_ERR_SHAPE;
+    if (coda::gemm3_tiles(M, V, false) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!h || !W || !r || !targets || !partials || !tgt_logit) return CODA_ERR_NULL;
+    if (fp8 && !w_scale) return CODA_ERR_NULL;
+    if (!aligned16(h) || !aligned16(W) || !aligned16(r) || !aligned16(targets) || !aligned16(partials) ||
+        !aligned16(tgt_logit))
+        return CODA_ERR_ALIGN;
+    const Range rp = span(partials, M * T * 8), rt = span(tgt_logit, M * 4);
+    const Range ins[] = {span(h, M * K * 2), span(W, V * K * (fp8 ? 1 : 2)), span(r, M * 4), span(targets, M * 4),
+                         w_scale ? span(w_scale, 4) : Range{0, 0}};
+    if (overlap(rp, rt)) return CODA_ERR_ALIAS;
+    for (const Range& in : ins)
+        if (overlap(rp, in) || overlap(rt, in)) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_rowscale_ce(int(M), int(V), int(K), h, W, fp8, w_scale, r, targets, partials,
+                                                    tgt_logit, as_stream(stream)));
+}
+
+coda_status coda_ce_reduce(int64_t M, int64_t V, const float* partials, const int32_t* targets,
+                           const float* tgt_logit, float* lse, float* loss, void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(V, 1) || V > kMaxRow) return CODA_ERR_SHAPE;
+    const int64_t T = coda::ce_partials_per_row(V);
+    if (!prod_ok(M, 2 * T)) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!partials || !targets || !tgt_logit || !lse || !loss) return CODA_ERR_NULL;
+    if (!aligned16(partials) || !aligned16(targets) || !aligned16(tgt_logit) || !aligned16(lse) || !aligned16(loss))
+        return CODA_ERR_ALIGN;
+    const Range rl = span(lse, M * 4), rs = span(loss, M * 4);
+    const Range ins[] = {span(partials, M * T * 8), span(targets, M * 4), span(tgt_logit, M * 4)};
+    if (overlap(rl, rs)) return CODA_ERR_ALIAS;
+    for (const Range& in : ins)
+        if (overlap(rl, in) || overlap(rs, in)) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_ce_reduce(int(M), int(V), int(T), partials, targets, tgt_logit, lse, loss,
+                                             as_stream(stream)));
+}
+
 }  // extern "C"

@@ -28,7 +28,7 @@
 
 namespace coda {
 
-enum { kActNone = 0, kActSwiglu = 1, kActRope = 2 };
+enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3 };
 
 // RoPE operands (unused by the other activations).
 struct RopeArgs {
@@ -38,6 +38,101 @@ struct RopeArgs {
     int table_rows;
     int rot_cols;             // leading rotated columns (whole 64-column heads)
 };
+
+// Cross-entropy operands (unused by the other activations).
+struct CeArgs {
+    const int32_t* targets;   // [M]
+    float* partials;          // [M, T, 2]: (max, sum exp(z - max)) per 256-column tile
+    float* tgt_logit;         // [M]: z[m, targets[m]], written by the tile holding it
+    int T;                    // tiles per row = ceil(V / 256)
+};
+
+// Cross-entropy epilogue (kucoin page, section "Cinco bloques y un lenguaje LEGO": a
+// block log-sum-exp and the max / sum-exp state of online normalisation, in the epilogue
+// of the LM-head product; section "CODA: El epilogo esconde un tesoro": the
+// reparameterisation covers the cross-entropy loss).  The logits z = r*sw*acc never
+// leave the chip: per 32-row slab they are staged row-major in LDS like the other
+// epilogues; each lane takes 8 consecutive columns of one row (columns >= V masked),
+// its max, a butterfly max over the lanes of the row, the sum of exp(z - max), a
+// butterfly sum; the waves sharing a row are combined in a fixed order; one (max,
+// sum-exp) pair per row and tile.  The lane whose 8 columns hold the row's target
+// writes that logit.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
+__device__ __forceinline__ void ce_epilogue(const f32x16_t (&acc)[TM][TN], const float (&rv)[BM / WAVES_M / 64],
+                                            const int (&tv)[BM / WAVES_M / 64], float sw, const CeArgs& ce,
+                                            int M, int V, int m0, int j0, int tile_n, int wm, int wn,
+                                            uint8_t* slab, float* red) {
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, NT = 64 * WAVES_M * WAVES_N;
+    using S = Slab<TN>;
+    const int lane = threadIdx.x & 63;
+    const int lh = lane >> 5;
+    const float ninf = -__builtin_inff();
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        float rr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rr[4 * g + e] = __shfl(rv[tm / 2], (tm % 2) * 32 + 8 * g + 4 * lh + e) * sw;
+        float v[TN][16];
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[b][i] = acc[tm][b][i] * rr[i];
+        S::put(slab, v);
+#pragma unroll
+        for (int j = 0; j < S::kSegPerLane; ++j) {
+            float t[8];
+            S::get(slab, j, t);
+            const int rl = tm * 32 + S::seg_row(j);            // row within the wave
+            const int n = j0 + wn * WN + S::seg_col(j);         // first column of the 8
+            float mx = ninf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < V) mx = fmaxf(mx, t[e]);
+#pragma unroll
+            for (int off = S::kSegPerRow / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, S::kSegPerRow));
+            float sum = 0.0f;
+            if (mx > ninf) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < V) sum += __expf(t[e] - mx);
+            }
+#pragma unroll
+            for (int off = S::kSegPerRow / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, S::kSegPerRow);
+            const int tg = __shfl(tv[rl / 64], rl % 64);
+            if (tg >= n && tg < n + 8 && tg < V) {
+                float z = t[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) z = (tg - n == e) ? t[e] : z;
+                ce.tgt_logit[m0 + wm * WM + rl] = z;
+            }
+            if ((lane & (S::kSegPerRow - 1)) == 0) {
+                red[2 * (wn * BM + wm * WM + rl)] = mx;
+                red[2 * (wn * BM + wm * WM + rl) + 1] = sum;
+            }
+        }
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < BM; r += NT) {
+        const int m = m0 + r;
+        if (m < M) {
+            float mt = ninf;
+#pragma unroll
+            for (int w = 0; w < WAVES_N; ++w) mt = fmaxf(mt, red[2 * (w * BM + r)]);
+            float st = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WAVES_N; ++w) {
+                const float mw = red[2 * (w * BM + r)];
+                if (mw > ninf) st += red[2 * (w * BM + r) + 1] * __expf(mw - mt);
+            }
+            float* pp = ce.partials + (static_cast<size_t>(m) * ce.T + tile_n) * 2;
+            pp[0] = mt;
+            pp[1] = st;
+        }
+    }
+}
 
 // Epilogue shared by the bf16 and 8-bit weight instantiations.  Wave (wm, wn) holds TM x TN 32x32 accumulator blocks;
 // with SwiGLU, blocks [0, TN/2) are gate columns and [TN/2, TN) the matching up columns.
@@ -157,7 +252,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
                        uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
-                       int tiles_n, RopeArgs rope) {
+                       int tiles_n, RopeArgs rope, CeArgs ce) {
     constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -169,6 +264,8 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     constexpr int kStage = BM * RB + BN * RBB;
     static_assert(!W8 || (RB == 128 && PIPE == 0), "8-bit weights: DMA mainloop, 64-k tiles");
     __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+    // cross-entropy: (max, sum-exp) of every row for each of the WAVES_N column halves
+    __shared__ float ce_red[ACT == kActCe ? 2 * WAVES_N * BM : 1];
     uint8_t* st[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) st[i] = stages[i];
@@ -184,12 +281,15 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     static_assert(WM % 64 == 0, "each lane holds WM / 64 row scales");
     float rv[WM / 64];
     int pv[WM / 64];                                // RoPE: positions of the same rows
+    int tv[WM / 64];                                // cross-entropy: their targets (-1 past M)
 #pragma unroll
     for (int i = 0; i < WM / 64; ++i) {
         const int m = m0 + wm * WM + 64 * i + (threadIdx.x & 63);
         rv[i] = m < M ? R[m] : 0.0f;
         pv[i] = 0;
+        tv[i] = -1;
         if constexpr (ACT == kActRope) pv[i] = (m < M && rope.rot_cols > 0) ? rope.pos[m] : 0;
+        if constexpr (ACT == kActCe) tv[i] = m < M ? ce.targets[m] : -1;
     }
 
     const int kbytes = K * 2;                       // bytes of an h row
@@ -238,7 +338,11 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 
     const float sw = w_scale ? *w_scale : 1.0f;
     uint8_t* slab = slab_region<NS, NW, kStage, Slab<SWIGLU ? TN / 2 : TN>::kBytes>(st, wave);
-    rowscale_epilogue<BM, BN, WAVES_M, TM, TN, ACT>(acc, rv, pv, rope, sw, Y, M, N_out, m0, j0, wm, wn, slab);
+    if constexpr (ACT == kActCe)
+        ce_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, tv, sw, ce, M, N_out, m0, j0, tile_n, wm, wn, slab,
+                                                      ce_red);
+    else
+        rowscale_epilogue<BM, BN, WAVES_M, TM, TN, ACT>(acc, rv, pv, rope, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
 // Tile configurations of the second GEMM (compile-time).
@@ -273,14 +377,14 @@ int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
 template <int ACT, bool WFP8>
 static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                           const float* w_scale, const float* r, void* y, const RopeArgs& rope,
-                          hipStream_t stream) {
+                          const CeArgs& ce, hipStream_t stream) {
     constexpr int BNO = ACT == kActSwiglu ? BN3 / 2 : BN3;
     const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BNO - 1) / BNO;
     const dim3 grid(tiles_m * tiles_n), block(64 * WM3 * WN3);
     hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, WFP8 ? 0 : PIPE3,
                                                OCC3, ACT, WFP8>),
                        grid, block, 0, stream, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W),
-                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n, rope);
+                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n, rope, ce);
     return hipGetLastError();
 }
 
@@ -288,11 +392,12 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
                                        const void* W, bool w_fp8, const float* w_scale,
                                        const float* r, void* y, hipStream_t stream) {
     const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
+    const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
     if (swiglu)
-        return w_fp8 ? launch3<kActSwiglu, true>(M, N_out, K, h, W, w_scale, r, y, none, stream)
-                     : launch3<kActSwiglu, false>(M, N_out, K, h, W, w_scale, r, y, none, stream);
-    return w_fp8 ? launch3<kActNone, true>(M, N_out, K, h, W, w_scale, r, y, none, stream)
-                 : launch3<kActNone, false>(M, N_out, K, h, W, w_scale, r, y, none, stream);
+        return w_fp8 ? launch3<kActSwiglu, true>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, stream)
+                     : launch3<kActSwiglu, false>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, stream);
+    return w_fp8 ? launch3<kActNone, true>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, stream)
+                 : launch3<kActNone, false>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, stream);
 }
 
 hipError_t launch_gemm_rowscale_rope(int M, int N_out, int K, const void* h, const void* W,
@@ -300,8 +405,20 @@ hipError_t launch_gemm_rowscale_rope(int M, int N_out, int K, const void* h, con
                                      const int32_t* pos, const float* cos, const float* sin,
                                      int table_rows, int rot_cols, void* y, hipStream_t stream) {
     const RopeArgs rope{pos, cos, sin, table_rows, rot_cols};
-    return w_fp8 ? launch3<kActRope, true>(M, N_out, K, h, W, w_scale, r, y, rope, stream)
-                 : launch3<kActRope, false>(M, N_out, K, h, W, w_scale, r, y, rope, stream);
+    const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
+    return w_fp8 ? launch3<kActRope, true>(M, N_out, K, h, W, w_scale, r, y, rope, no_ce, stream)
+                 : launch3<kActRope, false>(M, N_out, K, h, W, w_scale, r, y, rope, no_ce, stream);
+}
+
+int64_t ce_partials_per_row(int64_t V) { return V < 1 ? -1 : (V + BN3 - 1) / BN3; }
+
+hipError_t launch_gemm_rowscale_ce(int M, int V, int K, const void* h, const void* W, bool w_fp8,
+                                   const float* w_scale, const float* r, const int32_t* targets,
+                                   float* partials, float* tgt_logit, hipStream_t stream) {
+    const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
+    const CeArgs ce{targets, partials, tgt_logit, static_cast<int>(ce_partials_per_row(V))};
+    return w_fp8 ? launch3<kActCe, true>(M, V, K, h, W, w_scale, r, nullptr, none, ce, stream)
+                 : launch3<kActCe, false>(M, V, K, h, W, w_scale, r, nullptr, none, ce, stream);
 }
 
 }  // namespace coda

@@ -36,6 +36,14 @@ hipError_t launch_gemm_rowscale_rope(int M, int N_out, int K, const void* h, con
 
 hipError_t launch_rope_table(int rows, double base, float* cos, float* sin, hipStream_t stream);
 
+// Cross-entropy: LM-head GEMM with the block log-sum-exp epilogue, then the reduction.
+int64_t ce_partials_per_row(int64_t V);
+hipError_t launch_gemm_rowscale_ce(int M, int V, int K, const void* h, const void* W, bool w_fp8,
+                                   const float* w_scale, const float* r, const int32_t* targets,
+                                   float* partials, float* tgt_logit, hipStream_t stream);
+hipError_t launch_ce_reduce(int M, int V, int T, const float* partials, const int32_t* targets,
+                            const float* tgt_logit, float* lse, float* loss, hipStream_t stream);
+
 hipError_t launch_fold_bf16(int64_t N, int64_t K, const void* W, const float* gamma, void* Wp,
                             hipStream_t stream);
 

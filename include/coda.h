@@ -183,6 +183,47 @@ coda_status coda_gemm_rowscale_rope(int64_t M, int64_t N_out, int64_t K, const v
                                     const float* sin, int64_t table_rows, int64_t rot_cols,
                                     void* y, void* stream);
 
+/* --------------------------------------------------------------- cross-entropy ----
+ * The LM-head GEMM with the loss in its epilogue (kucoin page, section "CODA: El
+ * epilogo esconde un tesoro", last paragraph: the reparameterisation covers the
+ * cross-entropy loss; section "Cinco bloques y un lenguaje LEGO": a block log-sum-exp
+ * and the max / sum-exp state of online normalisation).  The logits never reach
+ * memory: the GEMM writes one (max, sum-exp) pair per row and 256-column tile, and a
+ * light reduction turns them into the log-sum-exp and the loss.
+ */
+
+/* Tiles per row of the cross-entropy partials for a vocabulary of V columns; the caller
+ * sizes `partials` as M * coda_ce_partials_per_row(V) * 2 floats.  -1 if V < 1.       */
+int64_t coda_ce_partials_per_row(int64_t V);
+
+/* LM-head GEMM with row scale + block log-sum-exp epilogue.  z = r[m] * sw * (h . W^T):
+ *   partials[m, t, 0] = max over the columns v of tile t (v in [256t, 256t+256) and
+ *                       v < V) of z[m, v]                                   (fp32)
+ *   partials[m, t, 1] = sum over the same columns of exp(z[m, v] - that max)  (fp32)
+ *   tgt_logit[m]      = z[m, targets[m]]  if 0 <= targets[m] < V (written by the tile
+ *                       that holds the column); left untouched otherwise.
+ *   h, W, w_dtype, w_scale, r as for coda_gemm_rowscale_swiglu with CODA_ACT_NONE,
+ *             W [V, K] (the LM-head weight with the final RMSNorm's gamma folded in)
+ *   targets   [M] int32, device
+ *   partials  [M, coda_ce_partials_per_row(V), 2] fp32, device, written
+ *   tgt_logit [M] fp32, device, written (see above)
+ * V in [1, 2^22]; granule of K as coda_gemm_rowscale_swiglu.  Outputs must not overlap
+ * each other or any input.                                                            */
+coda_status coda_gemm_rowscale_ce(int64_t M, int64_t V, int64_t K, const void* h, const void* W,
+                                  coda_dtype w_dtype, const float* w_scale, const float* r,
+                                  const int32_t* targets, float* partials, float* tgt_logit,
+                                  void* stream);
+
+/* The reduction of the partials:
+ *   lse[m]  = fl32( Mx + log( sum_t partials[m,t,1] * exp(partials[m,t,0] - Mx) ) ),
+ *             Mx = max_t partials[m,t,0]                           (fp64 inside)
+ *   loss[m] = fl32( lse - tgt_logit[m] )  if 0 <= targets[m] < V, else 0 (an ignored
+ *             row, e.g. targets[m] = -100)
+ *   partials, targets, tgt_logit as written / read by coda_gemm_rowscale_ce
+ *   lse, loss [M] fp32, device, written; must not overlap the inputs or each other.  */
+coda_status coda_ce_reduce(int64_t M, int64_t V, const float* partials, const int32_t* targets,
+                           const float* tgt_logit, float* lse, float* loss, void* stream);
+
 /* ------------------------------------------------------------------- utilities ---- */
 const char* coda_status_string(coda_status s);
 int coda_last_hip_error(void);      /* hipError_t of this thread's last CODA_ERR_HIP      */

@@ -161,3 +161,32 @@ def test_rope_validation():
     # rot_cols == 0: no table, positions or angles needed; M == 0 enqueues nothing
     assert f(0, 128, 64, P1, P2, 0, None, P3, None, None, None, 0, 0, P6 + 4096, None) == OK
     assert f(0, 128, 64, P1, P2, 0, None, P3, P4, P5, P6, 8, 64, P6 + 4096, None) == OK
+
+
+@no_gpu
+def test_cross_entropy_validation():
+    L = _lib.load()
+    assert L.coda_ce_partials_per_row(0) == -1
+    assert L.coda_ce_partials_per_row(256) == 1 and L.coda_ce_partials_per_row(257) == 2
+    assert L.coda_ce_partials_per_row(128256) == 501
+    f = L.coda_gemm_rowscale_ce
+    # M, V, K, h, W, wdt, sw, r, targets, partials, tgt_logit, stream
+    Q = P6 + 0x1000000
+    assert f(16, 100, 64, P1, P2, 2, None, P3, P4, P5, Q, None) == DTYPE
+    assert f(16, 0, 64, P1, P2, 0, None, P3, P4, P5, Q, None) == SHAPE
+    assert f(16, 100, 60, P1, P2, 0, None, P3, P4, P5, Q, None) == SHAPE          # K % 8
+    assert f(16, (1 << 22) + 1, 64, P1, P2, 0, None, P3, P4, P5, Q, None) == SHAPE
+    assert f(16, 100, 64, P1, P2, 0, None, P3, None, P5, Q, None) == NULL
+    assert f(16, 100, 64, P1, P2, 1, None, P3, P4, P5, Q, None) == NULL          # e4m3 scale
+    assert f(16, 100, 64, P1, P2, 0, None, P3, P4, P5 + 4, Q, None) == ALIGN
+    assert f(16, 100, 64, P1, P2, 0, None, P3, P4, P5, P5 + 16, None) == ALIAS   # outputs overlap
+    assert f(16, 100, 64, P1, P2, 0, None, P3, P4, P4, Q, None) == ALIAS         # partials over targets
+    assert f(0, 100, 64, None, None, 0, None, None, None, None, None, None) == OK
+    g = L.coda_ce_reduce
+    # M, V, partials, targets, tgt_logit, lse, loss, stream
+    assert g(16, 0, P1, P2, P3, P4, P5, None) == SHAPE
+    assert g(16, 100, P1, P2, P3, None, P5, None) == NULL
+    assert g(16, 100, P1, P2, P3, P4 + 8, P5, None) == ALIGN
+    assert g(16, 100, P1, P2, P3, P4, P4, None) == ALIAS
+    assert g(16, 100, P1, P2, P3, P1, P5, None) == ALIAS                          # lse over partials
+    assert g(0, 100, None, None, None, None, None, None) == OK
