@@ -295,6 +295,84 @@ int orc_rope(int64_t R, int64_t ncols, double* y, const int32_t* pos, double bas
     return 0;
 }
 
+/* ------------------------------------------------ backward of the MLP input ---- */
+
+/*
+ * Input gradient of the block  y = SwiGLU( RMSNorm(hb) . W_or^T )  (kucoin page, section
+ * "CODA: El epilogo esconde un tesoro", last paragraph: the reparameterisation also holds
+ * for the backward pass, whose structure the forward's blockwise-local final stage
+ * passes on; section "Resultados del experimento": the backward of this chain).  For
+ * each listed row m, given the upstream gradient dy[m, 0..F) of y, the unfused chain
+ * rule in the forward's order, reversed:
+ *   forward:   r = 1/sqrt(mean(hb^2) + eps),  n = hb r gamma,  z = n . W_or^T,
+ *              g = z[0..F), u = z[F..2F),  y = silu(g) u
+ *   SwiGLU:    dg = dy u sigma(g) (1 + g (1 - sigma(g))),   du = dy silu(g)
+ *   GEMM:      dn[k] = sum_j dz[j] W_or[j, k]                 (dz = [dg, du])
+ *   RMSNorm:   dhb[k] = r gamma[k] dn[k] - (r^3 / d) hb[k] sum_k' gamma[k'] dn[k'] hb[k']
+ * W_or = Wp * wp_scale / gamma as in orc_chain (Wp the prepared, gamma-folded weight).
+ * hb, dy are bf16 codes; outputs fp64: dh [R, d], r [R], dz [R, 2F].
+ */
+int orc_mlpin_bwd(int64_t R, const int64_t* rows, int64_t d, int64_t F,
+                  const uint16_t* hb_in, const float* gamma, const void* Wp, int wp_dt, double wp_scale,
+                  const uint16_t* dy_in, double eps, double* dh_out, double* r_out, double* dz_out) {
+    int64_t F2 = 2 * F;
+    double* wor = (double*)malloc(sizeof(double) * (size_t)(F2 * d));
+    if (!wor) return 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < F2; ++n)
+        for (int64_t k = 0; k < d; ++k)
+            wor[n * d + k] = decode(Wp, wp_dt, n * d + k) * wp_scale / (double)gamma[k];
+    int fail = 0;
+#pragma omp parallel
+    {
+        double* hb = (double*)malloc(sizeof(double) * (size_t)d);
+        double* nrm = (double*)malloc(sizeof(double) * (size_t)d);
+        double* dn = (double*)malloc(sizeof(double) * (size_t)d);
+        double* dz = (double*)malloc(sizeof(double) * (size_t)F2);
+        if (!hb || !nrm || !dn || !dz) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < R; ++i) {
+                int64_t m = rows ? rows[i] : i;
+                double S = 0.0;
+                for (int64_t k = 0; k < d; ++k) {
+                    hb[k] = orc_bf16_decode(hb_in[m * d + k]);
+                    S += hb[k] * hb[k];
+                }
+                double r = 1.0 / sqrt(S / (double)d + eps);
+                r_out[i] = r;
+                for (int64_t k = 0; k < d; ++k) nrm[k] = hb[k] * r * (double)gamma[k];
+                for (int64_t j = 0; j < F; ++j) {
+                    double g = 0.0, u = 0.0;
+                    for (int64_t k = 0; k < d; ++k) {
+                        g += nrm[k] * wor[j * d + k];
+                        u += nrm[k] * wor[(F + j) * d + k];
+                    }
+                    double dyj = orc_bf16_decode(dy_in[m * F + j]);
+                    double sg = 1.0 / (1.0 + exp(-g));
+                    dz[j] = dyj * u * sg * (1.0 + g * (1.0 - sg));
+                    dz[F + j] = dyj * g * sg;
+                }
+                for (int64_t k = 0; k < d; ++k) {
+                    double t = 0.0;
+                    for (int64_t j = 0; j < F2; ++j) t += dz[j] * wor[j * d + k];
+                    dn[k] = t;
+                }
+                double c = 0.0;
+                for (int64_t k = 0; k < d; ++k) c += (double)gamma[k] * dn[k] * hb[k];
+                for (int64_t k = 0; k < d; ++k)
+                    dh_out[i * d + k] = r * (double)gamma[k] * dn[k] - r * r * r / (double)d * hb[k] * c;
+                for (int64_t j = 0; j < F2; ++j) dz_out[i * F2 + j] = dz[j];
+            }
+        }
+        free(hb); free(nrm); free(dn); free(dz);
+    }
+    free(wor);
+    return fail ? 2 : 0;
+}
+
 /* -------------------------------------------------------- cross-entropy ---- */
 
 /*

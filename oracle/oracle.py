@@ -24,7 +24,7 @@ ACT_NONE = 0
 ACT_SWIGLU = 1
 
 __all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
-           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "cross_entropy", "chain", "prepare", "BF16", "E4M3",
+           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "cross_entropy", "mlpin_bwd", "chain", "prepare", "BF16", "E4M3",
            "ACT_NONE", "ACT_SWIGLU"]
 
 
@@ -64,6 +64,8 @@ def lib():
         L.orc_fold_bf16.argtypes = [i64, i64, P, P, P]
         L.orc_quant_e4m3.restype = None
         L.orc_quant_e4m3.argtypes = [i64, i64, P, P, P, P, P]
+        L.orc_mlpin_bwd.restype = C.c_int
+        L.orc_mlpin_bwd.argtypes = [i64, P, i64, i64, P, P, P, C.c_int, C.c_double, P, C.c_double, P, P, P]
         L.orc_cross_entropy.restype = C.c_int
         L.orc_cross_entropy.argtypes = [i64, i64, P, P, P, P]
         L.orc_rope.restype = C.c_int
@@ -222,3 +224,29 @@ def cross_entropy(z: np.ndarray, targets):
     if lib().orc_cross_entropy(zz.shape[0], zz.shape[1], _p(zz), _p(t), _p(lse), _p(loss)) != 0:
         raise ValueError("empty vocabulary")
     return lse, loss
+
+
+def mlpin_bwd(hb, gamma, Wp, wp_dt: int, wp_scale: float, dy, eps: float, rows=None):
+    """Input gradient of y = SwiGLU(RMSNorm(hb) . W_or^T) for the listed rows (default
+    all): hb uint16 [M, d] bf16 codes, gamma fp32 [d], Wp [2F, d] prepared second weight
+    codes (bf16 or e4m3, with wp_scale), dy uint16 [M, F] bf16 codes of the upstream
+    gradient.  Returns dict(dh [R, d], r [R], dz [R, 2F]) in fp64."""
+    hb = np.ascontiguousarray(hb, dtype=np.uint16)
+    dy = np.ascontiguousarray(dy, dtype=np.uint16)
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    Wp = np.ascontiguousarray(Wp)
+    M, d = hb.shape
+    F2 = Wp.shape[0]
+    F = F2 // 2
+    if F2 % 2 or Wp.shape[1] != d or dy.shape != (M, F) or g.shape != (d,):
+        raise ValueError("shape mismatch")
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = M if rows is None else rows_a.size
+    dh = np.empty((R, d), np.float64)
+    r = np.empty(R, np.float64)
+    dz = np.empty((R, F2), np.float64)
+    rc = lib().orc_mlpin_bwd(R, _p(rows_a), d, F, _p(hb), _p(g), _p(Wp), wp_dt, float(wp_scale), _p(dy),
+                             float(eps), _p(dh), _p(r), _p(dz))
+    if rc != 0:
+        raise RuntimeError(f"oracle backward failed ({rc})")
+    return dict(dh=dh, r=r, dz=dz)

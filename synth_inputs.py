@@ -34,6 +34,7 @@ ACT_NONE = 0
 ACT_SWIGLU = 1
 ACT_ROPE = 2      # rotary position embedding on the QKV product (no activation)
 ACT_CE = 3        # cross-entropy of the LM-head product against per-row targets
+ACT_SWIGLU_BWD = 4  # input gradient of the RMSNorm -> GEMM -> SwiGLU block (no first GEMM)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,7 +61,10 @@ class Workload:
 
     @property
     def gemm_flops(self) -> int:
-        """2*M*K*N for each of the two GEMMs (epilogue arithmetic not counted)."""
+        """2*M*K*N for each of the two GEMMs (epilogue arithmetic not counted); for the
+        backward workload the recomputed forward product and the input-gradient product."""
+        if self.act == ACT_SWIGLU_BWD:
+            return 2 * (2 * self.M * self.d * self.N2w)
         return 2 * self.M * self.K1 * self.d + 2 * self.M * self.d * self.N2w
 
 
@@ -71,7 +75,10 @@ class Workload:
 # 6: workload 3 with RoPE on its Q and K columns (32 + 8 heads of 64 = 2560 of the 3072
 # columns; V passes), 16384 tokens = 4 sequences of 4096 (same draws as workload 3);
 # 7: the last block of LLaMA-3-1B -- MLP-out + residual, final RMSNorm, LM head over the
-# 128256-token vocabulary -- ending in the cross-entropy loss against uniform targets.
+# 128256-token vocabulary -- ending in the cross-entropy loss against uniform targets;
+# 8: the backward of workload 2's second half -- the input gradient of the RMSNorm ->
+# gate/up GEMM -> SwiGLU block -- with the block input h and the upstream gradient dy
+# drawn directly (no first GEMM).
 WORKLOADS = {
     1: Workload("tiny_m128_d256_n512_none", 128, 256, 256, 512, ACT_NONE, "bf16", 1e-5, 1001),
     2: Workload("llama1b_attnout_mlpin_m16384", 16384, 2048, 2048, 16384, ACT_SWIGLU, "bf16", 1e-5, 1002),
@@ -81,13 +88,14 @@ WORKLOADS = {
     6: Workload("llama1b_mlpout_qkv_rope_m16384", 16384, 8192, 2048, 3072, ACT_ROPE, "bf16", 1e-5, 1003,
                 rot_cols=2560, seq_len=4096),
     7: Workload("llama1b_mlpout_lmhead_ce_m16384", 16384, 8192, 2048, 128256, ACT_CE, "bf16", 1e-5, 1007),
+    8: Workload("llama1b_mlpin_bwd_m16384", 16384, 0, 2048, 16384, ACT_SWIGLU_BWD, "bf16", 1e-5, 1008),
 }
 
 
 def custom(M: int, K1: int, d: int, N2w: int, act: int, seed: int, dtype: str = "bf16",
            eps: float = 1e-5, rot_cols: int = 0, seq_len: int = 0) -> Workload:
     """A workload of arbitrary shape (ragged and edge-case tests)."""
-    if act == ACT_SWIGLU and N2w % 2:
+    if act in (ACT_SWIGLU, ACT_SWIGLU_BWD) and N2w % 2:
         raise ValueError("SwiGLU needs an even number of second-weight rows")
     if act == ACT_ROPE and (rot_cols % 64 or rot_cols > N2w or seq_len < 1):
         raise ValueError("RoPE needs whole 64-value heads within the columns and a sequence length")
@@ -126,6 +134,8 @@ def generate(w: Workload, rows: int | None = None) -> dict:
     """
     rng = np.random.default_rng(w.seed)
     f32 = np.float32
+    if w.act == ACT_SWIGLU_BWD:
+        return _generate_bwd(w, rng, rows)
     A = rng.standard_normal((w.M, w.K1), dtype=f32)
     Wo = rng.standard_normal((w.d, w.K1), dtype=f32) * f32(1.0 / np.sqrt(w.K1))
     x = rng.standard_normal((w.M, w.d), dtype=f32)
@@ -147,3 +157,21 @@ def generate(w: Workload, rows: int | None = None) -> dict:
     if tgt is not None:
         out["targets"] = tgt
     return out
+
+
+def _generate_bwd(w: Workload, rng, rows):
+    """Inputs of the backward workload, drawn in the order h, gamma, W, dy:
+      h      uint16 [M, d]      bf16 bits, N(0, 1): the block's input (residual stream)
+      gamma  float32 [d]        1 + 0.1 N(0, 1)
+      W_t    uint16 [2F, d]     bf16 bits, N(0, 1/d) (gate rows, then up rows)
+      dy     uint16 [M, F]      bf16 bits, N(0, 1): the upstream gradient of y
+    """
+    f32 = np.float32
+    F = w.N2w // 2
+    h = rng.standard_normal((w.M, w.d), dtype=f32)
+    gamma = (f32(1.0) + f32(0.1) * rng.standard_normal(w.d, dtype=f32)).astype(f32)
+    W = rng.standard_normal((w.N2w, w.d), dtype=f32) * f32(1.0 / np.sqrt(w.d))
+    dy = rng.standard_normal((w.M, F), dtype=f32)
+    if rows is not None:
+        h, dy = h[:rows], dy[:rows]
+    return {"h": to_bf16_bits(h), "gamma": gamma, "W_t": to_bf16_bits(W), "dy": to_bf16_bits(dy)}
