@@ -23,7 +23,8 @@ SWIGLU = CODA_ACT_SWIGLU
 __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3",
            "partials_per_row", "gemm_resid_partialrms", "rowscale_reduce",
            "gemm_rowscale_swiglu", "rope_table", "gemm_rowscale_rope", "ce_partials_per_row",
-           "gemm_rowscale_ce", "ce_reduce", "chain", "version"]
+           "gemm_rowscale_ce", "ce_reduce", "rowscale_from_h", "transpose_bf16", "gemm_swiglu_bwd", "rmsnorm_bwd_reduce",
+           "gemm_rmsnorm_bwd", "mlpin_bwd", "chain", "version"]
 
 
 def _stream(stream):
@@ -188,6 +189,65 @@ def ce_reduce(partials, targets, tgt_logit, V, lse=None, loss=None, stream=None)
     _lib.check("coda_ce_reduce", _lib.load().coda_ce_reduce(
         M, V, _ptr(partials), _ptr(targets), _ptr(tgt_logit), _ptr(lse), _ptr(loss), _stream(stream)))
     return lse, loss
+
+
+def rowscale_from_h(h, eps, r=None, stream=None):
+    """r [M] = 1/sqrt(mean(h^2) + eps) of a stored bf16 h [M, N]."""
+    M, N = h.shape
+    r = torch.empty(M, dtype=torch.float32, device=h.device) if r is None else r
+    _lib.check("coda_rowscale_from_h", _lib.load().coda_rowscale_from_h(M, N, _ptr(h), eps, _ptr(r), _stream(stream)))
+    return r
+
+
+def transpose_bf16(src, out=None, stream=None):
+    """out [C, R] = src [R, C]^T (bf16)."""
+    _esize(src, 2)
+    R, C = src.shape
+    out = torch.empty((C, R), dtype=src.dtype, device=src.device) if out is None else out
+    _lib.check("coda_transpose_bf16", _lib.load().coda_transpose_bf16(R, C, _ptr(src), _ptr(out), _stream(stream)))
+    return out
+
+
+def gemm_swiglu_bwd(h, W, r, dy, dz=None, partials=None, stream=None):
+    """Recompute h.W'^T and apply the SwiGLU backward: returns (dz [M, 2F] = r * dL/dz,
+    partials [M, T] of dL/dr).  W [2F, K] (gate rows, then up rows), dy [M, F]."""
+    M, K = h.shape
+    F2 = W.shape[0]
+    F = F2 // 2
+    T = int(_lib.load().coda_swiglu_bwd_partials_per_row(F))
+    dz = torch.empty((M, F2), dtype=torch.bfloat16, device=h.device) if dz is None else dz
+    partials = torch.empty((M, T), dtype=torch.float32, device=h.device) if partials is None else partials
+    _lib.check("coda_gemm_swiglu_bwd", _lib.load().coda_gemm_swiglu_bwd(
+        M, F, K, _ptr(h), _ptr(W), _ptr(r), _ptr(dy), _ptr(dz), _ptr(partials), _stream(stream)))
+    return dz, partials
+
+
+def rmsnorm_bwd_reduce(partials, r, N, F, q=None, stream=None):
+    """q [M] = -(r^3 / N) * sum_t partials."""
+    M = partials.shape[0]
+    q = torch.empty(M, dtype=torch.float32, device=partials.device) if q is None else q
+    _lib.check("coda_rmsnorm_bwd_reduce", _lib.load().coda_rmsnorm_bwd_reduce(
+        M, N, F, _ptr(partials), _ptr(r), _ptr(q), _stream(stream)))
+    return q
+
+
+def gemm_rmsnorm_bwd(dz, Wt, h, q, dh_res=None, dh=None, stream=None):
+    """dh [M, N] = dz . Wt^T + q * h (+ dh_res); Wt [N, K] = W'^T."""
+    M, K = dz.shape
+    N = Wt.shape[0]
+    dh = torch.empty((M, N), dtype=torch.bfloat16, device=dz.device) if dh is None else dh
+    _lib.check("coda_gemm_rmsnorm_bwd", _lib.load().coda_gemm_rmsnorm_bwd(
+        M, N, K, _ptr(dz), _ptr(Wt), _ptr(h), _ptr(q), _ptr(dh_res), _ptr(dh), _stream(stream)))
+    return dh
+
+
+def mlpin_bwd(h, Wp, Wpt, r, dy, dh_res=None, out=None, stream=None):
+    """The three backward calls in order: returns (dh, dz, partials, q)."""
+    out = out or {}
+    dz, P = gemm_swiglu_bwd(h, Wp, r, dy, out.get("dz"), out.get("partials"), stream)
+    q = rmsnorm_bwd_reduce(P, r, h.shape[1], Wp.shape[0] // 2, out.get("q"), stream)
+    dh = gemm_rmsnorm_bwd(dz, Wpt, h, q, dh_res, out.get("dh"), stream)
+    return dh, dz, P, q
 
 
 def chain(A, Wo_t, x_res, Wp_t, eps, act=SWIGLU, a_scale=None, wo_scale=None, wp_scale=None,

@@ -30,6 +30,12 @@ SIGNATURES = {
     "coda_ce_partials_per_row": (_I64, [_I64]),
     "coda_gemm_rowscale_ce": (_I, [_I64, _I64, _I64, _P, _P, _I, _P, _P, _P, _P, _P, _P]),
     "coda_ce_reduce": (_I, [_I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "coda_rowscale_from_h": (_I, [_I64, _I64, _P, _F, _P, _P]),
+    "coda_transpose_bf16": (_I, [_I64, _I64, _P, _P, _P]),
+    "coda_swiglu_bwd_partials_per_row": (_I64, [_I64]),
+    "coda_gemm_swiglu_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "coda_rmsnorm_bwd_reduce": (_I, [_I64, _I64, _I64, _P, _P, _P, _P]),
+    "coda_gemm_rmsnorm_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "coda_status_string": (C.c_char_p, [_I]),
     "coda_last_hip_error": (_I, []),
     "coda_version": (C.c_char_p, []),

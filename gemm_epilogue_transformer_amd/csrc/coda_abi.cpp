@@ -261,4 +261,82 @@ coda_status coda_ce_reduce(int64_t M, int64_t V, const float* partials, const in
                                              as_stream(stream)));
 }
 
+coda_status coda_rowscale_from_h(int64_t M, int64_t N, const void* h, float eps, float* r, void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(N, 1) || N % 8 != 0 || N > kMaxRow || !prod_ok(M, N)) return CODA_ERR_SHAPE;
+    if (!std::isfinite(eps) || eps < 0.0f) return CODA_ERR_VALUE;
+    if (M == 0) return CODA_OK;
+    if (!h || !r) return CODA_ERR_NULL;
+    if (!aligned16(h) || !aligned16(r)) return CODA_ERR_ALIGN;
+    if (overlap(span(r, M * 4), span(h, M * N * 2))) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_rowscale_from_h(int(M), int(N), h, eps, r, as_stream(stream)));
+}
+
+coda_status coda_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, void* stream) {
+    if (!dim_ok(R, 1) || !dim_ok(C, 1) || !prod_ok(R, C)) return CODA_ERR_SHAPE;
+    if (!src || !dst) return CODA_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return CODA_ERR_ALIGN;
+    if (overlap(span(src, R * C * 2), span(dst, R * C * 2))) return CODA_ERR_ALIAS;
+    if ((R + 63) / 64 * ((C + 63) / 64) > kMaxDim) return CODA_ERR_SHAPE;
+    return hip_status(coda::launch_transpose_bf16(R, C, src, dst, as_stream(stream)));
+}
+
+int64_t coda_swiglu_bwd_partials_per_row(int64_t F) {
+    return F < 1 || F > kMaxRow / 2 ? -1 : coda::swiglu_bwd_partials_per_row(F);
+}
+
+coda_status coda_gemm_swiglu_bwd(int64_t M, int64_t F, int64_t K, const void* h, const void* W,
+                                 const float* r, const void* dy, void* dz, float* partials,
+                                 void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(F, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (F % 8 != 0 || K % 8 != 0 || 2 * F > kMaxRow || K > kMaxRow) return CODA_ERR_SHAPE;
+    const int64_t T = coda::swiglu_bwd_partials_per_row(F);
+    if (!prod_ok(M, K) || !prod_ok(2 * F, K) || !prod_ok(M, 2 * F) || !prod_ok(M, T)) return CODA_ERR_SHAPE;
+    if (coda::gemm3_tiles(M, F, true) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!h || !W || !r || !dy || !dz || !partials) return CODA_ERR_NULL;
+    if (!aligned16(h) || !aligned16(W) || !aligned16(r) || !aligned16(dy) || !aligned16(dz) || !aligned16(partials))
+        return CODA_ERR_ALIGN;
+    const Range rz = span(dz, M * 2 * F * 2), rp = span(partials, M * T * 4);
+    const Range ins[] = {span(h, M * K * 2), span(W, 2 * F * K * 2), span(r, M * 4), span(dy, M * F * 2)};
+    if (overlap(rz, rp)) return CODA_ERR_ALIAS;
+    for (const Range& in : ins)
+        if (overlap(rz, in) || overlap(rp, in)) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_swiglu_bwd(int(M), int(F), int(K), h, W, r, dy, dz, partials,
+                                                   as_stream(stream)));
+}
+
+coda_status coda_rmsnorm_bwd_reduce(int64_t M, int64_t N, int64_t F, const float* partials,
+                                    const float* r, float* q, void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(N, 1) || !dim_ok(F, 1) || 2 * F > kMaxRow) return CODA_ERR_SHAPE;
+    const int64_t T = coda::swiglu_bwd_partials_per_row(F);
+    if (!prod_ok(M, T)) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!partials || !r || !q) return CODA_ERR_NULL;
+    if (!aligned16(partials) || !aligned16(r) || !aligned16(q)) return CODA_ERR_ALIGN;
+    const Range rq = span(q, M * 4);
+    if (overlap(rq, span(partials, M * T * 4)) || overlap(rq, span(r, M * 4))) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_rmsnorm_bwd_reduce(int(M), int(N), int(T), partials, r, q, as_stream(stream)));
+}
+
+coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* dz, const void* Wt,
+                                  const void* h, const float* q, const void* dh_res, void* dh,
+                                  void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(N, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (N % 8 != 0 || K % 8 != 0 || N > kMaxRow || K > kMaxRow) return CODA_ERR_SHAPE;
+    if (!prod_ok(M, K) || !prod_ok(N, K) || !prod_ok(M, N)) return CODA_ERR_SHAPE;
+    if (coda::gemm_bwd2_tiles(M, N) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!dz || !Wt || !h || !q || !dh) return CODA_ERR_NULL;
+    if (!aligned16(dz) || !aligned16(Wt) || !aligned16(h) || !aligned16(q) || !aligned16(dh) ||
+        (dh_res && !aligned16(dh_res)))
+        return CODA_ERR_ALIGN;
+    const Range ro = span(dh, M * N * 2);
+    if (overlap(ro, span(dz, M * K * 2)) || overlap(ro, span(Wt, N * K * 2)) || overlap(ro, span(h, M * N * 2)) ||
+        overlap(ro, span(q, M * 4)))
+        return CODA_ERR_ALIAS;
+    if (dh_res && dh_res != dh && overlap(ro, span(dh_res, M * N * 2))) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_rmsnorm_bwd(int(M), int(N), int(K), dz, Wt, h, q, dh_res, dh,
+                                                    as_stream(stream)));
+}
+
 }  // extern "C"

@@ -28,7 +28,7 @@
 
 namespace coda {
 
-enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3 };
+enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3, kActSwigluBwd = 4 };
 
 // RoPE operands (unused by the other activations).
 struct RopeArgs {
@@ -130,6 +130,112 @@ __device__ __forceinline__ void ce_epilogue(const f32x16_t (&acc)[TM][TN], const
             float* pp = ce.partials + (static_cast<size_t>(m) * ce.T + tile_n) * 2;
             pp[0] = mt;
             pp[1] = st;
+        }
+    }
+}
+
+// Backward operands (unused by the forward activations).
+struct BwdArgs {
+    const uint16_t* dy;       // [M, F] bf16: upstream gradient of y
+    uint16_t* dz;             // [M, 2F] bf16: r * dL/dz (gate columns, then up columns)
+    float* partials;          // [M, T]: sum over the tile's columns of dL/dz * acc
+    int T;                    // tiles per row = ceil(F / (BN/2))
+};
+
+// SwiGLU backward epilogue (kucoin page, section "CODA: El epilogo esconde un tesoro":
+// the reparameterisation holds for the backward pass).  The mainloop has recomputed the
+// forward product acc (gate and up blocks of the same (m, j) in one lane, as in the
+// forward); with g = r*acc_g, u = r*acc_u, s = sigmoid(g) and the upstream dy:
+//   dL/dg = dy u s (1 + g (1 - s)),   dL/du = dy g s
+//   dz = r * (dL/dg, dL/du)  (bf16: the gradient at the accumulator, the next GEMM's A)
+//   partial c = sum over the tile's columns of dL/dz * acc  (= dL/dr, fp32)
+// The accumulators are staged row-major in LDS; each lane takes 8 gate columns of one
+// row and the matching 8 up columns, loads dy as one 16-byte vector, stores two 16-byte
+// vectors of dz; c: butterfly over the 8 lanes of the row, then the waves sharing it.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
+__device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN],
+                                                    const float (&rv)[BM / WAVES_M / 64], const BwdArgs& bw,
+                                                    int M, int F, int m0, int j0, int tile_n, int wm, int wn,
+                                                    uint8_t* slab, float* red) {
+    constexpr int WM = BM / WAVES_M, NT = 64 * WAVES_M * WAVES_N;
+    constexpr int NB = TN / 2;                       // gate (= up) blocks per wave
+    constexpr int kGseg = NB * 4;                    // 8-column gate segments per row
+    constexpr int kSegPerLane = 32 * kGseg / 64;
+    static_assert(kGseg == 8, "8 lanes per row: the butterfly below");
+    using S = Slab<TN>;
+    const int lane = threadIdx.x & 63;
+    const int valid_rows = min(BM, M - m0);
+    const uint32_t dy_row = static_cast<uint32_t>(F) * 2, dz_row = static_cast<uint32_t>(F) * 4;
+    const __amdgpu_buffer_rsrc_t dy_rsrc =
+        make_buffer_rsrc(bw.dy + static_cast<size_t>(m0) * F, static_cast<uint32_t>(valid_rows) * dy_row);
+    const __amdgpu_buffer_rsrc_t dz_rsrc =
+        make_buffer_rsrc(bw.dz + static_cast<size_t>(m0) * 2 * F, static_cast<uint32_t>(valid_rows) * dz_row);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        float v[TN][16];
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[b][i] = acc[tm][b][i];
+        S::put(slab, v);
+#pragma unroll
+        for (int jj = 0; jj < kSegPerLane; ++jj) {
+            const int q = lane + 64 * jj;
+            const int row = q / kGseg, gcol = (q % kGseg) * 8;
+            const int rw = tm * 32 + row;                          // row within the wave
+            const int col = j0 + wn * NB * 32 + gcol;              // output column (gate j)
+            const float rr = __shfl(rv[tm / 2], (tm % 2) * 32 + row);
+            const uint8_t* sp = slab + row * S::kStride;
+            const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(sp + gcol * 4);
+            const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(sp + gcol * 4 + 16);
+            const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(sp + (NB * 32 + gcol) * 4);
+            const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(sp + (NB * 32 + gcol) * 4 + 16);
+            const float ag[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+            const float au[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+            const uint32_t in_range = col < F;
+            const uint32_t trow = static_cast<uint32_t>(wm * WM + rw);
+            const i32x4_t dyv = __builtin_amdgcn_raw_buffer_load_b128(
+                dy_rsrc, in_range ? trow * dy_row + static_cast<uint32_t>(col) * 2 : kOobOffset, 0, 0);
+            float c = 0.0f;
+            uint32_t og[4], ou[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = static_cast<uint32_t>(dyv[e]);
+                float dgo[2], duo[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k = 2 * e + hh;
+                    const float d = bf16_bits_to_f32(static_cast<uint16_t>(hh ? x >> 16 : x & 0xFFFFu));
+                    const float g = ag[k] * rr, u = au[k] * rr;
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                    const float dg = d * u * sg * (1.0f + g * (1.0f - sg));
+                    const float du = d * g * sg;
+                    c += dg * ag[k] + du * au[k];
+                    dgo[hh] = rr * dg;
+                    duo[hh] = rr * du;
+                }
+                og[e] = pack_bf16x2(dgo[0], dgo[1]);
+                ou[e] = pack_bf16x2(duo[0], duo[1]);
+            }
+            const uint32_t vg = in_range ? trow * dz_row + static_cast<uint32_t>(col) * 2 : kOobOffset;
+            const uint32_t vu = in_range ? trow * dz_row + static_cast<uint32_t>(F + col) * 2 : kOobOffset;
+            __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(og[0]), int(og[1]), int(og[2]), int(og[3])},
+                                                   dz_rsrc, vg, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(ou[0]), int(ou[1]), int(ou[2]), int(ou[3])},
+                                                   dz_rsrc, vu, 0, 0);
+#pragma unroll
+            for (int off = kGseg / 2; off >= 1; off >>= 1) c += __shfl_xor(c, off, kGseg);
+            if ((lane & (kGseg - 1)) == 0) red[wn * BM + wm * WM + rw] = c;
+        }
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < BM; r += NT) {
+        const int m = m0 + r;
+        if (m < M) {
+            float c = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WAVES_N; ++w) c += red[w * BM + r];
+            bw.partials[static_cast<size_t>(m) * bw.T + tile_n] = c;
         }
     }
 }
@@ -252,8 +358,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
                        uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
-                       int tiles_n, RopeArgs rope, CeArgs ce) {
-    constexpr bool SWIGLU = ACT == kActSwiglu;
+                       int tiles_n, RopeArgs rope, CeArgs ce, BwdArgs bw) {
+    // the backward recomputes the forward's gate / up product: same B panel layout
+    constexpr bool SWIGLU = ACT == kActSwiglu || ACT == kActSwigluBwd;
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -265,7 +372,7 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     static_assert(!W8 || (RB == 128 && PIPE == 0), "8-bit weights: DMA mainloop, 64-k tiles");
     __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
     // cross-entropy: (max, sum-exp) of every row for each of the WAVES_N column halves
-    __shared__ float ce_red[ACT == kActCe ? 2 * WAVES_N * BM : 1];
+    __shared__ float ce_red[ACT == kActCe ? 2 * WAVES_N * BM : (ACT == kActSwigluBwd ? WAVES_N * BM : 1)];
     uint8_t* st[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) st[i] = stages[i];
@@ -337,10 +444,13 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     }
 
     const float sw = w_scale ? *w_scale : 1.0f;
-    uint8_t* slab = slab_region<NS, NW, kStage, Slab<SWIGLU ? TN / 2 : TN>::kBytes>(st, wave);
+    uint8_t* slab = slab_region<NS, NW, kStage, Slab<(ACT == kActSwiglu) ? TN / 2 : TN>::kBytes>(st, wave);
     if constexpr (ACT == kActCe)
         ce_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, tv, sw, ce, M, N_out, m0, j0, tile_n, wm, wn, slab,
                                                       ce_red);
+    else if constexpr (ACT == kActSwigluBwd)
+        swiglu_bwd_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, bw, M, N_out, m0, j0, tile_n, wm, wn, slab,
+                                                              ce_red);
     else
         rowscale_epilogue<BM, BN, WAVES_M, TM, TN, ACT>(acc, rv, pv, rope, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
@@ -377,14 +487,14 @@ int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
 template <int ACT, bool WFP8>
 static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                           const float* w_scale, const float* r, void* y, const RopeArgs& rope,
-                          const CeArgs& ce, hipStream_t stream) {
-    constexpr int BNO = ACT == kActSwiglu ? BN3 / 2 : BN3;
+                          const CeArgs& ce, const BwdArgs& bw, hipStream_t stream) {
+    constexpr int BNO = (ACT == kActSwiglu || ACT == kActSwigluBwd) ? BN3 / 2 : BN3;
     const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BNO - 1) / BNO;
     const dim3 grid(tiles_m * tiles_n), block(64 * WM3 * WN3);
     hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, WFP8 ? 0 : PIPE3,
                                                OCC3, ACT, WFP8>),
                        grid, block, 0, stream, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W),
-                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n, rope, ce);
+                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n, rope, ce, bw);
     return hipGetLastError();
 }
 
@@ -393,11 +503,12 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
                                        const float* r, void* y, hipStream_t stream) {
     const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
     const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
+    const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
     if (swiglu)
-        return w_fp8 ? launch3<kActSwiglu, true>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, stream)
-                     : launch3<kActSwiglu, false>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, stream);
-    return w_fp8 ? launch3<kActNone, true>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, stream)
-                 : launch3<kActNone, false>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, stream);
+        return w_fp8 ? launch3<kActSwiglu, true>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, no_bw, stream)
+                     : launch3<kActSwiglu, false>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, no_bw, stream);
+    return w_fp8 ? launch3<kActNone, true>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, no_bw, stream)
+                 : launch3<kActNone, false>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, no_bw, stream);
 }
 
 hipError_t launch_gemm_rowscale_rope(int M, int N_out, int K, const void* h, const void* W,
@@ -406,8 +517,9 @@ hipError_t launch_gemm_rowscale_rope(int M, int N_out, int K, const void* h, con
                                      int table_rows, int rot_cols, void* y, hipStream_t stream) {
     const RopeArgs rope{pos, cos, sin, table_rows, rot_cols};
     const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
-    return w_fp8 ? launch3<kActRope, true>(M, N_out, K, h, W, w_scale, r, y, rope, no_ce, stream)
-                 : launch3<kActRope, false>(M, N_out, K, h, W, w_scale, r, y, rope, no_ce, stream);
+    const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
+    return w_fp8 ? launch3<kActRope, true>(M, N_out, K, h, W, w_scale, r, y, rope, no_ce, no_bw, stream)
+                 : launch3<kActRope, false>(M, N_out, K, h, W, w_scale, r, y, rope, no_ce, no_bw, stream);
 }
 
 int64_t ce_partials_per_row(int64_t V) { return V < 1 ? -1 : (V + BN3 - 1) / BN3; }
@@ -417,8 +529,20 @@ hipError_t launch_gemm_rowscale_ce(int M, int V, int K, const void* h, const voi
                                    float* partials, float* tgt_logit, hipStream_t stream) {
     const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
     const CeArgs ce{targets, partials, tgt_logit, static_cast<int>(ce_partials_per_row(V))};
-    return w_fp8 ? launch3<kActCe, true>(M, V, K, h, W, w_scale, r, nullptr, none, ce, stream)
-                 : launch3<kActCe, false>(M, V, K, h, W, w_scale, r, nullptr, none, ce, stream);
+    const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
+    return w_fp8 ? launch3<kActCe, true>(M, V, K, h, W, w_scale, r, nullptr, none, ce, no_bw, stream)
+                 : launch3<kActCe, false>(M, V, K, h, W, w_scale, r, nullptr, none, ce, no_bw, stream);
+}
+
+int64_t swiglu_bwd_partials_per_row(int64_t F) { return F < 1 ? -1 : (F + BN3 / 2 - 1) / (BN3 / 2); }
+
+hipError_t launch_gemm_swiglu_bwd(int M, int F, int K, const void* h, const void* W, const float* r,
+                                  const void* dy, void* dz, float* partials, hipStream_t stream) {
+    const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
+    const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
+    const BwdArgs bw{static_cast<const uint16_t*>(dy), static_cast<uint16_t*>(dz), partials,
+                     static_cast<int>(swiglu_bwd_partials_per_row(F))};
+    return launch3<kActSwigluBwd, false>(M, F, K, h, W, nullptr, r, nullptr, none, no_ce, bw, stream);
 }
 
 }  // namespace coda

@@ -127,6 +127,35 @@ hipError_t launch_rope_table(int rows, double base, float* cos_t, float* sin_t, 
     return hipGetLastError();
 }
 
+// dst[c, r] = src[r, c] for a bf16 [R, C] matrix, through a 64x64 LDS tile (padded
+// rows against bank conflicts); 256 threads, each moves 16 elements.
+__global__ void __launch_bounds__(256)
+k_transpose_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t R, int64_t C,
+                 int64_t tiles_c) {
+    __shared__ uint16_t t[64][66];
+    const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
+    const int64_t r0 = tr * 64, c0 = tc * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
+        t[ty + 4 * i][tx] = (r < R && c < C) ? src[r * C + c] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t c = c0 + ty + 4 * i, r = r0 + tx;
+        if (c < C && r < R) dst[c * R + r] = t[tx][ty + 4 * i];
+    }
+}
+
+hipError_t launch_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, hipStream_t stream) {
+    const int64_t tiles_r = (R + 63) / 64, tiles_c = (C + 63) / 64;
+    hipLaunchKernelGGL(k_transpose_bf16, dim3(static_cast<unsigned>(tiles_r * tiles_c)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C, tiles_c);
+    return hipGetLastError();
+}
+
 hipError_t launch_fold_bf16(int64_t N, int64_t K, const void* W, const float* gamma, void* Wp,
                             hipStream_t stream) {
     const int64_t k_vec = K / 8, n_vec = N * k_vec;

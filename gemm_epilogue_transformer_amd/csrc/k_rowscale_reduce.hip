@@ -29,4 +29,60 @@ hipError_t launch_rowscale_reduce(int M, int N, int T, const float* P, float eps
     return hipGetLastError();
 }
 
+// The row scale of a stored h (the backward may recompute it instead of saving it):
+//   r[m] = fl32( 1 / sqrt( sum_n h[m,n]^2 / N + eps ) )
+// one wave per row, 16-byte loads, the squares (exact in fp32 for bf16 h) summed in fp64
+// in a fixed order (lane-strided, then a fixed butterfly).
+__global__ void __launch_bounds__(256)
+k_rowscale_from_h(const uint16_t* __restrict__ h, float* __restrict__ r, int M, int N, double eps) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M) return;                       // wave-uniform
+    const i32x4_t* p = reinterpret_cast<const i32x4_t*>(h + static_cast<size_t>(row) * N);
+    double s = 0.0;
+    for (int v = lane; v < N / 8; v += 64) {
+        const i32x4_t q = p[v];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t x = static_cast<uint32_t>(q[e]);
+            const float a = bf16_bits_to_f32(static_cast<uint16_t>(x & 0xFFFFu));
+            const float b = bf16_bits_to_f32(static_cast<uint16_t>(x >> 16));
+            s += static_cast<double>(a * a) + static_cast<double>(b * b);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) r[row] = static_cast<float>(1.0 / sqrt(s / static_cast<double>(N) + eps));
+}
+
+hipError_t launch_rowscale_from_h(int M, int N, const void* h, float eps, float* r, hipStream_t stream) {
+    const dim3 block(256), grid((M + 3) / 4);
+    hipLaunchKernelGGL(k_rowscale_from_h, grid, block, 0, stream, static_cast<const uint16_t*>(h), r, M, N,
+                       static_cast<double>(eps));
+    return hipGetLastError();
+}
+
+// Backward of the row scale: q[m] = fl32( -(r[m]^3 / N) * sum_t P[m,t] ), the partials
+// being sum_j dL/dz_j * acc_j = dL/dr over the tiles of the recomputed product (fixed
+// order, fp64).  With it the input gradient is dh = r * (dz . W') + q * h: the second
+// term is the RMSNorm backward through r = (mean(h^2) + eps)^(-1/2), dr/dh = -r^3 h / N.
+__global__ void __launch_bounds__(256)
+k_rmsnorm_bwd_reduce(const float* __restrict__ P, const float* __restrict__ r, float* __restrict__ q, int M,
+                     int T, double n) {
+    const int m = blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= M) return;
+    const float* p = P + static_cast<size_t>(m) * T;
+    double s = 0.0;
+    for (int t = 0; t < T; ++t) s += static_cast<double>(p[t]);
+    const double rr = static_cast<double>(r[m]);
+    q[m] = static_cast<float>(-(rr * rr * rr / n) * s);
+}
+
+hipError_t launch_rmsnorm_bwd_reduce(int M, int N, int T, const float* P, const float* r, float* q,
+                                     hipStream_t stream) {
+    const dim3 block(256), grid((M + 255) / 256);
+    hipLaunchKernelGGL(k_rmsnorm_bwd_reduce, grid, block, 0, stream, P, r, q, M, T, static_cast<double>(N));
+    return hipGetLastError();
+}
+
 }  // namespace coda

@@ -44,6 +44,20 @@ hipError_t launch_gemm_rowscale_ce(int M, int V, int K, const void* h, const voi
 hipError_t launch_ce_reduce(int M, int V, int T, const float* partials, const int32_t* targets,
                             const float* tgt_logit, float* lse, float* loss, hipStream_t stream);
 
+// Backward of the MLP-input block (input gradient): recompute + SwiGLU-backward epilogue,
+// the row coefficient reduction, the input-gradient GEMM with the RMSNorm-backward
+// epilogue, and the weight transpose it reads.
+int64_t swiglu_bwd_partials_per_row(int64_t F);
+hipError_t launch_gemm_swiglu_bwd(int M, int F, int K, const void* h, const void* W, const float* r,
+                                  const void* dy, void* dz, float* partials, hipStream_t stream);
+hipError_t launch_rowscale_from_h(int M, int N, const void* h, float eps, float* r, hipStream_t stream);
+hipError_t launch_rmsnorm_bwd_reduce(int M, int N, int T, const float* partials, const float* r, float* q,
+                                     hipStream_t stream);
+int64_t gemm_bwd2_tiles(int64_t M, int64_t N);
+hipError_t launch_gemm_rmsnorm_bwd(int M, int N, int K, const void* dz, const void* Wt, const void* h,
+                                   const float* q, const void* dh_res, void* dh, hipStream_t stream);
+hipError_t launch_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, hipStream_t stream);
+
 hipError_t launch_fold_bf16(int64_t N, int64_t K, const void* W, const float* gamma, void* Wp,
                             hipStream_t stream);
 

@@ -224,6 +224,59 @@ coda_status coda_gemm_rowscale_ce(int64_t M, int64_t V, int64_t K, const void* h
 coda_status coda_ce_reduce(int64_t M, int64_t V, const float* partials, const int32_t* targets,
                            const float* tgt_logit, float* lse, float* loss, void* stream);
 
+/* ------------------------------------------------ backward of the MLP input block ----
+ * Input gradient of  y = SwiGLU( RMSNorm(h) . W^T )  (kucoin page, section "CODA: El
+ * epilogo esconde un tesoro", last paragraph: the reparameterisation holds for the
+ * backward pass).  With acc = h . W'^T (W' = gamma-folded), r the forward's row scale,
+ * z = r * acc, g = z[:, :F], u = z[:, F:], s = sigmoid(g) and the upstream gradient dy:
+ *   dL/dg = dy u s (1 + g (1 - s)),   dL/du = dy g s,   c[m] = sum_j dL/dz[m,j] acc[m,j]
+ *   dh = r * ((dL/dz) . W') - (r^3 / N) * c * h   (+ the residual stream's gradient)
+ * Three calls: the recomputed forward product with the SwiGLU backward in its epilogue
+ * (writes r * dL/dz and per-tile partials of c), the reduction of c into the row
+ * coefficient q = -(r^3/N) c, and the input-gradient GEMM whose epilogue adds q * h.
+ * The second GEMM reduces over 2F, so it reads W' transposed (coda_transpose_bf16,
+ * once per weight update).  bf16 weights only.
+ */
+
+/* The row scale of a stored h, for a backward that recomputes it instead of saving it:
+ *   r[m] = fl32( 1 / sqrt( sum_n h[m,n]^2 / N + eps ) )     (fp64 inside)
+ *   h [M, N] bf16, device;  r [M] fp32, device, written, must not overlap h.
+ * Granule: N % 8 == 0.  eps finite and >= 0.                                         */
+coda_status coda_rowscale_from_h(int64_t M, int64_t N, const void* h, float eps, float* r,
+                                 void* stream);
+
+/* dst[c, r] = src[r, c] for bf16 [R, C] matrices; R, C in [1, 2^31); no overlap.      */
+coda_status coda_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, void* stream);
+
+/* Partials per row written by coda_gemm_swiglu_bwd for F gate columns; -1 if F < 1.    */
+int64_t coda_swiglu_bwd_partials_per_row(int64_t F);
+
+/* Recomputed gate/up product with the SwiGLU-backward epilogue:
+ *   h   [M, K] bf16 (the block input the forward read);  W [2F, K] bf16 (W', gate rows
+ *       then up rows);  r [M] fp32 (the forward's row scale);  dy [M, F] bf16
+ *   dz  [M, 2F] bf16, written: bf16_rne( r[m] * dL/dz[m, j] )  (gate columns, then up)
+ *   partials [M, coda_swiglu_bwd_partials_per_row(F)] fp32, written: per tile of 128 gate
+ *       (and the matching 128 up) columns, sum of dL/dz * acc   (fp32)
+ * Granules: K % 8 == 0, F % 8 == 0; F <= 2^21.  Outputs must not overlap the inputs.  */
+coda_status coda_gemm_swiglu_bwd(int64_t M, int64_t F, int64_t K, const void* h, const void* W,
+                                 const float* r, const void* dy, void* dz, float* partials,
+                                 void* stream);
+
+/* q[m] = fl32( -(r[m]^3 / N) * sum_t partials[m, t] )   (fp64 inside; N = hidden size,
+ * F = the gate width the partials were written for).  q must not overlap the inputs.  */
+coda_status coda_rmsnorm_bwd_reduce(int64_t M, int64_t N, int64_t F, const float* partials,
+                                    const float* r, float* q, void* stream);
+
+/* Input-gradient GEMM with the RMSNorm-backward epilogue:
+ *   dh[m,n] = bf16_rne( sum_k dz[m,k] Wt[n,k] + q[m] h[m,n] + dh_res[m,n] )
+ *   dz [M, K] bf16 (K = 2F);  Wt [N, K] bf16 = W'^T;  h [M, N] bf16;  q [M] fp32
+ *   dh_res [M, N] bf16 or NULL (= 0); may be EXACTLY equal to dh (in place)
+ *   dh [M, N] bf16, written; must not overlap any other input
+ * Granules: N % 8 == 0, K % 8 == 0.                                                   */
+coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* dz, const void* Wt,
+                                  const void* h, const float* q, const void* dh_res, void* dh,
+                                  void* stream);
+
 /* ------------------------------------------------------------------- utilities ---- */
 const char* coda_status_string(coda_status s);
 int coda_last_hip_error(void);      /* hipError_t of this thread's last CODA_ERR_HIP      */

@@ -190,3 +190,37 @@ def test_cross_entropy_validation():
     assert g(16, 100, P1, P2, P3, P4, P4, None) == ALIAS
     assert g(16, 100, P1, P2, P3, P1, P5, None) == ALIAS                          # lse over partials
     assert g(0, 100, None, None, None, None, None, None) == OK
+
+
+@no_gpu
+def test_backward_validation():
+    L = _lib.load()
+    assert L.coda_swiglu_bwd_partials_per_row(0) == -1
+    assert L.coda_swiglu_bwd_partials_per_row(8192) == 64 and L.coda_swiglu_bwd_partials_per_row(129) == 2
+    rs = L.coda_rowscale_from_h
+    assert rs(16, 60, P1, 1e-5, P2, None) == SHAPE
+    assert rs(16, 64, P1, -1.0, P2, None) == VALUE
+    assert rs(16, 64, None, 1e-5, P2, None) == NULL
+    assert rs(16, 64, P1, 1e-5, P1 + 64, None) == ALIAS
+    t = L.coda_transpose_bf16
+    assert t(0, 8, P1, P2, None) == SHAPE
+    assert t(8, 8, P1, P1 + 64, None) == ALIAS
+    assert t(8, 8, P1 + 2, P2, None) == ALIGN
+    f = L.coda_gemm_swiglu_bwd
+    # M, F, K, h, W, r, dy, dz, partials, stream
+    assert f(16, 60, 64, P1, P2, P3, P4, P5, P6, None) == SHAPE          # F % 8
+    assert f(16, 64, 60, P1, P2, P3, P4, P5, P6, None) == SHAPE          # K % 8
+    assert f(16, 64, 64, P1, P2, P3, None, P5, P6, None) == NULL
+    assert f(16, 64, 64, P1, P2, P3, P4, P5, P5 + 16, None) == ALIAS     # partials over dz
+    assert f(16, 64, 64, P1, P2, P3, P4, P4, P6, None) == ALIAS          # dz over dy
+    assert f(0, 64, 64, None, None, None, None, None, None, None) == OK
+    g = L.coda_rmsnorm_bwd_reduce
+    assert g(16, 0, 64, P1, P2, P3, None) == SHAPE
+    assert g(16, 64, 64, P1, P2, P2, None) == ALIAS
+    b = L.coda_gemm_rmsnorm_bwd
+    # M, N, K, dz, Wt, h, q, dh_res, dh, stream
+    assert b(16, 60, 64, P1, P2, P3, P4, None, P5, None) == SHAPE
+    assert b(16, 64, 64, P1, P2, P3, P4, None, P3, None) == ALIAS        # dh over h
+    assert b(16, 64, 64, P1, P2, P3, P4, P5 + 16, P5, None) == ALIAS     # partial overlap with dh_res
+    assert b(16, 64, 64, P1, P2, P3, None, None, P5, None) == NULL
+    assert b(0, 64, 64, None, None, None, None, None, None, None) == OK
