@@ -149,6 +149,129 @@ def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
     print("\n".join(lines))
 
 
+def bench_backward(w, args) -> dict:
+    """Input gradient of the MLP-input block (three calls), the saved forward state --
+    folded weight, its transpose, the row scale -- prepared outside the timed region."""
+    import numpy as np
+    import torch
+
+    import gemm_epilogue_transformer_amd as coda
+    import synth_inputs as si
+
+    inp = si.generate(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+    h, W, dy = dev(inp["h"]), dev(inp["W_t"]), dev(inp["dy"])
+    gamma = torch.from_numpy(inp["gamma"]).cuda()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    Wp = coda.prepare_weight_bf16(W, gamma)
+    Wpt = coda.transpose_bf16(Wp)
+    r = coda.rowscale_from_h(h, w.eps)
+    torch.cuda.synchronize()
+    prep_ms = (time.perf_counter() - t0) * 1e3
+    M, d, F = w.M, w.d, w.N2w // 2
+    out = {"dz": torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda"),
+           "partials": torch.empty((M, -(-F // 128)), dtype=torch.float32, device="cuda"),
+           "q": torch.empty(M, dtype=torch.float32, device="cuda"),
+           "dh": torch.empty((M, d), dtype=torch.bfloat16, device="cuda")}
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dz, P = coda.gemm_swiglu_bwd(h, Wp, r, dy, out["dz"], out["partials"])
+        if ev is not None:
+            ev[1].record(stream)
+        q = coda.rmsnorm_bwd_reduce(P, r, d, F, out["q"])
+        if ev is not None:
+            ev[2].record(stream)
+        coda.gemm_rmsnorm_bwd(dz, Wpt, h, q, None, out["dh"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    k_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
+    flops = w.gemm_flops
+    g_flops = 2 * M * d * 2 * F
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    dom = 0 if k_ms[0] >= k_ms[2] else 2
+    names = ["gemm_swiglu_bwd", "rmsnorm_bwd_reduce", "gemm_rmsnorm_bwd"]
+    kern = ["k_gemm_rowscale_swiglu", "k_rmsnorm_bwd_reduce", "k_gemm_rmsnorm_bwd"]
+    T = -(-F // 128)
+    byt = {"gemm_swiglu_bwd": M * d * 2 + 2 * F * d * 2 + M * 4 + M * F * 2 + M * 2 * F * 2 + M * T * 4,
+           "rmsnorm_bwd_reduce": M * T * 4 + 2 * M * 4,
+           "gemm_rmsnorm_bwd": M * 2 * F * 2 + d * 2 * F * 2 + M * d * 2 + M * 4 + M * d * 2}
+    achieved = g_flops / (k_ms[dom] * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "d": d, "F": F, "direction": "backward (input gradient)",
+                   "eps": w.eps, "seed": w.seed},
+        "note": "FLOPs of the two executed GEMMs: the recomputed gate/up product and the input-gradient product",
+        "kernels_ms": {n: round(t, 4) for n, t in zip(names, k_ms)},
+        "hbm_bytes_algorithmic": {"fused": sum(byt.values())},
+        "prep_ms": round(prep_ms, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": load_traffic(w.name, kern[dom]), "kernel": kern[dom],
+                     "kernel_ms": round(k_ms[dom], 4), "algorithmic_bytes": byt[names[dom]]},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if args.unfused:
+        # torch autograd of the unfused forward (bf16 GEMMs, element-wise RMSNorm / SwiGLU);
+        # the forward runs once outside the timed region and its saved activations are
+        # reused: this baseline does NOT recompute the gate/up product
+        hh = h.clone().requires_grad_(True)
+        hf = hh.float()
+        n = (hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + w.eps)).to(torch.bfloat16) * \
+            gamma.to(torch.bfloat16)
+        z = n @ W.t()
+        y = torch.nn.functional.silu(z[:, :F]) * z[:, F:]
+        for _ in range(3):
+            torch.autograd.grad(y, hh, dy, retain_graph=True)
+        torch.cuda.synchronize()
+        s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s2.record(stream)
+        for _ in range(args.steps):
+            torch.autograd.grad(y, hh, dy, retain_graph=True)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        ums = s2.elapsed_time(e2) / args.steps
+        rec["unfused_torch"] = {"ms_per_step": round(ums, 4), "speedup_of_fused": round(ums / ms_per_step, 3),
+                                "note": "autograd input gradient from saved activations (one GEMM)"}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        Wp_ref = oracle.fold_bf16(inp["W_t"], inp["gamma"])
+        rng = np.random.default_rng(0)
+        n_rows, dt = 8, 0.0
+        while True:
+            rows = np.sort(rng.choice(M, size=min(n_rows, M), replace=False))
+            t1 = time.perf_counter()
+            oracle.mlpin_bwd(inp["h"], inp["gamma"], Wp_ref, oracle.BF16, 1.0, inp["dy"], w.eps, rows=rows)
+            dt = time.perf_counter() - t1
+            if dt >= args.cpu_seconds / 2 or n_rows >= M:
+                break
+            n_rows *= 2
+        rec["cpu_baseline"] = {"value": round(rows.size * flops / M / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"{rows.size} random rows of the {M}-row workload (fp64 backward, "
+                                         f"recomputed forward included), {dt:.1f} s"}
+    return rec
+
+
 def _oracle_path(oracle, prep, inp, w, rows):
     """The oracle's whole path for the rows: the chain, then RoPE or the loss."""
     import synth_inputs as si
@@ -239,6 +362,9 @@ def main():
     import synth_inputs as si
 
     w = si.WORKLOADS[args.workload]
+    if w.act == si.ACT_SWIGLU_BWD:
+        print(json.dumps(bench_backward(w, args)), flush=True)
+        return
     inp = si.generate(w)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
     A, Wo, xr, W = dev(inp["A"]), dev(inp["Wo_t"]), dev(inp["x_res"]), dev(inp["W_t"])
