@@ -373,6 +373,63 @@ int orc_mlpin_bwd(int64_t R, const int64_t* rows, int64_t d, int64_t F,
     return fail ? 2 : 0;
 }
 
+/*
+ * Weight gradients of the same block, sampled: for the listed gate/up rows j of the
+ * second weight (j in [0, 2F)) and columns k, summed over ALL M tokens,
+ *   dW[j, k]   = sum_m dz[m, j] * n[m, k]       (n = hb r gamma, the RMSNorm output;
+ *                                                 the gradient of the raw weight W)
+ * and, when every j in [0, 2F) is listed (small problems), the RMSNorm weight gradient
+ *   dgamma[k]  = sum_m sum_j dz[m, j] * W[j, k] * hb[m, k] * r[m].
+ * dz[m, j] needs only the gate and up products of (m, j mod F), so a sampled column of
+ * dW costs M * 2d operations.  Inputs as orc_mlpin_bwd plus the raw weight W (bf16).
+ */
+int orc_mlpin_wgrad(int64_t M, int64_t d, int64_t F, const uint16_t* hb_in, const float* gamma,
+                    const void* Wp, int wp_dt, double wp_scale, const uint16_t* W_raw,
+                    const uint16_t* dy_in, double eps, int64_t nj, const int64_t* js,
+                    int64_t nk, const int64_t* ks, double* dW_out, double* dgamma_out) {
+    int64_t F2 = 2 * F;
+    double* r = (double*)malloc(sizeof(double) * (size_t)M);
+    double* dzc = (double*)malloc(sizeof(double) * (size_t)M);
+    if (!r || !dzc) { free(r); free(dzc); return 2; }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double S = 0.0;
+        for (int64_t k = 0; k < d; ++k) { double v = orc_bf16_decode(hb_in[m * d + k]); S += v * v; }
+        r[m] = 1.0 / sqrt(S / (double)d + eps);
+    }
+    if (dgamma_out) for (int64_t k = 0; k < nk; ++k) dgamma_out[k] = 0.0;
+    for (int64_t a = 0; a < nj; ++a) {
+        int64_t j = js[a], jg = j < F ? j : j - F;       /* the gate / up pair of column j */
+        /* dz[:, j] over all tokens */
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            double g = 0.0, u = 0.0;
+            for (int64_t k = 0; k < d; ++k) {
+                double nk_ = orc_bf16_decode(hb_in[m * d + k]) * r[m] * (double)gamma[k];
+                g += nk_ * decode(Wp, wp_dt, jg * d + k) * wp_scale / (double)gamma[k];
+                u += nk_ * decode(Wp, wp_dt, (F + jg) * d + k) * wp_scale / (double)gamma[k];
+            }
+            double dyv = orc_bf16_decode(dy_in[m * F + jg]);
+            double sg = 1.0 / (1.0 + exp(-g));
+            dzc[m] = j < F ? dyv * u * sg * (1.0 + g * (1.0 - sg)) : dyv * g * sg;
+        }
+        for (int64_t b = 0; b < nk; ++b) {
+            int64_t k = ks[b];
+            double acc = 0.0, accg = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double hv = orc_bf16_decode(hb_in[m * d + k]);
+                acc += dzc[m] * hv * r[m] * (double)gamma[k];
+                accg += dzc[m] * hv * r[m];
+            }
+            dW_out[a * nk + b] = acc;
+            if (dgamma_out) dgamma_out[b] += accg * orc_bf16_decode(W_raw[j * d + k]);
+        }
+    }
+    (void)F2;
+    free(r); free(dzc);
+    return 0;
+}
+
 /* -------------------------------------------------------- cross-entropy ---- */
 
 /*

@@ -24,7 +24,7 @@ ACT_NONE = 0
 ACT_SWIGLU = 1
 
 __all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
-           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "cross_entropy", "mlpin_bwd", "chain", "prepare", "BF16", "E4M3",
+           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "cross_entropy", "mlpin_bwd", "mlpin_wgrad", "chain", "prepare", "BF16", "E4M3",
            "ACT_NONE", "ACT_SWIGLU"]
 
 
@@ -66,6 +66,9 @@ def lib():
         L.orc_quant_e4m3.argtypes = [i64, i64, P, P, P, P, P]
         L.orc_mlpin_bwd.restype = C.c_int
         L.orc_mlpin_bwd.argtypes = [i64, P, i64, i64, P, P, P, C.c_int, C.c_double, P, C.c_double, P, P, P]
+        L.orc_mlpin_wgrad.restype = C.c_int
+        L.orc_mlpin_wgrad.argtypes = [i64, i64, i64, P, P, P, C.c_int, C.c_double, P, P, C.c_double,
+                                      i64, P, i64, P, P, P]
         L.orc_cross_entropy.restype = C.c_int
         L.orc_cross_entropy.argtypes = [i64, i64, P, P, P, P]
         L.orc_rope.restype = C.c_int
@@ -250,3 +253,30 @@ def mlpin_bwd(hb, gamma, Wp, wp_dt: int, wp_scale: float, dy, eps: float, rows=N
     if rc != 0:
         raise RuntimeError(f"oracle backward failed ({rc})")
     return dict(dh=dh, r=r, dz=dz)
+
+
+def mlpin_wgrad(hb, gamma, Wp, wp_dt: int, wp_scale: float, W_raw, dy, eps: float, js=None, ks=None):
+    """Weight gradients of y = SwiGLU(RMSNorm(hb) . W^T) summed over all tokens: dW [nj, nk]
+    at the listed rows js of W (default all 2F) and columns ks (default all d); dgamma
+    [nk] only when js covers every row (else None).  Inputs as :func:`mlpin_bwd` plus
+    the raw weight W_raw [2F, d] (bf16 codes)."""
+    hb = np.ascontiguousarray(hb, dtype=np.uint16)
+    dy = np.ascontiguousarray(dy, dtype=np.uint16)
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    Wp = np.ascontiguousarray(Wp)
+    Wr = np.ascontiguousarray(W_raw, dtype=np.uint16)
+    M, d = hb.shape
+    F2 = Wp.shape[0]
+    F = F2 // 2
+    if F2 % 2 or Wp.shape[1] != d or Wr.shape != Wp.shape or dy.shape != (M, F):
+        raise ValueError("shape mismatch")
+    j = np.arange(F2, dtype=np.int64) if js is None else np.ascontiguousarray(js, dtype=np.int64)
+    k = np.arange(d, dtype=np.int64) if ks is None else np.ascontiguousarray(ks, dtype=np.int64)
+    full = js is None
+    dW = np.empty((j.size, k.size), np.float64)
+    dgam = np.empty(k.size, np.float64) if full else None
+    rc = lib().orc_mlpin_wgrad(M, d, F, _p(hb), _p(g), _p(Wp), wp_dt, float(wp_scale), _p(Wr), _p(dy), float(eps),
+                               j.size, _p(j), k.size, _p(k), _p(dW), _p(dgam))
+    if rc != 0:
+        raise RuntimeError(f"oracle weight gradient failed ({rc})")
+    return dW, dgam

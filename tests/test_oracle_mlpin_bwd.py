@@ -90,3 +90,40 @@ def test_row_subset_equals_full():
     rows = np.array([8, 0, 4])
     part = oracle.mlpin_bwd(hb, g, Wp, oracle.BF16, 1.0, dy, eps, rows=rows)
     assert np.array_equal(part["dh"], full["dh"][rows])
+
+
+def _pow2_case(M, d, F, seed, eps=1e-5):
+    # gamma = powers of two makes the fold exact, so the raw weight and the unfused weight
+    # W' / gamma coincide and the gamma gradient has one unambiguous reference
+    rng = np.random.default_rng(seed)
+    hb = si.to_bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
+    dy = si.to_bf16_bits(rng.standard_normal((M, F)).astype(np.float32))
+    W = si.to_bf16_bits((rng.standard_normal((2 * F, d)) / np.sqrt(d)).astype(np.float32))
+    g = np.exp2(rng.integers(-2, 3, d)).astype(np.float32)
+    Wp = oracle.fold_bf16(W, g)
+    assert np.array_equal(oracle.bf16_decode(Wp) / g.astype(np.float64), oracle.bf16_decode(W))
+    return hb, dy, g, Wp, W, eps
+
+
+def test_weight_gradients_match_torch_autograd():
+    hb, dy, g, Wp, W, eps = _pow2_case(6, 32, 16, 11)
+    dW, dgam = oracle.mlpin_wgrad(hb, g, Wp, oracle.BF16, 1.0, W, dy, eps)
+    h = torch.from_numpy(oracle.bf16_decode(hb))
+    Wt = torch.from_numpy(oracle.bf16_decode(W)).requires_grad_(True)
+    gt = torch.from_numpy(g.astype(np.float64)).requires_grad_(True)
+    r = torch.rsqrt((h * h).mean(1, keepdim=True) + eps)
+    z = (h * r * gt) @ Wt.T
+    F = z.shape[1] // 2
+    y = torch.nn.functional.silu(z[:, :F]) * z[:, F:]
+    (y * torch.from_numpy(oracle.bf16_decode(dy))).sum().backward()
+    assert np.allclose(dW, Wt.grad.numpy(), rtol=1e-11, atol=1e-13)
+    assert np.allclose(dgam, gt.grad.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_weight_gradient_samples_equal_the_full_result():
+    hb, dy, g, Wp, W, eps = _pow2_case(9, 24, 8, 12)
+    dW, dgam = oracle.mlpin_wgrad(hb, g, Wp, oracle.BF16, 1.0, W, dy, eps)
+    js, ks = np.array([15, 0, 8, 3]), np.array([23, 1, 7])
+    part, none = oracle.mlpin_wgrad(hb, g, Wp, oracle.BF16, 1.0, W, dy, eps, js=js, ks=ks)
+    assert none is None
+    assert np.array_equal(part, dW[np.ix_(js, ks)])
