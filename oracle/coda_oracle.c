@@ -382,11 +382,17 @@ int orc_mlpin_bwd(int64_t R, const int64_t* rows, int64_t d, int64_t F,
  *   dgamma[k]  = sum_m sum_j dz[m, j] * W[j, k] * hb[m, k] * r[m].
  * dz[m, j] needs only the gate and up products of (m, j mod F), so a sampled column of
  * dW costs M * 2d operations.  Inputs as orc_mlpin_bwd plus the raw weight W (bf16).
+ *
+ * Optional (NULL to skip), for error bounds of an implementation that rounds the summed
+ * terms: the root-sum-square over the tokens of the terms of each sum,
+ *   rss[j, k]       = sqrt( sum_m (dz[m, j] r[m] hb[m, k])^2 )          (gamma left out)
+ *   rss_gamma[k]    = sqrt( sum_m sum_j (dz[m, j] W[j, k] r[m] hb[m, k])^2 )   (full j only)
  */
 int orc_mlpin_wgrad(int64_t M, int64_t d, int64_t F, const uint16_t* hb_in, const float* gamma,
                     const void* Wp, int wp_dt, double wp_scale, const uint16_t* W_raw,
                     const uint16_t* dy_in, double eps, int64_t nj, const int64_t* js,
-                    int64_t nk, const int64_t* ks, double* dW_out, double* dgamma_out) {
+                    int64_t nk, const int64_t* ks, double* dW_out, double* dgamma_out,
+                    double* rss_out, double* rss_gamma_out) {
     int64_t F2 = 2 * F;
     double* r = (double*)malloc(sizeof(double) * (size_t)M);
     double* dzc = (double*)malloc(sizeof(double) * (size_t)M);
@@ -398,6 +404,7 @@ int orc_mlpin_wgrad(int64_t M, int64_t d, int64_t F, const uint16_t* hb_in, cons
         r[m] = 1.0 / sqrt(S / (double)d + eps);
     }
     if (dgamma_out) for (int64_t k = 0; k < nk; ++k) dgamma_out[k] = 0.0;
+    if (rss_gamma_out) for (int64_t k = 0; k < nk; ++k) rss_gamma_out[k] = 0.0;
     for (int64_t a = 0; a < nj; ++a) {
         int64_t j = js[a], jg = j < F ? j : j - F;       /* the gate / up pair of column j */
         /* dz[:, j] over all tokens */
@@ -415,16 +422,21 @@ int orc_mlpin_wgrad(int64_t M, int64_t d, int64_t F, const uint16_t* hb_in, cons
         }
         for (int64_t b = 0; b < nk; ++b) {
             int64_t k = ks[b];
-            double acc = 0.0, accg = 0.0;
+            double acc = 0.0, accg = 0.0, sq = 0.0;
             for (int64_t m = 0; m < M; ++m) {
                 double hv = orc_bf16_decode(hb_in[m * d + k]);
                 acc += dzc[m] * hv * r[m] * (double)gamma[k];
                 accg += dzc[m] * hv * r[m];
+                sq += (dzc[m] * hv * r[m]) * (dzc[m] * hv * r[m]);
             }
             dW_out[a * nk + b] = acc;
-            if (dgamma_out) dgamma_out[b] += accg * orc_bf16_decode(W_raw[j * d + k]);
+            double wv = orc_bf16_decode(W_raw[j * d + k]);
+            if (dgamma_out) dgamma_out[b] += accg * wv;
+            if (rss_out) rss_out[a * nk + b] = sqrt(sq);
+            if (rss_gamma_out) rss_gamma_out[b] += sq * wv * wv;
         }
     }
+    if (rss_gamma_out) for (int64_t k = 0; k < nk; ++k) rss_gamma_out[k] = sqrt(rss_gamma_out[k]);
     (void)F2;
     free(r); free(dzc);
     return 0;

@@ -68,7 +68,7 @@ def lib():
         L.orc_mlpin_bwd.argtypes = [i64, P, i64, i64, P, P, P, C.c_int, C.c_double, P, C.c_double, P, P, P]
         L.orc_mlpin_wgrad.restype = C.c_int
         L.orc_mlpin_wgrad.argtypes = [i64, i64, i64, P, P, P, C.c_int, C.c_double, P, P, C.c_double,
-                                      i64, P, i64, P, P, P]
+                                      i64, P, i64, P, P, P, P, P]
         L.orc_cross_entropy.restype = C.c_int
         L.orc_cross_entropy.argtypes = [i64, i64, P, P, P, P]
         L.orc_rope.restype = C.c_int
@@ -255,11 +255,16 @@ def mlpin_bwd(hb, gamma, Wp, wp_dt: int, wp_scale: float, dy, eps: float, rows=N
     return dict(dh=dh, r=r, dz=dz)
 
 
-def mlpin_wgrad(hb, gamma, Wp, wp_dt: int, wp_scale: float, W_raw, dy, eps: float, js=None, ks=None):
+def mlpin_wgrad(hb, gamma, Wp, wp_dt: int, wp_scale: float, W_raw, dy, eps: float, js=None, ks=None,
+                rss=False):
     """Weight gradients of y = SwiGLU(RMSNorm(hb) . W^T) summed over all tokens: dW [nj, nk]
     at the listed rows js of W (default all 2F) and columns ks (default all d); dgamma
     [nk] only when js covers every row (else None).  Inputs as :func:`mlpin_bwd` plus
-    the raw weight W_raw [2F, d] (bf16 codes)."""
+    the raw weight W_raw [2F, d] (bf16 codes).
+
+    rss=True also returns the root-sum-square over the tokens of the summed terms,
+    (dW, dgamma, rss [nj, nk] (gamma left out), rss_gamma [nk] or None): the scale of a
+    sum's error when each of its terms carries an independent relative rounding."""
     hb = np.ascontiguousarray(hb, dtype=np.uint16)
     dy = np.ascontiguousarray(dy, dtype=np.uint16)
     g = np.ascontiguousarray(gamma, dtype=np.float32)
@@ -275,8 +280,10 @@ def mlpin_wgrad(hb, gamma, Wp, wp_dt: int, wp_scale: float, W_raw, dy, eps: floa
     full = js is None
     dW = np.empty((j.size, k.size), np.float64)
     dgam = np.empty(k.size, np.float64) if full else None
+    sq = np.empty((j.size, k.size), np.float64) if rss else None
+    sqg = np.empty(k.size, np.float64) if rss and full else None
     rc = lib().orc_mlpin_wgrad(M, d, F, _p(hb), _p(g), _p(Wp), wp_dt, float(wp_scale), _p(Wr), _p(dy), float(eps),
-                               j.size, _p(j), k.size, _p(k), _p(dW), _p(dgam))
+                               j.size, _p(j), k.size, _p(k), _p(dW), _p(dgam), _p(sq), _p(sqg))
     if rc != 0:
         raise RuntimeError(f"oracle weight gradient failed ({rc})")
-    return dW, dgam
+    return (dW, dgam, sq, sqg) if rss else (dW, dgam)

@@ -127,3 +127,26 @@ def test_weight_gradient_samples_equal_the_full_result():
     part, none = oracle.mlpin_wgrad(hb, g, Wp, oracle.BF16, 1.0, W, dy, eps, js=js, ks=ks)
     assert none is None
     assert np.array_equal(part, dW[np.ix_(js, ks)])
+
+
+def test_weight_gradient_rss_is_the_root_sum_square_of_the_per_token_gradients():
+    # the terms of the token sum are the one-token gradients: running the oracle on each
+    # token alone gives them, so rss^2 = sum_m (dW_m / gamma)^2 and
+    # rss_gamma^2 = sum_m sum_j (W dW_m / gamma)^2
+    hb, dy, g, Wp, W, eps = _pow2_case(5, 16, 8, 13)
+    dW, dgam, rss, rssg = oracle.mlpin_wgrad(hb, g, Wp, oracle.BF16, 1.0, W, dy, eps, rss=True)
+    Wr = oracle.bf16_decode(W)
+    sq, sqg = np.zeros_like(rss), np.zeros_like(rssg)
+    for m in range(hb.shape[0]):
+        dWm, _ = oracle.mlpin_wgrad(hb[m:m + 1], g, Wp, oracle.BF16, 1.0, W, dy[m:m + 1], eps)
+        t = dWm / g.astype(np.float64)[None, :]
+        sq += t * t
+        sqg += np.sum((Wr * t) ** 2, axis=0)
+    assert np.allclose(rss, np.sqrt(sq), rtol=1e-12, atol=0)
+    assert np.allclose(rssg, np.sqrt(sqg), rtol=1e-12, atol=0)
+    # Cauchy-Schwarz over the M terms
+    assert np.all(np.abs(dW) / g.astype(np.float64)[None, :] <= np.sqrt(hb.shape[0]) * rss * (1 + 1e-12))
+    # sampled rss equals the full one
+    js, ks = np.array([3, 12]), np.array([15, 0])
+    _, _, part, none = oracle.mlpin_wgrad(hb, g, Wp, oracle.BF16, 1.0, W, dy, eps, js=js, ks=ks, rss=True)
+    assert none is None and np.array_equal(part, rss[np.ix_(js, ks)])
