@@ -150,8 +150,10 @@ def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
 
 
 def bench_backward(w, args) -> dict:
-    """Input gradient of the MLP-input block (three calls), the saved forward state --
-    folded weight, its transpose, the row scale -- prepared outside the timed region."""
+    """Backward of the MLP-input block: the input gradient (three calls) and the weight
+    and gamma gradients (two transposes, the token-contracting GEMM, the column sum).
+    The saved forward state -- folded weight, its transpose, the row scale -- is prepared
+    outside the timed region."""
     import numpy as np
     import torch
 
@@ -170,29 +172,42 @@ def bench_backward(w, args) -> dict:
     torch.cuda.synchronize()
     prep_ms = (time.perf_counter() - t0) * 1e3
     M, d, F = w.M, w.d, w.N2w // 2
-    out = {"dz": torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda"),
-           "partials": torch.empty((M, -(-F // 128)), dtype=torch.float32, device="cuda"),
-           "q": torch.empty(M, dtype=torch.float32, device="cuda"),
-           "dh": torch.empty((M, d), dtype=torch.bfloat16, device="cuda")}
+    TW = coda.wgrad_partials_rows(2 * F)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    b16 = dict(dtype=torch.bfloat16, device="cuda")
+    out = {"dz": torch.empty((M, 2 * F), **b16), "partials": torch.empty((M, -(-F // 128)), **f32),
+           "q": torch.empty(M, **f32), "dh": torch.empty((M, d), **b16),
+           "dzt": torch.empty((2 * F, M), **b16), "ht": torch.empty((d, M), **b16),
+           "dW": torch.empty((2 * F, d), **f32), "wpartials": torch.empty((TW, d), **f32),
+           "dgamma": torch.empty(d, **f32)}
     stream = torch.cuda.current_stream()
+    names = ["gemm_swiglu_bwd", "rmsnorm_bwd_reduce", "gemm_rmsnorm_bwd", "transpose_dz", "transpose_h",
+             "gemm_wgrad", "colsum_reduce"]
+    kern = ["k_gemm_rowscale_swiglu", "k_rmsnorm_bwd_reduce", "k_gemm_rmsnorm_bwd", "k_transpose_bf16",
+            "k_transpose_bf16", "k_gemm_wgrad", "k_colsum_reduce"]
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+        mark = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        mark(0)
         dz, P = coda.gemm_swiglu_bwd(h, Wp, r, dy, out["dz"], out["partials"])
-        if ev is not None:
-            ev[1].record(stream)
+        mark(1)
         q = coda.rmsnorm_bwd_reduce(P, r, d, F, out["q"])
-        if ev is not None:
-            ev[2].record(stream)
+        mark(2)
         coda.gemm_rmsnorm_bwd(dz, Wpt, h, q, None, out["dh"])
-        if ev is not None:
-            ev[3].record(stream)
+        mark(3)
+        coda.transpose_bf16(dz, out["dzt"])
+        mark(4)
+        coda.transpose_bf16(h, out["ht"])
+        mark(5)
+        _, Pw = coda.gemm_wgrad(out["dzt"], out["ht"], gamma, W, out["dW"], out["wpartials"])
+        mark(6)
+        coda.colsum_reduce(Pw, out["dgamma"])
+        mark(7)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -201,26 +216,31 @@ def bench_backward(w, args) -> dict:
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
-    k_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
+    k_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(len(names))]
     flops = w.gemm_flops
     g_flops = 2 * M * d * 2 * F
     value = flops / (ms_per_step * 1e-3) / 1e12
-    dom = 0 if k_ms[0] >= k_ms[2] else 2
-    names = ["gemm_swiglu_bwd", "rmsnorm_bwd_reduce", "gemm_rmsnorm_bwd"]
-    kern = ["k_gemm_rowscale_swiglu", "k_rmsnorm_bwd_reduce", "k_gemm_rmsnorm_bwd"]
+    gemms = (0, 2, 5)
+    dom = max(gemms, key=lambda i: k_ms[i])
     T = -(-F // 128)
     byt = {"gemm_swiglu_bwd": M * d * 2 + 2 * F * d * 2 + M * 4 + M * F * 2 + M * 2 * F * 2 + M * T * 4,
            "rmsnorm_bwd_reduce": M * T * 4 + 2 * M * 4,
-           "gemm_rmsnorm_bwd": M * 2 * F * 2 + d * 2 * F * 2 + M * d * 2 + M * 4 + M * d * 2}
+           "gemm_rmsnorm_bwd": M * 2 * F * 2 + d * 2 * F * 2 + M * d * 2 + M * 4 + M * d * 2,
+           "transpose_dz": 2 * M * 2 * F * 2,
+           "transpose_h": 2 * M * d * 2,
+           "gemm_wgrad": 2 * F * M * 2 + d * M * 2 + d * 4 + 2 * F * d * 2 + 2 * F * d * 4 + TW * d * 4,
+           "colsum_reduce": TW * d * 4 + d * 4}
     achieved = g_flops / (k_ms[dom] * 1e-3) / 1e12
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "M": M, "d": d, "F": F, "direction": "backward (input gradient)",
-                   "eps": w.eps, "seed": w.seed},
-        "note": "FLOPs of the two executed GEMMs: the recomputed gate/up product and the input-gradient product",
+        "config": {"workload": w.name, "M": M, "d": d, "F": F,
+                   "direction": "backward (input, weight and gamma gradients)", "eps": w.eps, "seed": w.seed},
+        "note": "FLOPs of the three executed GEMMs: the recomputed gate/up product, the input-gradient "
+                "product and the weight-gradient product",
         "kernels_ms": {n: round(t, 4) for n, t in zip(names, k_ms)},
+        "gemm_tflops": {names[i]: round(g_flops / (k_ms[i] * 1e-3) / 1e12, 1) for i in gemms},
         "hbm_bytes_algorithmic": {"fused": sum(byt.values())},
         "prep_ms": round(prep_ms, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
@@ -230,45 +250,62 @@ def bench_backward(w, args) -> dict:
         "kernel_source_hash": kernel_source_hash(),
     }
     if args.unfused:
-        # torch autograd of the unfused forward (bf16 GEMMs, element-wise RMSNorm / SwiGLU);
-        # the forward runs once outside the timed region and its saved activations are
-        # reused: this baseline does NOT recompute the gate/up product
+        # torch autograd of the unfused forward (bf16 GEMMs, element-wise RMSNorm / SwiGLU)
+        # for the same three gradients; the forward runs once outside the timed region and
+        # its saved activations are reused: this baseline does NOT recompute the gate/up
+        # product
         hh = h.clone().requires_grad_(True)
+        Wl = W.clone().requires_grad_(True)
+        gl = gamma.clone().requires_grad_(True)
         hf = hh.float()
-        n = (hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + w.eps)).to(torch.bfloat16) * \
-            gamma.to(torch.bfloat16)
-        z = n @ W.t()
+        n = (hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + w.eps)).to(torch.bfloat16) * gl.to(torch.bfloat16)
+        z = n @ Wl.t()
         y = torch.nn.functional.silu(z[:, :F]) * z[:, F:]
         for _ in range(3):
-            torch.autograd.grad(y, hh, dy, retain_graph=True)
+            torch.autograd.grad(y, (hh, Wl, gl), dy, retain_graph=True)
         torch.cuda.synchronize()
         s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s2.record(stream)
         for _ in range(args.steps):
-            torch.autograd.grad(y, hh, dy, retain_graph=True)
+            torch.autograd.grad(y, (hh, Wl, gl), dy, retain_graph=True)
         e2.record(stream)
         torch.cuda.synchronize()
         ums = s2.elapsed_time(e2) / args.steps
         rec["unfused_torch"] = {"ms_per_step": round(ums, 4), "speedup_of_fused": round(ums / ms_per_step, 3),
-                                "note": "autograd input gradient from saved activations (one GEMM)"}
+                                "note": "autograd input, weight and gamma gradients from saved activations "
+                                        "(two GEMMs)"}
     if not args.no_cpu_baseline:
         import oracle
 
         Wp_ref = oracle.fold_bf16(inp["W_t"], inp["gamma"])
         rng = np.random.default_rng(0)
-        n_rows, dt = 8, 0.0
+        # input gradient: sampled rows (a fraction rows / M of the two GEMMs it runs);
+        # weight gradients: sampled rows of dW, every column (a fraction js / 2F of the third)
+        n_rows, dt1 = 8, 0.0
         while True:
             rows = np.sort(rng.choice(M, size=min(n_rows, M), replace=False))
             t1 = time.perf_counter()
             oracle.mlpin_bwd(inp["h"], inp["gamma"], Wp_ref, oracle.BF16, 1.0, inp["dy"], w.eps, rows=rows)
-            dt = time.perf_counter() - t1
-            if dt >= args.cpu_seconds / 2 or n_rows >= M:
+            dt1 = time.perf_counter() - t1
+            if dt1 >= args.cpu_seconds / 4 or n_rows >= M:
                 break
             n_rows *= 2
-        rec["cpu_baseline"] = {"value": round(rows.size * flops / M / dt / 1e12, 6), "unit": "TFLOP/s",
+        n_js, dt2 = 1, 0.0
+        while True:
+            js = np.sort(rng.choice(2 * F, size=min(n_js, 2 * F), replace=False))
+            t1 = time.perf_counter()
+            oracle.mlpin_wgrad(inp["h"], inp["gamma"], Wp_ref, oracle.BF16, 1.0, inp["W_t"], inp["dy"], w.eps,
+                               js=js)
+            dt2 = time.perf_counter() - t1
+            if dt2 >= args.cpu_seconds / 4 or n_js >= 2 * F:
+                break
+            n_js *= 2
+        done = rows.size / M * 2 * g_flops + js.size / (2 * F) * g_flops
+        rec["cpu_baseline"] = {"value": round(done / (dt1 + dt2) / 1e12, 6), "unit": "TFLOP/s",
                                "cores": oracle.max_threads(), "kind": "oracle",
-                               "sample": f"{rows.size} random rows of the {M}-row workload (fp64 backward, "
-                                         f"recomputed forward included), {dt:.1f} s"}
+                               "sample": f"{rows.size} random rows of dh ({dt1:.1f} s) and {js.size} random rows "
+                                         f"of dW, all columns ({dt2:.1f} s), of the {M}-token workload (fp64, "
+                                         f"recomputed forward included)"}
     return rec
 
 

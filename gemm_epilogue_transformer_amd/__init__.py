@@ -24,7 +24,8 @@ __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3"
            "partials_per_row", "gemm_resid_partialrms", "rowscale_reduce",
            "gemm_rowscale_swiglu", "rope_table", "gemm_rowscale_rope", "ce_partials_per_row",
            "gemm_rowscale_ce", "ce_reduce", "rowscale_from_h", "transpose_bf16", "gemm_swiglu_bwd", "rmsnorm_bwd_reduce",
-           "gemm_rmsnorm_bwd", "mlpin_bwd", "chain", "version"]
+           "gemm_rmsnorm_bwd", "mlpin_bwd", "wgrad_partials_rows", "gemm_wgrad", "colsum_reduce",
+           "mlpin_wgrad", "chain", "version"]
 
 
 def _stream(stream):
@@ -248,6 +249,47 @@ def mlpin_bwd(h, Wp, Wpt, r, dy, dh_res=None, out=None, stream=None):
     q = rmsnorm_bwd_reduce(P, r, h.shape[1], Wp.shape[0] // 2, out.get("q"), stream)
     dh = gemm_rmsnorm_bwd(dz, Wpt, h, q, dh_res, out.get("dh"), stream)
     return dh, dz, P, q
+
+
+def wgrad_partials_rows(NR: int) -> int:
+    return int(_lib.load().coda_wgrad_partials_rows(NR))
+
+
+def gemm_wgrad(At, Bt, gamma=None, W=None, dW=None, partials=None, stream=None):
+    """dW [NR, NC] fp32 = gamma * (At . Bt^T), a sum over the K tokens of At [NR, K] and
+    Bt [NC, K]; with the raw weight W [NR, NC] also the per-256-row-tile partials of the
+    gamma gradient sum_j W[j,k] * G[j,k] (else partials is None)."""
+    _esize(At, 2)
+    _esize(Bt, 2)
+    NR, K = At.shape
+    NC = Bt.shape[0]
+    dW = torch.empty((NR, NC), dtype=torch.float32, device=At.device) if dW is None else dW
+    if W is not None and partials is None:
+        partials = torch.empty((wgrad_partials_rows(NR), NC), dtype=torch.float32, device=At.device)
+    _lib.check("coda_gemm_wgrad", _lib.load().coda_gemm_wgrad(
+        NR, NC, K, _ptr(At), _ptr(Bt), _ptr(gamma), _ptr(W), _ptr(dW),
+        _ptr(partials) if W is not None else None, _stream(stream)))
+    return dW, (partials if W is not None else None)
+
+
+def colsum_reduce(partials, out=None, stream=None):
+    """out [NC] = sum over the rows of partials [T, NC] (fixed order, fp64 inside)."""
+    T, NC = partials.shape
+    out = torch.empty(NC, dtype=torch.float32, device=partials.device) if out is None else out
+    _lib.check("coda_colsum_reduce", _lib.load().coda_colsum_reduce(T, NC, _ptr(partials), _ptr(out), _stream(stream)))
+    return out
+
+
+def mlpin_wgrad(dz, h, gamma, W, dzt=None, ht=None, out=None, stream=None):
+    """Weight gradients of the MLP-input block from the backward's dz = r * dL/dz [M, 2F]
+    and the block input h [M, d]: returns (dW [2F, d], dgamma [d]) for the raw weight
+    W [2F, d] and gamma [d].  dzt / ht may pass already transposed operands."""
+    out = out or {}
+    dzt = transpose_bf16(dz, out.get("dzt"), stream) if dzt is None else dzt
+    ht = transpose_bf16(h, out.get("ht"), stream) if ht is None else ht
+    dW, P = gemm_wgrad(dzt, ht, gamma, W, out.get("dW"), out.get("wpartials"), stream)
+    dgam = colsum_reduce(P, out.get("dgamma"), stream)
+    return dW, dgam
 
 
 def chain(A, Wo_t, x_res, Wp_t, eps, act=SWIGLU, a_scale=None, wo_scale=None, wp_scale=None,

@@ -36,6 +36,9 @@ SIGNATURES = {
     "coda_gemm_swiglu_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "coda_rmsnorm_bwd_reduce": (_I, [_I64, _I64, _I64, _P, _P, _P, _P]),
     "coda_gemm_rmsnorm_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "coda_wgrad_partials_rows": (_I64, [_I64]),
+    "coda_gemm_wgrad": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "coda_colsum_reduce": (_I, [_I64, _I64, _P, _P, _P]),
     "coda_status_string": (C.c_char_p, [_I]),
     "coda_last_hip_error": (_I, []),
     "coda_version": (C.c_char_p, []),

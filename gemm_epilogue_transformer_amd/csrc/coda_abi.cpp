@@ -339,4 +339,40 @@ coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* d
                                                     as_stream(stream)));
 }
 
+int64_t coda_wgrad_partials_rows(int64_t NR) { return NR < 1 || NR > kMaxDim ? -1 : coda::wgrad_partials_rows(NR); }
+
+coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, const void* Bt,
+                            const float* gamma, const void* W, float* dW, float* partials,
+                            void* stream) {
+    if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0)) return CODA_ERR_SHAPE;
+    if (NC % 8 != 0 || K % 8 != 0 || K > kMaxRow || NC > kMaxRow / 2) return CODA_ERR_SHAPE;
+    const int64_t T = coda::wgrad_partials_rows(NR);
+    if (!prod_ok(NR, K) || !prod_ok(NC, K) || !prod_ok(NR, NC) || !prod_ok(T, NC)) return CODA_ERR_SHAPE;
+    if (coda::wgrad_tiles(NR, NC) > kMaxDim) return CODA_ERR_SHAPE;
+    if (!dW || (W && !partials) || (K > 0 && (!At || !Bt))) return CODA_ERR_NULL;
+    if (!aligned16(dW) || (W && !aligned16(W)) || (gamma && !aligned16(gamma)) || (partials && !aligned16(partials)) ||
+        (K > 0 && (!aligned16(At) || !aligned16(Bt))))
+        return CODA_ERR_ALIGN;
+    const Range ro = span(dW, NR * NC * 4), rp = W ? span(partials, T * NC * 4) : span(nullptr, 0);
+    if (W && overlap(ro, rp)) return CODA_ERR_ALIAS;
+    const Range ins[] = {K > 0 ? span(At, NR * K * 2) : span(nullptr, 0), K > 0 ? span(Bt, NC * K * 2) : span(nullptr, 0),
+                         gamma ? span(gamma, NC * 4) : span(nullptr, 0), W ? span(W, NR * NC * 2) : span(nullptr, 0)};
+    for (const Range& in : ins)
+        if (overlap(ro, in) || (W && overlap(rp, in))) return CODA_ERR_ALIAS;
+    hipStream_t s = as_stream(stream);
+    if (K == 0) {
+        hipError_t e = coda::launch_fill_zero_f32(NR * NC, dW, s);
+        if (e == hipSuccess && W) e = coda::launch_fill_zero_f32(T * NC, partials, s);
+        return hip_status(e);
+    }
+    return hip_status(coda::launch_gemm_wgrad(int(NR), int(NC), int(K), At, Bt, gamma, W, dW, W ? partials : nullptr, s));
+}
+
+coda_status coda_colsum_reduce(int64_t T, int64_t NC, const float* partials, float* out, void* stream) {
+    if (!dim_ok(T, 1) || !dim_ok(NC, 1) || !prod_ok(T, NC)) return CODA_ERR_SHAPE;
+    if (!partials || !out) return CODA_ERR_NULL;
+    if (overlap(span(out, NC * 4), span(partials, T * NC * 4))) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_colsum_reduce(int(T), int(NC), partials, out, as_stream(stream)));
+}
+
 }  // extern "C"

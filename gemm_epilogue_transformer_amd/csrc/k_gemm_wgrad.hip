@@ -1,0 +1,205 @@
+// Weight-gradient GEMM (a sum over the tokens) with a column-scale epilogue and the
+// column partials of the RMSNorm-weight gradient.
+//
+//   G[j,k]   = sum_m At[j,m] Bt[k,m]            (At = (r * dL/dz)^T, Bt = h^T: both passed
+//                                                token-contiguous, so the mainloop is the
+//                                                forward's)
+//   dW[j,k]  = gamma[k] * G[j,k]                 (fp32; gamma NULL: 1)
+//   Pg[t,k]  = sum over the rows j of tile t of W[j,k] * G[j,k]   (only when W is given)
+//
+// For the block y = SwiGLU(RMSNorm(h) . W^T) with the folded weight W' = gamma * W,
+// dL/dW = gamma * G and dL/dgamma[k] = sum_j W[j,k] G[j,k]: the vector operand gamma is
+// broadcast over the columns and the gamma gradient is a block reduction in the
+// epilogue, the forward's primitives (kucoin page, section "Cinco bloques y un lenguaje
+// LEGO"; section "CODA: El epilogo esconde un tesoro": the backward pass inherits the
+// forward's structure).  Per 32-row slab: accumulators staged row-major in LDS, each
+// lane takes runs of 8 columns; the column sums run over the lane's rows, the 4 lanes
+// holding the same columns, then the waves sharing them, in a fixed order.
+#include <algorithm>
+
+#include "epilogue.hpp"
+#include "gemm_pipeline.hpp"
+#include "launch.hpp"
+
+namespace coda {
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
+k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, const float* __restrict__ gamma,
+             const uint16_t* __restrict__ Wraw, float* __restrict__ dW, float* __restrict__ Pg, int NR, int NC,
+             int K, int tiles_m, int tiles_n) {
+    constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 32, TN = WN / 32;
+
+    constexpr int kStage = (BM + BN) * RB;
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+    __shared__ float red[WAVES_M][BN];
+    uint8_t* st[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) st[i] = stages[i];
+
+    int tile_m, tile_n;
+    tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    const int kbytes = K * 2;
+    DmaPanel<BM, BM, NW, RB> pa;
+    DmaPanel<BN, BN, NW, RB> pb;
+    const uint8_t* a0 = At + static_cast<size_t>(m0) * kbytes;
+    const uint8_t* b0 = Bt + static_cast<size_t>(n0) * kbytes;
+    pa.init(a0, min(BM, NR - m0), a0, 0, kbytes);
+    pb.init(b0, min(BN, NC - n0), b0, 0, kbytes);
+    auto a_row = [&](int tm) { return wm * WM + tm * 32; };
+    auto b_row = [&](int tn) { return wn * WN + tn * 32; };
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    mainloop_dma<Elt::BF16, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
+
+    using S = Slab<TN>;
+    static_assert(64 % S::kSegPerRow == 0, "a lane's segments share their columns");
+    uint8_t* slab = slab_region<NS, NW, kStage, S::kBytes>(st, wave);
+    const int valid_rows = min(BM, NR - m0);
+    const uint32_t wrow = static_cast<uint32_t>(NC) * 2, orow = static_cast<uint32_t>(NC) * 4;
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        make_buffer_rsrc(Wraw ? Wraw + static_cast<size_t>(m0) * NC : nullptr, Wraw ? valid_rows * wrow : 0u);
+    const __amdgpu_buffer_rsrc_t o_rsrc = make_buffer_rsrc(dW + static_cast<size_t>(m0) * NC, valid_rows * orow);
+    const __amdgpu_buffer_rsrc_t g_rsrc = make_buffer_rsrc(gamma, gamma ? static_cast<uint32_t>(NC) * 4 : 0u);
+    // this lane's 8 columns (the same for all its segments) and their gamma
+    const int col = n0 + wn * WN + (lane % S::kSegPerRow) * 8;
+    const bool col_in = col < NC;
+    float gm[8];
+    {
+        const uint32_t go = col_in ? static_cast<uint32_t>(col) * 4 : kOobOffset;
+        const f32x4_t g0 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(g_rsrc, go, 0, 0));
+        const f32x4_t g1 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(g_rsrc, go + 16, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gm[e] = gamma ? g0[e] : 1.0f;
+            gm[4 + e] = gamma ? g1[e] : 1.0f;
+        }
+    }
+    float cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        float v[TN][16];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[tn][i] = acc[tm][tn][i];
+        S::put(slab, v);
+#pragma unroll
+        for (int j = 0; j < S::kSegPerLane; ++j) {
+            float t[8];
+            S::get(slab, j, t);
+            const uint32_t tr = static_cast<uint32_t>(wm * WM + tm * 32 + S::seg_row(j));
+            i32x4_t wv = {0, 0, 0, 0};
+            if (Wraw) wv = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, col_in ? tr * wrow + col * 2u : kOobOffset, 0, 0);
+            f32x4_t o0, o1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o0[e] = gm[e] * t[e];
+                o1[e] = gm[4 + e] * t[4 + e];
+            }
+            const uint32_t oo = col_in ? tr * orow + col * 4u : kOobOffset;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, o0), o_rsrc, oo, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, o1), o_rsrc, oo + 16, 0, 0);
+            if (Wraw) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t x = static_cast<uint32_t>(wv[e]);
+                    cs[2 * e] += bf16_bits_to_f32(static_cast<uint16_t>(x & 0xFFFFu)) * t[2 * e];
+                    cs[2 * e + 1] += bf16_bits_to_f32(static_cast<uint16_t>(x >> 16)) * t[2 * e + 1];
+                }
+            }
+        }
+    }
+    if (Wraw) {
+        // the lanes that hold the same columns: lane % kSegPerRow equal
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int off = S::kSegPerRow; off < 64; off <<= 1) cs[e] += __shfl_xor(cs[e], off);
+        if (lane < S::kSegPerRow) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wm][wn * WN + lane * 8 + e] = cs[e];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < BN; c += NT) {
+            const int k = n0 + c;
+            if (k < NC) {
+                float s = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WAVES_M; ++w) s += red[w][c];
+                Pg[static_cast<size_t>(tile_m) * NC + k] = s;
+            }
+        }
+    }
+}
+
+// dgamma[k] = fl32( sum_t Pg[t, k] )  (fixed order, fp64), one thread per column
+__global__ void __launch_bounds__(256)
+k_colsum_reduce(const float* __restrict__ Pg, float* __restrict__ out, int T, int NC) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= NC) return;
+    double s = 0.0;
+    for (int t = 0; t < T; ++t) s += static_cast<double>(Pg[static_cast<size_t>(t) * NC + k]);
+    out[k] = static_cast<float>(s);
+}
+
+// dst[0, n) = 0 (the gradient of an empty token batch); a kernel rather than a memset so
+// that the call may be captured in a graph
+__global__ void __launch_bounds__(256) k_fill_zero_f32(float* __restrict__ dst, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        dst[i] = 0.0f;
+}
+
+#ifndef CODA_WG_BM
+#define CODA_WG_BM 256
+#define CODA_WG_BN 256
+#define CODA_WG_WM 2
+#define CODA_WG_WN 2
+#define CODA_WG_NS 2
+#define CODA_WG_RB 128
+#define CODA_WG_SPREAD 2
+#define CODA_WG_OCC 1
+#endif
+constexpr int BMW = CODA_WG_BM, BNW = CODA_WG_BN;
+
+int64_t wgrad_tiles(int64_t NR, int64_t NC) { return ((NR + BMW - 1) / BMW) * ((NC + BNW - 1) / BNW); }
+int64_t wgrad_partials_rows(int64_t NR) { return NR < 1 ? -1 : (NR + BMW - 1) / BMW; }
+
+hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
+                             const void* Wraw, float* dW, float* Pg, hipStream_t stream) {
+    const int tiles_m = (NR + BMW - 1) / BMW, tiles_n = (NC + BNW - 1) / BNW;
+    const dim3 grid(tiles_m * tiles_n), block(64 * CODA_WG_WM * CODA_WG_WN);
+    hipLaunchKernelGGL((k_gemm_wgrad<BMW, BNW, CODA_WG_WM, CODA_WG_WN, CODA_WG_NS, CODA_WG_RB, CODA_WG_SPREAD,
+                                     CODA_WG_OCC>),
+                       grid, block, 0, stream, static_cast<const uint8_t*>(At), static_cast<const uint8_t*>(Bt),
+                       gamma, static_cast<const uint16_t*>(Wraw), dW, Pg, NR, NC, K, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_colsum_reduce(int T, int NC, const float* Pg, float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(k_colsum_reduce, dim3((NC + 255) / 256), dim3(256), 0, stream, Pg, out, T, NC);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_f32(int64_t n, float* dst, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_fill_zero_f32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, dst, n);
+    return hipGetLastError();
+}
+
+}  // namespace coda

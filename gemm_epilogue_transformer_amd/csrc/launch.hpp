@@ -58,6 +58,15 @@ hipError_t launch_gemm_rmsnorm_bwd(int M, int N, int K, const void* dz, const vo
                                    const float* q, const void* dh_res, void* dh, hipStream_t stream);
 hipError_t launch_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, hipStream_t stream);
 
+// Weight gradients: token-contracting GEMM with the gamma column scale and the column
+// partials of the gamma gradient, and their fixed-order column sum.
+int64_t wgrad_tiles(int64_t NR, int64_t NC);
+int64_t wgrad_partials_rows(int64_t NR);
+hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
+                             const void* Wraw, float* dW, float* Pg, hipStream_t stream);
+hipError_t launch_colsum_reduce(int T, int NC, const float* Pg, float* out, hipStream_t stream);
+hipError_t launch_fill_zero_f32(int64_t n, float* dst, hipStream_t stream);
+
 hipError_t launch_fold_bf16(int64_t N, int64_t K, const void* W, const float* gamma, void* Wp,
                             hipStream_t stream);
 

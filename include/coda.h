@@ -277,6 +277,37 @@ coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* d
                                   const void* h, const float* q, const void* dh_res, void* dh,
                                   void* stream);
 
+/* --------------------------------------------- backward: weight gradients ---- */
+/* Weight gradients of the same block (kucoin page, section "CODA: El epilogo esconde un
+ * tesoro": the backward inherits the forward's structure; section "Cinco bloques y un
+ * lenguaje LEGO": a broadcast vector operand and a block reduction in the epilogue).
+ * With G = (r * dL/dz)^T h summed over the tokens, dL/dW = gamma * G (gamma broadcast
+ * over the columns) and dL/dgamma[k] = sum_j W[j,k] G[j,k] with the raw weight W.  The
+ * reduction runs over the tokens, so both operands are passed token-contiguous (the
+ * outputs of coda_transpose_bf16 of dz and of h).  With gamma = NULL and W = NULL the
+ * same call is the plain weight gradient of a linear layer (the first GEMM's).
+ */
+
+/* Partial rows written by coda_gemm_wgrad for NR gradient rows; -1 if NR < 1.          */
+int64_t coda_wgrad_partials_rows(int64_t NR);
+
+/* Weight-gradient GEMM, contraction over K tokens:
+ *   At [NR, K] bf16 (e.g. (r * dL/dz)^T, NR = 2F);  Bt [NC, K] bf16 (e.g. h^T, NC = d)
+ *   gamma [NC] fp32 or NULL (= 1);  W [NR, NC] bf16 raw weight or NULL (no partials)
+ *   dW [NR, NC] fp32, written: fl32( gamma[k] * sum_m At[j,m] Bt[k,m] )  (fp32 MFMA sums)
+ *   partials [coda_wgrad_partials_rows(NR), NC] fp32, written when W is given: per tile
+ *       of 256 rows j, sum of W[j,k] * G[j,k] (fixed order); may be NULL when W is NULL
+ * K = 0 (no tokens) writes zeros.  Granules: K % 8 == 0, NC % 8 == 0; K <= 2^22,
+ * NC <= 2^21.  Outputs must not overlap each other or the inputs.                    */
+coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, const void* Bt,
+                            const float* gamma, const void* W, float* dW, float* partials,
+                            void* stream);
+
+/* out[k] = fl32( sum_t partials[t, k] )  (fixed order, fp64 inside), T >= 1 rows of NC
+ * columns: the gamma gradient from coda_gemm_wgrad's partials.  out must not overlap.  */
+coda_status coda_colsum_reduce(int64_t T, int64_t NC, const float* partials, float* out,
+                               void* stream);
+
 /* ------------------------------------------------------------------- utilities ---- */
 const char* coda_status_string(coda_status s);
 int coda_last_hip_error(void);      /* hipError_t of this thread's last CODA_ERR_HIP      */

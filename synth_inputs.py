@@ -34,7 +34,7 @@ ACT_NONE = 0
 ACT_SWIGLU = 1
 ACT_ROPE = 2      # rotary position embedding on the QKV product (no activation)
 ACT_CE = 3        # cross-entropy of the LM-head product against per-row targets
-ACT_SWIGLU_BWD = 4  # input gradient of the RMSNorm -> GEMM -> SwiGLU block (no first GEMM)
+ACT_SWIGLU_BWD = 4  # backward of the RMSNorm -> GEMM -> SwiGLU block (no first GEMM)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,9 +62,10 @@ class Workload:
     @property
     def gemm_flops(self) -> int:
         """2*M*K*N for each of the two GEMMs (epilogue arithmetic not counted); for the
-        backward workload the recomputed forward product and the input-gradient product."""
+        backward workload the recomputed forward product, the input-gradient product and
+        the weight-gradient product (all three of shape M x d x 2F)."""
         if self.act == ACT_SWIGLU_BWD:
-            return 2 * (2 * self.M * self.d * self.N2w)
+            return 3 * (2 * self.M * self.d * self.N2w)
         return 2 * self.M * self.K1 * self.d + 2 * self.M * self.d * self.N2w
 
 
@@ -76,9 +77,9 @@ class Workload:
 # columns; V passes), 16384 tokens = 4 sequences of 4096 (same draws as workload 3);
 # 7: the last block of LLaMA-3-1B -- MLP-out + residual, final RMSNorm, LM head over the
 # 128256-token vocabulary -- ending in the cross-entropy loss against uniform targets;
-# 8: the backward of workload 2's second half -- the input gradient of the RMSNorm ->
-# gate/up GEMM -> SwiGLU block -- with the block input h and the upstream gradient dy
-# drawn directly (no first GEMM).
+# 8: the backward of workload 2's second half -- the input, weight and gamma gradients
+# of the RMSNorm -> gate/up GEMM -> SwiGLU block -- with the block input h and the
+# upstream gradient dy drawn directly (no first GEMM).
 WORKLOADS = {
     1: Workload("tiny_m128_d256_n512_none", 128, 256, 256, 512, ACT_NONE, "bf16", 1e-5, 1001),
     2: Workload("llama1b_attnout_mlpin_m16384", 16384, 2048, 2048, 16384, ACT_SWIGLU, "bf16", 1e-5, 1002),

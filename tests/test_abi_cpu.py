@@ -224,3 +224,26 @@ def test_backward_validation():
     assert b(16, 64, 64, P1, P2, P3, P4, P5 + 16, P5, None) == ALIAS     # partial overlap with dh_res
     assert b(16, 64, 64, P1, P2, P3, None, None, P5, None) == NULL
     assert b(0, 64, 64, None, None, None, None, None, None, None) == OK
+
+
+@no_gpu
+def test_weight_gradient_validation():
+    L = _lib.load()
+    assert L.coda_wgrad_partials_rows(0) == -1
+    assert L.coda_wgrad_partials_rows(256) == 1 and L.coda_wgrad_partials_rows(257) == 2
+    w = L.coda_gemm_wgrad
+    # NR, NC, K, At, Bt, gamma, W, dW, partials, stream
+    assert w(64, 60, 64, P1, P2, P3, P4, P5, P6, None) == SHAPE          # NC % 8
+    assert w(64, 64, 60, P1, P2, P3, P4, P5, P6, None) == SHAPE          # K % 8 (the tokens)
+    assert w(0, 64, 64, P1, P2, P3, P4, P5, P6, None) == SHAPE
+    assert w(64, 64, 64, P1, P2, P3, P4, P5, None, None) == NULL         # W without partials
+    assert w(64, 64, 64, None, P2, P3, P4, P5, P6, None) == NULL
+    assert w(64, 64, 0, None, None, None, None, None, None, None) == NULL  # no tokens still writes dW
+    assert w(64, 64, 64, P1, P2, P3 + 4, P4, P5, P6, None) == ALIGN      # gamma read 16 bytes at a time
+    assert w(64, 64, 64, P1, P2, P3, P4, P5, P5 + 64, None) == ALIAS     # partials over dW
+    assert w(64, 64, 64, P1, P2, P3, P4, P1 + 16, P6, None) == ALIAS     # dW over At
+    assert w(64, 64, 64, P1, P2, P3, P4, P5, P4, None) == ALIAS          # partials over W
+    c = L.coda_colsum_reduce
+    assert c(0, 64, P1, P2, None) == SHAPE
+    assert c(4, 64, None, P2, None) == NULL
+    assert c(4, 64, P1, P1 + 128, None) == ALIAS
