@@ -24,7 +24,7 @@ ACT_NONE = 0
 ACT_SWIGLU = 1
 
 __all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
-           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "cross_entropy", "mlpin_bwd", "mlpin_wgrad", "chain", "prepare", "BF16", "E4M3",
+           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "cross_entropy", "mlpin_bwd", "mlpin_wgrad", "chain_bwd", "chain", "prepare", "BF16", "E4M3",
            "ACT_NONE", "ACT_SWIGLU"]
 
 
@@ -287,3 +287,43 @@ def mlpin_wgrad(hb, gamma, Wp, wp_dt: int, wp_scale: float, W_raw, dy, eps: floa
     if rc != 0:
         raise RuntimeError(f"oracle weight gradient failed ({rc})")
     return (dW, dgam, sq, sqg) if rss else (dW, dgam)
+
+
+def chain_bwd(prep: dict, x_res, gamma, W_raw, dy, eps: float, dres=None, rows=None, rss=False):
+    """Backward of the whole chain  h = x_res + A . Wo^T,  y = SwiGLU(RMSNorm(h) . W^T)
+    (kucoin page, section "CODA: El epilogo esconde un tesoro": the backward keeps the
+    forward's structure; section "Resultados del experimento": the backward of
+    GEMM-Residual-PartialRMS-GEMM).  bf16 operands (``prep`` from :func:`prepare`).
+
+    The chain rule in reverse order, fp64:
+      dh     = d/dh of the MLP-input block (:func:`mlpin_bwd`, at the rounded hb the
+               forward stores) + dres (the gradient reaching h through the residual
+               stream; None = 0).  The bf16 rounding of h passes the gradient unchanged.
+      dx_res = dh;   dA = dh . Wo;   dWo[n, k] = sum_m dh[m, n] A[m, k]
+      dW, dgamma of the second weight and of gamma (:func:`mlpin_wgrad`).
+    Returns dict(dh [R, d], dA [R, K1], and with rows=None also dWo [d, K1], dW [2F, d],
+    dgamma [d]).  rss=True adds the root-sum-square of the summed terms of each entry of
+    dA (over n), dWo (over m), dW (gamma left out, as :func:`mlpin_wgrad`) and dgamma
+    (``rss_*``) for rounding-error bounds."""
+    if prep["a_dt"] != BF16 or prep["wo_dt"] != BF16 or prep["wp_dt"] != BF16:
+        raise ValueError("the backward is defined for bf16 operands")
+    M = prep["A"].shape[0]
+    sel = np.arange(M) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    fwd = chain(prep, x_res, gamma, ACT_SWIGLU, eps, rows=None if rows is None else sel)
+    hb = fwd["hb"]
+    dyr = np.ascontiguousarray(np.asarray(dy)[sel])
+    b = mlpin_bwd(hb, gamma, prep["Wp"], BF16, 1.0, dyr, eps)
+    dh = b["dh"] + (0.0 if dres is None else bf16_decode(np.asarray(dres)[sel]))
+    A = bf16_decode(prep["A"])
+    Wo = bf16_decode(prep["Wo"])
+    out = dict(dh=dh, dA=dh @ Wo)
+    if rss:
+        out["rss_dA"] = np.sqrt((dh * dh) @ (Wo * Wo))
+    if rows is None:
+        out["dWo"] = dh.T @ A
+        wg = mlpin_wgrad(hb, gamma, prep["Wp"], BF16, 1.0, W_raw, dyr, eps, rss=rss)
+        out["dW"], out["dgamma"] = wg[0], wg[1]
+        if rss:
+            out["rss_dWo"] = np.sqrt((dh * dh).T @ (A * A))
+            out["rss_dW"], out["rss_dgamma"] = wg[2], wg[3]
+    return out
