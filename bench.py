@@ -150,9 +150,12 @@ def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
 
 
 def bench_backward(w, args) -> dict:
-    """Backward of the MLP-input block: the input gradient (three calls) and the weight
-    and gamma gradients (two transposes, the token-contracting GEMM, the column sum).
-    The saved forward state -- folded weight, its transpose, the row scale -- is prepared
+    """Backward step.  Workload of the MLP-input block: its input gradient (three calls)
+    and the weight and gamma gradients (two transposes, the token-contracting GEMM, the
+    column sum).  Whole-chain workload: the same plus the first GEMM's input gradient dA
+    and weight gradient dWo (two more transposes, the plain GEMM, the token-contracting
+    GEMM); the residual input's gradient is dh itself.  The saved forward state -- folded
+    weight, weight transposes, h and r (from a forward run of the chain) -- is prepared
     outside the timed region."""
     import numpy as np
     import torch
@@ -160,18 +163,32 @@ def bench_backward(w, args) -> dict:
     import gemm_epilogue_transformer_amd as coda
     import synth_inputs as si
 
+    whole = w.act == si.ACT_CHAIN_BWD
     inp = si.generate(w)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
-    h, W, dy = dev(inp["h"]), dev(inp["W_t"]), dev(inp["dy"])
+    W, dy = dev(inp["W_t"]), dev(inp["dy"])
     gamma = torch.from_numpy(inp["gamma"]).cuda()
+    M, d, F, K1 = w.M, w.d, w.N2w // 2, w.K1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     Wp = coda.prepare_weight_bf16(W, gamma)
     Wpt = coda.transpose_bf16(Wp)
-    r = coda.rowscale_from_h(h, w.eps)
+    saved = args.saved_z
+    z = None
+    if whole:
+        A, Wo, xr, dres = dev(inp["A"]), dev(inp["Wo_t"]), dev(inp["x_res"]), dev(inp["dres"])
+        WoT = coda.transpose_bf16(Wo)
+        fwd = coda.chain(A, Wo, xr, Wp, w.eps, save_z=saved)
+        h, r = fwd[0], fwd[2]
+        z = fwd[4] if saved else None
+    else:
+        h = dev(inp["h"])
+        dres = None
+        r = coda.rowscale_from_h(h, w.eps)
+        if saved:
+            _, z = coda.gemm_rowscale_swiglu_save(h, Wp, r)
     torch.cuda.synchronize()
     prep_ms = (time.perf_counter() - t0) * 1e3
-    M, d, F = w.M, w.d, w.N2w // 2
     TW = coda.wgrad_partials_rows(2 * F)
     f32 = dict(dtype=torch.float32, device="cuda")
     b16 = dict(dtype=torch.bfloat16, device="cuda")
@@ -180,29 +197,48 @@ def bench_backward(w, args) -> dict:
            "dzt": torch.empty((2 * F, M), **b16), "ht": torch.empty((d, M), **b16),
            "dW": torch.empty((2 * F, d), **f32), "wpartials": torch.empty((TW, d), **f32),
            "dgamma": torch.empty(d, **f32)}
+    if whole:
+        out.update({"dA": torch.empty((M, K1), **b16), "dht": torch.empty((d, M), **b16),
+                    "At": torch.empty((K1, M), **b16), "dWo": torch.empty((d, K1), **f32)})
+        nws = coda.wgrad_workspace_bytes(d, K1, M)
+        out["ws"] = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws > 0 else None
     stream = torch.cuda.current_stream()
-    names = ["gemm_swiglu_bwd", "rmsnorm_bwd_reduce", "gemm_rmsnorm_bwd", "transpose_dz", "transpose_h",
-             "gemm_wgrad", "colsum_reduce"]
-    kern = ["k_gemm_rowscale_swiglu", "k_rmsnorm_bwd_reduce", "k_gemm_rmsnorm_bwd", "k_transpose_bf16",
-            "k_transpose_bf16", "k_gemm_wgrad", "k_colsum_reduce"]
+    # (name, kernel, call); the calls write into `out`
+    if saved:
+        stages = [("swiglu_bwd_saved", "k_swiglu_bwd_saved",
+                   lambda: coda.swiglu_bwd_saved(z, dy, r, out["dz"], out["dzt"], out["partials"]))]
+    else:
+        stages = [("gemm_swiglu_bwd", "k_gemm_rowscale_swiglu",
+                   lambda: coda.gemm_swiglu_bwd(h, Wp, r, dy, out["dz"], out["partials"]))]
+    stages += [
+        ("rmsnorm_bwd_reduce", "k_rmsnorm_bwd_reduce",
+         lambda: coda.rmsnorm_bwd_reduce(out["partials"], r, d, F, out["q"])),
+        ("gemm_rmsnorm_bwd", "k_gemm_rmsnorm_bwd",
+         lambda: coda.gemm_rmsnorm_bwd(out["dz"], Wpt, h, out["q"], dres, out["dh"]))]
+    if not saved:
+        stages.append(("transpose_dz", "k_transpose16_bf16", lambda: coda.transpose_bf16(out["dz"], out["dzt"])))
+    stages += [
+        ("transpose_h", "k_transpose16_bf16", lambda: coda.transpose_bf16(h, out["ht"])),
+        ("gemm_wgrad", "k_gemm_wgrad",
+         lambda: coda.gemm_wgrad(out["dzt"], out["ht"], gamma, W, out["dW"], out["wpartials"])),
+        ("colsum_reduce", "k_colsum_reduce", lambda: coda.colsum_reduce(out["wpartials"], out["dgamma"]))]
+    if whole:
+        stages += [
+            ("gemm_dA", "k_gemm_rmsnorm_bwd", lambda: coda.gemm_bf16(out["dh"], WoT, None, out["dA"])),
+            ("transpose_dh", "k_transpose16_bf16", lambda: coda.transpose_bf16(out["dh"], out["dht"])),
+            ("transpose_A", "k_transpose16_bf16", lambda: coda.transpose_bf16(A, out["At"])),
+            ("gemm_wgrad_dWo", "k_gemm_wgrad",                                # token split + its reduce
+             lambda: coda.gemm_wgrad(out["dht"], out["At"], None, None, out["dWo"], None, out["ws"]))]
+    names = [x[0] for x in stages]
+    kern = [x[1] for x in stages]
 
     def step(ev=None):
-        mark = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
-        mark(0)
-        dz, P = coda.gemm_swiglu_bwd(h, Wp, r, dy, out["dz"], out["partials"])
-        mark(1)
-        q = coda.rmsnorm_bwd_reduce(P, r, d, F, out["q"])
-        mark(2)
-        coda.gemm_rmsnorm_bwd(dz, Wpt, h, q, None, out["dh"])
-        mark(3)
-        coda.transpose_bf16(dz, out["dzt"])
-        mark(4)
-        coda.transpose_bf16(h, out["ht"])
-        mark(5)
-        _, Pw = coda.gemm_wgrad(out["dzt"], out["ht"], gamma, W, out["dW"], out["wpartials"])
-        mark(6)
-        coda.colsum_reduce(Pw, out["dgamma"])
-        mark(7)
+        for i, (_, _, call) in enumerate(stages):
+            if ev is not None:
+                ev[i].record(stream)
+            call()
+        if ev is not None:
+            ev[len(stages)].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -217,31 +253,44 @@ def bench_backward(w, args) -> dict:
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
     k_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(len(names))]
-    flops = w.gemm_flops
     g_flops = 2 * M * d * 2 * F
+    g1_flops = 2 * M * d * K1
+    flops = w.gemm_flops - (g_flops if saved else 0)          # the GEMMs executed
+    fl_of = {"gemm_swiglu_bwd": g_flops, "gemm_rmsnorm_bwd": g_flops, "gemm_wgrad": g_flops,
+             "gemm_dA": g1_flops, "gemm_wgrad_dWo": g1_flops}
+    gemm_fl = {i: fl_of[n] for i, n in enumerate(names) if n in fl_of}
+    gemms = list(gemm_fl)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    gemms = (0, 2, 5)
     dom = max(gemms, key=lambda i: k_ms[i])
     T = -(-F // 128)
     byt = {"gemm_swiglu_bwd": M * d * 2 + 2 * F * d * 2 + M * 4 + M * F * 2 + M * 2 * F * 2 + M * T * 4,
+           "swiglu_bwd_saved": M * 2 * F * 2 + M * F * 2 + M * 4 + 2 * (M * 2 * F * 2) + M * T * 4,
            "rmsnorm_bwd_reduce": M * T * 4 + 2 * M * 4,
-           "gemm_rmsnorm_bwd": M * 2 * F * 2 + d * 2 * F * 2 + M * d * 2 + M * 4 + M * d * 2,
+           "gemm_rmsnorm_bwd": M * 2 * F * 2 + d * 2 * F * 2 + M * d * 2 + M * 4 + M * d * 2
+                               + (M * d * 2 if whole else 0),
            "transpose_dz": 2 * M * 2 * F * 2,
            "transpose_h": 2 * M * d * 2,
            "gemm_wgrad": 2 * F * M * 2 + d * M * 2 + d * 4 + 2 * F * d * 2 + 2 * F * d * 4 + TW * d * 4,
            "colsum_reduce": TW * d * 4 + d * 4}
-    achieved = g_flops / (k_ms[dom] * 1e-3) / 1e12
+    if whole:
+        byt.update({"gemm_dA": M * d * 2 + K1 * d * 2 + M * K1 * 2, "transpose_dh": 2 * M * d * 2,
+                    "transpose_A": 2 * M * K1 * 2, "gemm_wgrad_dWo": d * M * 2 + K1 * M * 2 + d * K1 * 4})
+    achieved = gemm_fl[dom] / (k_ms[dom] * 1e-3) / 1e12
+    direction = "backward of the whole chain (dx_res = dh, dA, dWo, dW, dgamma)" if whole else \
+        "backward (input, weight and gamma gradients)"
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "M": M, "d": d, "F": F,
-                   "direction": "backward (input, weight and gamma gradients)", "eps": w.eps, "seed": w.seed},
-        "note": "FLOPs of the three executed GEMMs: the recomputed gate/up product, the input-gradient "
-                "product and the weight-gradient product",
+        "config": {"workload": w.name, "M": M, "K1": K1, "d": d, "F": F, "direction": direction,
+                   "pre_activation": "saved by the forward" if saved else "recomputed", "eps": w.eps,
+                   "seed": w.seed},
+        "note": "FLOPs of the executed GEMMs: " + ("" if saved else "the recomputed gate/up product, ")
+                + "the input-gradient product and the weight-gradient product"
+                + (", and the first GEMM's input- and weight-gradient products" if whole else ""),
         "kernels_ms": {n: round(t, 4) for n, t in zip(names, k_ms)},
-        "gemm_tflops": {names[i]: round(g_flops / (k_ms[i] * 1e-3) / 1e12, 1) for i in gemms},
-        "hbm_bytes_algorithmic": {"fused": sum(byt.values())},
+        "gemm_tflops": {names[i]: round(gemm_fl[i] / (k_ms[i] * 1e-3) / 1e12, 1) for i in gemms},
+        "hbm_bytes_algorithmic": {"fused": sum(byt[n] for n in names)},
         "prep_ms": round(prep_ms, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
@@ -251,61 +300,82 @@ def bench_backward(w, args) -> dict:
     }
     if args.unfused:
         # torch autograd of the unfused forward (bf16 GEMMs, element-wise RMSNorm / SwiGLU)
-        # for the same three gradients; the forward runs once outside the timed region and
-        # its saved activations are reused: this baseline does NOT recompute the gate/up
-        # product
-        hh = h.clone().requires_grad_(True)
+        # for the same gradients; the forward runs once outside the timed region and its
+        # saved activations are reused: this baseline does NOT recompute the gate/up product
         Wl = W.clone().requires_grad_(True)
         gl = gamma.clone().requires_grad_(True)
+        if whole:
+            Al, Wol, xl = A.clone().requires_grad_(True), Wo.clone().requires_grad_(True), \
+                xr.clone().requires_grad_(True)
+            hh = xl + Al @ Wol.t()
+            leaves = (Al, Wol, xl, Wl, gl)
+        else:
+            hh = h.clone().requires_grad_(True)
+            leaves = (hh, Wl, gl)
         hf = hh.float()
         n = (hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + w.eps)).to(torch.bfloat16) * gl.to(torch.bfloat16)
         z = n @ Wl.t()
         y = torch.nn.functional.silu(z[:, :F]) * z[:, F:]
+        outs, grads = ((y, hh), (dy, dres)) if whole else ((y,), (dy,))
+
+        def ubwd():
+            torch.autograd.grad(outs, leaves, grads, retain_graph=True)
+
         for _ in range(3):
-            torch.autograd.grad(y, (hh, Wl, gl), dy, retain_graph=True)
+            ubwd()
         torch.cuda.synchronize()
         s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s2.record(stream)
         for _ in range(args.steps):
-            torch.autograd.grad(y, (hh, Wl, gl), dy, retain_graph=True)
+            ubwd()
         e2.record(stream)
         torch.cuda.synchronize()
         ums = s2.elapsed_time(e2) / args.steps
         rec["unfused_torch"] = {"ms_per_step": round(ums, 4), "speedup_of_fused": round(ums / ms_per_step, 3),
-                                "note": "autograd input, weight and gamma gradients from saved activations "
-                                        "(two GEMMs)"}
+                                "note": "torch autograd of the same gradients from saved activations "
+                                        f"({4 if whole else 2} GEMMs, no recompute)"}
     if not args.no_cpu_baseline:
         import oracle
 
-        Wp_ref = oracle.fold_bf16(inp["W_t"], inp["gamma"])
         rng = np.random.default_rng(0)
         # input gradient: sampled rows (a fraction rows / M of the two GEMMs it runs);
         # weight gradients: sampled rows of dW, every column (a fraction js / 2F of the third)
+        if whole:
+            prep = oracle.prepare(inp, "bf16")
+            Wp_ref = prep["Wp"]
+        else:
+            Wp_ref = oracle.fold_bf16(inp["W_t"], inp["gamma"])
         n_rows, dt1 = 8, 0.0
         while True:
             rows = np.sort(rng.choice(M, size=min(n_rows, M), replace=False))
             t1 = time.perf_counter()
-            oracle.mlpin_bwd(inp["h"], inp["gamma"], Wp_ref, oracle.BF16, 1.0, inp["dy"], w.eps, rows=rows)
+            if whole:
+                oracle.chain_bwd(prep, inp["x_res"], inp["gamma"], inp["W_t"], inp["dy"], w.eps, dres=inp["dres"],
+                                 rows=rows)
+            else:
+                oracle.mlpin_bwd(inp["h"], inp["gamma"], Wp_ref, oracle.BF16, 1.0, inp["dy"], w.eps, rows=rows)
             dt1 = time.perf_counter() - t1
             if dt1 >= args.cpu_seconds / 4 or n_rows >= M:
                 break
             n_rows *= 2
+        hb_all = oracle.chain(prep, inp["x_res"], inp["gamma"], oracle.ACT_SWIGLU, w.eps)["hb"] if whole \
+            else inp["h"]
         n_js, dt2 = 1, 0.0
         while True:
             js = np.sort(rng.choice(2 * F, size=min(n_js, 2 * F), replace=False))
             t1 = time.perf_counter()
-            oracle.mlpin_wgrad(inp["h"], inp["gamma"], Wp_ref, oracle.BF16, 1.0, inp["W_t"], inp["dy"], w.eps,
-                               js=js)
+            oracle.mlpin_wgrad(hb_all, inp["gamma"], Wp_ref, oracle.BF16, 1.0, inp["W_t"], inp["dy"], w.eps, js=js)
             dt2 = time.perf_counter() - t1
             if dt2 >= args.cpu_seconds / 4 or n_js >= 2 * F:
                 break
             n_js *= 2
-        done = rows.size / M * 2 * g_flops + js.size / (2 * F) * g_flops
+        per_row = (2 * g_flops + (g1_flops if whole else 0)) / M       # recompute, dh (and dA) per row
+        done = rows.size * per_row + js.size / (2 * F) * g_flops
         rec["cpu_baseline"] = {"value": round(done / (dt1 + dt2) / 1e12, 6), "unit": "TFLOP/s",
                                "cores": oracle.max_threads(), "kind": "oracle",
-                               "sample": f"{rows.size} random rows of dh ({dt1:.1f} s) and {js.size} random rows "
-                                         f"of dW, all columns ({dt2:.1f} s), of the {M}-token workload (fp64, "
-                                         f"recomputed forward included)"}
+                               "sample": f"{rows.size} random rows of dh{' and dA' if whole else ''} ({dt1:.1f} s) "
+                                         f"and {js.size} random rows of dW, all columns ({dt2:.1f} s), of the "
+                                         f"{M}-token workload (fp64, recomputed forward included)"}
     return rec
 
 
@@ -358,10 +428,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, help="workload number (1-5)")
+    ap.add_argument("--workload", type=int, default=2, help="workload number (1-9)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="also time the unfused torch chain")
+    ap.add_argument("--saved-z", action="store_true",
+                    help="backward workloads: start from the pre-activation the forward saved (no recompute)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times): the "
                          "reference for scaling HBM byte counters, then exit")
@@ -399,7 +471,7 @@ def main():
     import synth_inputs as si
 
     w = si.WORKLOADS[args.workload]
-    if w.act == si.ACT_SWIGLU_BWD:
+    if w.act in (si.ACT_SWIGLU_BWD, si.ACT_CHAIN_BWD):
         print(json.dumps(bench_backward(w, args)), flush=True)
         return
     inp = si.generate(w)

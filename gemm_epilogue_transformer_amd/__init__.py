@@ -25,7 +25,8 @@ __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3"
            "gemm_rowscale_swiglu", "rope_table", "gemm_rowscale_rope", "ce_partials_per_row",
            "gemm_rowscale_ce", "ce_reduce", "rowscale_from_h", "transpose_bf16", "gemm_swiglu_bwd", "rmsnorm_bwd_reduce",
            "gemm_rmsnorm_bwd", "mlpin_bwd", "wgrad_partials_rows", "gemm_wgrad", "colsum_reduce",
-           "mlpin_wgrad", "chain", "version"]
+           "mlpin_wgrad", "gemm_bf16", "chain_bwd", "wgrad_workspace_bytes", "gemm_rowscale_swiglu_save",
+           "swiglu_bwd_saved", "chain", "version"]
 
 
 def _stream(stream):
@@ -251,14 +252,60 @@ def mlpin_bwd(h, Wp, Wpt, r, dy, dh_res=None, out=None, stream=None):
     return dh, dz, P, q
 
 
+def gemm_rowscale_swiglu_save(h, W, r, y=None, z=None, stream=None):
+    """The SwiGLU second GEMM (bf16 W [2F, K]) that also keeps the pre-activation:
+    returns (y [M, F], z [M, 2F] = r * (h . W^T) in bf16)."""
+    M, K = h.shape
+    F = W.shape[0] // 2
+    y = torch.empty((M, F), dtype=torch.bfloat16, device=h.device) if y is None else y
+    z = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=h.device) if z is None else z
+    _lib.check("coda_gemm_rowscale_swiglu_save", _lib.load().coda_gemm_rowscale_swiglu_save(
+        M, F, K, _ptr(h), _ptr(W), _ptr(r), _ptr(y), _ptr(z), _stream(stream)))
+    return y, z
+
+
+def swiglu_bwd_saved(z, dy, r, dz=None, dzt=None, partials=None, transpose=True, stream=None):
+    """SwiGLU backward from the saved z [M, 2F]: returns (dz [M, 2F] = r * dL/dz,
+    dzt [2F, M] (its transpose; None with transpose=False), partials [M, T])."""
+    M, F2 = z.shape
+    F = F2 // 2
+    T = int(_lib.load().coda_swiglu_bwd_partials_per_row(F))
+    dz = torch.empty((M, F2), dtype=torch.bfloat16, device=z.device) if dz is None else dz
+    if transpose and dzt is None:
+        dzt = torch.empty((F2, M), dtype=torch.bfloat16, device=z.device)
+    partials = torch.empty((M, T), dtype=torch.float32, device=z.device) if partials is None else partials
+    _lib.check("coda_swiglu_bwd_saved", _lib.load().coda_swiglu_bwd_saved(
+        M, F, _ptr(z), _ptr(dy), _ptr(r), _ptr(dz), _ptr(dzt if transpose else None), _ptr(partials),
+        _stream(stream)))
+    return dz, (dzt if transpose else None), partials
+
+
+def gemm_bf16(A, Bt, c_res=None, C=None, stream=None):
+    """C [M, N] = A [M, K] . Bt [N, K]^T (+ c_res) in bf16 (fp32 sums)."""
+    _esize(A, 2)
+    _esize(Bt, 2)
+    M, K = A.shape
+    N = Bt.shape[0]
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if C is None else C
+    _lib.check("coda_gemm_bf16", _lib.load().coda_gemm_bf16(
+        M, N, K, _ptr(A), _ptr(Bt), _ptr(c_res), _ptr(C), _stream(stream)))
+    return C
+
+
 def wgrad_partials_rows(NR: int) -> int:
     return int(_lib.load().coda_wgrad_partials_rows(NR))
 
 
-def gemm_wgrad(At, Bt, gamma=None, W=None, dW=None, partials=None, stream=None):
+def wgrad_workspace_bytes(NR: int, NC: int, K: int) -> int:
+    return int(_lib.load().coda_wgrad_workspace_bytes(NR, NC, K))
+
+
+def gemm_wgrad(At, Bt, gamma=None, W=None, dW=None, partials=None, workspace=None, stream=None):
     """dW [NR, NC] fp32 = gamma * (At . Bt^T), a sum over the K tokens of At [NR, K] and
     Bt [NC, K]; with the raw weight W [NR, NC] also the per-256-row-tile partials of the
-    gamma gradient sum_j W[j,k] * G[j,k] (else partials is None)."""
+    gamma gradient sum_j W[j,k] * G[j,k] (else partials is None).  Without W, a device
+    ``workspace`` (uint8 tensor) of wgrad_workspace_bytes(NR, NC, K) bytes, when that is
+    nonzero, lets the tokens be split over more blocks; workspace="auto" allocates it."""
     _esize(At, 2)
     _esize(Bt, 2)
     NR, K = At.shape
@@ -266,9 +313,15 @@ def gemm_wgrad(At, Bt, gamma=None, W=None, dW=None, partials=None, stream=None):
     dW = torch.empty((NR, NC), dtype=torch.float32, device=At.device) if dW is None else dW
     if W is not None and partials is None:
         partials = torch.empty((wgrad_partials_rows(NR), NC), dtype=torch.float32, device=At.device)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be a tensor, None or 'auto'")
+        n = wgrad_workspace_bytes(NR, NC, K) if W is None else 0
+        workspace = torch.empty(n, dtype=torch.uint8, device=At.device) if n > 0 else None
     _lib.check("coda_gemm_wgrad", _lib.load().coda_gemm_wgrad(
         NR, NC, K, _ptr(At), _ptr(Bt), _ptr(gamma), _ptr(W), _ptr(dW),
-        _ptr(partials) if W is not None else None, _stream(stream)))
+        _ptr(partials) if W is not None else None, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return dW, (partials if W is not None else None)
 
 
@@ -287,19 +340,49 @@ def mlpin_wgrad(dz, h, gamma, W, dzt=None, ht=None, out=None, stream=None):
     out = out or {}
     dzt = transpose_bf16(dz, out.get("dzt"), stream) if dzt is None else dzt
     ht = transpose_bf16(h, out.get("ht"), stream) if ht is None else ht
-    dW, P = gemm_wgrad(dzt, ht, gamma, W, out.get("dW"), out.get("wpartials"), stream)
+    dW, P = gemm_wgrad(dzt, ht, gamma, W, out.get("dW"), out.get("wpartials"), stream=stream)
     dgam = colsum_reduce(P, out.get("dgamma"), stream)
     return dW, dgam
 
 
-def chain(A, Wo_t, x_res, Wp_t, eps, act=SWIGLU, a_scale=None, wo_scale=None, wp_scale=None,
-          out=None, stream=None):
-    """The three calls in order on one stream.  Returns (h, P, r, y).
+def chain_bwd(A, WoT, h, r, Wp, Wpt, W, gamma, dy, dres=None, z=None, out=None, stream=None):
+    """Backward of the whole chain h = x_res + A . Wo^T -> r -> y = SwiGLU(r (h . W'^T))
+    from the forward's saved h and r: returns dict(dh (also the gradient of x_res), dA,
+    dWo [d, K1] fp32, dW [2F, d] fp32, dgamma [d] fp32).  WoT = Wo^T [K1, d] and
+    Wpt = W'^T [d, 2F] are the weight transposes (once per weight update); W is the raw
+    second weight, gamma the RMSNorm weight; dres the gradient reaching h through the
+    residual stream (None = 0).  With the pre-activation z saved by
+    gemm_rowscale_swiglu_save the gate/up product is not recomputed (Wp unused)."""
+    out = out or {}
+    if z is None:
+        dh, dz, _, _ = mlpin_bwd(h, Wp, Wpt, r, dy, dres, out, stream)
+        dzt = None
+    else:
+        dz, dzt, P = swiglu_bwd_saved(z, dy, r, out.get("dz"), out.get("dzt"), out.get("partials"), True, stream)
+        q = rmsnorm_bwd_reduce(P, r, h.shape[1], z.shape[1] // 2, out.get("q"), stream)
+        dh = gemm_rmsnorm_bwd(dz, Wpt, h, q, dres, out.get("dh"), stream)
+    dW, dgam = mlpin_wgrad(dz, h, gamma, W, dzt=dzt, out=out, stream=stream)
+    dA = gemm_bf16(dh, WoT, None, out.get("dA"), stream)
+    dht = transpose_bf16(dh, out.get("dht"), stream)
+    At = transpose_bf16(A, out.get("At"), stream)
+    dWo, _ = gemm_wgrad(dht, At, None, None, out.get("dWo"), None, out.get("ws", "auto"), stream)
+    return dict(dh=dh, dA=dA, dWo=dWo, dW=dW, dgamma=dgam)
 
-    ``out`` may hold preallocated h, partials, r, y tensors (dict)."""
+
+def chain(A, Wo_t, x_res, Wp_t, eps, act=SWIGLU, a_scale=None, wo_scale=None, wp_scale=None,
+          out=None, stream=None, save_z=False):
+    """The three calls in order on one stream.  Returns (h, P, r, y), and z last with
+    save_z=True (bf16 SwiGLU only: the pre-activation a backward can start from).
+
+    ``out`` may hold preallocated h, partials, r, y, z tensors (dict)."""
     out = out or {}
     h, P = gemm_resid_partialrms(A, Wo_t, x_res, a_scale, wo_scale, out.get("h"),
                                  out.get("partials"), stream)
     r = rowscale_reduce(P, Wo_t.shape[0], eps, out.get("r"), stream)
+    if save_z:
+        if act != SWIGLU or wp_scale is not None:
+            raise ValueError("save_z needs the bf16 SwiGLU chain")
+        y, z = gemm_rowscale_swiglu_save(h, Wp_t, r, out.get("y"), out.get("z"), stream)
+        return h, P, r, y, z
     y = gemm_rowscale_swiglu(h, Wp_t, r, act, wp_scale, out.get("y"), stream)
     return h, P, r, y

@@ -36,8 +36,12 @@ SIGNATURES = {
     "coda_gemm_swiglu_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "coda_rmsnorm_bwd_reduce": (_I, [_I64, _I64, _I64, _P, _P, _P, _P]),
     "coda_gemm_rmsnorm_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "coda_gemm_rowscale_swiglu_save": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "coda_swiglu_bwd_saved": (_I, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "coda_gemm_bf16": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "coda_wgrad_partials_rows": (_I64, [_I64]),
-    "coda_gemm_wgrad": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "coda_wgrad_workspace_bytes": (_I64, [_I64, _I64, _I64]),
+    "coda_gemm_wgrad": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I64, _P]),
     "coda_colsum_reduce": (_I, [_I64, _I64, _P, _P, _P]),
     "coda_status_string": (C.c_char_p, [_I]),
     "coda_last_hip_error": (_I, []),

@@ -339,11 +339,69 @@ coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* d
                                                     as_stream(stream)));
 }
 
+coda_status coda_gemm_rowscale_swiglu_save(int64_t M, int64_t F, int64_t K, const void* h, const void* W,
+                                           const float* r, void* y, void* z, void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(F, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (F % 8 != 0 || K % 8 != 0 || 2 * F > kMaxRow || K > kMaxRow) return CODA_ERR_SHAPE;
+    if (!prod_ok(M, K) || !prod_ok(2 * F, K) || !prod_ok(M, 2 * F)) return CODA_ERR_SHAPE;
+    if (coda::gemm3_tiles(M, F, true) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!h || !W || !r || !y || !z) return CODA_ERR_NULL;
+    if (!aligned16(h) || !aligned16(W) || !aligned16(r) || !aligned16(y) || !aligned16(z)) return CODA_ERR_ALIGN;
+    const Range ry = span(y, M * F * 2), rz = span(z, M * 2 * F * 2);
+    if (overlap(ry, rz)) return CODA_ERR_ALIAS;
+    const Range ins[] = {span(h, M * K * 2), span(W, 2 * F * K * 2), span(r, M * 4)};
+    for (const Range& in : ins)
+        if (overlap(ry, in) || overlap(rz, in)) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_rowscale_swiglu_save(int(M), int(F), int(K), h, W, r, y, z,
+                                                             as_stream(stream)));
+}
+
+coda_status coda_swiglu_bwd_saved(int64_t M, int64_t F, const void* z, const void* dy, const float* r, void* dz,
+                                  void* dzt, float* partials, void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(F, 1) || F % 8 != 0 || 2 * F > kMaxRow) return CODA_ERR_SHAPE;
+    if (dzt && M % 8 != 0) return CODA_ERR_SHAPE;
+    const int64_t T = coda::swiglu_bwd_partials_per_row(F);
+    if (!prod_ok(M, 2 * F) || !prod_ok(M, T) || ((M + 63) / 64) * T > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!z || !dy || !r || !dz || !partials) return CODA_ERR_NULL;
+    if (!aligned16(z) || !aligned16(dy) || !aligned16(dz) || (dzt && !aligned16(dzt))) return CODA_ERR_ALIGN;
+    const Range rd = span(dz, M * 2 * F * 2), rp = span(partials, M * T * 4);
+    const Range rt = dzt ? span(dzt, M * 2 * F * 2) : span(nullptr, 0);
+    if (overlap(rd, rp) || overlap(rd, rt) || overlap(rp, rt)) return CODA_ERR_ALIAS;
+    const Range ins[] = {span(z, M * 2 * F * 2), span(dy, M * F * 2), span(r, M * 4)};
+    for (const Range& in : ins)
+        if (overlap(rd, in) || overlap(rp, in) || overlap(rt, in)) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_swiglu_bwd_saved(int(M), int(F), z, dy, r, dz, dzt, partials,
+                                                    as_stream(stream)));
+}
+
+coda_status coda_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* Bt, const void* c_res,
+                           void* C, void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(N, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (N % 8 != 0 || K % 8 != 0 || N > kMaxRow || K > kMaxRow) return CODA_ERR_SHAPE;
+    if (!prod_ok(M, K) || !prod_ok(N, K) || !prod_ok(M, N)) return CODA_ERR_SHAPE;
+    if (coda::gemm_bwd2_tiles(M, N) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!A || !Bt || !C) return CODA_ERR_NULL;
+    if (!aligned16(A) || !aligned16(Bt) || !aligned16(C) || (c_res && !aligned16(c_res))) return CODA_ERR_ALIGN;
+    const Range ro = span(C, M * N * 2);
+    if (overlap(ro, span(A, M * K * 2)) || overlap(ro, span(Bt, N * K * 2))) return CODA_ERR_ALIAS;
+    if (c_res && c_res != C && overlap(ro, span(c_res, M * N * 2))) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_rmsnorm_bwd(int(M), int(N), int(K), A, Bt, nullptr, nullptr, c_res, C,
+                                                    as_stream(stream)));
+}
+
 int64_t coda_wgrad_partials_rows(int64_t NR) { return NR < 1 || NR > kMaxDim ? -1 : coda::wgrad_partials_rows(NR); }
+
+int64_t coda_wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K) {
+    if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0) || !prod_ok(NR, NC)) return -1;
+    return coda::wgrad_workspace_bytes(NR, NC, K);
+}
 
 coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, const void* Bt,
                             const float* gamma, const void* W, float* dW, float* partials,
-                            void* stream) {
+                            void* workspace, int64_t workspace_bytes, void* stream) {
     if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0)) return CODA_ERR_SHAPE;
     if (NC % 8 != 0 || K % 8 != 0 || K > kMaxRow || NC > kMaxRow / 2) return CODA_ERR_SHAPE;
     const int64_t T = coda::wgrad_partials_rows(NR);
@@ -353,19 +411,23 @@ coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, c
     if (!aligned16(dW) || (W && !aligned16(W)) || (gamma && !aligned16(gamma)) || (partials && !aligned16(partials)) ||
         (K > 0 && (!aligned16(At) || !aligned16(Bt))))
         return CODA_ERR_ALIGN;
+    if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return CODA_ERR_VALUE;
+    if (workspace && !aligned16(workspace)) return CODA_ERR_ALIGN;
     const Range ro = span(dW, NR * NC * 4), rp = W ? span(partials, T * NC * 4) : span(nullptr, 0);
-    if (W && overlap(ro, rp)) return CODA_ERR_ALIAS;
+    const Range rw = workspace ? span(workspace, workspace_bytes) : span(nullptr, 0);
+    if ((W && overlap(ro, rp)) || overlap(ro, rw) || overlap(rp, rw)) return CODA_ERR_ALIAS;
     const Range ins[] = {K > 0 ? span(At, NR * K * 2) : span(nullptr, 0), K > 0 ? span(Bt, NC * K * 2) : span(nullptr, 0),
                          gamma ? span(gamma, NC * 4) : span(nullptr, 0), W ? span(W, NR * NC * 2) : span(nullptr, 0)};
     for (const Range& in : ins)
-        if (overlap(ro, in) || (W && overlap(rp, in))) return CODA_ERR_ALIAS;
+        if (overlap(ro, in) || (W && overlap(rp, in)) || overlap(rw, in)) return CODA_ERR_ALIAS;
     hipStream_t s = as_stream(stream);
     if (K == 0) {
         hipError_t e = coda::launch_fill_zero_f32(NR * NC, dW, s);
         if (e == hipSuccess && W) e = coda::launch_fill_zero_f32(T * NC, partials, s);
         return hip_status(e);
     }
-    return hip_status(coda::launch_gemm_wgrad(int(NR), int(NC), int(K), At, Bt, gamma, W, dW, W ? partials : nullptr, s));
+    return hip_status(coda::launch_gemm_wgrad(int(NR), int(NC), int(K), At, Bt, gamma, W, dW, W ? partials : nullptr,
+                                              static_cast<float*>(workspace), workspace_bytes, s));
 }
 
 coda_status coda_colsum_reduce(int64_t T, int64_t NC, const float* partials, float* out, void* stream) {

@@ -9,7 +9,8 @@
 // row scale it is applied in the epilogue of the GEMM that produces the other term
 // (kucoin page, section "CODA: El epilogo esconde un tesoro": the reparameterisation
 // holds for the backward pass).  dh_res is the gradient that reaches h through the
-// residual stream (may be NULL).  Mainloop and tiles as the first GEMM; per 32-row slab
+// residual stream (may be NULL).  With h and q both NULL the same kernel is the plain
+// product C = A . B^T (+ C_res) in bf16: the first GEMM's input gradient.  Mainloop and tiles as the first GEMM; per 32-row slab
 // the accumulators are staged row-major in LDS and every lane takes runs of 8 columns:
 // 16-byte loads of h and dh_res (one slab ahead), fp32 arithmetic, one bf16 rounding,
 // one 16-byte store.
@@ -46,7 +47,7 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
 #pragma unroll
     for (int i = 0; i < WM / 64; ++i) {
         const int m = m0 + wm * WM + 64 * i + (threadIdx.x & 63);
-        qv[i] = m < M ? Q[m] : 0.0f;
+        qv[i] = (Q != nullptr && m < M) ? Q[m] : 0.0f;
     }
 
     const int kbytes = K * 2;
@@ -74,7 +75,8 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
     const int valid_rows = min(BM, M - m0);
     const uint32_t row_bytes = static_cast<uint32_t>(N) * 2;
     const size_t tile_off = static_cast<size_t>(m0) * N;
-    const __amdgpu_buffer_rsrc_t h_rsrc = make_buffer_rsrc(Hb + tile_off, valid_rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t h_rsrc =
+        make_buffer_rsrc(Hb ? Hb + tile_off : DH + tile_off, Hb ? valid_rows * row_bytes : 0u);
     const __amdgpu_buffer_rsrc_t r_rsrc =
         make_buffer_rsrc(DHres ? DHres + tile_off : Hb + tile_off, DHres ? valid_rows * row_bytes : 0u);
     const __amdgpu_buffer_rsrc_t o_rsrc = make_buffer_rsrc(DH + tile_off, valid_rows * row_bytes);

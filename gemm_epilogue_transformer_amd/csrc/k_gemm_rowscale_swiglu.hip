@@ -28,7 +28,7 @@
 
 namespace coda {
 
-enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3, kActSwigluBwd = 4 };
+enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3, kActSwigluBwd = 4, kActSwigluSave = 5 };
 
 // RoPE operands (unused by the other activations).
 struct RopeArgs {
@@ -240,6 +240,77 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN
     }
 }
 
+// SwiGLU forward that also keeps the pre-activation for a backward without recompute:
+// y = silu(g) * u as in the plain SwiGLU epilogue (the same fp32 operations, so the same
+// bits) and z = [g | u] = r * (h . W'^T) rounded to bf16, z [M, 2F] (gate columns, then
+// up).  The unscaled accumulators are staged in LDS; each lane takes 8 gate columns of a
+// row and the matching 8 up columns (the backward epilogue's walk): three 16-byte stores.
+template <int BM, int BN, int WAVES_M, int TM, int TN>
+__device__ __forceinline__ void swiglu_save_epilogue(const f32x16_t (&acc)[TM][TN],
+                                                     const float (&rv)[BM / WAVES_M / 64], float sw,
+                                                     uint16_t* __restrict__ Y, uint16_t* __restrict__ Z, int M,
+                                                     int F, int m0, int j0, int wm, int wn, uint8_t* slab) {
+    constexpr int WM = BM / WAVES_M;
+    constexpr int NB = TN / 2;
+    constexpr int kGseg = NB * 4;
+    constexpr int kSegPerLane = 32 * kGseg / 64;
+    using S = Slab<TN>;
+    const int lane = threadIdx.x & 63;
+    const int valid_rows = min(BM, M - m0);
+    const uint32_t y_row = static_cast<uint32_t>(F) * 2, z_row = static_cast<uint32_t>(F) * 4;
+    const __amdgpu_buffer_rsrc_t y_rsrc =
+        make_buffer_rsrc(Y + static_cast<size_t>(m0) * F, static_cast<uint32_t>(valid_rows) * y_row);
+    const __amdgpu_buffer_rsrc_t z_rsrc =
+        make_buffer_rsrc(Z + static_cast<size_t>(m0) * 2 * F, static_cast<uint32_t>(valid_rows) * z_row);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        float v[TN][16];
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[b][i] = acc[tm][b][i];
+        S::put(slab, v);
+#pragma unroll
+        for (int jj = 0; jj < kSegPerLane; ++jj) {
+            const int q = lane + 64 * jj;
+            const int row = q / kGseg, gcol = (q % kGseg) * 8;
+            const int col = j0 + wn * NB * 32 + gcol;
+            const float rr = __shfl(rv[tm / 2], (tm % 2) * 32 + row) * sw;
+            const uint8_t* sp = slab + row * S::kStride;
+            const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(sp + gcol * 4);
+            const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(sp + gcol * 4 + 16);
+            const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(sp + (NB * 32 + gcol) * 4);
+            const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(sp + (NB * 32 + gcol) * 4 + 16);
+            const float ag[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+            const float au[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+            float yv[8], gv[8], uv[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                gv[k] = ag[k] * rr;
+                uv[k] = au[k] * rr;
+                yv[k] = gv[k] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[k])) * uv[k];
+            }
+            const bool in_range = col < F;
+            const uint32_t trow = static_cast<uint32_t>(wm * WM + tm * 32 + row);
+            const uint32_t vy = in_range ? trow * y_row + static_cast<uint32_t>(col) * 2 : kOobOffset;
+            const uint32_t vg = in_range ? trow * z_row + static_cast<uint32_t>(col) * 2 : kOobOffset;
+            const uint32_t vu = in_range ? trow * z_row + static_cast<uint32_t>(F + col) * 2 : kOobOffset;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                i32x4_t{int(pack_bf16x2(yv[0], yv[1])), int(pack_bf16x2(yv[2], yv[3])),
+                        int(pack_bf16x2(yv[4], yv[5])), int(pack_bf16x2(yv[6], yv[7]))},
+                y_rsrc, vy, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                i32x4_t{int(pack_bf16x2(gv[0], gv[1])), int(pack_bf16x2(gv[2], gv[3])),
+                        int(pack_bf16x2(gv[4], gv[5])), int(pack_bf16x2(gv[6], gv[7]))},
+                z_rsrc, vg, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                i32x4_t{int(pack_bf16x2(uv[0], uv[1])), int(pack_bf16x2(uv[2], uv[3])),
+                        int(pack_bf16x2(uv[4], uv[5])), int(pack_bf16x2(uv[6], uv[7]))},
+                z_rsrc, vu, 0, 0);
+        }
+    }
+}
+
 // Epilogue shared by the bf16 and 8-bit weight instantiations.  Wave (wm, wn) holds TM x TN 32x32 accumulator blocks;
 // with SwiGLU, blocks [0, TN/2) are gate columns and [TN/2, TN) the matching up columns.
 // Per 32-row slab: r (times sw) is applied lane-locally to both accumulators before the
@@ -360,7 +431,7 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
                        uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
                        int tiles_n, RopeArgs rope, CeArgs ce, BwdArgs bw) {
     // the backward recomputes the forward's gate / up product: same B panel layout
-    constexpr bool SWIGLU = ACT == kActSwiglu || ACT == kActSwigluBwd;
+    constexpr bool SWIGLU = ACT == kActSwiglu || ACT == kActSwigluBwd || ACT == kActSwigluSave;
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -451,6 +522,8 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     else if constexpr (ACT == kActSwigluBwd)
         swiglu_bwd_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, bw, M, N_out, m0, j0, tile_n, wm, wn, slab,
                                                               ce_red);
+    else if constexpr (ACT == kActSwigluSave)
+        swiglu_save_epilogue<BM, BN, WAVES_M, TM, TN>(acc, rv, sw, Y, bw.dz, M, N_out, m0, j0, wm, wn, slab);
     else
         rowscale_epilogue<BM, BN, WAVES_M, TM, TN, ACT>(acc, rv, pv, rope, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
@@ -488,7 +561,7 @@ template <int ACT, bool WFP8>
 static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                           const float* w_scale, const float* r, void* y, const RopeArgs& rope,
                           const CeArgs& ce, const BwdArgs& bw, hipStream_t stream) {
-    constexpr int BNO = (ACT == kActSwiglu || ACT == kActSwigluBwd) ? BN3 / 2 : BN3;
+    constexpr int BNO = (ACT == kActSwiglu || ACT == kActSwigluBwd || ACT == kActSwigluSave) ? BN3 / 2 : BN3;
     const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BNO - 1) / BNO;
     const dim3 grid(tiles_m * tiles_n), block(64 * WM3 * WN3);
     hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, WFP8 ? 0 : PIPE3,
@@ -532,6 +605,14 @@ hipError_t launch_gemm_rowscale_ce(int M, int V, int K, const void* h, const voi
     const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
     return w_fp8 ? launch3<kActCe, true>(M, V, K, h, W, w_scale, r, nullptr, none, ce, no_bw, stream)
                  : launch3<kActCe, false>(M, V, K, h, W, w_scale, r, nullptr, none, ce, no_bw, stream);
+}
+
+hipError_t launch_gemm_rowscale_swiglu_save(int M, int F, int K, const void* h, const void* W, const float* r,
+                                            void* y, void* z, hipStream_t stream) {
+    const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
+    const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
+    const BwdArgs save{nullptr, static_cast<uint16_t*>(z), nullptr, 0};   // dz carries z
+    return launch3<kActSwigluSave, false>(M, F, K, h, W, nullptr, r, y, none, no_ce, save, stream);
 }
 
 int64_t swiglu_bwd_partials_per_row(int64_t F) { return F < 1 ? -1 : (F + BN3 / 2 - 1) / (BN3 / 2); }

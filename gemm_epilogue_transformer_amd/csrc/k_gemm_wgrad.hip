@@ -23,11 +23,14 @@
 
 namespace coda {
 
+// Split over the tokens (S > 1, only without W): block (s, tile) sums tokens
+// [s * k_split, min((s + 1) * k_split, K)) and writes its raw sums (no gamma) to slice s
+// of dW, which is then the [S, NR, NC] workspace that k_splitk_reduce adds up.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, const float* __restrict__ gamma,
              const uint16_t* __restrict__ Wraw, float* __restrict__ dW, float* __restrict__ Pg, int NR, int NC,
-             int K, int tiles_m, int tiles_n) {
+             int K, int tiles_m, int tiles_n, int k_split) {
     constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -39,17 +42,22 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
 #pragma unroll
     for (int i = 0; i < NS; ++i) st[i] = stages[i];
 
+    const int tiles = tiles_m * tiles_n;
+    const int split = blockIdx.x / tiles;
     int tile_m, tile_n;
-    tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+    tile_coords<8>(blockIdx.x - split * tiles, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
+    // rows are K tokens apart; this block reads tokens [k0, k0 + kext) of each (the
+    // descriptors start at token k0, the mainloop stops at kext)
     const int kbytes = K * 2;
+    const int k0 = split * k_split, kext = min(k_split, K - k0) * 2;
     DmaPanel<BM, BM, NW, RB> pa;
     DmaPanel<BN, BN, NW, RB> pb;
-    const uint8_t* a0 = At + static_cast<size_t>(m0) * kbytes;
-    const uint8_t* b0 = Bt + static_cast<size_t>(n0) * kbytes;
+    const uint8_t* a0 = At + static_cast<size_t>(m0) * kbytes + static_cast<size_t>(k0) * 2;
+    const uint8_t* b0 = Bt + static_cast<size_t>(n0) * kbytes + static_cast<size_t>(k0) * 2;
     pa.init(a0, min(BM, NR - m0), a0, 0, kbytes);
     pb.init(b0, min(BN, NC - n0), b0, 0, kbytes);
     auto a_row = [&](int tm) { return wm * WM + tm * 32; };
@@ -63,7 +71,8 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    mainloop_dma<Elt::BF16, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
+    mainloop_dma<Elt::BF16, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kext, st, a_row, b_row);
+    dW += static_cast<size_t>(split) * NR * NC;
 
     using S = Slab<TN>;
     static_assert(64 % S::kSegPerRow == 0, "a lane's segments share their columns");
@@ -146,6 +155,23 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
     }
 }
 
+// dW[i] = gamma[i % NC] * sum_s ws[s, i]  (fixed order s = 0, 1, ...; fp32), 4 per thread
+__global__ void __launch_bounds__(256)
+k_splitk_reduce(const f32x4_t* __restrict__ ws, const float* __restrict__ gamma, f32x4_t* __restrict__ dW,
+                int64_t n4, int NC4, int S) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        f32x4_t a = ws[i];
+        for (int s = 1; s < S; ++s) a += ws[static_cast<int64_t>(s) * n4 + i];
+        if (gamma) {
+            const int c = static_cast<int>(i % NC4) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] *= gamma[c + e];
+        }
+        dW[i] = a;
+    }
+}
+
 // dgamma[k] = fl32( sum_t Pg[t, k] )  (fixed order, fp64), one thread per column
 __global__ void __launch_bounds__(256)
 k_colsum_reduce(const float* __restrict__ Pg, float* __restrict__ out, int T, int NC) {
@@ -179,14 +205,41 @@ constexpr int BMW = CODA_WG_BM, BNW = CODA_WG_BN;
 int64_t wgrad_tiles(int64_t NR, int64_t NC) { return ((NR + BMW - 1) / BMW) * ((NC + BNW - 1) / BNW); }
 int64_t wgrad_partials_rows(int64_t NR) { return NR < 1 ? -1 : (NR + BMW - 1) / BMW; }
 
+// Token splits for a problem of `tiles` output tiles: enough blocks for the 256 CUs
+// (one 256 x 256 tile each at a time), each split at least kMinSplitTokens tokens.
+constexpr int kMinSplitTokens = 2048, kMaxSplits = 16;
+int wgrad_splits(int64_t NR, int64_t NC, int64_t K) {
+    const int64_t tiles = wgrad_tiles(NR, NC);
+    int64_t S = (256 + tiles - 1) / tiles;
+    S = std::min<int64_t>(S, std::max<int64_t>(1, K / kMinSplitTokens));
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(S, kMaxSplits)));
+}
+int64_t wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K) {
+    const int S = wgrad_splits(NR, NC, K);
+    return S > 1 ? static_cast<int64_t>(S) * NR * NC * 4 : 0;
+}
+
 hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
-                             const void* Wraw, float* dW, float* Pg, hipStream_t stream) {
+                             const void* Wraw, float* dW, float* Pg, float* ws, int64_t ws_bytes,
+                             hipStream_t stream) {
     const int tiles_m = (NR + BMW - 1) / BMW, tiles_n = (NC + BNW - 1) / BNW;
-    const dim3 grid(tiles_m * tiles_n), block(64 * CODA_WG_WM * CODA_WG_WN);
+    int S = Wraw ? 1 : wgrad_splits(NR, NC, K);
+    if (S > 1 && (ws == nullptr || ws_bytes < static_cast<int64_t>(S) * NR * NC * 4)) S = 1;
+    // tokens per split: a multiple of the 64-token k-step
+    const int k_split = S > 1 ? ((K + S - 1) / S + 63) / 64 * 64 : K;
+    S = (K + k_split - 1) / k_split;
+    const dim3 grid(tiles_m * tiles_n * S), block(64 * CODA_WG_WM * CODA_WG_WN);
     hipLaunchKernelGGL((k_gemm_wgrad<BMW, BNW, CODA_WG_WM, CODA_WG_WN, CODA_WG_NS, CODA_WG_RB, CODA_WG_SPREAD,
                                      CODA_WG_OCC>),
                        grid, block, 0, stream, static_cast<const uint8_t*>(At), static_cast<const uint8_t*>(Bt),
-                       gamma, static_cast<const uint16_t*>(Wraw), dW, Pg, NR, NC, K, tiles_m, tiles_n);
+                       S > 1 ? nullptr : gamma, static_cast<const uint16_t*>(Wraw), S > 1 ? ws : dW, Pg, NR, NC,
+                       K, tiles_m, tiles_n, k_split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    const int64_t n4 = static_cast<int64_t>(NR) * NC / 4;
+    const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       reinterpret_cast<const f32x4_t*>(ws), gamma, reinterpret_cast<f32x4_t*>(dW), n4, NC / 4, S);
     return hipGetLastError();
 }
 

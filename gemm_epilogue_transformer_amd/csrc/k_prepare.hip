@@ -149,7 +149,52 @@ k_transpose_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, i
     }
 }
 
+// The same for R % 8 == 0 and C % 8 == 0 (16-byte rows on both sides): a 128 x 64 tile,
+// 16-byte loads of 8 columns of a source row, 16-byte stores of 8 rows of a destination
+// row (the destination row's 128 tile rows = 256 contiguous bytes per tile).  LDS rows
+// padded to 72 elements (16-byte aligned); the transposed reads of a wave take one
+// element from each of 64 consecutive columns of a row: conflict-free.
+constexpr int kTrR = 128, kTrC = 64, kTrPad = 72;
+__global__ void __launch_bounds__(256)
+k_transpose16_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t R, int64_t C,
+                   int64_t tiles_c) {
+    __shared__ __attribute__((aligned(16))) uint16_t t[kTrR][kTrPad];
+    const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
+    const int64_t r0 = tr * kTrR, c0 = tc * kTrC;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kTrR * kTrC / 8 / 256; ++i) {
+        const int idx = tid + 256 * i;
+        const int rr = idx >> 3, ch = idx & 7;       // tile row, 8-column chunk
+        const int64_t r = r0 + rr, c = c0 + 8 * ch;
+        i32x4_t v = {0, 0, 0, 0};
+        if (r < R && c < C) v = *reinterpret_cast<const i32x4_t*>(src + r * C + c);
+        *reinterpret_cast<i32x4_t*>(&t[rr][8 * ch]) = v;
+    }
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t c = c0 + lane;
+#pragma unroll
+    for (int i = 0; i < kTrR / 8 / 4; ++i) {
+        const int rc = wave + 4 * i;                 // 8-row chunk of the tile
+        const int64_t r = r0 + 8 * rc;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = static_cast<uint32_t>(t[8 * rc + 2 * e][lane]) |
+                   (static_cast<uint32_t>(t[8 * rc + 2 * e + 1][lane]) << 16);
+        if (c < C && r < R)
+            *reinterpret_cast<i32x4_t*>(dst + c * R + r) = i32x4_t{int(w[0]), int(w[1]), int(w[2]), int(w[3])};
+    }
+}
+
 hipError_t launch_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, hipStream_t stream) {
+    if (R % 8 == 0 && C % 8 == 0) {
+        const int64_t tiles_r = (R + kTrR - 1) / kTrR, tiles_c = (C + kTrC - 1) / kTrC;
+        hipLaunchKernelGGL(k_transpose16_bf16, dim3(static_cast<unsigned>(tiles_r * tiles_c)), dim3(256), 0,
+                           stream, static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C, tiles_c);
+        return hipGetLastError();
+    }
     const int64_t tiles_r = (R + 63) / 64, tiles_c = (C + 63) / 64;
     hipLaunchKernelGGL(k_transpose_bf16, dim3(static_cast<unsigned>(tiles_r * tiles_c)), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C, tiles_c);

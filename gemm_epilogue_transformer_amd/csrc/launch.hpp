@@ -58,12 +58,20 @@ hipError_t launch_gemm_rmsnorm_bwd(int M, int N, int K, const void* dz, const vo
                                    const float* q, const void* dh_res, void* dh, hipStream_t stream);
 hipError_t launch_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, hipStream_t stream);
 
+// SwiGLU forward that keeps the pre-activation, and the backward that starts from it.
+hipError_t launch_gemm_rowscale_swiglu_save(int M, int F, int K, const void* h, const void* W, const float* r,
+                                            void* y, void* z, hipStream_t stream);
+hipError_t launch_swiglu_bwd_saved(int M, int F, const void* z, const void* dy, const float* r, void* dz,
+                                   void* dzt, float* partials, hipStream_t stream);
+
 // Weight gradients: token-contracting GEMM with the gamma column scale and the column
 // partials of the gamma gradient, and their fixed-order column sum.
 int64_t wgrad_tiles(int64_t NR, int64_t NC);
 int64_t wgrad_partials_rows(int64_t NR);
+int64_t wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K);
 hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
-                             const void* Wraw, float* dW, float* Pg, hipStream_t stream);
+                             const void* Wraw, float* dW, float* Pg, float* ws, int64_t ws_bytes,
+                             hipStream_t stream);
 hipError_t launch_colsum_reduce(int T, int NC, const float* Pg, float* out, hipStream_t stream);
 hipError_t launch_fill_zero_f32(int64_t n, float* dst, hipStream_t stream);
 

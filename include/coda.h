@@ -277,6 +277,38 @@ coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* d
                                   const void* h, const float* q, const void* dh_res, void* dh,
                                   void* stream);
 
+/* ------------------------------ backward from a saved pre-activation ---- */
+/* A forward that keeps the pre-activation lets the backward skip the recomputed gate/up
+ * product (memory for time: z is M x 2F bf16).  Same block and same gradients as above.  */
+
+/* The SwiGLU second GEMM of coda_gemm_rowscale_swiglu (bf16 weights) that also writes
+ *   z [M, 2F] bf16 = bf16_rne( r[m] * sum_k h[m,k] W[j,k] )   (gate columns, then up)
+ * y [M, F] is bit-identical to coda_gemm_rowscale_swiglu's.  h [M, K], W [2F, K] bf16,
+ * r [M] fp32.  Granules: K % 8 == 0, F % 8 == 0.  y, z must not overlap each other or
+ * the inputs.                                                                          */
+coda_status coda_gemm_rowscale_swiglu_save(int64_t M, int64_t F, int64_t K, const void* h, const void* W,
+                                           const float* r, void* y, void* z, void* stream);
+
+/* SwiGLU backward from the saved z, with g = z[m, j], u = z[m, F+j], d = dy[m, j]:
+ *   dz [M, 2F] bf16, written: bf16_rne( r[m] * dL/dz )  (as coda_gemm_swiglu_bwd)
+ *   dzt [2F, M] bf16 or NULL: the transpose of dz (the weight gradient's operand);
+ *       needs M % 8 == 0
+ *   partials [M, coda_swiglu_bwd_partials_per_row(F)] fp32: per tile of 128 gate
+ *       columns, (1/r[m]) * sum of dL/dz * z, the layout coda_rmsnorm_bwd_reduce takes
+ * Granule: F % 8 == 0.  Outputs must not overlap each other or the inputs.            */
+coda_status coda_swiglu_bwd_saved(int64_t M, int64_t F, const void* z, const void* dy, const float* r, void* dz,
+                                  void* dzt, float* partials, void* stream);
+
+/* Plain product with an optional residual, bf16 out (the first GEMM's input gradient
+ * dA = dh . Wo, with Bt = Wo^T passed K-contiguous; the same kernel as
+ * coda_gemm_rmsnorm_bwd without the row-scale term):
+ *   C[m,n] = bf16_rne( sum_k A[m,k] Bt[n,k] + c_res[m,n] )    (fp32 MFMA sums)
+ *   A [M, K] bf16;  Bt [N, K] bf16;  c_res [M, N] bf16 or NULL, may be EXACTLY C
+ *   C [M, N] bf16, written; must not overlap A or Bt
+ * Granules: N % 8 == 0, K % 8 == 0.                                                   */
+coda_status coda_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* Bt, const void* c_res,
+                           void* C, void* stream);
+
 /* --------------------------------------------- backward: weight gradients ---- */
 /* Weight gradients of the same block (kucoin page, section "CODA: El epilogo esconde un
  * tesoro": the backward inherits the forward's structure; section "Cinco bloques y un
@@ -291,17 +323,28 @@ coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* d
 /* Partial rows written by coda_gemm_wgrad for NR gradient rows; -1 if NR < 1.          */
 int64_t coda_wgrad_partials_rows(int64_t NR);
 
+/* Workspace bytes that let coda_gemm_wgrad (without W) split the K tokens over more
+ * blocks when the NR x NC output has too few 256 x 256 tiles to fill the GPU; 0 when no
+ * split helps; -1 for invalid sizes.                                                   */
+int64_t coda_wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K);
+
 /* Weight-gradient GEMM, contraction over K tokens:
  *   At [NR, K] bf16 (e.g. (r * dL/dz)^T, NR = 2F);  Bt [NC, K] bf16 (e.g. h^T, NC = d)
  *   gamma [NC] fp32 or NULL (= 1);  W [NR, NC] bf16 raw weight or NULL (no partials)
  *   dW [NR, NC] fp32, written: fl32( gamma[k] * sum_m At[j,m] Bt[k,m] )  (fp32 MFMA sums)
  *   partials [coda_wgrad_partials_rows(NR), NC] fp32, written when W is given: per tile
  *       of 256 rows j, sum of W[j,k] * G[j,k] (fixed order); may be NULL when W is NULL
+ *   workspace: device scratch of workspace_bytes (NULL / 0 for none), 16-byte aligned.
+ *       Without W, and with at least coda_wgrad_workspace_bytes(NR, NC, K) bytes, the
+ *       tokens are split over several blocks per tile whose fp32 sums are added in a
+ *       fixed order (then gamma applied): the result is reproducible for the same
+ *       arguments but its last bits depend on whether the split was taken.
  * K = 0 (no tokens) writes zeros.  Granules: K % 8 == 0, NC % 8 == 0; K <= 2^22,
- * NC <= 2^21.  Outputs must not overlap each other or the inputs.                    */
+ * NC <= 2^21.  Outputs and workspace must not overlap each other or the inputs.
+ * CODA_ERR_VALUE: workspace_bytes < 0, or > 0 with a NULL workspace.                 */
 coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, const void* Bt,
                             const float* gamma, const void* W, float* dW, float* partials,
-                            void* stream);
+                            void* workspace, int64_t workspace_bytes, void* stream);
 
 /* out[k] = fl32( sum_t partials[t, k] )  (fixed order, fp64 inside), T >= 1 rows of NC
  * columns: the gamma gradient from coda_gemm_wgrad's partials.  out must not overlap.  */

@@ -35,6 +35,7 @@ ACT_SWIGLU = 1
 ACT_ROPE = 2      # rotary position embedding on the QKV product (no activation)
 ACT_CE = 3        # cross-entropy of the LM-head product against per-row targets
 ACT_SWIGLU_BWD = 4  # backward of the RMSNorm -> GEMM -> SwiGLU block (no first GEMM)
+ACT_CHAIN_BWD = 5   # backward of the whole chain (first GEMM + residual included)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -66,6 +67,9 @@ class Workload:
         the weight-gradient product (all three of shape M x d x 2F)."""
         if self.act == ACT_SWIGLU_BWD:
             return 3 * (2 * self.M * self.d * self.N2w)
+        if self.act == ACT_CHAIN_BWD:
+            # plus the first GEMM's input-gradient and weight-gradient products
+            return 3 * (2 * self.M * self.d * self.N2w) + 2 * (2 * self.M * self.K1 * self.d)
         return 2 * self.M * self.K1 * self.d + 2 * self.M * self.d * self.N2w
 
 
@@ -79,7 +83,9 @@ class Workload:
 # 128256-token vocabulary -- ending in the cross-entropy loss against uniform targets;
 # 8: the backward of workload 2's second half -- the input, weight and gamma gradients
 # of the RMSNorm -> gate/up GEMM -> SwiGLU block -- with the block input h and the
-# upstream gradient dy drawn directly (no first GEMM).
+# upstream gradient dy drawn directly (no first GEMM); 9: the backward of workload 2's
+# whole chain (same forward draws as workload 2, then dy and the residual-stream
+# gradient dres).
 WORKLOADS = {
     1: Workload("tiny_m128_d256_n512_none", 128, 256, 256, 512, ACT_NONE, "bf16", 1e-5, 1001),
     2: Workload("llama1b_attnout_mlpin_m16384", 16384, 2048, 2048, 16384, ACT_SWIGLU, "bf16", 1e-5, 1002),
@@ -90,13 +96,14 @@ WORKLOADS = {
                 rot_cols=2560, seq_len=4096),
     7: Workload("llama1b_mlpout_lmhead_ce_m16384", 16384, 8192, 2048, 128256, ACT_CE, "bf16", 1e-5, 1007),
     8: Workload("llama1b_mlpin_bwd_m16384", 16384, 0, 2048, 16384, ACT_SWIGLU_BWD, "bf16", 1e-5, 1008),
+    9: Workload("llama1b_attnout_mlpin_bwd_m16384", 16384, 2048, 2048, 16384, ACT_CHAIN_BWD, "bf16", 1e-5, 1002),
 }
 
 
 def custom(M: int, K1: int, d: int, N2w: int, act: int, seed: int, dtype: str = "bf16",
            eps: float = 1e-5, rot_cols: int = 0, seq_len: int = 0) -> Workload:
     """A workload of arbitrary shape (ragged and edge-case tests)."""
-    if act in (ACT_SWIGLU, ACT_SWIGLU_BWD) and N2w % 2:
+    if act in (ACT_SWIGLU, ACT_SWIGLU_BWD, ACT_CHAIN_BWD) and N2w % 2:
         raise ValueError("SwiGLU needs an even number of second-weight rows")
     if act == ACT_ROPE and (rot_cols % 64 or rot_cols > N2w or seq_len < 1):
         raise ValueError("RoPE needs whole 64-value heads within the columns and a sequence length")
@@ -129,6 +136,10 @@ def generate(w: Workload, rows: int | None = None) -> dict:
       pos    int32 [M]        RoPE workloads only: token m's position, m mod seq_len
       targets int32 [M]       cross-entropy workloads only: uniform in [0, N2w), drawn
                               after W
+      dy     uint16 [M, N2w/2] whole-chain backward only: bf16 bits, N(0, 1), the
+                              upstream gradient of y, drawn after W
+      dres   uint16 [M, d]    whole-chain backward only: bf16 bits, N(0, 1), the gradient
+                              reaching h through the residual stream, drawn after dy
     For an e4m3 workload these are the pre-quantisation tensors (quantisation is a
     step of the chain's weight/activation preparation, not of input generation).
     ``rows`` (optional) truncates M, keeping the draws of the first rows identical.
@@ -143,9 +154,15 @@ def generate(w: Workload, rows: int | None = None) -> dict:
     gamma = (f32(1.0) + f32(0.1) * rng.standard_normal(w.d, dtype=f32)).astype(f32)
     W = rng.standard_normal((w.N2w, w.d), dtype=f32) * f32(1.0 / np.sqrt(w.d))
     tgt = rng.integers(0, w.N2w, size=w.M, dtype=np.int32) if w.act == ACT_CE else None
+    dy = dres = None
+    if w.act == ACT_CHAIN_BWD:
+        dy = rng.standard_normal((w.M, w.N2w // 2), dtype=f32)
+        dres = rng.standard_normal((w.M, w.d), dtype=f32)
     if rows is not None:
         A, x = A[:rows], x[:rows]
         tgt = None if tgt is None else tgt[:rows]
+        dy = None if dy is None else dy[:rows]
+        dres = None if dres is None else dres[:rows]
     out = {
         "A": to_bf16_bits(A),
         "Wo_t": to_bf16_bits(Wo),
@@ -157,6 +174,9 @@ def generate(w: Workload, rows: int | None = None) -> dict:
         out["pos"] = (np.arange(A.shape[0]) % w.seq_len).astype(np.int32)
     if tgt is not None:
         out["targets"] = tgt
+    if dy is not None:
+        out["dy"] = to_bf16_bits(dy)
+        out["dres"] = to_bf16_bits(dres)
     return out
 
 

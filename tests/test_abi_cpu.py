@@ -232,18 +232,63 @@ def test_weight_gradient_validation():
     assert L.coda_wgrad_partials_rows(0) == -1
     assert L.coda_wgrad_partials_rows(256) == 1 and L.coda_wgrad_partials_rows(257) == 2
     w = L.coda_gemm_wgrad
-    # NR, NC, K, At, Bt, gamma, W, dW, partials, stream
-    assert w(64, 60, 64, P1, P2, P3, P4, P5, P6, None) == SHAPE          # NC % 8
-    assert w(64, 64, 60, P1, P2, P3, P4, P5, P6, None) == SHAPE          # K % 8 (the tokens)
-    assert w(0, 64, 64, P1, P2, P3, P4, P5, P6, None) == SHAPE
-    assert w(64, 64, 64, P1, P2, P3, P4, P5, None, None) == NULL         # W without partials
-    assert w(64, 64, 64, None, P2, P3, P4, P5, P6, None) == NULL
-    assert w(64, 64, 0, None, None, None, None, None, None, None) == NULL  # no tokens still writes dW
-    assert w(64, 64, 64, P1, P2, P3 + 4, P4, P5, P6, None) == ALIGN      # gamma read 16 bytes at a time
-    assert w(64, 64, 64, P1, P2, P3, P4, P5, P5 + 64, None) == ALIAS     # partials over dW
-    assert w(64, 64, 64, P1, P2, P3, P4, P1 + 16, P6, None) == ALIAS     # dW over At
-    assert w(64, 64, 64, P1, P2, P3, P4, P5, P4, None) == ALIAS          # partials over W
+    # NR, NC, K, At, Bt, gamma, W, dW, partials, workspace, workspace_bytes, stream
+    assert w(64, 60, 64, P1, P2, P3, P4, P5, P6, None, 0, None) == SHAPE          # NC % 8
+    assert w(64, 64, 60, P1, P2, P3, P4, P5, P6, None, 0, None) == SHAPE          # K % 8 (the tokens)
+    assert w(0, 64, 64, P1, P2, P3, P4, P5, P6, None, 0, None) == SHAPE
+    assert w(64, 64, 64, P1, P2, P3, P4, P5, None, None, 0, None) == NULL         # W without partials
+    assert w(64, 64, 64, None, P2, P3, P4, P5, P6, None, 0, None) == NULL
+    assert w(64, 64, 0, None, None, None, None, None, None, None, 0, None) == NULL  # no tokens still writes dW
+    assert w(64, 64, 64, P1, P2, P3 + 4, P4, P5, P6, None, 0, None) == ALIGN      # gamma read 16 bytes at a time
+    assert w(64, 64, 64, P1, P2, P3, P4, P5, P5 + 64, None, 0, None) == ALIAS     # partials over dW
+    assert w(64, 64, 64, P1, P2, P3, P4, P1 + 16, P6, None, 0, None) == ALIAS     # dW over At
+    assert w(64, 64, 64, P1, P2, P3, P4, P5, P4, None, 0, None) == ALIAS          # partials over W
+    # NR, NC, K, At, Bt, gamma, W, dW, partials, workspace, workspace_bytes, stream
+    assert w(64, 64, 64, P1, P2, P3, None, P5, None, None, 64, None) == VALUE      # bytes without a workspace
+    assert w(64, 64, 64, P1, P2, P3, None, P5, None, P6, -1, None) == VALUE
+    assert w(64, 64, 64, P1, P2, P3, None, P5, None, P6 + 8, 64, None) == ALIGN
+    assert w(64, 64, 64, P1, P2, P3, None, P5, None, P5 + 64, 64, None) == ALIAS    # workspace over dW
+    assert w(64, 64, 64, P1, P2, P3, None, P5, None, P1 + 64, 64, None) == ALIAS    # workspace over At
+    assert L.coda_wgrad_workspace_bytes(0, 64, 64) == -1
+    assert L.coda_wgrad_workspace_bytes(16384, 2048, 16384) == 0                # 512 tiles: no split
+    assert L.coda_wgrad_workspace_bytes(2048, 2048, 16384) == 4 * 2048 * 2048 * 4   # 64 tiles: 4 splits
+    assert L.coda_wgrad_workspace_bytes(2048, 2048, 2048) == 0                  # too few tokens to split
     c = L.coda_colsum_reduce
     assert c(0, 64, P1, P2, None) == SHAPE
     assert c(4, 64, None, P2, None) == NULL
     assert c(4, 64, P1, P1 + 128, None) == ALIAS
+
+
+@no_gpu
+def test_plain_gemm_validation():
+    L = _lib.load()
+    g = L.coda_gemm_bf16
+    # M, N, K, A, Bt, c_res, C, stream
+    assert g(16, 60, 64, P1, P2, None, P3, None) == SHAPE             # N % 8
+    assert g(16, 64, 60, P1, P2, None, P3, None) == SHAPE             # K % 8
+    assert g(16, 64, 64, None, P2, None, P3, None) == NULL
+    assert g(16, 64, 64, P1 + 8, P2, None, P3, None) == ALIGN
+    assert g(16, 64, 64, P1, P2, None, P1 + 16, None) == ALIAS        # C over A
+    assert g(16, 64, 64, P1, P2, P3 + 16, P3, None) == ALIAS          # partial overlap with c_res
+    assert g(0, 64, 64, None, None, None, None, None) == OK
+
+
+@no_gpu
+def test_saved_pre_activation_validation():
+    L = _lib.load()
+    f = L.coda_gemm_rowscale_swiglu_save
+    # M, F, K, h, W, r, y, z, stream
+    assert f(16, 60, 64, P1, P2, P3, P4, P5, None) == SHAPE             # F % 8
+    assert f(16, 64, 64, P1, P2, P3, P4, None, None) == NULL
+    assert f(16, 64, 64, P1, P2, P3, P4, P4 + 64, None) == ALIAS         # z over y
+    assert f(16, 64, 64, P1, P2, P3, P4, P1, None) == ALIAS              # z over h
+    assert f(0, 64, 64, None, None, None, None, None, None) == OK
+    b = L.coda_swiglu_bwd_saved
+    # M, F, z, dy, r, dz, dzt, partials, stream
+    assert b(16, 60, P1, P2, P3, P4, P5, P6, None) == SHAPE              # F % 8
+    assert b(12, 64, P1, P2, P3, P4, P5, P6, None) == SHAPE              # transposed rows need M % 8
+    assert b(16, 64, P1, P2, P3, None, P5, P6, None) == NULL
+    assert b(16, 64, P1, P2, P3, P4, P5 + 8, P6, None) == ALIGN
+    assert b(16, 64, P1, P2, P3, P4, P4 + 64, P6, None) == ALIAS         # dzt over dz
+    assert b(16, 64, P1, P2, P3, P4, P5, P1, None) == ALIAS              # partials over z
+    assert b(0, 64, None, None, None, None, None, None, None) == OK

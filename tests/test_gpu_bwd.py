@@ -54,8 +54,11 @@ def _check(w, inp, dh, dz, r, rows=None, dh_res=None):
     assert np.all(np.abs(rg - o["r"]) <= 2 * np.spacing(np.float32(o["r"])).astype(np.float64))
 
 
-def test_transpose_is_exact():
-    x = torch.randint(-30000, 30000, (333, 130), dtype=torch.int16, device="cuda").view(torch.bfloat16)
+@pytest.mark.parametrize("R,C", [(333, 130), (328, 136), (8, 8), (136, 328), (1, 5)])
+def test_transpose_is_exact(R, C):
+    # general shapes and the 16-byte path (both sides multiples of 8, ragged against the
+    # 128 x 64 tile)
+    x = torch.randint(-30000, 30000, (R, C), dtype=torch.int16, device="cuda").view(torch.bfloat16)
     y = coda.transpose_bf16(x)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), x.view(torch.int16).t().contiguous())

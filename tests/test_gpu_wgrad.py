@@ -166,3 +166,29 @@ def test_wgrad_deterministic_bitwise():
     _, dW1, dg1 = _run(w)
     _, dW2, dg2 = _run(w)
     assert np.array_equal(dW1, dW2) and np.array_equal(dg1, dg2)
+
+
+def test_token_split_matches_the_definition_and_is_reproducible():
+    # 3 output tiles over 8200 tokens: the workspace lets 4 blocks share each tile (the
+    # last split ragged), their sums added in a fixed order, then gamma
+    rng = np.random.default_rng(20)
+    NR, NC, K = 520, 136, 8200
+    assert coda.wgrad_workspace_bytes(NR, NC, K) == 4 * NR * NC * 4
+    a = si.to_bf16_bits(rng.standard_normal((NR, K)).astype(np.float32))
+    b = si.to_bf16_bits(rng.standard_normal((NC, K)).astype(np.float32))
+    g = np.exp2(rng.integers(-3, 4, NC)).astype(np.float32)
+    ad, bd = dev_bf16(a), dev_bf16(b)
+    gd = torch.from_numpy(g).cuda()
+    ws = torch.empty(coda.wgrad_workspace_bytes(NR, NC, K), dtype=torch.uint8, device="cuda")
+    s1, _ = coda.gemm_wgrad(ad, bd, gd, workspace=ws)
+    s2, _ = coda.gemm_wgrad(ad, bd, gd, workspace=ws)
+    one, _ = coda.gemm_wgrad(ad, bd, gd)                       # no workspace: one block per tile
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    A, B = oracle.bf16_decode(a), oracle.bf16_decode(b)
+    ref = (A @ B.T) * g.astype(np.float64)[None, :]
+    bound = K * 2.0 ** -24 * (np.abs(A) @ np.abs(B).T) * g.astype(np.float64)[None, :]
+    for got in (s1, one):
+        err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
+        _log(f"  token split err max {err.max():.2e}, bound min {bound.min():.2e}")
+        assert np.all(err <= bound)

@@ -93,3 +93,15 @@ def test_rss_of_dA_is_over_the_hidden_columns():
         col[:, n] = dres[:, n]
         sq += oracle.chain_bwd(prep, x_res, inp["gamma"], inp["W_t"], zero, eps, dres=col)["dA"] ** 2
     assert np.allclose(o["rss_dA"], np.sqrt(sq), rtol=1e-12, atol=0)
+
+
+def test_whole_chain_backward_inputs_extend_the_forward_draws():
+    # the backward workload draws the forward's inputs first, in the same order, then the
+    # upstream and residual-stream gradients: its forward is the forward workload's
+    fwd = si.generate(si.custom(24, 16, 32, 48, si.ACT_SWIGLU, seed=7))
+    bwd = si.generate(si.custom(24, 16, 32, 48, si.ACT_CHAIN_BWD, seed=7))
+    for k in ("A", "Wo_t", "x_res", "gamma", "W_t"):
+        assert np.array_equal(fwd[k], bwd[k])
+    assert bwd["dy"].shape == (24, 24) and bwd["dres"].shape == (24, 32)
+    w2, w9 = si.WORKLOADS[2], si.WORKLOADS[9]
+    assert (w9.M, w9.K1, w9.d, w9.N2w, w9.seed) == (w2.M, w2.K1, w2.d, w2.N2w, w2.seed)
