@@ -26,7 +26,7 @@ __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3"
            "gemm_rowscale_ce", "ce_reduce", "rowscale_from_h", "transpose_bf16", "gemm_swiglu_bwd", "rmsnorm_bwd_reduce",
            "gemm_rmsnorm_bwd", "mlpin_bwd", "wgrad_partials_rows", "gemm_wgrad", "colsum_reduce",
            "mlpin_wgrad", "gemm_bf16", "chain_bwd", "wgrad_workspace_bytes", "gemm_rowscale_swiglu_save",
-           "swiglu_bwd_saved", "chain", "version"]
+           "swiglu_bwd_saved", "gemm_rowscale_gfold", "chain", "version"]
 
 
 def _stream(stream):
@@ -250,6 +250,19 @@ def mlpin_bwd(h, Wp, Wpt, r, dy, dh_res=None, out=None, stream=None):
     q = rmsnorm_bwd_reduce(P, r, h.shape[1], Wp.shape[0] // 2, out.get("q"), stream)
     dh = gemm_rmsnorm_bwd(dz, Wpt, h, q, dh_res, out.get("dh"), stream)
     return dh, dz, P, q
+
+
+def gemm_rowscale_gfold(h, W, gamma, r, act=SWIGLU, y=None, stream=None):
+    """The second GEMM from the raw bf16 weight W with gamma folded in on chip
+    (bit-identical to gemm_rowscale_swiglu with prepare_weight_bf16(W, gamma))."""
+    _esize(W, 2)
+    M, K = h.shape
+    n_w = W.shape[0]
+    N_out = n_w // 2 if act == SWIGLU else n_w
+    y = torch.empty((M, N_out), dtype=torch.bfloat16, device=h.device) if y is None else y
+    _lib.check("coda_gemm_rowscale_gfold", _lib.load().coda_gemm_rowscale_gfold(
+        M, N_out, K, act, _ptr(h), _ptr(W), _ptr(gamma), _ptr(r), _ptr(y), _stream(stream)))
+    return y
 
 
 def gemm_rowscale_swiglu_save(h, W, r, y=None, z=None, stream=None):

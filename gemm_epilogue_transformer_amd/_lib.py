@@ -36,6 +36,7 @@ SIGNATURES = {
     "coda_gemm_swiglu_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "coda_rmsnorm_bwd_reduce": (_I, [_I64, _I64, _I64, _P, _P, _P, _P]),
     "coda_gemm_rmsnorm_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "coda_gemm_rowscale_gfold": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P]),
     "coda_gemm_rowscale_swiglu_save": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "coda_swiglu_bwd_saved": (_I, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "coda_gemm_bf16": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P]),

@@ -339,6 +339,26 @@ coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* d
                                                     as_stream(stream)));
 }
 
+coda_status coda_gemm_rowscale_gfold(int64_t M, int64_t N_out, int64_t K, coda_act act, const void* h,
+                                     const void* W, const float* gamma, const float* r, void* y, void* stream) {
+    if (act != CODA_ACT_NONE && act != CODA_ACT_SWIGLU) return CODA_ERR_DTYPE;
+    const bool swiglu = act == CODA_ACT_SWIGLU;
+    if (!dim_ok(M, 0) || !dim_ok(N_out, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (N_out % 8 != 0 || K % 8 != 0 || N_out > kMaxRow || K > kMaxRow) return CODA_ERR_SHAPE;
+    const int64_t n_w = swiglu ? 2 * N_out : N_out;
+    if (n_w > kMaxDim || !prod_ok(M, K) || !prod_ok(n_w, K) || !prod_ok(M, N_out)) return CODA_ERR_SHAPE;
+    if (coda::gemm3_tiles(M, N_out, swiglu) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!h || !W || !gamma || !r || !y) return CODA_ERR_NULL;
+    if (!aligned16(h) || !aligned16(W) || !aligned16(gamma) || !aligned16(r) || !aligned16(y)) return CODA_ERR_ALIGN;
+    const Range ry = span(y, M * N_out * 2);
+    if (overlap(ry, span(h, M * K * 2)) || overlap(ry, span(W, n_w * K * 2)) || overlap(ry, span(gamma, K * 4)) ||
+        overlap(ry, span(r, M * 4)))
+        return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_rowscale_gfold(int(M), int(N_out), int(K), swiglu, h, W, gamma, r, y,
+                                                       as_stream(stream)));
+}
+
 coda_status coda_gemm_rowscale_swiglu_save(int64_t M, int64_t F, int64_t K, const void* h, const void* W,
                                            const float* r, void* y, void* z, void* stream) {
     if (!dim_ok(M, 0) || !dim_ok(F, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;

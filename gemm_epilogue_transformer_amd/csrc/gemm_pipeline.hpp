@@ -507,17 +507,67 @@ struct RegPanel {
     }
 };
 
+// Transform of the B chunks between their register stage and LDS (register-staged
+// mainloop only).  NoFold: none.  GammaFold: the RMSNorm weight folded into a raw bf16
+// weight on the fly, W'[n,k] = bf16_rne(fl32(gamma[k] W[n,k])) -- the separate fold's
+// arithmetic, so the LDS holds the same bits as with a pre-folded weight.  A lane's
+// chunk covers the same 8 k of every B row it stages, so per k-tile it loads those 8
+// gamma values once (prepare) and scales all its B chunks with them (apply).
+struct NoFold {
+    __device__ __forceinline__ void prepare(int) {}
+    __device__ __forceinline__ i32x4_t apply(const i32x4_t& v) const { return v; }
+};
+
+template <int RB>
+struct GammaFold {
+    __amdgpu_buffer_rsrc_t rsrc;     // gamma, K floats
+    uint32_t chunk_off;              // bytes of this lane's first k within a k-tile
+    float g[8];
+    __device__ __forceinline__ GammaFold(const float* gamma, int K) {
+        const uint64_t p = reinterpret_cast<uint64_t>(gamma);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+        void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, K * 4, 0x00020000);
+        chunk_off = static_cast<uint32_t>((threadIdx.x & 63) % (RB / 16)) * 32u;   // 8 bf16 k = 8 floats
+    }
+    // gamma of k-tile kt's 8 k values of this lane (zeros past K, where the weight
+    // chunk reads zeros too)
+    __device__ __forceinline__ void prepare(int kt) {
+        const uint32_t off = static_cast<uint32_t>(kt) * (RB / 2) * 4u + chunk_off;
+        const f32x4_t a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+        const f32x4_t b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            g[e] = a[e];
+            g[4 + e] = b[e];
+        }
+    }
+    __device__ __forceinline__ i32x4_t apply(const i32x4_t& v) const {
+        i32x4_t o;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const uint32_t u = static_cast<uint32_t>(v[h]);
+            const float p0 = g[2 * h] * bf16_bits_to_f32(static_cast<uint16_t>(u & 0xFFFFu));
+            const float p1 = g[2 * h + 1] * bf16_bits_to_f32(static_cast<uint16_t>(u >> 16));
+            o[h] = static_cast<int>(uint32_t(f32_to_bf16_bits(p0)) | (uint32_t(f32_to_bf16_bits(p1)) << 16));
+        }
+        return o;
+    }
+};
+
 // Two LDS stages + one register stage.  Per k-tile kt (reading stage kt%2):
 //   k-steps 0 .. KS-2: the registers holding tile kt+1 are written to stage (kt+1)%2
 //     (free since the barrier of tile kt-1), and each register is reloaded right after
 //     its write with the same chunk of tile kt+2;
 //   last k-step: wait for the own LDS writes, barrier (tile kt+1 complete in LDS, stage
 //     kt%2 read by every wave), then MFMAs with the reads of tile kt+1's first fragments.
-template <Elt E, int BM, int BN, int SPLIT, int NW, int RB, int TM, int TN, class ARow, class BRow>
+template <Elt E, int BM, int BN, int SPLIT, int NW, int RB, int TM, int TN, class ARow, class BRow,
+          class BFold = NoFold>
 __device__ __forceinline__ void mainloop_reg(f32x16_t (&acc)[TM][TN], const RegPanel<BM, BM, NW, RB>& pa,
                                              const RegPanel<BN, SPLIT, NW, RB>& pb, int kbytes,
                                              uint8_t* const (&st)[2], const ARow& a_row,
-                                             const BRow& b_row) {
+                                             const BRow& b_row, BFold fold = BFold()) {
     using F = Frags<E, TM, TN, RB>;
     constexpr int KS = F::kSteps;
     static_assert(KS >= 2, "writes go in the k-steps before the last");
@@ -534,11 +584,12 @@ __device__ __forceinline__ void mainloop_reg(f32x16_t (&acc)[TM][TN], const RegP
     };
     auto store_q = [&](int q, uint8_t* stage) {
         if (q < nA) pa.store_one(q, stage, g[q]);
-        else pb.store_one(q - nA, stage + BM * RB, g[q]);
+        else pb.store_one(q - nA, stage + BM * RB, fold.apply(g[q]));
     };
     F f[2];
     {
         uint32_t ba = pa.base_offset(0, kbytes), bb = pb.base_offset(0, kbytes);
+        fold.prepare(0);
         static_for<kPerTile>([&](auto Q) { load_q(decltype(Q)::value, ba, bb); });
         static_for<kPerTile>([&](auto Q) { store_q(decltype(Q)::value, st[0]); });
         ba = pa.base_offset(1, kbytes); bb = pb.base_offset(1, kbytes);
@@ -556,6 +607,7 @@ __device__ __forceinline__ void mainloop_reg(f32x16_t (&acc)[TM][TN], const RegP
             const int kt = gi * 2 + i;
             const uint32_t ba = pa.base_offset(kt + 2, kbytes);
             const uint32_t bb = pb.base_offset(kt + 2, kbytes);
+            fold.prepare(kt + 1);                      // the registers hold tile kt+1
 #pragma unroll
             for (int s = 0; s < KS - 1; ++s) {
                 // MFMA j; fragment read j of k-step s+1; on odd slots, register chunk q of

@@ -421,7 +421,9 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
     }
 }
 
-// Direct-to-LDS mainloop (PIPE 1: the register-staged one, bf16 weights only).  W8: the
+// Direct-to-LDS mainloop (PIPE 1: the register-staged one, bf16 weights only; PIPE 2: the
+// register-staged one with the RMSNorm weight gfold folded into a raw W on its way to
+// LDS, bit-identical to a pre-folded W').  W8: the
 // weights are e4m3, RB is the k-tile depth of a bf16 h row and a W row holds RB/2 bytes.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int PIPE, int OCC, int ACT,
           bool W8>
@@ -429,7 +431,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
                        uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
-                       int tiles_n, RopeArgs rope, CeArgs ce, BwdArgs bw) {
+                       int tiles_n, RopeArgs rope, CeArgs ce, BwdArgs bw, const float* __restrict__ gfold) {
     // the backward recomputes the forward's gate / up product: same B panel layout
     constexpr bool SWIGLU = ACT == kActSwiglu || ACT == kActSwigluBwd || ACT == kActSwigluSave;
     constexpr int NW = WAVES_M * WAVES_N;
@@ -472,8 +474,8 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 
     const int kbytes = K * 2;                       // bytes of an h row
     const int kbytes_b = W8 ? K : K * 2;            // bytes of a W row
-    using PanelA = std::conditional_t<PIPE == 1, RegPanel<BM, BM, NW, RB>, DmaPanel<BM, BM, NW, RB>>;
-    using PanelB = std::conditional_t<PIPE == 1, RegPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB>,
+    using PanelA = std::conditional_t<PIPE >= 1, RegPanel<BM, BM, NW, RB>, DmaPanel<BM, BM, NW, RB>>;
+    using PanelB = std::conditional_t<PIPE >= 1, RegPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB>,
                                       DmaPanel<BN, SWIGLU ? BN / 2 : BN, NW, RBB>>;
     PanelA pa;
     PanelB pb;
@@ -510,6 +512,10 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     } else if constexpr (PIPE == 1) {
         static_assert(NS == 2, "the register-staged mainloop has two LDS stages");
         mainloop_reg<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row);
+    } else if constexpr (PIPE == 2) {
+        static_assert(NS == 2, "the register-staged mainloop has two LDS stages");
+        mainloop_reg<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row,
+                                                                         GammaFold<RB>(gfold, K));
     } else {
         mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
     }
@@ -557,18 +563,32 @@ int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
     return ((M + BM3 - 1) / BM3) * ((N_out + bno - 1) / bno);
 }
 
-template <int ACT, bool WFP8>
+template <int ACT, bool WFP8, bool GFOLD = false>
 static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                           const float* w_scale, const float* r, void* y, const RopeArgs& rope,
-                          const CeArgs& ce, const BwdArgs& bw, hipStream_t stream) {
+                          const CeArgs& ce, const BwdArgs& bw, hipStream_t stream,
+                          const float* gfold = nullptr) {
     constexpr int BNO = (ACT == kActSwiglu || ACT == kActSwigluBwd || ACT == kActSwigluSave) ? BN3 / 2 : BN3;
     const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BNO - 1) / BNO;
     const dim3 grid(tiles_m * tiles_n), block(64 * WM3 * WN3);
-    hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, WFP8 ? 0 : PIPE3,
+    static_assert(!(GFOLD && WFP8), "the in-kernel fold takes a bf16 weight");
+    constexpr int PIPE = GFOLD ? 2 : (WFP8 ? 0 : PIPE3);
+    hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, PIPE,
                                                OCC3, ACT, WFP8>),
                        grid, block, 0, stream, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W),
-                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n, rope, ce, bw);
+                       w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n, rope, ce, bw, gfold);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_rowscale_gfold(int M, int N_out, int K, bool swiglu, const void* h, const void* W_raw,
+                                      const float* gamma, const float* r, void* y, hipStream_t stream) {
+    const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
+    const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
+    const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
+    return swiglu ? launch3<kActSwiglu, false, true>(M, N_out, K, h, W_raw, nullptr, r, y, none, no_ce, no_bw,
+                                                     stream, gamma)
+                  : launch3<kActNone, false, true>(M, N_out, K, h, W_raw, nullptr, r, y, none, no_ce, no_bw,
+                                                   stream, gamma);
 }
 
 hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, const void* h,

@@ -58,6 +58,10 @@ hipError_t launch_gemm_rmsnorm_bwd(int M, int N, int K, const void* dz, const vo
                                    const float* q, const void* dh_res, void* dh, hipStream_t stream);
 hipError_t launch_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, hipStream_t stream);
 
+// The second GEMM reading the raw weight and folding gamma in while staging it.
+hipError_t launch_gemm_rowscale_gfold(int M, int N_out, int K, bool swiglu, const void* h, const void* W_raw,
+                                      const float* gamma, const float* r, void* y, hipStream_t stream);
+
 // SwiGLU forward that keeps the pre-activation, and the backward that starts from it.
 hipError_t launch_gemm_rowscale_swiglu_save(int M, int F, int K, const void* h, const void* W, const float* r,
                                             void* y, void* z, hipStream_t stream);

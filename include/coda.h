@@ -277,6 +277,18 @@ coda_status coda_gemm_rmsnorm_bwd(int64_t M, int64_t N, int64_t K, const void* d
                                   const void* h, const float* q, const void* dh_res, void* dh,
                                   void* stream);
 
+/* The second GEMM from the RAW weight, with gamma folded in on chip (no weight
+ * preparation pass, no W' copy): each 16-byte chunk of W is multiplied by its 8 gamma
+ * values and rounded, bf16_rne(fl32(gamma[k] W[n,k])), between the registers and LDS --
+ * the arithmetic of coda_prepare_weight_bf16, so y is bit-identical to
+ * coda_gemm_rowscale_swiglu with the prepared W'.  (kucoin page, section "Cinco bloques y
+ * un lenguaje LEGO": the RMSNorm weight is a broadcast vector operand.)
+ *   act NONE or SWIGLU as coda_gemm_rowscale_swiglu;  W [n_w, K] bf16 raw weight;
+ *   gamma [K] fp32 (16-byte aligned);  h, r, y as there.
+ * Granules: N_out % 8 == 0, K % 8 == 0.  y must not overlap the inputs.               */
+coda_status coda_gemm_rowscale_gfold(int64_t M, int64_t N_out, int64_t K, coda_act act, const void* h,
+                                     const void* W, const float* gamma, const float* r, void* y, void* stream);
+
 /* ------------------------------ backward from a saved pre-activation ---- */
 /* A forward that keeps the pre-activation lets the backward skip the recomputed gate/up
  * product (memory for time: z is M x 2F bf16).  Same block and same gradients as above.  */

@@ -292,3 +292,16 @@ def test_saved_pre_activation_validation():
     assert b(16, 64, P1, P2, P3, P4, P4 + 64, P6, None) == ALIAS         # dzt over dz
     assert b(16, 64, P1, P2, P3, P4, P5, P1, None) == ALIAS              # partials over z
     assert b(0, 64, None, None, None, None, None, None, None) == OK
+
+
+@no_gpu
+def test_on_chip_fold_validation():
+    L = _lib.load()
+    f = L.coda_gemm_rowscale_gfold
+    # M, N_out, K, act, h, W, gamma, r, y, stream
+    assert f(16, 64, 64, 7, P1, P2, P3, P4, P5, None) == DTYPE
+    assert f(16, 60, 64, 1, P1, P2, P3, P4, P5, None) == SHAPE
+    assert f(16, 64, 64, 1, P1, P2, None, P4, P5, None) == NULL
+    assert f(16, 64, 64, 1, P1, P2, P3 + 4, P4, P5, None) == ALIGN
+    assert f(16, 64, 64, 1, P1, P2, P3, P4, P3, None) == ALIAS              # y over gamma
+    assert f(0, 64, 64, 1, None, None, None, None, None, None) == OK
