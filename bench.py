@@ -432,6 +432,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="also time the unfused torch chain")
+    ap.add_argument("--graph", action="store_true",
+                    help="forward workloads: also time the step replayed from a captured HIP graph")
     ap.add_argument("--saved-z", action="store_true",
                     help="backward workloads: start from the pre-activation the forward saved (no recompute)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -555,6 +557,28 @@ def main():
     k3_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     k4_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if ce_in is not None else None
 
+    # the same step captured once in a HIP graph and replayed K times (no per-kernel
+    # events inside): what a launch-bound caller would run
+    graph_ms = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gstart, gend = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gstart.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        gend.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = gstart.elapsed_time(gend) / args.steps
+
     flops = w.gemm_flops
     value = flops / (ms_per_step * 1e-3) / 1e12
     g1_flops = 2 * M * w.K1 * d
@@ -589,6 +613,9 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
 
+    if graph_ms is not None:
+        rec["graph"] = {"ms_per_step": round(graph_ms, 4), "value": round(flops / (graph_ms * 1e-3) / 1e12, 2),
+                        "note": "the same step replayed from a captured HIP graph"}
     if args.unfused and w.dtype == "bf16":
         def unfused():
             t = A @ Wo.t()
