@@ -35,12 +35,36 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "gemm_epilogue_transformer_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
+def _kernel_files(kernel: str) -> list:
+    """The source files a kernel's device code is built from: the translation unit that
+    defines it and the headers it includes, transitively (launch.hpp, host declarations
+    only, excluded)."""
+    import re
+
+    tus = [f for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".cpp"))]
+    defining = [f for f in tus if re.search(r"__global__[^;{]*?\b" + re.escape(kernel) + r"\s*\(",
+                                              open(os.path.join(CSRC, f)).read(), re.S)]
+    todo, seen = list(defining), set()
+    while todo:
+        f = todo.pop()
+        if f in seen or f == "launch.hpp" or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        seen.add(f)
+        todo += re.findall(r'#include\s+"([^"]+)"', open(os.path.join(CSRC, f)).read())
+    return sorted(seen)
+
+
+def kernel_source_hash(kernel: str | None = None) -> str:
+    """Hash of the kernel's source files (all sources when kernel is None): a stored
+    counter reading belongs to the kernel while this hash is unchanged."""
+    files = _kernel_files(kernel) if kernel else [f for f in sorted(os.listdir(CSRC))
+                                                   if f.endswith((".hip", ".hpp", ".cpp"))]
+    if kernel and not files:
+        return ""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(CSRC, f), "rb").read())
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -89,7 +113,7 @@ def load_traffic(workload: str, kernel: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -138,7 +162,7 @@ def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
         if not fk or not wk:
             continue
         traffic = fk[0] * 1024 / ff + wk[0] * 1024 / fw
-        rec = {"kernel": kname, "workload": workload, "source_hash": kernel_source_hash(),
+        rec = {"kernel": kname, "workload": workload, "source_hash": kernel_source_hash(kname),
                "fetch_kib": fk[0], "write_kib": wk[0], "copy_factor_fetch": ff,
                "copy_factor_write": fw, "hbm_bytes_per_launch": round(traffic), "command": command}
         with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{workload}.json"), "w") as fh:
@@ -295,7 +319,8 @@ def bench_backward(w, args) -> dict:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": load_traffic(w.name, kern[dom]), "kernel": kern[dom],
-                     "kernel_ms": round(k_ms[dom], 4), "algorithmic_bytes": byt[names[dom]]},
+                     "kernel_ms": round(k_ms[dom], 4), "algorithmic_bytes": byt[names[dom]],
+                     "kernel_source_hash": kernel_source_hash(kern[dom])},
         "kernel_source_hash": kernel_source_hash(),
     }
     if args.unfused:
@@ -590,7 +615,7 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name, "k_gemm_rowscale_swiglu"),
             "kernel": "k_gemm_rowscale_swiglu", "kernel_ms": round(k3_ms, 4),
-            "algorithmic_bytes": byt["gemm2"]}
+            "algorithmic_bytes": byt["gemm2"], "kernel_source_hash": kernel_source_hash("k_gemm_rowscale_swiglu")}
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
