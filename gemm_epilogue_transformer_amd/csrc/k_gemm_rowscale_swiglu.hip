@@ -22,8 +22,6 @@
 // 8-bit weights (weight-only): W is e4m3 in HBM and in LDS (half the bytes of a bf16
 // panel) and is converted exactly to bf16 in registers after the LDS read; the MFMA is
 // the bf16 one and sw is applied in the epilogue.
-#include <algorithm>
-
 #include "epilogue.hpp"
 #include "gemm_pipeline.hpp"
 #include "launch.hpp"
@@ -452,12 +450,8 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 #pragma unroll
     for (int i = 0; i < NS; ++i) st[i] = stages[i];
 
-    // one tile per workgroup, or (persistent grid) tiles pid, pid + gridDim.x, ...: the
-    // same pid -> tile map, so a workgroup keeps its XCD's tiles
-    const int tiles = tiles_m * tiles_n;
-    for (int pid = blockIdx.x; pid < tiles; pid += gridDim.x) {
     int tile_m, tile_n;
-    tile_coords<8>(pid, tiles_m, tiles_n, tile_m, tile_n);
+    tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, j0 = tile_n * BNO;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -538,8 +532,6 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
         swiglu_save_epilogue<BM, BN, WAVES_M, TM, TN>(acc, rv, sw, Y, bw.dz, M, N_out, m0, j0, wm, wn, slab);
     else
         rowscale_epilogue<BM, BN, WAVES_M, TM, TN, ACT>(acc, rv, pv, rope, sw, Y, M, N_out, m0, j0, wm, wn, slab);
-    __syncthreads();   // the epilogue's LDS slabs are free before the next tile's stages fill
-    }
 }
 
 // Tile configurations of the second GEMM (compile-time).
@@ -561,26 +553,10 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 #ifndef CODA_G3_NS8
 #define CODA_G3_NS8 2
 #endif
-#ifndef CODA_G3_PERSIST
-#define CODA_G3_PERSIST 1      // one workgroup per CU walks its tiles (measured ~0.7 % faster)
-#endif
 constexpr int BM3 = CODA_G3_BM, BN3 = CODA_G3_BN, NS3 = CODA_G3_NS, OCC3 = CODA_G3_OCC;
 constexpr int WM3 = CODA_G3_WM, WN3 = CODA_G3_WN, RB3 = CODA_G3_RB, SP3 = CODA_G3_SPREAD, PIPE3 = CODA_G3_PIPE;
 // 8-bit weights: a stage is 3/4 of a bf16 one, so a third stage fits where two do
 constexpr int NS3_8 = CODA_G3_NS8;
-
-// Compute units of the current device (cached per device; 0 if the query fails, which
-// leaves one workgroup per tile).
-static int compute_units() {
-    static int cache[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < 64 && cache[dev] > 0) return cache[dev];
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev < 64) cache[dev] = cus;
-    return cus;
-}
 
 int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
     const int64_t bno = swiglu ? BN3 / 2 : BN3;
@@ -594,12 +570,7 @@ static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                           const float* gfold = nullptr) {
     constexpr int BNO = (ACT == kActSwiglu || ACT == kActSwigluBwd || ACT == kActSwigluSave) ? BN3 / 2 : BN3;
     const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BNO - 1) / BNO;
-    int blocks = tiles_m * tiles_n;
-    if (CODA_G3_PERSIST) {
-        const int cus = compute_units();
-        if (cus > 0) blocks = std::min(blocks, cus * OCC3);
-    }
-    const dim3 grid(blocks), block(64 * WM3 * WN3);
+    const dim3 grid(tiles_m * tiles_n), block(64 * WM3 * WN3);
     static_assert(!(GFOLD && WFP8), "the in-kernel fold takes a bf16 weight");
     constexpr int PIPE = GFOLD ? 2 : (WFP8 ? 0 : PIPE3);
     hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, PIPE,
