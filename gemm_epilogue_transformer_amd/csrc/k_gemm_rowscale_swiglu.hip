@@ -170,8 +170,24 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN
         make_buffer_rsrc(bw.dy + static_cast<size_t>(m0) * F, static_cast<uint32_t>(valid_rows) * dy_row);
     const __amdgpu_buffer_rsrc_t dz_rsrc =
         make_buffer_rsrc(bw.dz + static_cast<size_t>(m0) * 2 * F, static_cast<uint32_t>(valid_rows) * dz_row);
+    // dy of segment jj of slab tm (16 bytes: 8 gate columns of one row), loaded one slab
+    // ahead so that its latency overlaps the previous slab's arithmetic and stores
+    auto dy_off = [&](int tm, int jj) -> uint32_t {
+        const int q = lane + 64 * jj;
+        const int col = j0 + wn * NB * 32 + (q % kGseg) * 8;
+        const uint32_t trow = static_cast<uint32_t>(wm * WM + tm * 32 + q / kGseg);
+        return col < F ? trow * dy_row + static_cast<uint32_t>(col) * 2 : kOobOffset;
+    };
+    i32x4_t dyb[2][kSegPerLane];
+#pragma unroll
+    for (int jj = 0; jj < kSegPerLane; ++jj) dyb[0][jj] = __builtin_amdgcn_raw_buffer_load_b128(dy_rsrc, dy_off(0, jj), 0, 0);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
+        if (tm + 1 < TM) {
+#pragma unroll
+            for (int jj = 0; jj < kSegPerLane; ++jj)
+                dyb[(tm + 1) & 1][jj] = __builtin_amdgcn_raw_buffer_load_b128(dy_rsrc, dy_off(tm + 1, jj), 0, 0);
+        }
         float v[TN][16];
 #pragma unroll
         for (int b = 0; b < TN; ++b)
@@ -194,8 +210,7 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN
             const float au[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
             const uint32_t in_range = col < F;
             const uint32_t trow = static_cast<uint32_t>(wm * WM + rw);
-            const i32x4_t dyv = __builtin_amdgcn_raw_buffer_load_b128(
-                dy_rsrc, in_range ? trow * dy_row + static_cast<uint32_t>(col) * 2 : kOobOffset, 0, 0);
+            const i32x4_t dyv = dyb[tm & 1][jj];
             float c = 0.0f;
             uint32_t og[4], ou[4];
 #pragma unroll
