@@ -98,8 +98,24 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
         }
     }
     float cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // raw W of this lane's segments, loaded one 32-row slab ahead (double-buffered) so
+    // that its latency overlaps the previous slab's work
+    auto w_off = [&](int tm, int j) -> uint32_t {
+        const uint32_t tr = static_cast<uint32_t>(wm * WM + tm * 32 + S::seg_row(j));
+        return col_in ? tr * wrow + col * 2u : kOobOffset;
+    };
+    i32x4_t wb[2][S::kSegPerLane];
+    if (Wraw) {
+#pragma unroll
+        for (int j = 0; j < S::kSegPerLane; ++j) wb[0][j] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off(0, j), 0, 0);
+    }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
+        if (Wraw && tm + 1 < TM) {
+#pragma unroll
+            for (int j = 0; j < S::kSegPerLane; ++j)
+                wb[(tm + 1) & 1][j] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off(tm + 1, j), 0, 0);
+        }
         float v[TN][16];
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
@@ -111,8 +127,7 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
             float t[8];
             S::get(slab, j, t);
             const uint32_t tr = static_cast<uint32_t>(wm * WM + tm * 32 + S::seg_row(j));
-            i32x4_t wv = {0, 0, 0, 0};
-            if (Wraw) wv = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, col_in ? tr * wrow + col * 2u : kOobOffset, 0, 0);
+            const i32x4_t wv = Wraw ? wb[tm & 1][j] : i32x4_t{0, 0, 0, 0};
             f32x4_t o0, o1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
