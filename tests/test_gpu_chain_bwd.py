@@ -173,3 +173,29 @@ def test_saved_pre_activation_and_its_backward():
     ref_P = np.stack([terms[:, 128 * t:128 * (t + 1)].sum(1) for t in range(T)], axis=1)
     scale = np.stack([np.abs(terms[:, 128 * t:128 * (t + 1)]).sum(1) for t in range(T)], axis=1)
     assert np.all(np.abs(P.cpu().numpy() - ref_P) <= 1e-5 * scale + 1e-30)
+
+
+@pytest.mark.parametrize("M", [13, 1, 70])
+def test_saved_backward_without_transpose_takes_any_row_count(M):
+    # without the transposed copy the row count is free (no 16-byte token runs); dz and the
+    # partials against the fp64 formulas from the same bf16 z, rows past the tile masked
+    rng = np.random.default_rng(24 + M)
+    F = 136
+    zb = si.to_bf16_bits(rng.standard_normal((M, 2 * F)).astype(np.float32))
+    dyb = si.to_bf16_bits(rng.standard_normal((M, F)).astype(np.float32))
+    rr = (0.5 + rng.random(M)).astype(np.float32)
+    dz, none, P = coda.swiglu_bwd_saved(dev_bf16(zb), dev_bf16(dyb), torch.from_numpy(rr).cuda(), transpose=False)
+    torch.cuda.synchronize()
+    assert none is None
+    zg, d, r = oracle.bf16_decode(zb), oracle.bf16_decode(dyb), rr.astype(np.float64)[:, None]
+    g, u = zg[:, :F], zg[:, F:]
+    s = 1.0 / (1.0 + np.exp(-g))
+    dg, du = d * u * s * (1 + g * (1 - s)), d * g * s
+    ref_dz = r * np.concatenate([dg, du], axis=1)
+    e = np.abs(oracle.bf16_decode(host_bits(dz)) - ref_dz) / (1e-3 + np.abs(ref_dz))
+    assert e.max() <= 2.0 ** -7
+    terms = (dg * g + du * u) / r
+    T = P.shape[1]
+    ref_P = np.stack([terms[:, 128 * t:128 * (t + 1)].sum(1) for t in range(T)], axis=1)
+    scale = np.stack([np.abs(terms[:, 128 * t:128 * (t + 1)]).sum(1) for t in range(T)], axis=1)
+    assert np.all(np.abs(P.cpu().numpy() - ref_P) <= 1e-5 * scale + 1e-30)
