@@ -59,6 +59,43 @@ struct Slab {
     }
 };
 
+// All-reduce over aligned groups of W = 8 or 16 lanes (lanes W*k .. W*k + W-1, inside
+// one 16-lane DPP row) with VALU data-parallel moves instead of LDS permutes: quad
+// permutes pair lanes 1 and 2 apart, the 8-lane mirror pairs the two 4-lane halves of an
+// 8-group, the 16-lane mirror the two 8-lane halves of a row.  Every lane of the group
+// ends with the reduction of its W lanes.
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                                 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                                 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_half_mirror(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                                 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_mirror(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                                 0x140, 0xF, 0xF, false));
+}
+template <int W, class Op>
+__device__ __forceinline__ float group_allreduce(float x, Op op) {
+    static_assert(W == 8 || W == 16, "groups of 8 or 16 lanes");
+    x = op(x, dpp_quad_xor1(x));
+    x = op(x, dpp_quad_xor2(x));
+    x = op(x, dpp_half_mirror(x));
+    if constexpr (W == 16) x = op(x, dpp_row_mirror(x));
+    return x;
+}
+struct AddOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return static_cast<uint32_t>(f32_to_bf16_bits(a)) | (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
 }

@@ -2,7 +2,7 @@
 //
 //   v[m,n] = sa*sw * sum_k A[m,k] W[n,k] + x_res[m,n];   h = bf16_rne(v)
 //   P[m,t] = sum over the tile's columns n of h[m,n]^2   (one fp32 partial per row and
-//            N-tile, reduced in a fixed order: 8 columns in lane, a butterfly over the
+//            N-tile, reduced in a fixed order: 8 columns in lane, a DPP all-reduce over the
 //            lanes that hold one row of a wave's slab, then the waves sharing the row)
 //
 // The output tile never leaves the chip between the accumulate and the epilogue (kucoin
@@ -63,7 +63,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     // Per 32-row slab of this wave: stage scale*acc row-major in the wave's own (now
     // free) LDS stage, then each lane takes runs of 8 columns: 16-byte residual load,
     // fp32 add, one bf16 rounding, 16-byte store of h, and the sum of the 8 squares.
-    // Row sums: 16 lanes hold one slab row -> butterfly over them -> per-wave partial in
+    // Row sums: 16 lanes hold one slab row -> DPP all-reduce over them -> per-wave partial in
     // `red`, then the WAVES_N waves sharing a row are added in a fixed order.
     const float scale = (a_scale ? *a_scale : 1.0f) * (w_scale ? *w_scale : 1.0f);
     using S = Slab<TN>;
@@ -116,8 +116,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
             __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])},
                                                    h_rsrc, seg_voff(tm, j), 0, 0);
             // columns past N contribute nothing (their residual reads and sums are zero)
-#pragma unroll
-            for (int off = S::kSegPerRow / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, S::kSegPerRow);
+            sq = group_allreduce<S::kSegPerRow>(sq, AddOp());
             if ((lane & (S::kSegPerRow - 1)) == 0) red[wn][wm * WM + tm * 32 + S::seg_row(j)] = sq;
         }
     }

@@ -53,8 +53,8 @@ struct CeArgs {
 // reparameterisation covers the cross-entropy loss).  The logits z = r*sw*acc never
 // leave the chip: per 32-row slab they are staged row-major in LDS like the other
 // epilogues; each lane takes 8 consecutive columns of one row (columns >= V masked),
-// its max, a butterfly max over the lanes of the row, the sum of exp(z - max), a
-// butterfly sum; the waves sharing a row are combined in a fixed order; one (max,
+// its max, a DPP all-reduce max over the lanes of the row, the sum of exp(z - max), a
+// DPP all-reduce sum; the waves sharing a row are combined in a fixed order; one (max,
 // sum-exp) pair per row and tile.  The lane whose 8 columns hold the row's target
 // writes that logit.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
@@ -91,16 +91,14 @@ __device__ __forceinline__ void ce_epilogue(const f32x16_t (&acc)[TM][TN], const
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (n + e < V) mx = fmaxf(mx, t[e]);
-#pragma unroll
-            for (int off = S::kSegPerRow / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, S::kSegPerRow));
+            mx = group_allreduce<S::kSegPerRow>(mx, MaxOp());
             float sum = 0.0f;
             if (mx > ninf) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     if (n + e < V) sum += __expf(t[e] - mx);
             }
-#pragma unroll
-            for (int off = S::kSegPerRow / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, S::kSegPerRow);
+            sum = group_allreduce<S::kSegPerRow>(sum, AddOp());
             const int tg = __shfl(tv[rl / 64], rl % 64);
             if (tg >= n && tg < n + 8 && tg < V) {
                 float z = t[0];
@@ -151,7 +149,7 @@ struct BwdArgs {
 //   partial c = sum over the tile's columns of dL/dz * acc  (= dL/dr, fp32)
 // The accumulators are staged row-major in LDS; each lane takes 8 gate columns of one
 // row and the matching 8 up columns, loads dy as one 16-byte vector, stores two 16-byte
-// vectors of dz; c: butterfly over the 8 lanes of the row, then the waves sharing it.
+// vectors of dz; c: DPP all-reduce over the 8 lanes of the row, then the waves sharing it.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
 __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN],
                                                     const float (&rv)[BM / WAVES_M / 64], const BwdArgs& bw,
@@ -161,7 +159,7 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN
     constexpr int NB = TN / 2;                       // gate (= up) blocks per wave
     constexpr int kGseg = NB * 4;                    // 8-column gate segments per row
     constexpr int kSegPerLane = 32 * kGseg / 64;
-    static_assert(kGseg == 8, "8 lanes per row: the butterfly below");
+    static_assert(kGseg == 8, "8 lanes per row: the all-reduce below");
     using S = Slab<TN>;
     const int lane = threadIdx.x & 63;
     const int valid_rows = min(BM, M - m0);
@@ -238,8 +236,7 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN
                                                    dz_rsrc, vg, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(ou[0]), int(ou[1]), int(ou[2]), int(ou[3])},
                                                    dz_rsrc, vu, 0, 0);
-#pragma unroll
-            for (int off = kGseg / 2; off >= 1; off >>= 1) c += __shfl_xor(c, off, kGseg);
+            c = group_allreduce<kGseg>(c, AddOp());
             if ((lane & (kGseg - 1)) == 0) red[wn * BM + wm * WM + rw] = c;
         }
     }

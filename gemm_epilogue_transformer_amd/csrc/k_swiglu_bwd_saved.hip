@@ -85,8 +85,7 @@ k_swiglu_bwd_saved(const uint16_t* __restrict__ Z, const uint16_t* __restrict__ 
         *reinterpret_cast<i32x4_t*>(&st[row][8 * (ch ^ sw)]) = vg;
         *reinterpret_cast<i32x4_t*>(&st[row][8 * ((16 + ch) ^ sw)]) = vu;
         // the row's 16 chunks sit in 16 consecutive lanes
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) c += __shfl_xor(c, off, 16);
+        c = group_allreduce<16>(c, AddOp());
         if (ch == 0 && m < M) P[static_cast<size_t>(m) * T + tf] = c / r;
     }
     if (DZT == nullptr) return;
