@@ -175,10 +175,10 @@ def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
 
 def bench_backward(w, args) -> dict:
     """Backward step.  Workload of the MLP-input block: its input gradient (three calls)
-    and the weight and gamma gradients (two transposes, the token-contracting GEMM, the
-    column sum).  Whole-chain workload: the same plus the first GEMM's input gradient dA
-    and weight gradient dWo (two more transposes, the plain GEMM, the token-contracting
-    GEMM); the residual input's gradient is dh itself.  The saved forward state -- folded
+    and the weight and gamma gradients (the token-contracting GEMM on dz and h as stored,
+    the column sum).  Whole-chain workload: the same plus the first GEMM's input gradient
+    dA and weight gradient dWo (the plain GEMM, the token-contracting GEMM on dh and A);
+    the residual input's gradient is dh itself.  The saved forward state -- folded
     weight, weight transposes, h and r (from a forward run of the chain) -- is prepared
     outside the timed region."""
     import numpy as np
@@ -218,19 +218,17 @@ def bench_backward(w, args) -> dict:
     b16 = dict(dtype=torch.bfloat16, device="cuda")
     out = {"dz": torch.empty((M, 2 * F), **b16), "partials": torch.empty((M, -(-F // 128)), **f32),
            "q": torch.empty(M, **f32), "dh": torch.empty((M, d), **b16),
-           "dzt": torch.empty((2 * F, M), **b16), "ht": torch.empty((d, M), **b16),
            "dW": torch.empty((2 * F, d), **f32), "wpartials": torch.empty((TW, d), **f32),
            "dgamma": torch.empty(d, **f32)}
     if whole:
-        out.update({"dA": torch.empty((M, K1), **b16), "dht": torch.empty((d, M), **b16),
-                    "At": torch.empty((K1, M), **b16), "dWo": torch.empty((d, K1), **f32)})
+        out.update({"dA": torch.empty((M, K1), **b16), "dWo": torch.empty((d, K1), **f32)})
         nws = coda.wgrad_workspace_bytes(d, K1, M)
         out["ws"] = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws > 0 else None
     stream = torch.cuda.current_stream()
     # (name, kernel, call); the calls write into `out`
     if saved:
         stages = [("swiglu_bwd_saved", "k_swiglu_bwd_saved",
-                   lambda: coda.swiglu_bwd_saved(z, dy, r, out["dz"], out["dzt"], out["partials"]))]
+                   lambda: coda.swiglu_bwd_saved(z, dy, r, out["dz"], None, out["partials"], transpose=False))]
     else:
         stages = [("gemm_swiglu_bwd", "k_gemm_rowscale_swiglu",
                    lambda: coda.gemm_swiglu_bwd(h, Wp, r, dy, out["dz"], out["partials"]))]
@@ -239,20 +237,16 @@ def bench_backward(w, args) -> dict:
          lambda: coda.rmsnorm_bwd_reduce(out["partials"], r, d, F, out["q"])),
         ("gemm_rmsnorm_bwd", "k_gemm_rmsnorm_bwd",
          lambda: coda.gemm_rmsnorm_bwd(out["dz"], Wpt, h, out["q"], dres, out["dh"]))]
-    if not saved:
-        stages.append(("transpose_dz", "k_transpose16_bf16", lambda: coda.transpose_bf16(out["dz"], out["dzt"])))
+    # the weight gradients read dz, h, dh and A as stored (token-major): no transposes
     stages += [
-        ("transpose_h", "k_transpose16_bf16", lambda: coda.transpose_bf16(h, out["ht"])),
         ("gemm_wgrad", "k_gemm_wgrad",
-         lambda: coda.gemm_wgrad(out["dzt"], out["ht"], gamma, W, out["dW"], out["wpartials"])),
+         lambda: coda.gemm_wgrad_tok(out["dz"], h, gamma, W, out["dW"], out["wpartials"])),
         ("colsum_reduce", "k_colsum_reduce", lambda: coda.colsum_reduce(out["wpartials"], out["dgamma"]))]
     if whole:
         stages += [
             ("gemm_dA", "k_gemm_rmsnorm_bwd", lambda: coda.gemm_bf16(out["dh"], WoT, None, out["dA"])),
-            ("transpose_dh", "k_transpose16_bf16", lambda: coda.transpose_bf16(out["dh"], out["dht"])),
-            ("transpose_A", "k_transpose16_bf16", lambda: coda.transpose_bf16(A, out["At"])),
             ("gemm_wgrad_dWo", "k_gemm_wgrad",                                # token split + its reduce
-             lambda: coda.gemm_wgrad(out["dht"], out["At"], None, None, out["dWo"], None, out["ws"]))]
+             lambda: coda.gemm_wgrad_tok(out["dh"], A, None, None, out["dWo"], None, out["ws"]))]
     names = [x[0] for x in stages]
     kern = [x[1] for x in stages]
 
@@ -288,7 +282,7 @@ def bench_backward(w, args) -> dict:
     dom = max(gemms, key=lambda i: k_ms[i])
     T = -(-F // 128)
     byt = {"gemm_swiglu_bwd": M * d * 2 + 2 * F * d * 2 + M * 4 + M * F * 2 + M * 2 * F * 2 + M * T * 4,
-           "swiglu_bwd_saved": M * 2 * F * 2 + M * F * 2 + M * 4 + 2 * (M * 2 * F * 2) + M * T * 4,
+           "swiglu_bwd_saved": M * 2 * F * 2 + M * F * 2 + M * 4 + M * 2 * F * 2 + M * T * 4,
            "rmsnorm_bwd_reduce": M * T * 4 + 2 * M * 4,
            "gemm_rmsnorm_bwd": M * 2 * F * 2 + d * 2 * F * 2 + M * d * 2 + M * 4 + M * d * 2
                                + (M * d * 2 if whole else 0),

@@ -26,7 +26,7 @@ __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3"
            "gemm_rowscale_ce", "ce_reduce", "rowscale_from_h", "transpose_bf16", "gemm_swiglu_bwd", "rmsnorm_bwd_reduce",
            "gemm_rmsnorm_bwd", "mlpin_bwd", "wgrad_partials_rows", "gemm_wgrad", "colsum_reduce",
            "mlpin_wgrad", "gemm_bf16", "chain_bwd", "wgrad_workspace_bytes", "gemm_rowscale_swiglu_save",
-           "swiglu_bwd_saved", "gemm_rowscale_gfold", "chain", "version"]
+           "swiglu_bwd_saved", "gemm_rowscale_gfold", "gemm_wgrad_tok", "chain", "version"]
 
 
 def _stream(stream):
@@ -338,6 +338,32 @@ def gemm_wgrad(At, Bt, gamma=None, W=None, dW=None, partials=None, workspace=Non
     return dW, (partials if W is not None else None)
 
 
+def gemm_wgrad_tok(X, Y, gamma=None, W=None, dW=None, partials=None, workspace=None, NR=None, NC=None,
+                   stream=None):
+    """dW [NR, NC] fp32 = gamma * (X^T . Y), the sum over the K token rows of the token-major
+    X [K, lda] (its first NR columns, default all) and Y [K, ldb] (first NC columns): the
+    weight gradient without transposed copies.  W, partials and workspace as gemm_wgrad."""
+    _esize(X, 2)
+    _esize(Y, 2)
+    K, lda = X.shape
+    ldb = Y.shape[1]
+    NR = lda if NR is None else NR
+    NC = ldb if NC is None else NC
+    dW = torch.empty((NR, NC), dtype=torch.float32, device=X.device) if dW is None else dW
+    if W is not None and partials is None:
+        partials = torch.empty((wgrad_partials_rows(NR), NC), dtype=torch.float32, device=X.device)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be a tensor, None or 'auto'")
+        n = wgrad_workspace_bytes(NR, NC, K) if W is None else 0
+        workspace = torch.empty(n, dtype=torch.uint8, device=X.device) if n > 0 else None
+    _lib.check("coda_gemm_wgrad_tok", _lib.load().coda_gemm_wgrad_tok(
+        NR, NC, K, _ptr(X), lda, _ptr(Y), ldb, _ptr(gamma), _ptr(W), _ptr(dW),
+        _ptr(partials) if W is not None else None, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dW, (partials if W is not None else None)
+
+
 def colsum_reduce(partials, out=None, stream=None):
     """out [NC] = sum over the rows of partials [T, NC] (fixed order, fp64 inside)."""
     T, NC = partials.shape
@@ -349,11 +375,13 @@ def colsum_reduce(partials, out=None, stream=None):
 def mlpin_wgrad(dz, h, gamma, W, dzt=None, ht=None, out=None, stream=None):
     """Weight gradients of the MLP-input block from the backward's dz = r * dL/dz [M, 2F]
     and the block input h [M, d]: returns (dW [2F, d], dgamma [d]) for the raw weight
-    W [2F, d] and gamma [d].  dzt / ht may pass already transposed operands."""
+    W [2F, d] and gamma [d].  The GEMM reads dz and h as stored (token-major); with both
+    dzt and ht given it reads those transposed copies instead."""
     out = out or {}
-    dzt = transpose_bf16(dz, out.get("dzt"), stream) if dzt is None else dzt
-    ht = transpose_bf16(h, out.get("ht"), stream) if ht is None else ht
-    dW, P = gemm_wgrad(dzt, ht, gamma, W, out.get("dW"), out.get("wpartials"), stream=stream)
+    if dzt is not None and ht is not None:
+        dW, P = gemm_wgrad(dzt, ht, gamma, W, out.get("dW"), out.get("wpartials"), stream=stream)
+    else:
+        dW, P = gemm_wgrad_tok(dz, h, gamma, W, out.get("dW"), out.get("wpartials"), stream=stream)
     dgam = colsum_reduce(P, out.get("dgamma"), stream)
     return dW, dgam
 
@@ -369,16 +397,14 @@ def chain_bwd(A, WoT, h, r, Wp, Wpt, W, gamma, dy, dres=None, z=None, out=None, 
     out = out or {}
     if z is None:
         dh, dz, _, _ = mlpin_bwd(h, Wp, Wpt, r, dy, dres, out, stream)
-        dzt = None
     else:
-        dz, dzt, P = swiglu_bwd_saved(z, dy, r, out.get("dz"), out.get("dzt"), out.get("partials"), True, stream)
+        dz, _, P = swiglu_bwd_saved(z, dy, r, out.get("dz"), None, out.get("partials"), False, stream)
         q = rmsnorm_bwd_reduce(P, r, h.shape[1], z.shape[1] // 2, out.get("q"), stream)
         dh = gemm_rmsnorm_bwd(dz, Wpt, h, q, dres, out.get("dh"), stream)
-    dW, dgam = mlpin_wgrad(dz, h, gamma, W, dzt=dzt, out=out, stream=stream)
+    # the weight gradients read dz, h, dh and A as stored (token-major): no transposes
+    dW, dgam = mlpin_wgrad(dz, h, gamma, W, out=out, stream=stream)
     dA = gemm_bf16(dh, WoT, None, out.get("dA"), stream)
-    dht = transpose_bf16(dh, out.get("dht"), stream)
-    At = transpose_bf16(A, out.get("At"), stream)
-    dWo, _ = gemm_wgrad(dht, At, None, None, out.get("dWo"), None, out.get("ws", "auto"), stream)
+    dWo, _ = gemm_wgrad_tok(dh, A, None, None, out.get("dWo"), None, out.get("ws", "auto"), stream=stream)
     return dict(dh=dh, dA=dA, dWo=dWo, dW=dW, dgamma=dgam)
 
 

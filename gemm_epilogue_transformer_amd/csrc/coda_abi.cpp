@@ -450,6 +450,41 @@ coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, c
                                               static_cast<float*>(workspace), workspace_bytes, s));
 }
 
+coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda, const void* Y,
+                                int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0)) return CODA_ERR_SHAPE;
+    if (NC % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || lda < NR || ldb < NC) return CODA_ERR_SHAPE;
+    if (lda > kMaxRow || ldb > kMaxRow || NC > kMaxRow / 2) return CODA_ERR_SHAPE;
+    // token rows addressed with 32-bit offsets (and the DMA runs up to 3 k-tiles past the end)
+    if ((K + 256) * lda * 2 > (int64_t(1) << 31) || (K + 256) * ldb * 2 > (int64_t(1) << 31)) return CODA_ERR_SHAPE;
+    const int64_t T = coda::wgrad_partials_rows(NR);
+    if (!prod_ok(NR, NC) || !prod_ok(T, NC)) return CODA_ERR_SHAPE;
+    if (coda::wgrad_tiles(NR, NC) > kMaxDim) return CODA_ERR_SHAPE;
+    if (!dW || (W && !partials) || (K > 0 && (!X || !Y))) return CODA_ERR_NULL;
+    if (!aligned16(dW) || (W && !aligned16(W)) || (gamma && !aligned16(gamma)) || (partials && !aligned16(partials)) ||
+        (K > 0 && (!aligned16(X) || !aligned16(Y))))
+        return CODA_ERR_ALIGN;
+    if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return CODA_ERR_VALUE;
+    if (workspace && !aligned16(workspace)) return CODA_ERR_ALIGN;
+    const Range ro = span(dW, NR * NC * 4), rp = W ? span(partials, T * NC * 4) : span(nullptr, 0);
+    const Range rw = workspace ? span(workspace, workspace_bytes) : span(nullptr, 0);
+    if ((W && overlap(ro, rp)) || overlap(ro, rw) || overlap(rp, rw)) return CODA_ERR_ALIAS;
+    const Range ins[] = {K > 0 ? span(X, K * lda * 2) : span(nullptr, 0), K > 0 ? span(Y, K * ldb * 2) : span(nullptr, 0),
+                         gamma ? span(gamma, NC * 4) : span(nullptr, 0), W ? span(W, NR * NC * 2) : span(nullptr, 0)};
+    for (const Range& in : ins)
+        if (overlap(ro, in) || (W && overlap(rp, in)) || overlap(rw, in)) return CODA_ERR_ALIAS;
+    hipStream_t s = as_stream(stream);
+    if (K == 0) {
+        hipError_t e = coda::launch_fill_zero_f32(NR * NC, dW, s);
+        if (e == hipSuccess && W) e = coda::launch_fill_zero_f32(T * NC, partials, s);
+        return hip_status(e);
+    }
+    return hip_status(coda::launch_gemm_wgrad_tok(int(NR), int(NC), int(K), X, int(lda), Y, int(ldb), gamma, W, dW,
+                                                  W ? partials : nullptr, static_cast<float*>(workspace),
+                                                  workspace_bytes, s));
+}
+
 coda_status coda_colsum_reduce(int64_t T, int64_t NC, const float* partials, float* out, void* stream) {
     if (!dim_ok(T, 1) || !dim_ok(NC, 1) || !prod_ok(T, NC)) return CODA_ERR_SHAPE;
     if (!partials || !out) return CODA_ERR_NULL;

@@ -225,6 +225,111 @@ struct Frags<Elt::E4M3, TM, TN, RB> {
     }
 };
 
+// ---------------------------------------------------------------------------------
+// Token-major operands (the weight gradients, whose contraction runs over the tokens of
+// row-major activations: G[j,k] = sum_m X[m,j] Y[m,k]).  A panel is 256 columns (512
+// bytes) of 64 consecutive token rows per k-tile; in LDS each token row is 512 bytes with
+// its 16-byte chunks XOR-swizzled by (token row mod 4) * 4, applied on the global side so
+// the DMA writes stay linear.  Fragments come from LDS transpose reads
+// (ds_read_b64_tr_b16): within each 16-lane group, lane L reads 4 consecutive columns of
+// token row L / 4, and lane i receives column i of those 4 token rows, i.e. 4 consecutive
+// k of one MFMA row; two reads give the 8 k a 32x32x16 fragment lane holds.  With the
+// swizzle the 4 token rows of a read land in 4 different 16-bank groups.
+template <int NW>
+struct DmaPanelTok {
+    static constexpr int kTok = 64;                   // tokens per k-tile
+    static constexpr int kRowBytes = 512;             // 256 bf16 columns
+    static constexpr int kRowsPerInst = 2 * NW;       // token rows per instruction index
+    static constexpr int kInst = kTok / kRowsPerInst; // DMA instructions per wave per k-tile
+    static_assert(NW % 2 == 0, "a lane's token row phase (mod 4) must not depend on the instruction");
+    u32x4_t rsrc;
+    uint32_t off0;      // byte offset of this lane's chunk in instruction 0 of k-tile 0
+    uint32_t stride;    // bytes between instruction j and j + 1
+    uint32_t tile;      // bytes between k-tiles (64 token rows)
+    bool col_in;        // this lane's chunk lies inside the matrix's columns
+
+    // base: the panel's first column in token row 0 (of the range); tokens: token rows in
+    // range from base (rows past them read zeros); ld: bytes between token rows; cols:
+    // columns of the panel inside the matrix (chunks past them read zeros).
+    __device__ __forceinline__ void init(const uint8_t* base, int tokens, int ld, int cols) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int r = 2 * wave + (lane >> 5);          // token row in instruction 0
+        const int p = lane & 31;                       // chunk position in the LDS row
+        const int c = p ^ ((r & 3) << 2);              // chunk of the matrix row it holds
+        col_in = c * 8 < cols;
+        rsrc = make_rsrc(base, static_cast<uint32_t>(max(tokens, 0)) * static_cast<uint32_t>(ld));
+        off0 = static_cast<uint32_t>(r) * ld + static_cast<uint32_t>(c) * 16;
+        stride = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kRowsPerInst) * static_cast<uint32_t>(ld));
+        tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kTok) * static_cast<uint32_t>(ld));
+    }
+    // k-tile kt's offset of this lane's chunk (kOob for a chunk past the columns; rows past
+    // the token range fall outside the descriptor and read zeros)
+    __device__ __forceinline__ uint32_t base_offset(int kt, int /*kbytes*/) const {
+        uint32_t base = col_in ? off0 + static_cast<uint32_t>(kt) * tile : kOob;
+        asm volatile("" : "+v"(base));
+        return base;
+    }
+    __device__ __forceinline__ void issue_one(int j, uint8_t* stage, uint32_t base) const {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        dma16(rsrc, base + static_cast<uint32_t>(j) * stride, lds_addr(stage + (2 * (NW * j + wave)) * kRowBytes));
+    }
+    __device__ __forceinline__ void issue(uint8_t* stage, int kt, int kbytes) const {
+        const uint32_t base = base_offset(kt, kbytes);
+#pragma unroll
+        for (int j = 0; j < kInst; ++j) issue_one(j, stage, base);
+    }
+};
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Fragments of 32x32x16 bf16 MFMAs from token-major LDS panels (DmaPanelTok layout):
+// k-step s covers tokens 16 s .. 16 s + 15 of the k-tile; a_row / b_row give the first
+// panel column of a block (a multiple of 32).
+template <int TM, int TN>
+struct FragsTok {
+    static constexpr int kSteps = DmaPanelTok<2>::kTok / 16;
+    static constexpr int kReads = TM + TN;
+    bf16x8_t a[TM], b[TN];
+    __device__ __forceinline__ static bf16x8_t read(const uint8_t* panel, int col0, int s) {
+        const int lane = threadIdx.x & 63;
+        const int g = lane >> 4, L = lane & 15;
+        const int col = col0 + 16 * (g & 1) + 4 * (L & 3);
+        i16x4_t v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tt = 16 * s + 8 * (g >> 1) + 4 * h + (L >> 2);
+            const int off = tt * DmaPanelTok<2>::kRowBytes + (((col >> 3) ^ ((tt & 3) << 2)) << 4) + (col & 7) * 2;
+            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)((__attribute__((address_space(3))) uint8_t*)(lds_ptr_t)panel + off));
+        }
+        const i16x4_t lo = v[0], hi = v[1];
+        return __builtin_bit_cast(bf16x8_t, (short __attribute__((ext_vector_type(8)))){
+            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    }
+    template <class ARow, class BRow>
+    __device__ __forceinline__ void load_one(int i, const uint8_t* sA, const uint8_t* sB, int s,
+                                             const ARow& a_row, const BRow& b_row) {
+        if (i == 0)
+            a[0] = read(sA, a_row(0), s);
+        else if (i <= TN)
+            b[i - 1] = read(sB, b_row(i - 1), s);
+        else
+            a[i - TN] = read(sA, a_row(i - TN), s);
+    }
+    template <class ARow, class BRow>
+    __device__ __forceinline__ void load(const uint8_t* sA, const uint8_t* sB, int s,
+                                         const ARow& a_row, const BRow& b_row) {
+#pragma unroll
+        for (int i = 0; i < kReads; ++i) load_one(i, sA, sB, s, a_row, b_row);
+    }
+    __device__ __forceinline__ void mma_one(int i, f32x16_t (&acc)[TM][TN]) const {
+        const int tm = i / TN, tn = i % TN;
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+    }
+};
+
 // Compile-time loop: f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>).
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -348,17 +453,16 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // after A).  kbytes is the byte length of an A row (k-tile count = ceil(kbytes / RBA));
 // the B panel's descriptor and K-tail checks use its own row length, set at init.
 template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
-          class ARow, class BRow>
-__device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RBA>& pa,
-                                                const DmaPanel<BN, SPLIT, NW, RBB>& pb, int kbytes,
+          class ARow, class BRow, class PA, class PB>
+__device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,
                                                 int kbytes_b, uint8_t* const (&st)[NS],
                                                 const ARow& a_row, const BRow& b_row) {
     static_assert(NS >= 2, "at least two stages");
     constexpr int KS = FP::kSteps;
     static_assert((NS * KS) % 2 == 0, "fragment double-buffer parity must repeat every stage group");
     constexpr int kMfma = TM * TN;
-    constexpr int nA = DmaPanel<BM, BM, NW, RBA>::kInst;
-    constexpr int kPerTile = nA + DmaPanel<BN, SPLIT, NW, RBB>::kInst;   // DMA per wave per tile
+    constexpr int nA = PA::kInst;
+    constexpr int kPerTile = nA + PB::kInst;   // DMA per wave per tile
     static_assert((NS - 1) * kPerTile < 64, "vmcnt range");
     static_assert(SPREAD >= 1 && SPREAD <= KS, "the DMA of a tile ends before the next tile's last k-step");
     constexpr int kPer = (kPerTile + SPREAD - 1) / SPREAD;            // DMA per k-step

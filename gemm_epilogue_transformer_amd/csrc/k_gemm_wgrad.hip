@@ -26,11 +26,16 @@ namespace coda {
 // Split over the tokens (S > 1, only without W): block (s, tile) sums tokens
 // [s * k_split, min((s + 1) * k_split, K)) and writes its raw sums (no gamma) to slice s
 // of dW, which is then the [S, NR, NC] workspace that k_splitk_reduce adds up.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC>
+//
+// TOK: the operands are token-major, X [K, lda] and Y [K, ldb] (the activations as the
+// forward and backward store them, NR and NC of their columns used), read through LDS
+// transpose reads (DmaPanelTok / FragsTok); otherwise token-contiguous At [NR, K] and
+// Bt [NC, K] (lda, ldb unused).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC, bool TOK>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, const float* __restrict__ gamma,
              const uint16_t* __restrict__ Wraw, float* __restrict__ dW, float* __restrict__ Pg, int NR, int NC,
-             int K, int tiles_m, int tiles_n, int k_split) {
+             int K, int tiles_m, int tiles_n, int k_split, int lda, int ldb) {
     constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -50,16 +55,8 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    // rows are K tokens apart; this block reads tokens [k0, k0 + kext) of each (the
-    // descriptors start at token k0, the mainloop stops at kext)
-    const int kbytes = K * 2;
-    const int k0 = split * k_split, kext = min(k_split, K - k0) * 2;
-    DmaPanel<BM, BM, NW, RB> pa;
-    DmaPanel<BN, BN, NW, RB> pb;
-    const uint8_t* a0 = At + static_cast<size_t>(m0) * kbytes + static_cast<size_t>(k0) * 2;
-    const uint8_t* b0 = Bt + static_cast<size_t>(n0) * kbytes + static_cast<size_t>(k0) * 2;
-    pa.init(a0, min(BM, NR - m0), a0, 0, kbytes);
-    pb.init(b0, min(BN, NC - n0), b0, 0, kbytes);
+    const int k0 = split * k_split, ktok = min(k_split, K - k0);   // this block's tokens
+    const int kext = ktok * 2;
     auto a_row = [&](int tm) { return wm * WM + tm * 32; };
     auto b_row = [&](int tn) { return wn * WN + tn * 32; };
 
@@ -71,7 +68,27 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    mainloop_dma<Elt::BF16, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kext, st, a_row, b_row);
+    if constexpr (TOK) {
+        static_assert(BM == 256 && BN == 256 && RB == 128, "token-major panels are 256 columns x 64 tokens");
+        // token row k0 of X, column m0 (and of Y, column n0); rows past this block's
+        // tokens are outside the descriptors and read zeros
+        DmaPanelTok<NW> pa, pb;
+        pa.init(At + (static_cast<size_t>(k0) * lda + m0) * 2, ktok, lda * 2, NR - m0);
+        pb.init(Bt + (static_cast<size_t>(k0) * ldb + n0) * 2, ktok, ldb * 2, NC - n0);
+        mainloop_dma_fp<FragPair<FragsTok<TM, TN>>, BM, BN, BN, NS, NW, RB, RB, SPREAD>(acc, pa, pb, kext, kext, st,
+                                                                                      a_row, b_row);
+    } else {
+        // rows are K tokens apart; this block reads tokens [k0, k0 + ktok) of each (the
+        // descriptors start at token k0, the mainloop stops at kext)
+        const int kbytes = K * 2;
+        DmaPanel<BM, BM, NW, RB> pa;
+        DmaPanel<BN, BN, NW, RB> pb;
+        const uint8_t* a0 = At + static_cast<size_t>(m0) * kbytes + static_cast<size_t>(k0) * 2;
+        const uint8_t* b0 = Bt + static_cast<size_t>(n0) * kbytes + static_cast<size_t>(k0) * 2;
+        pa.init(a0, min(BM, NR - m0), a0, 0, kbytes);
+        pb.init(b0, min(BN, NC - n0), b0, 0, kbytes);
+        mainloop_dma<Elt::BF16, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kext, st, a_row, b_row);
+    }
     dW += static_cast<size_t>(split) * NR * NC;
 
     using S = Slab<TN>;
@@ -234,9 +251,10 @@ int64_t wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K) {
     return S > 1 ? static_cast<int64_t>(S) * NR * NC * 4 : 0;
 }
 
-hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
-                             const void* Wraw, float* dW, float* Pg, float* ws, int64_t ws_bytes,
-                             hipStream_t stream) {
+template <bool TOK>
+static hipError_t launch_wgrad(int NR, int NC, int K, const void* At, int lda, const void* Bt, int ldb,
+                               const float* gamma, const void* Wraw, float* dW, float* Pg, float* ws,
+                               int64_t ws_bytes, hipStream_t stream) {
     const int tiles_m = (NR + BMW - 1) / BMW, tiles_n = (NC + BNW - 1) / BNW;
     int S = Wraw ? 1 : wgrad_splits(NR, NC, K);
     if (S > 1 && (ws == nullptr || ws_bytes < static_cast<int64_t>(S) * NR * NC * 4)) S = 1;
@@ -245,10 +263,10 @@ hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* 
     S = (K + k_split - 1) / k_split;
     const dim3 grid(tiles_m * tiles_n * S), block(64 * CODA_WG_WM * CODA_WG_WN);
     hipLaunchKernelGGL((k_gemm_wgrad<BMW, BNW, CODA_WG_WM, CODA_WG_WN, CODA_WG_NS, CODA_WG_RB, CODA_WG_SPREAD,
-                                     CODA_WG_OCC>),
+                                     CODA_WG_OCC, TOK>),
                        grid, block, 0, stream, static_cast<const uint8_t*>(At), static_cast<const uint8_t*>(Bt),
                        S > 1 ? nullptr : gamma, static_cast<const uint16_t*>(Wraw), S > 1 ? ws : dW, Pg, NR, NC,
-                       K, tiles_m, tiles_n, k_split);
+                       K, tiles_m, tiles_n, k_split, lda, ldb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     const int64_t n4 = static_cast<int64_t>(NR) * NC / 4;
@@ -256,6 +274,18 @@ hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* 
     hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                        reinterpret_cast<const f32x4_t*>(ws), gamma, reinterpret_cast<f32x4_t*>(dW), n4, NC / 4, S);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
+                             const void* Wraw, float* dW, float* Pg, float* ws, int64_t ws_bytes,
+                             hipStream_t stream) {
+    return launch_wgrad<false>(NR, NC, K, At, 0, Bt, 0, gamma, Wraw, dW, Pg, ws, ws_bytes, stream);
+}
+
+hipError_t launch_gemm_wgrad_tok(int NR, int NC, int K, const void* X, int lda, const void* Y, int ldb,
+                                 const float* gamma, const void* Wraw, float* dW, float* Pg, float* ws,
+                                 int64_t ws_bytes, hipStream_t stream) {
+    return launch_wgrad<true>(NR, NC, K, X, lda, Y, ldb, gamma, Wraw, dW, Pg, ws, ws_bytes, stream);
 }
 
 hipError_t launch_colsum_reduce(int T, int NC, const float* Pg, float* out, hipStream_t stream) {

@@ -76,6 +76,9 @@ int64_t wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K);
 hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
                              const void* Wraw, float* dW, float* Pg, float* ws, int64_t ws_bytes,
                              hipStream_t stream);
+hipError_t launch_gemm_wgrad_tok(int NR, int NC, int K, const void* X, int lda, const void* Y, int ldb,
+                                 const float* gamma, const void* Wraw, float* dW, float* Pg, float* ws,
+                                 int64_t ws_bytes, hipStream_t stream);
 hipError_t launch_colsum_reduce(int T, int NC, const float* Pg, float* out, hipStream_t stream);
 hipError_t launch_fill_zero_f32(int64_t n, float* dst, hipStream_t stream);
 

@@ -358,6 +358,20 @@ coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, c
                             const float* gamma, const void* W, float* dW, float* partials,
                             void* workspace, int64_t workspace_bytes, void* stream);
 
+/* The same weight-gradient GEMM on token-major operands, as the activations are stored
+ * (no transposes): the contraction runs down the rows of
+ *   X [K, lda] bf16, its first NR columns (e.g. r * dL/dz [M, 2F]: lda = NR = 2F)
+ *   Y [K, ldb] bf16, its first NC columns (e.g. h [M, d]: ldb = NC = d)
+ *   dW[j,k] = fl32( gamma[k] * sum_m X[m,j] Y[m,k] ); gamma, W, partials, workspace and the
+ *   token split exactly as coda_gemm_wgrad (workspace sized by coda_wgrad_workspace_bytes).
+ * The tiles are read through LDS transpose reads; the result is bit-identical to
+ * coda_gemm_wgrad on the transposed operands with the same split.  Any K (K = 0 writes
+ * zeros).  Granules: NC % 8 == 0, lda % 8 == 0, ldb % 8 == 0, lda >= NR, ldb >= NC;
+ * (K + 256) * lda * 2 and (K + 256) * ldb * 2 at most 2^31.                           */
+coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda, const void* Y,
+                                int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
+                                void* workspace, int64_t workspace_bytes, void* stream);
+
 /* out[k] = fl32( sum_t partials[t, k] )  (fixed order, fp64 inside), T >= 1 rows of NC
  * columns: the gamma gradient from coda_gemm_wgrad's partials.  out must not overlap.  */
 coda_status coda_colsum_reduce(int64_t T, int64_t NC, const float* partials, float* out,

@@ -305,3 +305,17 @@ def test_on_chip_fold_validation():
     assert f(16, 64, 64, 1, P1, P2, P3 + 4, P4, P5, None) == ALIGN
     assert f(16, 64, 64, 1, P1, P2, P3, P4, P3, None) == ALIAS              # y over gamma
     assert f(0, 64, 64, 1, None, None, None, None, None, None) == OK
+
+
+@no_gpu
+def test_token_major_weight_gradient_validation():
+    L = _lib.load()
+    w = L.coda_gemm_wgrad_tok
+    # NR, NC, K, X, lda, Y, ldb, gamma, W, dW, partials, workspace, workspace_bytes, stream
+    assert w(64, 60, 64, P1, 64, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # NC % 8
+    assert w(64, 64, 64, P1, 60, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # lda % 8
+    assert w(72, 64, 64, P1, 64, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # lda < NR
+    assert w(64, 64, 1 << 22, P1, 512, P2, 64, None, None, P5, None, None, 0, None) == SHAPE  # 32-bit rows
+    assert w(64, 64, 13, None, 64, P2, 64, None, None, P5, None, None, 0, None) == NULL
+    assert w(64, 64, 13, P1, 64, P2, 64, None, None, P1 + 64, None, None, 0, None) == ALIAS  # dW over X
+    assert w(64, 64, 13, P1, 64, P2 + 8, 64, None, None, P5, None, None, 0, None) == ALIGN

@@ -192,3 +192,39 @@ def test_token_split_matches_the_definition_and_is_reproducible():
         err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
         _log(f"  token split err max {err.max():.2e}, bound min {bound.min():.2e}")
         assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("K,NR,NC,lda,ldb", [(712, 300, 136, 304, 136), (520, 264, 72, 264, 80), (8200, 520, 136, 520, 136),
+                                             (64, 8, 8, 8, 8)])
+def test_token_major_operands_match_the_transposed_path(K, NR, NC, lda, ldb):
+    # the same MFMA k order: bit-identical to the GEMM on the transposed copies, with and
+    # without the raw weight's partials and the token split
+    print(f"wgrad tok K={K} NR={NR} NC={NC} lda={lda} ldb={ldb}", flush=True)
+    rng = np.random.default_rng(K + NR + NC)
+    X = dev_bf16(si.to_bf16_bits(rng.standard_normal((K, lda)).astype(np.float32)))
+    Y = dev_bf16(si.to_bf16_bits(rng.standard_normal((K, ldb)).astype(np.float32)))
+    W = dev_bf16(si.to_bf16_bits(rng.standard_normal((NR, NC)).astype(np.float32)))
+    g = torch.from_numpy((1 + 0.1 * rng.standard_normal(NC)).astype(np.float32)).cuda()
+    Xt = X[:, :NR].t().contiguous()
+    Yt = Y[:, :NC].t().contiguous()
+    t_dW, t_P = coda.gemm_wgrad_tok(X, Y, g, W, NR=NR, NC=NC)
+    r_dW, r_P = coda.gemm_wgrad(Xt, Yt, g, W)
+    t_s, _ = coda.gemm_wgrad_tok(X, Y, g, None, NR=NR, NC=NC, workspace="auto")
+    r_s, _ = coda.gemm_wgrad(Xt, Yt, g, None, workspace="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(t_dW, r_dW) and torch.equal(t_P, r_P) and torch.equal(t_s, r_s)
+
+
+@pytest.mark.parametrize("K", [1, 13, 77, 200])
+def test_token_major_any_token_count(K):
+    # no granule on the tokens: against the fp64 definition, |err| <= (K + 2) 2^-24 sum|terms|
+    rng = np.random.default_rng(50 + K)
+    NR, NC = 136, 72
+    xb = si.to_bf16_bits(rng.standard_normal((K, NR)).astype(np.float32))
+    yb = si.to_bf16_bits(rng.standard_normal((K, NC)).astype(np.float32))
+    dW, _ = coda.gemm_wgrad_tok(dev_bf16(xb), dev_bf16(yb))
+    torch.cuda.synchronize()
+    Xd, Yd = oracle.bf16_decode(xb), oracle.bf16_decode(yb)
+    ref = Xd.T @ Yd
+    bound = (K + 2) * 2.0 ** -24 * (np.abs(Xd).T @ np.abs(Yd))
+    assert np.all(np.abs(dW.cpu().numpy().astype(np.float64) - ref) <= bound)
