@@ -26,6 +26,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two round-to-nearest-even conversions in one v_cvt_pk_bf16_f32 (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
+}
+
 // ------------------------------------------------------------------ e4m3 ----------
 // OCP E4M3FN: bias 7, 3 mantissa bits, max 448, no infinities, NaN = S.1111.111.
 

@@ -96,8 +96,5 @@ struct MaxOp {
     __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return static_cast<uint32_t>(f32_to_bf16_bits(a)) | (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
-}
 
 }  // namespace coda

@@ -654,7 +654,7 @@ struct GammaFold {
             const uint32_t u = static_cast<uint32_t>(v[h]);
             const float p0 = g[2 * h] * bf16_bits_to_f32(static_cast<uint16_t>(u & 0xFFFFu));
             const float p1 = g[2 * h + 1] * bf16_bits_to_f32(static_cast<uint16_t>(u >> 16));
-            o[h] = static_cast<int>(uint32_t(f32_to_bf16_bits(p0)) | (uint32_t(f32_to_bf16_bits(p1)) << 16));
+            o[h] = static_cast<int>(pack_bf16x2(p0, p1));
         }
         return o;
     }

@@ -106,12 +106,11 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t x = static_cast<uint32_t>(xr[tm & 1][j][e]);
-                const uint16_t h0 = f32_to_bf16_bits(t[2 * e] + bf16_bits_to_f32(static_cast<uint16_t>(x & 0xFFFFu)));
-                const uint16_t h1 = f32_to_bf16_bits(t[2 * e + 1] + bf16_bits_to_f32(static_cast<uint16_t>(x >> 16)));
-                const float q0 = bf16_bits_to_f32(h0), q1 = bf16_bits_to_f32(h1);
+                o[e] = pack_bf16x2(t[2 * e] + bf16_bits_to_f32(static_cast<uint16_t>(x & 0xFFFFu)),
+                                   t[2 * e + 1] + bf16_bits_to_f32(static_cast<uint16_t>(x >> 16)));
+                const float q0 = __uint_as_float(o[e] << 16), q1 = __uint_as_float(o[e] & 0xFFFF0000u);
                 sq += q0 * q0;
                 sq += q1 * q1;
-                o[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
             }
             __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])},
                                                    h_rsrc, seg_voff(tm, j), 0, 0);

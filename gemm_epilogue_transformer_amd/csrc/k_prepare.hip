@@ -31,7 +31,7 @@ k_fold_bf16(const i32x4_t* __restrict__ W, const float* __restrict__ gamma,
             const float g1 = gamma ? gamma[k0 + 2 * h + 1] : 1.0f;
             const float p0 = g0 * bf16_bits_to_f32(static_cast<uint16_t>(u & 0xFFFFu));
             const float p1 = g1 * bf16_bits_to_f32(static_cast<uint16_t>(u >> 16));
-            o[h] = static_cast<int>(uint32_t(f32_to_bf16_bits(p0)) | (uint32_t(f32_to_bf16_bits(p1)) << 16));
+            o[h] = static_cast<int>(pack_bf16x2(p0, p1));
         }
         Wp[v] = o;
     }
