@@ -15,6 +15,9 @@ roofline   = the second GEMM kernel (the dominant one): its algorithmic FLOPs / 
              taken on the current kernel sources, else null
 cpu_baseline = the fp64 oracle on a bounded row sample of the same workload, on the
              host cores, scaled to TFLOP/s
+hbm_bytes_measured = L2-miss bytes of one whole step of the fused chain and of the
+             unfused torch chain, from the committed counter summary (two
+             --traffic-probe runs differenced) when taken on the current kernel sources
 """
 
 from __future__ import annotations
@@ -139,6 +142,82 @@ def _counter_means(directory: str, counter: str) -> dict:
         acc.setdefault(name, {}).setdefault(r["Dispatch_Id"], 0.0)
         acc[name][r["Dispatch_Id"]] += float(r["Counter_Value"])
     return {k: sum(v.values()) / len(v) for k, v in acc.items()}
+
+
+def _counter_sums(directory: str, counter: str) -> dict:
+    """Sum of a derived counter over all dispatches, per kernel name (rocprofv3 CSV)."""
+    acc = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") == counter:
+            acc[r["Kernel_Name"]] = acc.get(r["Kernel_Name"], 0.0) + float(r["Counter_Value"])
+    return acc
+
+
+def _short_kernel_name(name: str) -> str:
+    name = name.replace("void ", "")
+    return (name.split("(")[0].split("<")[0])[:72]
+
+
+def ingest_step_traffic(args_list, workload: str, copy_bytes: int, command: str) -> None:
+    """HBM bytes of one whole step of the fused chain and of the unfused torch chain.
+
+    args_list: n_small n_big, then for the fused and the unfused path the FETCH_SIZE run
+    at n_small and n_big steps and the WRITE_SIZE run at n_small and n_big steps
+    (``--traffic-probe``), then the FETCH_SIZE and WRITE_SIZE runs of the plain copy.  The
+    setup launches the same kernels at both step counts, so the difference of the summed
+    counters over n_big - n_small steps is what the steps themselves moved; each counter
+    is divided by what it reads per byte of the plain copy."""
+    import torch
+
+    n_small, n_big = int(args_list[0]), int(args_list[1])
+    dirs = args_list[2:]
+    pick = lambda d: next(v for k, v in d.items() if "copy" in k.lower())  # noqa: E731
+    kib = copy_bytes / 1024.0
+    ff = pick(_counter_means(dirs[8], "FETCH_SIZE")) / kib
+    fw = pick(_counter_means(dirs[9], "WRITE_SIZE")) / kib
+    steps = n_big - n_small
+    rec = {"workload": workload, "steps_differenced": steps, "copy_factor_fetch": ff, "copy_factor_write": fw,
+           "fused_source_hash": kernel_source_hash(), "torch": torch.__version__, "command": command}
+    lines = [f"# HBM bytes per step (FETCH_SIZE / copy factor + WRITE_SIZE / copy factor), workload {workload}",
+             f"# commands: {command}",
+             f"# per step = (counters summed over a run of {n_big} steps - the same over {n_small} steps) / {steps};"
+             f" copy factors FETCH_SIZE {ff:.4f}, WRITE_SIZE {fw:.4f} KiB per KiB copied",
+             "path, kernel, fetch bytes per step, write bytes per step"]
+    for i, path in enumerate(("fused", "unfused")):
+        fs, fb, ws, wb = (_counter_sums(d, c) for d, c in
+                          zip(dirs[4 * i: 4 * i + 4], ("FETCH_SIZE", "FETCH_SIZE", "WRITE_SIZE", "WRITE_SIZE")))
+        per = {}
+        for small, big, slot in ((fs, fb, 0), (ws, wb, 1)):
+            for k in set(small) | set(big):
+                v = (big.get(k, 0.0) - small.get(k, 0.0)) * 1024 / (ff if slot == 0 else fw) / steps
+                per.setdefault(_short_kernel_name(k), [0.0, 0.0])[slot] += v
+        # kernels of the setup alone difference to zero
+        per = {k: v for k, v in per.items() if abs(v[0]) + abs(v[1]) >= 1.0}
+        total = sum(v[0] + v[1] for v in per.values())
+        rec[path] = {"hbm_bytes_per_step": round(total),
+                     "kernels": {k: [round(v[0]), round(v[1])] for k, v in sorted(per.items())}}
+        for k, v in sorted(per.items(), key=lambda kv: -(kv[1][0] + kv[1][1])):
+            lines.append(f"{path}, {k}, {v[0]:.0f}, {v[1]:.0f}")
+        lines.append(f"{path}, TOTAL, {total:.0f}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"step_traffic_{workload}.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(os.path.join(ROOT, "profiles", f"step_traffic_{workload}.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_step_traffic(workload: str):
+    """Measured HBM bytes per step of the fused and the unfused chain, if the fused ones
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"step_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("fused_source_hash") != kernel_source_hash():
+        return None
+    f, u = rec["fused"]["hbm_bytes_per_step"], rec["unfused"]["hbm_bytes_per_step"]
+    return {"fused": f, "unfused": u, "unfused_over_fused": round(u / f, 3), "torch": rec.get("torch")}
 
 
 def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
@@ -462,7 +541,21 @@ def main():
                     help="write profiles/traffic_*.json from rocprofv3 --pmc output dirs: "
                          "FETCH_SIZE run, WRITE_SIZE run, FETCH_SIZE copy run, WRITE_SIZE copy run")
     ap.add_argument("--ingest-command", default="", help="command line recorded with --ingest-traffic")
+    ap.add_argument("--traffic-probe", choices=("fused", "unfused"), default=None,
+                    help="forward bf16 workloads: after the setup run exactly --steps steps of one path "
+                         "(no warm-up, no timing) and exit; two such runs under rocprofv3 --pmc at two "
+                         "step counts give the HBM bytes of one step by difference")
+    ap.add_argument("--ingest-step-traffic", nargs=12, metavar="ARG",
+                    help="write profiles/step_traffic_<workload>.json: n_small n_big, then FETCH_SIZE "
+                         "small / big and WRITE_SIZE small / big run dirs of the fused probe, the same "
+                         "four of the unfused probe, then the FETCH_SIZE and WRITE_SIZE copy run dirs")
     args = ap.parse_args()
+    if args.ingest_step_traffic:
+        import synth_inputs as si
+
+        ingest_step_traffic(args.ingest_step_traffic, si.WORKLOADS[args.workload].name,
+                            (args.copy_calibration or 1024) << 20, args.ingest_command)
+        return
     if args.ingest_traffic:
         import synth_inputs as si
 
@@ -557,6 +650,39 @@ def main():
             if ev is not None:
                 ev[4].record(stream)
 
+    # the unfused chain in torch (hipBLASLt GEMMs, element-wise RMSNorm / activation kernels)
+    def unfused():
+        t = A @ Wo.t()
+        hh = xr + t
+        hf = hh.float()
+        n = (hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + w.eps)).to(torch.bfloat16) \
+            * gamma.to(torch.bfloat16)
+        z = n @ W.t()
+        if w.act == si.ACT_SWIGLU:
+            F_ = w.n_out
+            return torch.nn.functional.silu(z[:, :F_]) * z[:, F_:]
+        if w.act == si.ACT_CE:
+            return torch.nn.functional.cross_entropy(z.float(), ce_in["targets"].long(), reduction="none")
+        if w.act == si.ACT_ROPE:
+            pos_t, cos_t, sin_t = rope_in
+            q = z[:, : w.rot_cols].view(M, -1, 64)
+            c, s_ = cos_t[pos_t].unsqueeze(1), sin_t[pos_t].unsqueeze(1)
+            x1, x2 = q[..., :32], q[..., 32:]
+            rq = torch.cat([x1 * c - x2 * s_, x2 * c + x1 * s_], -1).to(torch.bfloat16)
+            return torch.cat([rq.view(M, -1), z[:, w.rot_cols:]], 1)
+        return z
+
+    if args.traffic_probe:
+        if w.dtype != "bf16":
+            print("bench.py: --traffic-probe covers the bf16 workloads", file=sys.stderr)
+            sys.exit(2)
+        run = step if args.traffic_probe == "fused" else unfused
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": args.traffic_probe, "workload": w.name, "steps": args.steps}), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -627,6 +753,7 @@ def main():
                        **({"ce_reduce": round(k4_ms, 4)} if k4_ms is not None else {})},
         "gemm1_tflops": round(g1_flops / (k1_ms * 1e-3) / 1e12, 2),
         "hbm_bytes_algorithmic": {"fused": byt["total"], "unfused": algorithmic_bytes(w, False)["total"]},
+        "hbm_bytes_measured": load_step_traffic(w.name),
         "prep_ms": round(prep_ms, 3),
         "roofline": roof,
         "kernel_source_hash": kernel_source_hash(),
@@ -636,27 +763,6 @@ def main():
         rec["graph"] = {"ms_per_step": round(graph_ms, 4), "value": round(flops / (graph_ms * 1e-3) / 1e12, 2),
                         "note": "the same step replayed from a captured HIP graph"}
     if args.unfused and w.dtype == "bf16":
-        def unfused():
-            t = A @ Wo.t()
-            hh = xr + t
-            hf = hh.float()
-            n = (hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + w.eps)).to(torch.bfloat16) \
-                * gamma.to(torch.bfloat16)
-            z = n @ W.t()
-            if w.act == si.ACT_SWIGLU:
-                F_ = w.n_out
-                return torch.nn.functional.silu(z[:, :F_]) * z[:, F_:]
-            if w.act == si.ACT_CE:
-                return torch.nn.functional.cross_entropy(z.float(), ce_in["targets"].long(), reduction="none")
-            if w.act == si.ACT_ROPE:
-                pos_t, cos_t, sin_t = rope_in
-                q = z[:, : w.rot_cols].view(M, -1, 64)
-                c, s_ = cos_t[pos_t].unsqueeze(1), sin_t[pos_t].unsqueeze(1)
-                x1, x2 = q[..., :32], q[..., 32:]
-                rq = torch.cat([x1 * c - x2 * s_, x2 * c + x1 * s_], -1).to(torch.bfloat16)
-                return torch.cat([rq.view(M, -1), z[:, w.rot_cols:]], 1)
-            return z
-
         for _ in range(3):
             unfused()
         torch.cuda.synchronize()

@@ -1,0 +1,101 @@
+"""Host logic of bench.py, no GPU: the per-step HBM byte bookkeeping from profiler
+counters, its source-hash gate, the one-GPU guard and the algorithmic byte counts."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _write_run(directory, counter, rows):
+    """A rocprofv3-style counter CSV: rows of (kernel name, dispatch id, value)."""
+    os.makedirs(directory, exist_ok=True)
+    with open(os.path.join(directory, "pmc_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for kernel, dispatch, value in rows:
+            w.writerow([dispatch, kernel, counter, value])
+
+
+def _ingest(tmp_path):
+    # the same setup dispatch in every run (cancels in the difference), then one dispatch
+    # per step with a fixed counter value: fused fetch 100 KiB / write 50 KiB per step,
+    # unfused (two kernels) 300 + 40 KiB / 200 KiB per step
+    setup = [("void fill_kernel(int)", 1, 7000.0)]
+    per_step = {"fused": {"FETCH_SIZE": [("void coda::k_a(int)", 100.0)],
+                          "WRITE_SIZE": [("void coda::k_a(int)", 50.0)]},
+                "unfused": {"FETCH_SIZE": [("Cijk_x(int)", 300.0), ("at::native::ew(int)", 40.0)],
+                            "WRITE_SIZE": [("Cijk_x(int)", 200.0)]}}
+    dirs = []
+    for path in ("fused", "unfused"):
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            for n in (2, 6):
+                rows = list(setup)
+                for step in range(n):
+                    for j, (kernel, value) in enumerate(per_step[path][counter]):
+                        rows.append((kernel, 10 + 4 * step + j, value))
+                d = str(tmp_path / f"{path}_{counter}_{n}")
+                _write_run(d, counter, rows)
+                dirs.append(d)
+    # plain copy of 1 MiB: FETCH_SIZE reads 512 KiB (factor 0.5), WRITE_SIZE 1024 KiB (1.0)
+    _write_run(str(tmp_path / "copy_f"), "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 1, 512.0)])
+    _write_run(str(tmp_path / "copy_w"), "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1, 1024.0)])
+    bench.ingest_step_traffic(["2", "6", *dirs, str(tmp_path / "copy_f"), str(tmp_path / "copy_w")],
+                              "wl_test", 1 << 20, "test command")
+
+
+def test_step_traffic_by_difference(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    _ingest(tmp_path)
+    rec = json.load(open(tmp_path / "profiles" / "step_traffic_wl_test.json"))
+    assert rec["steps_differenced"] == 4
+    assert rec["copy_factor_fetch"] == 0.5 and rec["copy_factor_write"] == 1.0
+    # fetch counters are divided by 0.5, write counters by 1.0; the setup kernel cancels
+    assert rec["fused"]["hbm_bytes_per_step"] == (200 + 50) * 1024
+    assert rec["unfused"]["hbm_bytes_per_step"] == (600 + 80 + 200) * 1024
+    assert rec["unfused"]["kernels"]["Cijk_x"] == [600 * 1024, 200 * 1024]
+    assert "fill_kernel" not in rec["fused"]["kernels"]
+    assert os.path.exists(tmp_path / "profiles" / "step_traffic_wl_test.txt")
+
+
+def test_step_traffic_source_gate(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    _ingest(tmp_path)
+    got = bench.load_step_traffic("wl_test")
+    assert got["fused"] == 250 * 1024 and got["unfused"] == 880 * 1024
+    assert got["unfused_over_fused"] == round(880 / 250, 3)
+    # a summary taken on other kernel sources is not reported
+    p = tmp_path / "profiles" / "step_traffic_wl_test.json"
+    rec = json.load(open(p))
+    rec["fused_source_hash"] = "0" * 16
+    json.dump(rec, open(p, "w"))
+    assert bench.load_step_traffic("wl_test") is None
+    assert bench.load_step_traffic("no_such_workload") is None
+
+
+def test_one_gpu_guard():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "ONE GPU" in r.stderr and not r.stdout.strip()
+
+
+def test_algorithmic_bytes_workload2():
+    import synth_inputs as si
+
+    w = si.WORKLOADS[2]
+    fused = bench.algorithmic_bytes(w)
+    M, K1, d, N2w, F = 16384, 2048, 2048, 16384, 8192
+    # GEMM 1 reads A, Wo and x_res and writes h and 8 partials per row; the reduction
+    # reads the partials and writes r; GEMM 2 reads h, W' and r and writes y
+    assert fused["gemm1"] == 2 * (M * K1 + d * K1 + 2 * M * d) + 4 * M * 8
+    assert fused["reduce"] == 4 * M * 8 + 4 * M
+    assert fused["gemm2"] == 2 * (M * d + N2w * d + M * F) + 4 * M
+    assert fused["total"] == 613548032
+    # unfused: h = x_res + A.Wo written as two kernels, the RMSNorm kernel, the gate/up
+    # product written and read back by the SwiGLU kernel
+    assert bench.algorithmic_bytes(w, False)["total"] == 1954553856
