@@ -110,13 +110,13 @@ def algorithmic_bytes(w, fused=True) -> dict:
 
 
 def load_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the
-    current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    """HBM bytes per launch of a kernel from the committed counter summary of the workload,
+    if it was taken on the kernel's current sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    if rec.get("source_hash") != kernel_source_hash(kernel):
+    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    if rec is None or rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -220,12 +220,46 @@ def load_step_traffic(workload: str):
     return {"fused": f, "unfused": u, "unfused_over_fused": round(u / f, 3), "torch": rec.get("torch")}
 
 
+def _dispatches(directory: str, counter: str) -> dict:
+    """Per kernel name: its dispatches in launch order, each [counter value summed over
+    its rows, duration in ns] (rocprofv3 CSV)."""
+    acc = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        d = acc.setdefault(r["Kernel_Name"], {})
+        rec = d.setdefault(int(r["Dispatch_Id"]), [0.0, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
+        rec[0] += float(r["Counter_Value"])
+    return {k: [v[i] for i in sorted(v)] for k, v in acc.items()}
+
+
+def _launch_groups(durations: list) -> list:
+    """Indices of one kernel's dispatches split into groups of similar duration (the
+    same kernel launched on different problems within a step), longest first."""
+    order = sorted(range(len(durations)), key=lambda i: durations[i])
+    groups, cur = [], [order[0]]
+    for i in order[1:]:
+        if durations[i] > 1.5 * durations[cur[-1]]:
+            groups.append(cur)
+            cur = []
+        cur.append(i)
+    groups.append(cur)
+    return groups[::-1]
+
+
 def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, then of the
-    plain copy) into profiles/traffic_<kernel>_<workload>.json: HBM-side bytes per launch,
-    each counter divided by what it reads per byte of the plain copy."""
-    f_run, w_run, f_cal, w_cal = (_counter_means(d, c) for d, c in
-                                  zip(dirs, ("FETCH_SIZE", "WRITE_SIZE", "FETCH_SIZE", "WRITE_SIZE")))
+    plain copy) into profiles/traffic_<workload>.json: HBM-side bytes per launch of each kernel,
+    each counter divided by what it reads per byte of the plain copy.  Every library
+    kernel of the run is covered.  Where one kernel name ran in several template
+    instantiations (a forward run in a backward bench's setup), the instantiation with
+    the most dispatches -- the timed one -- is taken; where one instantiation ran on
+    problems of different size within a step (the input-gradient kernel for both GEMMs of
+    the whole-chain backward), its dispatches are grouped by duration, matched across the
+    two runs by launch order, and the longest group -- the dominant launch -- is stored
+    (every group is listed in the text summary)."""
+    f_run, w_run = _dispatches(dirs[0], "FETCH_SIZE"), _dispatches(dirs[1], "WRITE_SIZE")
+    f_cal, w_cal = _counter_means(dirs[2], "FETCH_SIZE"), _counter_means(dirs[3], "WRITE_SIZE")
     pick = lambda d: next(v for k, v in d.items() if "copy" in k.lower())  # noqa: E731
     kib = copy_bytes / 1024.0
     ff, fw = pick(f_cal) / kib, pick(w_cal) / kib
@@ -234,19 +268,31 @@ def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
              f"# commands: {command}",
              f"# copy calibration: {copy_bytes} bytes copied; FETCH_SIZE reads {ff:.4f} KiB per KiB, "
              f"WRITE_SIZE {fw:.4f} KiB per KiB",
-             "kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, traffic bytes (scaled)"]
-    for kname in ("k_gemm_resid_partialrms", "k_rowscale_reduce", "k_gemm_rowscale_swiglu"):
-        fk = [v for k, v in f_run.items() if kname in k and "swiglu_w8" not in k]
-        wk = [v for k, v in w_run.items() if kname in k and "swiglu_w8" not in k]
-        if not fk or not wk:
+             "kernel, launch group, dispatches, mean duration us (under the profiler), FETCH_SIZE KiB, "
+             "WRITE_SIZE KiB, traffic bytes (scaled)"]
+    out = {"workload": workload, "command": command, "copy_factor_fetch": ff, "copy_factor_write": fw,
+           "kernels": {}}
+    best = {}
+    for full, disp in f_run.items():
+        if "coda::" not in full or len(w_run.get(full, [])) != len(disp):
             continue
-        traffic = fk[0] * 1024 / ff + wk[0] * 1024 / fw
-        rec = {"kernel": kname, "workload": workload, "source_hash": kernel_source_hash(kname),
-               "fetch_kib": fk[0], "write_kib": wk[0], "copy_factor_fetch": ff,
-               "copy_factor_write": fw, "hbm_bytes_per_launch": round(traffic), "command": command}
-        with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{workload}.json"), "w") as fh:
-            json.dump(rec, fh, indent=1)
-        lines.append(f"{kname}, {fk[0]:.1f}, {wk[0]:.1f}, {traffic:.0f}")
+        base = _short_kernel_name(full).split("::")[-1]
+        if base not in best or len(disp) > len(f_run[best[base]]):
+            best[base] = full
+    for base, full in sorted(best.items()):
+        fd, wd = f_run[full], w_run[full]
+        for g, idx in enumerate(_launch_groups([x[1] for x in fd])):
+            fk = sum(fd[i][0] for i in idx) / len(idx)
+            wk = sum(wd[i][0] for i in idx) / len(idx)
+            us = sum(fd[i][1] for i in idx) / len(idx) / 1e3
+            traffic = fk * 1024 / ff + wk * 1024 / fw
+            if g == 0:
+                out["kernels"][base] = {"instantiation": full.split("(")[0], "source_hash": kernel_source_hash(base),
+                                        "dispatches": len(idx), "mean_duration_us_profiled": round(us, 1),
+                                        "fetch_kib": fk, "write_kib": wk, "hbm_bytes_per_launch": round(traffic)}
+            lines.append(f"{base}, {g}, {len(idx)}, {us:.1f}, {fk:.1f}, {wk:.1f}, {traffic:.0f}")
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
     with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -391,7 +437,7 @@ def bench_backward(w, args) -> dict:
         "prep_ms": round(prep_ms, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": load_traffic(w.name, kern[dom]), "kernel": kern[dom],
+                     "traffic": load_traffic(w.name + ("_saved_z" if saved else ""), kern[dom]), "kernel": kern[dom],
                      "kernel_ms": round(k_ms[dom], 4), "algorithmic_bytes": byt[names[dom]],
                      "kernel_source_hash": kernel_source_hash(kern[dom])},
         "kernel_source_hash": kernel_source_hash(),
@@ -559,7 +605,7 @@ def main():
     if args.ingest_traffic:
         import synth_inputs as si
 
-        ingest_traffic(args.ingest_traffic, si.WORKLOADS[args.workload].name,
+        ingest_traffic(args.ingest_traffic, si.WORKLOADS[args.workload].name + ("_saved_z" if args.saved_z else ""),
                        (args.copy_calibration or 1024) << 20, args.ingest_command)
         return
     if args.gpus != 1:

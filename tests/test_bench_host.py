@@ -99,3 +99,12 @@ def test_algorithmic_bytes_workload2():
     # unfused: h = x_res + A.Wo written as two kernels, the RMSNorm kernel, the gate/up
     # product written and read back by the SwiGLU kernel
     assert bench.algorithmic_bytes(w, False)["total"] == 1954553856
+
+
+def test_launch_groups():
+    # one kernel launched on two problem sizes per step, interleaved: grouped by
+    # duration, longest group first (within a group the indices come in duration order)
+    durs = [880.0, 128.0, 905.0, 121.0, 870.0, 131.0]
+    assert bench._launch_groups(durs) == [[4, 0, 2], [3, 1, 5]]
+    assert bench._launch_groups([50.0]) == [[0]]
+    assert bench._launch_groups([10.0, 11.0, 12.0]) == [[0, 1, 2]]
