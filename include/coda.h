@@ -78,7 +78,10 @@ typedef enum { CODA_ACT_NONE = 0, CODA_ACT_SWIGLU = 1 } coda_act;
 coda_status coda_prepare_weight_bf16(int64_t N, int64_t K, const void* W, const float* gamma,
                                      void* Wp, void* stream);
 
-/* Per-tensor e4m3 quantisation with an fp32 scale (the 8-bit variant of the chain):
+/* Per-tensor e4m3 quantisation with an fp32 scale (the 8-bit variant of the chain;
+ * kucoin page, section "El impuesto a la pereza para entrenar modelos grandes": 8-bit
+ * formats speed up the products and raise the share of the memory-bound work around
+ * them):
  *   x[n,k]  = fl32(gamma[k] * X[n,k])        (gamma == NULL: x = X)
  *   amax    = max |x|;   scale = fl32(amax / 448)   (amax == 0: scale = 1)
  *   Q[n,k]  = e4m3_saturate_rne( fl32(x[n,k] / scale) )
@@ -118,15 +121,19 @@ coda_status coda_gemm_resid_partialrms(int64_t M, int64_t N, int64_t K,
                                        const void* x_res, void* h, float* partials,
                                        void* stream);
 
-/* The light reduction that turns the partials into the row scale:
+/* The light reduction that turns the partials into the row scale (kucoin page, section
+ * "CODA: El epilogo esconde un tesoro": the partial sums are combined by a very light
+ * reduction kernel between the two GEMMs):
  *   r[m] = fl32( 1 / sqrt( (sum_t P[m,t]) / N + eps ) )   (sum and sqrt in fp64)
  *   partials [M, coda_partials_per_row(N)] fp32, device;  r [M] fp32, device, written.
  * eps must be finite and >= 0.  A row whose sum and eps are both 0 yields +inf.       */
 coda_status coda_rowscale_reduce(int64_t M, int64_t N, const float* partials, float eps,
                                  float* r, void* stream);
 
-/* Second GEMM with row-scale (+SwiGLU) epilogue.  z = sw * (h . W^T), with gamma
- * already folded into W:
+/* Second GEMM with row-scale (+SwiGLU) epilogue (kucoin page, section "CODA: El epilogo
+ * esconde un tesoro": r commutes with the next product and is applied at its end; the
+ * same reparameterisation covers SwiGLU).  z = sw * (h . W^T), with gamma already
+ * folded into W:
  *   CODA_ACT_NONE:   W [N_out, K];   y[m,n] = bf16_rne( r[m] * z[m,n] )
  *   CODA_ACT_SWIGLU: W [2*N_out, K], rows [0, N_out) = gate, [N_out, 2*N_out) = up;
  *                    g = r[m]*z[m,j], u = r[m]*z[m,N_out+j],
@@ -159,7 +166,8 @@ coda_status coda_gemm_rowscale_swiglu(int64_t M, int64_t N_out, int64_t K, coda_
  * rows in [1, 2^24); base finite and > 1 (CODA_ERR_VALUE otherwise).                   */
 coda_status coda_rope_table(int64_t rows, double base, float* cos, float* sin, void* stream);
 
-/* Second GEMM with row-scale + RoPE epilogue (no activation).  z = sw * (h . W^T):
+/* Second GEMM with row-scale + RoPE epilogue (no activation; the RoPE passages cited
+ * above).  z = sw * (h . W^T):
  *   x[m,n] = r[m] * z[m,n];
  *   for a column n < rot_cols in head c = n / 64 at offset i = n % 64 < 32, with
  *   p = pos[m], C = cos[p*32 + i], S = sin[p*32 + i]:
@@ -196,7 +204,8 @@ coda_status coda_gemm_rowscale_rope(int64_t M, int64_t N_out, int64_t K, const v
  * sizes `partials` as M * coda_ce_partials_per_row(V) * 2 floats.  -1 if V < 1.       */
 int64_t coda_ce_partials_per_row(int64_t V);
 
-/* LM-head GEMM with row scale + block log-sum-exp epilogue.  z = r[m] * sw * (h . W^T):
+/* LM-head GEMM with row scale + block log-sum-exp epilogue (the cross-entropy passages
+ * cited above: block log-sum-exp, max / sum-exp state).  z = r[m] * sw * (h . W^T):
  *   partials[m, t, 0] = max over the columns v of tile t (v in [256t, 256t+256) and
  *                       v < V) of z[m, v]                                   (fp32)
  *   partials[m, t, 1] = sum over the same columns of exp(z[m, v] - that max)  (fp32)
@@ -214,7 +223,8 @@ coda_status coda_gemm_rowscale_ce(int64_t M, int64_t V, int64_t K, const void* h
                                   const int32_t* targets, float* partials, float* tgt_logit,
                                   void* stream);
 
-/* The reduction of the partials:
+/* The reduction of the partials (the light reduction after the loss epilogue, as
+ * cited above):
  *   lse[m]  = fl32( Mx + log( sum_t partials[m,t,1] * exp(partials[m,t,0] - Mx) ) ),
  *             Mx = max_t partials[m,t,0]                           (fp64 inside)
  *   loss[m] = fl32( lse - tgt_logit[m] )  if 0 <= targets[m] < V, else 0 (an ignored
@@ -238,20 +248,24 @@ coda_status coda_ce_reduce(int64_t M, int64_t V, const float* partials, const in
  * once per weight update).  bf16 weights only.
  */
 
-/* The row scale of a stored h, for a backward that recomputes it instead of saving it:
+/* The row scale of a stored h, for a backward that recomputes it instead of saving it
+ * (the RMSNorm row scale of the kucoin page, section "CODA: El epilogo esconde un
+ * tesoro", from h directly):
  *   r[m] = fl32( 1 / sqrt( sum_n h[m,n]^2 / N + eps ) )     (fp64 inside)
  *   h [M, N] bf16, device;  r [M] fp32, device, written, must not overlap h.
  * Granule: N % 8 == 0.  eps finite and >= 0.                                         */
 coda_status coda_rowscale_from_h(int64_t M, int64_t N, const void* h, float eps, float* r,
                                  void* stream);
 
-/* dst[c, r] = src[r, c] for bf16 [R, C] matrices; R, C in [1, 2^31); no overlap.      */
+/* dst[c, r] = src[r, c] for bf16 [R, C] matrices; R, C in [1, 2^31); no overlap.  A
+ * layout utility (W'^T for the input-gradient GEMM), no operation of the pages.       */
 coda_status coda_transpose_bf16(int64_t R, int64_t C, const void* src, void* dst, void* stream);
 
 /* Partials per row written by coda_gemm_swiglu_bwd for F gate columns; -1 if F < 1.    */
 int64_t coda_swiglu_bwd_partials_per_row(int64_t F);
 
-/* Recomputed gate/up product with the SwiGLU-backward epilogue:
+/* Recomputed gate/up product with the SwiGLU-backward epilogue (the backward passage
+ * cited above; the SwiGLU derivative is the epilogue's element-wise transform):
  *   h   [M, K] bf16 (the block input the forward read);  W [2F, K] bf16 (W', gate rows
  *       then up rows);  r [M] fp32 (the forward's row scale);  dy [M, F] bf16
  *   dz  [M, 2F] bf16, written: bf16_rne( r[m] * dL/dz[m, j] )  (gate columns, then up)
@@ -262,12 +276,15 @@ coda_status coda_gemm_swiglu_bwd(int64_t M, int64_t F, int64_t K, const void* h,
                                  const float* r, const void* dy, void* dz, float* partials,
                                  void* stream);
 
-/* q[m] = fl32( -(r[m]^3 / N) * sum_t partials[m, t] )   (fp64 inside; N = hidden size,
+/* The light reduction of the backward (cited above): the RMSNorm backward's row
+ * coefficient
+ * q[m] = fl32( -(r[m]^3 / N) * sum_t partials[m, t] )   (fp64 inside; N = hidden size,
  * F = the gate width the partials were written for).  q must not overlap the inputs.  */
 coda_status coda_rmsnorm_bwd_reduce(int64_t M, int64_t N, int64_t F, const float* partials,
                                     const float* r, float* q, void* stream);
 
-/* Input-gradient GEMM with the RMSNorm-backward epilogue:
+/* Input-gradient GEMM with the RMSNorm-backward epilogue (the backward passage cited
+ * above: the row-scale term q * h is applied at the end of the product):
  *   dh[m,n] = bf16_rne( sum_k dz[m,k] Wt[n,k] + q[m] h[m,n] + dh_res[m,n] )
  *   dz [M, K] bf16 (K = 2F);  Wt [N, K] bf16 = W'^T;  h [M, N] bf16;  q [M] fp32
  *   dh_res [M, N] bf16 or NULL (= 0); may be EXACTLY equal to dh (in place)
@@ -291,7 +308,9 @@ coda_status coda_gemm_rowscale_gfold(int64_t M, int64_t N_out, int64_t K, coda_a
 
 /* ------------------------------ backward from a saved pre-activation ---- */
 /* A forward that keeps the pre-activation lets the backward skip the recomputed gate/up
- * product (memory for time: z is M x 2F bf16).  Same block and same gradients as above.  */
+ * product (memory for time: z is M x 2F bf16).  Same block and same gradients as above
+ * (kucoin page, section "Cinco bloques y un lenguaje LEGO": the matrix-block store
+ * primitive keeps intermediate activations for the backward pass).                     */
 
 /* The SwiGLU second GEMM of coda_gemm_rowscale_swiglu (bf16 weights) that also writes
  *   z [M, 2F] bf16 = bf16_rne( r[m] * sum_k h[m,k] W[j,k] )   (gate columns, then up)
@@ -311,7 +330,9 @@ coda_status coda_gemm_rowscale_swiglu_save(int64_t M, int64_t F, int64_t K, cons
 coda_status coda_swiglu_bwd_saved(int64_t M, int64_t F, const void* z, const void* dy, const float* r, void* dz,
                                   void* dzt, float* partials, void* stream);
 
-/* Plain product with an optional residual, bf16 out (the first GEMM's input gradient
+/* Plain product with an optional residual, bf16 out (the first GEMM's input gradient,
+ * the backward of the chain: kucoin page, section "CODA: El epilogo esconde un tesoro",
+ * last paragraph;
  * dA = dh . Wo, with Bt = Wo^T passed K-contiguous; the same kernel as
  * coda_gemm_rmsnorm_bwd without the row-scale term):
  *   C[m,n] = bf16_rne( sum_k A[m,k] Bt[n,k] + c_res[m,n] )    (fp32 MFMA sums)
@@ -340,7 +361,8 @@ int64_t coda_wgrad_partials_rows(int64_t NR);
  * split helps; -1 for invalid sizes.                                                   */
 int64_t coda_wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K);
 
-/* Weight-gradient GEMM, contraction over K tokens:
+/* Weight-gradient GEMM, contraction over K tokens (the weight-gradient passages cited
+ * above):
  *   At [NR, K] bf16 (e.g. (r * dL/dz)^T, NR = 2F);  Bt [NC, K] bf16 (e.g. h^T, NC = d)
  *   gamma [NC] fp32 or NULL (= 1);  W [NR, NC] bf16 raw weight or NULL (no partials)
  *   dW [NR, NC] fp32, written: fl32( gamma[k] * sum_m At[j,m] Bt[k,m] )  (fp32 MFMA sums)
@@ -358,8 +380,8 @@ coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, c
                             const float* gamma, const void* W, float* dW, float* partials,
                             void* workspace, int64_t workspace_bytes, void* stream);
 
-/* The same weight-gradient GEMM on token-major operands, as the activations are stored
- * (no transposes): the contraction runs down the rows of
+/* The same weight-gradient GEMM (cited above) on token-major operands, as the
+ * activations are stored (no transposes): the contraction runs down the rows of
  *   X [K, lda] bf16, its first NR columns (e.g. r * dL/dz [M, 2F]: lda = NR = 2F)
  *   Y [K, ldb] bf16, its first NC columns (e.g. h [M, d]: ldb = NC = d)
  *   dW[j,k] = fl32( gamma[k] * sum_m X[m,j] Y[m,k] ); gamma, W, partials, workspace and the
@@ -372,7 +394,8 @@ coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X
                                 int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
                                 void* workspace, int64_t workspace_bytes, void* stream);
 
-/* out[k] = fl32( sum_t partials[t, k] )  (fixed order, fp64 inside), T >= 1 rows of NC
+/* The block reduction's final sum (cited above):
+ * out[k] = fl32( sum_t partials[t, k] )  (fixed order, fp64 inside), T >= 1 rows of NC
  * columns: the gamma gradient from coda_gemm_wgrad's partials.  out must not overlap.  */
 coda_status coda_colsum_reduce(int64_t T, int64_t NC, const float* partials, float* out,
                                void* stream);
