@@ -24,7 +24,8 @@ ACT_NONE = 0
 ACT_SWIGLU = 1
 
 __all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
-           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "cross_entropy", "mlpin_bwd", "mlpin_wgrad", "chain_bwd", "chain", "prepare", "BF16", "E4M3",
+           "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "rope_transpose", "cross_entropy", "mlpin_bwd",
+           "mlpin_wgrad", "chain_bwd", "qkv_rope_bwd", "chain", "prepare", "BF16", "E4M3",
            "ACT_NONE", "ACT_SWIGLU"]
 
 
@@ -212,6 +213,82 @@ def rope(y: np.ndarray, pos, base: float, head_dim: int, rot_cols: int) -> np.nd
     rc = lib().orc_rope(out.shape[0], out.shape[1], _p(out), _p(p), float(base), int(head_dim), int(rot_cols))
     if rc != 0:
         raise ValueError("bad RoPE layout")
+    return out
+
+
+def rope_transpose(dy: np.ndarray, pos, base: float, head_dim: int, rot_cols: int) -> np.ndarray:
+    """The transpose of the RoPE rotation applied to ``dy`` (fp64 [R, ncols]): the
+    gradient with respect to RoPE's input given the gradient ``dy`` of its output.  Per
+    rotated head, for i < head_dim/2 with angle a = pos * base^(-2i/head_dim):
+      forward   y_i = x_i cos a - x_{i+h} sin a,   y_{i+h} = x_{i+h} cos a + x_i sin a
+      transpose dx_i = dy_i cos a + dy_{i+h} sin a,   dx_{i+h} = dy_{i+h} cos a - dy_i sin a
+    (h = head_dim/2); columns [rot_cols, ncols) pass through.  Plain fp64 numpy."""
+    g = np.array(dy, dtype=np.float64, copy=True)
+    p = np.asarray(pos, dtype=np.float64)
+    if g.ndim != 2 or p.shape != (g.shape[0],) or rot_cols % head_dim or rot_cols > g.shape[1]:
+        raise ValueError("bad RoPE layout")
+    half = head_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    a = p[:, None] * base ** (-2.0 * i / head_dim)[None, :]            # [R, half]
+    c, s = np.cos(a), np.sin(a)
+    for h0 in range(0, rot_cols, head_dim):
+        lo, hi = dy[:, h0:h0 + half].astype(np.float64), dy[:, h0 + half:h0 + head_dim].astype(np.float64)
+        g[:, h0:h0 + half] = lo * c + hi * s
+        g[:, h0 + half:h0 + head_dim] = hi * c - lo * s
+    return g
+
+
+def qkv_rope_bwd(hb, gamma, Wp, wp_scale: float, W_raw, dy, pos, base: float, head_dim: int,
+                 rot_cols: int, eps: float, rows=None, js=None, ks=None, rss=False):
+    """Backward of the QKV block  y = RoPE( RMSNorm(hb) . W_or^T )  (kucoin page, section
+    "CODA: El epilogo esconde un tesoro", last paragraph: the reparameterisation covers
+    RoPE and holds for the backward pass).  The chain rule in reverse order, plain fp64:
+      forward   r = 1/sqrt(mean(hb^2) + eps),  n = hb r gamma,  z = n . W_or^T,
+                y = RoPE(z)                      (W_or = Wp * wp_scale / gamma, the weight
+                                                  the prepared Wp stands for)
+      RoPE      dz = RoPE^T(dy)                  (:func:`rope_transpose`)
+      GEMM      dn = dz . W_or;   dW[j, k] = sum_m dz[m, j] n[m, k]   (the raw weight's)
+      RMSNorm   dhb[k] = r gamma[k] dn[k] - (r^3 / d) hb[k] sum_k' gamma[k'] dn[k'] hb[k']
+                dgamma[k] = sum_m sum_j dz[m, j] W_raw[j, k] hb[m, k] r[m]
+    hb uint16 [M, d] and dy uint16 [M, N] bf16 codes, gamma fp32 [d], Wp uint16 [N, d]
+    (bf16 codes of the gamma-folded weight), W_raw uint16 [N, d], pos int [M].
+
+    Returns dict(dh [R, d], r [R], dz [R, N]) for the listed rows (default all), dW
+    [nj, nk] summed over all M tokens at rows js of W (default all N) and columns ks
+    (default all d), dgamma [nk] when js covers every row (else None), and with rss=True
+    the root-sum-squares over the tokens of the summed terms, rss [nj, nk] (gamma left
+    out) and rss_gamma [nk] (full js only)."""
+    hbv = bf16_decode(np.asarray(hb, dtype=np.uint16))
+    dyv = bf16_decode(np.asarray(dy, dtype=np.uint16))
+    g = np.asarray(gamma, dtype=np.float64)
+    wor = bf16_decode(np.asarray(Wp, dtype=np.uint16)) * float(wp_scale) / g[None, :]
+    wraw = bf16_decode(np.asarray(W_raw, dtype=np.uint16))
+    M, d = hbv.shape
+    N = wor.shape[0]
+    if wor.shape != (N, d) or wraw.shape != (N, d) or dyv.shape != (M, N) or g.shape != (d,):
+        raise ValueError("shape mismatch")
+    r = 1.0 / np.sqrt((hbv * hbv).sum(axis=1) / d + eps)               # [M]
+    dz_all = rope_transpose(dyv, pos, base, head_dim, rot_cols)      # [M, N]
+    rr = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    dz = dz_all[rr]
+    dn = dz @ wor                                                    # [R, d]
+    hr, rv = hbv[rr], r[rr]
+    c = (g[None, :] * dn * hr).sum(axis=1)
+    dh = rv[:, None] * g[None, :] * dn - (rv ** 3 / d)[:, None] * hr * c[:, None]
+    j = np.arange(N) if js is None else np.asarray(js, dtype=np.int64)
+    k = np.arange(d) if ks is None else np.asarray(ks, dtype=np.int64)
+    t = dz_all[:, j]                                                 # [M, nj]
+    hk = hbv[:, k] * r[:, None]                                      # [M, nk]: hb r
+    dW = (t.T @ hk) * g[k][None, :]
+    dgam = None
+    if js is None:
+        dgam = ((dz_all @ wraw[:, k]) * hk).sum(axis=0)
+    out = dict(dh=dh, r=rv, dz=dz, dW=dW, dgamma=dgam)
+    if rss:
+        out["rss"] = np.sqrt((t * t).T @ (hk * hk))
+        out["rss_gamma"] = None
+        if js is None:
+            out["rss_gamma"] = np.sqrt((((dz_all * dz_all) @ (wraw[:, k] * wraw[:, k])) * hk * hk).sum(axis=0))
     return out
 
 
