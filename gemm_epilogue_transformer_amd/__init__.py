@@ -26,7 +26,8 @@ __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3"
            "gemm_rowscale_ce", "ce_reduce", "rowscale_from_h", "transpose_bf16", "gemm_swiglu_bwd", "rmsnorm_bwd_reduce",
            "gemm_rmsnorm_bwd", "mlpin_bwd", "wgrad_partials_rows", "gemm_wgrad", "colsum_reduce",
            "mlpin_wgrad", "gemm_bf16", "chain_bwd", "wgrad_workspace_bytes", "gemm_rowscale_swiglu_save",
-           "swiglu_bwd_saved", "gemm_rowscale_gfold", "gemm_wgrad_tok", "chain", "version"]
+           "swiglu_bwd_saved", "gemm_rowscale_gfold", "gemm_wgrad_tok", "rope_bwd", "qkv_rope_bwd", "chain",
+           "version"]
 
 
 def _stream(stream):
@@ -291,6 +292,36 @@ def swiglu_bwd_saved(z, dy, r, dz=None, dzt=None, partials=None, transpose=True,
         M, F, _ptr(z), _ptr(dy), _ptr(r), _ptr(dz), _ptr(dzt if transpose else None), _ptr(partials),
         _stream(stream)))
     return dz, (dzt if transpose else None), partials
+
+
+def rope_bwd(dy, y, r, pos, cos, sin, rot_cols, dz=None, partials=None, stream=None):
+    """Backward of the RoPE epilogue from the forward's output y [M, N]: returns (dz
+    [M, N] = r * RoPE^T(dy) in bf16, partials [M, T] = per 128-column tile
+    (1/r) * sum of dy * y, the layout rmsnorm_bwd_reduce takes with F = N)."""
+    M, N = dy.shape
+    if pos is not None and pos.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    T = int(_lib.load().coda_swiglu_bwd_partials_per_row(N))
+    rows = 0 if cos is None else cos.shape[0]
+    dz = torch.empty((M, N), dtype=torch.bfloat16, device=dy.device) if dz is None else dz
+    partials = torch.empty((M, T), dtype=torch.float32, device=dy.device) if partials is None else partials
+    _lib.check("coda_rope_bwd", _lib.load().coda_rope_bwd(
+        M, N, _ptr(dy), _ptr(y), _ptr(r), _ptr(pos), _ptr(cos), _ptr(sin), rows, rot_cols, _ptr(dz),
+        _ptr(partials), _stream(stream)))
+    return dz, partials
+
+
+def qkv_rope_bwd(h, r, Wpt, W, gamma, dy, y, pos, cos, sin, rot_cols, dh_res=None, out=None, stream=None):
+    """Backward of the QKV block y = RoPE(RMSNorm(h) . W^T) from the forward's h, r and y:
+    the RoPE backward, the row coefficient, the input-gradient GEMM (Wpt = W'^T [d, N])
+    and the weight / gamma gradients on dz and h as stored.  Returns dict(dh, dW [N, d]
+    fp32, dgamma [d] fp32, dz, q)."""
+    out = out or {}
+    dz, P = rope_bwd(dy, y, r, pos, cos, sin, rot_cols, out.get("dz"), out.get("partials"), stream)
+    q = rmsnorm_bwd_reduce(P, r, h.shape[1], dy.shape[1], out.get("q"), stream)
+    dh = gemm_rmsnorm_bwd(dz, Wpt, h, q, dh_res, out.get("dh"), stream)
+    dW, dgam = mlpin_wgrad(dz, h, gamma, W, out=out, stream=stream)
+    return dict(dh=dh, dW=dW, dgamma=dgam, dz=dz, q=q)
 
 
 def gemm_bf16(A, Bt, c_res=None, C=None, stream=None):

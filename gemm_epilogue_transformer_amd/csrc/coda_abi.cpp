@@ -396,6 +396,33 @@ coda_status coda_swiglu_bwd_saved(int64_t M, int64_t F, const void* z, const voi
                                                     as_stream(stream)));
 }
 
+coda_status coda_rope_bwd(int64_t M, int64_t N, const void* dy, const void* y, const float* r, const int32_t* pos,
+                          const float* cos, const float* sin, int64_t table_rows, int64_t rot_cols, void* dz,
+                          float* partials, void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(N, 1) || N % 8 != 0 || N > kMaxRow) return CODA_ERR_SHAPE;
+    if (rot_cols < 0 || rot_cols > N || rot_cols % 64 != 0) return CODA_ERR_SHAPE;
+    const bool rot = rot_cols > 0;
+    if (rot && (table_rows < 1 || table_rows >= (int64_t(1) << 24))) return CODA_ERR_SHAPE;
+    const int64_t T = coda::swiglu_bwd_partials_per_row(N);
+    if (!prod_ok(M, N) || !prod_ok(M, T) || ((M + 63) / 64) * T > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!dy || !y || !r || !dz || !partials) return CODA_ERR_NULL;
+    if (rot && (!pos || !cos || !sin)) return CODA_ERR_NULL;
+    if (!aligned16(dy) || !aligned16(y) || !aligned16(dz)) return CODA_ERR_ALIGN;
+    if (rot && (!aligned16(cos) || !aligned16(sin))) return CODA_ERR_ALIGN;
+    const Range rd = span(dz, M * N * 2), rp = span(partials, M * T * 4);
+    if (overlap(rd, rp)) return CODA_ERR_ALIAS;
+    const Range ins[] = {span(dy, M * N * 2), span(y, M * N * 2), span(r, M * 4),
+                         span(rot ? pos : nullptr, rot ? M * 4 : 0),
+                         span(rot ? cos : nullptr, rot ? table_rows * 128 : 0),
+                         span(rot ? sin : nullptr, rot ? table_rows * 128 : 0)};
+    for (const Range& in : ins)
+        if (overlap(rd, in) || overlap(rp, in)) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_rope_bwd(int(M), int(N), dy, y, r, rot ? pos : nullptr, rot ? cos : nullptr,
+                                            rot ? sin : nullptr, int(rot ? table_rows : 0), int(rot_cols), dz,
+                                            partials, as_stream(stream)));
+}
+
 coda_status coda_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* Bt, const void* c_res,
                            void* C, void* stream) {
     if (!dim_ok(M, 0) || !dim_ok(N, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;

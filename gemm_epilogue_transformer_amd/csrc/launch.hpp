@@ -65,6 +65,9 @@ hipError_t launch_gemm_rowscale_gfold(int M, int N_out, int K, bool swiglu, cons
 // SwiGLU forward that keeps the pre-activation, and the backward that starts from it.
 hipError_t launch_gemm_rowscale_swiglu_save(int M, int F, int K, const void* h, const void* W, const float* r,
                                             void* y, void* z, hipStream_t stream);
+hipError_t launch_rope_bwd(int M, int N, const void* dy, const void* y, const float* r, const int32_t* pos,
+                           const float* cos, const float* sin, int table_rows, int rot_cols, void* dz,
+                           float* partials, hipStream_t stream);
 hipError_t launch_swiglu_bwd_saved(int M, int F, const void* z, const void* dy, const float* r, void* dz,
                                    void* dzt, float* partials, hipStream_t stream);
 

@@ -330,6 +330,30 @@ coda_status coda_gemm_rowscale_swiglu_save(int64_t M, int64_t F, int64_t K, cons
 coda_status coda_swiglu_bwd_saved(int64_t M, int64_t F, const void* z, const void* dy, const float* r, void* dz,
                                   void* dzt, float* partials, void* stream);
 
+/* ------------------------------------------ backward of the RoPE epilogue ----
+ * Input side of the backward of the QKV block  y = RoPE( RMSNorm(h) . W^T )  (kucoin
+ * page, section "CODA: El epilogo esconde un tesoro", last paragraph: the
+ * reparameterisation covers RoPE and holds for the backward pass).  The rotation's
+ * gradient is its transpose and needs no recomputed product; the rest of the block's
+ * backward is coda_rmsnorm_bwd_reduce (with F = N), coda_gemm_rmsnorm_bwd (K = N) and
+ * coda_gemm_wgrad_tok + coda_colsum_reduce on dz and h, unchanged.
+ *   dL/dz = RoPE^T(dy): in a rotated head, for i < 32 with C, S the table's cos / sin at
+ *     (pos[m], i):  dL/dz[64c+i] = dy[64c+i] C + dy[64c+i+32] S,
+ *                   dL/dz[64c+i+32] = dy[64c+i+32] C - dy[64c+i] S;  dL/dz = dy past rot_cols
+ *   dz [M, N] bf16, written: bf16_rne( r[m] * dL/dz[m, j] )
+ *   partials [M, coda_swiglu_bwd_partials_per_row(N)] fp32, written: per tile of 128
+ *       columns, (1/r[m]) * sum of dy * y  (= sum of dL/dz * acc, acc = z / r: the
+ *       rotation is orthogonal and a tile holds whole heads)
+ *   dy [M, N] bf16 (upstream gradient);  y [M, N] bf16 (the forward's output, as
+ *       coda_gemm_rowscale_rope wrote it);  r [M] fp32 (the forward's row scale)
+ *   pos, cos, sin, table_rows, rot_cols as for coda_gemm_rowscale_rope (a position
+ *       outside the table reads zero angles there, so its rotated columns' gradient is
+ *       0, the derivative of that forward); cos and sin 16-byte aligned
+ * Granule: N % 8 == 0.  Outputs must not overlap each other or the inputs.             */
+coda_status coda_rope_bwd(int64_t M, int64_t N, const void* dy, const void* y, const float* r, const int32_t* pos,
+                          const float* cos, const float* sin, int64_t table_rows, int64_t rot_cols, void* dz,
+                          float* partials, void* stream);
+
 /* Plain product with an optional residual, bf16 out (the first GEMM's input gradient,
  * the backward of the chain: kucoin page, section "CODA: El epilogo esconde un tesoro",
  * last paragraph;

@@ -36,6 +36,7 @@ ACT_ROPE = 2      # rotary position embedding on the QKV product (no activation)
 ACT_CE = 3        # cross-entropy of the LM-head product against per-row targets
 ACT_SWIGLU_BWD = 4  # backward of the RMSNorm -> GEMM -> SwiGLU block (no first GEMM)
 ACT_CHAIN_BWD = 5   # backward of the whole chain (first GEMM + residual included)
+ACT_ROPE_BWD = 6    # backward of the RMSNorm -> QKV GEMM -> RoPE block (no first GEMM)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -70,6 +71,10 @@ class Workload:
         if self.act == ACT_CHAIN_BWD:
             # plus the first GEMM's input-gradient and weight-gradient products
             return 3 * (2 * self.M * self.d * self.N2w) + 2 * (2 * self.M * self.K1 * self.d)
+        if self.act == ACT_ROPE_BWD:
+            # the input-gradient and weight-gradient products (the rotation needs no
+            # recomputed forward product)
+            return 2 * (2 * self.M * self.d * self.N2w)
         return 2 * self.M * self.K1 * self.d + 2 * self.M * self.d * self.N2w
 
 
@@ -85,7 +90,8 @@ class Workload:
 # of the RMSNorm -> gate/up GEMM -> SwiGLU block -- with the block input h and the
 # upstream gradient dy drawn directly (no first GEMM); 9: the backward of workload 2's
 # whole chain (same forward draws as workload 2, then dy and the residual-stream
-# gradient dres).
+# gradient dres); 10: the backward of workload 6's second half -- the RMSNorm -> QKV
+# GEMM -> RoPE block -- with h, W and dy drawn directly, positions as in workload 6.
 WORKLOADS = {
     1: Workload("tiny_m128_d256_n512_none", 128, 256, 256, 512, ACT_NONE, "bf16", 1e-5, 1001),
     2: Workload("llama1b_attnout_mlpin_m16384", 16384, 2048, 2048, 16384, ACT_SWIGLU, "bf16", 1e-5, 1002),
@@ -97,6 +103,8 @@ WORKLOADS = {
     7: Workload("llama1b_mlpout_lmhead_ce_m16384", 16384, 8192, 2048, 128256, ACT_CE, "bf16", 1e-5, 1007),
     8: Workload("llama1b_mlpin_bwd_m16384", 16384, 0, 2048, 16384, ACT_SWIGLU_BWD, "bf16", 1e-5, 1008),
     9: Workload("llama1b_attnout_mlpin_bwd_m16384", 16384, 2048, 2048, 16384, ACT_CHAIN_BWD, "bf16", 1e-5, 1002),
+    10: Workload("llama1b_qkv_rope_bwd_m16384", 16384, 0, 2048, 3072, ACT_ROPE_BWD, "bf16", 1e-5, 1010,
+                 rot_cols=2560, seq_len=4096),
 }
 
 
@@ -105,7 +113,7 @@ def custom(M: int, K1: int, d: int, N2w: int, act: int, seed: int, dtype: str = 
     """A workload of arbitrary shape (ragged and edge-case tests)."""
     if act in (ACT_SWIGLU, ACT_SWIGLU_BWD, ACT_CHAIN_BWD) and N2w % 2:
         raise ValueError("SwiGLU needs an even number of second-weight rows")
-    if act == ACT_ROPE and (rot_cols % 64 or rot_cols > N2w or seq_len < 1):
+    if act in (ACT_ROPE, ACT_ROPE_BWD) and (rot_cols % 64 or rot_cols > N2w or seq_len < 1):
         raise ValueError("RoPE needs whole 64-value heads within the columns and a sequence length")
     return Workload(f"custom_m{M}_k{K1}_d{d}_n{N2w}_a{act}", M, K1, d, N2w, act, dtype, eps, seed,
                     rot_cols=rot_cols, seq_len=seq_len)
@@ -146,7 +154,7 @@ def generate(w: Workload, rows: int | None = None) -> dict:
     """
     rng = np.random.default_rng(w.seed)
     f32 = np.float32
-    if w.act == ACT_SWIGLU_BWD:
+    if w.act in (ACT_SWIGLU_BWD, ACT_ROPE_BWD):
         return _generate_bwd(w, rng, rows)
     A = rng.standard_normal((w.M, w.K1), dtype=f32)
     Wo = rng.standard_normal((w.d, w.K1), dtype=f32) * f32(1.0 / np.sqrt(w.K1))
@@ -181,18 +189,23 @@ def generate(w: Workload, rows: int | None = None) -> dict:
 
 
 def _generate_bwd(w: Workload, rng, rows):
-    """Inputs of the backward workload, drawn in the order h, gamma, W, dy:
+    """Inputs of the block-backward workloads, drawn in the order h, gamma, W, dy:
       h      uint16 [M, d]      bf16 bits, N(0, 1): the block's input (residual stream)
       gamma  float32 [d]        1 + 0.1 N(0, 1)
-      W_t    uint16 [2F, d]     bf16 bits, N(0, 1/d) (gate rows, then up rows)
-      dy     uint16 [M, F]      bf16 bits, N(0, 1): the upstream gradient of y
+      W_t    uint16 [N2w, d]    bf16 bits, N(0, 1/d) (SwiGLU: gate rows, then up rows)
+      dy     uint16 [M, n]      bf16 bits, N(0, 1): the upstream gradient of y (n = F for
+                                SwiGLU, N2w for RoPE)
+      pos    int32 [M]          RoPE only: token m's position, m mod seq_len
     """
     f32 = np.float32
-    F = w.N2w // 2
+    n = w.N2w // 2 if w.act == ACT_SWIGLU_BWD else w.N2w
     h = rng.standard_normal((w.M, w.d), dtype=f32)
     gamma = (f32(1.0) + f32(0.1) * rng.standard_normal(w.d, dtype=f32)).astype(f32)
     W = rng.standard_normal((w.N2w, w.d), dtype=f32) * f32(1.0 / np.sqrt(w.d))
-    dy = rng.standard_normal((w.M, F), dtype=f32)
+    dy = rng.standard_normal((w.M, n), dtype=f32)
     if rows is not None:
         h, dy = h[:rows], dy[:rows]
-    return {"h": to_bf16_bits(h), "gamma": gamma, "W_t": to_bf16_bits(W), "dy": to_bf16_bits(dy)}
+    out = {"h": to_bf16_bits(h), "gamma": gamma, "W_t": to_bf16_bits(W), "dy": to_bf16_bits(dy)}
+    if w.act == ACT_ROPE_BWD:
+        out["pos"] = (np.arange(h.shape[0]) % w.seq_len).astype(np.int32)
+    return out

@@ -319,3 +319,25 @@ def test_token_major_weight_gradient_validation():
     assert w(64, 64, 13, None, 64, P2, 64, None, None, P5, None, None, 0, None) == NULL
     assert w(64, 64, 13, P1, 64, P2, 64, None, None, P1 + 64, None, None, 0, None) == ALIAS  # dW over X
     assert w(64, 64, 13, P1, 64, P2 + 8, 64, None, None, P5, None, None, 0, None) == ALIGN
+
+
+@no_gpu
+def test_rope_backward_validation():
+    L = _lib.load()
+    f = L.coda_rope_bwd
+    DZ, PT = P6 + 0x1000000, P6 + 0x2000000
+    # M, N, dy, y, r, pos, cos, sin, table_rows, rot_cols, dz, partials, stream
+    assert f(16, 60, P1, P2, P3, P4, P5, P6, 8, 0, DZ, PT, None) == SHAPE       # N % 8
+    assert f(16, 128, P1, P2, P3, P4, P5, P6, 8, 96, DZ, PT, None) == SHAPE     # whole heads
+    assert f(16, 128, P1, P2, P3, P4, P5, P6, 8, 192, DZ, PT, None) == SHAPE    # rot_cols > N
+    assert f(16, 128, P1, P2, P3, P4, P5, P6, 0, 64, DZ, PT, None) == SHAPE     # empty table
+    assert f(16, 128, P1, P2, P3, None, P5, P6, 8, 64, DZ, PT, None) == NULL    # positions needed
+    # without rotation no table is read: a later check (alignment) is the one that fails
+    assert f(16, 128, P1 + 8, P2, P3, None, None, None, 0, 0, DZ, PT, None) == ALIGN
+    assert f(16, 128, P1, P2, P3, P4, P5, P6, 8, 64, None, PT, None) == NULL
+    assert f(16, 128, P1, P2, P3, P4, P5 + 4, P6, 8, 64, DZ, PT, None) == ALIGN  # cos 16-byte aligned
+    assert f(16, 128, P1 + 8, P2, P3, P4, P5, P6, 8, 64, DZ, PT, None) == ALIGN
+    assert f(16, 128, P1, P2, P3, P4, P5, P6, 8, 64, DZ, DZ + 64, None) == ALIAS  # partials over dz
+    assert f(16, 128, P1, P2, P3, P4, P5, P6, 8, 64, P2, PT, None) == ALIAS      # dz over y
+    assert f(16, 128, P1, P2, P3, P4, P5, P6, 8, 64, DZ, P6 + 64, None) == ALIAS  # partials over sin
+    assert f(0, 128, None, None, None, None, None, None, 0, 0, None, None, None) == OK     # empty batch
