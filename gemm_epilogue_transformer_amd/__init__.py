@@ -347,7 +347,7 @@ def wgrad_workspace_bytes(NR: int, NC: int, K: int) -> int:
 def gemm_wgrad(At, Bt, gamma=None, W=None, dW=None, partials=None, workspace=None, stream=None):
     """dW [NR, NC] fp32 = gamma * (At . Bt^T), a sum over the K tokens of At [NR, K] and
     Bt [NC, K]; with the raw weight W [NR, NC] also the per-256-row-tile partials of the
-    gamma gradient sum_j W[j,k] * G[j,k] (else partials is None).  Without W, a device
+    gamma gradient sum_j W[j,k] * G[j,k] (else partials is None).  A device
     ``workspace`` (uint8 tensor) of wgrad_workspace_bytes(NR, NC, K) bytes, when that is
     nonzero, lets the tokens be split over more blocks; workspace="auto" allocates it."""
     _esize(At, 2)
@@ -360,7 +360,7 @@ def gemm_wgrad(At, Bt, gamma=None, W=None, dW=None, partials=None, workspace=Non
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
-        n = wgrad_workspace_bytes(NR, NC, K) if W is None else 0
+        n = wgrad_workspace_bytes(NR, NC, K)
         workspace = torch.empty(n, dtype=torch.uint8, device=At.device) if n > 0 else None
     _lib.check("coda_gemm_wgrad", _lib.load().coda_gemm_wgrad(
         NR, NC, K, _ptr(At), _ptr(Bt), _ptr(gamma), _ptr(W), _ptr(dW),
@@ -386,7 +386,7 @@ def gemm_wgrad_tok(X, Y, gamma=None, W=None, dW=None, partials=None, workspace=N
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
-        n = wgrad_workspace_bytes(NR, NC, K) if W is None else 0
+        n = wgrad_workspace_bytes(NR, NC, K)
         workspace = torch.empty(n, dtype=torch.uint8, device=X.device) if n > 0 else None
     _lib.check("coda_gemm_wgrad_tok", _lib.load().coda_gemm_wgrad_tok(
         NR, NC, K, _ptr(X), lda, _ptr(Y), ldb, _ptr(gamma), _ptr(W), _ptr(dW),
@@ -409,10 +409,11 @@ def mlpin_wgrad(dz, h, gamma, W, dzt=None, ht=None, out=None, stream=None):
     W [2F, d] and gamma [d].  The GEMM reads dz and h as stored (token-major); with both
     dzt and ht given it reads those transposed copies instead."""
     out = out or {}
+    ws = out.get("wws", "auto")      # a token split when the weight has few 256-row tiles
     if dzt is not None and ht is not None:
-        dW, P = gemm_wgrad(dzt, ht, gamma, W, out.get("dW"), out.get("wpartials"), stream=stream)
+        dW, P = gemm_wgrad(dzt, ht, gamma, W, out.get("dW"), out.get("wpartials"), ws, stream=stream)
     else:
-        dW, P = gemm_wgrad_tok(dz, h, gamma, W, out.get("dW"), out.get("wpartials"), stream=stream)
+        dW, P = gemm_wgrad_tok(dz, h, gamma, W, out.get("dW"), out.get("wpartials"), ws, stream=stream)
     dgam = colsum_reduce(P, out.get("dgamma"), stream)
     return dW, dgam
 

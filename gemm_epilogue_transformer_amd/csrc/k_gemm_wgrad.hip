@@ -23,9 +23,10 @@
 
 namespace coda {
 
-// Split over the tokens (S > 1, only without W): block (s, tile) sums tokens
-// [s * k_split, min((s + 1) * k_split, K)) and writes its raw sums (no gamma) to slice s
-// of dW, which is then the [S, NR, NC] workspace that k_splitk_reduce adds up.
+// Split over the tokens (S > 1): block (s, tile) sums tokens [s * k_split,
+// min((s + 1) * k_split, K)) and writes its raw sums (no gamma) to slice s of dW, which
+// is then the [S, NR, NC] workspace, and (with W) its partial rows to slice s of an
+// [S, tiles_m, NC] workspace region; k_splitk_reduce adds up each in a fixed order.
 //
 // TOK: the operands are token-major, X [K, lda] and Y [K, ldb] (the activations as the
 // forward and backward store them, NR and NC of their columns used), read through LDS
@@ -90,6 +91,7 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
         mainloop_dma<Elt::BF16, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kext, st, a_row, b_row);
     }
     dW += static_cast<size_t>(split) * NR * NC;
+    if (Wraw) Pg += static_cast<size_t>(split) * tiles_m * NC;   // a token split's own partial rows
 
     using S = Slab<TN>;
     static_assert(64 % S::kSegPerRow == 0, "a lane's segments share their columns");
@@ -237,18 +239,34 @@ constexpr int BMW = CODA_WG_BM, BNW = CODA_WG_BN;
 int64_t wgrad_tiles(int64_t NR, int64_t NC) { return ((NR + BMW - 1) / BMW) * ((NC + BNW - 1) / BNW); }
 int64_t wgrad_partials_rows(int64_t NR) { return NR < 1 ? -1 : (NR + BMW - 1) / BMW; }
 
-// Token splits for a problem of `tiles` output tiles: enough blocks for the 256 CUs
-// (one 256 x 256 tile each at a time), each split at least kMinSplitTokens tokens.
+// Token splits for a problem of `tiles` output tiles, each split at least
+// kMinSplitTokens tokens: the S that minimises the estimated time of the rounds of
+// blocks the 256 CUs run (one 256 x 256 tile each at a time; a round costs the block's
+// tokens at ~30 ns per token and tile) plus the fp32 slices the split writes and its
+// reduce reads back (2 S NR NC 4 bytes at ~5 TB/s).  A partly filled last round costs
+// as much as a full one, so S is chosen against it, not just to reach 256 blocks.
 constexpr int kMinSplitTokens = 2048, kMaxSplits = 16;
 int wgrad_splits(int64_t NR, int64_t NC, int64_t K) {
     const int64_t tiles = wgrad_tiles(NR, NC);
-    int64_t S = (256 + tiles - 1) / tiles;
-    S = std::min<int64_t>(S, std::max<int64_t>(1, K / kMinSplitTokens));
-    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(S, kMaxSplits)));
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, K / kMinSplitTokens));
+    constexpr double kNsPerTileToken = 30.5, kBytesPerNs = 5000.0;
+    int best = 1;
+    double best_ns = 0.0;
+    for (int64_t S = 1; S <= smax; ++S) {
+        const int64_t rounds = (tiles * S + 255) / 256;
+        const double ns = static_cast<double>(rounds) * static_cast<double>((K + S - 1) / S) * kNsPerTileToken +
+                          (S > 1 ? 2.0 * static_cast<double>(S) * NR * NC * 4 / kBytesPerNs : 0.0);
+        if (S == 1 || ns < best_ns) {
+            best = static_cast<int>(S);
+            best_ns = ns;
+        }
+    }
+    return best;
 }
+// the split's dW slices [S, NR, NC], then its gamma-gradient partial slices [S, tiles_m, NC]
 int64_t wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K) {
     const int S = wgrad_splits(NR, NC, K);
-    return S > 1 ? static_cast<int64_t>(S) * NR * NC * 4 : 0;
+    return S > 1 ? static_cast<int64_t>(S) * (NR + (NR + BMW - 1) / BMW) * NC * 4 : 0;
 }
 
 template <bool TOK>
@@ -256,23 +274,34 @@ static hipError_t launch_wgrad(int NR, int NC, int K, const void* At, int lda, c
                                const float* gamma, const void* Wraw, float* dW, float* Pg, float* ws,
                                int64_t ws_bytes, hipStream_t stream) {
     const int tiles_m = (NR + BMW - 1) / BMW, tiles_n = (NC + BNW - 1) / BNW;
-    int S = Wraw ? 1 : wgrad_splits(NR, NC, K);
-    if (S > 1 && (ws == nullptr || ws_bytes < static_cast<int64_t>(S) * NR * NC * 4)) S = 1;
+    int S = wgrad_splits(NR, NC, K);
+    auto need = [&](int s) { return static_cast<int64_t>(s) * (NR + (Wraw ? tiles_m : 0)) * NC * 4; };
+    if (S > 1 && (ws == nullptr || ws_bytes < need(S))) S = 1;
     // tokens per split: a multiple of the 64-token k-step
     const int k_split = S > 1 ? ((K + S - 1) / S + 63) / 64 * 64 : K;
     S = (K + k_split - 1) / k_split;
+    // split: dW slices, then (with W) the partial slices, in the workspace
+    float* ws_p = S > 1 ? ws + static_cast<int64_t>(S) * NR * NC : nullptr;
     const dim3 grid(tiles_m * tiles_n * S), block(64 * CODA_WG_WM * CODA_WG_WN);
     hipLaunchKernelGGL((k_gemm_wgrad<BMW, BNW, CODA_WG_WM, CODA_WG_WN, CODA_WG_NS, CODA_WG_RB, CODA_WG_SPREAD,
                                      CODA_WG_OCC, TOK>),
                        grid, block, 0, stream, static_cast<const uint8_t*>(At), static_cast<const uint8_t*>(Bt),
-                       S > 1 ? nullptr : gamma, static_cast<const uint16_t*>(Wraw), S > 1 ? ws : dW, Pg, NR, NC,
-                       K, tiles_m, tiles_n, k_split, lda, ldb);
+                       S > 1 ? nullptr : gamma, static_cast<const uint16_t*>(Wraw), S > 1 ? ws : dW,
+                       S > 1 && Wraw ? ws_p : Pg, NR, NC, K, tiles_m, tiles_n, k_split, lda, ldb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     const int64_t n4 = static_cast<int64_t>(NR) * NC / 4;
     const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
     hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                        reinterpret_cast<const f32x4_t*>(ws), gamma, reinterpret_cast<f32x4_t*>(dW), n4, NC / 4, S);
+    e = hipGetLastError();
+    if (e != hipSuccess || !Wraw) return e;
+    // the gamma-gradient partials: the splits' rows added in the same fixed order (the
+    // sums are linear in G, so adding per-split partials equals partials of the sum)
+    const int64_t p4 = static_cast<int64_t>(tiles_m) * NC / 4;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>(std::min<int64_t>((p4 + 255) / 256, 4096))),
+                       dim3(256), 0, stream, reinterpret_cast<const f32x4_t*>(ws_p), nullptr,
+                       reinterpret_cast<f32x4_t*>(Pg), p4, NC / 4, S);
     return hipGetLastError();
 }
 

@@ -380,9 +380,10 @@ coda_status coda_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const
 /* Partial rows written by coda_gemm_wgrad for NR gradient rows; -1 if NR < 1.          */
 int64_t coda_wgrad_partials_rows(int64_t NR);
 
-/* Workspace bytes that let coda_gemm_wgrad (without W) split the K tokens over more
- * blocks when the NR x NC output has too few 256 x 256 tiles to fill the GPU; 0 when no
- * split helps; -1 for invalid sizes.                                                   */
+/* Workspace bytes that let coda_gemm_wgrad split the K tokens over more blocks when the
+ * NR x NC output has too few 256 x 256 tiles to fill the GPU (room for the split's dW
+ * slices and, with W, its gamma-gradient partial slices); 0 when no split helps; -1 for
+ * invalid sizes.                                                                       */
 int64_t coda_wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K);
 
 /* Weight-gradient GEMM, contraction over K tokens (the weight-gradient passages cited
@@ -393,10 +394,10 @@ int64_t coda_wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K);
  *   partials [coda_wgrad_partials_rows(NR), NC] fp32, written when W is given: per tile
  *       of 256 rows j, sum of W[j,k] * G[j,k] (fixed order); may be NULL when W is NULL
  *   workspace: device scratch of workspace_bytes (NULL / 0 for none), 16-byte aligned.
- *       Without W, and with at least coda_wgrad_workspace_bytes(NR, NC, K) bytes, the
- *       tokens are split over several blocks per tile whose fp32 sums are added in a
- *       fixed order (then gamma applied): the result is reproducible for the same
- *       arguments but its last bits depend on whether the split was taken.
+ *       With at least coda_wgrad_workspace_bytes(NR, NC, K) bytes, the tokens are split
+ *       over several blocks per tile whose fp32 sums (and, with W, partial rows) are
+ *       added in a fixed order (then gamma applied): the result is reproducible for the
+ *       same arguments but its last bits depend on whether the split was taken.
  * K = 0 (no tokens) writes zeros.  Granules: K % 8 == 0, NC % 8 == 0; K <= 2^22,
  * NC <= 2^21.  Outputs and workspace must not overlap each other or the inputs.
  * CODA_ERR_VALUE: workspace_bytes < 0, or > 0 with a NULL workspace.                 */

@@ -251,7 +251,8 @@ def test_weight_gradient_validation():
     assert w(64, 64, 64, P1, P2, P3, None, P5, None, P1 + 64, 64, None) == ALIAS    # workspace over At
     assert L.coda_wgrad_workspace_bytes(0, 64, 64) == -1
     assert L.coda_wgrad_workspace_bytes(16384, 2048, 16384) == 0                # 512 tiles: no split
-    assert L.coda_wgrad_workspace_bytes(2048, 2048, 16384) == 4 * 2048 * 2048 * 4   # 64 tiles: 4 splits
+    # 64 tiles: 4 splits, each a dW slice and the partial rows of its 8 row tiles
+    assert L.coda_wgrad_workspace_bytes(2048, 2048, 16384) == 4 * (2048 + 8) * 2048 * 4
     assert L.coda_wgrad_workspace_bytes(2048, 2048, 2048) == 0                  # too few tokens to split
     c = L.coda_colsum_reduce
     assert c(0, 64, P1, P2, None) == SHAPE

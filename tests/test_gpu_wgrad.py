@@ -173,7 +173,7 @@ def test_token_split_matches_the_definition_and_is_reproducible():
     # last split ragged), their sums added in a fixed order, then gamma
     rng = np.random.default_rng(20)
     NR, NC, K = 520, 136, 8200
-    assert coda.wgrad_workspace_bytes(NR, NC, K) == 4 * NR * NC * 4
+    assert coda.wgrad_workspace_bytes(NR, NC, K) == 4 * (NR + 3) * NC * 4    # dW slices + 3 row tiles' partials
     a = si.to_bf16_bits(rng.standard_normal((NR, K)).astype(np.float32))
     b = si.to_bf16_bits(rng.standard_normal((NC, K)).astype(np.float32))
     g = np.exp2(rng.integers(-3, 4, NC)).astype(np.float32)
@@ -192,6 +192,47 @@ def test_token_split_matches_the_definition_and_is_reproducible():
         err = np.abs(got.cpu().numpy().astype(np.float64) - ref)
         _log(f"  token split err max {err.max():.2e}, bound min {bound.min():.2e}")
         assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("tok", [False, True], ids=["transposed", "token_major"])
+def test_token_split_with_gamma_partials(tok):
+    # few output tiles and a raw weight: each split writes its dW slice and the partial
+    # rows sum_j W[j,k] G_s[j,k] of its tokens; both are added in a fixed order.  Against
+    # the fp64 definitions (fp32 sums: |err| <= (K + 256) 2^-24 sum |terms|), reproducible
+    rng = np.random.default_rng(21)
+    NR, NC, K = 520, 136, 8200
+    a = si.to_bf16_bits(rng.standard_normal((K, NR)).astype(np.float32))      # token-major
+    b = si.to_bf16_bits(rng.standard_normal((K, NC)).astype(np.float32))
+    w = si.to_bf16_bits(rng.standard_normal((NR, NC)).astype(np.float32))
+    g = np.exp2(rng.integers(-3, 4, NC)).astype(np.float32)
+    ad, bd, wd = dev_bf16(a), dev_bf16(b), dev_bf16(w)
+    gd = torch.from_numpy(g).cuda()
+    if tok:
+        run = lambda ws: coda.gemm_wgrad_tok(ad, bd, gd, wd, workspace=ws)  # noqa: E731
+    else:
+        at, bt = ad.t().contiguous(), bd.t().contiguous()
+        run = lambda ws: coda.gemm_wgrad(at, bt, gd, wd, workspace=ws)  # noqa: E731
+    ws = torch.empty(coda.wgrad_workspace_bytes(NR, NC, K), dtype=torch.uint8, device="cuda")
+    d1, p1 = run(ws)
+    d2, p2 = run(ws)
+    d0, p0 = run(None)                                              # one block per tile
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(p1, p2)
+    A, B, W = oracle.bf16_decode(a), oracle.bf16_decode(b), oracle.bf16_decode(w)
+    G, Ga = A.T @ B, np.abs(A).T @ np.abs(B)
+    u = (K + 256) * 2.0 ** -24
+    gg = g.astype(np.float64)[None, :]
+    for dW, P in ((d1, p1), (d0, p0)):
+        err = np.abs(dW.cpu().numpy().astype(np.float64) - G * gg)
+        assert np.all(err <= u * Ga * gg)
+        Pn = P.cpu().numpy().astype(np.float64)
+        assert Pn.shape == (3, NC)
+        for t in range(3):
+            rows = slice(256 * t, min(256 * (t + 1), NR))
+            ref = (W[rows] * G[rows]).sum(axis=0)
+            bound = u * (np.abs(W[rows]) * Ga[rows]).sum(axis=0)
+            _log(f"  partials tile {t}: err max {np.abs(Pn[t] - ref).max():.2e}, bound min {bound.min():.2e}")
+            assert np.all(np.abs(Pn[t] - ref) <= bound)
 
 
 @pytest.mark.parametrize("K,NR,NC,lda,ldb", [(712, 300, 136, 304, 136), (520, 264, 72, 264, 80), (8200, 520, 136, 520, 136),
