@@ -25,7 +25,7 @@ ACT_SWIGLU = 1
 
 __all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
            "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "rope_transpose", "cross_entropy", "mlpin_bwd",
-           "mlpin_wgrad", "chain_bwd", "qkv_rope_bwd", "chain", "prepare", "BF16", "E4M3",
+           "mlpin_wgrad", "chain_bwd", "qkv_rope_bwd", "lmhead_ce_bwd", "chain", "prepare", "BF16", "E4M3",
            "ACT_NONE", "ACT_SWIGLU"]
 
 
@@ -289,6 +289,72 @@ def qkv_rope_bwd(hb, gamma, Wp, wp_scale: float, W_raw, dy, pos, base: float, he
         out["rss_gamma"] = None
         if js is None:
             out["rss_gamma"] = np.sqrt((((dz_all * dz_all) @ (wraw[:, k] * wraw[:, k])) * hk * hk).sum(axis=0))
+    return out
+
+
+def lmhead_ce_bwd(hb, gamma, Wp, wp_scale: float, W_raw, targets, g, eps: float, rows=None, js=None, ks=None,
+                  rss=False):
+    """Backward of the LM-head block  loss_m = CE( RMSNorm(hb) . W_or^T, t_m )  weighted by
+    g[m] = d(total loss)/d(loss_m) (kucoin page, section "CODA: El epilogo esconde un
+    tesoro", last paragraph: the reparameterisation covers the cross-entropy loss and
+    holds for the backward pass).  The chain rule in reverse order, plain fp64:
+      forward   r = 1/sqrt(mean(hb^2) + eps),  n = hb r gamma,  z = n . W_or^T,
+                lse = log sum_v exp z_v,  loss = lse - z_t   (0 for t outside [0, V))
+      loss      dz_v = g (softmax(z)_v - [v == t])           (0 for an ignored row)
+      GEMM      dn = dz . W_or;   dW[j, k] = sum_m dz[m, j] n[m, k]   (the raw weight's)
+      RMSNorm   dhb[k] = r gamma[k] dn[k] - (r^3 / d) hb[k] sum_k' gamma[k'] dn[k'] hb[k']
+                dgamma[k] = sum_m sum_j dz[m, j] W_raw[j, k] hb[m, k] r[m]
+    (W_or = Wp * wp_scale / gamma.)  hb uint16 [M, d] bf16 codes, gamma fp32 [d], Wp and
+    W_raw uint16 [V, d], targets int [M], g float [M].
+
+    Returns dict(dh [R, d], r [R], dz [R, V], lse [R]) for the listed rows (default all);
+    with js given (a list of weight rows, or "all") also dW [nj, nk] summed over all M
+    tokens at columns ks (default all d), dgamma [nk] for js == "all", and with rss=True
+    the root-sum-squares of their terms (rss [nj, nk] with gamma left out, rss_gamma).
+    The weight gradient needs the softmax of every token's logits (M V d operations)."""
+    hbv = bf16_decode(np.asarray(hb, dtype=np.uint16))
+    g_ = np.asarray(gamma, dtype=np.float64)
+    wor = bf16_decode(np.asarray(Wp, dtype=np.uint16)) * float(wp_scale) / g_[None, :]
+    wraw = bf16_decode(np.asarray(W_raw, dtype=np.uint16))
+    t = np.asarray(targets, dtype=np.int64)
+    gw = np.asarray(g, dtype=np.float64)
+    M, d = hbv.shape
+    V = wor.shape[0]
+    if wor.shape != (V, d) or wraw.shape != (V, d) or t.shape != (M,) or gw.shape != (M,) or g_.shape != (d,):
+        raise ValueError("shape mismatch")
+    r_all = 1.0 / np.sqrt((hbv * hbv).sum(axis=1) / d + eps)
+
+    def dlogits(idx):
+        n = hbv[idx] * r_all[idx, None] * g_[None, :]
+        z = n @ wor.T
+        mx = z.max(axis=1, keepdims=True)
+        lse = mx[:, 0] + np.log(np.exp(z - mx).sum(axis=1))
+        p = np.exp(z - lse[:, None])
+        ti = t[idx]
+        valid = (ti >= 0) & (ti < V)
+        p[valid, ti[valid]] -= 1.0
+        return p * (gw[idx] * valid)[:, None], lse
+
+    rr = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    dz, lse = dlogits(rr)
+    dn = dz @ wor
+    hr, rv = hbv[rr], r_all[rr]
+    c = (g_[None, :] * dn * hr).sum(axis=1)
+    dh = rv[:, None] * g_[None, :] * dn - (rv ** 3 / d)[:, None] * hr * c[:, None]
+    out = dict(dh=dh, r=rv, dz=dz, lse=lse)
+    if js is not None:
+        full = isinstance(js, str)
+        j = np.arange(V) if full else np.asarray(js, dtype=np.int64)
+        k = np.arange(d) if ks is None else np.asarray(ks, dtype=np.int64)
+        dz_all, _ = dlogits(np.arange(M))
+        tj = dz_all[:, j]
+        hk = hbv[:, k] * r_all[:, None]
+        out["dW"] = (tj.T @ hk) * g_[k][None, :]
+        out["dgamma"] = ((dz_all @ wraw[:, k]) * hk).sum(axis=0) if full else None
+        if rss:
+            out["rss"] = np.sqrt((tj * tj).T @ (hk * hk))
+            out["rss_gamma"] = (np.sqrt((((dz_all * dz_all) @ (wraw[:, k] * wraw[:, k])) * hk * hk).sum(axis=0))
+                                if full else None)
     return out
 
 
