@@ -681,6 +681,166 @@ def bench_rope_backward(w, args) -> dict:
     return rec
 
 
+def bench_ce_backward(w, args) -> dict:
+    """Backward step of the LM-head block loss_m = CE(RMSNorm(h) . W^T, t_m) for the mean
+    loss: the recomputed logits product with the loss backward in its epilogue, the row
+    coefficient, the input-gradient GEMM, the weight-gradient GEMM on dz and h as stored
+    (split over the tokens: dz's rows are too wide for one 32-bit addressed range) and
+    the column sum for gamma.  The forward state -- folded weight and its transpose, r
+    and the log-sum-exp from a forward run of the loss -- is prepared outside the timed
+    region."""
+    import numpy as np
+    import torch
+
+    import gemm_epilogue_transformer_amd as coda
+    import synth_inputs as si
+
+    inp = si.generate(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+    h, W = dev(inp["h"]), dev(inp["W_t"])
+    gamma = torch.from_numpy(inp["gamma"]).cuda()
+    tgt = torch.from_numpy(inp["targets"]).cuda()
+    gw = torch.from_numpy(inp["g"]).cuda()
+    M, d, V = w.M, w.d, w.N2w
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    Wp = coda.prepare_weight_bf16(W, gamma)
+    Wpt = coda.transpose_bf16(Wp)
+    r = coda.rowscale_from_h(h, w.eps)
+    fp, tl = coda.gemm_rowscale_ce(h, Wp, r, tgt)
+    lse, _ = coda.ce_reduce(fp, tgt, tl, V)
+    del fp
+    torch.cuda.synchronize()
+    prep_ms = (time.perf_counter() - t0) * 1e3
+    T = -(-V // 128)
+    TW = coda.wgrad_partials_rows(V)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    b16 = dict(dtype=torch.bfloat16, device="cuda")
+    out = {"dz": torch.empty((M, V), **b16), "partials": torch.empty((M, T), **f32), "q": torch.empty(M, **f32),
+           "dh": torch.empty((M, d), **b16), "dW": torch.empty((V, d), **f32),
+           "wpartials": torch.empty((TW, d), **f32), "dgamma": torch.empty(d, **f32)}
+    nws = int(coda._lib.load().coda_wgrad_tok_workspace_bytes(V, d, M, V, d))
+    out["wws"] = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws > 0 else None
+    stream = torch.cuda.current_stream()
+    stages = [
+        ("gemm_ce_bwd", "k_gemm_rowscale_swiglu",
+         lambda: coda.gemm_ce_bwd(h, Wp, r, tgt, lse, gw, out["dz"], out["partials"])),
+        ("rmsnorm_bwd_reduce", "k_rmsnorm_bwd_reduce",
+         lambda: coda.rmsnorm_bwd_reduce(out["partials"], r, d, V, out["q"])),
+        ("gemm_rmsnorm_bwd", "k_gemm_rmsnorm_bwd",
+         lambda: coda.gemm_rmsnorm_bwd(out["dz"], Wpt, h, out["q"], None, out["dh"])),
+        ("gemm_wgrad", "k_gemm_wgrad",
+         lambda: coda.gemm_wgrad_tok(out["dz"], h, gamma, W, out["dW"], out["wpartials"], out["wws"])),
+        ("colsum_reduce", "k_colsum_reduce", lambda: coda.colsum_reduce(out["wpartials"], out["dgamma"]))]
+    names = [x[0] for x in stages]
+    kern = [x[1] for x in stages]
+
+    def step(ev=None):
+        for i, (_, _, call) in enumerate(stages):
+            if ev is not None:
+                ev[i].record(stream)
+            call()
+        if ev is not None:
+            ev[len(stages)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    k_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(len(names))]
+    g_flops = 2 * M * d * V
+    gemm_fl = {names.index("gemm_ce_bwd"): g_flops, names.index("gemm_rmsnorm_bwd"): g_flops,
+               names.index("gemm_wgrad"): g_flops}
+    value = w.gemm_flops / (ms_per_step * 1e-3) / 1e12
+    dom = max(gemm_fl, key=lambda i: k_ms[i])
+    byt = {"gemm_ce_bwd": M * d * 2 + V * d * 2 + 4 * M * 4 + M * V * 2 + M * T * 4,
+           "rmsnorm_bwd_reduce": M * T * 4 + 2 * M * 4,
+           "gemm_rmsnorm_bwd": M * V * 2 + d * V * 2 + M * d * 2 + M * 4 + M * d * 2,
+           "gemm_wgrad": M * V * 2 + M * d * 2 + d * 4 + V * d * 2 + V * d * 4 + TW * d * 4,
+           "colsum_reduce": TW * d * 4 + d * 4}
+    achieved = gemm_fl[dom] / (k_ms[dom] * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "d": d, "V": V, "loss": "mean cross-entropy",
+                   "direction": "backward of the LM-head block (dh, dW, dgamma)", "eps": w.eps, "seed": w.seed},
+        "note": "FLOPs of the executed GEMMs: the recomputed logits product, the input-gradient product and "
+                "the weight-gradient product",
+        "kernels_ms": {n: round(t, 4) for n, t in zip(names, k_ms)},
+        "gemm_tflops": {names[i]: round(gemm_fl[i] / (k_ms[i] * 1e-3) / 1e12, 1) for i in gemm_fl},
+        "hbm_bytes_algorithmic": {"fused": sum(byt[n] for n in names)},
+        "prep_ms": round(prep_ms, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": load_traffic(w.name, kern[dom]), "kernel": kern[dom],
+                     "kernel_ms": round(k_ms[dom], 4), "algorithmic_bytes": byt[names[dom]],
+                     "kernel_source_hash": kernel_source_hash(kern[dom])},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if args.unfused:
+        # torch autograd of the unfused forward (bf16 GEMM writing the logits, element-wise
+        # RMSNorm, torch's cross_entropy on fp32 logits, mean) for the same gradients
+        for k in ("dz", "dW", "wws"):
+            out[k] = None
+        torch.cuda.empty_cache()
+        hh = h.clone().requires_grad_(True)
+        Wl = W.clone().requires_grad_(True)
+        gl = gamma.clone().requires_grad_(True)
+        hf = hh.float()
+        n = (hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + w.eps)).to(torch.bfloat16) * gl.to(torch.bfloat16)
+        z = n @ Wl.t()
+        loss = torch.nn.functional.cross_entropy(z.float(), tgt.long())
+
+        def ubwd():
+            torch.autograd.grad((loss,), (hh, Wl, gl), retain_graph=True)
+
+        for _ in range(2):
+            ubwd()
+        torch.cuda.synchronize()
+        s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nu = max(1, min(args.steps, 10))
+        s2.record(stream)
+        for _ in range(nu):
+            ubwd()
+        e2.record(stream)
+        torch.cuda.synchronize()
+        ums = s2.elapsed_time(e2) / nu
+        rec["unfused_torch"] = {"ms_per_step": round(ums, 4), "speedup_of_fused": round(ums / ms_per_step, 3),
+                                "note": f"torch autograd of the same gradients from saved activations (2 GEMMs, "
+                                        f"fp32 logits), {nu} steps"}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        rng = np.random.default_rng(0)
+        Wp_ref = oracle.fold_bf16(inp["W_t"], inp["gamma"])
+        n_rows = 2
+        while True:
+            rows = np.sort(rng.choice(M, size=min(n_rows, M), replace=False))
+            t1 = time.perf_counter()
+            oracle.lmhead_ce_bwd(inp["h"], inp["gamma"], Wp_ref, 1.0, inp["W_t"], inp["targets"], inp["g"], w.eps,
+                                 rows=rows)
+            dt = time.perf_counter() - t1
+            if dt >= args.cpu_seconds / 2 or n_rows >= M:
+                break
+            n_rows *= 2
+        done = rows.size * 2 * (2 * V * d)                 # the recomputed logits and dh per row
+        rec["cpu_baseline"] = {"value": round(done / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"{rows.size} random rows of dh (their logits recomputed) of the {M}-token "
+                                         f"workload in one oracle call (fp64), {dt:.1f} s; the weight gradient, "
+                                         f"which needs every token's softmax, is not sampled"}
+    return rec
+
+
 def _oracle_path(oracle, prep, inp, w, rows):
     """The oracle's whole path for the rows: the chain, then RoPE or the loss."""
     import synth_inputs as si
@@ -730,7 +890,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, help="workload number (1-10)")
+    ap.add_argument("--workload", type=int, default=2, help="workload number (1-11)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="also time the unfused torch chain")
@@ -794,6 +954,9 @@ def main():
         return
     if w.act == si.ACT_ROPE_BWD:
         print(json.dumps(bench_rope_backward(w, args)), flush=True)
+        return
+    if w.act == si.ACT_CE_BWD:
+        print(json.dumps(bench_ce_backward(w, args)), flush=True)
         return
     inp = si.generate(w)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731

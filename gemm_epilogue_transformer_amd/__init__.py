@@ -26,7 +26,8 @@ __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3"
            "gemm_rowscale_ce", "ce_reduce", "rowscale_from_h", "transpose_bf16", "gemm_swiglu_bwd", "rmsnorm_bwd_reduce",
            "gemm_rmsnorm_bwd", "mlpin_bwd", "wgrad_partials_rows", "gemm_wgrad", "colsum_reduce",
            "mlpin_wgrad", "gemm_bf16", "chain_bwd", "wgrad_workspace_bytes", "gemm_rowscale_swiglu_save",
-           "swiglu_bwd_saved", "gemm_rowscale_gfold", "gemm_wgrad_tok", "rope_bwd", "qkv_rope_bwd", "chain",
+           "swiglu_bwd_saved", "gemm_rowscale_gfold", "gemm_wgrad_tok", "rope_bwd", "qkv_rope_bwd", "gemm_ce_bwd",
+           "lmhead_ce_bwd", "chain",
            "version"]
 
 
@@ -324,6 +325,40 @@ def qkv_rope_bwd(h, r, Wpt, W, gamma, dy, y, pos, cos, sin, rot_cols, dh_res=Non
     return dict(dh=dh, dW=dW, dgamma=dgam, dz=dz, q=q)
 
 
+def gemm_ce_bwd(h, W, r, targets, lse, g, dz=None, partials=None, stream=None):
+    """The LM-head product recomputed with the cross-entropy backward in its epilogue:
+    returns (dz [M, V] = r * g * (softmax - onehot) in bf16 (zero rows for ignored
+    targets), partials [M, T] = per 128 columns sum of dL/dz * acc, the layout
+    rmsnorm_bwd_reduce takes with F = V).  W [V, K] is the gamma-folded weight."""
+    _esize(W, 2)
+    M, K = h.shape
+    V = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("h and W disagree on K")
+    if targets.dtype != torch.int32:
+        raise ValueError("targets must be int32")
+    T = int(_lib.load().coda_swiglu_bwd_partials_per_row(V))
+    dz = torch.empty((M, V), dtype=torch.bfloat16, device=h.device) if dz is None else dz
+    partials = torch.empty((M, T), dtype=torch.float32, device=h.device) if partials is None else partials
+    _lib.check("coda_gemm_ce_bwd", _lib.load().coda_gemm_ce_bwd(
+        M, V, K, _ptr(h), _ptr(W), _ptr(r), _ptr(targets), _ptr(lse), _ptr(g), _ptr(dz), _ptr(partials),
+        _stream(stream)))
+    return dz, partials
+
+
+def lmhead_ce_bwd(h, r, Wp, Wpt, W, gamma, targets, lse, g, dh_res=None, out=None, stream=None):
+    """Backward of the LM-head block from the forward's h, r and lse: the recomputed
+    product with the loss backward, the row coefficient, the input-gradient GEMM (Wpt =
+    W'^T [d, V]) and the weight / gamma gradients on dz and h as stored.  Returns dict(dh,
+    dW [V, d] fp32, dgamma [d] fp32, dz, q)."""
+    out = out or {}
+    dz, P = gemm_ce_bwd(h, Wp, r, targets, lse, g, out.get("dz"), out.get("partials"), stream)
+    q = rmsnorm_bwd_reduce(P, r, h.shape[1], Wp.shape[0], out.get("q"), stream)
+    dh = gemm_rmsnorm_bwd(dz, Wpt, h, q, dh_res, out.get("dh"), stream)
+    dW, dgam = mlpin_wgrad(dz, h, gamma, W, out=out, stream=stream)
+    return dict(dh=dh, dW=dW, dgamma=dgam, dz=dz, q=q)
+
+
 def gemm_bf16(A, Bt, c_res=None, C=None, stream=None):
     """C [M, N] = A [M, K] . Bt [N, K]^T (+ c_res) in bf16 (fp32 sums)."""
     _esize(A, 2)
@@ -386,7 +421,7 @@ def gemm_wgrad_tok(X, Y, gamma=None, W=None, dW=None, partials=None, workspace=N
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
-        n = wgrad_workspace_bytes(NR, NC, K)
+        n = int(_lib.load().coda_wgrad_tok_workspace_bytes(NR, NC, K, lda, ldb))
         workspace = torch.empty(n, dtype=torch.uint8, device=X.device) if n > 0 else None
     _lib.check("coda_gemm_wgrad_tok", _lib.load().coda_gemm_wgrad_tok(
         NR, NC, K, _ptr(X), lda, _ptr(Y), ldb, _ptr(gamma), _ptr(W), _ptr(dW),

@@ -40,6 +40,8 @@ SIGNATURES = {
     "coda_gemm_rowscale_swiglu_save": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "coda_swiglu_bwd_saved": (_I, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "coda_rope_bwd": (_I, [_I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P]),
+    "coda_gemm_ce_bwd": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "coda_wgrad_tok_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64, _I64]),
     "coda_gemm_bf16": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "coda_wgrad_partials_rows": (_I64, [_I64]),
     "coda_wgrad_workspace_bytes": (_I64, [_I64, _I64, _I64]),

@@ -6,6 +6,8 @@
 #include <cmath>
 #include <cstdint>
 
+#include <algorithm>
+
 #include "../../include/coda.h"
 #include "launch.hpp"
 
@@ -305,6 +307,28 @@ coda_status coda_gemm_swiglu_bwd(int64_t M, int64_t F, int64_t K, const void* h,
                                                    as_stream(stream)));
 }
 
+coda_status coda_gemm_ce_bwd(int64_t M, int64_t V, int64_t K, const void* h, const void* W, const float* r,
+                             const int32_t* targets, const float* lse, const float* g, void* dz, float* partials,
+                             void* stream) {
+    if (!dim_ok(M, 0) || !dim_ok(V, 1) || !dim_ok(K, 1)) return CODA_ERR_SHAPE;
+    if (V % 8 != 0 || K % 8 != 0 || 2 * V > kMaxRow || K > kMaxRow) return CODA_ERR_SHAPE;
+    const int64_t T = coda::swiglu_bwd_partials_per_row(V);
+    if (!prod_ok(M, K) || !prod_ok(V, K) || !prod_ok(M, V) || !prod_ok(M, T)) return CODA_ERR_SHAPE;
+    if (coda::gemm3_tiles(M, V, false) > kMaxDim) return CODA_ERR_SHAPE;
+    if (M == 0) return CODA_OK;
+    if (!h || !W || !r || !targets || !lse || !g || !dz || !partials) return CODA_ERR_NULL;
+    if (!aligned16(h) || !aligned16(W) || !aligned16(r) || !aligned16(dz) || !aligned16(partials))
+        return CODA_ERR_ALIGN;
+    const Range rz = span(dz, M * V * 2), rp = span(partials, M * T * 4);
+    const Range ins[] = {span(h, M * K * 2), span(W, V * K * 2), span(r, M * 4), span(targets, M * 4),
+                         span(lse, M * 4), span(g, M * 4)};
+    if (overlap(rz, rp)) return CODA_ERR_ALIAS;
+    for (const Range& in : ins)
+        if (overlap(rz, in) || overlap(rp, in)) return CODA_ERR_ALIAS;
+    return hip_status(coda::launch_gemm_ce_bwd(int(M), int(V), int(K), h, W, r, targets, lse, g, dz, partials,
+                                               as_stream(stream)));
+}
+
 coda_status coda_rmsnorm_bwd_reduce(int64_t M, int64_t N, int64_t F, const float* partials,
                                     const float* r, float* q, void* stream) {
     if (!dim_ok(M, 0) || !dim_ok(N, 1) || !dim_ok(F, 1) || 2 * F > kMaxRow) return CODA_ERR_SHAPE;
@@ -441,6 +465,12 @@ coda_status coda_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const
 
 int64_t coda_wgrad_partials_rows(int64_t NR) { return NR < 1 || NR > kMaxDim ? -1 : coda::wgrad_partials_rows(NR); }
 
+int64_t coda_wgrad_tok_workspace_bytes(int64_t NR, int64_t NC, int64_t K, int64_t lda, int64_t ldb) {
+    if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0) || lda < NR || ldb < NC || lda > kMaxRow || ldb > kMaxRow)
+        return -1;
+    return coda::wgrad_tok_workspace_bytes(NR, NC, K, lda, ldb);
+}
+
 int64_t coda_wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K) {
     if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0) || !prod_ok(NR, NC)) return -1;
     return coda::wgrad_workspace_bytes(NR, NC, K);
@@ -483,8 +513,10 @@ coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X
     if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0)) return CODA_ERR_SHAPE;
     if (NC % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || lda < NR || ldb < NC) return CODA_ERR_SHAPE;
     if (lda > kMaxRow || ldb > kMaxRow || NC > kMaxRow / 2) return CODA_ERR_SHAPE;
-    // token rows addressed with 32-bit offsets (and the DMA runs up to 3 k-tiles past the end)
-    if ((K + 256) * lda * 2 > (int64_t(1) << 31) || (K + 256) * ldb * 2 > (int64_t(1) << 31)) return CODA_ERR_SHAPE;
+    // token rows are addressed with 32-bit offsets from a split's first row: a long token
+    // range with wide rows must be split (and then needs its workspace)
+    const int64_t ld_max = std::max(lda, ldb);
+    if (K > 0 && coda::wgrad_plan(NR, NC, K, ld_max).S == 0) return CODA_ERR_SHAPE;
     const int64_t T = coda::wgrad_partials_rows(NR);
     if (!prod_ok(NR, NC) || !prod_ok(T, NC)) return CODA_ERR_SHAPE;
     if (coda::wgrad_tiles(NR, NC) > kMaxDim) return CODA_ERR_SHAPE;
@@ -493,6 +525,9 @@ coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X
         (K > 0 && (!aligned16(X) || !aligned16(Y))))
         return CODA_ERR_ALIGN;
     if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return CODA_ERR_VALUE;
+    if (K > coda::wgrad_tok_max_split_tokens(ld_max) &&
+        workspace_bytes < coda::wgrad_tok_workspace_bytes(NR, NC, K, lda, ldb))
+        return CODA_ERR_VALUE;                           // the split the addressing needs has no room
     if (workspace && !aligned16(workspace)) return CODA_ERR_ALIGN;
     const Range ro = span(dW, NR * NC * 4), rp = W ? span(partials, T * NC * 4) : span(nullptr, 0);
     const Range rw = workspace ? span(workspace, workspace_bytes) : span(nullptr, 0);

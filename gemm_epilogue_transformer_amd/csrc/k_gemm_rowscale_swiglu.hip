@@ -28,7 +28,7 @@
 
 namespace coda {
 
-enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3, kActSwigluBwd = 4, kActSwigluSave = 5 };
+enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3, kActSwigluBwd = 4, kActSwigluSave = 5, kActCeBwd = 6 };
 
 // RoPE operands (unused by the other activations).
 struct RopeArgs {
@@ -45,6 +45,8 @@ struct CeArgs {
     float* partials;          // [M, T, 2]: (max, sum exp(z - max)) per 256-column tile
     float* tgt_logit;         // [M]: z[m, targets[m]], written by the tile holding it
     int T;                    // tiles per row = ceil(V / 256)
+    const float* lse;         // backward: [M] the forward's log-sum-exp
+    const float* gw;          // backward: [M] d(total loss) / d(loss of row m)
 };
 
 // Cross-entropy epilogue (kucoin page, section "Cinco bloques y un lenguaje LEGO": a
@@ -248,6 +250,81 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN
 #pragma unroll
             for (int w = 0; w < WAVES_N; ++w) c += red[w * BM + r];
             bw.partials[static_cast<size_t>(m) * bw.T + tile_n] = c;
+        }
+    }
+}
+
+// Cross-entropy backward epilogue (kucoin page, section "CODA: El epilogo esconde un
+// tesoro", last paragraph: the reparameterisation covers the loss and holds for the
+// backward pass).  The mainloop has recomputed the LM-head product acc (bf16 weights);
+// with z = r*acc, the forward's log-sum-exp lse, the target t and the row's weight g
+// (the gradient of the total loss with respect to the row's loss):
+//   dL/dz[m, v] = g (exp(z - lse) - [v == t])      (0 for a row whose t lies outside
+//                                                    [0, V): its loss is the constant 0)
+//   dz = bf16( r dL/dz )                  (the input-gradient and weight-gradient GEMMs' operand)
+//   partial c = sum over the wave's 128 columns of dL/dz * acc   (fp32, one per row and wave)
+// Per 32-row slab the accumulators are staged row-major in LDS; each lane takes 8
+// columns of one row (16 lanes per row), its row's values shuffled from the registers
+// that hold them (lane l: rows l, 64 + l of the wave), one 16-byte store of dz, and c
+// through a 16-lane DPP all-reduce.  Partial column 2 * tile_n + wn of T = ceil(V/128).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
+__device__ __forceinline__ void ce_bwd_epilogue(const f32x16_t (&acc)[TM][TN],
+                                                const float (&rv)[BM / WAVES_M / 64],
+                                                const int (&tv)[BM / WAVES_M / 64],
+                                                const float (&lv)[BM / WAVES_M / 64],
+                                                const float (&gv)[BM / WAVES_M / 64], const BwdArgs& bw,
+                                                int M, int V, int m0, int j0, int tile_n, int wm, int wn,
+                                                uint8_t* slab) {
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    using S = Slab<TN>;
+    static_assert(S::kSegPerRow == 16, "16 lanes per row: the all-reduce below");
+    const int lane = threadIdx.x & 63;
+    const int valid_rows = min(BM, M - m0);
+    const uint32_t dz_row = static_cast<uint32_t>(V) * 2;
+    const __amdgpu_buffer_rsrc_t dz_rsrc =
+        make_buffer_rsrc(bw.dz + static_cast<size_t>(m0) * V, static_cast<uint32_t>(valid_rows) * dz_row);
+    const int pcol = 2 * tile_n + wn;                       // this wave's partial column
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        float v[TN][16];
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[b][i] = acc[tm][b][i];
+        S::put(slab, v);
+#pragma unroll
+        for (int j = 0; j < S::kSegPerLane; ++j) {
+            float t[8];
+            S::get(slab, j, t);
+            const int rl = tm * 32 + S::seg_row(j);            // row within the wave
+            const int n = j0 + wn * WN + S::seg_col(j);         // first column of the 8
+            const float rr = __shfl(rv[rl / 64], rl % 64);
+            const float ls = __shfl(lv[rl / 64], rl % 64);
+            const float gg = __shfl(gv[rl / 64], rl % 64);
+            const int tg = __shfl(tv[rl / 64], rl % 64);
+            const float gr = (tg >= 0 && tg < V) ? gg : 0.0f;  // an ignored row: no gradient
+            float c = 0.0f;
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float dzo[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k = 2 * e + hh;
+                    const float p = __expf(rr * t[k] - ls);
+                    const float dl = (n + k < V) ? gr * (p - (n + k == tg ? 1.0f : 0.0f)) : 0.0f;
+                    c += dl * t[k];
+                    dzo[hh] = rr * dl;
+                }
+                o[e] = pack_bf16x2(dzo[0], dzo[1]);
+            }
+            const uint32_t trow = static_cast<uint32_t>(wm * WM + rl);
+            const uint32_t voff = n < V ? trow * dz_row + static_cast<uint32_t>(n) * 2 : kOobOffset;
+            __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])}, dz_rsrc,
+                                                   voff, 0, 0);
+            c = group_allreduce<16>(c, AddOp());
+            const int m = m0 + wm * WM + rl;
+            if ((lane & 15) == 0 && m < M && pcol < bw.T) bw.partials[static_cast<size_t>(m) * bw.T + pcol] = c;
         }
     }
 }
@@ -474,6 +551,7 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     float rv[WM / 64];
     int pv[WM / 64];                                // RoPE: positions of the same rows
     int tv[WM / 64];                                // cross-entropy: their targets (-1 past M)
+    float lv[WM / 64], gv[WM / 64];                 // cross-entropy backward: lse and row weight
 #pragma unroll
     for (int i = 0; i < WM / 64; ++i) {
         const int m = m0 + wm * WM + 64 * i + (threadIdx.x & 63);
@@ -481,7 +559,13 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
         pv[i] = 0;
         tv[i] = -1;
         if constexpr (ACT == kActRope) pv[i] = (m < M && rope.rot_cols > 0) ? rope.pos[m] : 0;
-        if constexpr (ACT == kActCe) tv[i] = m < M ? ce.targets[m] : -1;
+        if constexpr (ACT == kActCe || ACT == kActCeBwd) tv[i] = m < M ? ce.targets[m] : -1;
+        lv[i] = 0.0f;
+        gv[i] = 0.0f;
+        if constexpr (ACT == kActCeBwd) {
+            lv[i] = m < M ? ce.lse[m] : 0.0f;
+            gv[i] = m < M ? ce.gw[m] : 0.0f;
+        }
     }
 
     const int kbytes = K * 2;                       // bytes of an h row
@@ -540,6 +624,9 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     else if constexpr (ACT == kActSwigluBwd)
         swiglu_bwd_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, bw, M, N_out, m0, j0, tile_n, wm, wn, slab,
                                                               ce_red);
+    else if constexpr (ACT == kActCeBwd)
+        ce_bwd_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, tv, lv, gv, bw, M, N_out, m0, j0, tile_n, wm, wn,
+                                                          slab);
     else if constexpr (ACT == kActSwigluSave)
         swiglu_save_epilogue<BM, BN, WAVES_M, TM, TN>(acc, rv, sw, Y, bw.dz, M, N_out, m0, j0, wm, wn, slab);
     else
@@ -648,6 +735,16 @@ hipError_t launch_gemm_rowscale_swiglu_save(int M, int F, int K, const void* h, 
 }
 
 int64_t swiglu_bwd_partials_per_row(int64_t F) { return F < 1 ? -1 : (F + BN3 / 2 - 1) / (BN3 / 2); }
+
+hipError_t launch_gemm_ce_bwd(int M, int V, int K, const void* h, const void* W, const float* r,
+                              const int32_t* targets, const float* lse, const float* gw, void* dz, float* partials,
+                              hipStream_t stream) {
+    const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
+    const CeArgs ce{targets, nullptr, nullptr, 0, lse, gw};
+    // partials per row and 128 columns (a wave's share of a 256-column tile)
+    const BwdArgs bw{nullptr, static_cast<uint16_t*>(dz), partials, static_cast<int>(swiglu_bwd_partials_per_row(V))};
+    return launch3<kActCeBwd, false>(M, V, K, h, W, nullptr, r, nullptr, none, ce, bw, stream);
+}
 
 hipError_t launch_gemm_swiglu_bwd(int M, int F, int K, const void* h, const void* W, const float* r,
                                   const void* dy, void* dz, float* partials, hipStream_t stream) {

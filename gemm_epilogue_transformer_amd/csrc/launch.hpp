@@ -65,6 +65,9 @@ hipError_t launch_gemm_rowscale_gfold(int M, int N_out, int K, bool swiglu, cons
 // SwiGLU forward that keeps the pre-activation, and the backward that starts from it.
 hipError_t launch_gemm_rowscale_swiglu_save(int M, int F, int K, const void* h, const void* W, const float* r,
                                             void* y, void* z, hipStream_t stream);
+hipError_t launch_gemm_ce_bwd(int M, int V, int K, const void* h, const void* W, const float* r,
+                              const int32_t* targets, const float* lse, const float* gw, void* dz, float* partials,
+                              hipStream_t stream);
 hipError_t launch_rope_bwd(int M, int N, const void* dy, const void* y, const float* r, const int32_t* pos,
                            const float* cos, const float* sin, int table_rows, int rot_cols, void* dz,
                            float* partials, hipStream_t stream);
@@ -76,6 +79,13 @@ hipError_t launch_swiglu_bwd_saved(int M, int F, const void* z, const void* dy, 
 int64_t wgrad_tiles(int64_t NR, int64_t NC);
 int64_t wgrad_partials_rows(int64_t NR);
 int64_t wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K);
+struct WgradPlan {
+    int S;          // token splits (0: not feasible)
+    int k_split;    // tokens per split
+};
+WgradPlan wgrad_plan(int64_t NR, int64_t NC, int64_t K, int64_t ld_max);
+int64_t wgrad_tok_max_split_tokens(int64_t ld);
+int64_t wgrad_tok_workspace_bytes(int64_t NR, int64_t NC, int64_t K, int64_t lda, int64_t ldb);
 hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
                              const void* Wraw, float* dW, float* Pg, float* ws, int64_t ws_bytes,
                              hipStream_t stream);

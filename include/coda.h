@@ -330,6 +330,28 @@ coda_status coda_gemm_rowscale_swiglu_save(int64_t M, int64_t F, int64_t K, cons
 coda_status coda_swiglu_bwd_saved(int64_t M, int64_t F, const void* z, const void* dy, const float* r, void* dz,
                                   void* dzt, float* partials, void* stream);
 
+/* -------------------------------------- backward of the cross-entropy epilogue ----
+ * Input side of the backward of the LM-head block  loss_m = CE( RMSNorm(h) . W^T, t_m )
+ * (kucoin page, section "CODA: El epilogo esconde un tesoro", last paragraph: the
+ * reparameterisation covers the cross-entropy loss and holds for the backward pass).  As
+ * the SwiGLU backward, it recomputes the product and turns it into the input-gradient
+ * GEMM's operand in the epilogue; the rest is coda_rmsnorm_bwd_reduce (with F = V),
+ * coda_gemm_rmsnorm_bwd (K = V, Wt = W'^T [d, V]) and coda_gemm_wgrad_tok +
+ * coda_colsum_reduce on dz and h, unchanged.  With acc = h . W'^T and z = r * acc:
+ *   dL/dz[m, v] = g[m] * ( exp(z[m, v] - lse[m]) - [v == targets[m]] ),  and 0 for a row
+ *       whose target lies outside [0, V) (its loss is the constant 0)
+ *   dz [M, V] bf16, written: bf16_rne( r[m] * dL/dz[m, v] )
+ *   partials [M, coda_swiglu_bwd_partials_per_row(V)] fp32, written: per 128 columns,
+ *       sum of dL/dz * acc  (fp32)
+ *   h [M, K] bf16;  W [V, K] bf16 (W', gamma folded);  r [M] fp32 (the forward's row
+ *   scale);  targets [M] int32;  lse [M] fp32 (the forward's log-sum-exp, coda_ce_reduce);
+ *   g [M] fp32 = d(total loss) / d(loss of row m), e.g. 1/n for a mean over n rows
+ * Granules: K % 8 == 0, V % 8 == 0, V <= 2^21.  Outputs must not overlap each other or
+ * the inputs.  bf16 weights only.                                                      */
+coda_status coda_gemm_ce_bwd(int64_t M, int64_t V, int64_t K, const void* h, const void* W, const float* r,
+                             const int32_t* targets, const float* lse, const float* g, void* dz, float* partials,
+                             void* stream);
+
 /* ------------------------------------------ backward of the RoPE epilogue ----
  * Input side of the backward of the QKV block  y = RoPE( RMSNorm(h) . W^T )  (kucoin
  * page, section "CODA: El epilogo esconde un tesoro", last paragraph: the
@@ -405,6 +427,12 @@ coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, c
                             const float* gamma, const void* W, float* dW, float* partials,
                             void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Workspace bytes for coda_gemm_wgrad_tok: as coda_wgrad_workspace_bytes, and more where
+ * the leading dimension makes a split necessary (token rows are addressed with 32-bit
+ * offsets from a split's first row: a split holds at most 2^31 / (2 max(lda, ldb)) - 256
+ * tokens); -1 for invalid sizes or a leading dimension no split can address.          */
+int64_t coda_wgrad_tok_workspace_bytes(int64_t NR, int64_t NC, int64_t K, int64_t lda, int64_t ldb);
+
 /* The same weight-gradient GEMM (cited above) on token-major operands, as the
  * activations are stored (no transposes): the contraction runs down the rows of
  *   X [K, lda] bf16, its first NR columns (e.g. r * dL/dz [M, 2F]: lda = NR = 2F)
@@ -413,8 +441,10 @@ coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, c
  *   token split exactly as coda_gemm_wgrad (workspace sized by coda_wgrad_workspace_bytes).
  * The tiles are read through LDS transpose reads; the result is bit-identical to
  * coda_gemm_wgrad on the transposed operands with the same split.  Any K (K = 0 writes
- * zeros).  Granules: NC % 8 == 0, lda % 8 == 0, ldb % 8 == 0, lda >= NR, ldb >= NC;
- * (K + 256) * lda * 2 and (K + 256) * ldb * 2 at most 2^31.                           */
+ * zeros).  Granules: NC % 8 == 0, lda % 8 == 0, ldb % 8 == 0, lda >= NR, ldb >= NC.
+ * Where (K + 256) * max(lda, ldb) * 2 exceeds 2^31 the tokens must be split: the call
+ * then needs coda_wgrad_tok_workspace_bytes bytes of workspace (CODA_ERR_VALUE with
+ * less; CODA_ERR_SHAPE where no split of at most 64 ranges can address the rows).     */
 coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda, const void* Y,
                                 int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
                                 void* workspace, int64_t workspace_bytes, void* stream);

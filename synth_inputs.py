@@ -37,6 +37,7 @@ ACT_CE = 3        # cross-entropy of the LM-head product against per-row targets
 ACT_SWIGLU_BWD = 4  # backward of the RMSNorm -> GEMM -> SwiGLU block (no first GEMM)
 ACT_CHAIN_BWD = 5   # backward of the whole chain (first GEMM + residual included)
 ACT_ROPE_BWD = 6    # backward of the RMSNorm -> QKV GEMM -> RoPE block (no first GEMM)
+ACT_CE_BWD = 7      # backward of the RMSNorm -> LM head -> cross-entropy block (no first GEMM)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -71,6 +72,9 @@ class Workload:
         if self.act == ACT_CHAIN_BWD:
             # plus the first GEMM's input-gradient and weight-gradient products
             return 3 * (2 * self.M * self.d * self.N2w) + 2 * (2 * self.M * self.K1 * self.d)
+        if self.act == ACT_CE_BWD:
+            # the recomputed logits product, the input-gradient and weight-gradient products
+            return 3 * (2 * self.M * self.d * self.N2w)
         if self.act == ACT_ROPE_BWD:
             # the input-gradient and weight-gradient products (the rotation needs no
             # recomputed forward product)
@@ -91,7 +95,10 @@ class Workload:
 # upstream gradient dy drawn directly (no first GEMM); 9: the backward of workload 2's
 # whole chain (same forward draws as workload 2, then dy and the residual-stream
 # gradient dres); 10: the backward of workload 6's second half -- the RMSNorm -> QKV
-# GEMM -> RoPE block -- with h, W and dy drawn directly, positions as in workload 6.
+# GEMM -> RoPE block -- with h, W and dy drawn directly, positions as in workload 6;
+# 11: the backward of workload 7's second half -- the RMSNorm -> LM head ->
+# cross-entropy block -- with h, W and the targets drawn directly and the mean loss
+# (row weights 1/M).
 WORKLOADS = {
     1: Workload("tiny_m128_d256_n512_none", 128, 256, 256, 512, ACT_NONE, "bf16", 1e-5, 1001),
     2: Workload("llama1b_attnout_mlpin_m16384", 16384, 2048, 2048, 16384, ACT_SWIGLU, "bf16", 1e-5, 1002),
@@ -105,6 +112,7 @@ WORKLOADS = {
     9: Workload("llama1b_attnout_mlpin_bwd_m16384", 16384, 2048, 2048, 16384, ACT_CHAIN_BWD, "bf16", 1e-5, 1002),
     10: Workload("llama1b_qkv_rope_bwd_m16384", 16384, 0, 2048, 3072, ACT_ROPE_BWD, "bf16", 1e-5, 1010,
                  rot_cols=2560, seq_len=4096),
+    11: Workload("llama1b_lmhead_ce_bwd_m16384", 16384, 0, 2048, 128256, ACT_CE_BWD, "bf16", 1e-5, 1011),
 }
 
 
@@ -154,7 +162,7 @@ def generate(w: Workload, rows: int | None = None) -> dict:
     """
     rng = np.random.default_rng(w.seed)
     f32 = np.float32
-    if w.act in (ACT_SWIGLU_BWD, ACT_ROPE_BWD):
+    if w.act in (ACT_SWIGLU_BWD, ACT_ROPE_BWD, ACT_CE_BWD):
         return _generate_bwd(w, rng, rows)
     A = rng.standard_normal((w.M, w.K1), dtype=f32)
     Wo = rng.standard_normal((w.d, w.K1), dtype=f32) * f32(1.0 / np.sqrt(w.K1))
@@ -194,7 +202,9 @@ def _generate_bwd(w: Workload, rng, rows):
       gamma  float32 [d]        1 + 0.1 N(0, 1)
       W_t    uint16 [N2w, d]    bf16 bits, N(0, 1/d) (SwiGLU: gate rows, then up rows)
       dy     uint16 [M, n]      bf16 bits, N(0, 1): the upstream gradient of y (n = F for
-                                SwiGLU, N2w for RoPE)
+                                SwiGLU, N2w for RoPE); cross-entropy: not drawn, instead
+      targets int32 [M]         uniform in [0, N2w), and
+      g      float32 [M]        1/M: the row weights of the mean loss
       pos    int32 [M]          RoPE only: token m's position, m mod seq_len
     """
     f32 = np.float32
@@ -202,6 +212,12 @@ def _generate_bwd(w: Workload, rng, rows):
     h = rng.standard_normal((w.M, w.d), dtype=f32)
     gamma = (f32(1.0) + f32(0.1) * rng.standard_normal(w.d, dtype=f32)).astype(f32)
     W = rng.standard_normal((w.N2w, w.d), dtype=f32) * f32(1.0 / np.sqrt(w.d))
+    if w.act == ACT_CE_BWD:
+        tgt = rng.integers(0, w.N2w, size=w.M, dtype=np.int32)
+        if rows is not None:
+            h, tgt = h[:rows], tgt[:rows]
+        return {"h": to_bf16_bits(h), "gamma": gamma, "W_t": to_bf16_bits(W), "targets": tgt,
+                "g": np.full(h.shape[0], 1.0 / w.M, dtype=f32)}
     dy = rng.standard_normal((w.M, n), dtype=f32)
     if rows is not None:
         h, dy = h[:rows], dy[:rows]

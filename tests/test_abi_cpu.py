@@ -316,7 +316,13 @@ def test_token_major_weight_gradient_validation():
     assert w(64, 60, 64, P1, 64, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # NC % 8
     assert w(64, 64, 64, P1, 60, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # lda % 8
     assert w(72, 64, 64, P1, 64, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # lda < NR
-    assert w(64, 64, 1 << 22, P1, 512, P2, 64, None, None, P5, None, None, 0, None) == SHAPE  # 32-bit rows
+    # 32-bit row offsets: a long range of wide rows must be split, which needs a workspace
+    assert w(64, 64, 1 << 22, P1, 512, P2, 64, None, None, P5, None, None, 0, None) == VALUE
+    assert w(64, 64, 1 << 22, P1, 1 << 21, P2, 64, None, None, P5, None, None, 0, None) == SHAPE  # > 64 splits
+    # the LM head's dz [16384, 128256]: 3 splits of at most 8064 tokens
+    assert L.coda_wgrad_tok_workspace_bytes(128256, 2048, 16384, 128256, 2048) == 3 * (128256 + 501) * 2048 * 4
+    assert L.coda_wgrad_tok_workspace_bytes(16384, 2048, 16384, 16384, 2048) == 0     # fits, 512 tiles
+    assert L.coda_wgrad_tok_workspace_bytes(64, 64, 64, 32, 64) == -1                   # lda < NR
     assert w(64, 64, 13, None, 64, P2, 64, None, None, P5, None, None, 0, None) == NULL
     assert w(64, 64, 13, P1, 64, P2, 64, None, None, P1 + 64, None, None, 0, None) == ALIAS  # dW over X
     assert w(64, 64, 13, P1, 64, P2 + 8, 64, None, None, P5, None, None, 0, None) == ALIGN
@@ -342,3 +348,22 @@ def test_rope_backward_validation():
     assert f(16, 128, P1, P2, P3, P4, P5, P6, 8, 64, P2, PT, None) == ALIAS      # dz over y
     assert f(16, 128, P1, P2, P3, P4, P5, P6, 8, 64, DZ, P6 + 64, None) == ALIAS  # partials over sin
     assert f(0, 128, None, None, None, None, None, None, 0, 0, None, None, None) == OK     # empty batch
+
+
+@no_gpu
+def test_cross_entropy_backward_validation():
+    L = _lib.load()
+    f = L.coda_gemm_ce_bwd
+    DZ, PT = P6 + 0x1000000, P6 + 0x2000000
+    # M, V, K, h, W, r, targets, lse, g, dz, partials, stream
+    assert f(16, 100, 64, P1, P2, P3, P4, P5, P6, DZ, PT, None) == SHAPE        # V % 8
+    assert f(16, 128, 60, P1, P2, P3, P4, P5, P6, DZ, PT, None) == SHAPE        # K % 8
+    assert f(16, 1 << 22, 64, P1, P2, P3, P4, P5, P6, DZ, PT, None) == SHAPE    # V past 2^21
+    assert f(16, 128, 64, P1, P2, P3, None, P5, P6, DZ, PT, None) == NULL       # targets
+    assert f(16, 128, 64, P1, P2, P3, P4, None, P6, DZ, PT, None) == NULL       # lse
+    assert f(16, 128, 64, P1, P2, P3, P4, P5, None, DZ, PT, None) == NULL       # g
+    assert f(16, 128, 64, P1 + 8, P2, P3, P4, P5, P6, DZ, PT, None) == ALIGN
+    assert f(16, 128, 64, P1, P2, P3, P4, P5, P6, DZ, DZ + 64, None) == ALIAS   # partials over dz
+    assert f(16, 128, 64, P1, P2, P3, P4, P5, P6, P2, PT, None) == ALIAS        # dz over W
+    assert f(16, 128, 64, P1, P2, P3, P4, P5, P6, DZ, P5, None) == ALIAS        # partials over lse
+    assert f(0, 128, 64, None, None, None, None, None, None, None, None, None) == OK
