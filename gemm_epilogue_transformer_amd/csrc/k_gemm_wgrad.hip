@@ -206,14 +206,25 @@ k_splitk_reduce(const f32x4_t* __restrict__ ws, const float* __restrict__ gamma,
     }
 }
 
-// dgamma[k] = fl32( sum_t Pg[t, k] )  (fixed order, fp64), one thread per column
+// dgamma[k] = fl32( sum_t Pg[t, k] )  (fp64, fixed order): a block takes 32 columns; its
+// 8 row groups g add rows t = g, g + 8, ... (coalesced 128-byte column runs), then group
+// 0 adds the 8 group sums in order
 __global__ void __launch_bounds__(256)
 k_colsum_reduce(const float* __restrict__ Pg, float* __restrict__ out, int T, int NC) {
-    const int k = blockIdx.x * 256 + threadIdx.x;
-    if (k >= NC) return;
+    __shared__ double part[8][32];
+    const int c = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const int k = blockIdx.x * 32 + c;
     double s = 0.0;
-    for (int t = 0; t < T; ++t) s += static_cast<double>(Pg[static_cast<size_t>(t) * NC + k]);
-    out[k] = static_cast<float>(s);
+    if (k < NC)
+        for (int t = g; t < T; t += 8) s += static_cast<double>(Pg[static_cast<size_t>(t) * NC + k]);
+    part[g][c] = s;
+    __syncthreads();
+    if (g == 0 && k < NC) {
+        double a = part[0][c];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) a += part[i][c];
+        out[k] = static_cast<float>(a);
+    }
 }
 
 // dst[0, n) = 0 (the gradient of an empty token batch); a kernel rather than a memset so
@@ -354,7 +365,7 @@ hipError_t launch_gemm_wgrad_tok(int NR, int NC, int K, const void* X, int lda, 
 }
 
 hipError_t launch_colsum_reduce(int T, int NC, const float* Pg, float* out, hipStream_t stream) {
-    hipLaunchKernelGGL(k_colsum_reduce, dim3((NC + 255) / 256), dim3(256), 0, stream, Pg, out, T, NC);
+    hipLaunchKernelGGL(k_colsum_reduce, dim3((NC + 31) / 32), dim3(256), 0, stream, Pg, out, T, NC);
     return hipGetLastError();
 }
 

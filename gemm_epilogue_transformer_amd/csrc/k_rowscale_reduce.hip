@@ -69,18 +69,26 @@ hipError_t launch_rowscale_from_h(int M, int N, const void* h, float eps, float*
 __global__ void __launch_bounds__(256)
 k_rmsnorm_bwd_reduce(const float* __restrict__ P, const float* __restrict__ r, float* __restrict__ q, int M,
                      int T, double n) {
-    const int m = blockIdx.x * blockDim.x + threadIdx.x;
-    if (m >= M) return;
+    // one wave per row: lane l adds t = l, l + 64, ... in fp64 (coalesced 256-byte rows of
+    // partials), then an xor butterfly over the 64 lanes in a fixed pattern (addition
+    // commutes, so every lane ends with the same bits)
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (m >= M) return;                                  // whole waves
     const float* p = P + static_cast<size_t>(m) * T;
     double s = 0.0;
-    for (int t = 0; t < T; ++t) s += static_cast<double>(p[t]);
-    const double rr = static_cast<double>(r[m]);
-    q[m] = static_cast<float>(-(rr * rr * rr / n) * s);
+    for (int t = lane; t < T; t += 64) s += static_cast<double>(p[t]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) {
+        const double rr = static_cast<double>(r[m]);
+        q[m] = static_cast<float>(-(rr * rr * rr / n) * s);
+    }
 }
 
 hipError_t launch_rmsnorm_bwd_reduce(int M, int N, int T, const float* P, const float* r, float* q,
                                      hipStream_t stream) {
-    const dim3 block(256), grid((M + 255) / 256);
+    const dim3 block(256), grid((M + 3) / 4);
     hipLaunchKernelGGL(k_rmsnorm_bwd_reduce, grid, block, 0, stream, P, r, q, M, T, static_cast<double>(N));
     return hipGetLastError();
 }
