@@ -466,9 +466,10 @@ coda_status coda_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const
 int64_t coda_wgrad_partials_rows(int64_t NR) { return NR < 1 || NR > kMaxDim ? -1 : coda::wgrad_partials_rows(NR); }
 
 int64_t coda_wgrad_tok_workspace_bytes(int64_t NR, int64_t NC, int64_t K, int64_t lda, int64_t ldb) {
-    if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0) || lda < NR || ldb < NC || lda > kMaxRow || ldb > kMaxRow)
+    if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0) || lda < NR || ldb < NC || lda > kMaxRow || ldb > kMaxRow ||
+        !prod_ok(NR, NC))
         return -1;
-    return coda::wgrad_tok_workspace_bytes(NR, NC, K, lda, ldb);
+    return coda::wgrad_workspace_bytes(NR, NC, K);
 }
 
 int64_t coda_wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K) {
@@ -513,10 +514,6 @@ coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X
     if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0)) return CODA_ERR_SHAPE;
     if (NC % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || lda < NR || ldb < NC) return CODA_ERR_SHAPE;
     if (lda > kMaxRow || ldb > kMaxRow || NC > kMaxRow / 2) return CODA_ERR_SHAPE;
-    // token rows are addressed with 32-bit offsets from a split's first row: a long token
-    // range with wide rows must be split (and then needs its workspace)
-    const int64_t ld_max = std::max(lda, ldb);
-    if (K > 0 && coda::wgrad_plan(NR, NC, K, ld_max).S == 0) return CODA_ERR_SHAPE;
     const int64_t T = coda::wgrad_partials_rows(NR);
     if (!prod_ok(NR, NC) || !prod_ok(T, NC)) return CODA_ERR_SHAPE;
     if (coda::wgrad_tiles(NR, NC) > kMaxDim) return CODA_ERR_SHAPE;
@@ -525,9 +522,6 @@ coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X
         (K > 0 && (!aligned16(X) || !aligned16(Y))))
         return CODA_ERR_ALIGN;
     if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return CODA_ERR_VALUE;
-    if (K > coda::wgrad_tok_max_split_tokens(ld_max) &&
-        workspace_bytes < coda::wgrad_tok_workspace_bytes(NR, NC, K, lda, ldb))
-        return CODA_ERR_VALUE;                           // the split the addressing needs has no room
     if (workspace && !aligned16(workspace)) return CODA_ERR_ALIGN;
     const Range ro = span(dW, NR * NC * 4), rp = W ? span(partials, T * NC * 4) : span(nullptr, 0);
     const Range rw = workspace ? span(workspace, workspace_bytes) : span(nullptr, 0);

@@ -147,11 +147,14 @@ struct DmaPanel {
 // Fragments of one MFMA k-step for a wave's TM x TN 32x32 blocks.  bf16: a k-step is
 // k16 (RB/32 per k-tile), one 16-byte ds_read per fragment.  e4m3: a k-step is k64
 // (RB/64 per k-tile), two 16-byte ds_reads per fragment.
-template <Elt E, int TM, int TN, int RB>
+// TC: the MFMA takes the B fragment as its first operand, so each 32x32 accumulator
+// block holds the transposed product (lane = A row, registers = B rows); the operand
+// layouts are the same, only the roles swap.
+template <Elt E, int TM, int TN, int RB, bool TC = false>
 struct Frags;
 
-template <int TM, int TN, int RB>
-struct Frags<Elt::BF16, TM, TN, RB> {
+template <int TM, int TN, int RB, bool TC>
+struct Frags<Elt::BF16, TM, TN, RB, TC> {
     static constexpr int kSteps = RB / 32;
     static constexpr int kReads = TM + TN;         // ds_read_b128 per k-step
     bf16x8_t a[TM], b[TN];
@@ -178,7 +181,10 @@ struct Frags<Elt::BF16, TM, TN, RB> {
     // MFMA i of the k-step: block (i / TN, i % TN)
     __device__ __forceinline__ void mma_one(int i, f32x16_t (&acc)[TM][TN]) const {
         const int tm = i / TN, tn = i % TN;
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+        if constexpr (TC)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[tn], a[tm], acc[tm][tn], 0, 0, 0);
+        else
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
     }
     __device__ __forceinline__ void mma(f32x16_t (&acc)[TM][TN]) const {
 #pragma unroll
@@ -187,7 +193,7 @@ struct Frags<Elt::BF16, TM, TN, RB> {
 };
 
 template <int TM, int TN, int RB>
-struct Frags<Elt::E4M3, TM, TN, RB> {
+struct Frags<Elt::E4M3, TM, TN, RB, false> {
     static constexpr int kSteps = RB / 64;
     static constexpr int kReads = TM + TN;         // fragments (two ds_read_b128 each)
     i32x8_t a[TM], b[TN];
@@ -235,6 +241,14 @@ struct Frags<Elt::E4M3, TM, TN, RB> {
 // token row L / 4, and lane i receives column i of those 4 token rows, i.e. 4 consecutive
 // k of one MFMA row; two reads give the 8 k a 32x32x16 fragment lane holds.  With the
 // swizzle the 4 token rows of a read land in 4 different 16-bank groups.
+// A k-tile's address of one lane's chunk in a token-major panel: a descriptor of that
+// k-tile's 64 token rows alone (rebased on every k-tile, so operands larger than 4 GB
+// need no 64-bit offsets) and the lane's offset inside it.
+struct TokAddr {
+    u32x4_t rsrc;
+    uint32_t voff;
+};
+
 template <int NW>
 struct DmaPanelTok {
     static constexpr int kTok = 64;                   // tokens per k-tile
@@ -242,42 +256,49 @@ struct DmaPanelTok {
     static constexpr int kRowsPerInst = 2 * NW;       // token rows per instruction index
     static constexpr int kInst = kTok / kRowsPerInst; // DMA instructions per wave per k-tile
     static_assert(NW % 2 == 0, "a lane's token row phase (mod 4) must not depend on the instruction");
-    u32x4_t rsrc;
-    uint32_t off0;      // byte offset of this lane's chunk in instruction 0 of k-tile 0
-    uint32_t stride;    // bytes between instruction j and j + 1
-    uint32_t tile;      // bytes between k-tiles (64 token rows)
-    bool col_in;        // this lane's chunk lies inside the matrix's columns
+    const uint8_t* base;  // the panel's first column in token row 0 of the range
+    int tokens;           // token rows in the range
+    uint32_t ld;          // bytes between token rows
+    uint32_t off0;        // byte offset of this lane's chunk in instruction 0 of a k-tile
+    uint32_t stride;      // bytes between instruction j and j + 1
+    bool col_in;          // this lane's chunk lies inside the matrix's columns
 
     // base: the panel's first column in token row 0 (of the range); tokens: token rows in
-    // range from base (rows past them read zeros); ld: bytes between token rows; cols:
-    // columns of the panel inside the matrix (chunks past them read zeros).
-    __device__ __forceinline__ void init(const uint8_t* base, int tokens, int ld, int cols) {
+    // range from base (rows past them read zeros); ld: bytes between token rows (64 rows
+    // of it must stay below 2^31); cols: columns of the panel inside the matrix (chunks
+    // past them read zeros).
+    __device__ __forceinline__ void init(const uint8_t* base_, int tokens_, int ld_, int cols) {
         const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int r = 2 * wave + (lane >> 5);          // token row in instruction 0
         const int p = lane & 31;                       // chunk position in the LDS row
         const int c = p ^ ((r & 3) << 2);              // chunk of the matrix row it holds
         col_in = c * 8 < cols;
-        rsrc = make_rsrc(base, static_cast<uint32_t>(max(tokens, 0)) * static_cast<uint32_t>(ld));
+        base = base_;
+        tokens = __builtin_amdgcn_readfirstlane(max(tokens_, 0));
+        ld = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ld_));
         off0 = static_cast<uint32_t>(r) * ld + static_cast<uint32_t>(c) * 16;
-        stride = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kRowsPerInst) * static_cast<uint32_t>(ld));
-        tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kTok) * static_cast<uint32_t>(ld));
+        stride = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kRowsPerInst) * ld);
     }
-    // k-tile kt's offset of this lane's chunk (kOob for a chunk past the columns; rows past
-    // the token range fall outside the descriptor and read zeros)
-    __device__ __forceinline__ uint32_t base_offset(int kt, int /*kbytes*/) const {
-        uint32_t base = col_in ? off0 + static_cast<uint32_t>(kt) * tile : kOob;
-        asm volatile("" : "+v"(base));
-        return base;
+    // k-tile kt: a descriptor of its token rows inside the range (none past the range:
+    // reads of zeros) and this lane's chunk offset (kOob for a chunk past the columns)
+    __device__ __forceinline__ TokAddr base_offset(int kt, int /*kbytes*/) const {
+        const int rows = min(max(tokens - kt * kTok, 0), kTok);
+        TokAddr a;
+        a.rsrc = make_rsrc(base + static_cast<uint64_t>(kt) * kTok * ld, static_cast<uint32_t>(rows) * ld);
+        uint32_t v = col_in ? off0 : kOob;
+        asm volatile("" : "+v"(v));
+        a.voff = v;
+        return a;
     }
-    __device__ __forceinline__ void issue_one(int j, uint8_t* stage, uint32_t base) const {
+    __device__ __forceinline__ void issue_one(int j, uint8_t* stage, const TokAddr& a) const {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        dma16(rsrc, base + static_cast<uint32_t>(j) * stride, lds_addr(stage + (2 * (NW * j + wave)) * kRowBytes));
+        dma16(a.rsrc, a.voff + static_cast<uint32_t>(j) * stride, lds_addr(stage + (2 * (NW * j + wave)) * kRowBytes));
     }
     __device__ __forceinline__ void issue(uint8_t* stage, int kt, int kbytes) const {
-        const uint32_t base = base_offset(kt, kbytes);
+        const TokAddr a = base_offset(kt, kbytes);
 #pragma unroll
-        for (int j = 0; j < kInst; ++j) issue_one(j, stage, base);
+        for (int j = 0; j < kInst; ++j) issue_one(j, stage, a);
     }
 };
 
@@ -476,7 +497,7 @@ __device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const P
     constexpr int kOffB = BM * RBA;          // B panel offset inside a stage
     FP f;
     // DMA instruction q (0 .. kPerTile-1) of the tile with base offsets (ba, bb)
-    auto issue_q = [&](int q, uint8_t* stage, uint32_t ba, uint32_t bb) {
+    auto issue_q = [&](int q, uint8_t* stage, const auto& ba, const auto& bb) {
         if (q < nA) pa.issue_one(q, stage, ba);
         else pb.issue_one(q - nA, stage + kOffB, bb);
     };
@@ -486,8 +507,8 @@ __device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const P
         pb.issue(st[i] + kOffB, i, kbytes_b);
     });
     // tile NS-1: its first share now, the rest as pending DMA during tile 0
-    uint32_t pend_a = pa.base_offset(NS - 1, kbytes);
-    uint32_t pend_b = pb.base_offset(NS - 1, kbytes_b);
+    auto pend_a = pa.base_offset(NS - 1, kbytes);     // a 32-bit offset, or a TokAddr
+    auto pend_b = pb.base_offset(NS - 1, kbytes_b);
     static_for<kPer>([&](auto Q) { issue_q(decltype(Q)::value, st[NS - 1], pend_a, pend_b); });
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile + kPer));   // tile 0 landed
     __syncthreads();
@@ -538,13 +559,13 @@ __device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const P
 }
 
 // Both operands of one element type E with RB-byte k-tile rows.
-template <Elt E, int BM, int BN, int SPLIT, int NS, int NW, int RB, int SPREAD, int TM, int TN, class ARow,
-          class BRow>
+template <Elt E, int BM, int BN, int SPLIT, int NS, int NW, int RB, int SPREAD, bool TC = false, int TM, int TN,
+          class ARow, class BRow>
 __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
                                              const DmaPanel<BN, SPLIT, NW, RB>& pb, int kbytes,
                                              uint8_t* const (&st)[NS], const ARow& a_row,
                                              const BRow& b_row) {
-    mainloop_dma_fp<FragPair<Frags<E, TM, TN, RB>>, BM, BN, SPLIT, NS, NW, RB, RB, SPREAD>(
+    mainloop_dma_fp<FragPair<Frags<E, TM, TN, RB, TC>>, BM, BN, SPLIT, NS, NW, RB, RB, SPREAD>(
         acc, pa, pb, kbytes, kbytes, st, a_row, b_row);
 }
 

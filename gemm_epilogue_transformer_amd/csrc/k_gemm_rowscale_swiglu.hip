@@ -26,6 +26,10 @@
 #include "gemm_pipeline.hpp"
 #include "launch.hpp"
 
+#ifndef CODA_G3_TC
+#define CODA_G3_TC 1      // 0: the forward SwiGLU epilogue stages through LDS like the others
+#endif
+
 namespace coda {
 
 enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3, kActSwigluBwd = 4, kActSwigluSave = 5, kActCeBwd = 6 };
@@ -510,6 +514,67 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
     }
 }
 
+// SwiGLU epilogue on transposed accumulator blocks (the mainloop's MFMA took the W
+// fragment first): in block (tm, b) lane l holds row 32*tm + l%32 of the wave and, in
+// register i, column 8*(i/4) + 4*(l/32) + i%4 of the block.  So r is one value per lane
+// and block row, and every group of 4 registers is 4 consecutive output columns of one
+// row; one cross-half lane swap per pair of groups makes them 8, stored with one 16-byte
+// store, with no LDS staging.  Same fp32 operations per element, in the same order, as
+// rowscale_epilogue.
+template <int BM, int BN, int WAVES_M, int TM, int TN>
+__device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN],
+                                                   const float (&rv)[BM / WAVES_M / 64], float sw,
+                                                   uint16_t* __restrict__ Y, int M, int N_out, int m0, int j0,
+                                                   int wm, int wn) {
+    constexpr int WM = BM / WAVES_M;
+    constexpr int NB = TN / 2;
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int valid_rows = min(BM, M - m0);
+    const uint32_t row_bytes = static_cast<uint32_t>(N_out) * 2;
+    const __amdgpu_buffer_rsrc_t y_rsrc =
+        make_buffer_rsrc(Y + static_cast<size_t>(m0) * N_out, static_cast<uint32_t>(valid_rows) * row_bytes);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const float rr = __shfl(rv[tm / 2], (tm % 2) * 32 + lr) * sw;
+        const uint32_t row_off = static_cast<uint32_t>(wm * WM + tm * 32 + lr) * row_bytes;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint32_t pk[4][2];    // group g: columns 8g + 4lh .. +3 as two bf16 pairs
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gv = acc[tm][b][4 * g + e] * rr;
+                    const float uv = acc[tm][b + NB][4 * g + e] * rr;
+                    v[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+                }
+                pk[g][0] = pack_bf16x2(v[0], v[1]);
+                pk[g][1] = pack_bf16x2(v[2], v[3]);
+            }
+            // groups 2q and 2q+1: the upper half-wave's group 2q and the lower's group 2q+1
+            // trade places (v_permlane32_swap), so lane l < 32 holds columns 16q .. 16q+7
+            // and lane l + 32 columns 16q+8 .. 16q+15 of its row: 16-byte stores
+            const int nb = j0 + wn * NB * 32 + b * 32;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                uint32_t w[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const auto sw2 = __builtin_amdgcn_permlane32_swap(pk[2 * q][h], pk[2 * q + 1][h], false, false);
+                    w[h] = sw2[0];
+                    w[2 + h] = sw2[1];
+                }
+                const int n = nb + 16 * q + 8 * lh;
+                const uint32_t voff = n < N_out ? row_off + static_cast<uint32_t>(n) * 2 : kOobOffset;
+                __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(w[0]), int(w[1]), int(w[2]), int(w[3])}, y_rsrc,
+                                                       voff, 0, 0);
+            }
+        }
+    }
+}
+
 // Direct-to-LDS mainloop (PIPE 1: the register-staged one, bf16 weights only; PIPE 2: the
 // register-staged one with the RMSNorm weight gfold folded into a raw W on its way to
 // LDS, bit-identical to a pre-folded W').  W8: the
@@ -528,6 +593,9 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     constexpr int TM = WM / 32, TN = WN / 32;
     static_assert(!SWIGLU || (TN % 2 == 0), "SwiGLU pairs gate and up blocks");
     constexpr int BNO = SWIGLU ? BN / 2 : BN;       // output columns of one block tile
+    // transposed accumulator blocks (16-byte stores straight from registers) for the
+    // forward SwiGLU on the bf16 DMA mainloop
+    constexpr bool TC = CODA_G3_TC && ACT == kActSwiglu && !W8 && PIPE == 0;
 
     constexpr int RBB = W8 ? RB / 2 : RB;            // bytes of a W row per k-tile
     constexpr int kStage = BM * RB + BN * RBB;
@@ -613,7 +681,8 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
         mainloop_reg<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row,
                                                                          GammaFold<RB>(gfold, K));
     } else {
-        mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
+        mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NS, NW, RB, SPREAD, TC>(acc, pa, pb, kbytes, st, a_row,
+                                                                                     b_row);
     }
 
     const float sw = w_scale ? *w_scale : 1.0f;
@@ -627,6 +696,8 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     else if constexpr (ACT == kActCeBwd)
         ce_bwd_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, tv, lv, gv, bw, M, N_out, m0, j0, tile_n, wm, wn,
                                                           slab);
+    else if constexpr (TC)
+        swiglu_epilogue_tc<BM, BN, WAVES_M, TM, TN>(acc, rv, sw, Y, M, N_out, m0, j0, wm, wn);
     else if constexpr (ACT == kActSwigluSave)
         swiglu_save_epilogue<BM, BN, WAVES_M, TM, TN>(acc, rv, sw, Y, bw.dz, M, N_out, m0, j0, wm, wn, slab);
     else

@@ -256,7 +256,7 @@ int64_t wgrad_partials_rows(int64_t NR) { return NR < 1 ? -1 : (NR + BMW - 1) / 
 // tokens at ~30 ns per token and tile) plus the fp32 slices the split writes and its
 // reduce reads back (2 S NR NC 4 bytes at ~5 TB/s).  A partly filled last round costs
 // as much as a full one, so S is chosen against it, not just to reach 256 blocks.
-constexpr int kMinSplitTokens = 2048, kMaxSplits = 16, kMaxTokSplits = 64;
+constexpr int kMinSplitTokens = 2048, kMaxSplits = 16;
 int wgrad_splits(int64_t NR, int64_t NC, int64_t K) {
     const int64_t tiles = wgrad_tiles(NR, NC);
     const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, K / kMinSplitTokens));
@@ -280,36 +280,15 @@ int64_t wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K) {
     return S > 1 ? static_cast<int64_t>(S) * (NR + (NR + BMW - 1) / BMW) * NC * 4 : 0;
 }
 
-// Token-major operands are addressed with 32-bit offsets from the first token row of a
-// block's split, and the DMA runs up to 3 k-tiles (192 tokens) past the split's end: a
-// split may hold at most ((2^31 / (2 ld)) - 256) tokens, rounded down to the 64-token
-// k-step (0: ld too large for any split).
-int64_t wgrad_tok_max_split_tokens(int64_t ld) {
-    const int64_t k = (int64_t(1) << 31) / (2 * ld) - 256;
-    return k < 64 ? 0 : k / 64 * 64;
-}
-
-// Splits and tokens per split: the time model's choice (wgrad_splits), then, for
-// token-major operands with leading dimension ld_max (0: token-contiguous operands), at
-// most wgrad_tok_max_split_tokens(ld_max) tokens per split.  S == 0: not feasible.
-WgradPlan wgrad_plan(int64_t NR, int64_t NC, int64_t K, int64_t ld_max) {
+// Splits and tokens per split: the time model's choice (wgrad_splits).  Token-major
+// operands are addressed per 64-token k-tile (the descriptor is rebased on every
+// k-tile), so their leading dimension puts no limit on a split's token count.
+WgradPlan wgrad_plan(int64_t NR, int64_t NC, int64_t K) {
     if (K <= 0) return {1, 0};
     int64_t S = wgrad_splits(NR, NC, K);
-    int64_t k_split = S > 1 ? ((K + S - 1) / S + 63) / 64 * 64 : K;
-    if (ld_max > 0) {
-        const int64_t kmax = wgrad_tok_max_split_tokens(ld_max);
-        if (kmax == 0) return {0, 0};
-        k_split = std::min(k_split, kmax);
-    }
+    const int64_t k_split = S > 1 ? ((K + S - 1) / S + 63) / 64 * 64 : K;
     S = (K + k_split - 1) / k_split;
-    if (S > kMaxTokSplits) return {0, 0};
     return {static_cast<int>(S), static_cast<int>(k_split)};
-}
-
-int64_t wgrad_tok_workspace_bytes(int64_t NR, int64_t NC, int64_t K, int64_t lda, int64_t ldb) {
-    const WgradPlan p = wgrad_plan(NR, NC, K, std::max(lda, ldb));
-    if (p.S == 0) return -1;
-    return p.S > 1 ? static_cast<int64_t>(p.S) * (NR + (NR + BMW - 1) / BMW) * NC * 4 : 0;
 }
 
 template <bool TOK>
@@ -317,13 +296,11 @@ static hipError_t launch_wgrad(int NR, int NC, int K, const void* At, int lda, c
                                const float* gamma, const void* Wraw, float* dW, float* Pg, float* ws,
                                int64_t ws_bytes, hipStream_t stream) {
     const int tiles_m = (NR + BMW - 1) / BMW, tiles_n = (NC + BNW - 1) / BNW;
-    const WgradPlan plan = wgrad_plan(NR, NC, K, TOK ? std::max(lda, ldb) : 0);
+    const WgradPlan plan = wgrad_plan(NR, NC, K);
     int S = plan.S, k_split = plan.k_split;                  // tokens per split: a multiple of 64
     auto need = [&](int s) { return static_cast<int64_t>(s) * (NR + (Wraw ? tiles_m : 0)) * NC * 4; };
-    if (S == 0) return hipErrorInvalidValue;
     if (S > 1 && (ws == nullptr || ws_bytes < need(S))) {
-        // without room for the split: one block per tile, if the addressing allows it
-        if (TOK && K > wgrad_tok_max_split_tokens(std::max(lda, ldb))) return hipErrorInvalidValue;
+        // without room for the split: one block per tile
         S = 1;
         k_split = K;
     }

@@ -80,12 +80,10 @@ int64_t wgrad_tiles(int64_t NR, int64_t NC);
 int64_t wgrad_partials_rows(int64_t NR);
 int64_t wgrad_workspace_bytes(int64_t NR, int64_t NC, int64_t K);
 struct WgradPlan {
-    int S;          // token splits (0: not feasible)
+    int S;          // token splits
     int k_split;    // tokens per split
 };
-WgradPlan wgrad_plan(int64_t NR, int64_t NC, int64_t K, int64_t ld_max);
-int64_t wgrad_tok_max_split_tokens(int64_t ld);
-int64_t wgrad_tok_workspace_bytes(int64_t NR, int64_t NC, int64_t K, int64_t lda, int64_t ldb);
+WgradPlan wgrad_plan(int64_t NR, int64_t NC, int64_t K);
 hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* Bt, const float* gamma,
                              const void* Wraw, float* dW, float* Pg, float* ws, int64_t ws_bytes,
                              hipStream_t stream);

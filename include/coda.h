@@ -427,10 +427,9 @@ coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, c
                             const float* gamma, const void* W, float* dW, float* partials,
                             void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes for coda_gemm_wgrad_tok: as coda_wgrad_workspace_bytes, and more where
- * the leading dimension makes a split necessary (token rows are addressed with 32-bit
- * offsets from a split's first row: a split holds at most 2^31 / (2 max(lda, ldb)) - 256
- * tokens); -1 for invalid sizes or a leading dimension no split can address.          */
+/* Workspace bytes for coda_gemm_wgrad_tok: the same as coda_wgrad_workspace_bytes (token
+ * rows are addressed per 64-token k-tile, so the leading dimensions need no split of
+ * their own); -1 for invalid sizes (lda < NR, ldb < NC, or either above 2^22).        */
 int64_t coda_wgrad_tok_workspace_bytes(int64_t NR, int64_t NC, int64_t K, int64_t lda, int64_t ldb);
 
 /* The same weight-gradient GEMM (cited above) on token-major operands, as the
@@ -442,9 +441,8 @@ int64_t coda_wgrad_tok_workspace_bytes(int64_t NR, int64_t NC, int64_t K, int64_
  * The tiles are read through LDS transpose reads; the result is bit-identical to
  * coda_gemm_wgrad on the transposed operands with the same split.  Any K (K = 0 writes
  * zeros).  Granules: NC % 8 == 0, lda % 8 == 0, ldb % 8 == 0, lda >= NR, ldb >= NC.
- * Where (K + 256) * max(lda, ldb) * 2 exceeds 2^31 the tokens must be split: the call
- * then needs coda_wgrad_tok_workspace_bytes bytes of workspace (CODA_ERR_VALUE with
- * less; CODA_ERR_SHAPE where no split of at most 64 ranges can address the rows).     */
+ * Operands of any size (above 4 GB too): every 64-token k-tile is addressed from its own
+ * base.  Without workspace (or with less than the split needs) one block per tile.     */
 coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda, const void* Y,
                                 int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
                                 void* workspace, int64_t workspace_bytes, void* stream);

@@ -316,13 +316,14 @@ def test_token_major_weight_gradient_validation():
     assert w(64, 60, 64, P1, 64, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # NC % 8
     assert w(64, 64, 64, P1, 60, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # lda % 8
     assert w(72, 64, 64, P1, 64, P2, 64, None, None, P5, None, None, 0, None) == SHAPE     # lda < NR
-    # 32-bit row offsets: a long range of wide rows must be split, which needs a workspace
-    assert w(64, 64, 1 << 22, P1, 512, P2, 64, None, None, P5, None, None, 0, None) == VALUE
-    assert w(64, 64, 1 << 22, P1, 1 << 21, P2, 64, None, None, P5, None, None, 0, None) == SHAPE  # > 64 splits
-    # the LM head's dz [16384, 128256]: 3 splits of at most 8064 tokens
-    assert L.coda_wgrad_tok_workspace_bytes(128256, 2048, 16384, 128256, 2048) == 3 * (128256 + 501) * 2048 * 4
-    assert L.coda_wgrad_tok_workspace_bytes(16384, 2048, 16384, 16384, 2048) == 0     # fits, 512 tiles
+    # rows are addressed per 64-token k-tile: the LM head's 4.2 GB dz [16384, 128256] needs
+    # no split (4008 tiles), the split is the time model's alone, as on transposed operands
+    assert L.coda_wgrad_tok_workspace_bytes(128256, 2048, 16384, 128256, 2048) == 0
+    assert L.coda_wgrad_tok_workspace_bytes(16384, 2048, 16384, 16384, 2048) == 0     # 512 tiles
+    ws = L.coda_wgrad_workspace_bytes(2048, 2048, 16384)                                # 64 tiles: split
+    assert ws > 0 and L.coda_wgrad_tok_workspace_bytes(2048, 2048, 16384, 2048, 2048) == ws
     assert L.coda_wgrad_tok_workspace_bytes(64, 64, 64, 32, 64) == -1                   # lda < NR
+    assert L.coda_wgrad_tok_workspace_bytes(64, 64, 64, (1 << 22) + 8, 64) == -1        # lda > 2^22
     assert w(64, 64, 13, None, 64, P2, 64, None, None, P5, None, None, 0, None) == NULL
     assert w(64, 64, 13, P1, 64, P2, 64, None, None, P1 + 64, None, None, 0, None) == ALIAS  # dW over X
     assert w(64, 64, 13, P1, 64, P2 + 8, 64, None, None, P5, None, None, 0, None) == ALIGN
