@@ -473,30 +473,38 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // bytes of one k-tile in the A and B panels (a stage holds BM*RBA + BN*RBB bytes, B
 // after A).  kbytes is the byte length of an A row (k-tile count = ceil(kbytes / RBA));
 // the B panel's descriptor and K-tail checks use its own row length, set at init.
-template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
-          class ARow, class BRow, class PA, class PB>
-__device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,
-                                                int kbytes_b, uint8_t* const (&st)[NS],
-                                                const ARow& a_row, const BRow& b_row) {
+// The pending DMA of k-tile NS-1 (its base offsets) between the prologue and the run.
+template <class OA, class OB>
+struct DmaPending {
+    OA a;
+    OB b;
+};
+
+// Compile-time schedule constants of mainloop_dma_fp.
+template <class FP, int NS, int SPREAD, int TM, int TN, class PA, class PB>
+struct DmaSched {
+    static constexpr int KS = FP::kSteps;
+    static constexpr int kMfma = TM * TN;
+    static constexpr int nA = PA::kInst;
+    static constexpr int kPerTile = nA + PB::kInst;                        // DMA per wave per tile
+    static constexpr int kPer = (kPerTile + SPREAD - 1) / SPREAD;          // DMA per k-step
     static_assert(NS >= 2, "at least two stages");
-    constexpr int KS = FP::kSteps;
     static_assert((NS * KS) % 2 == 0, "fragment double-buffer parity must repeat every stage group");
-    constexpr int kMfma = TM * TN;
-    constexpr int nA = PA::kInst;
-    constexpr int kPerTile = nA + PB::kInst;   // DMA per wave per tile
     static_assert((NS - 1) * kPerTile < 64, "vmcnt range");
     static_assert(SPREAD >= 1 && SPREAD <= KS, "the DMA of a tile ends before the next tile's last k-step");
-    constexpr int kPer = (kPerTile + SPREAD - 1) / SPREAD;            // DMA per k-step
     static_assert(kPer <= kMfma, "one MFMA ahead of every DMA instruction");
-    const int nk = (kbytes + RBA - 1) / RBA;
-    // k-tiles run in groups of NS (one per stage); the count is padded to a multiple of NS
-    // with k-tiles past K, which the DMA fills with zeros.  The DMA always runs NS tiles
-    // ahead, past the padded end too (zeros into stages that are not read again), so the
-    // wait counts are exact on every tile.
-    const int ng = (nk + NS - 1) / NS;
-    constexpr int kOffB = BM * RBA;          // B panel offset inside a stage
-    FP f;
-    // DMA instruction q (0 .. kPerTile-1) of the tile with base offsets (ba, bb)
+};
+
+// Prologue of the pipelined mainloop: the DMA of k-tiles 0 .. NS-2 and the first share of
+// k-tile NS-1, nothing waited for.  Issued on its own (mainloop_dma_run follows), it lets
+// a caller that owns the LDS stages start the next tile's loads before other work (a
+// persistent kernel's epilogue that does not touch the LDS).
+template <class FP, int BM, int NS, int RBA, int SPREAD, int TM, int TN, class PA, class PB>
+__device__ __forceinline__ auto mainloop_dma_prologue(const PA& pa, const PB& pb, int kbytes, int kbytes_b,
+                                                      uint8_t* const (&st)[NS]) {
+    using D = DmaSched<FP, NS, SPREAD, TM, TN, PA, PB>;
+    constexpr int nA = D::nA, kPer = D::kPer;
+    constexpr int kOffB = BM * RBA;
     auto issue_q = [&](int q, uint8_t* stage, const auto& ba, const auto& bb) {
         if (q < nA) pa.issue_one(q, stage, ba);
         else pb.issue_one(q - nA, stage + kOffB, bb);
@@ -507,9 +515,39 @@ __device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const P
         pb.issue(st[i] + kOffB, i, kbytes_b);
     });
     // tile NS-1: its first share now, the rest as pending DMA during tile 0
-    auto pend_a = pa.base_offset(NS - 1, kbytes);     // a 32-bit offset, or a TokAddr
-    auto pend_b = pb.base_offset(NS - 1, kbytes_b);
-    static_for<kPer>([&](auto Q) { issue_q(decltype(Q)::value, st[NS - 1], pend_a, pend_b); });
+    DmaPending<decltype(pa.base_offset(0, kbytes)), decltype(pb.base_offset(0, kbytes_b))> pend{
+        pa.base_offset(NS - 1, kbytes), pb.base_offset(NS - 1, kbytes_b)};
+    static_for<kPer>([&](auto Q) { issue_q(decltype(Q)::value, st[NS - 1], pend.a, pend.b); });
+    return pend;
+}
+
+// The rest of the pipelined mainloop after mainloop_dma_prologue: wait for k-tile 0, the
+// k-loop, and the drain of the DMA that ran past the end.  The first wait, vmcnt
+// <= (NS-2) kPerTile + kPer, is exact when only the prologue's DMA was issued after
+// k-tile 0; vector memory operations issued after the prologue (an epilogue's stores)
+// only make it wait longer: loads complete in order, so while any load of k-tile 0 is
+// outstanding, so are all later loads of the prologue.
+template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
+          class ARow, class BRow, class PA, class PB, class Pend>
+__device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,
+                                                 int kbytes_b, uint8_t* const (&st)[NS], const ARow& a_row,
+                                                 const BRow& b_row, const Pend& pend0) {
+    using D = DmaSched<FP, NS, SPREAD, TM, TN, PA, PB>;
+    constexpr int KS = D::KS, kMfma = D::kMfma, nA = D::nA, kPerTile = D::kPerTile, kPer = D::kPer;
+    const int nk = (kbytes + RBA - 1) / RBA;
+    // k-tiles run in groups of NS (one per stage); the count is padded to a multiple of NS
+    // with k-tiles past K, which the DMA fills with zeros.  The DMA always runs NS tiles
+    // ahead, past the padded end too (zeros into stages that are not read again), so the
+    // wait counts are exact on every tile.
+    const int ng = (nk + NS - 1) / NS;
+    constexpr int kOffB = BM * RBA;          // B panel offset inside a stage
+    FP f;
+    auto issue_q = [&](int q, uint8_t* stage, const auto& ba, const auto& bb) {
+        if (q < nA) pa.issue_one(q, stage, ba);
+        else pb.issue_one(q - nA, stage + kOffB, bb);
+    };
+    auto pend_a = pend0.a;
+    auto pend_b = pend0.b;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile + kPer));   // tile 0 landed
     __syncthreads();
     f.load(0, st[0], st[0] + kOffB, 0, a_row, b_row);
@@ -556,6 +594,16 @@ __device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const P
     // drain the DMA that ran past the end before the LDS is reused or released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+}
+
+template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
+          class ARow, class BRow, class PA, class PB>
+__device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,
+                                                int kbytes_b, uint8_t* const (&st)[NS],
+                                                const ARow& a_row, const BRow& b_row) {
+    const auto pend = mainloop_dma_prologue<FP, BM, NS, RBA, SPREAD, TM, TN>(pa, pb, kbytes, kbytes_b, st);
+    mainloop_dma_run<FP, BM, BN, SPLIT, NS, NW, RBA, RBB, SPREAD>(acc, pa, pb, kbytes, kbytes_b, st, a_row, b_row,
+                                                                  pend);
 }
 
 // Both operands of one element type E with RB-byte k-tile rows.

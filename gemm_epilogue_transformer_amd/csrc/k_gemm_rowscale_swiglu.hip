@@ -515,20 +515,23 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
 }
 
 // SwiGLU epilogue on transposed accumulator blocks (the mainloop's MFMA took the W
-// fragment first): in block (tm, b) lane l holds row 32*tm + l%32 of the wave and, in
+// fragment first; rt[tm]: r of the lane's row 32*tm + l%32 of the wave, 0 past M): in
+// block (tm, b) lane l holds row 32*tm + l%32 of the wave and, in
 // register i, column 8*(i/4) + 4*(l/32) + i%4 of the block.  So r is one value per lane
 // and block row, and every group of 4 registers is 4 consecutive output columns of one
 // row; one cross-half lane swap per pair of groups makes them 8, stored with one 16-byte
 // store, with no LDS staging.  Same fp32 operations per element, in the same order, as
 // rowscale_epilogue.
 template <int BM, int BN, int WAVES_M, int TM, int TN>
-__device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN],
-                                                   const float (&rv)[BM / WAVES_M / 64], float sw,
+__device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN], const float (&rt)[TM], float sw,
                                                    uint16_t* __restrict__ Y, int M, int N_out, int m0, int j0,
                                                    int wm, int wn) {
     constexpr int WM = BM / WAVES_M;
     constexpr int NB = TN / 2;
-    const int lane = threadIdx.x & 63;
+    // lane-derived addresses are formed here, not hoisted out of a persistent kernel's
+    // tile loop (where they would stay live through the mainloop)
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
     const int lr = lane & 31, lh = lane >> 5;
     const int valid_rows = min(BM, M - m0);
     const uint32_t row_bytes = static_cast<uint32_t>(N_out) * 2;
@@ -536,7 +539,7 @@ __device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN]
         make_buffer_rsrc(Y + static_cast<size_t>(m0) * N_out, static_cast<uint32_t>(valid_rows) * row_bytes);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-        const float rr = __shfl(rv[tm / 2], (tm % 2) * 32 + lr) * sw;
+        const float rr = rt[tm] * sw;
         const uint32_t row_off = static_cast<uint32_t>(wm * WM + tm * 32 + lr) * row_bytes;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -696,12 +699,100 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     else if constexpr (ACT == kActCeBwd)
         ce_bwd_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, tv, lv, gv, bw, M, N_out, m0, j0, tile_n, wm, wn,
                                                           slab);
-    else if constexpr (TC)
-        swiglu_epilogue_tc<BM, BN, WAVES_M, TM, TN>(acc, rv, sw, Y, M, N_out, m0, j0, wm, wn);
+    else if constexpr (TC) {
+        float rt[TM];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) rt[tm] = __shfl(rv[tm / 2], (tm % 2) * 32 + (threadIdx.x & 31));
+        swiglu_epilogue_tc<BM, BN, WAVES_M, TM, TN>(acc, rt, sw, Y, M, N_out, m0, j0, wm, wn);
+    }
     else if constexpr (ACT == kActSwigluSave)
         swiglu_save_epilogue<BM, BN, WAVES_M, TM, TN>(acc, rv, sw, Y, bw.dz, M, N_out, m0, j0, wm, wn, slab);
     else
         rowscale_epilogue<BM, BN, WAVES_M, TM, TN, ACT>(acc, rv, pv, rope, sw, Y, M, N_out, m0, j0, wm, wn, slab);
+}
+
+// Persistent form of the forward SwiGLU GEMM (bf16 weights, transposed accumulator
+// blocks, the epilogue of swiglu_epilogue_tc): a grid of at most one workgroup per CU
+// walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... in the XCD-aware order of the
+// one-tile-per-workgroup launch (with gridDim.x a multiple of 8, tile t still runs on XCD
+// t mod 8).  The epilogue touches no LDS, so the next tile's first k-tiles are issued
+// into the stages right after the mainloop's drain, and their latency hides behind the
+// epilogue's arithmetic and stores; the row scales of the next tile are loaded there too.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
+k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
+                         const float* __restrict__ w_scale, const float* __restrict__ R, uint16_t* __restrict__ Y,
+                         int M, int N_out, int K, int tiles_m, int tiles_n) {
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int BNO = BN / 2;                      // output columns of one block tile
+    static_assert(TN % 2 == 0, "SwiGLU pairs gate and up blocks");
+    constexpr int kStage = BM * RB + BN * RB;
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+    uint8_t* st[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) st[i] = stages[i];
+    using FP = FragPair<Frags<Elt::BF16, TM, TN, RB, true>>;
+    using PanelA = DmaPanel<BM, BM, NW, RB>;
+    using PanelB = DmaPanel<BN, BN / 2, NW, RB>;
+
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int kbytes = K * 2;
+    const int ntiles = tiles_m * tiles_n;
+    auto a_row = [&](int tm) { return wm * WM + tm * 32; };
+    // blocks [0, TN/2) = this wave's gate rows, [TN/2, TN) = the matching up rows
+    auto b_row = [&](int tn) {
+        constexpr int TH = TN / 2;
+        return (tn < TH ? 0 : BN / 2) + wn * TH * 32 + (tn % TH) * 32;
+    };
+    PanelA pa;
+    PanelB pb;
+    int m0 = 0, j0 = 0;
+    float rv[TM];                                    // r of the lane's row in each block row
+    // panels and row scales of tile t (r of rows past M: 0)
+    auto setup = [&](int t) {
+        int tile_m, tile_n;
+        tile_coords<8>(t, tiles_m, tiles_n, tile_m, tile_n);
+        m0 = tile_m * BM;
+        j0 = tile_n * BNO;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * WM + 32 * i + (threadIdx.x & 31);
+            rv[i] = m < M ? R[m] : 0.0f;
+        }
+        const uint8_t* a0 = H + static_cast<size_t>(m0) * kbytes;
+        pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
+        const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes;
+        const uint8_t* u0 = W + static_cast<size_t>(N_out + j0) * kbytes;
+        pb.init(g0, min(BN / 2, N_out - j0), u0, min(BN / 2, N_out - j0), kbytes);
+    };
+    const float sw = w_scale ? *w_scale : 1.0f;
+    int t = blockIdx.x;                              // the grid holds at most ntiles workgroups
+    setup(t);
+    auto pend = mainloop_dma_prologue<FP, BM, NS, RB, SPREAD, TM, TN>(pa, pb, kbytes, kbytes, st);
+    for (; t < ntiles; t += gridDim.x) {
+        f32x16_t acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        mainloop_dma_run<FP, BM, BN, BN / 2, NS, NW, RB, RB, SPREAD>(acc, pa, pb, kbytes, kbytes, st, a_row, b_row,
+                                                                     pend);
+        // the mainloop ended with every DMA drained and a barrier: the stages are free
+        const int cm0 = m0, cj0 = j0;
+        float rc[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) rc[i] = rv[i];
+        if (t + static_cast<int>(gridDim.x) < ntiles) {     // uniform over the workgroup
+            setup(t + gridDim.x);
+            pend = mainloop_dma_prologue<FP, BM, NS, RB, SPREAD, TM, TN>(pa, pb, kbytes, kbytes, st);
+        }
+        swiglu_epilogue_tc<BM, BN, WAVES_M, TM, TN>(acc, rc, sw, Y, M, N_out, cm0, cj0, wm, wn);
+    }
 }
 
 // Tile configurations of the second GEMM (compile-time).
@@ -722,6 +813,9 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 #endif
 #ifndef CODA_G3_NS8
 #define CODA_G3_NS8 2
+#endif
+#ifndef CODA_G3_PERSIST
+#define CODA_G3_PERSIST 1   // forward SwiGLU on bf16 weights: the persistent kernel
 #endif
 constexpr int BM3 = CODA_G3_BM, BN3 = CODA_G3_BN, NS3 = CODA_G3_NS, OCC3 = CODA_G3_OCC;
 constexpr int WM3 = CODA_G3_WM, WN3 = CODA_G3_WN, RB3 = CODA_G3_RB, SP3 = CODA_G3_SPREAD, PIPE3 = CODA_G3_PIPE;
@@ -767,6 +861,19 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
     const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
     const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
     const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
+    if (swiglu && !w_fp8 && CODA_G3_PERSIST && CODA_G3_TC && PIPE3 == 0) {
+        const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BN3 / 2 - 1) / (BN3 / 2);
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const int grid = std::min(tiles_m * tiles_n, std::max(cus, 1));
+        hipLaunchKernelGGL((k_gemm_swiglu_persistent<BM3, BN3, WM3, WN3, NS3, RB3, SP3>), dim3(grid),
+                           dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
+                           static_cast<const uint8_t*>(W), w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m,
+                           tiles_n);
+        return hipGetLastError();
+    }
     if (swiglu)
         return w_fp8 ? launch3<kActSwiglu, true>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, no_bw, stream)
                      : launch3<kActSwiglu, false>(M, N_out, K, h, W, w_scale, r, y, none, no_ce, no_bw, stream);
