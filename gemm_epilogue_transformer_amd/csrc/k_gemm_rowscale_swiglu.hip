@@ -29,6 +29,9 @@
 #ifndef CODA_G3_TC
 #define CODA_G3_TC 1      // 0: the forward SwiGLU epilogue stages through LDS like the others
 #endif
+#ifndef CODA_G3_TC_CE
+#define CODA_G3_TC_CE 1   // the loss statistics from transposed accumulator blocks too
+#endif
 
 namespace coda {
 
@@ -116,6 +119,116 @@ __device__ __forceinline__ void ce_epilogue(const f32x16_t (&acc)[TM][TN], const
                 red[2 * (wn * BM + wm * WM + rl)] = mx;
                 red[2 * (wn * BM + wm * WM + rl) + 1] = sum;
             }
+        }
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < BM; r += NT) {
+        const int m = m0 + r;
+        if (m < M) {
+            float mt = ninf;
+#pragma unroll
+            for (int w = 0; w < WAVES_N; ++w) mt = fmaxf(mt, red[2 * (w * BM + r)]);
+            float st = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WAVES_N; ++w) {
+                const float mw = red[2 * (w * BM + r)];
+                if (mw > ninf) st += red[2 * (w * BM + r) + 1] * __expf(mw - mt);
+            }
+            float* pp = ce.partials + (static_cast<size_t>(m) * ce.T + tile_n) * 2;
+            pp[0] = mt;
+            pp[1] = st;
+        }
+    }
+}
+
+// Sum / max of a value over lane l and lane l ^ 32: v_permlane32_swap on two copies of
+// it (one result holds the lower half-wave's value in every lane, the other the
+// upper's), the same operation order in both lanes.  Both the second operand and the
+// two results pass through empty asm statements: used directly in arithmetic, the
+// compiler at hand reads the instruction's first result register for both results.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    uint32_t v = u;
+    asm volatile("" : "+v"(v));
+    const auto p = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+    uint32_t a = p[0], b = p[1];
+    asm volatile("" : "+v"(a), "+v"(b));
+    lo = __builtin_bit_cast(float, a);
+    hi = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float halves_max(float x) {
+    float lo, hi;
+    halves(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    float lo, hi;
+    halves(x, lo, hi);
+    return lo + hi;
+}
+
+// Cross-entropy epilogue on transposed accumulator blocks (the mainloop's MFMA took the
+// W fragment first): in block (tm, b) lane l holds logits of row 32*tm + l%32 of the
+// wave, columns 32*b + 8*(i/4) + 4*(l/32) + i%4 of the wave's columns in register i.  So
+// a row's max and sum of exponentials over the wave's columns are in-lane reductions
+// over 16*TN values and one exchange between the two half-waves, with no LDS staging;
+// the waves sharing a row combine in a fixed order as in ce_epilogue.  rt[tm], tt[tm]:
+// r and the target of the lane's row (0 and -1 past M).  The lane holding a row's target
+// column writes that logit.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
+__device__ __forceinline__ void ce_epilogue_tc(const f32x16_t (&acc)[TM][TN], const float (&rt)[TM],
+                                               const int (&tt)[TM], float sw, const CeArgs& ce, int M, int V,
+                                               int m0, int j0, int tile_n, int wm, int wn, float* red) {
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, NT = 64 * WAVES_M * WAVES_N;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int lr = lane & 31, lh = lane >> 5;
+    const float ninf = -__builtin_inff();
+    const int nw = j0 + wn * WN;                    // first column of the wave
+    const bool full = nw + WN <= V;                 // wave-uniform: no column past V
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const float rr = rt[tm] * sw;
+        float z[TN][16];
+        float mx = ninf;
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                z[b][i] = acc[tm][b][i] * rr;
+                const int n = nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3);
+                if (full || n < V) mx = fmaxf(mx, z[b][i]);
+            }
+        mx = halves_max(mx);
+        float sum = 0.0f;
+        if (mx > ninf) {
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int n = nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3);
+                    if (full || n < V) sum += __expf(z[b][i] - mx);
+                }
+        }
+        sum = halves_sum(sum);
+        const int rl = wm * WM + tm * 32 + lr;      // row within the block tile
+        const int tg = tt[tm];
+        const int o = tg - nw;
+        if (o >= 0 && o < WN && tg < V) {
+            const int c = o & 31;
+            if (((c >> 2) & 1) == lh) {
+                const int k = (o >> 5) * 16 + ((c >> 3) << 2) + (c & 3);
+                float zt = 0.0f;
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) zt = (k == 16 * b + i) ? z[b][i] : zt;
+                ce.tgt_logit[m0 + rl] = zt;
+            }
+        }
+        if (lh == 0) {
+            red[2 * (wn * BM + rl)] = mx;
+            red[2 * (wn * BM + rl) + 1] = sum;
         }
     }
     __syncthreads();
@@ -598,7 +711,7 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     constexpr int BNO = SWIGLU ? BN / 2 : BN;       // output columns of one block tile
     // transposed accumulator blocks (16-byte stores straight from registers) for the
     // forward SwiGLU on the bf16 DMA mainloop
-    constexpr bool TC = CODA_G3_TC && ACT == kActSwiglu && !W8 && PIPE == 0;
+    constexpr bool TC = CODA_G3_TC && (ACT == kActSwiglu || (ACT == kActCe && CODA_G3_TC_CE)) && !W8 && PIPE == 0;
 
     constexpr int RBB = W8 ? RB / 2 : RB;            // bytes of a W row per k-tile
     constexpr int kStage = BM * RB + BN * RBB;
@@ -637,6 +750,16 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
             lv[i] = m < M ? ce.lse[m] : 0.0f;
             gv[i] = m < M ? ce.gw[m] : 0.0f;
         }
+    }
+
+    // transposed layout: r and the target of the lane's row in each block row
+    float rt[TM];
+    int tt[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WM + 32 * i + (threadIdx.x & 31);
+        rt[i] = (TC && ACT == kActCe && m < M) ? R[m] : 0.0f;
+        tt[i] = (TC && ACT == kActCe && m < M) ? ce.targets[m] : -1;
     }
 
     const int kbytes = K * 2;                       // bytes of an h row
@@ -690,7 +813,10 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 
     const float sw = w_scale ? *w_scale : 1.0f;
     uint8_t* slab = slab_region<NS, NW, kStage, Slab<(ACT == kActSwiglu) ? TN / 2 : TN>::kBytes>(st, wave);
-    if constexpr (ACT == kActCe)
+    if constexpr (ACT == kActCe && TC)
+        ce_epilogue_tc<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rt, tt, sw, ce, M, N_out, m0, j0, tile_n, wm, wn,
+                                                         ce_red);
+    else if constexpr (ACT == kActCe)
         ce_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, tv, sw, ce, M, N_out, m0, j0, tile_n, wm, wn, slab,
                                                       ce_red);
     else if constexpr (ACT == kActSwigluBwd)
