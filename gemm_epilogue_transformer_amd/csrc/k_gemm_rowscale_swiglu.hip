@@ -30,7 +30,7 @@
 #define CODA_G3_TC 1      // 0: the forward SwiGLU epilogue stages through LDS like the others
 #endif
 #ifndef CODA_G3_TC_CE
-#define CODA_G3_TC_CE 1   // the loss statistics from transposed accumulator blocks too
+#define CODA_G3_TC_CE 1   // the loss statistics and their backward from transposed blocks too
 #endif
 
 namespace coda {
@@ -189,26 +189,31 @@ __device__ __forceinline__ void ce_epilogue_tc(const f32x16_t (&acc)[TM][TN], co
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const float rr = rt[tm] * sw;
+        // logits; past V (only in the last column tile) -inf, which adds nothing below
         float z[TN][16];
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) z[b][i] = acc[tm][b][i] * rr;
+        if (!full) {
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3) >= V) z[b][i] = ninf;
+        }
         float mx = ninf;
 #pragma unroll
         for (int b = 0; b < TN; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                z[b][i] = acc[tm][b][i] * rr;
-                const int n = nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3);
-                if (full || n < V) mx = fmaxf(mx, z[b][i]);
-            }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, z[b][i]);
         mx = halves_max(mx);
         float sum = 0.0f;
         if (mx > ninf) {
 #pragma unroll
             for (int b = 0; b < TN; ++b)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int n = nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3);
-                    if (full || n < V) sum += __expf(z[b][i] - mx);
-                }
+                for (int i = 0; i < 16; ++i) sum += __expf(z[b][i] - mx);
         }
         sum = halves_sum(sum);
         const int rl = wm * WM + tm * 32 + lr;      // row within the block tile
@@ -443,6 +448,87 @@ __device__ __forceinline__ void ce_bwd_epilogue(const f32x16_t (&acc)[TM][TN],
             const int m = m0 + wm * WM + rl;
             if ((lane & 15) == 0 && m < M && pcol < bw.T) bw.partials[static_cast<size_t>(m) * bw.T + pcol] = c;
         }
+    }
+}
+
+// Backward of the loss epilogue on transposed accumulator blocks (the layout of
+// ce_epilogue_tc): per lane and block row the 16*TN logits of one row, so the row's
+// r, lse, weight and target are per-lane values, dz leaves as 16-byte stores after one
+// half-wave exchange per pair of 4-column groups (as in swiglu_epilogue_tc), and the
+// partial sum of dL/dz * acc over the wave's 128 columns is an in-lane sum plus one
+// exchange.  rt, tt, lt, gt: r, target, lse and weight of the lane's row in each block
+// row (0, -1, 0, 0 past M).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
+__device__ __forceinline__ void ce_bwd_epilogue_tc(const f32x16_t (&acc)[TM][TN], const float (&rt)[TM],
+                                                   const int (&tt)[TM], const float (&lt)[TM], const float (&gt)[TM],
+                                                   const BwdArgs& bw, int M, int V, int m0, int j0, int tile_n,
+                                                   int wm, int wn) {
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    static_assert(WN == 128, "one partial per wave and row: 128 columns");
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int lr = lane & 31, lh = lane >> 5;
+    const int valid_rows = min(BM, M - m0);
+    const uint32_t dz_row = static_cast<uint32_t>(V) * 2;
+    const __amdgpu_buffer_rsrc_t dz_rsrc =
+        make_buffer_rsrc(bw.dz + static_cast<size_t>(m0) * V, static_cast<uint32_t>(valid_rows) * dz_row);
+    const int pcol = 2 * tile_n + wn;                       // this wave's partial column
+    const int nw = j0 + wn * WN;                            // first column of the wave
+    const bool full = nw + WN <= V;                         // wave-uniform: no column past V
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const float rr = rt[tm], ls = lt[tm];
+        const int tg = tt[tm];
+        const float gr = (tg >= 0 && tg < V) ? gt[tm] : 0.0f;  // an ignored row: no gradient
+        const int rl = wm * WM + tm * 32 + lr;                 // row within the block tile
+        const uint32_t row_off = static_cast<uint32_t>(rl) * dz_row;
+        float c = 0.0f;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+            // dL/dz of the block's 16 columns; past V (only in the last column tile) 0
+            float dl[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int n = nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3);
+                const float p = __expf(rr * acc[tm][b][i] - ls);
+                dl[i] = gr * (p - (n == tg ? 1.0f : 0.0f));
+            }
+            if (!full) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3) >= V) dl[i] = 0.0f;
+            }
+            uint32_t pk[4][2];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float dzo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    c += dl[4 * g + e] * acc[tm][b][4 * g + e];
+                    dzo[e] = rr * dl[4 * g + e];
+                }
+                pk[g][0] = pack_bf16x2(dzo[0], dzo[1]);
+                pk[g][1] = pack_bf16x2(dzo[2], dzo[3]);
+            }
+            const int nb = nw + 32 * b;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                uint32_t w[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const auto sw2 = __builtin_amdgcn_permlane32_swap(pk[2 * q][h], pk[2 * q + 1][h], false, false);
+                    w[h] = sw2[0];
+                    w[2 + h] = sw2[1];
+                }
+                const int n = nb + 16 * q + 8 * lh;
+                const uint32_t voff = n < V ? row_off + static_cast<uint32_t>(n) * 2 : kOobOffset;
+                __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(w[0]), int(w[1]), int(w[2]), int(w[3])}, dz_rsrc,
+                                                       voff, 0, 0);
+            }
+        }
+        c = halves_sum(c);
+        const int m = m0 + rl;
+        if (lh == 0 && m < M && pcol < bw.T) bw.partials[static_cast<size_t>(m) * bw.T + pcol] = c;
     }
 }
 
@@ -711,7 +797,9 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     constexpr int BNO = SWIGLU ? BN / 2 : BN;       // output columns of one block tile
     // transposed accumulator blocks (16-byte stores straight from registers) for the
     // forward SwiGLU on the bf16 DMA mainloop
-    constexpr bool TC = CODA_G3_TC && (ACT == kActSwiglu || (ACT == kActCe && CODA_G3_TC_CE)) && !W8 && PIPE == 0;
+    constexpr bool TC = CODA_G3_TC && (ACT == kActSwiglu || ((ACT == kActCe || ACT == kActCeBwd) && CODA_G3_TC_CE)) &&
+                        !W8 && PIPE == 0;
+    constexpr bool TC_CE = TC && (ACT == kActCe || ACT == kActCeBwd);
 
     constexpr int RBB = W8 ? RB / 2 : RB;            // bytes of a W row per k-tile
     constexpr int kStage = BM * RB + BN * RBB;
@@ -753,13 +841,15 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     }
 
     // transposed layout: r and the target of the lane's row in each block row
-    float rt[TM];
+    float rt[TM], lt[TM], gt[TM];
     int tt[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = m0 + wm * WM + 32 * i + (threadIdx.x & 31);
-        rt[i] = (TC && ACT == kActCe && m < M) ? R[m] : 0.0f;
-        tt[i] = (TC && ACT == kActCe && m < M) ? ce.targets[m] : -1;
+        rt[i] = (TC_CE && m < M) ? R[m] : 0.0f;
+        tt[i] = (TC_CE && m < M) ? ce.targets[m] : -1;
+        lt[i] = (TC_CE && ACT == kActCeBwd && m < M) ? ce.lse[m] : 0.0f;
+        gt[i] = (TC_CE && ACT == kActCeBwd && m < M) ? ce.gw[m] : 0.0f;
     }
 
     const int kbytes = K * 2;                       // bytes of an h row
@@ -822,6 +912,9 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     else if constexpr (ACT == kActSwigluBwd)
         swiglu_bwd_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, bw, M, N_out, m0, j0, tile_n, wm, wn, slab,
                                                               ce_red);
+    else if constexpr (ACT == kActCeBwd && TC)
+        ce_bwd_epilogue_tc<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rt, tt, lt, gt, bw, M, N_out, m0, j0, tile_n, wm,
+                                                             wn);
     else if constexpr (ACT == kActCeBwd)
         ce_bwd_epilogue<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rv, tv, lv, gv, bw, M, N_out, m0, j0, tile_n, wm, wn,
                                                           slab);
