@@ -130,8 +130,8 @@ def test_chain_small_all_rows(M, K1, d, N2w, act, dtype):
 def test_many_tiles_per_workgroup_all_rows():
     """More output tiles than CUs, not a multiple of them (17 x 31 = 527 tiles of 256 x 128
     outputs): the forward SwiGLU GEMM's persistent workgroups take two or three tiles each,
-    the last round partly; every row is checked, so a tile skipped or written twice by the
-    tile loop fails."""
+    the last pass over the CUs filling them partly; every row is checked, so a tile skipped
+    or written twice by the tile loop fails."""
     w = si.custom(4196, 72, 192, 2 * 3880, si.ACT_SWIGLU, seed=4196)
     _log(f"chain many tiles {w.name}")
     inp = si.generate(w)
