@@ -108,3 +108,18 @@ def test_launch_groups():
     assert bench._launch_groups(durs) == [[4, 0, 2], [3, 1, 5]]
     assert bench._launch_groups([50.0]) == [[0]]
     assert bench._launch_groups([10.0, 11.0, 12.0]) == [[0, 1, 2]]
+
+
+def test_roofline_kernels_resolve_to_their_sources():
+    """Every kernel a bench line names for its roofline is defined in a translation unit the
+    source hash covers, so its stored traffic is checked against the right files; the
+    default workload's stored traffic belongs to the current sources of its kernel."""
+    for k in ("k_gemm_swiglu_persistent", "k_gemm_rowscale_swiglu", "k_gemm_resid_partialrms",
+              "k_gemm_rmsnorm_bwd", "k_gemm_wgrad", "k_rope_bwd", "k_swiglu_bwd_saved"):
+        files = bench._kernel_files(k)
+        assert any(f.endswith(".hip") for f in files), (k, files)
+        if k.startswith("k_gemm"):
+            assert "gemm_pipeline.hpp" in files, (k, files)     # the mainloops count too
+        assert bench.kernel_source_hash(k) != ""
+    rec = json.load(open(os.path.join(bench.ROOT, "profiles", "traffic_llama1b_attnout_mlpin_m16384.json")))
+    assert "k_gemm_swiglu_persistent" in rec["kernels"]
