@@ -41,15 +41,59 @@ def _ptr(t):
     if t is None:
         return None
     if not t.is_cuda:
-        raise ValueError("expected a device tensor")
+        raise ValueError(f"expected a device (GPU) tensor, got one on {t.device}")
     if not t.is_contiguous():
         raise ValueError("expected a contiguous tensor")
     return t.data_ptr()
 
 
-def _esize(t, n):
-    if t.element_size() != n:
-        raise ValueError(f"expected {n}-byte elements, got {t.dtype}")
+# Storage kinds the library reads and writes: bf16 codes (2 bytes), e4m3 codes (1 byte),
+# fp32 and int32.  The library sees plain pointers, so every tensor a caller hands in is
+# checked here -- shape, element type, contiguity, device -- before any call is made: a
+# mismatched buffer would otherwise be read or written out of bounds on the GPU.
+B16 = (torch.bfloat16, torch.int16, torch.uint16)
+B8 = (torch.uint8, torch.int8, torch.float8_e4m3fn)
+F32 = (torch.float32,)
+I32 = (torch.int32,)
+
+
+def _dims(t, name, nd):
+    """The shape of a caller's operand whose sizes define the problem (ndim checked)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.dim() != nd:
+        raise ValueError(f"{name}: expected {nd} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _need(t, name, shape, kinds, dev, optional=True):
+    """Raise ValueError unless tensor ``t`` has exactly ``shape`` (None: any), a dtype in
+    ``kinds``, is contiguous and sits on device ``dev`` (the call's first operand's); ``t``
+    may be None when ``optional``.  That the device is a GPU is checked last, when the
+    pointers are taken (``_ptr``), after every operand's shape has been checked."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in kinds:
+        raise ValueError(f"{name}: expected dtype in {[str(k) for k in kinds]}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name}: on {t.device}, the other operands on {dev}")
+
+
+def _scalar(t, name, dev):
+    """A device fp32 scalar (a one-element tensor, or a longer one whose first element is used)."""
+    if t is None:
+        return
+    _need(t, name, None, F32, dev)
+    if t.numel() < 1:
+        raise ValueError(f"{name}: expected at least one fp32 element")
 
 
 def version() -> str:
@@ -62,9 +106,12 @@ def partials_per_row(N: int) -> int:
 
 def prepare_weight_bf16(W_t, gamma=None, out=None, stream=None):
     """Wp[n,k] = bf16(gamma[k] * W[n,k]);  W_t [N, K] bf16, gamma [K] fp32."""
-    _esize(W_t, 2)
-    N, K = W_t.shape
-    out = torch.empty((N, K), dtype=torch.bfloat16, device=W_t.device) if out is None else out
+    N, K = _dims(W_t, "W_t", 2)
+    dev = W_t.device
+    _need(W_t, "W_t", (N, K), B16, dev)
+    _need(gamma, "gamma", (K,), F32, dev)
+    _need(out, "out", (N, K), B16, dev)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=dev) if out is None else out
     _lib.check("coda_prepare_weight_bf16", _lib.load().coda_prepare_weight_bf16(
         N, K, _ptr(W_t), _ptr(gamma), _ptr(out), _stream(stream)))
     return out
@@ -74,11 +121,15 @@ def quantize_e4m3(X, gamma=None, out=None, amax_scale=None, stream=None):
     """Per-tensor e4m3 quantisation (gamma folded first if given).
 
     Returns (Q uint8 [N, K], amax_scale fp32 [2] = {amax, scale})."""
-    _esize(X, 2)
-    N, K = X.shape
-    out = torch.empty((N, K), dtype=torch.uint8, device=X.device) if out is None else out
+    N, K = _dims(X, "X", 2)
+    dev = X.device
+    _need(X, "X", (N, K), B16, dev)
+    _need(gamma, "gamma", (K,), F32, dev)
+    _need(out, "out", (N, K), B8, dev)
+    _need(amax_scale, "amax_scale", (2,), F32, dev)
+    out = torch.empty((N, K), dtype=torch.uint8, device=dev) if out is None else out
     if amax_scale is None:
-        amax_scale = torch.empty(2, dtype=torch.float32, device=X.device)
+        amax_scale = torch.empty(2, dtype=torch.float32, device=dev)
     _lib.check("coda_quantize_e4m3", _lib.load().coda_quantize_e4m3(
         N, K, _ptr(X), _ptr(gamma), _ptr(out), _ptr(amax_scale), _stream(stream)))
     return out, amax_scale
@@ -89,17 +140,25 @@ def gemm_resid_partialrms(A, W, x_res=None, a_scale=None, w_scale=None, h=None,
     """h = bf16(sa*sw*A.W^T + x_res);  P[m,t] = sum of h^2 over N-tile t.
 
     A [M, K] and W [N, K] both bf16 (2-byte) or both e4m3 (1-byte, scales required)."""
-    fp8 = A.element_size() == 1
-    _esize(W, A.element_size())
-    M, K = A.shape
-    N = W.shape[0]
-    if W.shape[1] != K:
+    M, K = _dims(A, "A", 2)
+    N, KW = _dims(W, "W", 2)
+    if KW != K:
         raise ValueError("A and W disagree on K")
     dev = A.device
+    fp8 = A.element_size() == 1
+    kinds = B8 if fp8 else B16
+    _need(A, "A", (M, K), kinds, dev)
+    _need(W, "W", (N, K), kinds, dev)
+    _need(x_res, "x_res", (M, N), B16, dev)
+    _scalar(a_scale, "a_scale", dev)
+    _scalar(w_scale, "w_scale", dev)
+    T = partials_per_row(N)
+    _need(h, "h", (M, N), B16, dev)
+    _need(partials, "partials", (M, T), F32, dev)
     if h is None:
         h = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if partials is None:
-        partials = torch.empty((M, partials_per_row(N)), dtype=torch.float32, device=dev)
+        partials = torch.empty((M, T), dtype=torch.float32, device=dev)
     _lib.check("coda_gemm_resid_partialrms", _lib.load().coda_gemm_resid_partialrms(
         M, N, K, _ptr(A), CODA_E4M3 if fp8 else CODA_BF16, _ptr(a_scale), _ptr(W), _ptr(w_scale),
         _ptr(x_res), _ptr(h), _ptr(partials), _stream(stream)))
@@ -108,24 +167,40 @@ def gemm_resid_partialrms(A, W, x_res=None, a_scale=None, w_scale=None, h=None,
 
 def rowscale_reduce(partials, N: int, eps: float, r=None, stream=None):
     """r[m] = 1/sqrt(sum_t P[m,t]/N + eps)."""
-    M = partials.shape[0]
-    r = torch.empty(M, dtype=torch.float32, device=partials.device) if r is None else r
+    M, _ = _dims(partials, "partials", 2)
+    dev = partials.device
+    _need(partials, "partials", (M, partials_per_row(N)), F32, dev)
+    _need(r, "r", (M,), F32, dev)
+    r = torch.empty(M, dtype=torch.float32, device=dev) if r is None else r
     _lib.check("coda_rowscale_reduce", _lib.load().coda_rowscale_reduce(
         M, N, _ptr(partials), float(eps), _ptr(r), _stream(stream)))
     return r
 
 
+def _second_gemm_operands(h, W, r, w_scale):
+    """Shapes and checks shared by the second-GEMM calls: h [M, K] bf16, W [n_w, K] bf16
+    or e4m3, r [M] fp32, w_scale a device fp32 scalar."""
+    M, K = _dims(h, "h", 2)
+    n_w, KW = _dims(W, "W", 2)
+    if KW != K:
+        raise ValueError("h and W disagree on K")
+    dev = h.device
+    _need(h, "h", (M, K), B16, dev)
+    _need(W, "W", (n_w, K), B8 if W.element_size() == 1 else B16, dev)
+    _need(r, "r", (M,), F32, dev, optional=False)
+    _scalar(w_scale, "w_scale", dev)
+    return M, K, n_w, dev
+
+
 def gemm_rowscale_swiglu(h, W, r, act=SWIGLU, w_scale=None, y=None, stream=None):
     """y = act(r * sw * h.W^T); W [2F, K] (SwiGLU: gate rows then up rows) or [N, K]."""
-    M, K = h.shape
+    M, K, n_w, dev = _second_gemm_operands(h, W, r, w_scale)
     fp8 = W.element_size() == 1
-    n_w = W.shape[0]
-    if W.shape[1] != K:
-        raise ValueError("h and W disagree on K")
     if act == SWIGLU and n_w % 2:
-        raise ValueError("SwiGLU weight needs an even number of rows")
+        raise ValueError("W: a SwiGLU weight needs an even number of rows")
     n_out = n_w // 2 if act == SWIGLU else n_w
-    y = torch.empty((M, n_out), dtype=torch.bfloat16, device=h.device) if y is None else y
+    _need(y, "y", (M, n_out), B16, dev)
+    y = torch.empty((M, n_out), dtype=torch.bfloat16, device=dev) if y is None else y
     _lib.check("coda_gemm_rowscale_swiglu", _lib.load().coda_gemm_rowscale_swiglu(
         M, n_out, K, act, _ptr(h), _ptr(W), CODA_E4M3 if fp8 else CODA_BF16, _ptr(w_scale),
         _ptr(r), _ptr(y), _stream(stream)))
@@ -134,7 +209,9 @@ def gemm_rowscale_swiglu(h, W, r, act=SWIGLU, w_scale=None, y=None, stream=None)
 
 def rope_table(rows, base=500000.0, cos=None, sin=None, stream=None):
     """cos / sin [rows, 32] fp32 of the angles p * base^(-2i/64) (RoPE, heads of 64)."""
-    dev = torch.device("cuda")
+    dev = torch.device("cuda") if cos is None else cos.device
+    _need(cos, "cos", (rows, 32), F32, dev)
+    _need(sin, "sin", (rows, 32), F32, dev)
     cos = torch.empty((rows, 32), dtype=torch.float32, device=dev) if cos is None else cos
     sin = torch.empty((rows, 32), dtype=torch.float32, device=dev) if sin is None else sin
     _lib.check("coda_rope_table", _lib.load().coda_rope_table(rows, float(base), _ptr(cos), _ptr(sin),
@@ -142,19 +219,26 @@ def rope_table(rows, base=500000.0, cos=None, sin=None, stream=None):
     return cos, sin
 
 
+def _rope_operands(M, pos, cos, sin, dev):
+    """Positions [M] int32 (or None) and the angle table cos / sin [rows, 32] fp32."""
+    _need(pos, "pos", (M,), I32, dev)
+    rows = 0 if cos is None else _dims(cos, "cos", 2)[0]
+    _need(cos, "cos", (rows, 32), F32, dev)
+    _need(sin, "sin", (rows, 32), F32, dev, optional=cos is None)
+    if cos is None and sin is not None:
+        raise ValueError("cos: required with sin")
+    return rows
+
+
 def gemm_rowscale_rope(h, W, r, pos, cos, sin, rot_cols, w_scale=None, y=None, stream=None):
     """y = RoPE(r * sw * h.W^T): W [N_out, K]; the first rot_cols columns (Q and K heads
     of 64) turn by the angles of their row's position pos [M] (int32) from the cos / sin
     table [rows, 32]; the rest (V) pass."""
-    M, K = h.shape
+    M, K, n_out, dev = _second_gemm_operands(h, W, r, w_scale)
     fp8 = W.element_size() == 1
-    if W.shape[1] != K:
-        raise ValueError("h and W disagree on K")
-    n_out = W.shape[0]
-    if pos is not None and pos.dtype != torch.int32:
-        raise ValueError("positions must be int32")
-    rows = 0 if cos is None else cos.shape[0]
-    y = torch.empty((M, n_out), dtype=torch.bfloat16, device=h.device) if y is None else y
+    rows = _rope_operands(M, pos, cos, sin, dev)
+    _need(y, "y", (M, n_out), B16, dev)
+    y = torch.empty((M, n_out), dtype=torch.bfloat16, device=dev) if y is None else y
     _lib.check("coda_gemm_rowscale_rope", _lib.load().coda_gemm_rowscale_rope(
         M, n_out, K, _ptr(h), _ptr(W), CODA_E4M3 if fp8 else CODA_BF16, _ptr(w_scale), _ptr(r),
         _ptr(pos), _ptr(cos), _ptr(sin), rows, rot_cols, _ptr(y), _stream(stream)))
@@ -168,14 +252,11 @@ def ce_partials_per_row(V: int) -> int:
 def gemm_rowscale_ce(h, W, r, targets, w_scale=None, partials=None, tgt_logit=None, stream=None):
     """LM-head GEMM with the block log-sum-exp epilogue: W [V, K]; returns (partials
     [M, T, 2] = per-tile (max, sum exp(z - max)), tgt_logit [M] = z[m, targets[m]])."""
-    M, K = h.shape
-    V = W.shape[0]
-    if W.shape[1] != K:
-        raise ValueError("h and W disagree on K")
-    if targets.dtype != torch.int32:
-        raise ValueError("targets must be int32")
+    M, K, V, dev = _second_gemm_operands(h, W, r, w_scale)
+    _need(targets, "targets", (M,), I32, dev, optional=False)
     T = ce_partials_per_row(V)
-    dev = h.device
+    _need(partials, "partials", (M, T, 2), F32, dev)
+    _need(tgt_logit, "tgt_logit", (M,), F32, dev)
     partials = torch.empty((M, T, 2), dtype=torch.float32, device=dev) if partials is None else partials
     tgt_logit = torch.empty(M, dtype=torch.float32, device=dev) if tgt_logit is None else tgt_logit
     fp8 = W.element_size() == 1
@@ -187,9 +268,15 @@ def gemm_rowscale_ce(h, W, r, targets, w_scale=None, partials=None, tgt_logit=No
 
 def ce_reduce(partials, targets, tgt_logit, V, lse=None, loss=None, stream=None):
     """(lse [M], loss [M]) from the LM-head GEMM's partials (loss 0 for ignored rows)."""
-    M = partials.shape[0]
-    lse = torch.empty(M, dtype=torch.float32, device=partials.device) if lse is None else lse
-    loss = torch.empty(M, dtype=torch.float32, device=partials.device) if loss is None else loss
+    M = _dims(partials, "partials", 3)[0]
+    dev = partials.device
+    _need(partials, "partials", (M, ce_partials_per_row(V), 2), F32, dev)
+    _need(targets, "targets", (M,), I32, dev, optional=False)
+    _need(tgt_logit, "tgt_logit", (M,), F32, dev, optional=False)
+    _need(lse, "lse", (M,), F32, dev)
+    _need(loss, "loss", (M,), F32, dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev) if lse is None else lse
+    loss = torch.empty(M, dtype=torch.float32, device=dev) if loss is None else loss
     _lib.check("coda_ce_reduce", _lib.load().coda_ce_reduce(
         M, V, _ptr(partials), _ptr(targets), _ptr(tgt_logit), _ptr(lse), _ptr(loss), _stream(stream)))
     return lse, loss
@@ -197,17 +284,22 @@ def ce_reduce(partials, targets, tgt_logit, V, lse=None, loss=None, stream=None)
 
 def rowscale_from_h(h, eps, r=None, stream=None):
     """r [M] = 1/sqrt(mean(h^2) + eps) of a stored bf16 h [M, N]."""
-    M, N = h.shape
-    r = torch.empty(M, dtype=torch.float32, device=h.device) if r is None else r
+    M, N = _dims(h, "h", 2)
+    dev = h.device
+    _need(h, "h", (M, N), B16, dev)
+    _need(r, "r", (M,), F32, dev)
+    r = torch.empty(M, dtype=torch.float32, device=dev) if r is None else r
     _lib.check("coda_rowscale_from_h", _lib.load().coda_rowscale_from_h(M, N, _ptr(h), eps, _ptr(r), _stream(stream)))
     return r
 
 
 def transpose_bf16(src, out=None, stream=None):
     """out [C, R] = src [R, C]^T (bf16)."""
-    _esize(src, 2)
-    R, C = src.shape
-    out = torch.empty((C, R), dtype=src.dtype, device=src.device) if out is None else out
+    R, C = _dims(src, "src", 2)
+    dev = src.device
+    _need(src, "src", (R, C), B16, dev)
+    _need(out, "out", (C, R), B16, dev)
+    out = torch.empty((C, R), dtype=src.dtype, device=dev) if out is None else out
     _lib.check("coda_transpose_bf16", _lib.load().coda_transpose_bf16(R, C, _ptr(src), _ptr(out), _stream(stream)))
     return out
 
@@ -215,12 +307,17 @@ def transpose_bf16(src, out=None, stream=None):
 def gemm_swiglu_bwd(h, W, r, dy, dz=None, partials=None, stream=None):
     """Recompute h.W'^T and apply the SwiGLU backward: returns (dz [M, 2F] = r * dL/dz,
     partials [M, T] of dL/dr).  W [2F, K] (gate rows, then up rows), dy [M, F]."""
-    M, K = h.shape
-    F2 = W.shape[0]
+    M, K, F2, dev = _second_gemm_operands(h, W, r, None)
+    _need(W, "W", (F2, K), B16, dev)
+    if F2 % 2:
+        raise ValueError("W: a SwiGLU weight needs an even number of rows")
     F = F2 // 2
     T = int(_lib.load().coda_swiglu_bwd_partials_per_row(F))
-    dz = torch.empty((M, F2), dtype=torch.bfloat16, device=h.device) if dz is None else dz
-    partials = torch.empty((M, T), dtype=torch.float32, device=h.device) if partials is None else partials
+    _need(dy, "dy", (M, F), B16, dev, optional=False)
+    _need(dz, "dz", (M, F2), B16, dev)
+    _need(partials, "partials", (M, T), F32, dev)
+    dz = torch.empty((M, F2), dtype=torch.bfloat16, device=dev) if dz is None else dz
+    partials = torch.empty((M, T), dtype=torch.float32, device=dev) if partials is None else partials
     _lib.check("coda_gemm_swiglu_bwd", _lib.load().coda_gemm_swiglu_bwd(
         M, F, K, _ptr(h), _ptr(W), _ptr(r), _ptr(dy), _ptr(dz), _ptr(partials), _stream(stream)))
     return dz, partials
@@ -228,8 +325,12 @@ def gemm_swiglu_bwd(h, W, r, dy, dz=None, partials=None, stream=None):
 
 def rmsnorm_bwd_reduce(partials, r, N, F, q=None, stream=None):
     """q [M] = -(r^3 / N) * sum_t partials."""
-    M = partials.shape[0]
-    q = torch.empty(M, dtype=torch.float32, device=partials.device) if q is None else q
+    M = _dims(partials, "partials", 2)[0]
+    dev = partials.device
+    _need(partials, "partials", (M, int(_lib.load().coda_swiglu_bwd_partials_per_row(F))), F32, dev)
+    _need(r, "r", (M,), F32, dev, optional=False)
+    _need(q, "q", (M,), F32, dev)
+    q = torch.empty(M, dtype=torch.float32, device=dev) if q is None else q
     _lib.check("coda_rmsnorm_bwd_reduce", _lib.load().coda_rmsnorm_bwd_reduce(
         M, N, F, _ptr(partials), _ptr(r), _ptr(q), _stream(stream)))
     return q
@@ -237,9 +338,18 @@ def rmsnorm_bwd_reduce(partials, r, N, F, q=None, stream=None):
 
 def gemm_rmsnorm_bwd(dz, Wt, h, q, dh_res=None, dh=None, stream=None):
     """dh [M, N] = dz . Wt^T + q * h (+ dh_res); Wt [N, K] = W'^T."""
-    M, K = dz.shape
-    N = Wt.shape[0]
-    dh = torch.empty((M, N), dtype=torch.bfloat16, device=dz.device) if dh is None else dh
+    M, K = _dims(dz, "dz", 2)
+    N, KW = _dims(Wt, "Wt", 2)
+    if KW != K:
+        raise ValueError("dz and Wt disagree on K")
+    dev = dz.device
+    _need(dz, "dz", (M, K), B16, dev)
+    _need(Wt, "Wt", (N, K), B16, dev)
+    _need(h, "h", (M, N), B16, dev)
+    _need(q, "q", (M,), F32, dev)
+    _need(dh_res, "dh_res", (M, N), B16, dev)
+    _need(dh, "dh", (M, N), B16, dev)
+    dh = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if dh is None else dh
     _lib.check("coda_gemm_rmsnorm_bwd", _lib.load().coda_gemm_rmsnorm_bwd(
         M, N, K, _ptr(dz), _ptr(Wt), _ptr(h), _ptr(q), _ptr(dh_res), _ptr(dh), _stream(stream)))
     return dh
@@ -257,11 +367,14 @@ def mlpin_bwd(h, Wp, Wpt, r, dy, dh_res=None, out=None, stream=None):
 def gemm_rowscale_gfold(h, W, gamma, r, act=SWIGLU, y=None, stream=None):
     """The second GEMM from the raw bf16 weight W with gamma folded in on chip
     (bit-identical to gemm_rowscale_swiglu with prepare_weight_bf16(W, gamma))."""
-    _esize(W, 2)
-    M, K = h.shape
-    n_w = W.shape[0]
+    M, K, n_w, dev = _second_gemm_operands(h, W, r, None)
+    _need(W, "W", (n_w, K), B16, dev)
+    _need(gamma, "gamma", (K,), F32, dev, optional=False)
+    if act == SWIGLU and n_w % 2:
+        raise ValueError("W: a SwiGLU weight needs an even number of rows")
     N_out = n_w // 2 if act == SWIGLU else n_w
-    y = torch.empty((M, N_out), dtype=torch.bfloat16, device=h.device) if y is None else y
+    _need(y, "y", (M, N_out), B16, dev)
+    y = torch.empty((M, N_out), dtype=torch.bfloat16, device=dev) if y is None else y
     _lib.check("coda_gemm_rowscale_gfold", _lib.load().coda_gemm_rowscale_gfold(
         M, N_out, K, act, _ptr(h), _ptr(W), _ptr(gamma), _ptr(r), _ptr(y), _stream(stream)))
     return y
@@ -270,10 +383,15 @@ def gemm_rowscale_gfold(h, W, gamma, r, act=SWIGLU, y=None, stream=None):
 def gemm_rowscale_swiglu_save(h, W, r, y=None, z=None, stream=None):
     """The SwiGLU second GEMM (bf16 W [2F, K]) that also keeps the pre-activation:
     returns (y [M, F], z [M, 2F] = r * (h . W^T) in bf16)."""
-    M, K = h.shape
-    F = W.shape[0] // 2
-    y = torch.empty((M, F), dtype=torch.bfloat16, device=h.device) if y is None else y
-    z = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=h.device) if z is None else z
+    M, K, F2, dev = _second_gemm_operands(h, W, r, None)
+    _need(W, "W", (F2, K), B16, dev)
+    if F2 % 2:
+        raise ValueError("W: a SwiGLU weight needs an even number of rows")
+    F = F2 // 2
+    _need(y, "y", (M, F), B16, dev)
+    _need(z, "z", (M, 2 * F), B16, dev)
+    y = torch.empty((M, F), dtype=torch.bfloat16, device=dev) if y is None else y
+    z = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev) if z is None else z
     _lib.check("coda_gemm_rowscale_swiglu_save", _lib.load().coda_gemm_rowscale_swiglu_save(
         M, F, K, _ptr(h), _ptr(W), _ptr(r), _ptr(y), _ptr(z), _stream(stream)))
     return y, z
@@ -282,13 +400,22 @@ def gemm_rowscale_swiglu_save(h, W, r, y=None, z=None, stream=None):
 def swiglu_bwd_saved(z, dy, r, dz=None, dzt=None, partials=None, transpose=True, stream=None):
     """SwiGLU backward from the saved z [M, 2F]: returns (dz [M, 2F] = r * dL/dz,
     dzt [2F, M] (its transpose; None with transpose=False), partials [M, T])."""
-    M, F2 = z.shape
+    M, F2 = _dims(z, "z", 2)
+    dev = z.device
+    if F2 % 2:
+        raise ValueError("z needs an even number of columns (gate, then up)")
     F = F2 // 2
     T = int(_lib.load().coda_swiglu_bwd_partials_per_row(F))
-    dz = torch.empty((M, F2), dtype=torch.bfloat16, device=z.device) if dz is None else dz
+    _need(z, "z", (M, F2), B16, dev)
+    _need(dy, "dy", (M, F), B16, dev, optional=False)
+    _need(r, "r", (M,), F32, dev, optional=False)
+    _need(dz, "dz", (M, F2), B16, dev)
+    _need(dzt if transpose else None, "dzt", (F2, M), B16, dev)
+    _need(partials, "partials", (M, T), F32, dev)
+    dz = torch.empty((M, F2), dtype=torch.bfloat16, device=dev) if dz is None else dz
     if transpose and dzt is None:
-        dzt = torch.empty((F2, M), dtype=torch.bfloat16, device=z.device)
-    partials = torch.empty((M, T), dtype=torch.float32, device=z.device) if partials is None else partials
+        dzt = torch.empty((F2, M), dtype=torch.bfloat16, device=dev)
+    partials = torch.empty((M, T), dtype=torch.float32, device=dev) if partials is None else partials
     _lib.check("coda_swiglu_bwd_saved", _lib.load().coda_swiglu_bwd_saved(
         M, F, _ptr(z), _ptr(dy), _ptr(r), _ptr(dz), _ptr(dzt if transpose else None), _ptr(partials),
         _stream(stream)))
@@ -299,13 +426,17 @@ def rope_bwd(dy, y, r, pos, cos, sin, rot_cols, dz=None, partials=None, stream=N
     """Backward of the RoPE epilogue from the forward's output y [M, N]: returns (dz
     [M, N] = r * RoPE^T(dy) in bf16, partials [M, T] = per 128-column tile
     (1/r) * sum of dy * y, the layout rmsnorm_bwd_reduce takes with F = N)."""
-    M, N = dy.shape
-    if pos is not None and pos.dtype != torch.int32:
-        raise ValueError("positions must be int32")
+    M, N = _dims(dy, "dy", 2)
+    dev = dy.device
+    _need(dy, "dy", (M, N), B16, dev)
+    _need(y, "y", (M, N), B16, dev, optional=False)
+    _need(r, "r", (M,), F32, dev, optional=False)
+    rows = _rope_operands(M, pos, cos, sin, dev)
     T = int(_lib.load().coda_swiglu_bwd_partials_per_row(N))
-    rows = 0 if cos is None else cos.shape[0]
-    dz = torch.empty((M, N), dtype=torch.bfloat16, device=dy.device) if dz is None else dz
-    partials = torch.empty((M, T), dtype=torch.float32, device=dy.device) if partials is None else partials
+    _need(dz, "dz", (M, N), B16, dev)
+    _need(partials, "partials", (M, T), F32, dev)
+    dz = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if dz is None else dz
+    partials = torch.empty((M, T), dtype=torch.float32, device=dev) if partials is None else partials
     _lib.check("coda_rope_bwd", _lib.load().coda_rope_bwd(
         M, N, _ptr(dy), _ptr(y), _ptr(r), _ptr(pos), _ptr(cos), _ptr(sin), rows, rot_cols, _ptr(dz),
         _ptr(partials), _stream(stream)))
@@ -330,16 +461,16 @@ def gemm_ce_bwd(h, W, r, targets, lse, g, dz=None, partials=None, stream=None):
     returns (dz [M, V] = r * g * (softmax - onehot) in bf16 (zero rows for ignored
     targets), partials [M, T] = per 128 columns sum of dL/dz * acc, the layout
     rmsnorm_bwd_reduce takes with F = V).  W [V, K] is the gamma-folded weight."""
-    _esize(W, 2)
-    M, K = h.shape
-    V = W.shape[0]
-    if W.shape[1] != K:
-        raise ValueError("h and W disagree on K")
-    if targets.dtype != torch.int32:
-        raise ValueError("targets must be int32")
+    M, K, V, dev = _second_gemm_operands(h, W, r, None)
+    _need(W, "W", (V, K), B16, dev)
+    _need(targets, "targets", (M,), I32, dev, optional=False)
+    _need(lse, "lse", (M,), F32, dev, optional=False)
+    _need(g, "g", (M,), F32, dev, optional=False)
     T = int(_lib.load().coda_swiglu_bwd_partials_per_row(V))
-    dz = torch.empty((M, V), dtype=torch.bfloat16, device=h.device) if dz is None else dz
-    partials = torch.empty((M, T), dtype=torch.float32, device=h.device) if partials is None else partials
+    _need(dz, "dz", (M, V), B16, dev)
+    _need(partials, "partials", (M, T), F32, dev)
+    dz = torch.empty((M, V), dtype=torch.bfloat16, device=dev) if dz is None else dz
+    partials = torch.empty((M, T), dtype=torch.float32, device=dev) if partials is None else partials
     _lib.check("coda_gemm_ce_bwd", _lib.load().coda_gemm_ce_bwd(
         M, V, K, _ptr(h), _ptr(W), _ptr(r), _ptr(targets), _ptr(lse), _ptr(g), _ptr(dz), _ptr(partials),
         _stream(stream)))
@@ -361,11 +492,16 @@ def lmhead_ce_bwd(h, r, Wp, Wpt, W, gamma, targets, lse, g, dh_res=None, out=Non
 
 def gemm_bf16(A, Bt, c_res=None, C=None, stream=None):
     """C [M, N] = A [M, K] . Bt [N, K]^T (+ c_res) in bf16 (fp32 sums)."""
-    _esize(A, 2)
-    _esize(Bt, 2)
-    M, K = A.shape
-    N = Bt.shape[0]
-    C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if C is None else C
+    M, K = _dims(A, "A", 2)
+    N, KB = _dims(Bt, "Bt", 2)
+    if KB != K:
+        raise ValueError("A and Bt disagree on K")
+    dev = A.device
+    _need(A, "A", (M, K), B16, dev)
+    _need(Bt, "Bt", (N, K), B16, dev)
+    _need(c_res, "c_res", (M, N), B16, dev)
+    _need(C, "C", (M, N), B16, dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if C is None else C
     _lib.check("coda_gemm_bf16", _lib.load().coda_gemm_bf16(
         M, N, K, _ptr(A), _ptr(Bt), _ptr(c_res), _ptr(C), _stream(stream)))
     return C
@@ -379,24 +515,41 @@ def wgrad_workspace_bytes(NR: int, NC: int, K: int) -> int:
     return int(_lib.load().coda_wgrad_workspace_bytes(NR, NC, K))
 
 
+def _wgrad_outputs(NR, NC, gamma, W, dW, partials, workspace, dev):
+    """Checks shared by the weight-gradient calls; returns (dW, partials) allocated where
+    the caller gave none."""
+    _need(gamma, "gamma", (NC,), F32, dev)
+    _need(W, "W", (NR, NC), B16, dev)
+    _need(dW, "dW", (NR, NC), F32, dev)
+    TW = wgrad_partials_rows(NR)
+    _need(partials if W is not None else None, "partials", (TW, NC), F32, dev)
+    if workspace is not None and not isinstance(workspace, str):
+        _need(workspace, "workspace", None, (torch.uint8,), dev)
+    dW = torch.empty((NR, NC), dtype=torch.float32, device=dev) if dW is None else dW
+    if W is not None and partials is None:
+        partials = torch.empty((TW, NC), dtype=torch.float32, device=dev)
+    return dW, partials
+
+
 def gemm_wgrad(At, Bt, gamma=None, W=None, dW=None, partials=None, workspace=None, stream=None):
     """dW [NR, NC] fp32 = gamma * (At . Bt^T), a sum over the K tokens of At [NR, K] and
     Bt [NC, K]; with the raw weight W [NR, NC] also the per-256-row-tile partials of the
     gamma gradient sum_j W[j,k] * G[j,k] (else partials is None).  A device
     ``workspace`` (uint8 tensor) of wgrad_workspace_bytes(NR, NC, K) bytes, when that is
     nonzero, lets the tokens be split over more blocks; workspace="auto" allocates it."""
-    _esize(At, 2)
-    _esize(Bt, 2)
-    NR, K = At.shape
-    NC = Bt.shape[0]
-    dW = torch.empty((NR, NC), dtype=torch.float32, device=At.device) if dW is None else dW
-    if W is not None and partials is None:
-        partials = torch.empty((wgrad_partials_rows(NR), NC), dtype=torch.float32, device=At.device)
+    NR, K = _dims(At, "At", 2)
+    NC, KB = _dims(Bt, "Bt", 2)
+    if KB != K:
+        raise ValueError("At and Bt disagree on K")
+    dev = At.device
+    _need(At, "At", (NR, K), B16, dev)
+    _need(Bt, "Bt", (NC, K), B16, dev)
+    dW, partials = _wgrad_outputs(NR, NC, gamma, W, dW, partials, workspace, dev)
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
         n = wgrad_workspace_bytes(NR, NC, K)
-        workspace = torch.empty(n, dtype=torch.uint8, device=At.device) if n > 0 else None
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n > 0 else None
     _lib.check("coda_gemm_wgrad", _lib.load().coda_gemm_wgrad(
         NR, NC, K, _ptr(At), _ptr(Bt), _ptr(gamma), _ptr(W), _ptr(dW),
         _ptr(partials) if W is not None else None, _ptr(workspace),
@@ -409,20 +562,23 @@ def gemm_wgrad_tok(X, Y, gamma=None, W=None, dW=None, partials=None, workspace=N
     """dW [NR, NC] fp32 = gamma * (X^T . Y), the sum over the K token rows of the token-major
     X [K, lda] (its first NR columns, default all) and Y [K, ldb] (first NC columns): the
     weight gradient without transposed copies.  W, partials and workspace as gemm_wgrad."""
-    _esize(X, 2)
-    _esize(Y, 2)
-    K, lda = X.shape
-    ldb = Y.shape[1]
+    K, lda = _dims(X, "X", 2)
+    KY, ldb = _dims(Y, "Y", 2)
+    if KY != K:
+        raise ValueError("X and Y disagree on the token count")
+    dev = X.device
+    _need(X, "X", (K, lda), B16, dev)
+    _need(Y, "Y", (K, ldb), B16, dev)
     NR = lda if NR is None else NR
     NC = ldb if NC is None else NC
-    dW = torch.empty((NR, NC), dtype=torch.float32, device=X.device) if dW is None else dW
-    if W is not None and partials is None:
-        partials = torch.empty((wgrad_partials_rows(NR), NC), dtype=torch.float32, device=X.device)
+    if not (0 < NR <= lda and 0 < NC <= ldb):
+        raise ValueError(f"NR, NC = {NR}, {NC} must lie in (0, {lda}] and (0, {ldb}]")
+    dW, partials = _wgrad_outputs(NR, NC, gamma, W, dW, partials, workspace, dev)
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be a tensor, None or 'auto'")
         n = int(_lib.load().coda_wgrad_tok_workspace_bytes(NR, NC, K, lda, ldb))
-        workspace = torch.empty(n, dtype=torch.uint8, device=X.device) if n > 0 else None
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n > 0 else None
     _lib.check("coda_gemm_wgrad_tok", _lib.load().coda_gemm_wgrad_tok(
         NR, NC, K, _ptr(X), lda, _ptr(Y), ldb, _ptr(gamma), _ptr(W), _ptr(dW),
         _ptr(partials) if W is not None else None, _ptr(workspace),
@@ -432,8 +588,11 @@ def gemm_wgrad_tok(X, Y, gamma=None, W=None, dW=None, partials=None, workspace=N
 
 def colsum_reduce(partials, out=None, stream=None):
     """out [NC] = sum over the rows of partials [T, NC] (fixed order, fp64 inside)."""
-    T, NC = partials.shape
-    out = torch.empty(NC, dtype=torch.float32, device=partials.device) if out is None else out
+    T, NC = _dims(partials, "partials", 2)
+    dev = partials.device
+    _need(partials, "partials", (T, NC), F32, dev)
+    _need(out, "out", (NC,), F32, dev)
+    out = torch.empty(NC, dtype=torch.float32, device=dev) if out is None else out
     _lib.check("coda_colsum_reduce", _lib.load().coda_colsum_reduce(T, NC, _ptr(partials), _ptr(out), _stream(stream)))
     return out
 

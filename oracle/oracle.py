@@ -25,7 +25,7 @@ ACT_SWIGLU = 1
 
 __all__ = ["build", "lib", "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode",
            "e4m3_encode", "fold_bf16", "quant_e4m3", "rope", "rope_transpose", "cross_entropy", "mlpin_bwd",
-           "mlpin_wgrad", "chain_bwd", "qkv_rope_bwd", "lmhead_ce_bwd", "chain", "prepare", "BF16", "E4M3",
+           "mlpin_wgrad", "chain_bwd", "qkv_rope_bwd", "lmhead_ce_bwd", "chain", "chain_textbook", "prepare", "BF16", "E4M3",
            "ACT_NONE", "ACT_SWIGLU"]
 
 
@@ -200,6 +200,41 @@ def chain(prep: dict, x_res, gamma, act: int, eps: float, rows=None, M: int | No
     if rc != 0:
         raise RuntimeError(f"oracle chain failed ({rc})")
     return dict(h=h, hb=hb, S=S, r=r, y=y)
+
+
+def chain_textbook(inputs: dict, act: int, eps: float, rows=None, round_h: bool = False) -> dict:
+    """The chain as a model defines it, before any reparameterisation or preparation:
+    the raw second weight, gamma inside RMSNorm, and (by default) no rounding of the
+    residual stream -- the reference the pages' numerics claim is about (kucoin page,
+    section "Resultados del experimento", last paragraph: the reparameterised chain's
+    error is comparable to the unfused PyTorch chain's, sometimes lower).  Plain fp64
+    numpy on the decoded bf16 inputs (the pre-quantisation ones for an 8-bit workload),
+    in the order the pages give the chain (kucoin, section "CODA: El epilogo esconde un
+    tesoro"):
+      t = A . Wo^T,  h = x_res + t            (round_h: h = bf16_rne(h), as the chain stores it)
+      r = 1 / sqrt(mean_n(h^2) + eps),  n = h * r * gamma
+      z = n . W^T                             (W the raw second weight, [N2w, d])
+      NONE: y = z;  SWIGLU: y = silu(z[:, :F]) * z[:, F:],  silu(g) = g / (1 + exp(-g))
+    Returns dict(h, r, y) for the listed rows (all rows by default)."""
+    A = inputs["A"] if rows is None else inputs["A"][rows]
+    xr = inputs["x_res"] if rows is None else inputs["x_res"][rows]
+    a = bf16_decode(A)
+    wo = bf16_decode(inputs["Wo_t"])
+    h = bf16_decode(xr) + a @ wo.T
+    if round_h:
+        h = bf16_decode(bf16_encode(h))
+    d = h.shape[1]
+    r = 1.0 / np.sqrt((h * h).sum(1) / d + eps)
+    n = h * r[:, None] * inputs["gamma"].astype(np.float64)[None, :]
+    z = n @ bf16_decode(inputs["W_t"]).T
+    if act == ACT_SWIGLU:
+        F = z.shape[1] // 2
+        g, u = z[:, :F], z[:, F:]
+        with np.errstate(over="ignore"):          # exp(-g) = inf for g << 0 gives silu = -0
+            y = g / (1.0 + np.exp(-g)) * u
+    else:
+        y = z
+    return dict(h=h, r=r, y=y)
 
 
 def rope(y: np.ndarray, pos, base: float, head_dim: int, rot_cols: int) -> np.ndarray:

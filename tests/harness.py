@@ -51,6 +51,15 @@ def gpu_prepare(w: si.Workload, d: dict) -> dict:
                 amax_scale=(sa, so, sw))
 
 
+def gpu_chain_gfold(w: si.Workload, d: dict, gamma=None):
+    """The bf16 chain with the second GEMM on the raw weight, gamma folded in on chip."""
+    g = d["gamma"] if gamma is None else gamma
+    h, P = coda.gemm_resid_partialrms(d["A"], d["Wo_t"], d["x_res"])
+    r = coda.rowscale_reduce(P, d["Wo_t"].shape[0], w.eps)
+    y = coda.gemm_rowscale_gfold(h, d["W_t"], g, r, act=w.act)
+    return h, P, r, y
+
+
 def gpu_chain(w: si.Workload, d: dict, prep: dict, x_res="x_res", h_out=None):
     xr = d[x_res] if isinstance(x_res, str) else x_res
     h, P, r, y = coda.chain(prep["A"], prep["Wo"], xr, prep["Wp"], w.eps, act=w.act,
@@ -75,7 +84,7 @@ def check_chain(w: si.Workload, inp: dict, h, P, r, y, rows=None, ref=None, prep
         prep_ref = oracle.prepare(inp, w.dtype)
     if ref is None:
         ref = oracle.chain(prep_ref, inp["x_res"], inp["gamma"], w.act, w.eps, rows=rows)
-    sel = slice(None) if rows is None else torch.from_numpy(rows).cuda()
+    sel = slice(None) if rows is None else torch.from_numpy(rows).to(h.device)
     hg = oracle.bf16_decode(host_bits(h[sel]))
     yg = oracle.bf16_decode(host_bits(y[sel]))
     Pg = P[sel].cpu().numpy().astype(np.float64)

@@ -1,10 +1,16 @@
-"""The second GEMM with the RMSNorm weight folded in on chip (raw bf16 weight + gamma):
-bit-identical to the same GEMM on the separately prepared W' = bf16(gamma * W), for the
-SwiGLU and plain epilogues, on ragged shapes (rows, columns and K not multiples of the
-tiles; gamma of mixed signs and magnitudes) and on the LLaMA-3-1B MLP-in shape.  The
-on-chip fold uses the preparation's arithmetic and the same MFMA order, so any
-difference is a mistake (a gamma of the wrong k, a stale per-tile gamma, a rounding
-that differs).
+"""The second GEMM with the RMSNorm weight folded in on chip (raw bf16 weight + gamma).
+
+Against the fp64 oracle: the chain with this GEMM as its second step matches the
+oracle's unfused chain on ragged shapes and on the LLaMA-3-1B MLP-in shape (sampled
+rows), for gamma drawn as the workloads draw it and over a wide range of signs and
+magnitudes.
+
+Against the library's other path: bit-identical to the same GEMM on the separately
+prepared W' = bf16(gamma * W), for the SwiGLU and plain epilogues, on ragged shapes
+(rows, columns and K not multiples of the tiles; gamma of mixed signs and magnitudes)
+and on the LLaMA-3-1B MLP-in shape.  The on-chip fold uses the preparation's arithmetic
+and the same MFMA order, so any difference is a mistake (a gamma of the wrong k, a
+stale per-tile gamma, a rounding that differs).
 """
 
 import numpy as np
@@ -13,7 +19,7 @@ import torch
 
 import gemm_epilogue_transformer_amd as coda
 import synth_inputs as si
-from harness import dev_bf16
+from harness import check_chain, dev_bf16, gpu_chain_gfold, sample_rows, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -49,3 +55,49 @@ def test_on_chip_fold_workload_shape():
     got = coda.gemm_rowscale_gfold(h, W, gamma, r)
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+# ---------------------------------------------------------------- against the oracle ----
+# The whole chain with the on-chip fold as its second GEMM, compared element by element
+# with the fp64 oracle's unfused chain (its own fold of the raw weight, the weight that
+# fold stands for = W' / gamma) at the bf16 tolerance 2e-2 (1 + |ref|).  gamma is drawn as
+# the workloads draw it (1 + 0.1 N(0, 1)) or over a wide range (mixed signs, magnitudes
+# 2^-4 .. 2^4 times N(0, 1)), where a gamma applied to the wrong k would show at once.
+
+def _wide_gamma(d: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(d) * np.exp2(rng.integers(-4, 5, d))).astype(np.float32)
+
+
+@pytest.mark.parametrize("gamma_kind", ["workload", "wide"])
+@pytest.mark.parametrize("M,K1,d,N2w,act", [(300, 136, 200, 2 * 104, si.ACT_SWIGLU),
+                                            (257, 72, 264, 392, si.ACT_NONE),
+                                            (513, 64, 1032, 2 * 136, si.ACT_SWIGLU),
+                                            (64, 16, 8, 16, si.ACT_NONE)])
+def test_on_chip_fold_chain_matches_oracle(M, K1, d, N2w, act, gamma_kind):
+    w = si.custom(M, K1, d, N2w, act, seed=M + d + N2w)
+    print(f"gfold chain vs oracle {w.name} gamma={gamma_kind}", flush=True)
+    inp = si.generate(w)
+    if gamma_kind == "wide":
+        inp["gamma"] = _wide_gamma(d, M + d)
+    dd = upload(inp)
+    h, P, r, y = gpu_chain_gfold(w, dd)
+    torch.cuda.synchronize()
+    stats = check_chain(w, inp, h, P, r, y)
+    print(f"  {stats}", flush=True)
+
+
+@pytest.mark.parametrize("gamma_kind", ["workload", "wide"])
+def test_on_chip_fold_workload_shape_matches_oracle(gamma_kind):
+    w = si.WORKLOADS[2]
+    print(f"gfold chain vs oracle {w.name} gamma={gamma_kind}: generating", flush=True)
+    inp = si.generate(w)
+    if gamma_kind == "wide":
+        inp["gamma"] = _wide_gamma(w.d, 2)
+    dd = upload(inp)
+    h, P, r, y = gpu_chain_gfold(w, dd)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.M, 48, seed=7)
+    print(f"  gpu done; oracle on {rows.size} sampled rows", flush=True)
+    stats = check_chain(w, inp, h, P, r, y, rows=rows)
+    print(f"  {stats}", flush=True)
