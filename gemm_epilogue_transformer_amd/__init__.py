@@ -26,7 +26,7 @@ __all__ = ["NONE", "SWIGLU", "CodaError", "prepare_weight_bf16", "quantize_e4m3"
            "gemm_rowscale_ce", "ce_reduce", "rowscale_from_h", "transpose_bf16", "gemm_swiglu_bwd", "rmsnorm_bwd_reduce",
            "gemm_rmsnorm_bwd", "mlpin_bwd", "wgrad_partials_rows", "gemm_wgrad", "colsum_reduce",
            "mlpin_wgrad", "gemm_bf16", "chain_bwd", "wgrad_workspace_bytes", "gemm_rowscale_swiglu_save",
-           "swiglu_bwd_saved", "gemm_rowscale_gfold", "gemm_wgrad_tok", "rope_bwd", "qkv_rope_bwd", "gemm_ce_bwd",
+           "swiglu_bwd_saved", "gemm_rowscale_gfold", "gemm_wgrad_tok", "gemm_wgrad_tok_noalloc", "rope_bwd", "qkv_rope_bwd", "gemm_ce_bwd",
            "lmhead_ce_bwd", "chain",
            "version"]
 
@@ -583,6 +583,28 @@ def gemm_wgrad_tok(X, Y, gamma=None, W=None, dW=None, partials=None, workspace=N
         NR, NC, K, _ptr(X), lda, _ptr(Y), ldb, _ptr(gamma), _ptr(W), _ptr(dW),
         _ptr(partials) if W is not None else None, _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dW, (partials if W is not None else None)
+
+
+def gemm_wgrad_tok_noalloc(X, Y, gamma=None, W=None, dW=None, partials=None, NR=None, NC=None, stream=None):
+    """gemm_wgrad_tok for callers that cannot allocate: the token split (when taken) runs
+    in the library's static per-device scratch instead of a workspace.  Bit-identical
+    to gemm_wgrad_tok with a sufficient workspace; calls that overlap on one GPU race."""
+    K, lda = _dims(X, "X", 2)
+    KY, ldb = _dims(Y, "Y", 2)
+    if KY != K:
+        raise ValueError("X and Y disagree on the token count")
+    dev = X.device
+    _need(X, "X", (K, lda), B16, dev)
+    _need(Y, "Y", (K, ldb), B16, dev)
+    NR = lda if NR is None else NR
+    NC = ldb if NC is None else NC
+    if not (0 < NR <= lda and 0 < NC <= ldb):
+        raise ValueError(f"NR, NC = {NR}, {NC} must lie in (0, {lda}] and (0, {ldb}]")
+    dW, partials = _wgrad_outputs(NR, NC, gamma, W, dW, partials, None, dev)
+    _lib.check("coda_gemm_wgrad_tok_noalloc", _lib.load().coda_gemm_wgrad_tok_noalloc(
+        NR, NC, K, _ptr(X), lda, _ptr(Y), ldb, _ptr(gamma), _ptr(W), _ptr(dW),
+        _ptr(partials) if W is not None else None, _stream(stream)))
     return dW, (partials if W is not None else None)
 
 

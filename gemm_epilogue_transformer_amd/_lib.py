@@ -47,6 +47,7 @@ SIGNATURES = {
     "coda_wgrad_workspace_bytes": (_I64, [_I64, _I64, _I64]),
     "coda_gemm_wgrad": (_I, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I64, _P]),
     "coda_gemm_wgrad_tok": (_I, [_I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _I64, _P]),
+    "coda_gemm_wgrad_tok_noalloc": (_I, [_I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P, _P, _P]),
     "coda_colsum_reduce": (_I, [_I64, _I64, _P, _P, _P]),
     "coda_status_string": (C.c_char_p, [_I]),
     "coda_last_hip_error": (_I, []),

@@ -13,6 +13,8 @@
 
 namespace {
 
+static_assert(CODA_NOALLOC_SCRATCH_BYTES == coda::kNoAllocScratchBytes, "the header states the scratch size");
+
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxDim = INT32_MAX;
@@ -508,15 +510,24 @@ coda_status coda_gemm_wgrad(int64_t NR, int64_t NC, int64_t K, const void* At, c
                                               static_cast<float*>(workspace), workspace_bytes, s));
 }
 
-coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda, const void* Y,
-                                int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
-                                void* workspace, int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of the token-major weight gradient shared by its two entry points: the caller's
+// workspace (caller_workspace), or the library's static scratch, which must hold the
+// split the call plans (else CODA_ERR_SHAPE, before anything is touched).
+coda_status check_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda, const void* Y,
+                            int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
+                            void* workspace, int64_t workspace_bytes, bool caller_workspace) {
     if (!dim_ok(NR, 1) || !dim_ok(NC, 1) || !dim_ok(K, 0)) return CODA_ERR_SHAPE;
     if (NC % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || lda < NR || ldb < NC) return CODA_ERR_SHAPE;
     if (lda > kMaxRow || ldb > kMaxRow || NC > kMaxRow / 2) return CODA_ERR_SHAPE;
     const int64_t T = coda::wgrad_partials_rows(NR);
     if (!prod_ok(NR, NC) || !prod_ok(T, NC)) return CODA_ERR_SHAPE;
     if (coda::wgrad_tiles(NR, NC) > kMaxDim) return CODA_ERR_SHAPE;
+    if (!caller_workspace && coda::wgrad_workspace_bytes(NR, NC, K) > coda::kNoAllocScratchBytes)
+        return CODA_ERR_SHAPE;
     if (!dW || (W && !partials) || (K > 0 && (!X || !Y))) return CODA_ERR_NULL;
     if (!aligned16(dW) || (W && !aligned16(W)) || (gamma && !aligned16(gamma)) || (partials && !aligned16(partials)) ||
         (K > 0 && (!aligned16(X) || !aligned16(Y))))
@@ -530,15 +541,42 @@ coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X
                          gamma ? span(gamma, NC * 4) : span(nullptr, 0), W ? span(W, NR * NC * 2) : span(nullptr, 0)};
     for (const Range& in : ins)
         if (overlap(ro, in) || (W && overlap(rp, in)) || overlap(rw, in)) return CODA_ERR_ALIAS;
+    return CODA_OK;
+}
+
+// K = 0: zeros in dW (and the partials); no scratch involved.
+coda_status wgrad_zero(int64_t NR, int64_t NC, const void* W, float* dW, float* partials, hipStream_t s) {
+    hipError_t e = coda::launch_fill_zero_f32(NR * NC, dW, s);
+    if (e == hipSuccess && W) e = coda::launch_fill_zero_f32(coda::wgrad_partials_rows(NR) * NC, partials, s);
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda, const void* Y,
+                                int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
+    const coda_status st = check_wgrad_tok(NR, NC, K, X, lda, Y, ldb, gamma, W, dW, partials, workspace,
+                                           workspace_bytes, true);
+    if (st != CODA_OK) return st;
     hipStream_t s = as_stream(stream);
-    if (K == 0) {
-        hipError_t e = coda::launch_fill_zero_f32(NR * NC, dW, s);
-        if (e == hipSuccess && W) e = coda::launch_fill_zero_f32(T * NC, partials, s);
-        return hip_status(e);
-    }
+    if (K == 0) return wgrad_zero(NR, NC, W, dW, partials, s);
     return hip_status(coda::launch_gemm_wgrad_tok(int(NR), int(NC), int(K), X, int(lda), Y, int(ldb), gamma, W, dW,
                                                   W ? partials : nullptr, static_cast<float*>(workspace),
                                                   workspace_bytes, s));
+}
+
+coda_status coda_gemm_wgrad_tok_noalloc(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda,
+                                        const void* Y, int64_t ldb, const float* gamma, const void* W, float* dW,
+                                        float* partials, void* stream) {
+    const coda_status st = check_wgrad_tok(NR, NC, K, X, lda, Y, ldb, gamma, W, dW, partials, nullptr, 0, false);
+    if (st != CODA_OK) return st;
+    hipStream_t s = as_stream(stream);
+    if (K == 0) return wgrad_zero(NR, NC, W, dW, partials, s);
+    return hip_status(coda::launch_gemm_wgrad_tok_noalloc(int(NR), int(NC), int(K), X, int(lda), Y, int(ldb), gamma,
+                                                          W, dW, W ? partials : nullptr, s));
 }
 
 coda_status coda_colsum_reduce(int64_t T, int64_t NC, const float* partials, float* out, void* stream) {

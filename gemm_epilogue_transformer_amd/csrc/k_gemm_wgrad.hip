@@ -16,6 +16,7 @@
 // lane takes runs of 8 columns; the column sums run over the lane's rows, the 4 lanes
 // holding the same columns, then the waves sharing them, in a fixed order.
 #include <algorithm>
+#include <mutex>
 
 #include "epilogue.hpp"
 #include "gemm_pipeline.hpp"
@@ -339,6 +340,48 @@ hipError_t launch_gemm_wgrad_tok(int NR, int NC, int K, const void* X, int lda, 
                                  const float* gamma, const void* Wraw, float* dW, float* Pg, float* ws,
                                  int64_t ws_bytes, hipStream_t stream) {
     return launch_wgrad<true>(NR, NC, K, X, lda, Y, ldb, gamma, Wraw, dW, Pg, ws, ws_bytes, stream);
+}
+
+// Scratch of the allocation-free entry point: the token split's dW slices and partial
+// slices, in a file-scope device array of kNoAllocScratchBytes that every GPU the library
+// runs on holds from the module's load to the end of the process.  In host code the
+// array's name is only a host-side stand-in; its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that address is used.
+// Calls on one device share the array: two such calls that overlap in time race.  Every
+// element the split reduce reads is written by the GEMM of the same call first, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / 4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(float** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<float*>(g_scratch_ptr[dev]);
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_gemm_wgrad_tok_noalloc(int NR, int NC, int K, const void* X, int lda, const void* Y, int ldb,
+                                         const float* gamma, const void* Wraw, float* dW, float* Pg,
+                                         hipStream_t stream) {
+    float* ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    return launch_wgrad<true>(NR, NC, K, X, lda, Y, ldb, gamma, Wraw, dW, Pg, ws, kNoAllocScratchBytes, stream);
 }
 
 hipError_t launch_colsum_reduce(int T, int NC, const float* Pg, float* out, hipStream_t stream) {

@@ -90,6 +90,13 @@ hipError_t launch_gemm_wgrad(int NR, int NC, int K, const void* At, const void* 
 hipError_t launch_gemm_wgrad_tok(int NR, int NC, int K, const void* X, int lda, const void* Y, int ldb,
                                  const float* gamma, const void* Wraw, float* dW, float* Pg, float* ws,
                                  int64_t ws_bytes, hipStream_t stream);
+// The same, with the token split's slices in the library's static per-device scratch
+// (kNoAllocScratchBytes) instead of a caller workspace: nothing is allocated.  The
+// caller has checked wgrad_workspace_bytes(NR, NC, K) <= kNoAllocScratchBytes.
+constexpr int64_t kNoAllocScratchBytes = int64_t(128) << 20;
+hipError_t launch_gemm_wgrad_tok_noalloc(int NR, int NC, int K, const void* X, int lda, const void* Y, int ldb,
+                                         const float* gamma, const void* Wraw, float* dW, float* Pg,
+                                         hipStream_t stream);
 hipError_t launch_colsum_reduce(int T, int NC, const float* Pg, float* out, hipStream_t stream);
 hipError_t launch_fill_zero_f32(int64_t n, float* dst, hipStream_t stream);
 

@@ -447,6 +447,22 @@ coda_status coda_gemm_wgrad_tok(int64_t NR, int64_t NC, int64_t K, const void* X
                                 int64_t ldb, const float* gamma, const void* W, float* dW, float* partials,
                                 void* workspace, int64_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): coda_gemm_wgrad_tok without the
+ * workspace arguments.  The token split, when the call's plan takes one, keeps its
+ * slices in a static device array of the library (CODA_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's load to the end of the process); nothing is allocated, freed
+ * or cleared by the call.  Arguments, result and determinism as coda_gemm_wgrad_tok
+ * with a sufficient workspace (bit-identical to it).
+ * CODA_ERR_SHAPE (nothing enqueued) when coda_wgrad_workspace_bytes(NR, NC, K) exceeds
+ * CODA_NOALLOC_SCRATCH_BYTES, besides the checks of coda_gemm_wgrad_tok.
+ * Calls on the same GPU share the array: two calls that overlap in time (on different
+ * streams, or from different threads without ordering) race and give wrong results.  */
+#define CODA_NOALLOC_SCRATCH_BYTES (128ll << 20)
+coda_status coda_gemm_wgrad_tok_noalloc(int64_t NR, int64_t NC, int64_t K, const void* X, int64_t lda,
+                                        const void* Y, int64_t ldb, const float* gamma, const void* W, float* dW,
+                                        float* partials, void* stream);
+
 /* The block reduction's final sum (cited above):
  * out[k] = fl32( sum_t partials[t, k] )  (fixed order, fp64 inside), T >= 1 rows of NC
  * columns: the gamma gradient from coda_gemm_wgrad's partials.  out must not overlap.  */
