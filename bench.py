@@ -841,6 +841,251 @@ def bench_ce_backward(w, args) -> dict:
     return rec
 
 
+class ClockSampler:
+    """The GPU's graphics clock (MHz) from the firmware's metrics table (amdsmi gpu
+    metrics: ``average_gfxclk_frequency``, and the mean over the XCDs of
+    ``current_gfxclks``), sampled in a background thread while a loop runs;
+    ``result()`` gives mean / min / max of the samples, or the reason none could be
+    read.  (The DPM "current clock" amdsmi also reports shows the selected level, not the
+    clock the chip holds under its power limit.)"""
+
+    def __init__(self, interval_s: float = 0.005):
+        import threading
+
+        self.samples, self.cur_samples, self.error, self.handle = [], [], None, None
+        self._stop = threading.Event()
+        self._thread = None
+        self._interval = interval_s
+        try:
+            import amdsmi
+            import torch
+
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            handles = amdsmi.amdsmi_get_processor_handles()
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # dddd:bb:dd.f
+                if int(bdf.split(":")[1], 16) == bus:
+                    self.handle = h
+            if self.handle is None and len(handles) == 1:
+                self.handle = handles[0]
+            if self.handle is None:
+                self.error = f"no amdsmi device on PCI bus {bus:#x}"
+        except Exception as e:  # noqa: BLE001 -- a missing clock is reported, not fatal
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        avg = m.get("average_gfxclk_frequency")
+        cur = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        ok = lambda v: isinstance(v, (int, float)) and 0 < v < 10000  # noqa: E731
+        return (float(avg) if ok(avg) else None), (sum(cur) / len(cur) if cur else None)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                avg, cur = self._read()
+                if avg is not None:
+                    self.samples.append(avg)
+                if cur is not None:
+                    self.cur_samples.append(cur)
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self._interval)
+
+    def __enter__(self):
+        import threading
+
+        if self.handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def result(self) -> dict:
+        import numpy as np
+
+        out = {}
+        for key, smp in (("average_gfxclk", self.samples), ("current_gfxclks_xcd_mean", self.cur_samples)):
+            if smp:
+                a = np.array(smp)
+                # consecutive equal readings are one firmware update
+                distinct = [float(v) for i, v in enumerate(smp) if i == 0 or v != smp[i - 1]]
+                out[key] = {"mhz_mean": round(float(a.mean()), 1), "mhz_min": round(float(a.min()), 1),
+                            "mhz_max": round(float(a.max()), 1), "samples": int(a.size),
+                            "readings": [round(v, 1) for v in distinct[:12]]}
+        if not out:
+            return {"mhz_mean": None, "error": self.error or "no samples"}
+        out["source"] = ("amdsmi gpu metrics (firmware-reported graphics clock), sampled every 5 ms during "
+                         "the loop; readings below ~500 MHz are idle moments between dispatches")
+        return out
+
+
+def timing_stats(ms: list) -> dict:
+    import numpy as np
+
+    a = np.array(ms, dtype=np.float64)
+    return {"n": int(a.size), "median_ms": round(float(np.median(a)), 4), "min_ms": round(float(a.min()), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "mean_ms": round(float(a.mean()), 4)}
+
+
+def numerics_o1(w, inp, y_fused, y_unfused, h_fused, rows) -> dict:
+    """Error of the fused chain and of the unfused torch chain against the chain as a
+    model defines it (raw second weight, gamma inside RMSNorm, unrounded residual
+    stream, fp64: oracle.chain_textbook), on the sampled rows.  Per output y: max and
+    rms of |y - ref| / (1 + |ref|) and rms of |y - ref| / rms(ref)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    ref = oracle.chain_textbook(inp, w.act, w.eps, rows=rows)
+    dec = lambda t: oracle.bf16_decode(t.view(torch.int16).cpu().numpy().view(np.uint16))  # noqa: E731
+    out = {"rows": int(rows.size), "reference": "fp64, raw second weight, gamma in RMSNorm, h unrounded"}
+    yr = ref["y"]
+    scale = float(np.sqrt(np.mean(yr * yr)))
+    for name, y in (("fused", y_fused), ("unfused_torch", y_unfused)):
+        if y is None:
+            continue
+        yg = dec(y)
+        rel = np.abs(yg - yr) / (1 + np.abs(yr))
+        out[name] = {"y_max_rel": float(f"{rel.max():.4e}"), "y_rms_rel": float(f"{np.sqrt(np.mean(rel ** 2)):.4e}"),
+                     "y_rms_over_rms_ref": float(f"{np.sqrt(np.mean((yg - yr) ** 2)) / scale:.4e}")}
+    if h_fused is not None:
+        hr = ref["h"]
+        eh = np.abs(dec(h_fused) - hr) / (1 + np.abs(hr))
+        out["fused"]["h_max_rel"] = float(f"{eh.max():.4e}")
+    return out
+
+
+def forward_summary(w, inp, args, numerics_rows: int = 512) -> dict:
+    """One forward workload (NONE or SwiGLU second GEMM), compact: each of
+    ``args.stat_steps`` chains timed on its own with HIP events (median / min / p90, and
+    per kernel the median), the GPU clock during that loop, the dominant kernel's
+    roofline against its own dtype's dense MFMA peak, the algorithmic HBM bytes of the
+    fused and the unfused chain, the unfused torch chain's time, and the O1 numerics
+    diagnostic on sampled rows."""
+    import numpy as np
+    import torch
+
+    import gemm_epilogue_transformer_amd as coda
+    import synth_inputs as si
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+    A, Wo, xr, W = dev(inp["A"]), dev(inp["Wo_t"]), dev(inp["x_res"]), dev(inp["W_t"])
+    gamma = torch.from_numpy(inp["gamma"]).cuda()
+    if w.dtype == "bf16":
+        Wp = coda.prepare_weight_bf16(W, gamma)
+        a_in, wo_in, sa, so, sw = A, Wo, None, None, None
+    else:
+        a_in, sa2 = coda.quantize_e4m3(A)
+        wo_in, so2 = coda.quantize_e4m3(Wo)
+        Wp, sw2 = coda.quantize_e4m3(W, gamma)
+        sa, so, sw = sa2[1:], so2[1:], sw2[1:]
+    M, d = w.M, w.d
+    out = {"h": torch.empty((M, d), dtype=torch.bfloat16, device="cuda"),
+           "partials": torch.empty((M, coda.partials_per_row(d)), dtype=torch.float32, device="cuda"),
+           "r": torch.empty(M, dtype=torch.float32, device="cuda"),
+           "y": torch.empty((M, w.n_out), dtype=torch.bfloat16, device="cuda")}
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        coda.gemm_resid_partialrms(a_in, wo_in, xr, sa, so, out["h"], out["partials"])
+        if ev is not None:
+            ev[1].record(stream)
+        coda.rowscale_reduce(out["partials"], d, w.eps, out["r"])
+        if ev is not None:
+            ev[2].record(stream)
+        coda.gemm_rowscale_swiglu(out["h"], Wp, out["r"], w.act, sw, out["y"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(max(args.warmup, 3)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    # at least stat_steps chains, and at least a second of them (the firmware's clock
+    # readings change only every few hundred ms)
+    n = max(args.stat_steps, int(1.0 / max(time.perf_counter() - t0, 1e-4)))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    with ClockSampler() as clk:
+        for i in range(n):
+            step(evs[i])
+        torch.cuda.synchronize()
+    chain_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    k_ms = [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(3)]
+    med = [float(np.median(k)) for k in k_ms]
+    g1 = 2 * M * w.K1 * d
+    g2 = 2 * M * d * w.N2w
+    # the first GEMM runs on the 8-bit MFMA for the e4m3 workload, the second always on bf16
+    kern = [("gemm_resid_partialrms", g1, "e4m3" if w.dtype == "e4m3" else "bf16"),
+            ("gemm_rowscale_swiglu", g2, "bf16")]
+    dom = 0 if med[0] > med[2] else 1
+    name, fl, dt = kern[dom]
+    kms = med[0] if dom == 0 else med[2]
+    ach = fl / (kms * 1e-3) / 1e12
+    byt = algorithmic_bytes(w)
+    rec = {"workload": w.name, "M": M, "K1": w.K1, "d": d, "N2w": w.N2w,
+           "act": "swiglu" if w.act == si.ACT_SWIGLU else "none", "dtype": w.dtype,
+           "timing": timing_stats(chain_ms),
+           "tflops_median": round(w.gemm_flops / (np.median(chain_ms) * 1e-3) / 1e12, 2),
+           "frac_of_bf16_peak_median": round(w.gemm_flops / (np.median(chain_ms) * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+                                             4),
+           "kernels_ms_median": {"gemm_resid_partialrms": round(med[0], 4), "rowscale_reduce": round(med[1], 4),
+                                 "gemm_rowscale_swiglu": round(med[2], 4)},
+           "gemm1_tflops_median": round(g1 / (med[0] * 1e-3) / 1e12, 1),
+           "gemm2_tflops_median": round(g2 / (med[2] * 1e-3) / 1e12, 1),
+           "roofline": {"bound": "mfma", "kernel": name, "dtype": dt, "achieved": round(ach, 1),
+                        "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[dt], 4),
+                        "kernel_ms_median": round(kms, 4)},
+           "clock": clk.result(),
+           "hbm_bytes_algorithmic": {"fused": byt["total"], "unfused": algorithmic_bytes(w, False)["total"]}}
+
+    # the unfused torch chain (hipBLASLt GEMMs, element-wise residual, RMSNorm, SwiGLU),
+    # on the same bf16 inputs (the 8-bit workload: its bf16 source tensors)
+    def unfused():
+        t = A @ Wo.t()
+        hh = xr + t
+        hf = hh.float()
+        nn_ = (hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + w.eps)).to(torch.bfloat16) \
+            * gamma.to(torch.bfloat16)
+        z = nn_ @ W.t()
+        if w.act == si.ACT_SWIGLU:
+            return torch.nn.functional.silu(z[:, : w.n_out]) * z[:, w.n_out:]
+        return z
+
+    y_unf = unfused()
+    torch.cuda.synchronize()
+    if w.dtype == "bf16":
+        ue = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(min(n, 30))]
+        for e in ue:
+            e[0].record(stream)
+            unfused()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        ums = float(np.median([e[0].elapsed_time(e[1]) for e in ue]))
+        rec["unfused_torch"] = {"median_ms": round(ums, 4), "speedup_of_fused": round(ums / np.median(chain_ms), 3),
+                                "steps": len(ue)}
+    if numerics_rows > 0:
+        rng = np.random.default_rng(w.seed)
+        rows = np.sort(rng.choice(M, size=min(numerics_rows, M), replace=False))
+        sel = torch.from_numpy(rows).cuda()
+        rec["numerics_o1"] = numerics_o1(w, inp, out["y"][sel], y_unf[sel], out["h"][sel], rows)
+    del A, Wo, xr, W, Wp, out, y_unf
+    torch.cuda.empty_cache()
+    return rec
+
+
 def _oracle_path(oracle, prep, inp, w, rows):
     """The oracle's whole path for the rows: the chain, then RoPE or the loss."""
     import synth_inputs as si
@@ -854,13 +1099,23 @@ def _oracle_path(oracle, prep, inp, w, rows):
     return ref
 
 
-def cpu_baseline(w, inp, target_s: float) -> dict:
+def cpu_baseline(w, inp, target_s: float, rows_all: bool = True) -> dict:
+    """The oracle timed on the host cores: on every row of the workload in one call
+    (rows_all), else on a random row sample grown until one call takes about target_s."""
     import numpy as np
 
     import oracle
 
     prep = oracle.prepare(inp, w.dtype)
     per_row = 2 * (w.K1 * w.d + w.d * w.N2w)
+    if rows_all:
+        t0 = time.perf_counter()
+        _oracle_path(oracle, prep, inp, w, np.arange(w.M, dtype=np.int64))
+        dt = time.perf_counter() - t0
+        return {"value": round(w.M * per_row / dt / 1e12, 6), "unit": "TFLOP/s",
+                "cores": oracle.max_threads(), "kind": "oracle",
+                "sample": f"all {w.M} rows of the workload in one oracle call (fp64, includes its weight "
+                          f"decode), {dt:.1f} s"}
     rng = np.random.default_rng(0)
     # grow the sample until one call takes >= 1/4 of the target, then size it to the target
     n, dt = 8, 0.0
@@ -892,6 +1147,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="workload number (1-11)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-sample", action="store_true",
+                    help="time the oracle on a row sample (about --cpu-seconds) instead of every row")
+    ap.add_argument("--stat-steps", type=int, default=100,
+                    help="forward workloads: chains timed one by one for median / min / p90 (after the K steps)")
+    ap.add_argument("--numerics-rows", type=int, default=512,
+                    help="rows sampled for the numerics diagnostic against the textbook definition (0: none)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="workload 2: skip the summaries of workloads 3, 4 and 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true", help="also time the unfused torch chain")
     ap.add_argument("--graph", action="store_true",
@@ -1150,8 +1413,29 @@ def main():
                                 "tflops": round(flops / (ums * 1e-3) / 1e12, 2),
                                 "speedup_of_fused": round(ums / ms_per_step, 3)}
 
+    if w.act in (si.ACT_NONE, si.ACT_SWIGLU) and args.stat_steps > 0:
+        # the same workload, each chain timed on its own, with the clock and the numerics
+        # diagnostic; then (default workload) the other 16K-token forward configurations
+        del out
+        torch.cuda.empty_cache()
+        summ = forward_summary(w, inp, args, args.numerics_rows)
+        for k in ("timing", "clock", "numerics_o1", "kernels_ms_median"):
+            if k in summ:
+                rec[k] = summ[k]
+        if "unfused_torch" in summ:
+            rec.setdefault("unfused_torch", summ["unfused_torch"])
+        if args.workload == 2 and not args.no_configs:
+            rec["configs"] = {}
+            for c in (3, 4, 5):
+                wc = si.WORKLOADS[c]
+                print(f"bench.py: summary of workload {c} ({wc.name})", file=sys.stderr, flush=True)
+                inp_c = inp if (wc.seed == w.seed and wc.M == w.M and wc.K1 == w.K1 and wc.d == w.d
+                                and wc.N2w == w.N2w) else si.generate(wc)
+                rec["configs"][wc.name] = forward_summary(wc, inp_c, args, args.numerics_rows)
+                del inp_c
+
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds, rows_all=not args.cpu_sample)
     print(json.dumps(rec), flush=True)
 
 

