@@ -95,8 +95,6 @@ struct DmaPanel {
     uint32_t off0;            // byte offset of this lane's chunk in instruction 0 at k-tile 0
     uint32_t chunk_byte;      // 16 * the chunk this lane fetches
     uint32_t stride;          // bytes between instruction j and j+1, wave-uniform
-    int krev;                 // 0: k-tiles in order; else the k-tile the mainloop's tile kt
-                              // loads is krev - kt (the k range walked backwards)
 
     // seg_base[s]: address of the segment's first row; seg_rows[s]: rows of the segment that
     // exist in the matrix (the descriptor range); kbytes: bytes of one matrix row.
@@ -115,19 +113,14 @@ struct DmaPanel {
         chunk_byte = static_cast<uint32_t>(chunk) << 4;
         off0 = static_cast<uint32_t>(r) * kbytes + chunk_byte;
         stride = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kRowsPerInst) * static_cast<uint32_t>(kbytes));
-        krev = 0;
     }
-    // Walk the k range backwards: tile kt of the mainloop loads k-tile last - kt, where
-    // last = the mainloop's padded k-tile count - 1 (k-tiles past K and before 0 read zeros).
-    __device__ __forceinline__ void reverse_k(int last) { krev = __builtin_amdgcn_readfirstlane(last); }
 
     // Offset of this lane's chunk for k-tile kt (kOob past K): a chunk past K starts from
     // kOob, and kOob + jj*stride stays beyond every range (each descriptor spans < 2^31
     // bytes), so the whole lane reads zeros.
     __device__ __forceinline__ uint32_t base_offset(int kt, int kbytes) const {
-        if (krev) kt = krev - kt;                     // wave-uniform; below 0: zeros
         const uint32_t kb = static_cast<uint32_t>(kt) * RB;
-        const bool kin = kt >= 0 && kb + chunk_byte < static_cast<uint32_t>(kbytes);
+        const bool kin = kb + chunk_byte < static_cast<uint32_t>(kbytes);
         uint32_t base = kin ? off0 + kb : kOob;
         // keep the per-instruction offsets derived at their use (not kInst live registers)
         asm volatile("" : "+v"(base));

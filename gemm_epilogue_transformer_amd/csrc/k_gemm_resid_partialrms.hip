@@ -144,7 +144,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #define CODA_G1_OCC 1
 #endif
 #ifndef CODA_G1_SPREAD
-#define CODA_G1_SPREAD 2
+#define CODA_G1_SPREAD 3
 #endif
 constexpr int BM1 = CODA_G1_BM, BN1 = CODA_G1_BN, NS1 = CODA_G1_NS, OCC1 = CODA_G1_OCC;
 constexpr int RB1 = CODA_G1_RB;

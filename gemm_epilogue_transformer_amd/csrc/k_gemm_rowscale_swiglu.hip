@@ -22,15 +22,15 @@
 // 8-bit weights (weight-only): W is e4m3 in HBM and in LDS (half the bytes of a bf16
 // panel) and is converted exactly to bf16 in registers after the LDS read; the MFMA is
 // the bf16 one and sw is applied in the epilogue.
+#include <algorithm>
+#include <atomic>
+
 #include "epilogue.hpp"
 #include "gemm_pipeline.hpp"
 #include "launch.hpp"
 
 #ifndef CODA_G3_TC
 #define CODA_G3_TC 1      // 0: the forward SwiGLU epilogue stages through LDS like the others
-#endif
-#ifndef CODA_G3_SERP
-#define CODA_G3_SERP 1    // the persistent GEMM walks k backwards on every other tile (0: always forwards)
 #endif
 #ifndef CODA_G3_TC_CE
 #define CODA_G3_TC_CE 1   // the loss statistics and their backward from transposed blocks too
@@ -940,10 +940,6 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
 // t mod 8).  The epilogue touches no LDS, so the next tile's first k-tiles are issued
 // into the stages right after the mainloop's drain, and their latency hides behind the
 // epilogue's arithmetic and stores; the row scales of the next tile are loaded there too.
-// Every other tile of a workgroup walks k backwards: consecutive tiles on an XCD share
-// their rows of h, so the k-tiles the previous pass over those rows fetched last are the
-// first ones needed, while they are still in the XCD's L2 (7.6 % fewer L2-miss bytes on
-// the LLaMA-3-1B MLP-in shape, same time).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
 k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
@@ -993,13 +989,6 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
         const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes;
         const uint8_t* u0 = W + static_cast<size_t>(N_out + j0) * kbytes;
         pb.init(g0, min(BN / 2, N_out - j0), u0, min(BN / 2, N_out - j0), kbytes);
-        if (CODA_G3_SERP && ((t / static_cast<int>(gridDim.x)) & 1)) {
-            // every other tile of a workgroup walks k backwards: it starts on the k-tiles
-            // its predecessor (on the same XCD, same rows) fetched last
-            const int nkp = ((kbytes + RB - 1) / RB + NS - 1) / NS * NS;
-            pa.reverse_k(nkp - 1);
-            pb.reverse_k(nkp - 1);
-        }
     };
     const float sw = w_scale ? *w_scale : 1.0f;
     int t = blockIdx.x;                              // the grid holds at most ntiles workgroups
@@ -1039,7 +1028,7 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
 #define CODA_G3_OCC 1
 #endif
 #ifndef CODA_G3_SPREAD
-#define CODA_G3_SPREAD 2
+#define CODA_G3_SPREAD 3
 #endif
 #ifndef CODA_G3_PIPE
 #define CODA_G3_PIPE 0
@@ -1058,6 +1047,27 @@ constexpr int NS3_8 = CODA_G3_NS8;
 int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
     const int64_t bno = swiglu ? BN3 / 2 : BN3;
     return ((M + BM3 - 1) / BM3) * ((N_out + bno - 1) / bno);
+}
+
+// Compute units of the current device, queried once per device (the persistent grid size).
+static hipError_t cu_count(int* cus) {
+    static std::atomic<int> cache[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return hipSuccess;
+        }
+    }
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) cache[dev].store(c, std::memory_order_relaxed);
+    *cus = c;
+    return hipSuccess;
 }
 
 template <int ACT, bool WFP8, bool GFOLD = false>
@@ -1096,9 +1106,8 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
     const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
     if (swiglu && !w_fp8 && CODA_G3_PERSIST && CODA_G3_TC && PIPE3 == 0) {
         const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BN3 / 2 - 1) / (BN3 / 2);
-        int dev = 0, cus = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        int cus = 0;
+        const hipError_t e = cu_count(&cus);
         if (e != hipSuccess) return e;
         const int grid = std::min(tiles_m * tiles_n, std::max(cus, 1));
         hipLaunchKernelGGL((k_gemm_swiglu_persistent<BM3, BN3, WM3, WN3, NS3, RB3, SP3>), dim3(grid),
