@@ -41,7 +41,9 @@ def sources():
 
 
 def build(verbose: bool = False, save_temps: bool = False, defines=(), out: str = LIB,
-          build_dir: str = BUILD) -> str:
+          build_dir: str = BUILD, host_flags=()) -> str:
+    """Compile and link; host_flags (e.g. the tests' host-only sanitizer options, each
+    preceded by -Xarch_host) go on every compile and on the link line."""
     hipcc = _hipcc()
     os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
@@ -49,7 +51,7 @@ def build(verbose: bool = False, save_temps: bool = False, defines=(), out: str 
 
     def compile_one(src):
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, *(f"-D{d}" for d in defines), "-c", src, "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *host_flags, *(f"-D{d}" for d in defines), "-c", src, "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         if save_temps:
@@ -68,7 +70,7 @@ def build(verbose: bool = False, save_temps: bool = False, defines=(), out: str 
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(compile_one, srcs))
     tmp = out + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *host_flags, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

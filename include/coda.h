@@ -47,7 +47,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the enumerations get int as their fixed underlying type, so that any int a C
+ * caller passes (a value outside the enumerators included) is a valid value of the
+ * parameter's type and is rejected by the checks instead of being undefined. */
+#ifdef __cplusplus
+#define CODA_ENUM_INT : int
+#else
+#define CODA_ENUM_INT
+#endif
+
+typedef enum CODA_ENUM_INT {
     CODA_OK = 0,
     CODA_ERR_NULL = 1,   /* a required pointer is NULL                                   */
     CODA_ERR_SHAPE = 2,  /* a dimension is negative, zero where >= 1 is needed, too large,
@@ -60,8 +69,8 @@ typedef enum {
     CODA_ERR_ALIGN = 7   /* a tensor pointer is not 16-byte aligned                       */
 } coda_status;
 
-typedef enum { CODA_BF16 = 0, CODA_E4M3 = 1 } coda_dtype;
-typedef enum { CODA_ACT_NONE = 0, CODA_ACT_SWIGLU = 1 } coda_act;
+typedef enum CODA_ENUM_INT { CODA_BF16 = 0, CODA_E4M3 = 1 } coda_dtype;
+typedef enum CODA_ENUM_INT { CODA_ACT_NONE = 0, CODA_ACT_SWIGLU = 1 } coda_act;
 
 /* ------------------------------------------------------------ weight preparation ----
  * The RMSNorm weight gamma multiplies the second GEMM's reduction dimension, so it is

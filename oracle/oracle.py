@@ -16,7 +16,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "coda_oracle.c")
-_LIB = os.path.join(_HERE, "liborcl.so")
+# ORC_LIB: a separately built copy (the sanitizer build of the tests) is loaded as is
+_LIB = os.environ.get("ORC_LIB") or os.path.join(_HERE, "liborcl.so")
 
 BF16 = 0
 E4M3 = 1
@@ -45,7 +46,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build(force=False)
+        if not os.environ.get("ORC_LIB"):
+            build(force=False)
         L = C.CDLL(_LIB)
         P = C.c_void_p
         i64 = C.c_int64
