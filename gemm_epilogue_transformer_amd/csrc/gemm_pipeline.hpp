@@ -521,6 +521,15 @@ __device__ __forceinline__ auto mainloop_dma_prologue(const PA& pa, const PB& pb
     return pend;
 }
 
+// Extra loads a kernel issues once per k-tile of the pipelined mainloop, kOps vector
+// memory instructions every k-tile (for instance a prefetch of the epilogue's operand).
+// They go out in the k-step after the previous tile's DMA batch is complete, so the
+// tile-end wait allows them to be in flight.  NoExtra: none.
+struct NoExtra {
+    static constexpr int kOps = 0;
+    __device__ __forceinline__ void issue(int /*kt*/, int /*nk*/) const {}
+};
+
 // The rest of the pipelined mainloop after mainloop_dma_prologue: wait for k-tile 0, the
 // k-loop, and the drain of the DMA that ran past the end.  The first wait, vmcnt
 // <= (NS-2) kPerTile + kPer, is exact when only the prologue's DMA was issued after
@@ -528,10 +537,10 @@ __device__ __forceinline__ auto mainloop_dma_prologue(const PA& pa, const PB& pb
 // only make it wait longer: loads complete in order, so while any load of k-tile 0 is
 // outstanding, so are all later loads of the prologue.
 template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
-          class ARow, class BRow, class PA, class PB, class Pend>
+          class ARow, class BRow, class PA, class PB, class Pend, class X = NoExtra>
 __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,
                                                  int kbytes_b, uint8_t* const (&st)[NS], const ARow& a_row,
-                                                 const BRow& b_row, const Pend& pend0) {
+                                                 const BRow& b_row, const Pend& pend0, const X& xtra = X()) {
     using D = DmaSched<FP, NS, SPREAD, TM, TN, PA, PB>;
     constexpr int KS = D::KS, kMfma = D::kMfma, nA = D::nA, kPerTile = D::kPerTile, kPer = D::kPer;
     const int nk = (kbytes + RBA - 1) / RBA;
@@ -570,11 +579,15 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
                     if (s + 1 < SPREAD && j < kPer && (s + 1) * kPer + j < kPerTile)
                         issue_q((s + 1) * kPer + j, prv, pend_a, pend_b);
                     f.template slot<j>((par + s + 1) & 1, cur, cur + kOffB, s + 1, a_row, b_row);
+                    // the extra loads, after the batch's last instruction
+                    if (X::kOps > 0 && j == kMfma - 1 && s == (SPREAD - 1 < KS - 2 ? SPREAD - 1 : KS - 2))
+                        xtra.issue(kt, nk);
                     __builtin_amdgcn_sched_barrier(0);
                 });
             }
-            // last k-step of the tile: cross into tile kt+1
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile));  // tile kt+1 landed
+            // last k-step of the tile: cross into tile kt+1 (the extra loads of this tile
+            // may still be in flight)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile + X::kOps));  // tile kt+1 landed
             __syncthreads();                                             // ... for every wave
             __builtin_amdgcn_sched_barrier(0);
             pend_a = pa.base_offset(kt + NS, kbytes);
@@ -597,24 +610,24 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
 }
 
 template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
-          class ARow, class BRow, class PA, class PB>
+          class ARow, class BRow, class PA, class PB, class X = NoExtra>
 __device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,
                                                 int kbytes_b, uint8_t* const (&st)[NS],
-                                                const ARow& a_row, const BRow& b_row) {
+                                                const ARow& a_row, const BRow& b_row, const X& xtra = X()) {
     const auto pend = mainloop_dma_prologue<FP, BM, NS, RBA, SPREAD, TM, TN>(pa, pb, kbytes, kbytes_b, st);
     mainloop_dma_run<FP, BM, BN, SPLIT, NS, NW, RBA, RBB, SPREAD>(acc, pa, pb, kbytes, kbytes_b, st, a_row, b_row,
-                                                                  pend);
+                                                                  pend, xtra);
 }
 
 // Both operands of one element type E with RB-byte k-tile rows.
 template <Elt E, int BM, int BN, int SPLIT, int NS, int NW, int RB, int SPREAD, bool TC = false, int TM, int TN,
-          class ARow, class BRow>
+          class ARow, class BRow, class X = NoExtra>
 __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
                                              const DmaPanel<BN, SPLIT, NW, RB>& pb, int kbytes,
                                              uint8_t* const (&st)[NS], const ARow& a_row,
-                                             const BRow& b_row) {
+                                             const BRow& b_row, const X& xtra = X()) {
     mainloop_dma_fp<FragPair<Frags<E, TM, TN, RB, TC>>, BM, BN, SPLIT, NS, NW, RB, RB, SPREAD>(
-        acc, pa, pb, kbytes, kbytes, st, a_row, b_row);
+        acc, pa, pb, kbytes, kbytes, st, a_row, b_row, xtra);
 }
 
 // ---------------------------------------------------------------------------------

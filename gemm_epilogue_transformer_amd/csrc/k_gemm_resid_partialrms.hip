@@ -15,6 +15,33 @@
 
 namespace coda {
 
+// Prefetch of the residual tile during the mainloop.  In the epilogue every workgroup
+// reads its 256 x 256 residual tile (128 KB) at the same moment, a burst from HBM that no
+// MFMA work overlaps; read once during the last k-tiles instead (into a junk LDS block:
+// only the cache fill matters), the epilogue finds it in the last-level cache.  Wave w
+// takes tile rows 64w .. 64w+63, two rows (1 KB) per instruction, P instructions per k-tile
+// over the last 32 / P k-tiles; on earlier k-tiles, and without a residual, the
+// instructions address past the descriptor's range (zeros, no traffic), so that every
+// k-tile issues the same count.
+template <int P>
+struct XresPrefetch {
+    static constexpr int kOps = P;
+    static constexpr int kInst = 32;      // instructions per wave for 64 rows of 512 bytes
+    u32x4_t rsrc;
+    uint32_t lane_off;                    // this lane's byte offset in instruction 0
+    uint32_t step;                        // bytes between instructions (two rows)
+    uint32_t junk;                        // LDS address of the wave's junk block
+    __device__ __forceinline__ void issue(int kt, int nk) const {
+        const int i0 = (kt - (nk - kInst / P)) * P;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int i = i0 + p;
+            const uint32_t voff = (i >= 0 && i < kInst) ? lane_off + static_cast<uint32_t>(i) * step : kOob;
+            dma16(rsrc, voff, junk);
+        }
+    }
+};
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC, Elt E>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
@@ -29,6 +56,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     constexpr int kStage = (BM + BN) * RB;
     __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
     __shared__ float red[WAVES_N][BM];
+    __shared__ __attribute__((aligned(1024))) uint8_t junk[NW][1024];
     uint8_t* st[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) st[i] = stages[i];
@@ -57,7 +85,20 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    mainloop_dma<E, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
+    // the residual tile's cache fill during the last k-tiles (1 KB per wave and k-tile for
+    // bf16 operands, 2 KB for the 8-bit ones, whose k-tiles are half as many)
+    static_assert(BM == 64 * NW && BN == 256, "the prefetch covers 256 columns of 64 rows per wave");
+    XresPrefetch<E == Elt::E4M3 ? 2 : 1> xpf;
+    {
+        const uint32_t rb = static_cast<uint32_t>(N) * 2;
+        xpf.rsrc = make_rsrc(x_res ? x_res + static_cast<size_t>(m0) * N : h,
+                             x_res ? static_cast<uint32_t>(min(BM, M - m0)) * rb : 0u);
+        xpf.lane_off = static_cast<uint32_t>(64 * wave + (lane >> 5)) * rb + static_cast<uint32_t>(n0) * 2u +
+                       static_cast<uint32_t>(lane & 31) * 16u;
+        xpf.step = __builtin_amdgcn_readfirstlane(2u * rb);
+        xpf.junk = __builtin_amdgcn_readfirstlane(lds_addr(junk[wave]));
+    }
+    mainloop_dma<E, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row, xpf);
 
     // ---------------------------------------------------------------- epilogue ----
     // Per 32-row slab of this wave: stage scale*acc row-major in the wave's own (now
