@@ -1076,6 +1076,37 @@ def forward_summary(w, inp, args, numerics_rows: int = 512) -> dict:
         ums = float(np.median([e[0].elapsed_time(e[1]) for e in ue]))
         rec["unfused_torch"] = {"median_ms": round(ums, 4), "speedup_of_fused": round(ums / np.median(chain_ms), 3),
                                 "steps": len(ue)}
+        # the vendor library's plain product of each GEMM's shape (torch.matmul on the same
+        # operands, hipBLASLt on ROCm), timed alternately with the library's kernel on the
+        # same box: the GEMM-only reference the fused kernels are held against
+        hbuf = out["h"]
+        vend = {}
+        for name, fn_ours, fn_vendor, fl in (
+                ("gemm_resid_partialrms", lambda: coda.gemm_resid_partialrms(A, Wo, xr, None, None, out["h"],
+                                                                             out["partials"]),
+                 lambda: torch.matmul(A, Wo.t()), g1),
+                ("gemm_rowscale_swiglu", lambda: coda.gemm_rowscale_swiglu(hbuf, Wp, out["r"], w.act, sw, out["y"]),
+                 lambda: torch.matmul(hbuf, Wp.t()), g2)):
+            ts = {"ours": [], "vendor": []}
+            for _ in range(3):
+                fn_ours()
+                fn_vendor()
+            torch.cuda.synchronize()
+            for _ in range(20):
+                for key, fn in (("ours", fn_ours), ("vendor", fn_vendor)):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    ts[key].append((e0, e1))
+            torch.cuda.synchronize()
+            med = {k: float(np.median([a.elapsed_time(b) for a, b in v])) for k, v in ts.items()}
+            vend[name] = {"ours_ms": round(med["ours"], 4), "vendor_matmul_ms": round(med["vendor"], 4),
+                          "ours_tflops": round(fl / (med["ours"] * 1e-3) / 1e12, 1),
+                          "vendor_tflops": round(fl / (med["vendor"] * 1e-3) / 1e12, 1)}
+        vend["note"] = ("torch.matmul of the same operands (no residual, no row scale, no activation; it writes "
+                        "the full [M, N2w] product), alternated with the library's kernel, 20 each, medians")
+        rec["vendor_gemm"] = vend
     if numerics_rows > 0:
         rng = np.random.default_rng(w.seed)
         rows = np.sort(rng.choice(M, size=min(numerics_rows, M), replace=False))
@@ -1419,7 +1450,7 @@ def main():
         del out
         torch.cuda.empty_cache()
         summ = forward_summary(w, inp, args, args.numerics_rows)
-        for k in ("timing", "clock", "numerics_o1", "kernels_ms_median"):
+        for k in ("timing", "clock", "numerics_o1", "kernels_ms_median", "vendor_gemm"):
             if k in summ:
                 rec[k] = summ[k]
         if "unfused_torch" in summ:
