@@ -33,6 +33,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
 }
 
+// ------------------------------------------------------------ accumulators ------
+// One accumulator element read out of its AGPR right here (v_accvgpr_read_b32).  Plain
+// reads let the compiler copy all 256 accumulators of a finished tile into VGPRs in one
+// block after the mainloop, which in a persistent kernel spills, and the spill reloads'
+// full vmcnt waits then also wait for the next tile's DMA.  The MFMA that wrote the
+// element must be done: callers run acc_read_fence() once between the last MFMA and the
+// first read (the read is inline asm, so the compiler inserts no wait states for it).
+__device__ __forceinline__ float acc_read(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+// 32 wait states: more than the 32x32 MFMA's result latency requires
+__device__ __forceinline__ void acc_read_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+
 // ------------------------------------------------------------------ e4m3 ----------
 // OCP E4M3FN: bias 7, 3 mantissa bits, max 448, no infinities, NaN = S.1111.111.
 

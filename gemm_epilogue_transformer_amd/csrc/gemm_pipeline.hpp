@@ -474,8 +474,11 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // after A).  kbytes is the byte length of an A row (k-tile count = ceil(kbytes / RBA));
 // the B panel's descriptor and K-tail checks use its own row length, set at init.
 // The pending DMA of k-tile NS-1 (its base offsets) between the prologue and the run.
-template <class OA, class OB>
+// LATER: loads the caller issues after the prologue and before the run (for instance the
+// next tile's row scales), which the run's first wait may leave in flight.
+template <class OA, class OB, int LATER = 0>
 struct DmaPending {
+    static constexpr int kLater = LATER;
     OA a;
     OB b;
 };
@@ -521,6 +524,40 @@ __device__ __forceinline__ auto mainloop_dma_prologue(const PA& pa, const PB& pb
     return pend;
 }
 
+// mainloop_dma_prologue one instruction at a time, so that a caller can spread it over
+// other work (a persistent kernel's epilogue): instruction Q of kOps, in the order the
+// prologue issues them (tiles 0 .. NS-2 whole, A panel before B, then the first share of
+// tile NS-1).  pending<LATER>() is then what mainloop_dma_prologue would have returned.
+template <class FP, int BM, int NS, int RBA, int SPREAD, int TM, int TN, class PA, class PB>
+struct DmaPrologue {
+    using D = DmaSched<FP, NS, SPREAD, TM, TN, PA, PB>;
+    static constexpr int kOps = (NS - 1) * D::kPerTile + D::kPer;
+    const PA& pa;
+    const PB& pb;
+    int kbytes, kbytes_b;
+    uint8_t* const (&st)[NS];
+    template <int Q>
+    __device__ __forceinline__ void issue() const {
+        static_assert(Q >= 0 && Q < kOps, "prologue instruction");
+        constexpr int i = Q / D::kPerTile, r = Q % D::kPerTile;
+        if constexpr (r < D::nA) pa.issue_one(r, st[i], pa.base_offset(i, kbytes));
+        else pb.issue_one(r - D::nA, st[i] + BM * RBA, pb.base_offset(i, kbytes_b));
+    }
+    // instructions [kOps * c / parts, kOps * (c + 1) / parts): share c of `parts`
+    template <int C, int PARTS>
+    __device__ __forceinline__ void issue_share() const {
+        static_for<kOps>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+            if constexpr (q * PARTS >= kOps * C && q * PARTS < kOps * (C + 1)) issue<q>();
+        });
+    }
+    template <int LATER>
+    __device__ __forceinline__ auto pending() const {
+        return DmaPending<decltype(pa.base_offset(0, kbytes)), decltype(pb.base_offset(0, kbytes_b)), LATER>{
+            pa.base_offset(NS - 1, kbytes), pb.base_offset(NS - 1, kbytes_b)};
+    }
+};
+
 // Extra loads a kernel issues once per k-tile of the pipelined mainloop, kOps vector
 // memory instructions every k-tile (for instance a prefetch of the epilogue's operand).
 // They go out in the k-step after the previous tile's DMA batch is complete, so the
@@ -532,10 +569,11 @@ struct NoExtra {
 
 // The rest of the pipelined mainloop after mainloop_dma_prologue: wait for k-tile 0, the
 // k-loop, and the drain of the DMA that ran past the end.  The first wait, vmcnt
-// <= (NS-2) kPerTile + kPer, is exact when only the prologue's DMA was issued after
-// k-tile 0; vector memory operations issued after the prologue (an epilogue's stores)
-// only make it wait longer: loads complete in order, so while any load of k-tile 0 is
-// outstanding, so are all later loads of the prologue.
+// <= (NS-2) kPerTile + kPer + Pend::kLater, is exact when only the prologue's DMA and
+// kLater further loads were issued after k-tile 0; other vector memory operations issued
+// after the prologue (an epilogue's stores) only make it wait longer: loads complete in
+// order, so while any load of k-tile 0 is outstanding, so are all later loads of the
+// prologue and the kLater loads after it.
 template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
           class ARow, class BRow, class PA, class PB, class Pend, class X = NoExtra>
 __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,
@@ -557,7 +595,7 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
     };
     auto pend_a = pend0.a;
     auto pend_b = pend0.b;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile + kPer));   // tile 0 landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile + kPer + Pend::kLater));   // tile 0 landed
     __syncthreads();
     f.load(0, st[0], st[0] + kOffB, 0, a_row, b_row);
 

@@ -724,10 +724,16 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
 // row; one cross-half lane swap per pair of groups makes them 8, stored with one 16-byte
 // store, with no LDS staging.  Same fp32 operations per element, in the same order, as
 // rowscale_epilogue.
-template <int BM, int BN, int WAVES_M, int TM, int TN>
+// hook.at<P>() runs after the stores of gate/up block pair P = tm * TN/2 + b (a persistent
+// kernel issues a share of the next tile's DMA there).
+struct NoEpiHook {
+    template <int P>
+    __device__ __forceinline__ void at() const {}
+};
+template <int BM, int BN, int WAVES_M, int TM, int TN, class Hook = NoEpiHook>
 __device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN], const float (&rt)[TM], float sw,
                                                    uint16_t* __restrict__ Y, int M, int N_out, int m0, int j0,
-                                                   int wm, int wn) {
+                                                   int wm, int wn, const Hook& hook = Hook()) {
     constexpr int WM = BM / WAVES_M;
     constexpr int NB = TN / 2;
     // lane-derived addresses are formed here, not hoisted out of a persistent kernel's
@@ -739,20 +745,21 @@ __device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN]
     const uint32_t row_bytes = static_cast<uint32_t>(N_out) * 2;
     const __amdgpu_buffer_rsrc_t y_rsrc =
         make_buffer_rsrc(Y + static_cast<size_t>(m0) * N_out, static_cast<uint32_t>(valid_rows) * row_bytes);
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
+    acc_read_fence();
+    static_for<TM>([&](auto TMc) {
+        constexpr int tm = decltype(TMc)::value;
         const float rr = rt[tm] * sw;
         const uint32_t row_off = static_cast<uint32_t>(wm * WM + tm * 32 + lr) * row_bytes;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        static_for<NB>([&](auto Bc) {
+            constexpr int b = decltype(Bc)::value;
             uint32_t pk[4][2];    // group g: columns 8g + 4lh .. +3 as two bf16 pairs
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float gv = acc[tm][b][4 * g + e] * rr;
-                    const float uv = acc[tm][b + NB][4 * g + e] * rr;
+                    const float gv = acc_read(acc[tm][b][4 * g + e]) * rr;
+                    const float uv = acc_read(acc[tm][b + NB][4 * g + e]) * rr;
                     v[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
                 }
                 pk[g][0] = pack_bf16x2(v[0], v[1]);
@@ -776,8 +783,10 @@ __device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN]
                 __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(w[0]), int(w[1]), int(w[2]), int(w[3])}, y_rsrc,
                                                        voff, 0, 0);
             }
-        }
-    }
+            hook.template at<tm * NB + b>();
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    });
 }
 
 // Direct-to-LDS mainloop (PIPE 1: the register-staged one, bf16 weights only; PIPE 2: the
@@ -933,13 +942,27 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
         rowscale_epilogue<BM, BN, WAVES_M, TM, TN, ACT>(acc, rv, pv, rope, sw, Y, M, N_out, m0, j0, wm, wn, slab);
 }
 
+// Epilogue hook of the persistent kernel: after block pair P of PARTS, share P of the next
+// tile's prologue DMA (when there is a next tile).
+template <class Pro, int PARTS>
+struct ProHook {
+    const Pro& pro;
+    bool more;
+    template <int P>
+    __device__ __forceinline__ void at() const {
+        if (more) pro.template issue_share<P, PARTS>();
+    }
+};
+
 // Persistent form of the forward SwiGLU GEMM (bf16 weights, transposed accumulator
 // blocks, the epilogue of swiglu_epilogue_tc): a grid of at most one workgroup per CU
 // walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... in the XCD-aware order of the
 // one-tile-per-workgroup launch (with gridDim.x a multiple of 8, tile t still runs on XCD
 // t mod 8).  The epilogue touches no LDS, so the next tile's first k-tiles are issued
-// into the stages right after the mainloop's drain, and their latency hides behind the
-// epilogue's arithmetic and stores; the row scales of the next tile are loaded there too.
+// into the stages during it, a share after each block pair's stores (one burst of them
+// stalls the issuing wave once the address queue is full), and their latency hides
+// behind the rest of the epilogue; the next tile's row scales are loaded after it (the
+// mainloop's first wait leaves those loads in flight).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
 k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
@@ -973,27 +996,35 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
     PanelB pb;
     int m0 = 0, j0 = 0;
     float rv[TM];                                    // r of the lane's row in each block row
-    // panels and row scales of tile t (r of rows past M: 0)
+    // panels of tile t
     auto setup = [&](int t) {
         int tile_m, tile_n;
         tile_coords<8>(t, tiles_m, tiles_n, tile_m, tile_n);
         m0 = tile_m * BM;
         j0 = tile_n * BNO;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int m = m0 + wm * WM + 32 * i + (threadIdx.x & 31);
-            rv[i] = m < M ? R[m] : 0.0f;
-        }
         const uint8_t* a0 = H + static_cast<size_t>(m0) * kbytes;
         pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
         const uint8_t* g0 = W + static_cast<size_t>(j0) * kbytes;
         const uint8_t* u0 = W + static_cast<size_t>(N_out + j0) * kbytes;
         pb.init(g0, min(BN / 2, N_out - j0), u0, min(BN / 2, N_out - j0), kbytes);
     };
+    // row scales of the tile set up last (rows past M: 0); TM loads, issued after its
+    // prologue DMA (the mainloop's first wait leaves them in flight)
+    auto load_r = [&]() {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * WM + 32 * i + (threadIdx.x & 31);
+            rv[i] = m < M ? R[m] : 0.0f;
+        }
+    };
+    using Pro = DmaPrologue<FP, BM, NS, RB, SPREAD, TM, TN, PanelA, PanelB>;
+    const Pro pro{pa, pb, kbytes, kbytes, st};
     const float sw = w_scale ? *w_scale : 1.0f;
     int t = blockIdx.x;                              // the grid holds at most ntiles workgroups
     setup(t);
-    auto pend = mainloop_dma_prologue<FP, BM, NS, RB, SPREAD, TM, TN>(pa, pb, kbytes, kbytes, st);
+    static_for<Pro::kOps>([&](auto Q) { pro.template issue<decltype(Q)::value>(); });
+    auto pend = pro.template pending<TM>();
+    load_r();
     for (; t < ntiles; t += gridDim.x) {
         f32x16_t acc[TM][TN];
 #pragma unroll
@@ -1009,11 +1040,14 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
         float rc[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) rc[i] = rv[i];
-        if (t + static_cast<int>(gridDim.x) < ntiles) {     // uniform over the workgroup
-            setup(t + gridDim.x);
-            pend = mainloop_dma_prologue<FP, BM, NS, RB, SPREAD, TM, TN>(pa, pb, kbytes, kbytes, st);
+        const bool more = t + static_cast<int>(gridDim.x) < ntiles;     // uniform over the workgroup
+        if (more) setup(t + gridDim.x);
+        swiglu_epilogue_tc<BM, BN, WAVES_M, TM, TN>(acc, rc, sw, Y, M, N_out, cm0, cj0, wm, wn,
+                                                    ProHook<Pro, TM * (TN / 2)>{pro, more});
+        if (more) {
+            pend = pro.template pending<TM>();
+            load_r();
         }
-        swiglu_epilogue_tc<BM, BN, WAVES_M, TM, TN>(acc, rc, sw, Y, M, N_out, cm0, cj0, wm, wn);
     }
 }
 
