@@ -475,7 +475,9 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // the B panel's descriptor and K-tail checks use its own row length, set at init.
 // The pending DMA of k-tile NS-1 (its base offsets) between the prologue and the run.
 // LATER: loads the caller issues after the prologue and before the run (for instance the
-// next tile's row scales), which the run's first wait may leave in flight.
+// next tile's row scales), which the run's first wait may leave in flight.  Every wave
+// must issue exactly LATER such loads (no load skipped behind a branch), else the wait
+// would let k-tile 0's DMA still be in flight.
 template <class OA, class OB, int LATER = 0>
 struct DmaPending {
     static constexpr int kLater = LATER;
@@ -607,22 +609,22 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
             uint8_t* nxt = st[(i + 1) % NS];
             uint8_t* prv = st[(i + NS - 1) % NS];    // stage receiving the pending DMA
             const int kt = g * NS + i;
-#pragma unroll
-            for (int s = 0; s < KS - 1; ++s) {
+            static_for<KS - 1>([&](auto Sc) {
+                constexpr int s = decltype(Sc)::value;
                 // k-step s: MFMA j, then pending DMA instruction (s+1)*kPer + j, then
                 // fragment read j of k-step s+1
                 static_for<kMfma>([&](auto J) {
                     constexpr int j = decltype(J)::value;
                     f.mma_one((par + s) & 1, j, acc);
-                    if (s + 1 < SPREAD && j < kPer && (s + 1) * kPer + j < kPerTile)
+                    if constexpr (s + 1 < SPREAD && j < kPer && (s + 1) * kPer + j < kPerTile)
                         issue_q((s + 1) * kPer + j, prv, pend_a, pend_b);
                     f.template slot<j>((par + s + 1) & 1, cur, cur + kOffB, s + 1, a_row, b_row);
                     // the extra loads, after the batch's last instruction
-                    if (X::kOps > 0 && j == kMfma - 1 && s == (SPREAD - 1 < KS - 2 ? SPREAD - 1 : KS - 2))
+                    if constexpr (X::kOps > 0 && j == kMfma - 1 && s == (SPREAD - 1 < KS - 2 ? SPREAD - 1 : KS - 2))
                         xtra.issue(kt, nk);
                     __builtin_amdgcn_sched_barrier(0);
                 });
-            }
+            });
             // last k-step of the tile: cross into tile kt+1 (the extra loads of this tile
             // may still be in flight)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * kPerTile + X::kOps));  // tile kt+1 landed
@@ -636,7 +638,7 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
             static_for<kMfma>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 f.mma_one((par + KS - 1) & 1, j, acc);
-                if (j < kPer) issue_q(j, cur, pend_a, pend_b);
+                if constexpr (j < kPer) issue_q(j, cur, pend_a, pend_b);
                 f.template slot<j>((par + KS) & 1, nxt, nxt + kOffB, 0, a_row, b_row);
                 __builtin_amdgcn_sched_barrier(0);
             });

@@ -29,14 +29,14 @@ struct XresPrefetch {
     static constexpr int kInst = 32;      // instructions per wave for 64 rows of 512 bytes
     u32x4_t rsrc;
     uint32_t lane_off;                    // this lane's byte offset in instruction 0
-    uint32_t step;                        // bytes between instructions (two rows)
+    uint32_t inst_step;                   // bytes between instructions (two rows)
     uint32_t junk;                        // LDS address of the wave's junk block
     __device__ __forceinline__ void issue(int kt, int nk) const {
         const int i0 = (kt - (nk - kInst / P)) * P;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int i = i0 + p;
-            const uint32_t voff = (i >= 0 && i < kInst) ? lane_off + static_cast<uint32_t>(i) * step : kOob;
+            const uint32_t voff = (i >= 0 && i < kInst) ? lane_off + static_cast<uint32_t>(i) * inst_step : kOob;
             dma16(rsrc, voff, junk);
         }
     }
@@ -95,7 +95,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
                              x_res ? static_cast<uint32_t>(min(BM, M - m0)) * rb : 0u);
         xpf.lane_off = static_cast<uint32_t>(64 * wave + (lane >> 5)) * rb + static_cast<uint32_t>(n0) * 2u +
                        static_cast<uint32_t>(lane & 31) * 16u;
-        xpf.step = __builtin_amdgcn_readfirstlane(2u * rb);
+        xpf.inst_step = __builtin_amdgcn_readfirstlane(2u * rb);
         xpf.junk = __builtin_amdgcn_readfirstlane(lds_addr(junk[wave]));
     }
     mainloop_dma<E, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row, xpf);

@@ -769,8 +769,8 @@ __device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN]
             // trade places (v_permlane32_swap), so lane l < 32 holds columns 16q .. 16q+7
             // and lane l + 32 columns 16q+8 .. 16q+15 of its row: 16-byte stores
             const int nb = j0 + wn * NB * 32 + b * 32;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            static_for<2>([&](auto Qc) {
+                constexpr int q = decltype(Qc)::value;
                 uint32_t w[4];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -782,7 +782,7 @@ __device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN]
                 const uint32_t voff = n < N_out ? row_off + static_cast<uint32_t>(n) * 2 : kOobOffset;
                 __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{int(w[0]), int(w[1]), int(w[2]), int(w[3])}, y_rsrc,
                                                        voff, 0, 0);
-            }
+            });
             hook.template at<tm * NB + b>();
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -1008,13 +1008,16 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
         const uint8_t* u0 = W + static_cast<size_t>(N_out + j0) * kbytes;
         pb.init(g0, min(BN / 2, N_out - j0), u0, min(BN / 2, N_out - j0), kbytes);
     };
-    // row scales of the tile set up last (rows past M: 0); TM loads, issued after its
-    // prologue DMA (the mainloop's first wait leaves them in flight)
+    // row scales of the tile set up last (rows past M: 0, through the descriptor's range
+    // check); TM loads, issued after its prologue DMA: the mainloop's first wait leaves
+    // exactly TM loads in flight after the prologue, so every wave issues all of them
+    // (a load guarded by a row check would be skipped by waves whose rows all lie past M)
+    const __amdgpu_buffer_rsrc_t r_rsrc = make_buffer_rsrc(R, static_cast<uint32_t>(M) * 4u);
     auto load_r = [&]() {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int m = m0 + wm * WM + 32 * i + (threadIdx.x & 31);
-            rv[i] = m < M ? R[m] : 0.0f;
+            const uint32_t m = static_cast<uint32_t>(m0 + wm * WM + 32 * i + (threadIdx.x & 31));
+            rv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_rsrc, m * 4u, 0, 0));
         }
     };
     using Pro = DmaPrologue<FP, BM, NS, RB, SPREAD, TM, TN, PanelA, PanelB>;
