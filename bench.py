@@ -247,6 +247,66 @@ def _launch_groups(durations: list) -> list:
     return groups[::-1]
 
 
+def _template_args(name: str) -> str:
+    """The template argument list of a demangled kernel name ('' if none)."""
+    i = name.find("<")
+    if i < 0 or name.find("(") < i:
+        return ""
+    depth = 0
+    for j in range(i, len(name)):
+        if name[j] == "<":
+            depth += 1
+        elif name[j] == ">":
+            depth -= 1
+            if depth == 0:
+                return name[i + 1:j]
+    return ""
+
+
+def summarize_trace(directory: str, workload: str, bench_log: str, command: str, out_dir: str = "") -> str:
+    """Write profiles/kernel_trace_<workload>.txt from a rocprofv3 --kernel-trace csv run:
+    the library's kernels per template instantiation and launch group (one kernel on
+    problems of different size in one step, told apart by duration), with launches and
+    average / min / max duration, plus the bench line of the same run."""
+    acc = {}
+    for r in _csv_rows(directory, "kernel_trace.csv"):
+        n = r["Kernel_Name"]
+        if "coda::" not in n:
+            continue
+        key = (_short_kernel_name(n).split("::")[-1], _template_args(n))
+        acc.setdefault(key, []).append((int(r["Dispatch_Id"]),
+                                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    line = ""
+    for ln in open(bench_log):
+        if ln.startswith("{") and '"metric"' in ln:
+            line = ln
+    b = json.loads(line) if line else {}
+    out = [f"# rocprofv3 kernel-trace summary, workload {workload}",
+           f"# command: {command}",
+           f"# summary: python3 bench.py --summarize-trace DIR {workload} BENCH_LOG --ingest-command '<the command>'",
+           f"# kernel source hash (all sources): {kernel_source_hash()}; the same run's bench line: "
+           f"{b.get('ms_per_step')} ms per step, {b.get('value')} {b.get('unit', '')}, per-kernel HIP events (ms) "
+           f"{json.dumps(b.get('kernels_ms'))}",
+           "# per kernel instantiation and launch group (the same kernel on problems of different size in one step, "
+           "grouped by duration): launches, average / min / max duration in us",
+           "kernel, template arguments, group, launches, avg_us, min_us, max_us"]
+    recs = []
+    for (base, ta), disp in acc.items():
+        disp.sort()
+        durs = [x[1] for x in disp]
+        for g, idx in enumerate(_launch_groups(durs)):
+            v = [durs[i] for i in idx]
+            recs.append((len(disp), base, ta, g, len(v), sum(v) / len(v), min(v), max(v)))
+    recs.sort(key=lambda x: (-x[0], x[1], x[3]))
+    for _, base, ta, g, n, a, mn, mx in recs:
+        out.append(f'{base}, "{ta}", {g}, {n}, {a:.1f}, {mn:.1f}, {mx:.1f}')
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"kernel_trace_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+    return path
+
+
 def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, then of the
     plain copy) into profiles/traffic_<workload>.json: HBM-side bytes per launch of each kernel,
@@ -1198,7 +1258,11 @@ def main():
     ap.add_argument("--ingest-traffic", nargs=4, metavar="DIR",
                     help="write profiles/traffic_*.json from rocprofv3 --pmc output dirs: "
                          "FETCH_SIZE run, WRITE_SIZE run, FETCH_SIZE copy run, WRITE_SIZE copy run")
-    ap.add_argument("--ingest-command", default="", help="command line recorded with --ingest-traffic")
+    ap.add_argument("--ingest-command", default="",
+                    help="command line recorded with --ingest-traffic / --summarize-trace")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "WORKLOAD", "BENCH_LOG"),
+                    help="write profiles/kernel_trace_<WORKLOAD>.txt from a rocprofv3 --kernel-trace csv "
+                         "run in DIR whose stdout (with the bench line) is BENCH_LOG")
     ap.add_argument("--traffic-probe", choices=("fused", "unfused"), default=None,
                     help="forward bf16 workloads: after the setup run exactly --steps steps of one path "
                          "(no warm-up, no timing) and exit; two such runs under rocprofv3 --pmc at two "
@@ -1208,6 +1272,9 @@ def main():
                          "small / big and WRITE_SIZE small / big run dirs of the fused probe, the same "
                          "four of the unfused probe, then the FETCH_SIZE and WRITE_SIZE copy run dirs")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.ingest_command)
+        return
     if args.ingest_step_traffic:
         import synth_inputs as si
 

@@ -123,3 +123,29 @@ def test_roofline_kernels_resolve_to_their_sources():
         assert bench.kernel_source_hash(k) != ""
     rec = json.load(open(os.path.join(bench.ROOT, "profiles", "traffic_llama1b_attnout_mlpin_m16384.json")))
     assert "k_gemm_swiglu_persistent" in rec["kernels"]
+
+
+def test_kernel_trace_summary_groups_launches(tmp_path):
+    """--summarize-trace: per kernel instantiation, launches of one kernel on two problem
+    sizes fall into two duration groups; other kernels are left out; the bench line of the
+    same run is quoted."""
+    d = tmp_path / "kt"
+    d.mkdir()
+    with open(d / "kt_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        i = 0
+        for dur in (100_000, 101_000, 900_000, 905_000, 99_000):      # ns: two sizes
+            i += 1
+            w.writerow([i, "void coda::k_gemm_x<256, 256, 2>(int)", 1000 * i, 1000 * i + dur])
+        w.writerow([99, "Cijk_vendor(int)", 0, 5000])
+    log = tmp_path / "bench.log"
+    log.write_text('noise\n{"metric": "m", "value": 1.5, "unit": "TFLOP/s", "ms_per_step": 1.0, '
+                   '"kernels_ms": {"a": 1}}\n')
+    path = bench.summarize_trace(str(d), "wl", str(log), "the command", out_dir=str(tmp_path))
+    text = open(path).read()
+    assert "# command: the command" in text and "1.0 ms per step, 1.5 TFLOP/s" in text
+    rows = [r for r in text.splitlines() if r.startswith("k_gemm_x")]
+    assert rows == ['k_gemm_x, "256, 256, 2", 0, 2, 902.5, 900.0, 905.0',     # longest group first
+                    'k_gemm_x, "256, 256, 2", 1, 3, 100.0, 99.0, 101.0']
+    assert "Cijk" not in text

@@ -46,6 +46,23 @@ def test_on_chip_fold_is_bit_identical(M, K, n_w, act):
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("M,K,n_w", [(257, 264, 528), (10241, 264, 2048)])
+def test_persistent_ragged_row_tiles_repeat_bit_identical(M, K, n_w):
+    """The persistent SwiGLU GEMM on row tiles whose last one holds a single row (so some
+    waves' rows all lie past M), once with one tile per workgroup and once with more tiles
+    than compute units: ten calls in a row, each bit-identical to the on-chip-fold path
+    (a separate kernel with its own mainloop).  A row-scale load skipped by such waves let
+    the mainloop's first wait pass before its DMA had landed."""
+    print(f"persistent ragged rows M={M} K={K} n_w={n_w}", flush=True)
+    h, W, gamma, r = _case(M, K, n_w, M + 3 * K + n_w)
+    Wp = coda.prepare_weight_bf16(W, gamma)
+    ref = coda.gemm_rowscale_gfold(h, W, gamma, r, coda.SWIGLU)
+    for i in range(10):
+        got = coda.gemm_rowscale_swiglu(h, Wp, r, coda.SWIGLU)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"call {i}"
+
+
 def test_on_chip_fold_workload_shape():
     w = si.WORKLOADS[2]
     print(f"gfold {w.name}", flush=True)
