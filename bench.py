@@ -307,6 +307,78 @@ def summarize_trace(directory: str, workload: str, bench_log: str, command: str,
     return path
 
 
+def ingest_counters(dirs, w, command: str, out_dir: str = "") -> str:
+    """profiles/counters_<workload>.txt: per kernel of a --vendor-probe run (the library's two
+    GEMMs and the vendor GEMM of each shape, told apart by duration), the median over its
+    dispatches of every counter collected in the passes `dirs`, and derived figures:
+    clock = GRBM_GUI_ACTIVE / 8 XCDs / duration, MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /
+    1024 SIMDs / (GRBM_GUI_ACTIVE / 8), L2 hit rate, mean fabric read latency =
+    TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ, TFLOP/s of the dispatch."""
+    import statistics
+
+    flops = {"gemm1": 2.0 * w.M * w.K1 * w.d, "gemm2": 2.0 * w.M * w.d * w.N2w}
+    vals, durs = {}, {}
+    for dr in dirs:
+        per = {}
+        for r in _csv_rows(dr, "counter_collection.csv"):
+            name = r["Kernel_Name"]
+            if "coda::" in name:
+                kind = "gemm1" if "resid_partialrms" in name else ("gemm2" if "swiglu" in name else None)
+                who = "library"
+            elif name.startswith("Cijk") or "Cijk" in name[:40]:
+                kind, who = None, "vendor"
+            else:
+                continue
+            key = (name, int(r["Dispatch_Id"]))
+            rec = per.setdefault(key, {"who": who, "kind": kind, "dur": int(r["End_Timestamp"]) -
+                                       int(r["Start_Timestamp"]), "c": {}})
+            rec["c"][r["Counter_Name"]] = rec["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        # the vendor dispatches alternate between the two shapes: the longer ones are GEMM 2
+        vend = sorted([k for k, v in per.items() if v["who"] == "vendor"], key=lambda k: per[k]["dur"])
+        for k in vend[: len(vend) // 2]:
+            per[k]["kind"] = "gemm1"
+        for k in vend[len(vend) // 2:]:
+            per[k]["kind"] = "gemm2"
+        for (name, _), v in per.items():
+            if v["kind"] is None:
+                continue
+            row = (v["kind"], v["who"])
+            durs.setdefault(row, []).append(v["dur"])
+            for c, x in v["c"].items():
+                vals.setdefault(row, {}).setdefault(c, []).append(x)
+    rows = sorted(vals, key=lambda r: (r[0], r[1] != "library"))
+    counters = sorted({c for r in rows for c in vals[r]})
+    med = {r: {c: statistics.median(vals[r][c]) for c in vals[r]} for r in rows}
+    mdur = {r: statistics.median(durs[r]) for r in rows}
+    lines = [f"# counters per dispatch, workload {w.name}: the library's GEMMs against the vendor GEMM "
+             f"(torch.matmul, hipBLASLt) of the same operands",
+             f"# command: {command}",
+             f"# summary: python3 bench.py --workload <n> --ingest-counters DIR... --ingest-command '<the command>'",
+             f"# kernel source hash (all sources): {kernel_source_hash()}",
+             "# medians over each kernel's dispatches (durations under the profiler); derived: clock_ghz = "
+             "GRBM_GUI_ACTIVE / 8 / duration, mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 / (GRBM_GUI_ACTIVE / 8), "
+             "l2_hit = TCC_HIT / (TCC_HIT + TCC_MISS), fabric_read_latency = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ",
+             "shape, kernel, " + ", ".join(["dur_us", "tflops"] + counters +
+                                           ["clock_ghz", "mfma_busy", "l2_hit", "fabric_read_latency"])]
+    for r in rows:
+        m, du = med[r], mdur[r]
+        g = m.get("GRBM_GUI_ACTIVE")
+        der = [g / 8 / du if g else None,
+               m["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (g / 8) if g and "SQ_VALU_MFMA_BUSY_CYCLES" in m else None,
+               m["TCC_HIT"] / (m["TCC_HIT"] + m["TCC_MISS"]) if "TCC_HIT" in m and "TCC_MISS" in m else None,
+               m["TCC_EA0_RDREQ_LEVEL"] / m["TCC_EA0_RDREQ"] if m.get("TCC_EA0_RDREQ") and
+               "TCC_EA0_RDREQ_LEVEL" in m else None]
+        cells = [f"{du / 1e3:.1f}", f"{flops[r[0]] / du / 1e3:.1f}"] + \
+                [f"{m[c]:.4g}" if c in m else "" for c in counters] + \
+                [f"{x:.3f}" if x is not None else "" for x in der]
+        lines.append(f"{r[0]}, {r[1]}, " + ", ".join(cells))
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"counters_{w.name}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return path
+
+
 def ingest_traffic(dirs, workload: str, copy_bytes: int, command: str) -> None:
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, then of the
     plain copy) into profiles/traffic_<workload>.json: HBM-side bytes per launch of each kernel,
@@ -1263,6 +1335,14 @@ def main():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "WORKLOAD", "BENCH_LOG"),
                     help="write profiles/kernel_trace_<WORKLOAD>.txt from a rocprofv3 --kernel-trace csv "
                          "run in DIR whose stdout (with the bench line) is BENCH_LOG")
+    ap.add_argument("--vendor-probe", action="store_true",
+                    help="bf16 forward workloads: after the setup run --steps rounds of (the library's first "
+                         "GEMM, torch.matmul of its operands, the library's second GEMM, torch.matmul of its "
+                         "operands) and exit: counter runs of it compare each kernel with the vendor GEMM of "
+                         "the same shape")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="DIR",
+                    help="write profiles/counters_<workload>.txt from rocprofv3 --pmc runs of --vendor-probe "
+                         "(one directory per counter pass)")
     ap.add_argument("--traffic-probe", choices=("fused", "unfused"), default=None,
                     help="forward bf16 workloads: after the setup run exactly --steps steps of one path "
                          "(no warm-up, no timing) and exit; two such runs under rocprofv3 --pmc at two "
@@ -1272,6 +1352,11 @@ def main():
                          "small / big and WRITE_SIZE small / big run dirs of the fused probe, the same "
                          "four of the unfused probe, then the FETCH_SIZE and WRITE_SIZE copy run dirs")
     args = ap.parse_args()
+    if args.ingest_counters:
+        import synth_inputs as si
+
+        ingest_counters(args.ingest_counters, si.WORKLOADS[args.workload], args.ingest_command)
+        return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.ingest_command)
         return
@@ -1402,6 +1487,22 @@ def main():
             rq = torch.cat([x1 * c - x2 * s_, x2 * c + x1 * s_], -1).to(torch.bfloat16)
             return torch.cat([rq.view(M, -1), z[:, w.rot_cols:]], 1)
         return z
+
+    if args.vendor_probe:
+        if w.dtype != "bf16" or w.act not in (si.ACT_NONE, si.ACT_SWIGLU):
+            print("bench.py: --vendor-probe covers the bf16 forward workloads", file=sys.stderr)
+            sys.exit(2)
+        hbuf = out["h"]
+        coda.gemm_resid_partialrms(A, Wo, xr, None, None, hbuf, out["partials"])
+        coda.rowscale_reduce(out["partials"], d, w.eps, out["r"])
+        for _ in range(args.steps):
+            coda.gemm_resid_partialrms(A, Wo, xr, None, None, hbuf, out["partials"])
+            torch.matmul(A, Wo.t())
+            coda.gemm_rowscale_swiglu(hbuf, Wp, out["r"], w.act, None, out["y"])
+            torch.matmul(hbuf, Wp.t())
+        torch.cuda.synchronize()
+        print(json.dumps({"vendor_probe": w.name, "rounds": args.steps}), flush=True)
+        return
 
     if args.traffic_probe:
         if w.dtype != "bf16":

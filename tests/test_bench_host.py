@@ -149,3 +149,40 @@ def test_kernel_trace_summary_groups_launches(tmp_path):
     assert rows == ['k_gemm_x, "256, 256, 2", 0, 2, 902.5, 900.0, 905.0',     # longest group first
                     'k_gemm_x, "256, 256, 2", 1, 3, 100.0, 99.0, 101.0']
     assert "Cijk" not in text
+
+
+def test_counter_ingest_pairs_library_and_vendor_kernels(tmp_path):
+    """--ingest-counters: the vendor dispatches of a --vendor-probe run are split into the
+    two GEMM shapes by duration; medians and the derived clock / MFMA busy / hit rate /
+    fabric latency come out of the counters as defined."""
+    import synth_inputs as si
+
+    w = si.WORKLOADS[2]
+    kern = {"g1": "void coda::k_gemm_resid_partialrms<256>(int)", "g2": "void coda::k_gemm_swiglu_persistent<256>(int)",
+            "v": "Cijk_Alik_Bljk_x"}
+    # (kernel, dispatch, duration ns); per pass the counters below, the same on every dispatch
+    disp = [("g1", 1, 100_000), ("v", 2, 90_000), ("g2", 3, 800_000), ("v", 4, 700_000),
+            ("g1", 5, 100_000), ("v", 6, 90_000), ("g2", 7, 800_000), ("v", 8, 700_000)]
+    passes = {"p1": {"GRBM_GUI_ACTIVE": 8 * 150_000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 75_000.0},
+              "p2": {"TCC_HIT": 80.0, "TCC_MISS": 20.0, "TCC_EA0_RDREQ": 10.0, "TCC_EA0_RDREQ_LEVEL": 5000.0}}
+    dirs = []
+    for pname, cs in passes.items():
+        d = tmp_path / pname
+        d.mkdir()
+        with open(d / "pmc_counter_collection.csv", "w", newline="") as fh:
+            wr = csv.writer(fh)
+            wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                         "End_Timestamp"])
+            for k, i, dur in disp:
+                for c, v in cs.items():
+                    wr.writerow([i, kern[k], c, v, 0, dur])
+        dirs.append(str(d))
+    path = bench.ingest_counters(dirs, w, "cmd", out_dir=str(tmp_path))
+    rows = {tuple(r.split(", ")[:2]): r.split(", ") for r in open(path).read().splitlines()
+            if not r.startswith("#") and not r.startswith("shape")}
+    assert set(rows) == {("gemm1", "library"), ("gemm1", "vendor"), ("gemm2", "library"), ("gemm2", "vendor")}
+    lib2 = rows[("gemm2", "library")]
+    assert lib2[2] == "800.0" and float(lib2[3]) == round(2.0 * w.M * w.d * w.N2w / 800_000 / 1e3, 1)
+    # clock 150000 cycles / 800 us = 0.1875 GHz; busy 75000 / 150000 = 0.5; hit 0.8; latency 500
+    assert lib2[-4:] == ["0.188", "0.500", "0.800", "500.000"]
+    assert rows[("gemm1", "vendor")][2] == "90.0" and rows[("gemm2", "vendor")][2] == "700.0"
