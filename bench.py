@@ -1210,7 +1210,7 @@ def forward_summary(w, inp, args, numerics_rows: int = 512) -> dict:
                                 "steps": len(ue)}
         # the vendor library's plain product of each GEMM's shape (torch.matmul on the same
         # operands, hipBLASLt on ROCm), timed alternately with the library's kernel on the
-        # same box: the GEMM-only reference the fused kernels are held against
+        # same machine: the GEMM-only reference the fused kernels are held against
         hbuf = out["h"]
         vend = {}
         for name, fn_ours, fn_vendor, fl in (
