@@ -46,7 +46,10 @@ __device__ __forceinline__ float acc_read(float a) {
     return v;
 }
 // 32 wait states: more than the 32x32 MFMA's result latency requires
-__device__ __forceinline__ void acc_read_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+__device__ __forceinline__ void acc_read_fence() {
+    __builtin_amdgcn_sched_barrier(0);       // no MFMA is moved below the wait states
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+}
 
 // ------------------------------------------------------------------ e4m3 ----------
 // OCP E4M3FN: bias 7, 3 mantissa bits, max 448, no infinities, NaN = S.1111.111.

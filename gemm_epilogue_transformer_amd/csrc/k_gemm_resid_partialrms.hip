@@ -121,6 +121,10 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
         const int n = n0 + wn * WN + S::seg_col(j);
         return n < N ? static_cast<uint32_t>(tr) * row_bytes + static_cast<uint32_t>(n) * 2 : kOobOffset;
     };
+    // accumulators are read at their use (acc_read): plain reads had the compiler spill 8
+    // of them after the mainloop, and the reloads' vmcnt waits in the last slab then
+    // waited for every h store and residual load before them
+    acc_read_fence();
     i32x4_t xr[2][S::kSegPerLane];
 #pragma unroll
     for (int j = 0; j < S::kSegPerLane; ++j)
@@ -136,7 +140,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[tn][i] = acc[tm][tn][i] * scale;
+            for (int i = 0; i < 16; ++i) v[tn][i] = acc_read(acc[tm][tn][i]) * scale;
         S::put(slab, v);
 #pragma unroll
         for (int j = 0; j < S::kSegPerLane; ++j) {

@@ -74,6 +74,7 @@ __device__ __forceinline__ void ce_epilogue(const f32x16_t (&acc)[TM][TN], const
                                             const int (&tv)[BM / WAVES_M / 64], float sw, const CeArgs& ce,
                                             int M, int V, int m0, int j0, int tile_n, int wm, int wn,
                                             uint8_t* slab, float* red) {
+    acc_read_fence();                       // accumulators are read with acc_read
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, NT = 64 * WAVES_M * WAVES_N;
     using S = Slab<TN>;
     const int lane = threadIdx.x & 63;
@@ -91,7 +92,7 @@ __device__ __forceinline__ void ce_epilogue(const f32x16_t (&acc)[TM][TN], const
 #pragma unroll
         for (int b = 0; b < TN; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[b][i] = acc[tm][b][i] * rr[i];
+            for (int i = 0; i < 16; ++i) v[b][i] = acc_read(acc[tm][b][i]) * rr[i];
         S::put(slab, v);
 #pragma unroll
         for (int j = 0; j < S::kSegPerLane; ++j) {
@@ -182,6 +183,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
 __device__ __forceinline__ void ce_epilogue_tc(const f32x16_t (&acc)[TM][TN], const float (&rt)[TM],
                                                const int (&tt)[TM], float sw, const CeArgs& ce, int M, int V,
                                                int m0, int j0, int tile_n, int wm, int wn, float* red) {
+    acc_read_fence();                       // accumulators are read with acc_read
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, NT = 64 * WAVES_M * WAVES_N;
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
@@ -197,7 +199,7 @@ __device__ __forceinline__ void ce_epilogue_tc(const f32x16_t (&acc)[TM][TN], co
 #pragma unroll
         for (int b = 0; b < TN; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) z[b][i] = acc[tm][b][i] * rr;
+            for (int i = 0; i < 16; ++i) z[b][i] = acc_read(acc[tm][b][i]) * rr;
         if (!full) {
 #pragma unroll
             for (int b = 0; b < TN; ++b)
@@ -282,6 +284,7 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN
                                                     const float (&rv)[BM / WAVES_M / 64], const BwdArgs& bw,
                                                     int M, int F, int m0, int j0, int tile_n, int wm, int wn,
                                                     uint8_t* slab, float* red) {
+    acc_read_fence();                       // accumulators are read with acc_read
     constexpr int WM = BM / WAVES_M, NT = 64 * WAVES_M * WAVES_N;
     constexpr int NB = TN / 2;                       // gate (= up) blocks per wave
     constexpr int kGseg = NB * 4;                    // 8-column gate segments per row
@@ -317,7 +320,7 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(const f32x16_t (&acc)[TM][TN
 #pragma unroll
         for (int b = 0; b < TN; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[b][i] = acc[tm][b][i];
+            for (int i = 0; i < 16; ++i) v[b][i] = acc_read(acc[tm][b][i]);
         S::put(slab, v);
 #pragma unroll
         for (int jj = 0; jj < kSegPerLane; ++jj) {
@@ -400,6 +403,7 @@ __device__ __forceinline__ void ce_bwd_epilogue(const f32x16_t (&acc)[TM][TN],
                                                 const float (&gv)[BM / WAVES_M / 64], const BwdArgs& bw,
                                                 int M, int V, int m0, int j0, int tile_n, int wm, int wn,
                                                 uint8_t* slab) {
+    acc_read_fence();                       // accumulators are read with acc_read
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     using S = Slab<TN>;
     static_assert(S::kSegPerRow == 16, "16 lanes per row: the all-reduce below");
@@ -415,7 +419,7 @@ __device__ __forceinline__ void ce_bwd_epilogue(const f32x16_t (&acc)[TM][TN],
 #pragma unroll
         for (int b = 0; b < TN; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[b][i] = acc[tm][b][i];
+            for (int i = 0; i < 16; ++i) v[b][i] = acc_read(acc[tm][b][i]);
         S::put(slab, v);
 #pragma unroll
         for (int j = 0; j < S::kSegPerLane; ++j) {
@@ -466,6 +470,7 @@ __device__ __forceinline__ void ce_bwd_epilogue_tc(const f32x16_t (&acc)[TM][TN]
                                                    const int (&tt)[TM], const float (&lt)[TM], const float (&gt)[TM],
                                                    const BwdArgs& bw, int M, int V, int m0, int j0, int tile_n,
                                                    int wm, int wn) {
+    acc_read_fence();                       // accumulators are read with acc_read
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static_assert(WN == 128, "one partial per wave and row: 128 columns");
     int lane = threadIdx.x & 63;
@@ -493,7 +498,7 @@ __device__ __forceinline__ void ce_bwd_epilogue_tc(const f32x16_t (&acc)[TM][TN]
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int n = nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3);
-                const float p = __expf(rr * acc[tm][b][i] - ls);
+                const float p = __expf(rr * acc_read(acc[tm][b][i]) - ls);
                 dl[i] = gr * (p - (n == tg ? 1.0f : 0.0f));
             }
             if (!full) {
@@ -507,7 +512,7 @@ __device__ __forceinline__ void ce_bwd_epilogue_tc(const f32x16_t (&acc)[TM][TN]
                 float dzo[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    c += dl[4 * g + e] * acc[tm][b][4 * g + e];
+                    c += dl[4 * g + e] * acc_read(acc[tm][b][4 * g + e]);
                     dzo[e] = rr * dl[4 * g + e];
                 }
                 pk[g][0] = pack_bf16x2(dzo[0], dzo[1]);
@@ -545,6 +550,7 @@ __device__ __forceinline__ void swiglu_save_epilogue(const f32x16_t (&acc)[TM][T
                                                      const float (&rv)[BM / WAVES_M / 64], float sw,
                                                      uint16_t* __restrict__ Y, uint16_t* __restrict__ Z, int M,
                                                      int F, int m0, int j0, int wm, int wn, uint8_t* slab) {
+    acc_read_fence();                       // accumulators are read with acc_read
     constexpr int WM = BM / WAVES_M;
     constexpr int NB = TN / 2;
     constexpr int kGseg = NB * 4;
@@ -563,7 +569,7 @@ __device__ __forceinline__ void swiglu_save_epilogue(const f32x16_t (&acc)[TM][T
 #pragma unroll
         for (int b = 0; b < TN; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[b][i] = acc[tm][b][i];
+            for (int i = 0; i < 16; ++i) v[b][i] = acc_read(acc[tm][b][i]);
         S::put(slab, v);
 #pragma unroll
         for (int jj = 0; jj < kSegPerLane; ++jj) {
@@ -626,6 +632,7 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
                                                   const int (&pv)[BM / WAVES_M / 64], const RopeArgs& rope,
                                                   float sw, uint16_t* __restrict__ Y, int M, int N_out,
                                                   int m0, int j0, int wm, int wn, uint8_t* slab) {
+    acc_read_fence();                       // accumulators are read with acc_read
     constexpr bool SWIGLU = ACT == kActSwiglu;
     constexpr int WM = BM / WAVES_M;
     constexpr int NB = SWIGLU ? TN / 2 : TN;          // output blocks per wave
@@ -673,15 +680,15 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
                 if (n_wave + b * 32 < rope.rot_cols) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const float x1 = acc[tm][b][i] * rr[i], x2 = acc[tm][b + 1][i] * rr[i];
+                        const float x1 = acc_read(acc[tm][b][i]) * rr[i], x2 = acc_read(acc[tm][b + 1][i]) * rr[i];
                         v[b][i] = x1 * cs[i] - x2 * sn[i];
                         v[b + 1][i] = x2 * cs[i] + x1 * sn[i];
                     }
                 } else {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        v[b][i] = acc[tm][b][i] * rr[i];
-                        v[b + 1][i] = acc[tm][b + 1][i] * rr[i];
+                        v[b][i] = acc_read(acc[tm][b][i]) * rr[i];
+                        v[b + 1][i] = acc_read(acc[tm][b + 1][i]) * rr[i];
                     }
                 }
             }
@@ -691,11 +698,11 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     if constexpr (SWIGLU) {
-                        const float gv = acc[tm][b][i] * rr[i];
-                        const float uv = acc[tm][b + NB][i] * rr[i];
+                        const float gv = acc_read(acc[tm][b][i]) * rr[i];
+                        const float uv = acc_read(acc[tm][b + NB][i]) * rr[i];
                         v[b][i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
                     } else {
-                        v[b][i] = acc[tm][b][i] * rr[i];
+                        v[b][i] = acc_read(acc[tm][b][i]) * rr[i];
                     }
                 }
         }
