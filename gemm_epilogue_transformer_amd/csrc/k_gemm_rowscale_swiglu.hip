@@ -49,6 +49,14 @@ struct RopeArgs {
     int rot_cols;             // leading rotated columns (whole 64-column heads)
 };
 
+// hook.at<P>() runs after part P of an epilogue (a block pair of the SwiGLU epilogue, a
+// block row of the loss epilogue): a persistent kernel issues a share of the next tile's
+// DMA there.
+struct NoEpiHook {
+    template <int P>
+    __device__ __forceinline__ void at() const {}
+};
+
 // Cross-entropy operands (unused by the other activations).
 struct CeArgs {
     const int32_t* targets;   // [M]
@@ -179,10 +187,11 @@ __device__ __forceinline__ float halves_sum(float x) {
 // the waves sharing a row combine in a fixed order as in ce_epilogue.  rt[tm], tt[tm]:
 // r and the target of the lane's row (0 and -1 past M).  The lane holding a row's target
 // column writes that logit.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN, class Hook = NoEpiHook>
 __device__ __forceinline__ void ce_epilogue_tc(const f32x16_t (&acc)[TM][TN], const float (&rt)[TM],
                                                const int (&tt)[TM], float sw, const CeArgs& ce, int M, int V,
-                                               int m0, int j0, int tile_n, int wm, int wn, float* red) {
+                                               int m0, int j0, int tile_n, int wm, int wn, float* red,
+                                               const Hook& hook = Hook()) {
     acc_read_fence();                       // accumulators are read with acc_read
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, NT = 64 * WAVES_M * WAVES_N;
     int lane = threadIdx.x & 63;
@@ -191,8 +200,8 @@ __device__ __forceinline__ void ce_epilogue_tc(const f32x16_t (&acc)[TM][TN], co
     const float ninf = -__builtin_inff();
     const int nw = j0 + wn * WN;                    // first column of the wave
     const bool full = nw + WN <= V;                 // wave-uniform: no column past V
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
+    static_for<TM>([&](auto TMc) {
+        constexpr int tm = decltype(TMc)::value;
         const float rr = rt[tm] * sw;
         // logits; past V (only in the last column tile) -inf, which adds nothing below
         float z[TN][16];
@@ -240,7 +249,9 @@ __device__ __forceinline__ void ce_epilogue_tc(const f32x16_t (&acc)[TM][TN], co
             red[2 * (wn * BM + rl)] = mx;
             red[2 * (wn * BM + rl) + 1] = sum;
         }
-    }
+        hook.template at<tm>();
+        __builtin_amdgcn_sched_barrier(0);
+    });
     __syncthreads();
     for (int r = threadIdx.x; r < BM; r += NT) {
         const int m = m0 + r;
@@ -731,12 +742,6 @@ __device__ __forceinline__ void rowscale_epilogue(const f32x16_t (&acc)[TM][TN],
 // row; one cross-half lane swap per pair of groups makes them 8, stored with one 16-byte
 // store, with no LDS staging.  Same fp32 operations per element, in the same order, as
 // rowscale_epilogue.
-// hook.at<P>() runs after the stores of gate/up block pair P = tm * TN/2 + b (a persistent
-// kernel issues a share of the next tile's DMA there).
-struct NoEpiHook {
-    template <int P>
-    __device__ __forceinline__ void at() const {}
-};
 template <int BM, int BN, int WAVES_M, int TM, int TN, class Hook = NoEpiHook>
 __device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN], const float (&rt)[TM], float sw,
                                                    uint16_t* __restrict__ Y, int M, int N_out, int m0, int j0,
@@ -1061,6 +1066,100 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
     }
 }
 
+// Persistent form of the LM-head GEMM with the loss epilogue (bf16 weights, transposed
+// accumulator blocks, ce_epilogue_tc), the same tile walk and prologue overlap as the
+// persistent SwiGLU GEMM: the next tile's DMA goes out in four shares, one after each of
+// the epilogue's block rows, and the next tile's row scales and targets load after the
+// epilogue (both through buffer descriptors over [0, M), so every wave issues all of
+// them; a target past M is replaced by -1 after the load).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
+k_gemm_ce_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
+                     const float* __restrict__ w_scale, const float* __restrict__ R, CeArgs ce, int M, int V,
+                     int K, int tiles_m, int tiles_n) {
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int kStage = BM * RB + BN * RB;
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+    __shared__ float ce_red[2 * WAVES_N * BM];
+    uint8_t* st[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) st[i] = stages[i];
+    using FP = FragPair<Frags<Elt::BF16, TM, TN, RB, true>>;
+    using PanelA = DmaPanel<BM, BM, NW, RB>;
+    using PanelB = DmaPanel<BN, BN, NW, RB>;
+
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int kbytes = K * 2;
+    const int ntiles = tiles_m * tiles_n;
+    auto a_row = [&](int tm) { return wm * WM + tm * 32; };
+    auto b_row = [&](int tn) { return wn * WN + tn * 32; };
+    PanelA pa;
+    PanelB pb;
+    int m0 = 0, j0 = 0, tn0 = 0;
+    float rv[TM];                                    // r and target of the lane's row in each block row
+    int tv[TM];
+    auto setup = [&](int t) {
+        int tile_m, tile_n;
+        tile_coords<8>(t, tiles_m, tiles_n, tile_m, tile_n);
+        m0 = tile_m * BM;
+        j0 = tile_n * BN;
+        tn0 = tile_n;
+        const uint8_t* a0 = H + static_cast<size_t>(m0) * kbytes;
+        pa.init(a0, min(BM, M - m0), a0, 0, kbytes);
+        const uint8_t* b0 = W + static_cast<size_t>(j0) * kbytes;
+        pb.init(b0, min(BN, V - j0), b0, 0, kbytes);
+    };
+    const __amdgpu_buffer_rsrc_t r_rsrc = make_buffer_rsrc(R, static_cast<uint32_t>(M) * 4u);
+    const __amdgpu_buffer_rsrc_t t_rsrc = make_buffer_rsrc(ce.targets, static_cast<uint32_t>(M) * 4u);
+    auto load_rows = [&]() {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * WM + 32 * i + (threadIdx.x & 31);
+            const uint32_t off = static_cast<uint32_t>(m) * 4u;
+            rv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_rsrc, off, 0, 0));
+            const int x = __builtin_amdgcn_raw_buffer_load_b32(t_rsrc, off, 0, 0);
+            tv[i] = m < M ? x : -1;
+        }
+    };
+    using Pro = DmaPrologue<FP, BM, NS, RB, SPREAD, TM, TN, PanelA, PanelB>;
+    const Pro pro{pa, pb, kbytes, kbytes, st};
+    const float sw = w_scale ? *w_scale : 1.0f;
+    int t = blockIdx.x;                              // the grid holds at most ntiles workgroups
+    setup(t);
+    static_for<Pro::kOps>([&](auto Q) { pro.template issue<decltype(Q)::value>(); });
+    auto pend = pro.template pending<2 * TM>();
+    load_rows();
+    for (; t < ntiles; t += gridDim.x) {
+        f32x16_t acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        mainloop_dma_run<FP, BM, BN, BN, NS, NW, RB, RB, SPREAD>(acc, pa, pb, kbytes, kbytes, st, a_row, b_row, pend);
+        const int cm0 = m0, cj0 = j0, ctn = tn0;
+        float rc[TM];
+        int tc[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            rc[i] = rv[i];
+            tc[i] = tv[i];
+        }
+        const bool more = t + static_cast<int>(gridDim.x) < ntiles;     // uniform over the workgroup
+        if (more) setup(t + gridDim.x);
+        ce_epilogue_tc<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rc, tc, sw, ce, M, V, cm0, cj0, ctn, wm, wn, ce_red,
+                                                         ProHook<Pro, TM>{pro, more});
+        if (more) {
+            pend = pro.template pending<2 * TM>();
+            load_rows();
+        }
+    }
+}
+
 // Tile configurations of the second GEMM (compile-time).
 #ifndef CODA_G3_BM
 #define CODA_G3_BM 256
@@ -1082,6 +1181,9 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
 #endif
 #ifndef CODA_G3_PERSIST
 #define CODA_G3_PERSIST 1   // forward SwiGLU on bf16 weights: the persistent kernel
+#endif
+#ifndef CODA_G3_PERSIST_CE
+#define CODA_G3_PERSIST_CE 1   // the loss epilogue on bf16 weights: the persistent kernel
 #endif
 constexpr int BM3 = CODA_G3_BM, BN3 = CODA_G3_BN, NS3 = CODA_G3_NS, OCC3 = CODA_G3_OCC;
 constexpr int WM3 = CODA_G3_WM, WN3 = CODA_G3_WN, RB3 = CODA_G3_RB, SP3 = CODA_G3_SPREAD, PIPE3 = CODA_G3_PIPE;
@@ -1186,6 +1288,17 @@ hipError_t launch_gemm_rowscale_ce(int M, int V, int K, const void* h, const voi
     const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
     const CeArgs ce{targets, partials, tgt_logit, static_cast<int>(ce_partials_per_row(V))};
     const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
+    if (!w_fp8 && CODA_G3_PERSIST_CE && CODA_G3_TC && CODA_G3_TC_CE && PIPE3 == 0) {
+        const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (V + BN3 - 1) / BN3;
+        int cus = 0;
+        const hipError_t e = cu_count(&cus);
+        if (e != hipSuccess) return e;
+        const int grid = std::min(tiles_m * tiles_n, std::max(cus, 1));
+        hipLaunchKernelGGL((k_gemm_ce_persistent<BM3, BN3, WM3, WN3, NS3, RB3, SP3>), dim3(grid),
+                           dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
+                           static_cast<const uint8_t*>(W), w_scale, r, ce, M, V, K, tiles_m, tiles_n);
+        return hipGetLastError();
+    }
     return w_fp8 ? launch3<kActCe, true>(M, V, K, h, W, w_scale, r, nullptr, none, ce, no_bw, stream)
                  : launch3<kActCe, false>(M, V, K, h, W, w_scale, r, nullptr, none, ce, no_bw, stream);
 }
