@@ -59,6 +59,9 @@ SMALL = [
     (257, 72, 264, 2916, "bf16"),     # last tile: the second wave's 128 columns lie past V
     (64, 48, 128, 1, "bf16"),         # one-column vocabulary: lse = z, loss = 0
     (130, 64, 144, 513, "e4m3"),
+    # more tiles than compute units (the persistent kernel walks several per workgroup) and
+    # a last row tile holding one row (some waves' rows all lie past M)
+    (257, 64, 128, 33280, "bf16"),
 ]
 
 
