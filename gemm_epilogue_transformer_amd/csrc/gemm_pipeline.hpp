@@ -178,13 +178,16 @@ struct Frags<Elt::BF16, TM, TN, RB, TC> {
 #pragma unroll
         for (int i = 0; i < kReads; ++i) load_one(i, sA, sB, s, a_row, b_row);
     }
-    // MFMA i of the k-step: block (i / TN, i % TN)
+    // MFMA i of the k-step: block (i / TN, i % TN); Z: the block starts from zero (the
+    // MFMA's C operand is the inline constant 0, so the block needs no zeroing before)
+    template <bool Z = false>
     __device__ __forceinline__ void mma_one(int i, f32x16_t (&acc)[TM][TN]) const {
         const int tm = i / TN, tn = i % TN;
+        const f32x16_t c = Z ? f32x16_t{} : acc[tm][tn];
         if constexpr (TC)
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[tn], a[tm], acc[tm][tn], 0, 0, 0);
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[tn], a[tm], c, 0, 0, 0);
         else
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], c, 0, 0, 0);
     }
     __device__ __forceinline__ void mma(f32x16_t (&acc)[TM][TN]) const {
 #pragma unroll
@@ -219,11 +222,12 @@ struct Frags<Elt::E4M3, TM, TN, RB, false> {
 #pragma unroll
         for (int i = 0; i < kReads; ++i) load_one(i, sA, sB, s, a_row, b_row);
     }
+    template <bool Z = false>
     __device__ __forceinline__ void mma_one(int i, f32x16_t (&acc)[TM][TN]) const {
         const int tm = i / TN, tn = i % TN;
         // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
-        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[tm], b[tn], acc[tm][tn], 0, 0, 0,
-                                                                      127, 0, 127);
+        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[tm], b[tn], Z ? f32x16_t{} : acc[tm][tn],
+                                                                      0, 0, 0, 127, 0, 127);
     }
     __device__ __forceinline__ void mma(f32x16_t (&acc)[TM][TN]) const {
 #pragma unroll
@@ -345,9 +349,10 @@ struct FragsTok {
 #pragma unroll
         for (int i = 0; i < kReads; ++i) load_one(i, sA, sB, s, a_row, b_row);
     }
+    template <bool Z = false>
     __device__ __forceinline__ void mma_one(int i, f32x16_t (&acc)[TM][TN]) const {
         const int tm = i / TN, tn = i % TN;
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], Z ? f32x16_t{} : acc[tm][tn], 0, 0, 0);
     }
 };
 
@@ -378,9 +383,9 @@ struct FragPair {
                                          const ARow& a_row, const BRow& b_row) {
         f[p].load(sA, sB, s, a_row, b_row);
     }
-    template <int TM, int TN>
+    template <bool Z = false, int TM, int TN>
     __device__ __forceinline__ void mma_one(int p, int j, f32x16_t (&acc)[TM][TN]) const {
-        f[p].mma_one(j, acc);
+        f[p].template mma_one<Z>(j, acc);
     }
 };
 
@@ -436,9 +441,11 @@ struct FragsW8 {
                                          const ARow& a_row, const BRow& b_row) {
         static_for<kMfma>([&](auto J) { slot<decltype(J)::value>(p, sA, sB, s, a_row, b_row); });
     }
+    template <bool Z = false>
     __device__ __forceinline__ void mma_one(int p, int i, f32x16_t (&acc)[TM][TN]) const {
         const int tm = i / TN, tn = i % TN;
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p][tm], b[p][tn], acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p][tm], b[p][tn], Z ? f32x16_t{} : acc[tm][tn],
+                                                              0, 0, 0);
     }
 };
 
@@ -585,10 +592,11 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
     constexpr int KS = D::KS, kMfma = D::kMfma, nA = D::nA, kPerTile = D::kPerTile, kPer = D::kPer;
     const int nk = (kbytes + RBA - 1) / RBA;
     // k-tiles run in groups of NS (one per stage); the count is padded to a multiple of NS
-    // with k-tiles past K, which the DMA fills with zeros.  The DMA always runs NS tiles
+    // with k-tiles past K, which the DMA fills with zeros, and is at least one group (K = 0
+    // computes a group of zeros, so acc is always written).  The DMA always runs NS tiles
     // ahead, past the padded end too (zeros into stages that are not read again), so the
     // wait counts are exact on every tile.
-    const int ng = (nk + NS - 1) / NS;
+    const int ng = max((nk + NS - 1) / NS, 1);
     constexpr int kOffB = BM * RBA;          // B panel offset inside a stage
     FP f;
     auto issue_q = [&](int q, uint8_t* stage, const auto& ba, const auto& bb) {
@@ -601,7 +609,11 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
     __syncthreads();
     f.load(0, st[0], st[0] + kOffB, 0, a_row, b_row);
 
-    for (int g = 0; g < ng; ++g) {
+    // group(First, g): the NS k-tiles of group g.  The first group is peeled: its first
+    // k-step's MFMAs take a zero C operand, so acc's contents on entry are never read (the
+    // callers' zero fill is dead code and no accumulator is written before the first MFMA).
+    auto group = [&](auto FirstC, int g) {
+        constexpr bool kFirst = decltype(FirstC)::value;
         static_for<NS>([&](auto I) {
             constexpr int i = decltype(I)::value;
             constexpr int par = (i * KS) & 1;     // k-step s of this tile uses f[(par + s) & 1]
@@ -615,7 +627,7 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
                 // fragment read j of k-step s+1
                 static_for<kMfma>([&](auto J) {
                     constexpr int j = decltype(J)::value;
-                    f.mma_one((par + s) & 1, j, acc);
+                    f.template mma_one<kFirst && i == 0 && s == 0>((par + s) & 1, j, acc);
                     if constexpr (s + 1 < SPREAD && j < kPer && (s + 1) * kPer + j < kPerTile)
                         issue_q((s + 1) * kPer + j, prv, pend_a, pend_b);
                     f.template slot<j>((par + s + 1) & 1, cur, cur + kOffB, s + 1, a_row, b_row);
@@ -635,6 +647,7 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
             // MFMA j, then DMA instruction j of tile kt+NS into this tile's stage (the
             // first kPer; the rest follow in tile kt+1), then fragment read j of tile
             // kt+1's first k-step
+            static_assert(KS >= 2, "the tile-crossing k-step is not the first");
             static_for<kMfma>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 f.mma_one((par + KS - 1) & 1, j, acc);
@@ -643,7 +656,9 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
-    }
+    };
+    group(std::true_type{}, 0);
+    for (int g = 1; g < ng; ++g) group(std::false_type{}, g);
     // drain the DMA that ran past the end before the LDS is reused or released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();

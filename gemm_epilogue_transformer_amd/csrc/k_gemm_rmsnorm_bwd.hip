@@ -86,6 +86,7 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
         return n < N ? static_cast<uint32_t>(tr) * row_bytes + static_cast<uint32_t>(n) * 2 : kOobOffset;
     };
     i32x4_t hv[2][S::kSegPerLane], gv[2][S::kSegPerLane];
+    acc_read_fence();
 #pragma unroll
     for (int j = 0; j < S::kSegPerLane; ++j) {
         hv[0][j] = __builtin_amdgcn_raw_buffer_load_b128(h_rsrc, seg_voff(0, j), 0, 0);
@@ -104,7 +105,7 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[tn][i] = acc[tm][tn][i];
+            for (int i = 0; i < 16; ++i) v[tn][i] = acc_read(acc[tm][tn][i]);
         S::put(slab, v);
 #pragma unroll
         for (int j = 0; j < S::kSegPerLane; ++j) {

@@ -125,6 +125,7 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
         return col_in ? tr * wrow + col * 2u : kOobOffset;
     };
     i32x4_t wb[2][S::kSegPerLane];
+    acc_read_fence();
     if (Wraw) {
 #pragma unroll
         for (int j = 0; j < S::kSegPerLane; ++j) wb[0][j] = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off(0, j), 0, 0);
@@ -140,7 +141,7 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[tn][i] = acc[tm][tn][i];
+            for (int i = 0; i < 16; ++i) v[tn][i] = acc_read(acc[tm][tn][i]);
         S::put(slab, v);
 #pragma unroll
         for (int j = 0; j < S::kSegPerLane; ++j) {
