@@ -664,6 +664,93 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
     __syncthreads();
 }
 
+// Continuous mainloop of a persistent kernel (two stages): the k-tiles 1 .. nkp-1 of the
+// current tile (panels pa, pb), whose k-tile 0 the caller has already multiplied into acc
+// (it does so during the previous tile's epilogue), and the first loads of the next tile
+// (panels na, nb): the DMA stream does not stop at the tile's end, so the crossings of
+// k-tiles nkp-2 and nkp-1 load the next tile's k-tiles 0 and 1 into the stages they free.
+// nkp is the k-tile count padded to an even number (k-tile kt lives in stage kt & 1); the
+// caller guarantees nkp >= 4.
+//
+// On entry: k-tile 1 has landed for every wave (the caller waited and passed a barrier
+// after issuing its last DMA instruction), the stage of k-tile 0 may still be read by
+// other waves.  On return: the next tile's k-tile 0 has landed in stage 0 (every wave
+// waited and passed the barrier), f[0] holds its first k-step's fragments, and the DMA of
+// its k-tile 1 into stage 1 has issued its first kPer instructions; the returned offsets
+// are that k-tile's, for the caller to issue instructions kPer .. kPerTile-1.
+//
+// The crossing at the end of k-tile kt waits with vmcnt(0) (with two stages nothing later
+// than k-tile kt+1's DMA has been issued but stores and the caller's loads), passes the
+// barrier, runs kt's last k-step with the first share of k-tile kt+2's DMA and the reads of
+// kt+1's first k-step; the rest of kt+2's DMA goes out during kt+1's first SPREAD-1 k-steps.
+template <class FP, int BM, int RBA, int SPREAD, int TM, int TN, class ARow, class BRow, class PA, class PB>
+__device__ __forceinline__ auto mainloop_dma_cont(f32x16_t (&acc)[TM][TN], FP& f, const PA& pa, const PB& pb,
+                                                  const PA& na, const PB& nb, int kbytes, uint8_t* const (&st)[2],
+                                                  const ARow& a_row, const BRow& b_row) {
+    using D = DmaSched<FP, 2, SPREAD, TM, TN, PA, PB>;
+    constexpr int KS = D::KS, kMfma = D::kMfma, nA = D::nA, kPerTile = D::kPerTile, kPer = D::kPer;
+    static_assert(KS % 2 == 0, "fragment parity: k-step 0 of every k-tile uses f[0]");
+    constexpr int kOffB = BM * RBA;
+    const int nkp = (((kbytes + RBA - 1) / RBA) + 1) & ~1;
+    using Off = DmaPending<decltype(pa.base_offset(0, kbytes)), decltype(pb.base_offset(0, kbytes))>;
+    auto issue = [&](const PA& A, const PB& B, int q, uint8_t* stage, const Off& o) {
+        if (q < nA) A.issue_one(q, stage, o.a);
+        else B.issue_one(q - nA, stage + kOffB, o.b);
+    };
+    // k-steps 0 .. KS-2 of a k-tile in stage S, with the rest of the pending DMA (into the
+    // other stage, panels A / B)
+    auto steps = [&](auto SC, const PA& A, const PB& B, const Off& o) {
+        constexpr int S = decltype(SC)::value;
+        uint8_t* cur = st[S];
+        uint8_t* oth = st[S ^ 1];
+        static_for<KS - 1>([&](auto Sc) {
+            constexpr int s = decltype(Sc)::value;
+            static_for<kMfma>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                f.mma_one(s & 1, j, acc);
+                if constexpr (s + 1 < SPREAD && j < kPer && (s + 1) * kPer + j < kPerTile)
+                    issue(A, B, (s + 1) * kPer + j, oth, o);
+                f.template slot<j>((s + 1) & 1, cur, cur + kOffB, s + 1, a_row, b_row);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    };
+    // the crossing at the end of the k-tile in stage S (MMA: its last k-step; without, the
+    // caller has run it): DMA of k-tile dkt of panels A / B into stage S
+    auto crossing = [&](auto SC, auto MmaC, const PA& A, const PB& B, int dkt) {
+        constexpr int S = decltype(SC)::value;
+        constexpr bool kMma = decltype(MmaC)::value;
+        if constexpr (kMma) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));     // k-tile kt+1 landed
+        __syncthreads();                                                     // ... for every wave
+        __builtin_amdgcn_sched_barrier(0);
+        const Off o{A.base_offset(dkt, kbytes), B.base_offset(dkt, kbytes)};
+        uint8_t* nxt = st[S ^ 1];
+        static_for<kMfma>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            if constexpr (kMma) f.mma_one((KS - 1) & 1, j, acc);
+            if constexpr (j < kPer) issue(A, B, j, st[S], o);
+            f.template slot<j>(0, nxt, nxt + kOffB, 0, a_row, b_row);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        return o;
+    };
+    Off o = crossing(std::integral_constant<int, 0>{}, std::false_type{}, pa, pb, 2);
+    int kt = 1;
+    for (; kt < nkp - 3; kt += 2) {
+        steps(std::integral_constant<int, 1>{}, pa, pb, o);
+        o = crossing(std::integral_constant<int, 1>{}, std::true_type{}, pa, pb, kt + 2);
+        steps(std::integral_constant<int, 0>{}, pa, pb, o);
+        o = crossing(std::integral_constant<int, 0>{}, std::true_type{}, pa, pb, kt + 3);
+    }
+    // k-tiles nkp-3, nkp-2, nkp-1: the last two crossings load the next tile's k-tiles 0, 1
+    steps(std::integral_constant<int, 1>{}, pa, pb, o);
+    o = crossing(std::integral_constant<int, 1>{}, std::true_type{}, pa, pb, kt + 2);
+    steps(std::integral_constant<int, 0>{}, pa, pb, o);
+    o = crossing(std::integral_constant<int, 0>{}, std::true_type{}, na, nb, 0);
+    steps(std::integral_constant<int, 1>{}, na, nb, o);
+    return crossing(std::integral_constant<int, 1>{}, std::true_type{}, na, nb, 1);
+}
+
 template <class FP, int BM, int BN, int SPLIT, int NS, int NW, int RBA, int RBB, int SPREAD, int TM, int TN,
           class ARow, class BRow, class PA, class PB, class X = NoExtra>
 __device__ __forceinline__ void mainloop_dma_fp(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,

@@ -1066,6 +1066,289 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
     }
 }
 
+// Output staging of the overlapped SwiGLU GEMM: one wave's slab in LDS (two halves of
+// 4 KB), each half one block row of the tile, i.e. 32 rows x the wave's 64 output columns
+// (128 bytes per row).  16-byte chunk c of slab row r lies at r*128 + (c ^ ((r >> 1) & 7))*16,
+// so both the epilogue's row-wise writes (16 rows at one chunk per 16 lanes) and the
+// line-wise reads (2 rows x 8 chunks) are conflict-free.  Block row tm is stored by four
+// instructions, store i covering rows 8i .. 8i+7 with 8 lanes per 128-byte row (lane l:
+// row 8i + l/8, chunk l%8); the transposed accumulator layout alone would give 32 rows x
+// 32 bytes per instruction.
+struct YSlab {
+    uint8_t* ys;                     // this wave's slab
+    __amdgpu_buffer_rsrc_t rsrc;     // y rows [m0, m0 + valid rows) of the tile
+    uint32_t row_bytes;
+    int row0, col0, n_out;           // the wave's first row (tile-relative) and output column
+    __device__ __forceinline__ static int off(int hf, int r, int c) {
+        return hf * 4096 + r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    }
+    // store i of block row tm from half hf
+    __device__ __forceinline__ void store(int hf, int tm, int i) const {
+        const int lane = threadIdx.x & 63;
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(ys + off(hf, r, c));
+        const uint32_t row_off = static_cast<uint32_t>(row0 + tm * 32 + r) * row_bytes;
+        const int n = col0 + c * 8;
+        const uint32_t voff = n < n_out ? row_off + static_cast<uint32_t>(n) * 2 : kOobOffset;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voff, 0, 0);
+    }
+};
+
+// One tile boundary of the overlapped persistent SwiGLU GEMM (k_gemm_swiglu_ovl):
+// EPI: the SwiGLU epilogue of the tile whose sums acc holds (row scales rt, origin m0, j0),
+// the arithmetic of swiglu_epilogue_tc in the same order, its output through the slab
+// (YSlab);
+// MMA: the next tile's k-tile 0 (stage 0; its first k-step's fragments in f.f[0], the
+// other k-steps read here) multiplied into acc block pair by block pair, each pair right
+// after the epilogue has read its accumulators out (a zero C operand starts the pair), so
+// the matrix cores run while the epilogue's VALU work does; the rest of the next tile's
+// k-tile 1 DMA (instructions kPer .. kPerTile-1, offsets o) is issued over the first
+// pairs, and after pair HOLD-1 the wave waits for it (vmcnt 0: no store has been issued
+// yet, the first HOLD / NB block rows wait in the slab) and passes a barrier, so that
+// k-tile 1 has landed for every wave when the next mainloop starts; the later block rows
+// leave as soon as they are complete.
+template <bool EPI, bool MMA, int BM, int BN, int WAVES_M, int TM, int TN, int RB, int SPREAD, int HOLD, class FP,
+          class PA, class PB, class Off, class ARow, class BRow>
+__device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], const FP& f, const float (&rt)[TM],
+                                                     float sw, uint16_t* __restrict__ Y, int M, int N_out, int m0,
+                                                     int j0, int wm, int wn, const PA& pa, const PB& pb,
+                                                     const Off& o, uint8_t* const (&st)[2], uint8_t* ys,
+                                                     const ARow& a_row, const BRow& b_row) {
+    using D = DmaSched<FP, 2, SPREAD, TM, TN, PA, PB>;
+    constexpr int KS = D::KS, kPer = D::kPer, kPerTile = D::kPerTile, nA = D::nA;
+    constexpr int kRest = kPerTile - kPer;          // DMA instructions of k-tile 1 still to issue
+    constexpr int kRestParts = 3;                   // ... spread over the first three pairs
+    constexpr int WM = BM / WAVES_M;
+    constexpr int NB = TN / 2;
+    constexpr int NP = TM * NB;                     // block pairs
+    constexpr int kHeldRows = HOLD / NB;            // block rows stored after the wait
+    static_assert(!MMA || (HOLD >= kRestParts && HOLD <= NP), "the wait follows the last DMA share");
+    static_assert(NB == 2 && HOLD % NB == 0 && HOLD / NB <= 2,
+                  "a block row fills one slab half; the held block rows fit the two halves");
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int lr = lane & 31, lh = lane >> 5;
+    const int valid_rows = min(BM, M - m0);
+    const uint32_t row_bytes = static_cast<uint32_t>(N_out) * 2;
+    const YSlab ysl{ys,
+                    make_buffer_rsrc(Y + static_cast<size_t>(m0) * N_out,
+                                     EPI ? static_cast<uint32_t>(valid_rows) * row_bytes : 0u),
+                    row_bytes, wm * WM, j0 + wn * NB * 32, N_out};
+    // fragments of k-steps 1 .. KS-1 of the next tile's k-tile 0: every B block, A per block row
+    const uint8_t* sA = st[0];
+    const uint8_t* sB = st[0] + BM * RB;
+    bf16x8_t bq[KS - 1][TN], aq[KS - 1];
+    if constexpr (MMA) {
+        static_for<KS - 1>([&](auto Sc) {
+            constexpr int s = decltype(Sc)::value + 1;
+            static_for<TN>([&](auto Tc) {
+                constexpr int tn = decltype(Tc)::value;
+                bq[s - 1][tn] = *reinterpret_cast<const bf16x8_t*>(sB + swz<RB>(b_row(tn) + lr, 2 * s + lh));
+            });
+        });
+    }
+    if constexpr (EPI) acc_read_fence();
+    static_for<TM>([&](auto TMc) {
+        constexpr int tm = decltype(TMc)::value;
+        if constexpr (MMA) {
+            static_for<KS - 1>([&](auto Sc) {
+                constexpr int s = decltype(Sc)::value + 1;
+                aq[s - 1] = *reinterpret_cast<const bf16x8_t*>(sA + swz<RB>(a_row(tm) + lr, 2 * s + lh));
+            });
+        }
+        const float rr = EPI ? rt[tm] * sw : 0.0f;
+        static_for<NB>([&](auto Bc) {
+            constexpr int b = decltype(Bc)::value;
+            constexpr int p = tm * NB + b;
+            float gv[16], uv[16];
+            if constexpr (EPI) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    gv[i] = acc_read(acc[tm][b][i]);
+                    uv[i] = acc_read(acc[tm][b + NB][i]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (MMA) {
+                // the pair's blocks of the next tile: k-step 0 from f.f[0], then aq / bq
+                static_for<KS>([&](auto Sc) {
+                    constexpr int s = decltype(Sc)::value;
+                    static_for<2>([&](auto Xc) {
+                        constexpr int x = b + decltype(Xc)::value * NB;
+                        const bf16x8_t av = s == 0 ? f.f[0].a[tm] : aq[s - 1 < 0 ? 0 : s - 1];
+                        const bf16x8_t bv = s == 0 ? f.f[0].b[x] : bq[s - 1 < 0 ? 0 : s - 1][x];
+                        acc[tm][x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, s == 0 ? f32x16_t{} : acc[tm][x],
+                                                                             0, 0, 0);
+                    });
+                });
+            }
+            if constexpr (EPI) {
+                uint32_t pk[4][2];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float gs = gv[4 * g + e] * rr;
+                        const float us = uv[4 * g + e] * rr;
+                        v[e] = gs * __builtin_amdgcn_rcpf(1.0f + __expf(-gs)) * us;
+                    }
+                    pk[g][0] = pack_bf16x2(v[0], v[1]);
+                    pk[g][1] = pack_bf16x2(v[2], v[3]);
+                }
+                static_for<2>([&](auto Qc) {
+                    constexpr int q = decltype(Qc)::value;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const auto sw2 = __builtin_amdgcn_permlane32_swap(pk[2 * q][h], pk[2 * q + 1][h], false, false);
+                        w[h] = sw2[0];
+                        w[2 + h] = sw2[1];
+                    }
+                    // lane (row lr, half lh) holds chunk 4b + 2q + lh of its row
+                    *reinterpret_cast<i32x4_t*>(ys + YSlab::off(tm & 1, lr, 4 * b + 2 * q + lh)) =
+                        i32x4_t{int(w[0]), int(w[1]), int(w[2]), int(w[3])};
+                });
+                // a complete block row leaves at once unless it is held for the wait
+                if constexpr (b == NB - 1 && !(MMA && tm < kHeldRows))
+                    static_for<4>([&](auto Ic) { ysl.store(tm & 1, tm, Ic); });
+            }
+            if constexpr (MMA) {
+                static_for<kRest>([&](auto Qc) {
+                    constexpr int q = decltype(Qc)::value;
+                    if constexpr (q * kRestParts / kRest == p) {
+                        constexpr int qq = kPer + q;
+                        if constexpr (qq < nA) pa.issue_one(qq, st[1], o.a);
+                        else pb.issue_one(qq - nA, st[1] + BM * RB, o.b);
+                    }
+                });
+                if constexpr (p == HOLD - 1) {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // k-tile 1 landed (no store issued yet)
+                    __syncthreads();                               // ... for every wave
+                    if constexpr (EPI) {
+                        static_for<kHeldRows>([&](auto Tc) {
+                            constexpr int th = decltype(Tc)::value;
+                            static_for<4>([&](auto Ic) { ysl.store(th & 1, th, Ic); });
+                        });
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    });
+}
+
+// Persistent SwiGLU GEMM with the epilogue overlapped (bf16 weights, transposed
+// accumulator blocks): the tile walk of k_gemm_swiglu_persistent, the DMA stream running
+// across tiles (mainloop_dma_cont loads the next tile's k-tiles 0 and 1 in the current
+// tile's last two crossings), and each tile's epilogue fused with the next tile's k-tile 0
+// (swiglu_epilogue_ovl).  The first tile's k-tile 0 runs alone, the last tile's epilogue
+// alone.  A tile's row scales load once its predecessor's epilogue is done.  Needs at
+// least 4 k-tiles (K > 128); when this workgroup has no next tile the "next" panels are the
+// current ones (their loads are in bounds and never used).  LDS: the two 64 KB stages and
+// four 8 KB output slabs, the whole 160 KB.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int RB, int SPREAD, int HOLD>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
+k_gemm_swiglu_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
+                  const float* __restrict__ R, uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
+                  int tiles_n) {
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int BNO = BN / 2;
+    static_assert(TN % 2 == 0, "SwiGLU pairs gate and up blocks");
+    static_assert(WN == 128, "a wave's 64 output columns are one 128-byte row segment");
+    constexpr int kStage = BM * RB + BN * RB;
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[2][kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t yslab[NW][8192];
+    uint8_t* st[2] = {stages[0], stages[1]};
+    using FP = FragPair<Frags<Elt::BF16, TM, TN, RB, true>>;
+    using PanelA = DmaPanel<BM, BM, NW, RB>;
+    using PanelB = DmaPanel<BN, BN / 2, NW, RB>;
+    using D = DmaSched<FP, 2, SPREAD, TM, TN, PanelA, PanelB>;
+
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    uint8_t* ys = yslab[wave];
+    const int kbytes = K * 2;
+    const int ntiles = tiles_m * tiles_n;
+    const int G = gridDim.x;
+    auto a_row = [&](int tm) { return wm * WM + tm * 32; };
+    auto b_row = [&](int tn) {
+        constexpr int TH = TN / 2;
+        return (tn < TH ? 0 : BN / 2) + wn * TH * 32 + (tn % TH) * 32;
+    };
+    auto setup = [&](int t, PanelA& A, PanelB& B, int& tm0, int& tj0) {
+        int tile_m, tile_n;
+        tile_coords<8>(t, tiles_m, tiles_n, tile_m, tile_n);
+        tm0 = tile_m * BM;
+        tj0 = tile_n * BNO;
+        const uint8_t* a0 = H + static_cast<size_t>(tm0) * kbytes;
+        A.init(a0, min(BM, M - tm0), a0, 0, kbytes);
+        const uint8_t* g0 = W + static_cast<size_t>(tj0) * kbytes;
+        const uint8_t* u0 = W + static_cast<size_t>(N_out + tj0) * kbytes;
+        B.init(g0, min(BNO, N_out - tj0), u0, min(BNO, N_out - tj0), kbytes);
+    };
+    const __amdgpu_buffer_rsrc_t r_rsrc = make_buffer_rsrc(R, static_cast<uint32_t>(M) * 4u);
+    float rv[TM];
+    auto load_r = [&](int tm0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const uint32_t m = static_cast<uint32_t>(tm0 + wm * WM + 32 * i + (threadIdx.x & 31));
+            rv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_rsrc, m * 4u, 0, 0));
+        }
+    };
+    const float sw = w_scale ? *w_scale : 1.0f;
+    PanelA pa, na;
+    PanelB pb, nb;
+    int m0 = 0, j0 = 0, nm0 = 0, nj0 = 0;
+    int t = blockIdx.x;                              // the grid holds at most ntiles workgroups
+    setup(t, pa, pb, m0, j0);
+    if (t + G < ntiles) setup(t + G, na, nb, nm0, nj0);
+    else { na = pa; nb = pb; }
+    // k-tile 0 of the first tile and the first share of its k-tile 1
+    using Off = DmaPending<decltype(pa.base_offset(0, kbytes)), decltype(pb.base_offset(0, kbytes))>;
+    {
+        const Off o0{pa.base_offset(0, kbytes), pb.base_offset(0, kbytes)};
+        static_for<D::kPerTile>([&](auto Qc) {
+            constexpr int q = decltype(Qc)::value;
+            if constexpr (q < D::nA) pa.issue_one(q, st[0], o0.a);
+            else pb.issue_one(q - D::nA, st[0] + BM * RB, o0.b);
+        });
+    }
+    Off o{pa.base_offset(1, kbytes), pb.base_offset(1, kbytes)};
+    static_for<D::kPer>([&](auto Qc) {
+        constexpr int q = decltype(Qc)::value;
+        if constexpr (q < D::nA) pa.issue_one(q, st[1], o.a);
+        else pb.issue_one(q - D::nA, st[1] + BM * RB, o.b);
+    });
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(D::kPer));    // k-tile 0 landed
+    __syncthreads();
+    FP f;
+    f.load(0, st[0], st[0] + BM * RB, 0, a_row, b_row);
+    f32x16_t acc[TM][TN];
+    swiglu_epilogue_ovl<false, true, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
+        acc, f, rv, sw, Y, M, N_out, m0, j0, wm, wn, pa, pb, o, st, ys, a_row, b_row);
+    load_r(m0);
+    for (;;) {
+        o = mainloop_dma_cont<FP, BM, RB, SPREAD, TM, TN>(acc, f, pa, pb, na, nb, kbytes, st, a_row, b_row);
+        const int cm0 = m0, cj0 = j0;                // the tile whose sums acc holds
+        t += G;
+        if (t >= ntiles) break;                      // uniform over the workgroup
+        pa = na;
+        pb = nb;
+        m0 = nm0;
+        j0 = nj0;
+        if (t + G < ntiles) setup(t + G, na, nb, nm0, nj0);
+        swiglu_epilogue_ovl<true, true, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
+            acc, f, rv, sw, Y, M, N_out, cm0, cj0, wm, wn, pa, pb, o, st, ys, a_row, b_row);
+        load_r(m0);
+    }
+    swiglu_epilogue_ovl<true, false, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
+        acc, f, rv, sw, Y, M, N_out, m0, j0, wm, wn, pa, pb, o, st, ys, a_row, b_row);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));       // the unused loads of the last crossings
+}
+
 // Persistent form of the LM-head GEMM with the loss epilogue (bf16 weights, transposed
 // accumulator blocks, ce_epilogue_tc), the same tile walk and prologue overlap as the
 // persistent SwiGLU GEMM: the next tile's DMA goes out in four shares, one after each of
@@ -1179,6 +1462,12 @@ k_gemm_ce_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ 
 #ifndef CODA_G3_NS8
 #define CODA_G3_NS8 2
 #endif
+#ifndef CODA_G3_OVL
+#define CODA_G3_OVL 1       // ... with the epilogue overlapped (K > 128)
+#endif
+#ifndef CODA_G3_HOLD
+#define CODA_G3_HOLD 4      // block pairs whose stores wait for the next tile's k-tile 1
+#endif
 #ifndef CODA_G3_PERSIST
 #define CODA_G3_PERSIST 1   // forward SwiGLU on bf16 weights: the persistent kernel
 #endif
@@ -1256,6 +1545,13 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
         const hipError_t e = cu_count(&cus);
         if (e != hipSuccess) return e;
         const int grid = std::min(tiles_m * tiles_n, std::max(cus, 1));
+        if (CODA_G3_OVL && NS3 == 2 && 2 * K > 2 * RB3) {     // at least 3 k-tiles (4 padded)
+            hipLaunchKernelGGL((k_gemm_swiglu_ovl<BM3, BN3, WM3, WN3, RB3, SP3, CODA_G3_HOLD>), dim3(grid),
+                               dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
+                               static_cast<const uint8_t*>(W), w_scale, r, static_cast<uint16_t*>(y), M, N_out, K,
+                               tiles_m, tiles_n);
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL((k_gemm_swiglu_persistent<BM3, BN3, WM3, WN3, NS3, RB3, SP3>), dim3(grid),
                            dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
                            static_cast<const uint8_t*>(W), w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m,

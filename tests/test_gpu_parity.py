@@ -129,12 +129,15 @@ def test_chain_small_all_rows(M, K1, d, N2w, act, dtype):
     check_chain(w, inp, h, P, r, y)
 
 
-def test_many_tiles_per_workgroup_all_rows():
+@pytest.mark.parametrize("d", [128, 192, 328])
+def test_many_tiles_per_workgroup_all_rows(d):
     """More output tiles than CUs, not a multiple of them (17 x 31 = 527 tiles of 256 x 128
     outputs): the forward SwiGLU GEMM's persistent workgroups take two or three tiles each,
     the last pass over the CUs filling them partly; every row is checked, so a tile skipped
-    or written twice by the tile loop fails."""
-    w = si.custom(4196, 72, 192, 2 * 3880, si.ACT_SWIGLU, seed=4196)
+    or written twice by the tile loop fails.  d = 128 (2 k-tiles) runs the persistent
+    kernel, d = 192 (3 k-tiles, the fewest it takes) and d = 328 (6 k-tiles, the last one
+    ragged) the one whose epilogues overlap the next tile's first k-tile."""
+    w = si.custom(4196, 72, d, 2 * 3880, si.ACT_SWIGLU, seed=4196 + d)
     _log(f"chain many tiles {w.name}")
     inp = si.generate(w)
     dd = upload(inp)
