@@ -1443,6 +1443,255 @@ k_gemm_ce_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ 
     }
 }
 
+// One tile boundary of the overlapped LM-head GEMM with the loss epilogue (k_gemm_ce_ovl),
+// as swiglu_epilogue_ovl for the SwiGLU GEMM:
+// EPI: the loss statistics of the tile whose sums acc holds (ce_epilogue_tc's arithmetic
+// in the same order: per block row the logits r*s*acc, columns past V at -inf, the row's
+// max and sum of exponentials over the wave's columns, the target's logit; then across the
+// waves of a row through red, one (max, sum) partial per row and tile);
+// MMA: the next tile's k-tile 0 multiplied into acc block row by block row, each right
+// after the epilogue has read that block row out, and the rest of the next tile's k-tile 1
+// DMA issued over the first block rows; the barrier that precedes the cross-wave step
+// follows a wait for that DMA (vmcnt 0: only the rare target-logit stores can be in
+// flight), so k-tile 1 has landed for every wave when the next mainloop starts.
+template <bool EPI, bool MMA, int BM, int BN, int WAVES_M, int WAVES_N, int TM, int TN, int RB, int SPREAD,
+          class FP, class PA, class PB, class Off, class ARow, class BRow>
+__device__ __forceinline__ void ce_epilogue_ovl(f32x16_t (&acc)[TM][TN], const FP& f, const float (&rt)[TM],
+                                                const int (&tt)[TM], float sw, const CeArgs& ce, int M, int V,
+                                                int m0, int j0, int tile_n, int wm, int wn, float* red, const PA& pa,
+                                                const PB& pb, const Off& o, uint8_t* const (&st)[2],
+                                                const ARow& a_row, const BRow& b_row) {
+    using D = DmaSched<FP, 2, SPREAD, TM, TN, PA, PB>;
+    constexpr int KS = D::KS, kPer = D::kPer, kPerTile = D::kPerTile, nA = D::nA;
+    constexpr int kRest = kPerTile - kPer;
+    constexpr int kRestParts = TM < 3 ? TM : 3;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, NT = 64 * WAVES_M * WAVES_N;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int lr = lane & 31, lh = lane >> 5;
+    const float ninf = -__builtin_inff();
+    const int nw = j0 + wn * WN;                    // first column of the wave
+    const bool full = nw + WN <= V;                 // wave-uniform: no column past V
+    const uint8_t* sA = st[0];
+    const uint8_t* sB = st[0] + BM * RB;
+    if constexpr (EPI) acc_read_fence();
+    static_for<TM>([&](auto TMc) {
+        constexpr int tm = decltype(TMc)::value;
+        const float rr = EPI ? rt[tm] * sw : 0.0f;
+        float z[TN][16];
+        if constexpr (EPI) {
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) z[b][i] = acc_read(acc[tm][b][i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MMA) {
+            // fragments read per k-step from stage 0 (the logits hold 64 registers here, so
+            // none are kept across block rows; f's copy of k-step 0 is not used)
+            static_for<KS>([&](auto Sc) {
+                constexpr int s = decltype(Sc)::value;
+                const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(sA + swz<RB>(a_row(tm) + lr, 2 * s + lh));
+                static_for<TN>([&](auto Bc) {
+                    constexpr int b = decltype(Bc)::value;
+                    const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(sB + swz<RB>(b_row(b) + lr, 2 * s + lh));
+                    acc[tm][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, s == 0 ? f32x16_t{} : acc[tm][b],
+                                                                         0, 0, 0);
+                });
+            });
+            // a k-step's five reads, then its four MFMAs (no reads hoisted further ahead:
+            // the logits hold 64 registers here)
+            static_for<KS>([&](auto) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1 + TN, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+            });
+        }
+        if constexpr (EPI) {
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) z[b][i] *= rr;
+            if (!full) {
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (nw + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3) >= V) z[b][i] = ninf;
+            }
+            float mx = ninf;
+#pragma unroll
+            for (int b = 0; b < TN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, z[b][i]);
+            mx = halves_max(mx);
+            float sum = 0.0f;
+            if (mx > ninf) {
+#pragma unroll
+                for (int b = 0; b < TN; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sum += __expf(z[b][i] - mx);
+            }
+            sum = halves_sum(sum);
+            const int rl = wm * WM + tm * 32 + lr;      // row within the block tile
+            const int tg = tt[tm];
+            const int ot = tg - nw;
+            if (ot >= 0 && ot < WN && tg < V) {
+                const int c = ot & 31;
+                if (((c >> 2) & 1) == lh) {
+                    const int k = (ot >> 5) * 16 + ((c >> 3) << 2) + (c & 3);
+                    float zt = 0.0f;
+#pragma unroll
+                    for (int b = 0; b < TN; ++b)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) zt = (k == 16 * b + i) ? z[b][i] : zt;
+                    ce.tgt_logit[m0 + rl] = zt;
+                }
+            }
+            if (lh == 0) {
+                red[2 * (wn * BM + rl)] = mx;
+                red[2 * (wn * BM + rl) + 1] = sum;
+            }
+        }
+        if constexpr (MMA) {
+            static_for<kRest>([&](auto Qc) {
+                constexpr int q = decltype(Qc)::value;
+                if constexpr (q * kRestParts / kRest == tm) {
+                    constexpr int qq = kPer + q;
+                    if constexpr (qq < nA) pa.issue_one(qq, st[1], o.a);
+                    else pb.issue_one(qq - nA, st[1] + BM * RB, o.b);
+                }
+            });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (MMA) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));     // k-tile 1 landed
+    __syncthreads();                                                   // ... and red is complete
+    if constexpr (EPI) {
+        for (int r = threadIdx.x; r < BM; r += NT) {
+            const int m = m0 + r;
+            if (m < M) {
+                float mt = ninf;
+#pragma unroll
+                for (int w = 0; w < WAVES_N; ++w) mt = fmaxf(mt, red[2 * (w * BM + r)]);
+                float st_ = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WAVES_N; ++w) {
+                    const float mw = red[2 * (w * BM + r)];
+                    if (mw > ninf) st_ += red[2 * (w * BM + r) + 1] * __expf(mw - mt);
+                }
+                float* pp = ce.partials + (static_cast<size_t>(m) * ce.T + tile_n) * 2;
+                pp[0] = mt;
+                pp[1] = st_;
+            }
+        }
+    }
+}
+
+// Overlapped form of the LM-head GEMM with the loss epilogue (bf16 weights, transposed
+// accumulator blocks): k_gemm_ce_persistent's tile walk with the DMA stream running across
+// tiles (mainloop_dma_cont) and each tile's loss statistics fused with the next tile's
+// k-tile 0 (ce_epilogue_ovl).  A tile's row scales and targets load once its predecessor's
+// epilogue is done (through descriptors over [0, M); a target past M becomes -1).  Needs
+// at least 4 k-tiles (K > 128).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int RB, int SPREAD>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
+k_gemm_ce_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
+              const float* __restrict__ R, CeArgs ce, int M, int V, int K, int tiles_m, int tiles_n) {
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int kStage = BM * RB + BN * RB;
+    __shared__ __attribute__((aligned(1024))) uint8_t stages[2][kStage];
+    __shared__ float ce_red[2 * WAVES_N * BM];
+    uint8_t* st[2] = {stages[0], stages[1]};
+    using FP = FragPair<Frags<Elt::BF16, TM, TN, RB, true>>;
+    using PanelA = DmaPanel<BM, BM, NW, RB>;
+    using PanelB = DmaPanel<BN, BN, NW, RB>;
+    using D = DmaSched<FP, 2, SPREAD, TM, TN, PanelA, PanelB>;
+
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int kbytes = K * 2;
+    const int ntiles = tiles_m * tiles_n;
+    const int G = gridDim.x;
+    auto a_row = [&](int tm) { return wm * WM + tm * 32; };
+    auto b_row = [&](int tn) { return wn * WN + tn * 32; };
+    auto setup = [&](int t, PanelA& A, PanelB& B, int& tm0, int& tj0, int& ttn) {
+        int tile_m, tile_n;
+        tile_coords<8>(t, tiles_m, tiles_n, tile_m, tile_n);
+        tm0 = tile_m * BM;
+        tj0 = tile_n * BN;
+        ttn = tile_n;
+        const uint8_t* a0 = H + static_cast<size_t>(tm0) * kbytes;
+        A.init(a0, min(BM, M - tm0), a0, 0, kbytes);
+        const uint8_t* b0 = W + static_cast<size_t>(tj0) * kbytes;
+        B.init(b0, min(BN, V - tj0), b0, 0, kbytes);
+    };
+    const __amdgpu_buffer_rsrc_t r_rsrc = make_buffer_rsrc(R, static_cast<uint32_t>(M) * 4u);
+    const __amdgpu_buffer_rsrc_t t_rsrc = make_buffer_rsrc(ce.targets, static_cast<uint32_t>(M) * 4u);
+    float rv[TM];
+    int tv[TM];
+    auto load_rows = [&](int tm0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = tm0 + wm * WM + 32 * i + (threadIdx.x & 31);
+            const uint32_t off = static_cast<uint32_t>(m) * 4u;
+            rv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_rsrc, off, 0, 0));
+            const int x = __builtin_amdgcn_raw_buffer_load_b32(t_rsrc, off, 0, 0);
+            tv[i] = m < M ? x : -1;
+        }
+    };
+    const float sw = w_scale ? *w_scale : 1.0f;
+    PanelA pa, na;
+    PanelB pb, nb;
+    int m0 = 0, j0 = 0, tn0 = 0, nm0 = 0, nj0 = 0, ntn = 0;
+    int t = blockIdx.x;                              // the grid holds at most ntiles workgroups
+    setup(t, pa, pb, m0, j0, tn0);
+    if (t + G < ntiles) setup(t + G, na, nb, nm0, nj0, ntn);
+    else { na = pa; nb = pb; }
+    using Off = DmaPending<decltype(pa.base_offset(0, kbytes)), decltype(pb.base_offset(0, kbytes))>;
+    {
+        const Off o0{pa.base_offset(0, kbytes), pb.base_offset(0, kbytes)};
+        static_for<D::kPerTile>([&](auto Qc) {
+            constexpr int q = decltype(Qc)::value;
+            if constexpr (q < D::nA) pa.issue_one(q, st[0], o0.a);
+            else pb.issue_one(q - D::nA, st[0] + BM * RB, o0.b);
+        });
+    }
+    Off o{pa.base_offset(1, kbytes), pb.base_offset(1, kbytes)};
+    static_for<D::kPer>([&](auto Qc) {
+        constexpr int q = decltype(Qc)::value;
+        if constexpr (q < D::nA) pa.issue_one(q, st[1], o.a);
+        else pb.issue_one(q - D::nA, st[1] + BM * RB, o.b);
+    });
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(D::kPer));    // k-tile 0 landed
+    __syncthreads();
+    FP f;
+    f.load(0, st[0], st[0] + BM * RB, 0, a_row, b_row);
+    f32x16_t acc[TM][TN];
+    ce_epilogue_ovl<false, true, BM, BN, WAVES_M, WAVES_N, TM, TN, RB, SPREAD>(
+        acc, f, rv, tv, sw, ce, M, V, m0, j0, tn0, wm, wn, ce_red, pa, pb, o, st, a_row, b_row);
+    load_rows(m0);
+    for (;;) {
+        o = mainloop_dma_cont<FP, BM, RB, SPREAD, TM, TN>(acc, f, pa, pb, na, nb, kbytes, st, a_row, b_row);
+        const int cm0 = m0, cj0 = j0, ctn = tn0;     // the tile whose sums acc holds
+        t += G;
+        if (t >= ntiles) break;                      // uniform over the workgroup
+        pa = na;
+        pb = nb;
+        m0 = nm0;
+        j0 = nj0;
+        tn0 = ntn;
+        if (t + G < ntiles) setup(t + G, na, nb, nm0, nj0, ntn);
+        ce_epilogue_ovl<true, true, BM, BN, WAVES_M, WAVES_N, TM, TN, RB, SPREAD>(
+            acc, f, rv, tv, sw, ce, M, V, cm0, cj0, ctn, wm, wn, ce_red, pa, pb, o, st, a_row, b_row);
+        load_rows(m0);
+    }
+    ce_epilogue_ovl<true, false, BM, BN, WAVES_M, WAVES_N, TM, TN, RB, SPREAD>(
+        acc, f, rv, tv, sw, ce, M, V, m0, j0, tn0, wm, wn, ce_red, pa, pb, o, st, a_row, b_row);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));       // the unused loads of the last crossings
+}
+
 // Tile configurations of the second GEMM (compile-time).
 #ifndef CODA_G3_BM
 #define CODA_G3_BM 256
@@ -1590,6 +1839,12 @@ hipError_t launch_gemm_rowscale_ce(int M, int V, int K, const void* h, const voi
         const hipError_t e = cu_count(&cus);
         if (e != hipSuccess) return e;
         const int grid = std::min(tiles_m * tiles_n, std::max(cus, 1));
+        if (CODA_G3_OVL && NS3 == 2 && 2 * K > 2 * RB3) {     // at least 3 k-tiles (4 padded)
+            hipLaunchKernelGGL((k_gemm_ce_ovl<BM3, BN3, WM3, WN3, RB3, SP3>), dim3(grid), dim3(64 * WM3 * WN3), 0,
+                               stream, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W), w_scale, r,
+                               ce, M, V, K, tiles_m, tiles_n);
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL((k_gemm_ce_persistent<BM3, BN3, WM3, WN3, NS3, RB3, SP3>), dim3(grid),
                            dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
                            static_cast<const uint8_t*>(W), w_scale, r, ce, M, V, K, tiles_m, tiles_n);

@@ -59,9 +59,11 @@ SMALL = [
     (257, 72, 264, 2916, "bf16"),     # last tile: the second wave's 128 columns lie past V
     (64, 48, 128, 1, "bf16"),         # one-column vocabulary: lse = z, loss = 0
     (130, 64, 144, 513, "e4m3"),
-    # more tiles than compute units (the persistent kernel walks several per workgroup) and
-    # a last row tile holding one row (some waves' rows all lie past M)
+    # more tiles than compute units (the persistent kernels walk several per workgroup) and
+    # a last row tile holding one row (some waves' rows all lie past M): K = 128 runs the
+    # persistent kernel, K = 264 the one whose epilogues overlap the next tile's k-tile 0
     (257, 64, 128, 33280, "bf16"),
+    (257, 64, 264, 33280, "bf16"),
 ]
 
 
