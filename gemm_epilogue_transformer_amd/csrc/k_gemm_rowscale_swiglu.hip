@@ -1117,7 +1117,7 @@ __device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], con
     using D = DmaSched<FP, 2, SPREAD, TM, TN, PA, PB>;
     constexpr int KS = D::KS, kPer = D::kPer, kPerTile = D::kPerTile, nA = D::nA;
     constexpr int kRest = kPerTile - kPer;          // DMA instructions of k-tile 1 still to issue
-    constexpr int kRestParts = 3;                   // ... spread over the first three pairs
+    constexpr int kRestParts = HOLD < 3 ? HOLD : 3; // ... spread over the first pairs
     constexpr int WM = BM / WAVES_M;
     constexpr int NB = TN / 2;
     constexpr int NP = TM * NB;                     // block pairs
