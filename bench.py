@@ -1564,10 +1564,15 @@ def main():
     achieved = g2_flops / (k3_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[k2_dtype]
     byt = algorithmic_bytes(w)
-    # the library runs the forward SwiGLU on bf16 weights as a persistent kernel, with its
-    # epilogues overlapping the next tile's first k-tile when K spans more than 2 k-tiles
-    k3_name = (("k_gemm_swiglu_ovl" if d > 128 else "k_gemm_swiglu_persistent")
-               if w.act == si.ACT_SWIGLU and w.dtype == "bf16" else "k_gemm_rowscale_swiglu")
+    # on bf16 weights the library runs the forward SwiGLU and the plain row-scaled product
+    # as persistent kernels whose epilogues overlap the next tile's first k-tile when K
+    # spans more than 2 k-tiles (the SwiGLU one in a plain persistent form below that)
+    if w.dtype == "bf16" and w.act in (si.ACT_SWIGLU, si.ACT_NONE) and d > 128:
+        k3_name = "k_gemm_rowscale_ovl"
+    elif w.dtype == "bf16" and w.act == si.ACT_SWIGLU:
+        k3_name = "k_gemm_swiglu_persistent"
+    else:
+        k3_name = "k_gemm_rowscale_swiglu"
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": load_traffic(w.name, k3_name),
             "kernel": k3_name, "kernel_ms": round(k3_ms, 4),

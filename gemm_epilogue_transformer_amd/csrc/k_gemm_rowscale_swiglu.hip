@@ -1066,14 +1066,15 @@ k_gemm_swiglu_persistent(const uint8_t* __restrict__ H, const uint8_t* __restric
     }
 }
 
-// Output staging of the overlapped SwiGLU GEMM: one wave's slab in LDS (two halves of
-// 4 KB), each half one block row of the tile, i.e. 32 rows x the wave's 64 output columns
-// (128 bytes per row).  16-byte chunk c of slab row r lies at r*128 + (c ^ ((r >> 1) & 7))*16,
-// so both the epilogue's row-wise writes (16 rows at one chunk per 16 lanes) and the
-// line-wise reads (2 rows x 8 chunks) are conflict-free.  Block row tm is stored by four
-// instructions, store i covering rows 8i .. 8i+7 with 8 lanes per 128-byte row (lane l:
-// row 8i + l/8, chunk l%8); the transposed accumulator layout alone would give 32 rows x
-// 32 bytes per instruction.
+// Output staging of the overlapped GEMMs: one wave's slab in LDS (two halves of 4 KB), each
+// half 32 rows x 64 output columns (128 bytes per row): with SwiGLU a half is one block row
+// of the tile (the wave's 64 output columns), without an activation a block row's 128
+// output columns fill both halves (col_off 0 and 64).  16-byte chunk c of slab row r lies
+// at r*128 + (c ^ ((r >> 1) & 7))*16, so both the epilogue's row-wise writes (16 rows at one
+// chunk per 16 lanes) and the line-wise reads (2 rows x 8 chunks) are conflict-free.  A
+// half is stored by four instructions, store i covering rows 8i .. 8i+7 with 8 lanes per
+// 128-byte row (lane l: row 8i + l/8, chunk l%8); the transposed accumulator layout alone
+// would give 32 rows x 32 bytes per instruction.
 struct YSlab {
     uint8_t* ys;                     // this wave's slab
     __amdgpu_buffer_rsrc_t rsrc;     // y rows [m0, m0 + valid rows) of the tile
@@ -1082,49 +1083,53 @@ struct YSlab {
     __device__ __forceinline__ static int off(int hf, int r, int c) {
         return hf * 4096 + r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
     }
-    // store i of block row tm from half hf
-    __device__ __forceinline__ void store(int hf, int tm, int i) const {
+    // store i of block row tm from half hf, whose first column is col0 + col_off
+    __device__ __forceinline__ void store(int hf, int tm, int i, int col_off) const {
         const int lane = threadIdx.x & 63;
         const int r = 8 * i + (lane >> 3), c = lane & 7;
         const i32x4_t v = *reinterpret_cast<const i32x4_t*>(ys + off(hf, r, c));
         const uint32_t row_off = static_cast<uint32_t>(row0 + tm * 32 + r) * row_bytes;
-        const int n = col0 + c * 8;
+        const int n = col0 + col_off + c * 8;
         const uint32_t voff = n < n_out ? row_off + static_cast<uint32_t>(n) * 2 : kOobOffset;
         __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voff, 0, 0);
     }
 };
 
-// One tile boundary of the overlapped persistent SwiGLU GEMM (k_gemm_swiglu_ovl):
-// EPI: the SwiGLU epilogue of the tile whose sums acc holds (row scales rt, origin m0, j0),
-// the arithmetic of swiglu_epilogue_tc in the same order, its output through the slab
-// (YSlab);
+// One tile boundary of the overlapped persistent GEMM with the row-scale epilogue
+// (k_gemm_rowscale_ovl), SWIGLU: y = SiLU(r s acc_gate) * r s acc_up from gate/up block
+// pairs (blocks b and b + TN/2), else y = r s acc from pairs of adjacent column blocks
+// (2b, 2b + 1):
+// EPI: the epilogue of the tile whose sums acc holds (row scales rt, origin m0, j0), the
+// arithmetic of swiglu_epilogue_tc / the staged plain epilogue in the same order, its
+// output through the slab (YSlab);
 // MMA: the next tile's k-tile 0 (stage 0; its first k-step's fragments in f.f[0], the
 // other k-steps read here) multiplied into acc block pair by block pair, each pair right
 // after the epilogue has read its accumulators out (a zero C operand starts the pair), so
 // the matrix cores run while the epilogue's VALU work does; the rest of the next tile's
 // k-tile 1 DMA (instructions kPer .. kPerTile-1, offsets o) is issued over the first
 // pairs, and after pair HOLD-1 the wave waits for it (vmcnt 0: no store has been issued
-// yet, the first HOLD / NB block rows wait in the slab) and passes a barrier, so that
+// yet, the first HOLD / 2 block rows wait in the slab) and passes a barrier, so that
 // k-tile 1 has landed for every wave when the next mainloop starts; the later block rows
 // leave as soon as they are complete.
-template <bool EPI, bool MMA, int BM, int BN, int WAVES_M, int TM, int TN, int RB, int SPREAD, int HOLD, class FP,
-          class PA, class PB, class Off, class ARow, class BRow>
-__device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], const FP& f, const float (&rt)[TM],
-                                                     float sw, uint16_t* __restrict__ Y, int M, int N_out, int m0,
-                                                     int j0, int wm, int wn, const PA& pa, const PB& pb,
-                                                     const Off& o, uint8_t* const (&st)[2], uint8_t* ys,
-                                                     const ARow& a_row, const BRow& b_row) {
+template <bool SWIGLU, bool EPI, bool MMA, int BM, int BN, int WAVES_M, int TM, int TN, int RB, int SPREAD, int HOLD,
+          class FP, class PA, class PB, class Off, class ARow, class BRow>
+__device__ __forceinline__ void rowscale_epilogue_ovl(f32x16_t (&acc)[TM][TN], const FP& f, const float (&rt)[TM],
+                                                      float sw, uint16_t* __restrict__ Y, int M, int N_out, int m0,
+                                                      int j0, int wm, int wn, const PA& pa, const PB& pb,
+                                                      const Off& o, uint8_t* const (&st)[2], uint8_t* ys,
+                                                      const ARow& a_row, const BRow& b_row) {
     using D = DmaSched<FP, 2, SPREAD, TM, TN, PA, PB>;
     constexpr int KS = D::KS, kPer = D::kPer, kPerTile = D::kPerTile, nA = D::nA;
     constexpr int kRest = kPerTile - kPer;          // DMA instructions of k-tile 1 still to issue
     constexpr int kRestParts = HOLD < 3 ? HOLD : 3; // ... spread over the first pairs
     constexpr int WM = BM / WAVES_M;
-    constexpr int NB = TN / 2;
+    constexpr int NB = TN / 2;                      // pairs per block row
     constexpr int NP = TM * NB;                     // block pairs
+    constexpr int kHalves = SWIGLU ? 1 : 2;         // slab halves per block row
     constexpr int kHeldRows = HOLD / NB;            // block rows stored after the wait
     static_assert(!MMA || (HOLD >= kRestParts && HOLD <= NP), "the wait follows the last DMA share");
-    static_assert(NB == 2 && HOLD % NB == 0 && HOLD / NB <= 2,
-                  "a block row fills one slab half; the held block rows fit the two halves");
+    static_assert(NB == 2 && HOLD % NB == 0 && kHeldRows * kHalves <= 2,
+                  "a block row fills kHalves slab halves; the held block rows fit the two halves");
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const int lr = lane & 31, lh = lane >> 5;
@@ -1133,7 +1138,15 @@ __device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], con
     const YSlab ysl{ys,
                     make_buffer_rsrc(Y + static_cast<size_t>(m0) * N_out,
                                      EPI ? static_cast<uint32_t>(valid_rows) * row_bytes : 0u),
-                    row_bytes, wm * WM, j0 + wn * NB * 32, N_out};
+                    row_bytes, wm * WM, j0 + wn * NB * 32 * kHalves, N_out};
+    // block row tm's output from the slab
+    auto store_row = [&](int tm) {
+        static_for<kHalves>([&](auto Hc) {
+            constexpr int hx = decltype(Hc)::value;
+            const int hf = SWIGLU ? (tm & 1) : hx;
+            static_for<4>([&](auto Ic) { ysl.store(hf, tm, Ic, hx * 64); });
+        });
+    };
     // fragments of k-steps 1 .. KS-1 of the next tile's k-tile 0: every B block, A per block row
     const uint8_t* sA = st[0];
     const uint8_t* sB = st[0] + BM * RB;
@@ -1160,12 +1173,13 @@ __device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], con
         static_for<NB>([&](auto Bc) {
             constexpr int b = decltype(Bc)::value;
             constexpr int p = tm * NB + b;
+            constexpr int x0 = SWIGLU ? b : 2 * b, x1 = SWIGLU ? b + NB : 2 * b + 1;   // the pair's blocks
             float gv[16], uv[16];
             if constexpr (EPI) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    gv[i] = acc_read(acc[tm][b][i]);
-                    uv[i] = acc_read(acc[tm][b + NB][i]);
+                    gv[i] = acc_read(acc[tm][x0][i]);
+                    uv[i] = acc_read(acc[tm][x1][i]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1174,7 +1188,7 @@ __device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], con
                 static_for<KS>([&](auto Sc) {
                     constexpr int s = decltype(Sc)::value;
                     static_for<2>([&](auto Xc) {
-                        constexpr int x = b + decltype(Xc)::value * NB;
+                        constexpr int x = decltype(Xc)::value == 0 ? x0 : x1;
                         const bf16x8_t av = s == 0 ? f.f[0].a[tm] : aq[s - 1 < 0 ? 0 : s - 1];
                         const bf16x8_t bv = s == 0 ? f.f[0].b[x] : bq[s - 1 < 0 ? 0 : s - 1][x];
                         acc[tm][x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, s == 0 ? f32x16_t{} : acc[tm][x],
@@ -1183,35 +1197,53 @@ __device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], con
                 });
             }
             if constexpr (EPI) {
-                uint32_t pk[4][2];
+                // lane (row lr, half lh) ends with 16-byte chunks of its slab row: SwiGLU
+                // 4b + 2q + lh of half tm & 1; plain, block x0 / x1 give 2q + lh / 4 + 2q + lh
+                // of half b
+                auto put = [&](const uint32_t (&pk)[4][2], int hf, int c0) {
+                    static_for<2>([&](auto Qc) {
+                        constexpr int q = decltype(Qc)::value;
+                        uint32_t w[4];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float v[4];
+                        for (int h = 0; h < 2; ++h) {
+                            const auto sw2 =
+                                __builtin_amdgcn_permlane32_swap(pk[2 * q][h], pk[2 * q + 1][h], false, false);
+                            w[h] = sw2[0];
+                            w[2 + h] = sw2[1];
+                        }
+                        *reinterpret_cast<i32x4_t*>(ys + YSlab::off(hf, lr, c0 + 2 * q + lh)) =
+                            i32x4_t{int(w[0]), int(w[1]), int(w[2]), int(w[3])};
+                    });
+                };
+                if constexpr (SWIGLU) {
+                    uint32_t pk[4][2];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float gs = gv[4 * g + e] * rr;
-                        const float us = uv[4 * g + e] * rr;
-                        v[e] = gs * __builtin_amdgcn_rcpf(1.0f + __expf(-gs)) * us;
+                    for (int g = 0; g < 4; ++g) {
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float gs = gv[4 * g + e] * rr;
+                            const float us = uv[4 * g + e] * rr;
+                            v[e] = gs * __builtin_amdgcn_rcpf(1.0f + __expf(-gs)) * us;
+                        }
+                        pk[g][0] = pack_bf16x2(v[0], v[1]);
+                        pk[g][1] = pack_bf16x2(v[2], v[3]);
                     }
-                    pk[g][0] = pack_bf16x2(v[0], v[1]);
-                    pk[g][1] = pack_bf16x2(v[2], v[3]);
+                    put(pk, tm & 1, 4 * b);
+                } else {
+                    uint32_t pk0[4][2], pk1[4][2];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        pk0[g][0] = pack_bf16x2(gv[4 * g] * rr, gv[4 * g + 1] * rr);
+                        pk0[g][1] = pack_bf16x2(gv[4 * g + 2] * rr, gv[4 * g + 3] * rr);
+                        pk1[g][0] = pack_bf16x2(uv[4 * g] * rr, uv[4 * g + 1] * rr);
+                        pk1[g][1] = pack_bf16x2(uv[4 * g + 2] * rr, uv[4 * g + 3] * rr);
+                    }
+                    put(pk0, b, 0);
+                    put(pk1, b, 4);
                 }
-                static_for<2>([&](auto Qc) {
-                    constexpr int q = decltype(Qc)::value;
-                    uint32_t w[4];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const auto sw2 = __builtin_amdgcn_permlane32_swap(pk[2 * q][h], pk[2 * q + 1][h], false, false);
-                        w[h] = sw2[0];
-                        w[2 + h] = sw2[1];
-                    }
-                    // lane (row lr, half lh) holds chunk 4b + 2q + lh of its row
-                    *reinterpret_cast<i32x4_t*>(ys + YSlab::off(tm & 1, lr, 4 * b + 2 * q + lh)) =
-                        i32x4_t{int(w[0]), int(w[1]), int(w[2]), int(w[3])};
-                });
                 // a complete block row leaves at once unless it is held for the wait
-                if constexpr (b == NB - 1 && !(MMA && tm < kHeldRows))
-                    static_for<4>([&](auto Ic) { ysl.store(tm & 1, tm, Ic); });
+                if constexpr (b == NB - 1 && !(MMA && tm < kHeldRows)) store_row(tm);
             }
             if constexpr (MMA) {
                 static_for<kRest>([&](auto Qc) {
@@ -1225,12 +1257,7 @@ __device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], con
                 if constexpr (p == HOLD - 1) {
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // k-tile 1 landed (no store issued yet)
                     __syncthreads();                               // ... for every wave
-                    if constexpr (EPI) {
-                        static_for<kHeldRows>([&](auto Tc) {
-                            constexpr int th = decltype(Tc)::value;
-                            static_for<4>([&](auto Ic) { ysl.store(th & 1, th, Ic); });
-                        });
-                    }
+                    if constexpr (EPI) static_for<kHeldRows>([&](auto Tc) { store_row(decltype(Tc)::value); });
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1238,33 +1265,34 @@ __device__ __forceinline__ void swiglu_epilogue_ovl(f32x16_t (&acc)[TM][TN], con
     });
 }
 
-// Persistent SwiGLU GEMM with the epilogue overlapped (bf16 weights, transposed
-// accumulator blocks): the tile walk of k_gemm_swiglu_persistent, the DMA stream running
+// Persistent GEMM with the row-scale epilogue overlapped (bf16 weights, transposed
+// accumulator blocks; SWIGLU: gate/up panels and the SwiGLU epilogue, else one weight
+// panel and y = r s acc): the tile walk of k_gemm_swiglu_persistent, the DMA stream running
 // across tiles (mainloop_dma_cont loads the next tile's k-tiles 0 and 1 in the current
 // tile's last two crossings), and each tile's epilogue fused with the next tile's k-tile 0
-// (swiglu_epilogue_ovl).  The first tile's k-tile 0 runs alone, the last tile's epilogue
+// (rowscale_epilogue_ovl).  The first tile's k-tile 0 runs alone, the last tile's epilogue
 // alone.  A tile's row scales load once its predecessor's epilogue is done.  Needs at
-// least 4 k-tiles (K > 128); when this workgroup has no next tile the "next" panels are the
-// current ones (their loads are in bounds and never used).  LDS: the two 64 KB stages and
-// four 8 KB output slabs, the whole 160 KB.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int RB, int SPREAD, int HOLD>
+// least 3 k-tiles (K > 128); when this workgroup has no next tile the "next" panels are
+// the current ones (their loads are in bounds and never used).  LDS: the two 64 KB stages
+// and four 8 KB output slabs, the whole 160 KB.
+template <bool SWIGLU, int BM, int BN, int WAVES_M, int WAVES_N, int RB, int SPREAD, int HOLD>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
-k_gemm_swiglu_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
-                  const float* __restrict__ R, uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
-                  int tiles_n) {
+k_gemm_rowscale_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
+                    const float* __restrict__ R, uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
+                    int tiles_n) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int BNO = BN / 2;
-    static_assert(TN % 2 == 0, "SwiGLU pairs gate and up blocks");
-    static_assert(WN == 128, "a wave's 64 output columns are one 128-byte row segment");
+    constexpr int BNO = SWIGLU ? BN / 2 : BN;       // output columns of one block tile
+    static_assert(TN % 2 == 0, "block pairs");
+    static_assert(WN == 128, "a wave's output columns are one (SwiGLU) or two 128-byte row segments");
     constexpr int kStage = BM * RB + BN * RB;
     __shared__ __attribute__((aligned(1024))) uint8_t stages[2][kStage];
     __shared__ __attribute__((aligned(16))) uint8_t yslab[NW][8192];
     uint8_t* st[2] = {stages[0], stages[1]};
     using FP = FragPair<Frags<Elt::BF16, TM, TN, RB, true>>;
     using PanelA = DmaPanel<BM, BM, NW, RB>;
-    using PanelB = DmaPanel<BN, BN / 2, NW, RB>;
+    using PanelB = DmaPanel<BN, SWIGLU ? BN / 2 : BN, NW, RB>;
     using D = DmaSched<FP, 2, SPREAD, TM, TN, PanelA, PanelB>;
 
     const int wave = threadIdx.x >> 6;
@@ -1274,9 +1302,13 @@ k_gemm_swiglu_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, 
     const int ntiles = tiles_m * tiles_n;
     const int G = gridDim.x;
     auto a_row = [&](int tm) { return wm * WM + tm * 32; };
+    // SWIGLU: blocks [0, TN/2) = this wave's gate rows, [TN/2, TN) = the matching up rows
     auto b_row = [&](int tn) {
-        constexpr int TH = TN / 2;
-        return (tn < TH ? 0 : BN / 2) + wn * TH * 32 + (tn % TH) * 32;
+        if constexpr (SWIGLU) {
+            constexpr int TH = TN / 2;
+            return (tn < TH ? 0 : BN / 2) + wn * TH * 32 + (tn % TH) * 32;
+        }
+        return wn * WN + tn * 32;
     };
     auto setup = [&](int t, PanelA& A, PanelB& B, int& tm0, int& tj0) {
         int tile_m, tile_n;
@@ -1286,8 +1318,12 @@ k_gemm_swiglu_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, 
         const uint8_t* a0 = H + static_cast<size_t>(tm0) * kbytes;
         A.init(a0, min(BM, M - tm0), a0, 0, kbytes);
         const uint8_t* g0 = W + static_cast<size_t>(tj0) * kbytes;
-        const uint8_t* u0 = W + static_cast<size_t>(N_out + tj0) * kbytes;
-        B.init(g0, min(BNO, N_out - tj0), u0, min(BNO, N_out - tj0), kbytes);
+        if constexpr (SWIGLU) {
+            const uint8_t* u0 = W + static_cast<size_t>(N_out + tj0) * kbytes;
+            B.init(g0, min(BNO, N_out - tj0), u0, min(BNO, N_out - tj0), kbytes);
+        } else {
+            B.init(g0, min(BNO, N_out - tj0), g0, 0, kbytes);
+        }
     };
     const __amdgpu_buffer_rsrc_t r_rsrc = make_buffer_rsrc(R, static_cast<uint32_t>(M) * 4u);
     float rv[TM];
@@ -1327,7 +1363,7 @@ k_gemm_swiglu_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, 
     FP f;
     f.load(0, st[0], st[0] + BM * RB, 0, a_row, b_row);
     f32x16_t acc[TM][TN];
-    swiglu_epilogue_ovl<false, true, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
+    rowscale_epilogue_ovl<SWIGLU, false, true, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
         acc, f, rv, sw, Y, M, N_out, m0, j0, wm, wn, pa, pb, o, st, ys, a_row, b_row);
     load_r(m0);
     for (;;) {
@@ -1340,11 +1376,11 @@ k_gemm_swiglu_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, 
         m0 = nm0;
         j0 = nj0;
         if (t + G < ntiles) setup(t + G, na, nb, nm0, nj0);
-        swiglu_epilogue_ovl<true, true, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
+        rowscale_epilogue_ovl<SWIGLU, true, true, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
             acc, f, rv, sw, Y, M, N_out, cm0, cj0, wm, wn, pa, pb, o, st, ys, a_row, b_row);
         load_r(m0);
     }
-    swiglu_epilogue_ovl<true, false, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
+    rowscale_epilogue_ovl<SWIGLU, true, false, BM, BN, WAVES_M, TM, TN, RB, SPREAD, HOLD>(
         acc, f, rv, sw, Y, M, N_out, m0, j0, wm, wn, pa, pb, o, st, ys, a_row, b_row);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));       // the unused loads of the last crossings
 }
@@ -1444,7 +1480,7 @@ k_gemm_ce_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ 
 }
 
 // One tile boundary of the overlapped LM-head GEMM with the loss epilogue (k_gemm_ce_ovl),
-// as swiglu_epilogue_ovl for the SwiGLU GEMM:
+// as rowscale_epilogue_ovl for the SwiGLU GEMM:
 // EPI: the loss statistics of the tile whose sums acc holds (ce_epilogue_tc's arithmetic
 // in the same order: per block row the logits r*s*acc, columns past V at -inf, the row's
 // max and sum of exponentials over the wave's columns, the target's logit; then across the
@@ -1788,6 +1824,19 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
     const RopeArgs none{nullptr, nullptr, nullptr, 0, 0};
     const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
     const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
+    if (!swiglu && !w_fp8 && CODA_G3_OVL && NS3 == 2 && PIPE3 == 0 && 2 * K > 2 * RB3) {
+        // plain row-scaled output: the overlapped persistent kernel, one block row held
+        const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BN3 - 1) / BN3;
+        int cus = 0;
+        const hipError_t e = cu_count(&cus);
+        if (e != hipSuccess) return e;
+        const int grid = std::min(tiles_m * tiles_n, std::max(cus, 1));
+        hipLaunchKernelGGL((k_gemm_rowscale_ovl<false, BM3, BN3, WM3, WN3, RB3, SP3, 2>), dim3(grid),
+                           dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
+                           static_cast<const uint8_t*>(W), w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m,
+                           tiles_n);
+        return hipGetLastError();
+    }
     if (swiglu && !w_fp8 && CODA_G3_PERSIST && CODA_G3_TC && PIPE3 == 0) {
         const int tiles_m = (M + BM3 - 1) / BM3, tiles_n = (N_out + BN3 / 2 - 1) / (BN3 / 2);
         int cus = 0;
@@ -1795,7 +1844,7 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
         if (e != hipSuccess) return e;
         const int grid = std::min(tiles_m * tiles_n, std::max(cus, 1));
         if (CODA_G3_OVL && NS3 == 2 && 2 * K > 2 * RB3) {     // at least 3 k-tiles (4 padded)
-            hipLaunchKernelGGL((k_gemm_swiglu_ovl<BM3, BN3, WM3, WN3, RB3, SP3, CODA_G3_HOLD>), dim3(grid),
+            hipLaunchKernelGGL((k_gemm_rowscale_ovl<true, BM3, BN3, WM3, WN3, RB3, SP3, CODA_G3_HOLD>), dim3(grid),
                                dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
                                static_cast<const uint8_t*>(W), w_scale, r, static_cast<uint16_t*>(y), M, N_out, K,
                                tiles_m, tiles_n);

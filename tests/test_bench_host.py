@@ -114,7 +114,7 @@ def test_roofline_kernels_resolve_to_their_sources():
     """Every kernel a bench line names for its roofline is defined in a translation unit the
     source hash covers, so its stored traffic is checked against the right files; the
     default workload's stored traffic belongs to the current sources of its kernel."""
-    for k in ("k_gemm_swiglu_ovl", "k_gemm_swiglu_persistent", "k_gemm_ce_ovl", "k_gemm_rowscale_swiglu",
+    for k in ("k_gemm_rowscale_ovl", "k_gemm_swiglu_persistent", "k_gemm_ce_ovl", "k_gemm_rowscale_swiglu",
               "k_gemm_resid_partialrms",
               "k_gemm_rmsnorm_bwd", "k_gemm_wgrad", "k_rope_bwd", "k_swiglu_bwd_saved"):
         files = bench._kernel_files(k)
@@ -123,7 +123,7 @@ def test_roofline_kernels_resolve_to_their_sources():
             assert "gemm_pipeline.hpp" in files, (k, files)     # the mainloops count too
         assert bench.kernel_source_hash(k) != ""
     rec = json.load(open(os.path.join(bench.ROOT, "profiles", "traffic_llama1b_attnout_mlpin_m16384.json")))
-    assert "k_gemm_swiglu_ovl" in rec["kernels"]
+    assert "k_gemm_rowscale_ovl" in rec["kernels"]
 
 
 def test_kernel_trace_summary_groups_launches(tmp_path):
