@@ -323,7 +323,8 @@ def ingest_counters(dirs, w, command: str, out_dir: str = "") -> str:
         for r in _csv_rows(dr, "counter_collection.csv"):
             name = r["Kernel_Name"]
             if "coda::" in name:
-                kind = "gemm1" if "resid_partialrms" in name else ("gemm2" if "swiglu" in name else None)
+                kind = ("gemm1" if "resid_partialrms" in name else
+                        ("gemm2" if "swiglu" in name or "rowscale_ovl" in name else None))
                 who = "library"
             elif name.startswith("Cijk") or "Cijk" in name[:40]:
                 kind, who = None, "vendor"
