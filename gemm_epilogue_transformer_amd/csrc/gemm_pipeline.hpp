@@ -500,11 +500,20 @@ struct DmaSched {
     static constexpr int nA = PA::kInst;
     static constexpr int kPerTile = nA + PB::kInst;                        // DMA per wave per tile
     static constexpr int kPer = (kPerTile + SPREAD - 1) / SPREAD;          // DMA per k-step
+    // the continuous mainloop (mainloop_dma_cont): kPer0 instructions at the crossing, the
+    // rest kPerS per k-step over the next SPREAD-1 k-steps
+#ifdef CODA_CONT_D0
+    static constexpr int kPer0 = CODA_CONT_D0 < kPerTile ? CODA_CONT_D0 : kPerTile;
+#else
+    static constexpr int kPer0 = kPer;
+#endif
+    static constexpr int kPerS = SPREAD > 1 ? (kPerTile - kPer0 + SPREAD - 2) / (SPREAD - 1) : 0;
     static_assert(NS >= 2, "at least two stages");
     static_assert((NS * KS) % 2 == 0, "fragment double-buffer parity must repeat every stage group");
     static_assert((NS - 1) * kPerTile < 64, "vmcnt range");
     static_assert(SPREAD >= 1 && SPREAD <= KS, "the DMA of a tile ends before the next tile's last k-step");
-    static_assert(kPer <= kMfma, "one MFMA ahead of every DMA instruction");
+    static_assert(kPer <= kMfma && kPer0 <= kMfma && kPerS <= kMfma, "one MFMA ahead of every DMA instruction");
+    static_assert(SPREAD > 1 || kPer0 == kPerTile, "without a spread the crossing issues the whole k-tile");
 };
 
 // Prologue of the pipelined mainloop: the DMA of k-tiles 0 .. NS-2 and the first share of
@@ -676,19 +685,21 @@ __device__ __forceinline__ void mainloop_dma_run(f32x16_t (&acc)[TM][TN], const 
 // after issuing its last DMA instruction), the stage of k-tile 0 may still be read by
 // other waves.  On return: the next tile's k-tile 0 has landed in stage 0 (every wave
 // waited and passed the barrier), f[0] holds its first k-step's fragments, and the DMA of
-// its k-tile 1 into stage 1 has issued its first kPer instructions; the returned offsets
-// are that k-tile's, for the caller to issue instructions kPer .. kPerTile-1.
+// its k-tile 1 into stage 1 has issued its first kPer0 instructions; the returned offsets
+// are that k-tile's, for the caller to issue instructions kPer0 .. kPerTile-1.
 //
 // The crossing at the end of k-tile kt waits with vmcnt(0) (with two stages nothing later
 // than k-tile kt+1's DMA has been issued but stores and the caller's loads), passes the
-// barrier, runs kt's last k-step with the first share of k-tile kt+2's DMA and the reads of
-// kt+1's first k-step; the rest of kt+2's DMA goes out during kt+1's first SPREAD-1 k-steps.
+// barrier, runs kt's last k-step with the first share of k-tile kt+2's DMA (kPer0
+// instructions) and the reads of kt+1's first k-step; the rest of kt+2's DMA goes out during
+// kt+1's first SPREAD-1 k-steps (kPerS per k-step).
 template <class FP, int BM, int RBA, int SPREAD, int TM, int TN, class ARow, class BRow, class PA, class PB>
 __device__ __forceinline__ auto mainloop_dma_cont(f32x16_t (&acc)[TM][TN], FP& f, const PA& pa, const PB& pb,
                                                   const PA& na, const PB& nb, int kbytes, uint8_t* const (&st)[2],
                                                   const ARow& a_row, const BRow& b_row) {
     using D = DmaSched<FP, 2, SPREAD, TM, TN, PA, PB>;
-    constexpr int KS = D::KS, kMfma = D::kMfma, nA = D::nA, kPerTile = D::kPerTile, kPer = D::kPer;
+    constexpr int KS = D::KS, kMfma = D::kMfma, nA = D::nA, kPerTile = D::kPerTile;
+    constexpr int kPer0 = D::kPer0, kPerS = D::kPerS;
     static_assert(KS % 2 == 0, "fragment parity: k-step 0 of every k-tile uses f[0]");
     constexpr int kOffB = BM * RBA;
     const int nkp = (((kbytes + RBA - 1) / RBA) + 1) & ~1;
@@ -708,8 +719,8 @@ __device__ __forceinline__ auto mainloop_dma_cont(f32x16_t (&acc)[TM][TN], FP& f
             static_for<kMfma>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 f.mma_one(s & 1, j, acc);
-                if constexpr (s + 1 < SPREAD && j < kPer && (s + 1) * kPer + j < kPerTile)
-                    issue(A, B, (s + 1) * kPer + j, oth, o);
+                if constexpr (s + 1 < SPREAD && j < kPerS && kPer0 + s * kPerS + j < kPerTile)
+                    issue(A, B, kPer0 + s * kPerS + j, oth, o);
                 f.template slot<j>((s + 1) & 1, cur, cur + kOffB, s + 1, a_row, b_row);
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -728,7 +739,7 @@ __device__ __forceinline__ auto mainloop_dma_cont(f32x16_t (&acc)[TM][TN], FP& f
         static_for<kMfma>([&](auto J) {
             constexpr int j = decltype(J)::value;
             if constexpr (kMma) f.mma_one((KS - 1) & 1, j, acc);
-            if constexpr (j < kPer) issue(A, B, j, st[S], o);
+            if constexpr (j < kPer0) issue(A, B, j, st[S], o);
             f.template slot<j>(0, nxt, nxt + kOffB, 0, a_row, b_row);
             __builtin_amdgcn_sched_barrier(0);
         });

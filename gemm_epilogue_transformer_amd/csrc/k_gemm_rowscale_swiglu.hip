@@ -1119,7 +1119,7 @@ __device__ __forceinline__ void rowscale_epilogue_ovl(f32x16_t (&acc)[TM][TN], c
                                                       const Off& o, uint8_t* const (&st)[2], uint8_t* ys,
                                                       const ARow& a_row, const BRow& b_row) {
     using D = DmaSched<FP, 2, SPREAD, TM, TN, PA, PB>;
-    constexpr int KS = D::KS, kPer = D::kPer, kPerTile = D::kPerTile, nA = D::nA;
+    constexpr int KS = D::KS, kPer = D::kPer0, kPerTile = D::kPerTile, nA = D::nA;   // kPer0 went out at the crossing
     constexpr int kRest = kPerTile - kPer;          // DMA instructions of k-tile 1 still to issue
     constexpr int kRestParts = HOLD < 3 ? HOLD : 3; // ... spread over the first pairs
     constexpr int WM = BM / WAVES_M;
@@ -1353,12 +1353,12 @@ k_gemm_rowscale_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W
         });
     }
     Off o{pa.base_offset(1, kbytes), pb.base_offset(1, kbytes)};
-    static_for<D::kPer>([&](auto Qc) {
+    static_for<D::kPer0>([&](auto Qc) {
         constexpr int q = decltype(Qc)::value;
         if constexpr (q < D::nA) pa.issue_one(q, st[1], o.a);
         else pb.issue_one(q - D::nA, st[1] + BM * RB, o.b);
     });
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(D::kPer));    // k-tile 0 landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(D::kPer0));   // k-tile 0 landed
     __syncthreads();
     FP f;
     f.load(0, st[0], st[0] + BM * RB, 0, a_row, b_row);
@@ -1498,7 +1498,7 @@ __device__ __forceinline__ void ce_epilogue_ovl(f32x16_t (&acc)[TM][TN], const F
                                                 const PB& pb, const Off& o, uint8_t* const (&st)[2],
                                                 const ARow& a_row, const BRow& b_row) {
     using D = DmaSched<FP, 2, SPREAD, TM, TN, PA, PB>;
-    constexpr int KS = D::KS, kPer = D::kPer, kPerTile = D::kPerTile, nA = D::nA;
+    constexpr int KS = D::KS, kPer = D::kPer0, kPerTile = D::kPerTile, nA = D::nA;   // kPer0 went out at the crossing
     constexpr int kRest = kPerTile - kPer;
     constexpr int kRestParts = TM < 3 ? TM : 3;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, NT = 64 * WAVES_M * WAVES_N;
@@ -1695,12 +1695,12 @@ k_gemm_ce_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, cons
         });
     }
     Off o{pa.base_offset(1, kbytes), pb.base_offset(1, kbytes)};
-    static_for<D::kPer>([&](auto Qc) {
+    static_for<D::kPer0>([&](auto Qc) {
         constexpr int q = decltype(Qc)::value;
         if constexpr (q < D::nA) pa.issue_one(q, st[1], o.a);
         else pb.issue_one(q - D::nA, st[1] + BM * RB, o.b);
     });
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(D::kPer));    // k-tile 0 landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(D::kPer0));   // k-tile 0 landed
     __syncthreads();
     FP f;
     f.load(0, st[0], st[0] + BM * RB, 0, a_row, b_row);
