@@ -34,8 +34,12 @@ def _case(M, K, n_w, seed):
     return h, W, gamma, r
 
 
+# K = 8: the first persistent kernel; the others the overlapped one (K > 128), with one row
+# (1 x 136: the fewest k-tiles it takes), tiles per workgroup from one to three, ragged
+# edges in every dimension and a K tail inside a k-tile
 @pytest.mark.parametrize("act", [coda.SWIGLU, coda.NONE], ids=["swiglu", "none"])
-@pytest.mark.parametrize("M,K,n_w", [(300, 200, 208), (257, 264, 528), (64, 8, 16), (513, 1032, 272)])
+@pytest.mark.parametrize("M,K,n_w", [(300, 200, 208), (257, 264, 528), (64, 8, 16), (513, 1032, 272),
+                                     (1, 136, 16), (2049, 192, 1040), (4100, 328, 2000)])
 def test_on_chip_fold_is_bit_identical(M, K, n_w, act):
     print(f"gfold M={M} K={K} n_w={n_w} act={act}", flush=True)
     h, W, gamma, r = _case(M, K, n_w, M + K + n_w)
