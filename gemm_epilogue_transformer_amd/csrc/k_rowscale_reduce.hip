@@ -10,20 +10,31 @@
 
 namespace coda {
 
-__global__ void __launch_bounds__(256)
+// One thread per row.  The partials are loaded eight at a time before they are added (a
+// load per add would put T memory latencies in series); the additions keep the order
+// t = 0, 1, ..., T-1.  64-thread blocks spread the rows over every CU.
+__global__ void __launch_bounds__(64)
 k_rowscale_reduce(const float* __restrict__ P, float* __restrict__ r, int M, int T,
                   double n, double eps) {
     const int m = blockIdx.x * blockDim.x + threadIdx.x;
     if (m >= M) return;
     const float* p = P + static_cast<size_t>(m) * T;
     double s = 0.0;
-    for (int t = 0; t < T; ++t) s += static_cast<double>(p[t]);
+    int t = 0;
+    for (; t + 8 <= T; t += 8) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = p[t + e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += static_cast<double>(v[e]);
+    }
+    for (; t < T; ++t) s += static_cast<double>(p[t]);
     r[m] = static_cast<float>(1.0 / sqrt(s / n + eps));
 }
 
 hipError_t launch_rowscale_reduce(int M, int N, int T, const float* P, float eps, float* r,
                                   hipStream_t stream) {
-    const dim3 block(256), grid((M + 255) / 256);
+    const dim3 block(64), grid((M + 63) / 64);
     hipLaunchKernelGGL(k_rowscale_reduce, grid, block, 0, stream, P, r, M, T, static_cast<double>(N),
                        static_cast<double>(eps));
     return hipGetLastError();
