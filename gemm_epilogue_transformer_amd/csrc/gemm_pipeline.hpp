@@ -583,6 +583,7 @@ struct DmaPrologue {
 struct NoExtra {
     static constexpr int kOps = 0;
     __device__ __forceinline__ void issue(int /*kt*/, int /*nk*/) const {}
+    __device__ __forceinline__ void issue_into(int /*kt*/, int /*nk*/, uint8_t* /*stage*/) const {}
 };
 
 // The rest of the pipelined mainloop after mainloop_dma_prologue: wait for k-tile 0, the
@@ -781,6 +782,101 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
                                              const BRow& b_row, const X& xtra = X()) {
     mainloop_dma_fp<FragPair<Frags<E, TM, TN, RB, TC>>, BM, BN, SPLIT, NS, NW, RB, RB, SPREAD>(
         acc, pa, pb, kbytes, kbytes, st, a_row, b_row, xtra);
+}
+
+// Mainloop with a ring of LDS stages per operand: three for the A panel, two for the B
+// panel (one element type E, RB-byte k-tile rows).  The crossing at the end of k-tile j
+// waits for k-tile j+1 (vmcnt(nA): only the A DMA of k-tile j+2 may be in flight),
+// passes the barrier, and issues the DMA of B(j+2) and then A(j+3) into the stages j's
+// own operands leave free (the first kPer instructions there, the rest over k-tile j+1's
+// first SPREAD-1 k-steps), so an A k-tile is loaded two k-tiles before it is read and a
+// B k-tile one.  B goes first so that the wait's in-order count never includes it.  For
+// an operand that streams from HBM (each A row panel is read by few tiles at a time)
+// the extra stage doubles the DMA's lead over memory latency at the same 128-byte rows.
+// sa: three A stages of BM*RB bytes, sb: two B stages of BN*RB bytes.  K = 0 computes
+// one k-tile of zeros; k-tiles past K are loaded as zeros.
+// The extra loads (xtra.issue_into) go out at each crossing right after the barrier,
+// before the batch, into the A stage just freed: the rows there that this wave's own
+// first A instructions of the batch fill later, which lands after them (a wave's loads
+// complete in order).  The next crossing's wait then covers them.
+template <Elt E, int BM, int BN, int NW, int RB, int SPREAD, int TM, int TN, class ARow, class BRow,
+          class X = NoExtra>
+__device__ __forceinline__ void mainloop_dma_ring(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
+                                                  const DmaPanel<BN, BN, NW, RB>& pb, int kbytes,
+                                                  uint8_t* const (&sa)[3], uint8_t* const (&sb)[2],
+                                                  const ARow& a_row, const BRow& b_row, const X& xtra = X()) {
+    using FP = FragPair<Frags<E, TM, TN, RB>>;
+    constexpr int KS = FP::kSteps, kMfma = TM * TN;
+    constexpr int nA = DmaPanel<BM, BM, NW, RB>::kInst, nB = DmaPanel<BN, BN, NW, RB>::kInst;
+    constexpr int kPerTile = nA + nB;
+    constexpr int kPer = (kPerTile + SPREAD - 1) / SPREAD;
+    static_assert(KS >= 2 && KS % 2 == 0, "the last k-step crosses; the fragment parity repeats every k-tile");
+    static_assert(SPREAD >= 1 && SPREAD <= KS, "the DMA of a batch ends before the next crossing");
+    static_assert(kPer <= kMfma, "one MFMA ahead of every DMA instruction");
+    static_assert(nA + kPer < 64, "vmcnt range");
+    static_assert(X::kOps <= nA, "the extra loads' rows are filled by the wave's own A instructions");
+    const int nk = max((kbytes + RB - 1) / RB, 1);
+    FP f;
+    // batch instruction q: B first (q < nB), then A
+    auto issue_q = [&](int q, uint8_t* a_st, uint8_t* b_st, uint32_t oa, uint32_t ob) {
+        if (q < nB) pb.issue_one(q, b_st, ob);
+        else pa.issue_one(q - nB, a_st, oa);
+    };
+    // prologue: A(0), B(0), A(1), then the first share of the batch {B(1), A(2)}
+    pa.issue(sa[0], 0, kbytes);
+    pb.issue(sb[0], 0, kbytes);
+    pa.issue(sa[1], 1, kbytes);
+    uint32_t ob = pb.base_offset(1, kbytes), oa = pa.base_offset(2, kbytes);
+    static_for<kPer>([&](auto Q) { issue_q(decltype(Q)::value, sa[2], sb[1], oa, ob); });
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(nA + kPer));   // A(0) and B(0) landed
+    __syncthreads();
+    f.load(0, sa[0], sb[0], 0, a_row, b_row);
+    // stages of k-tile j: A in a_cur, B in b_cur; j+1's in a_nxt / b_nxt; the pending
+    // batch (B(j+1), A(j+2)) goes to b_nxt / a_nn
+    uint8_t* a_cur = sa[0];
+    uint8_t* a_nxt = sa[1];
+    uint8_t* a_nn = sa[2];
+    uint8_t* b_cur = sb[0];
+    uint8_t* b_nxt = sb[1];
+    auto ktile = [&](auto FirstC, int j) {
+        constexpr bool kFirst = decltype(FirstC)::value;
+        static_for<KS - 1>([&](auto Sc) {
+            constexpr int s = decltype(Sc)::value;
+            static_for<kMfma>([&](auto J) {
+                constexpr int jj = decltype(J)::value;
+                f.template mma_one<kFirst && s == 0>(s & 1, jj, acc);
+                if constexpr (s + 1 < SPREAD && jj < kPer && (s + 1) * kPer + jj < kPerTile)
+                    issue_q((s + 1) * kPer + jj, a_nn, b_nxt, oa, ob);
+                f.template slot<jj>((s + 1) & 1, a_cur, b_cur, s + 1, a_row, b_row);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(nA));   // k-tile j+1 landed (A(j+2) may be in flight)
+        __syncthreads();                              // ... for every wave; j's stages are free
+        __builtin_amdgcn_sched_barrier(0);
+        xtra.issue_into(j, nk, a_cur);
+        ob = pb.base_offset(j + 2, kbytes);
+        oa = pa.base_offset(j + 3, kbytes);
+        static_for<kMfma>([&](auto J) {
+            constexpr int jj = decltype(J)::value;
+            f.mma_one((KS - 1) & 1, jj, acc);
+            if constexpr (jj < kPer) issue_q(jj, a_cur, b_cur, oa, ob);
+            f.template slot<jj>(KS & 1, a_nxt, b_nxt, 0, a_row, b_row);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        uint8_t* const a_old = a_cur;
+        a_cur = a_nxt;
+        a_nxt = a_nn;
+        a_nn = a_old;
+        uint8_t* const b_old = b_cur;
+        b_cur = b_nxt;
+        b_nxt = b_old;
+    };
+    ktile(std::true_type{}, 0);
+    for (int j = 1; j < nk; ++j) ktile(std::false_type{}, j);
+    // drain the DMA that ran past the end before the LDS is reused or released
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------------

@@ -40,9 +40,34 @@ struct XresPrefetch {
             dma16(rsrc, voff, junk);
         }
     }
+    // The same loads into a freed A stage of the ring mainloop: load p into the 1 KB that
+    // this wave's A DMA instruction p fills (rows (NW p + wave) * 8 of 128-byte rows).
+    template <int NW>
+    __device__ __forceinline__ void issue_stage(int kt, int nk, uint8_t* stage) const {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int i0 = (kt - (nk - kInst / P)) * P;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int i = i0 + p;
+            const uint32_t voff = (i >= 0 && i < kInst) ? lane_off + static_cast<uint32_t>(i) * inst_step : kOob;
+            dma16(rsrc, voff, lds_addr(stage + (NW * p + wave) * 1024));
+        }
+    }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC, Elt E>
+// XresPrefetch for the ring mainloop (its hook names the stage).
+template <int P, int NW>
+struct XresPrefetchRing : XresPrefetch<P> {
+    __device__ __forceinline__ void issue_into(int kt, int nk, uint8_t* stage) const {
+        this->template issue_stage<NW>(kt, nk, stage);
+    }
+};
+
+// RING: the mainloop with three A stages and two B stages (mainloop_dma_ring), which take
+// the whole LDS: the residual prefetch then loads into the A stage each crossing frees
+// (XresPrefetchRing), and the epilogue's row sums live behind the slabs in the stage
+// memory.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC, bool RING, Elt E>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
                         const float* __restrict__ a_scale, const float* __restrict__ w_scale,
@@ -54,17 +79,37 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     constexpr int EB = EltInfo<E>::kBytes;
 
     constexpr int kStage = (BM + BN) * RB;
-    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
-    __shared__ float red[WAVES_N][BM];
-    __shared__ __attribute__((aligned(1024))) uint8_t junk[NW][1024];
-    uint8_t* st[NS];
+    using S = Slab<TN>;
+    uint8_t* st[NS];          // shared stages (RING = false)
+    uint8_t* sa[3];           // the rings (RING = true)
+    uint8_t* sb[2];
+    float* red;               // [WAVES_N][BM] row sums of the epilogue
+    uint8_t* slab;            // this wave's epilogue slab
+    uint8_t* junk = nullptr;  // this wave's 1 KB block for the residual prefetch
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if constexpr (RING) {
+        __shared__ __attribute__((aligned(1024))) uint8_t rings[3 * BM * RB + 2 * BN * RB];
+        static_assert(NW * S::kBytes + WAVES_N * BM * 4 <= 3 * BM * RB + 2 * BN * RB, "slabs and row sums fit");
 #pragma unroll
-    for (int i = 0; i < NS; ++i) st[i] = stages[i];
+        for (int i = 0; i < 3; ++i) sa[i] = rings + i * BM * RB;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sb[i] = rings + 3 * BM * RB + i * BN * RB;
+        slab = rings + wave * S::kBytes;
+        red = reinterpret_cast<float*>(rings + NW * S::kBytes);
+    } else {
+        __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+        __shared__ float red_s[WAVES_N][BM];
+        __shared__ __attribute__((aligned(1024))) uint8_t junk_s[NW][1024];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) st[i] = stages[i];
+        slab = slab_region<NS, NW, kStage, S::kBytes>(st, wave);
+        red = &red_s[0][0];
+        junk = junk_s[wave];
+    }
 
     int tile_m, tile_n;
     tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     const int kbytes = K * EB;
@@ -88,7 +133,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     // the residual tile's cache fill during the last k-tiles (1 KB per wave and k-tile for
     // bf16 operands, 2 KB for the 8-bit ones, whose k-tiles are half as many)
     static_assert(BM == 64 * NW && BN == 256, "the prefetch covers 256 columns of 64 rows per wave");
-    XresPrefetch<E == Elt::E4M3 ? 2 : 1> xpf;
+    XresPrefetchRing<E == Elt::E4M3 ? 2 : 1, NW> xpf;
     {
         const uint32_t rb = static_cast<uint32_t>(N) * 2;
         xpf.rsrc = make_rsrc(x_res ? x_res + static_cast<size_t>(m0) * N : h,
@@ -96,9 +141,12 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
         xpf.lane_off = static_cast<uint32_t>(64 * wave + (lane >> 5)) * rb + static_cast<uint32_t>(n0) * 2u +
                        static_cast<uint32_t>(lane & 31) * 16u;
         xpf.inst_step = __builtin_amdgcn_readfirstlane(2u * rb);
-        xpf.junk = __builtin_amdgcn_readfirstlane(lds_addr(junk[wave]));
+        if constexpr (!RING) xpf.junk = __builtin_amdgcn_readfirstlane(lds_addr(junk));
     }
-    mainloop_dma<E, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row, xpf);
+    if constexpr (RING)
+        mainloop_dma_ring<E, BM, BN, NW, RB, SPREAD>(acc, pa, pb, kbytes, sa, sb, a_row, b_row, xpf);
+    else
+        mainloop_dma<E, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row, xpf);
 
     // ---------------------------------------------------------------- epilogue ----
     // Per 32-row slab of this wave: stage scale*acc row-major in the wave's own (now
@@ -107,8 +155,6 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
     // Row sums: 16 lanes hold one slab row -> DPP all-reduce over them -> per-wave partial in
     // `red`, then the WAVES_N waves sharing a row are added in a fixed order.
     const float scale = (a_scale ? *a_scale : 1.0f) * (w_scale ? *w_scale : 1.0f);
-    using S = Slab<TN>;
-    uint8_t* slab = slab_region<NS, NW, kStage, S::kBytes>(st, wave);
     const int valid_rows = min(BM, M - m0);
     const uint32_t row_bytes = static_cast<uint32_t>(N) * 2;
     const size_t tile_off = static_cast<size_t>(m0) * N;
@@ -161,7 +207,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
                                                    h_rsrc, seg_voff(tm, j), 0, 0);
             // columns past N contribute nothing (their residual reads and sums are zero)
             sq = group_allreduce<S::kSegPerRow>(sq, AddOp());
-            if ((lane & (S::kSegPerRow - 1)) == 0) red[wn][wm * WM + tm * 32 + S::seg_row(j)] = sq;
+            if ((lane & (S::kSegPerRow - 1)) == 0) red[wn * BM + wm * WM + tm * 32 + S::seg_row(j)] = sq;
         }
     }
     __syncthreads();
@@ -171,7 +217,7 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
         if (m < M) {
             float s = 0.0f;
 #pragma unroll
-            for (int w = 0; w < WAVES_N; ++w) s += red[w][r];
+            for (int w = 0; w < WAVES_N; ++w) s += red[w * BM + r];
             P[static_cast<size_t>(m) * T + tile_n] = s;
         }
     }
@@ -190,6 +236,9 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #endif
 #ifndef CODA_G1_SPREAD
 #define CODA_G1_SPREAD 3
+#endif
+#ifndef CODA_G1_RING
+#define CODA_G1_RING 1
 #endif
 constexpr int BM1 = CODA_G1_BM, BN1 = CODA_G1_BN, NS1 = CODA_G1_NS, OCC1 = CODA_G1_OCC;
 constexpr int RB1 = CODA_G1_RB;
@@ -211,12 +260,12 @@ hipError_t launch_gemm_resid_partialrms(int M, int N, int K, const void* A, bool
     const int tiles_m = (M + BM1 - 1) / BM1, tiles_n = (N + BN1 - 1) / BN1;
     const dim3 grid(tiles_m * tiles_n), block(64 * WM1 * WN1);
     if (fp8) {
-        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1_8, RB1, SP1_8, OCC1, Elt::E4M3>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1_8, RB1, SP1_8, OCC1, CODA_G1_RING != 0, Elt::E4M3>), grid, block, 0,
                            stream, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W),
                            a_scale, w_scale, static_cast<const uint16_t*>(x_res),
                            static_cast<uint16_t*>(h), P, M, N, K, tiles_m, tiles_n);
     } else {
-        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1, RB1, SP1, OCC1, Elt::BF16>), grid, block, 0,
+        hipLaunchKernelGGL((k_gemm_resid_partialrms<BM1, BN1, WM1, WN1, NS1, RB1, SP1, OCC1, CODA_G1_RING != 0, Elt::BF16>), grid, block, 0,
                            stream, static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(W),
                            a_scale, w_scale, static_cast<const uint16_t*>(x_res),
                            static_cast<uint16_t*>(h), P, M, N, K, tiles_m, tiles_n);

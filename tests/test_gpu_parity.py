@@ -113,6 +113,10 @@ SMALL = [
     (130, 64, 144, 2 * 72, si.ACT_SWIGLU, "e4m3"),
     (333, 272, 528, 2 * 200, si.ACT_SWIGLU, "e4m3"),
     (64, 48, 128, 136, si.ACT_NONE, "e4m3"),
+    # six k-tiles with a ragged last one: every combination of the first GEMM's three A
+    # stages and two B stages, and the residual prefetch on a short loop
+    (200, 328, 256, 2 * 128, si.ACT_SWIGLU, "bf16"),
+    (200, 704, 256, 2 * 128, si.ACT_NONE, "e4m3"),
 ]
 
 
