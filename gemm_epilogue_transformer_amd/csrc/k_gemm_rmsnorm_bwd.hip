@@ -13,14 +13,16 @@
 // product C = A . B^T (+ C_res) in bf16: the first GEMM's input gradient.  Mainloop and tiles as the first GEMM; per 32-row slab
 // the accumulators are staged row-major in LDS and every lane takes runs of 8 columns:
 // 16-byte loads of h and dh_res (one slab ahead), fp32 arithmetic, one bf16 rounding,
-// one 16-byte store.
+// one 16-byte store.  RING: the mainloop on LDS stage rings (three stages of the dz
+// panel, which streams from HBM, two of the weight panel; mainloop_dma_ring), whose 160 KB
+// then also hold the epilogue's slabs.
 #include "epilogue.hpp"
 #include "gemm_pipeline.hpp"
 #include "launch.hpp"
 
 namespace coda {
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC, bool RING>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ WT, const uint16_t* Hb,
                    const float* __restrict__ Q, const uint16_t* DHres, uint16_t* DH, int M, int N, int K,
@@ -30,15 +32,30 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
     constexpr int TM = WM / 32, TN = WN / 32;
 
     constexpr int kStage = (BM + BN) * RB;
-    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
-    uint8_t* st[NS];
+    using S = Slab<TN>;
+    const int wave = threadIdx.x >> 6;
+    uint8_t* st[NS];          // shared stages (RING = false)
+    uint8_t* sa[3];           // the rings (RING = true)
+    uint8_t* sb[2];
+    uint8_t* slab;            // this wave's epilogue slab
+    if constexpr (RING) {
+        __shared__ __attribute__((aligned(1024))) uint8_t rings[3 * BM * RB + 2 * BN * RB];
+        static_assert(NW * S::kBytes <= 3 * BM * RB + 2 * BN * RB, "the slabs fit the rings");
 #pragma unroll
-    for (int i = 0; i < NS; ++i) st[i] = stages[i];
+        for (int i = 0; i < 3; ++i) sa[i] = rings + i * BM * RB;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sb[i] = rings + 3 * BM * RB + i * BN * RB;
+        slab = rings + wave * S::kBytes;
+    } else {
+        __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) st[i] = stages[i];
+        slab = slab_region<NS, NW, kStage, S::kBytes>(st, wave);
+    }
 
     int tile_m, tile_n;
     tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
-    const int wave = threadIdx.x >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     // q of this wave's rows (lane l: rows l, 64 + l, ...); rows past M hold 0
@@ -68,10 +85,11 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    mainloop_dma<Elt::BF16, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
+    if constexpr (RING)
+        mainloop_dma_ring<Elt::BF16, BM, BN, NW, RB, SPREAD>(acc, pa, pb, kbytes, sa, sb, a_row, b_row);
+    else
+        mainloop_dma<Elt::BF16, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row);
 
-    using S = Slab<TN>;
-    uint8_t* slab = slab_region<NS, NW, kStage, S::kBytes>(st, wave);
     const int valid_rows = min(BM, M - m0);
     const uint32_t row_bytes = static_cast<uint32_t>(N) * 2;
     const size_t tile_off = static_cast<size_t>(m0) * N;
@@ -141,6 +159,13 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
 #define CODA_B2_SPREAD 2
 #define CODA_B2_OCC 1
 #endif
+// Contractions of at least this many k run on the stage rings: there dz streams from HBM
+// (16384 tokens x 16384 of K: 0.836 against 0.861 ms; K = 128256: 6.46 against 6.66 ms),
+// while at K = 2048 or 3072 (operands in the cache) the two shared stages are as fast or
+// 1 % faster.  Both give the same bits.
+#ifndef CODA_B2_RING_MIN_K
+#define CODA_B2_RING_MIN_K 8192
+#endif
 constexpr int BMB = CODA_B2_BM, BNB = CODA_B2_BN;
 
 int64_t gemm_bwd2_tiles(int64_t M, int64_t N) { return ((M + BMB - 1) / BMB) * ((N + BNB - 1) / BNB); }
@@ -149,11 +174,18 @@ hipError_t launch_gemm_rmsnorm_bwd(int M, int N, int K, const void* dz, const vo
                                    const float* q, const void* dh_res, void* dh, hipStream_t stream) {
     const int tiles_m = (M + BMB - 1) / BMB, tiles_n = (N + BNB - 1) / BNB;
     const dim3 grid(tiles_m * tiles_n), block(64 * CODA_B2_WM * CODA_B2_WN);
-    hipLaunchKernelGGL((k_gemm_rmsnorm_bwd<BMB, BNB, CODA_B2_WM, CODA_B2_WN, CODA_B2_NS, CODA_B2_RB, CODA_B2_SPREAD,
-                                           CODA_B2_OCC>),
-                       grid, block, 0, stream, static_cast<const uint8_t*>(dz), static_cast<const uint8_t*>(Wt),
-                       static_cast<const uint16_t*>(h), q, static_cast<const uint16_t*>(dh_res),
-                       static_cast<uint16_t*>(dh), M, N, K, tiles_m, tiles_n);
+    if (K >= CODA_B2_RING_MIN_K)
+        hipLaunchKernelGGL((k_gemm_rmsnorm_bwd<BMB, BNB, CODA_B2_WM, CODA_B2_WN, CODA_B2_NS, CODA_B2_RB,
+                                               CODA_B2_SPREAD, CODA_B2_OCC, true>),
+                           grid, block, 0, stream, static_cast<const uint8_t*>(dz), static_cast<const uint8_t*>(Wt),
+                           static_cast<const uint16_t*>(h), q, static_cast<const uint16_t*>(dh_res),
+                           static_cast<uint16_t*>(dh), M, N, K, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL((k_gemm_rmsnorm_bwd<BMB, BNB, CODA_B2_WM, CODA_B2_WN, CODA_B2_NS, CODA_B2_RB,
+                                               CODA_B2_SPREAD, CODA_B2_OCC, false>),
+                           grid, block, 0, stream, static_cast<const uint8_t*>(dz), static_cast<const uint8_t*>(Wt),
+                           static_cast<const uint16_t*>(h), q, static_cast<const uint16_t*>(dh_res),
+                           static_cast<uint16_t*>(dh), M, N, K, tiles_m, tiles_n);
     return hipGetLastError();
 }
 

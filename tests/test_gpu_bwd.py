@@ -43,14 +43,18 @@ def _check(w, inp, dh, dz, r, rows=None, dh_res=None):
     dzg = oracle.bf16_decode(host_bits(dz))[sel]
     rg = r.cpu().numpy().astype(np.float64)[sel]
     ref_dz = o["r"][:, None] * o["dz"]
-    e_dh = np.abs(dhg - ref_dh) / (1 + np.abs(ref_dh))
+    tol = TOL["bf16"]
+    # dh sums 2F products whose dz operand the path rounds to bf16: its error grows with
+    # the root-sum-square of the terms (reading 18: 2e-2 (1 + |ref|) + 8 * 2^-8 * rss)
+    Wd = oracle.bf16_decode(Wp_ref)
+    rss = np.sqrt((ref_dz ** 2) @ (Wd ** 2))
+    e_dh = np.abs(dhg - ref_dh) / (tol * (1 + np.abs(ref_dh)) + 8 * 2.0 ** -8 * rss)
     e_dz = np.abs(dzg - ref_dz) / (1 + np.abs(ref_dz))
     rel_dh = np.linalg.norm(dhg - ref_dh) / np.linalg.norm(ref_dh)
-    _log(f"  dh err max {e_dh.max():.2e} (rel fro {rel_dh:.2e}), dz err max {e_dz.max():.2e}, "
+    _log(f"  dh err/bound max {e_dh.max():.2e} (rel fro {rel_dh:.2e}), dz err max {e_dz.max():.2e}, "
          f"r rel {np.max(np.abs(rg - o['r']) / o['r']):.2e}")
-    tol = TOL["bf16"]
     assert np.all(np.isfinite(dhg))
-    assert e_dh.max() <= tol and e_dz.max() <= tol
+    assert e_dh.max() <= 1 and rel_dh <= 1e-2 and e_dz.max() <= tol
     assert np.all(np.abs(rg - o["r"]) <= 2 * np.spacing(np.float32(o["r"])).astype(np.float64))
 
 
@@ -70,6 +74,8 @@ SMALL = [
     (257, 264, 200),
     (64, 128, 256),
     (1, 8, 8),
+    # a contraction of 2F = 8208 (a ragged k-tile): the input-gradient GEMM on its stage rings
+    (130, 136, 4104),
 ]
 
 

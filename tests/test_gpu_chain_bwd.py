@@ -136,6 +136,21 @@ def test_plain_gemm_matches_its_definition_and_adds_the_residual():
         assert np.all(np.abs(g - ref) <= bound * 1.01)
 
 
+def test_plain_gemm_long_contraction_matches_its_definition():
+    # K = 8200: the stage-ring mainloop, 129 k-tiles with a ragged last one
+    rng = np.random.default_rng(20)
+    M, N, K = 300, 136, 8200
+    a = si.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    b = si.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
+    Cg = coda.gemm_bf16(dev_bf16(a), dev_bf16(b))
+    torch.cuda.synchronize()
+    ad, bd = oracle.bf16_decode(a), oracle.bf16_decode(b)
+    ref = ad @ bd.T
+    g = oracle.bf16_decode(host_bits(Cg))
+    bound = 2.0 ** -8 * np.abs(ref) + (K + 2) * 2.0 ** -24 * (np.abs(ad) @ np.abs(bd).T)
+    assert np.all(np.abs(g - ref) <= bound * 1.01)
+
+
 def test_saved_pre_activation_and_its_backward():
     # z = bf16(r * (h . W'^T)) against its definition over the GPU's own h and r; the
     # saved backward's transposed copy is the exact transpose of its dz; ragged rows
