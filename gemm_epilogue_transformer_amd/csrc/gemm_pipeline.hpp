@@ -785,7 +785,8 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
 }
 
 // Mainloop with a ring of LDS stages per operand: three for the A panel, two for the B
-// panel (one element type E, RB-byte k-tile rows).  The crossing at the end of k-tile j
+// panel (FP: the fragments; PA, PB: the DMA panels, row-major or token-major; RB: the
+// bytes of a k-tile row, 32 KB stages for 256-row panels).  The crossing at the end of k-tile j
 // waits for k-tile j+1 (vmcnt(nA): only the A DMA of k-tile j+2 may be in flight),
 // passes the barrier, and issues the DMA of B(j+2) and then A(j+3) into the stages j's
 // own operands leave free (the first kPer instructions there, the rest over k-tile j+1's
@@ -793,21 +794,19 @@ __device__ __forceinline__ void mainloop_dma(f32x16_t (&acc)[TM][TN], const DmaP
 // B k-tile one.  B goes first so that the wait's in-order count never includes it.  For
 // an operand that streams from HBM (each A row panel is read by few tiles at a time)
 // the extra stage doubles the DMA's lead over memory latency at the same 128-byte rows.
-// sa: three A stages of BM*RB bytes, sb: two B stages of BN*RB bytes.  K = 0 computes
-// one k-tile of zeros; k-tiles past K are loaded as zeros.
+// sa: three A stages, sb: two B stages.  K = 0 computes one k-tile of zeros; k-tiles past
+// K are loaded as zeros.
 // The extra loads (xtra.issue_into) go out at each crossing right after the barrier,
 // before the batch, into the A stage just freed: the rows there that this wave's own
 // first A instructions of the batch fill later, which lands after them (a wave's loads
 // complete in order).  The next crossing's wait then covers them.
-template <Elt E, int BM, int BN, int NW, int RB, int SPREAD, int TM, int TN, class ARow, class BRow,
+template <class FP, int NW, int RB, int SPREAD, int TM, int TN, class PA, class PB, class ARow, class BRow,
           class X = NoExtra>
-__device__ __forceinline__ void mainloop_dma_ring(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
-                                                  const DmaPanel<BN, BN, NW, RB>& pb, int kbytes,
-                                                  uint8_t* const (&sa)[3], uint8_t* const (&sb)[2],
-                                                  const ARow& a_row, const BRow& b_row, const X& xtra = X()) {
-    using FP = FragPair<Frags<E, TM, TN, RB>>;
+__device__ __forceinline__ void mainloop_dma_ring_fp(f32x16_t (&acc)[TM][TN], const PA& pa, const PB& pb, int kbytes,
+                                                     uint8_t* const (&sa)[3], uint8_t* const (&sb)[2],
+                                                     const ARow& a_row, const BRow& b_row, const X& xtra = X()) {
     constexpr int KS = FP::kSteps, kMfma = TM * TN;
-    constexpr int nA = DmaPanel<BM, BM, NW, RB>::kInst, nB = DmaPanel<BN, BN, NW, RB>::kInst;
+    constexpr int nA = PA::kInst, nB = PB::kInst;
     constexpr int kPerTile = nA + nB;
     constexpr int kPer = (kPerTile + SPREAD - 1) / SPREAD;
     static_assert(KS >= 2 && KS % 2 == 0, "the last k-step crosses; the fragment parity repeats every k-tile");
@@ -818,7 +817,7 @@ __device__ __forceinline__ void mainloop_dma_ring(f32x16_t (&acc)[TM][TN], const
     const int nk = max((kbytes + RB - 1) / RB, 1);
     FP f;
     // batch instruction q: B first (q < nB), then A
-    auto issue_q = [&](int q, uint8_t* a_st, uint8_t* b_st, uint32_t oa, uint32_t ob) {
+    auto issue_q = [&](int q, uint8_t* a_st, uint8_t* b_st, const auto& oa, const auto& ob) {
         if (q < nB) pb.issue_one(q, b_st, ob);
         else pa.issue_one(q - nB, a_st, oa);
     };
@@ -826,7 +825,8 @@ __device__ __forceinline__ void mainloop_dma_ring(f32x16_t (&acc)[TM][TN], const
     pa.issue(sa[0], 0, kbytes);
     pb.issue(sb[0], 0, kbytes);
     pa.issue(sa[1], 1, kbytes);
-    uint32_t ob = pb.base_offset(1, kbytes), oa = pa.base_offset(2, kbytes);
+    auto ob = pb.base_offset(1, kbytes);
+    auto oa = pa.base_offset(2, kbytes);
     static_for<kPer>([&](auto Q) { issue_q(decltype(Q)::value, sa[2], sb[1], oa, ob); });
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(nA + kPer));   // A(0) and B(0) landed
     __syncthreads();
@@ -877,6 +877,17 @@ __device__ __forceinline__ void mainloop_dma_ring(f32x16_t (&acc)[TM][TN], const
     // drain the DMA that ran past the end before the LDS is reused or released
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+}
+
+// Both operands of one element type E with RB-byte k-tile rows.
+template <Elt E, int BM, int BN, int NW, int RB, int SPREAD, int TM, int TN, class ARow, class BRow,
+          class X = NoExtra>
+__device__ __forceinline__ void mainloop_dma_ring(f32x16_t (&acc)[TM][TN], const DmaPanel<BM, BM, NW, RB>& pa,
+                                                  const DmaPanel<BN, BN, NW, RB>& pb, int kbytes,
+                                                  uint8_t* const (&sa)[3], uint8_t* const (&sb)[2],
+                                                  const ARow& a_row, const BRow& b_row, const X& xtra = X()) {
+    mainloop_dma_ring_fp<FragPair<Frags<E, TM, TN, RB>>, NW, RB, SPREAD>(acc, pa, pb, kbytes, sa, sb, a_row, b_row,
+                                                                        xtra);
 }
 
 // ---------------------------------------------------------------------------------

@@ -33,7 +33,7 @@ namespace coda {
 // forward and backward store them, NR and NC of their columns used), read through LDS
 // transpose reads (DmaPanelTok / FragsTok); otherwise token-contiguous At [NR, K] and
 // Bt [NC, K] (lda, ldb unused).
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC, bool TOK>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int OCC, bool TOK, bool RING>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, const float* __restrict__ gamma,
              const uint16_t* __restrict__ Wraw, float* __restrict__ dW, float* __restrict__ Pg, int NR, int NC,
@@ -43,11 +43,33 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
     constexpr int TM = WM / 32, TN = WN / 32;
 
     constexpr int kStage = (BM + BN) * RB;
-    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
-    __shared__ float red[WAVES_M][BN];
-    uint8_t* st[NS];
+    using S = Slab<TN>;
+    static_assert(!RING || TOK, "the stage rings run the token-major panels");
+    uint8_t* st[NS];          // shared stages (RING = false)
+    uint8_t* sa[3];           // the rings (RING = true): three stages of the A panel, two of B
+    uint8_t* sb[2];
+    uint8_t* slab;            // this wave's epilogue slab
+    float* red;               // [WAVES_M][BN] column partials of the epilogue
+    {
+        const int w = threadIdx.x >> 6;
+        if constexpr (RING) {
+            __shared__ __attribute__((aligned(1024))) uint8_t rings[3 * BM * RB + 2 * BN * RB];
+            static_assert(NW * S::kBytes + WAVES_M * BN * 4 <= 3 * BM * RB + 2 * BN * RB, "slabs and partials fit");
 #pragma unroll
-    for (int i = 0; i < NS; ++i) st[i] = stages[i];
+            for (int i = 0; i < 3; ++i) sa[i] = rings + i * BM * RB;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) sb[i] = rings + 3 * BM * RB + i * BN * RB;
+            slab = rings + w * S::kBytes;
+            red = reinterpret_cast<float*>(rings + NW * S::kBytes);
+        } else {
+            __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+            __shared__ float red_s[WAVES_M][BN];
+#pragma unroll
+            for (int i = 0; i < NS; ++i) st[i] = stages[i];
+            slab = slab_region<NS, NW, kStage, S::kBytes>(st, w);
+            red = &red_s[0][0];
+        }
+    }
 
     const int tiles = tiles_m * tiles_n;
     const int split = blockIdx.x / tiles;
@@ -77,8 +99,11 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
         DmaPanelTok<NW> pa, pb;
         pa.init(At + (static_cast<size_t>(k0) * lda + m0) * 2, ktok, lda * 2, NR - m0);
         pb.init(Bt + (static_cast<size_t>(k0) * ldb + n0) * 2, ktok, ldb * 2, NC - n0);
-        mainloop_dma_fp<FragPair<FragsTok<TM, TN>>, BM, BN, BN, NS, NW, RB, RB, SPREAD>(acc, pa, pb, kext, kext, st,
-                                                                                      a_row, b_row);
+        if constexpr (RING)
+            mainloop_dma_ring_fp<FragPair<FragsTok<TM, TN>>, NW, RB, SPREAD>(acc, pa, pb, kext, sa, sb, a_row, b_row);
+        else
+            mainloop_dma_fp<FragPair<FragsTok<TM, TN>>, BM, BN, BN, NS, NW, RB, RB, SPREAD>(acc, pa, pb, kext, kext,
+                                                                                          st, a_row, b_row);
     } else {
         // rows are K tokens apart; this block reads tokens [k0, k0 + ktok) of each (the
         // descriptors start at token k0, the mainloop stops at kext)
@@ -94,9 +119,7 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
     dW += static_cast<size_t>(split) * NR * NC;
     if (Wraw) Pg += static_cast<size_t>(split) * tiles_m * NC;   // a token split's own partial rows
 
-    using S = Slab<TN>;
     static_assert(64 % S::kSegPerRow == 0, "a lane's segments share their columns");
-    uint8_t* slab = slab_region<NS, NW, kStage, S::kBytes>(st, wave);
     const int valid_rows = min(BM, NR - m0);
     const uint32_t wrow = static_cast<uint32_t>(NC) * 2, orow = static_cast<uint32_t>(NC) * 4;
     const __amdgpu_buffer_rsrc_t w_rsrc =
@@ -176,7 +199,7 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
             for (int off = S::kSegPerRow; off < 64; off <<= 1) cs[e] += __shfl_xor(cs[e], off);
         if (lane < S::kSegPerRow) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[wm][wn * WN + lane * 8 + e] = cs[e];
+            for (int e = 0; e < 8; ++e) red[wm * BN + wn * WN + lane * 8 + e] = cs[e];
         }
         __syncthreads();
         for (int c = threadIdx.x; c < BN; c += NT) {
@@ -184,7 +207,7 @@ k_gemm_wgrad(const uint8_t* __restrict__ At, const uint8_t* __restrict__ Bt, con
             if (k < NC) {
                 float s = 0.0f;
 #pragma unroll
-                for (int w = 0; w < WAVES_M; ++w) s += red[w][c];
+                for (int w = 0; w < WAVES_M; ++w) s += red[w * BN + c];
                 Pg[static_cast<size_t>(tile_m) * NC + k] = s;
             }
         }
@@ -246,6 +269,13 @@ __global__ void __launch_bounds__(256) k_fill_zero_f32(float* __restrict__ dst, 
 #define CODA_WG_RB 128
 #define CODA_WG_SPREAD 2
 #define CODA_WG_OCC 1
+#endif
+// Token-major weight gradients whose blocks each sum at least this many tokens run on the
+// LDS stage rings (three stages of the A panel, two of B; mainloop_dma_ring_fp): dz, the A
+// panel, streams from HBM there (16384 tokens x 16384 columns: 0.833-0.840 against
+// 0.841-0.847 ms); a token split's shorter blocks keep the two shared stages.  Same bits.
+#ifndef CODA_WG_RING_MIN_K
+#define CODA_WG_RING_MIN_K 8192
 #endif
 constexpr int BMW = CODA_WG_BM, BNW = CODA_WG_BN;
 
@@ -309,11 +339,18 @@ static hipError_t launch_wgrad(int NR, int NC, int K, const void* At, int lda, c
     // split: dW slices, then (with W) the partial slices, in the workspace
     float* ws_p = S > 1 ? ws + static_cast<int64_t>(S) * NR * NC : nullptr;
     const dim3 grid(tiles_m * tiles_n * S), block(64 * CODA_WG_WM * CODA_WG_WN);
-    hipLaunchKernelGGL((k_gemm_wgrad<BMW, BNW, CODA_WG_WM, CODA_WG_WN, CODA_WG_NS, CODA_WG_RB, CODA_WG_SPREAD,
-                                     CODA_WG_OCC, TOK>),
-                       grid, block, 0, stream, static_cast<const uint8_t*>(At), static_cast<const uint8_t*>(Bt),
-                       S > 1 ? nullptr : gamma, static_cast<const uint16_t*>(Wraw), S > 1 ? ws : dW,
-                       S > 1 && Wraw ? ws_p : Pg, NR, NC, K, tiles_m, tiles_n, k_split, lda, ldb);
+    if (TOK && k_split >= CODA_WG_RING_MIN_K)
+        hipLaunchKernelGGL((k_gemm_wgrad<BMW, BNW, CODA_WG_WM, CODA_WG_WN, CODA_WG_NS, CODA_WG_RB, CODA_WG_SPREAD,
+                                         CODA_WG_OCC, TOK, TOK>),
+                           grid, block, 0, stream, static_cast<const uint8_t*>(At), static_cast<const uint8_t*>(Bt),
+                           S > 1 ? nullptr : gamma, static_cast<const uint16_t*>(Wraw), S > 1 ? ws : dW,
+                           S > 1 && Wraw ? ws_p : Pg, NR, NC, K, tiles_m, tiles_n, k_split, lda, ldb);
+    else
+        hipLaunchKernelGGL((k_gemm_wgrad<BMW, BNW, CODA_WG_WM, CODA_WG_WN, CODA_WG_NS, CODA_WG_RB, CODA_WG_SPREAD,
+                                         CODA_WG_OCC, TOK, false>),
+                           grid, block, 0, stream, static_cast<const uint8_t*>(At), static_cast<const uint8_t*>(Bt),
+                           S > 1 ? nullptr : gamma, static_cast<const uint16_t*>(Wraw), S > 1 ? ws : dW,
+                           S > 1 && Wraw ? ws_p : Pg, NR, NC, K, tiles_m, tiles_n, k_split, lda, ldb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     const int64_t n4 = static_cast<int64_t>(NR) * NC / 4;
