@@ -806,7 +806,7 @@ __device__ __forceinline__ void swiglu_epilogue_tc(const f32x16_t (&acc)[TM][TN]
 // LDS, bit-identical to a pre-folded W').  W8: the
 // weights are e4m3, RB is the k-tile depth of a bf16 h row and a W row holds RB/2 bytes.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int RB, int SPREAD, int PIPE, int OCC, int ACT,
-          bool W8>
+          bool W8, bool RING = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, OCC)
 k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W,
                        const float* __restrict__ w_scale, const float* __restrict__ R,
@@ -828,12 +828,34 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     constexpr int RBB = W8 ? RB / 2 : RB;            // bytes of a W row per k-tile
     constexpr int kStage = BM * RB + BN * RBB;
     static_assert(!W8 || (RB == 128 && PIPE == 0), "8-bit weights: DMA mainloop, 64-k tiles");
-    __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
-    // cross-entropy: (max, sum-exp) of every row for each of the WAVES_N column halves
-    __shared__ float ce_red[ACT == kActCe ? 2 * WAVES_N * BM : (ACT == kActSwigluBwd ? WAVES_N * BM : 1)];
+    // RING: the mainloop on LDS stage rings (three h stages, two weight stages), which take
+    // the whole LDS; the epilogue's slabs and row partials then live in the ring memory
+    static_assert(!RING || (!W8 && PIPE == 0 && (ACT == kActSwigluBwd || ACT == kActCeBwd || ACT == kActRope)),
+                  "rings: the bf16 SwiGLU and loss backward, RoPE");
+    constexpr int kSlabBytes = Slab<(ACT == kActSwiglu) ? TN / 2 : TN>::kBytes;
+    constexpr int kRed = ACT == kActCe ? 2 * WAVES_N * BM : (ACT == kActSwigluBwd ? WAVES_N * BM : 1);
     uint8_t* st[NS];
+    uint8_t* sa[3];
+    uint8_t* sb[2];
+    float* ce_red;            // cross-entropy: (max, sum-exp) of every row for each of the WAVES_N column halves
+    uint8_t* slab;            // this wave's epilogue slab
+    if constexpr (RING) {
+        __shared__ __attribute__((aligned(1024))) uint8_t rings[3 * BM * RB + 2 * BN * RBB];
+        static_assert(NW * kSlabBytes + kRed * 4 <= 3 * BM * RB + 2 * BN * RBB, "slabs and partials fit");
 #pragma unroll
-    for (int i = 0; i < NS; ++i) st[i] = stages[i];
+        for (int i = 0; i < 3; ++i) sa[i] = rings + i * BM * RB;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sb[i] = rings + 3 * BM * RB + i * BN * RBB;
+        slab = rings + (threadIdx.x >> 6) * kSlabBytes;
+        ce_red = reinterpret_cast<float*>(rings + NW * kSlabBytes);
+    } else {
+        __shared__ __attribute__((aligned(1024))) uint8_t stages[NS][kStage];
+        __shared__ float ce_red_s[kRed];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) st[i] = stages[i];
+        slab = slab_region<NS, NW, kStage, kSlabBytes>(st, threadIdx.x >> 6);
+        ce_red = ce_red_s;
+    }
 
     int tile_m, tile_n;
     tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
@@ -920,13 +942,15 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
         static_assert(NS == 2, "the register-staged mainloop has two LDS stages");
         mainloop_reg<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NW, RB>(acc, pa, pb, kbytes, st, a_row, b_row,
                                                                          GammaFold<RB>(gfold, K));
+    } else if constexpr (RING) {
+        mainloop_dma_ring_fp<FragPair<Frags<Elt::BF16, TM, TN, RB, TC>>, NW, RB, SPREAD>(acc, pa, pb, kbytes, sa, sb,
+                                                                                       a_row, b_row);
     } else {
         mainloop_dma<Elt::BF16, BM, BN, (SWIGLU ? BN / 2 : BN), NS, NW, RB, SPREAD, TC>(acc, pa, pb, kbytes, st, a_row,
                                                                                      b_row);
     }
 
     const float sw = w_scale ? *w_scale : 1.0f;
-    uint8_t* slab = slab_region<NS, NW, kStage, Slab<(ACT == kActSwiglu) ? TN / 2 : TN>::kBytes>(st, wave);
     if constexpr (ACT == kActCe && TC)
         ce_epilogue_tc<BM, BN, WAVES_M, WAVES_N, TM, TN>(acc, rt, tt, sw, ce, M, N_out, m0, j0, tile_n, wm, wn,
                                                          ce_red);
@@ -1741,6 +1765,21 @@ k_gemm_ce_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, cons
 #ifndef CODA_G3_SPREAD
 #define CODA_G3_SPREAD 3
 #endif
+// The one-tile-per-workgroup GEMM on LDS stage rings (three h stages, two weight stages,
+// mainloop_dma_ring_fp) for the recomputing SwiGLU backward (0.968-0.982 against 0.976-0.992
+// ms on the 16K-token MLP input) and the loss backward (7.20-7.21 against 7.28 ms on the
+// 128256-token LM head), whose operands the backward's other kernels have pushed out of the
+// last-level cache; RoPE (operands in the cache) measured within noise and keeps the two
+// shared stages.  The same bits either way.
+#ifndef CODA_G3_RING_BWD
+#define CODA_G3_RING_BWD 1
+#endif
+#ifndef CODA_G3_RING_CEBWD
+#define CODA_G3_RING_CEBWD 1
+#endif
+#ifndef CODA_G3_RING_ROPE
+#define CODA_G3_RING_ROPE 0
+#endif
 #ifndef CODA_G3_PIPE
 #define CODA_G3_PIPE 0
 #endif
@@ -1790,7 +1829,7 @@ static hipError_t cu_count(int* cus) {
     return hipSuccess;
 }
 
-template <int ACT, bool WFP8, bool GFOLD = false>
+template <int ACT, bool WFP8, bool GFOLD = false, bool RING = false>
 static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
                           const float* w_scale, const float* r, void* y, const RopeArgs& rope,
                           const CeArgs& ce, const BwdArgs& bw, hipStream_t stream,
@@ -1801,7 +1840,7 @@ static hipError_t launch3(int M, int N_out, int K, const void* h, const void* W,
     static_assert(!(GFOLD && WFP8), "the in-kernel fold takes a bf16 weight");
     constexpr int PIPE = GFOLD ? 2 : (WFP8 ? 0 : PIPE3);
     hipLaunchKernelGGL((k_gemm_rowscale_swiglu<BM3, BN3, WM3, WN3, WFP8 ? NS3_8 : NS3, RB3, SP3, PIPE,
-                                               OCC3, ACT, WFP8>),
+                                               OCC3, ACT, WFP8, RING>),
                        grid, block, 0, stream, static_cast<const uint8_t*>(h), static_cast<const uint8_t*>(W),
                        w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m, tiles_n, rope, ce, bw, gfold);
     return hipGetLastError();
@@ -1871,7 +1910,8 @@ hipError_t launch_gemm_rowscale_rope(int M, int N_out, int K, const void* h, con
     const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
     const BwdArgs no_bw{nullptr, nullptr, nullptr, 0};
     return w_fp8 ? launch3<kActRope, true>(M, N_out, K, h, W, w_scale, r, y, rope, no_ce, no_bw, stream)
-                 : launch3<kActRope, false>(M, N_out, K, h, W, w_scale, r, y, rope, no_ce, no_bw, stream);
+                 : launch3<kActRope, false, false, CODA_G3_RING_ROPE != 0>(M, N_out, K, h, W, w_scale, r, y, rope,
+                                                                         no_ce, no_bw, stream);
 }
 
 int64_t ce_partials_per_row(int64_t V) { return V < 1 ? -1 : (V + BN3 - 1) / BN3; }
@@ -1920,7 +1960,8 @@ hipError_t launch_gemm_ce_bwd(int M, int V, int K, const void* h, const void* W,
     const CeArgs ce{targets, nullptr, nullptr, 0, lse, gw};
     // partials per row and 128 columns (a wave's share of a 256-column tile)
     const BwdArgs bw{nullptr, static_cast<uint16_t*>(dz), partials, static_cast<int>(swiglu_bwd_partials_per_row(V))};
-    return launch3<kActCeBwd, false>(M, V, K, h, W, nullptr, r, nullptr, none, ce, bw, stream);
+    return launch3<kActCeBwd, false, false, CODA_G3_RING_CEBWD != 0>(M, V, K, h, W, nullptr, r, nullptr, none, ce,
+                                                                      bw, stream);
 }
 
 hipError_t launch_gemm_swiglu_bwd(int M, int F, int K, const void* h, const void* W, const float* r,
@@ -1929,7 +1970,8 @@ hipError_t launch_gemm_swiglu_bwd(int M, int F, int K, const void* h, const void
     const CeArgs no_ce{nullptr, nullptr, nullptr, 0};
     const BwdArgs bw{static_cast<const uint16_t*>(dy), static_cast<uint16_t*>(dz), partials,
                      static_cast<int>(swiglu_bwd_partials_per_row(F))};
-    return launch3<kActSwigluBwd, false>(M, F, K, h, W, nullptr, r, nullptr, none, no_ce, bw, stream);
+    return launch3<kActSwigluBwd, false, false, CODA_G3_RING_BWD != 0>(M, F, K, h, W, nullptr, r, nullptr, none,
+                                                                        no_ce, bw, stream);
 }
 
 }  // namespace coda
