@@ -234,8 +234,10 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
 #define CODA_G1_RB 128
 #define CODA_G1_OCC 1
 #endif
+// k-steps a k-tile's DMA is spread over (on the rings 4: 135.8-138.1 against 139.4-140.8 us
+// for 3 and 145.8-147.2 for 2 inside the chain; the 8-bit k-tiles have two k-steps)
 #ifndef CODA_G1_SPREAD
-#define CODA_G1_SPREAD 3
+#define CODA_G1_SPREAD 4
 #endif
 #ifndef CODA_G1_RING
 #define CODA_G1_RING 1

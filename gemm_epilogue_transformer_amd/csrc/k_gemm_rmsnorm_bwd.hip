@@ -156,7 +156,7 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
 #define CODA_B2_WN 2
 #define CODA_B2_NS 2
 #define CODA_B2_RB 128
-#define CODA_B2_SPREAD 2
+#define CODA_B2_SPREAD 3
 #define CODA_B2_OCC 1
 #endif
 // Contractions of at least this many k run on the stage rings: there dz streams from HBM
@@ -165,6 +165,11 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
 // 1 % faster.  Both give the same bits.
 #ifndef CODA_B2_RING_MIN_K
 #define CODA_B2_RING_MIN_K 8192
+#endif
+// k-steps a k-tile's DMA is spread over on the rings (on the shared stages: CODA_B2_SPREAD;
+// 4 there made dA 7 % slower, 4 on the rings is 0.2-0.8 % faster than 3)
+#ifndef CODA_B2_SPREAD_RING
+#define CODA_B2_SPREAD_RING 4
 #endif
 constexpr int BMB = CODA_B2_BM, BNB = CODA_B2_BN;
 
@@ -176,7 +181,7 @@ hipError_t launch_gemm_rmsnorm_bwd(int M, int N, int K, const void* dz, const vo
     const dim3 grid(tiles_m * tiles_n), block(64 * CODA_B2_WM * CODA_B2_WN);
     if (K >= CODA_B2_RING_MIN_K)
         hipLaunchKernelGGL((k_gemm_rmsnorm_bwd<BMB, BNB, CODA_B2_WM, CODA_B2_WN, CODA_B2_NS, CODA_B2_RB,
-                                               CODA_B2_SPREAD, CODA_B2_OCC, true>),
+                                               CODA_B2_SPREAD_RING, CODA_B2_OCC, true>),
                            grid, block, 0, stream, static_cast<const uint8_t*>(dz), static_cast<const uint8_t*>(Wt),
                            static_cast<const uint16_t*>(h), q, static_cast<const uint16_t*>(dh_res),
                            static_cast<uint16_t*>(dh), M, N, K, tiles_m, tiles_n);
