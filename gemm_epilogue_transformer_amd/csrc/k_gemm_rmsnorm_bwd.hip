@@ -159,12 +159,13 @@ k_gemm_rmsnorm_bwd(const uint8_t* __restrict__ DZ, const uint8_t* __restrict__ W
 #define CODA_B2_SPREAD 3
 #define CODA_B2_OCC 1
 #endif
-// Contractions of at least this many k run on the stage rings: there dz streams from HBM
+// Contractions of at least this many k run on the stage rings: where dz streams from HBM
 // (16384 tokens x 16384 of K: 0.836 against 0.861 ms; K = 128256: 6.46 against 6.66 ms),
-// while at K = 2048 or 3072 (operands in the cache) the two shared stages are as fast or
-// 1 % faster.  Both give the same bits.
+// and with the rings' wider DMA spread also at K = 2048 (dA: 0.1245-0.1248 against
+// 0.1297-0.1302 ms) and 3072 (0.184 against 0.189 ms); shorter ones keep the two shared
+// stages.  Both give the same bits.
 #ifndef CODA_B2_RING_MIN_K
-#define CODA_B2_RING_MIN_K 8192
+#define CODA_B2_RING_MIN_K 2048
 #endif
 // k-steps a k-tile's DMA is spread over on the rings (on the shared stages: CODA_B2_SPREAD;
 // 4 there made dA 7 % slower, 4 on the rings is 0.2-0.8 % faster than 3)
