@@ -1769,8 +1769,8 @@ k_gemm_ce_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, cons
 // mainloop_dma_ring_fp) for the recomputing SwiGLU backward (0.968-0.982 against 0.976-0.992
 // ms on the 16K-token MLP input) and the loss backward (7.20-7.21 against 7.28 ms on the
 // 128256-token LM head), whose operands the backward's other kernels have pushed out of the
-// last-level cache; RoPE (operands in the cache) measured within noise and keeps the two
-// shared stages.  The same bits either way.
+// last-level cache, and for RoPE (with the rings' DMA spread of 4: 0.1905-0.1910 against
+// 0.1936-0.1962 ms on the 16K-token QKV projection).  The same bits either way.
 #ifndef CODA_G3_RING_BWD
 #define CODA_G3_RING_BWD 1
 #endif
@@ -1783,7 +1783,7 @@ k_gemm_ce_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, cons
 #define CODA_G3_RING_CEBWD 1
 #endif
 #ifndef CODA_G3_RING_ROPE
-#define CODA_G3_RING_ROPE 0
+#define CODA_G3_RING_ROPE 1
 #endif
 #ifndef CODA_G3_PIPE
 #define CODA_G3_PIPE 0
