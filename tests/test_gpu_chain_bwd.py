@@ -136,10 +136,11 @@ def test_plain_gemm_matches_its_definition_and_adds_the_residual():
         assert np.all(np.abs(g - ref) <= bound * 1.01)
 
 
-def test_plain_gemm_long_contraction_matches_its_definition():
-    # K = 8200: the stage-ring mainloop, 129 k-tiles with a ragged last one
-    rng = np.random.default_rng(20)
-    M, N, K = 300, 136, 8200
+@pytest.mark.parametrize("K", [2056, 8200])
+def test_plain_gemm_long_contraction_matches_its_definition(K):
+    # K from 2048 up: the stage-ring mainloop (33 or 129 k-tiles, the last one ragged)
+    rng = np.random.default_rng(20 + K)
+    M, N = 300, 136
     a = si.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
     b = si.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
     Cg = coda.gemm_bf16(dev_bf16(a), dev_bf16(b))

@@ -117,6 +117,9 @@ SMALL = [
     # stages and two B stages, and the residual prefetch on a short loop
     (200, 328, 256, 2 * 128, si.ACT_SWIGLU, "bf16"),
     (200, 704, 256, 2 * 128, si.ACT_NONE, "e4m3"),
+    # two and five k-tiles (the rings' other phases)
+    (130, 256, 144, 2 * 64, si.ACT_SWIGLU, "e4m3"),
+    (260, 320, 264, 136, si.ACT_NONE, "bf16"),
 ]
 
 

@@ -256,9 +256,10 @@ def test_token_major_operands_match_the_transposed_path(K, NR, NC, lda, ldb):
     assert torch.equal(t_dW, r_dW) and torch.equal(t_P, r_P) and torch.equal(t_s, r_s)
 
 
-@pytest.mark.parametrize("K", [1, 13, 77, 200])
+@pytest.mark.parametrize("K", [1, 13, 77, 200, 8221])
 def test_token_major_any_token_count(K):
     # no granule on the tokens: against the fp64 definition, |err| <= (K + 2) 2^-24 sum|terms|
+    # (8221 tokens in one block: the stage-ring mainloop with a ragged last k-tile)
     rng = np.random.default_rng(50 + K)
     NR, NC = 136, 72
     xb = si.to_bf16_bits(rng.standard_normal((K, NR)).astype(np.float32))
