@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace coda {
 
@@ -86,8 +87,10 @@ __device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t c) {
 // each XCD with its own L2).  Give every XCD one contiguous range of the linear tile
 // order, then walk that order in groups of `G` tile-rows so that the tiles resident at
 // the same time on one XCD share A row-panels and B column-panels in its L2.
-template <int G>
-__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+// (G a runtime value: tile_coords_g, for a kernel that picks the group by its shape.)
+template <class GT>
+__device__ __forceinline__ void tile_coords_impl(int pid, int tiles_m, int tiles_n, GT gt, int& tm, int& tn) {
+    const int G = gt;
     const int total = tiles_m * tiles_n;
     const int xcd = pid & 7, local = pid >> 3;
     const int q = total >> 3, rem = total & 7;
@@ -98,6 +101,15 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     const int in = lin - group * G * tiles_n;
     tm = first_m + in % gsize;
     tn = in / gsize;
+}
+
+template <int G>
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    tile_coords_impl(pid, tiles_m, tiles_n, std::integral_constant<int, G>{}, tm, tn);
+}
+
+__device__ __forceinline__ void tile_coords_g(int pid, int tiles_m, int tiles_n, int G, int& tm, int& tn) {
+    tile_coords_impl(pid, tiles_m, tiles_n, G, tm, tn);
 }
 
 }  // namespace coda

@@ -38,6 +38,20 @@
 
 namespace coda {
 
+// Tile-rows per group of the tile walks (tile_coords): the one-tile-per-workgroup kernel
+// (4 rather than 8: 1-3 % faster on the 16K-token shapes) and the overlapped loss kernel
+// (no difference measured); the overlapped row-scale kernels take theirs at launch.
+// Outputs do not depend on the walk.
+#ifndef CODA_G3_NP_GROUP
+#define CODA_G3_NP_GROUP 4
+#endif
+#ifndef CODA_G3_CE_GROUP
+#define CODA_G3_CE_GROUP 8
+#endif
+#ifndef CODA_G3_OVL_SMALL_K
+#define CODA_G3_OVL_SMALL_K 2048
+#endif
+
 enum { kActNone = 0, kActSwiglu = 1, kActRope = 2, kActCe = 3, kActSwigluBwd = 4, kActSwigluSave = 5, kActCeBwd = 6 };
 
 // RoPE operands (unused by the other activations).
@@ -858,7 +872,7 @@ k_gemm_rowscale_swiglu(const uint8_t* __restrict__ H, const uint8_t* __restrict_
     }
 
     int tile_m, tile_n;
-    tile_coords<8>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+    tile_coords<CODA_G3_NP_GROUP>(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, j0 = tile_n * BNO;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -1303,7 +1317,7 @@ template <bool SWIGLU, int BM, int BN, int WAVES_M, int WAVES_N, int RB, int SPR
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1)
 k_gemm_rowscale_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
                     const float* __restrict__ R, uint16_t* __restrict__ Y, int M, int N_out, int K, int tiles_m,
-                    int tiles_n) {
+                    int tiles_n, int group) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -1336,7 +1350,7 @@ k_gemm_rowscale_ovl(const uint8_t* __restrict__ H, const uint8_t* __restrict__ W
     };
     auto setup = [&](int t, PanelA& A, PanelB& B, int& tm0, int& tj0) {
         int tile_m, tile_n;
-        tile_coords<8>(t, tiles_m, tiles_n, tile_m, tile_n);
+        tile_coords_g(t, tiles_m, tiles_n, group, tile_m, tile_n);
         tm0 = tile_m * BM;
         tj0 = tile_n * BNO;
         const uint8_t* a0 = H + static_cast<size_t>(tm0) * kbytes;
@@ -1446,7 +1460,7 @@ k_gemm_ce_persistent(const uint8_t* __restrict__ H, const uint8_t* __restrict__ 
     int tv[TM];
     auto setup = [&](int t) {
         int tile_m, tile_n;
-        tile_coords<8>(t, tiles_m, tiles_n, tile_m, tile_n);
+        tile_coords<CODA_G3_CE_GROUP>(t, tiles_m, tiles_n, tile_m, tile_n);
         m0 = tile_m * BM;
         j0 = tile_n * BN;
         tn0 = tile_n;
@@ -1813,6 +1827,14 @@ int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
     return ((M + BM3 - 1) / BM3) * ((N_out + bno - 1) / bno);
 }
 
+// Tile-rows per group of the overlapped row-scale kernels' walk.  The 32 tiles an XCD runs
+// at once cover G tile-rows x 32/G tile-columns.  With 1 MB K-panels (K <= 2048) G = 2
+// keeps the two row panels in the XCD's L2 across rounds and writes y in 4 KB row runs
+// (workload 2: -3.3 %, the QKV projection -5.2 % against G = 8); with larger panels
+// that no longer fits and G = 8 (12 panels per round) is the best (K = 4096: G = 2 +4.3 %,
+// G = 4 +1.2 %).
+static int ovl_group(int K) { return K <= CODA_G3_OVL_SMALL_K ? 2 : 8; }
+
 // Compute units of the current device, queried once per device (the persistent grid size).
 static hipError_t cu_count(int* cus) {
     static std::atomic<int> cache[64] = {};
@@ -1878,7 +1900,7 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
         hipLaunchKernelGGL((k_gemm_rowscale_ovl<false, BM3, BN3, WM3, WN3, RB3, SP3, 2>), dim3(grid),
                            dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
                            static_cast<const uint8_t*>(W), w_scale, r, static_cast<uint16_t*>(y), M, N_out, K, tiles_m,
-                           tiles_n);
+                           tiles_n, ovl_group(K));
         return hipGetLastError();
     }
     if (swiglu && !w_fp8 && CODA_G3_PERSIST && CODA_G3_TC && PIPE3 == 0) {
@@ -1891,7 +1913,7 @@ hipError_t launch_gemm_rowscale_swiglu(int M, int N_out, int K, bool swiglu, con
             hipLaunchKernelGGL((k_gemm_rowscale_ovl<true, BM3, BN3, WM3, WN3, RB3, SP3, CODA_G3_HOLD>), dim3(grid),
                                dim3(64 * WM3 * WN3), 0, stream, static_cast<const uint8_t*>(h),
                                static_cast<const uint8_t*>(W), w_scale, r, static_cast<uint16_t*>(y), M, N_out, K,
-                               tiles_m, tiles_n);
+                               tiles_m, tiles_n, ovl_group(K));
             return hipGetLastError();
         }
         hipLaunchKernelGGL((k_gemm_swiglu_persistent<BM3, BN3, WM3, WN3, NS3, RB3, SP3>), dim3(grid),
