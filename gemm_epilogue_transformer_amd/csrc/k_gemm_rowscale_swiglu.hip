@@ -1828,12 +1828,12 @@ int64_t gemm3_tiles(int64_t M, int64_t N_out, bool swiglu) {
 }
 
 // Tile-rows per group of the overlapped row-scale kernels' walk.  The 32 tiles an XCD runs
-// at once cover G tile-rows x 32/G tile-columns.  With 1 MB K-panels (K <= 2048) G = 2
-// keeps the two row panels in the XCD's L2 across rounds and writes y in 4 KB row runs
-// (workload 2: -3.3 %, the QKV projection -5.2 % against G = 8); with larger panels
-// that no longer fits and G = 8 (12 panels per round) is the best (K = 4096: G = 2 +4.3 %,
-// G = 4 +1.2 %).
-static int ovl_group(int K) { return K <= CODA_G3_OVL_SMALL_K ? 2 : 8; }
+// at once cover G tile-rows x 32/G tile-columns.  With 1 MB K-panels (K <= 2048) G = 4
+// touches the same 12 panels per round as G = 8 and writes y in 2 KB row runs (workload
+// 2: -2.0 %, the QKV projection -4.0 % against G = 8).  G = 2 was another 1.3 % faster
+// there but moved 2.70 instead of 1.89 GB through the L2 per launch (18 panels per round);
+// with larger panels G = 8 is the best (K = 4096: G = 4 +1.2 %, G = 2 +4.3 %).
+static int ovl_group(int K) { return K <= CODA_G3_OVL_SMALL_K ? 4 : 8; }
 
 // Compute units of the current device, queried once per device (the persistent grid size).
 static hipError_t cu_count(int* cus) {
