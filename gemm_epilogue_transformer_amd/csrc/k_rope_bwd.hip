@@ -18,7 +18,9 @@
 // Tile: 64 rows x 128 columns, 256 threads.  A thread takes 4 (row, 8-column chunk)
 // pairs: rows (thread / 16) + 16 i at chunk thread % 16, so 16 consecutive lanes cover
 // one row's 128 columns.  A chunk lies in one half of one head (8 | 32), so it needs the
-// partner chunk 32 columns away and 8 consecutive frequencies of the table row.  Every
+// partner chunk 32 columns away, which lane chunk ^ 4 of the same row holds (an 8-lane
+// mirror, then a reversal inside each quad, as two data-parallel moves instead of a second
+// load of dy), and 8 consecutive frequencies of the table row.  Every
 // operand goes through buffer descriptors spanning the tile's rows; columns past N, and
 // table rows outside [0, table_rows) (the forward read zero angles there), read at an
 // offset beyond every range, i.e. zeros, and stores there are dropped.
@@ -61,10 +63,9 @@ k_rope_bwd(const uint16_t* __restrict__ DY, const uint16_t* __restrict__ Y, cons
     const bool rotated = j < rot_cols;                       // rot_cols % 64 == 0: whole chunks
     const int i0 = j & 63;
     const bool first = i0 < 32;                              // first half of its head
-    const int partner = first ? j + 32 : j - 32;
     const uint32_t freq_off = static_cast<uint32_t>(i0 & 31) * 4u;
 
-    i32x4_t dv[kRbPairs], pv[kRbPairs], yv[kRbPairs];
+    i32x4_t dv[kRbPairs], yv[kRbPairs];
     f32x4_t c0[kRbPairs], c1[kRbPairs], s0[kRbPairs], s1[kRbPairs];
     float rv[kRbPairs];
     uint32_t off[kRbPairs];
@@ -72,10 +73,7 @@ k_rope_bwd(const uint16_t* __restrict__ DY, const uint16_t* __restrict__ Y, cons
     for (int it = 0; it < kRbPairs; ++it) {
         const uint32_t row = static_cast<uint32_t>((tid >> 4) + 16 * it);
         off[it] = col_in ? row * row_bytes + static_cast<uint32_t>(j) * 2u : kOobOffset;
-        const uint32_t poff = (col_in && rotated) ? row * row_bytes + static_cast<uint32_t>(partner) * 2u
-                                                  : kOobOffset;
         dv[it] = __builtin_amdgcn_raw_buffer_load_b128(dy_rsrc, off[it], 0, 0);
-        pv[it] = __builtin_amdgcn_raw_buffer_load_b128(dy_rsrc, poff, 0, 0);
         yv[it] = __builtin_amdgcn_raw_buffer_load_b128(y_rsrc, off[it], 0, 0);
         rv[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_rsrc, row * 4u, 0, 0));
         const int p = __builtin_amdgcn_raw_buffer_load_b32(pos_rsrc, row * 4u, 0, 0);
@@ -94,7 +92,11 @@ k_rope_bwd(const uint16_t* __restrict__ DY, const uint16_t* __restrict__ Y, cons
         uint32_t o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint32_t xd = static_cast<uint32_t>(dv[it][e]), xp = static_cast<uint32_t>(pv[it][e]);
+            // lane l reads lane l ^ 4 of its 16-lane row: the 8-lane mirror takes l to
+            // l ^ 7, the quad reversal (quad_perm 3,2,1,0) then flips the low two bits
+            const int mirrored = __builtin_amdgcn_update_dpp(dv[it][e], dv[it][e], 0x141, 0xF, 0xF, false);
+            const uint32_t xp = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(mirrored, mirrored, 0x1B, 0xF, 0xF, false));
+            const uint32_t xd = static_cast<uint32_t>(dv[it][e]);
             const uint32_t xy = static_cast<uint32_t>(yv[it][e]);
             float g[2];
 #pragma unroll
