@@ -17,6 +17,14 @@ namespace coda {
 
 // Tile-rows per group of the tile walk (tile_coords): 4 rather than 8 was 1-4 % faster on
 // the 16K-token shapes (11 % on the 8-bit first GEMM); outputs do not depend on the walk.
+// The residual prefetch on the stage rings (XresPrefetchRing): off.  With the walk in
+// groups of 4 tile-rows it no longer pays (one machine each, alternating, bits equal): the
+// 16K-token attention output 0.1248-0.1252 against 0.1250-0.1251 ms without and with it,
+// the 8192-deep MLP output 0.4115-0.4125 against 0.4163-0.4166 ms, the 8-bit form
+// 0.0740-0.0748 against 0.0755-0.0756 ms.
+#ifndef CODA_G1_XPF
+#define CODA_G1_XPF 0
+#endif
 #ifndef CODA_G1_GROUP
 #define CODA_G1_GROUP 4
 #endif
@@ -149,8 +157,10 @@ k_gemm_resid_partialrms(const uint8_t* __restrict__ A, const uint8_t* __restrict
         xpf.inst_step = __builtin_amdgcn_readfirstlane(2u * rb);
         if constexpr (!RING) xpf.junk = __builtin_amdgcn_readfirstlane(lds_addr(junk));
     }
-    if constexpr (RING)
+    if constexpr (RING && CODA_G1_XPF)
         mainloop_dma_ring<E, BM, BN, NW, RB, SPREAD>(acc, pa, pb, kbytes, sa, sb, a_row, b_row, xpf);
+    else if constexpr (RING)
+        mainloop_dma_ring<E, BM, BN, NW, RB, SPREAD>(acc, pa, pb, kbytes, sa, sb, a_row, b_row, NoExtra{});
     else
         mainloop_dma<E, BM, BN, BN, NS, NW, RB, SPREAD>(acc, pa, pb, kbytes, st, a_row, b_row, xpf);
 
